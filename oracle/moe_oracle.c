@@ -1,0 +1,407 @@
+/*
+ * moe_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU implementation of the forward pass of a
+ * token-choice Mixture-of-Experts SwiGLU FFN layer, written from the plain
+ * definition of what the layer computes.  Only the tests, the smoke check and
+ * the benchmark's CPU-baseline leg may load this library; the GPU product path
+ * never calls it and shares no code, header or table with it.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [P1] "Port necessary FBGEMM MoE kernels" (world_engine pull request):
+ *       Summary -- the layer's index shuffling (per-expert grouping of token
+ *       routes) and the top-k weighted scatter-add back into tokens.
+ *  [P3] "perf: add small-batch route MMA for MoE" (hpc-ops pull request):
+ *       Motivation -- the grouped pipeline count/sort -> gather -> prefix ->
+ *       Gate/Up GEMM -> activation/quantisation -> Down GEMM -> top-k
+ *       reduction, and the route-order pipeline that reaches the same result
+ *       without the sort;  Summary -- SwiGLU, FP8 per-tensor and 128x128
+ *       blockwise quantisation, Down-input FP8 requantisation.
+ *
+ * Everything here is computed per token with no sort (the sorted form is
+ * derived separately in oracle_route), in IEEE double, with the method's
+ * quantisation decisions taken in fp32 as the method takes them.
+ *
+ * Readings taken where the pages are silent (each is also listed in the design
+ * notes of the repository):
+ *  - top-k selects on the fp32 logits, descending, exact fp32 equality (so -0
+ *    equals +0) broken to the lower expert id; slot j is the j-th pick;
+ *  - gates are the softmax over all E experts renormalised over the k picks;
+ *  - the Gate/Up weight [H, 2I] holds the gate in columns [0, I) and the up
+ *    projection in columns [I, 2I); h = silu(gate) * up, silu(z) = z/(1+e^-z);
+ *  - e4m3 is the OCP e4m3fn format (bias 7, max 448, no infinities), encoded
+ *    round-to-nearest-even and saturated to +-448 (never NaN);
+ *  - a scale is amax/448 in fp32 (1 when amax is 0); a code is e4m3(v / s)
+ *    with v / s a true fp32 division;
+ *  - per-tensor: one scale for all of x [T,H] and one for all of h [T*k, I];
+ *    blockwise: one scale per token per 128 channels (x) and per route row per
+ *    128 channels (h); weight scales are given with the weights;
+ *  - the combine sums j = 0..k-1 in ascending order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_BF16 0
+#define ORC_FP8_PER_TENSOR 1
+#define ORC_FP8_BLOCK128 2
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------- codecs -- */
+
+/* bf16 is the upper half of an IEEE binary32. */
+float oracle_bf16_decode(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* OCP e4m3fn: s.eeee.mmm, bias 7.  e == 0 are subnormals m * 2^-9; otherwise
+ * (1 + m/8) * 2^(e-7) = (8 + m) * 2^(e-10).  s.1111.111 is NaN. */
+double oracle_e4m3_decode(uint8_t q) {
+    int s = q >> 7, e = (q >> 3) & 15, m = q & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+/* Round-to-nearest-even onto the e4m3fn grid, saturating at +-448.  The
+ * spacing of the grid is 2^-9 below 2^-6 and 2^(floor(log2|v|) - 3) above. */
+uint8_t oracle_e4m3_encode(float f) {
+    uint8_t sign = signbit(f) ? 0x80 : 0x00;
+    double a = fabs((double)f), quantum, n, fl, r, v;
+    int ex;
+    if (isnan(f)) return 0x7f;
+    if (a >= 448.0) return sign | 0x7e;
+    if (a < ldexp(1.0, -6)) {
+        quantum = ldexp(1.0, -9);
+    } else {
+        frexp(a, &ex);                 /* a = f * 2^ex, f in [0.5, 1) */
+        quantum = ldexp(1.0, ex - 1 - 3);
+    }
+    n = a / quantum;                   /* exact: division by a power of two */
+    fl = floor(n);
+    if (n - fl > 0.5) r = fl + 1.0;
+    else if (n - fl < 0.5) r = fl;
+    else r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;   /* tie: even mantissa */
+    v = r * quantum;                   /* <= 448 because a < 448 */
+    if (v == 0.0) return sign;
+    if (v < ldexp(1.0, -6)) {
+        return sign | (uint8_t)(v / ldexp(1.0, -9));   /* subnormal m */
+    }
+    frexp(v, &ex);
+    {
+        int E = ex - 1;                                  /* floor(log2 v) */
+        int m = (int)(v / ldexp(1.0, E - 3)) - 8;
+        return sign | (uint8_t)(((E + 7) << 3) | m);
+    }
+}
+
+/* Scale of a quantisation group: amax / 448 in fp32, or 1 for an all-zero group. */
+float oracle_scale_from_amax(float amax) {
+    return amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
+/* Quantise n fp32 values with one scale; returns the scale. */
+float oracle_quantise_group(const float *v, long n, uint8_t *q) {
+    float amax = 0.0f, s;
+    long i;
+    for (i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    s = oracle_scale_from_amax(amax);
+    for (i = 0; i < n; ++i) q[i] = oracle_e4m3_encode(v[i] / s);
+    return s;
+}
+
+/* --------------------------------------------------------------- routing -- */
+
+/* Token-choice routing.  For each token: pick k experts greedily by largest
+ * logit (ties to the lower id), gates = softmax over E renormalised over the
+ * picks.  Then the grouped form [P1 Summary "index shuffling"; P3 Motivation
+ * "count/sort", "prefix"]: per-expert counts, their exclusive prefix (E+1
+ * entries), and the route ids r = t*k + j listed expert by expert, in
+ * increasing r inside each expert (a counting sort), with its inverse. */
+void oracle_route(const float *logits, int T, int E, int k,
+                  int32_t *ids, float *weights, int32_t *counts,
+                  int32_t *offsets, int32_t *perm, int32_t *route_pos) {
+    long R = (long)T * k, r;
+    int t, e;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        const float *l = logits + (long)t * E;
+        unsigned char *taken = (unsigned char *)calloc((size_t)E, 1);
+        double m, z = 0.0, zs = 0.0;
+        int j, i;
+        for (j = 0; j < k; ++j) {
+            int best = -1;
+            for (i = 0; i < E; ++i) {
+                if (taken[i]) continue;
+                if (best < 0 || l[i] > l[best]) best = i;   /* '>' keeps the lower id on ties */
+            }
+            taken[best] = 1;
+            ids[(long)t * k + j] = best;
+        }
+        m = l[0];
+        for (i = 1; i < E; ++i) if (l[i] > m) m = l[i];
+        for (i = 0; i < E; ++i) z += exp((double)l[i] - m);
+        for (j = 0; j < k; ++j) zs += exp((double)l[ids[(long)t * k + j]] - m) / z;
+        for (j = 0; j < k; ++j) {
+            double p = exp((double)l[ids[(long)t * k + j]] - m) / z;
+            weights[(long)t * k + j] = (float)(p / zs);
+        }
+        free(taken);
+    }
+    for (e = 0; e < E; ++e) counts[e] = 0;
+    for (r = 0; r < R; ++r) counts[ids[r]]++;
+    offsets[0] = 0;
+    for (e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    {
+        int32_t *next = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+        for (e = 0; e < E; ++e) next[e] = offsets[e];
+        for (r = 0; r < R; ++r) perm[next[ids[r]]++] = (int32_t)r;
+        free(next);
+    }
+    for (r = 0; r < R; ++r) route_pos[perm[r]] = (int32_t)r;
+}
+
+/* --------------------------------------------------------------- forward -- */
+
+typedef struct {
+    int T, H, I, E, k, quant;
+    const uint16_t *x;        /* bf16 [T, H] */
+    const void *w_gu;         /* [E, H, 2I] bf16 or e4m3 */
+    const void *w_d;          /* [E, I, H]  bf16 or e4m3 */
+    const float *s_gu;        /* per-tensor [E]; block128 [E, H/128, 2I/128] */
+    const float *s_d;         /* per-tensor [E]; block128 [E, I/128, H/128] */
+    float s_x;                /* per-tensor activation scale */
+    const float *s_x_blk;     /* block128 activation scales [T, H/128] */
+    const uint8_t *q_x;       /* fp8 activation codes [T, H] */
+} orc_layer;
+
+static double w_gu_at(const orc_layer *L, int e, int h, int n) {
+    long idx = ((long)e * L->H + h) * (2L * L->I) + n;
+    if (L->quant == ORC_BF16) return oracle_bf16_decode(((const uint16_t *)L->w_gu)[idx]);
+    {
+        double q = oracle_e4m3_decode(((const uint8_t *)L->w_gu)[idx]);
+        if (L->quant == ORC_FP8_PER_TENSOR) return q * L->s_gu[e];
+        return q * L->s_gu[((long)e * (L->H / 128) + h / 128) * (2L * L->I / 128) + n / 128];
+    }
+}
+
+static double w_d_at(const orc_layer *L, int e, int i, int n) {
+    long idx = ((long)e * L->I + i) * L->H + n;
+    if (L->quant == ORC_BF16) return oracle_bf16_decode(((const uint16_t *)L->w_d)[idx]);
+    {
+        double q = oracle_e4m3_decode(((const uint8_t *)L->w_d)[idx]);
+        if (L->quant == ORC_FP8_PER_TENSOR) return q * L->s_d[e];
+        return q * L->s_d[((long)e * (L->I / 128) + i / 128) * (L->H / 128) + n / 128];
+    }
+}
+
+/* The activation entering the Gate/Up projection for token t. */
+static void activation(const orc_layer *L, int t, double *a) {
+    int h;
+    for (h = 0; h < L->H; ++h) {
+        long idx = (long)t * L->H + h;
+        if (L->quant == ORC_BF16) a[h] = oracle_bf16_decode(L->x[idx]);
+        else if (L->quant == ORC_FP8_PER_TENSOR) a[h] = oracle_e4m3_decode(L->q_x[idx]) * L->s_x;
+        else a[h] = oracle_e4m3_decode(L->q_x[idx]) * L->s_x_blk[(long)t * (L->H / 128) + h / 128];
+    }
+}
+
+/* h = silu(a W_gate) * (a W_up) for one route, in double. */
+static void gate_up_swiglu(const orc_layer *L, int e, const double *a, double *h_out, double *acc) {
+    int h, n, I2 = 2 * L->I;
+    for (n = 0; n < I2; ++n) acc[n] = 0.0;
+    for (h = 0; h < L->H; ++h) {
+        double ah = a[h];
+        if (ah == 0.0) continue;
+        for (n = 0; n < I2; ++n) acc[n] += ah * w_gu_at(L, e, h, n);
+    }
+    for (n = 0; n < L->I; ++n) {
+        double g = acc[n], u = acc[L->I + n];
+        h_out[n] = g / (1.0 + exp(-g)) * u;
+    }
+}
+
+/* y = h W_down for one route. */
+static void down(const orc_layer *L, int e, const double *h, double *y) {
+    int i, n;
+    for (n = 0; n < L->H; ++n) y[n] = 0.0;
+    for (i = 0; i < L->I; ++i) {
+        double hi = h[i];
+        if (hi == 0.0) continue;
+        for (n = 0; n < L->H; ++n) y[n] += hi * w_d_at(L, e, i, n);
+    }
+}
+
+/*
+ * Layer output for the tokens listed in tok (n_tok of them; tok == NULL means
+ * all T tokens in order), written to out[n_tok, H] in double.
+ * x: bf16 [T,H]; ids/weights: [T,k] as produced by oracle_route.
+ * quant 1 (per-tensor) needs h of every route for its scale, so it runs the
+ * Gate/Up pass over all T tokens first, whatever tok lists.
+ * Returns 0, or -1 on an unsupported shape or an allocation failure.
+ */
+int oracle_forward(const uint16_t *x, int T, int H, int I, int E, int k,
+                   const int32_t *ids, const float *weights,
+                   const void *w_gu, const void *w_d,
+                   const float *s_gu, const float *s_d, int quant,
+                   const int32_t *tok, int n_tok, double *out) {
+    orc_layer L;
+    uint8_t *q_x = NULL;
+    float *s_x_blk = NULL, *h_all = NULL, s_h = 1.0f;
+    double *hq_all = NULL;
+    int bad = 0, ti;
+    long i;
+    (void)E;
+    if (quant < 0 || quant > 2) return -1;
+    if (quant == ORC_FP8_BLOCK128 && (H % 128 || I % 128)) return -1;
+    memset(&L, 0, sizeof L);
+    L.T = T; L.H = H; L.I = I; L.E = E; L.k = k; L.quant = quant;
+    L.x = x; L.w_gu = w_gu; L.w_d = w_d; L.s_gu = s_gu; L.s_d = s_d;
+    if (n_tok == 0 || T == 0) return 0;
+
+    /* activation quantisation [P3 Summary: FP8 activations before each GEMM] */
+    if (quant != ORC_BF16) {
+        q_x = (uint8_t *)malloc((size_t)T * H);
+        if (!q_x) return -1;
+        if (quant == ORC_FP8_PER_TENSOR) {
+            float *xf = (float *)malloc(sizeof(float) * (size_t)T * H);
+            if (!xf) { free(q_x); return -1; }
+            for (i = 0; i < (long)T * H; ++i) xf[i] = oracle_bf16_decode(x[i]);
+            L.s_x = oracle_quantise_group(xf, (long)T * H, q_x);
+            free(xf);
+        } else {
+            int nb = H / 128, t, c, j;
+            s_x_blk = (float *)malloc(sizeof(float) * (size_t)T * nb);
+            if (!s_x_blk) { free(q_x); return -1; }
+            for (t = 0; t < T; ++t)
+                for (c = 0; c < nb; ++c) {
+                    float v[128];
+                    for (j = 0; j < 128; ++j) v[j] = oracle_bf16_decode(x[(long)t * H + c * 128 + j]);
+                    s_x_blk[(long)t * nb + c] = oracle_quantise_group(v, 128, q_x + (long)t * H + c * 128);
+                }
+            L.s_x_blk = s_x_blk;
+        }
+        L.q_x = q_x;
+    }
+
+    /* per-tensor Down-input requantisation needs every route's h first */
+    if (quant == ORC_FP8_PER_TENSOR) {
+        long R = (long)T * k;
+        uint8_t *q_h;
+        h_all = (float *)malloc(sizeof(float) * (size_t)R * I);
+        q_h = (uint8_t *)malloc((size_t)R * I);
+        if (!h_all || !q_h) { free(h_all); free(q_h); free(q_x); return -1; }
+#pragma omp parallel for schedule(dynamic)
+        for (ti = 0; ti < T; ++ti) {
+            double *a = (double *)malloc(sizeof(double) * (size_t)H);
+            double *acc = (double *)malloc(sizeof(double) * 2 * (size_t)I);
+            double *hr = (double *)malloc(sizeof(double) * (size_t)I);
+            int j, n;
+            activation(&L, ti, a);
+            for (j = 0; j < k; ++j) {
+                long r = (long)ti * k + j;
+                gate_up_swiglu(&L, ids[r], a, hr, acc);
+                /* the quantiser sees h as fp32, the width the method holds it in */
+                for (n = 0; n < I; ++n) h_all[r * I + n] = (float)hr[n];
+            }
+            free(a); free(acc); free(hr);
+        }
+        s_h = oracle_quantise_group(h_all, R * I, q_h);
+        free(h_all);
+        h_all = NULL;
+        hq_all = (double *)malloc(sizeof(double) * (size_t)R * I);
+        if (!hq_all) { free(q_h); free(q_x); return -1; }
+        for (i = 0; i < R * I; ++i) hq_all[i] = oracle_e4m3_decode(q_h[i]) * s_h;
+        free(q_h);
+    }
+
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (ti = 0; ti < n_tok; ++ti) {
+        int t = tok ? tok[ti] : ti, j, n, c;
+        double *a = (double *)malloc(sizeof(double) * (size_t)H);
+        double *acc = (double *)malloc(sizeof(double) * 2 * (size_t)I);
+        double *hd = (double *)malloc(sizeof(double) * (size_t)I);
+        double *y = (double *)malloc(sizeof(double) * (size_t)H);
+        double *h = (double *)malloc(sizeof(double) * (size_t)I);
+        double *o = out + (long)ti * H;
+        if (!a || !acc || !hd || !y || !h || t < 0 || t >= T) {
+            bad |= 1;
+        } else {
+            for (n = 0; n < H; ++n) o[n] = 0.0;
+            if (quant != ORC_FP8_PER_TENSOR) activation(&L, t, a);
+            for (j = 0; j < k; ++j) {
+                long r = (long)t * k + j;
+                int e = ids[r];
+                if (quant == ORC_FP8_PER_TENSOR) {
+                    for (n = 0; n < I; ++n) hd[n] = hq_all[r * I + n];
+                } else {
+                    gate_up_swiglu(&L, e, a, h, acc);
+                    if (quant == ORC_FP8_BLOCK128) {
+                        uint8_t q[128];
+                        float hf[128];
+                        for (c = 0; c < I / 128; ++c) {
+                            float s;
+                            for (n = 0; n < 128; ++n) hf[n] = (float)h[c * 128 + n];
+                            s = oracle_quantise_group(hf, 128, q);
+                            for (n = 0; n < 128; ++n) hd[c * 128 + n] = oracle_e4m3_decode(q[n]) * s;
+                        }
+                    } else {
+                        for (n = 0; n < I; ++n) hd[n] = h[n];
+                    }
+                }
+                down(&L, e, hd, y);
+                /* top-k weighted combine [P1 Summary "scatter_add"; P3 Motivation "top-k reduction"] */
+                for (n = 0; n < H; ++n) o[n] += (double)weights[r] * y[n];
+            }
+        }
+        free(a); free(acc); free(hd); free(y); free(h);
+    }
+    free(q_x); free(s_x_blk); free(h_all); free(hq_all);
+    return bad ? -1 : 0;
+}
+
+/* The quantised activations exactly as the method defines them, exposed so
+ * the tests can compare codes: per-tensor writes one scale, block128 writes
+ * [T, H/128] scales. */
+int oracle_quantise_activations(const uint16_t *x, int T, int H, int quant,
+                                uint8_t *q, float *scales) {
+    long i;
+    if (quant == ORC_FP8_PER_TENSOR) {
+        float *xf = (float *)malloc(sizeof(float) * ((size_t)T * H + 1));
+        if (!xf) return -1;
+        for (i = 0; i < (long)T * H; ++i) xf[i] = oracle_bf16_decode(x[i]);
+        scales[0] = oracle_quantise_group(xf, (long)T * H, q);
+        free(xf);
+        return 0;
+    }
+    if (quant == ORC_FP8_BLOCK128) {
+        int t, c, j, nb = H / 128;
+        if (H % 128) return -1;
+        for (t = 0; t < T; ++t)
+            for (c = 0; c < nb; ++c) {
+                float v[128];
+                for (j = 0; j < 128; ++j) v[j] = oracle_bf16_decode(x[(long)t * H + c * 128 + j]);
+                scales[(long)t * nb + c] = oracle_quantise_group(v, 128, q + (long)t * H + c * 128);
+            }
+        return 0;
+    }
+    return -1;
+}

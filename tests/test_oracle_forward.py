@@ -1,0 +1,184 @@
+"""Pins of the oracle's layer output (CPU only).
+
+Each pin reaches the same numbers by another route than the oracle's C code:
+  * a hand-evaluated example (tests/golden/hand_example.json);
+  * E=1: the plain SwiGLU FFN in torch float64 matrix form;
+  * k=E with equal logits: the mean of all experts' FFNs;
+  * brute force: every expert evaluated densely for every token with torch,
+    then masked by the routing and weighted (no permutation anywhere);
+  * FP8: the same dense formulation on tensors quantised with torch's own e4m3
+    cast, per-tensor and 128x128 blockwise.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from workloads import (bf16_bits_to_f32, random_activations, random_weights,
+                       to_bf16_bits)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
+
+
+def dense_experts(a, wgu, wd):
+    """a [T,H] f64, wgu [E,H,2I] f64, wd [E,I,H] f64 -> Y [T,E,H] (every expert)."""
+    I = wd.shape[1]
+    gu = torch.einsum("th,ehn->ten", a, wgu)
+    h = F.silu(gu[..., :I]) * gu[..., I:]
+    return torch.einsum("tei,eih->teh", h, wd)
+
+
+def combine_dense(Y, ids, w):
+    T, E, H = Y.shape
+    mask = torch.zeros(T, E, dtype=torch.float64)
+    mask.scatter_(1, torch.from_numpy(ids.astype(np.int64)), torch.from_numpy(w.astype(np.float64)))
+    return torch.einsum("te,teh->th", mask, Y)
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def test_golden_hand_example_forward():
+    g = json.load(open(GOLDEN))
+    x = to_bf16_bits(np.array(g["x"], np.float32))
+    assert np.array_equal(bf16_bits_to_f32(x), np.array(g["x"], np.float32))
+    wgu = to_bf16_bits(np.array(g["w_gate_up"], np.float32))
+    wd = to_bf16_bits(np.array(g["w_down"], np.float32))
+    r = oracle.route(np.array(g["logits"], np.float32), g["k"])
+    out = oracle.forward(x, r["topk_ids"], r["topk_weights"], wgu, wd)
+    ex = np.array(g["expected"]["out"])
+    assert np.max(np.abs(out - ex)) <= g["expected"]["tolerance_out"]
+
+
+def test_single_expert_is_plain_swiglu_ffn():
+    T, H, I = 9, 64, 32
+    a = random_activations(T, H, 1, 21)
+    w = random_weights(1, H, I, "bf16", 22)
+    r = oracle.route(a["logits"], 1)
+    out = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"])
+    x = torch.from_numpy(bf16_bits_to_f32(a["x"])).double()
+    wg = torch.from_numpy(bf16_bits_to_f32(w["w_gate_up"][0])).double()
+    wdn = torch.from_numpy(bf16_bits_to_f32(w["w_down"][0])).double()
+    ref = (F.silu(x @ wg[:, :I]) * (x @ wg[:, I:])) @ wdn
+    assert np.max(np.abs(out - ref.numpy())) <= 1e-12
+
+
+def test_all_experts_equal_gates_is_expert_mean():
+    T, H, I, E = 6, 32, 16, 8
+    a = random_activations(T, H, E, 23)
+    w = random_weights(E, H, I, "bf16", 24)
+    lg = np.zeros((T, E), np.float32)
+    r = oracle.route(lg, E)
+    out = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"])
+    x = torch.from_numpy(bf16_bits_to_f32(a["x"])).double()
+    Y = dense_experts(x, torch.from_numpy(bf16_bits_to_f32(w["w_gate_up"])).double(),
+                      torch.from_numpy(bf16_bits_to_f32(w["w_down"])).double())
+    assert np.max(np.abs(out - Y.mean(dim=1).numpy())) <= 1e-12
+
+
+@pytest.mark.parametrize("T,H,I,E,k,seed", [(12, 32, 16, 6, 3, 30), (20, 64, 32, 16, 8, 31),
+                                            (5, 16, 8, 3, 1, 32)])
+def test_brute_force_dense_masked(T, H, I, E, k, seed):
+    a = random_activations(T, H, E, seed)
+    w = random_weights(E, H, I, "bf16", seed + 100)
+    r = oracle.route(a["logits"], k)
+    out = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"])
+    x = torch.from_numpy(bf16_bits_to_f32(a["x"])).double()
+    Y = dense_experts(x, torch.from_numpy(bf16_bits_to_f32(w["w_gate_up"])).double(),
+                      torch.from_numpy(bf16_bits_to_f32(w["w_down"])).double())
+    ref = combine_dense(Y, r["topk_ids"], r["topk_weights"]).numpy()
+    assert np.max(np.abs(out - ref)) <= 1e-12
+    # a token subset gives the same rows
+    sub = np.array([T - 1, 0, T // 2], np.int32)
+    out_s = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"],
+                           tokens=sub)
+    assert np.array_equal(out_s, out[sub])
+
+
+def torch_e4m3(v):
+    return torch.clamp(v.float(), -448, 448).to(torch.float8_e4m3fn).double()
+
+
+def torch_scale(amax):
+    amax = torch.as_tensor(amax, dtype=torch.float32)
+    return torch.where(amax > 0, amax / torch.tensor(448.0, dtype=torch.float32),
+                       torch.tensor(1.0, dtype=torch.float32))
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (6, 3)])
+def test_fp8_per_tensor_dense_reformulation(E, k):
+    T, H, I = 10, 64, 32
+    a = random_activations(T, H, E, 40 + E)
+    w = random_weights(E, H, I, "fp8_per_tensor", 41 + E)
+    r = oracle.route(a["logits"], k)
+    out = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"],
+                         quant="fp8_per_tensor", s_gate_up=w["s_gate_up"], s_down=w["s_down"])
+    x = torch.from_numpy(bf16_bits_to_f32(a["x"]))
+    sx = torch_scale(x.abs().max())
+    xa = torch_e4m3(x / sx) * sx.double()
+    wgu = (torch.from_numpy(w["w_gate_up"]).view(torch.float8_e4m3fn).double()
+           * torch.from_numpy(w["s_gate_up"]).double()[:, None, None])
+    wdn = (torch.from_numpy(w["w_down"]).view(torch.float8_e4m3fn).double()
+           * torch.from_numpy(w["s_down"]).double()[:, None, None])
+    gu = torch.einsum("th,ehn->ten", xa, wgu)
+    h = (F.silu(gu[..., :I]) * gu[..., I:]).float()          # [T,E,I] fp32
+    ids = torch.from_numpy(r["topk_ids"].astype(np.int64))
+    h_routes = torch.gather(h, 1, ids[:, :, None].expand(T, k, I))   # the routed rows only
+    sh = torch_scale(h_routes.abs().max())
+    hq = torch_e4m3(h_routes / sh) * sh.double()                     # [T,k,I]
+    y = torch.einsum("tji,tjih->tjh", hq, wdn[ids])
+    ref = (y * torch.from_numpy(r["topk_weights"]).double()[:, :, None]).sum(dim=1)
+    assert np.max(np.abs(out - ref.numpy())) <= 1e-12
+
+
+def test_fp8_block128_dense_reformulation():
+    T, H, I, E, k = 7, 256, 256, 4, 2
+    a = random_activations(T, H, E, 50)
+    w = random_weights(E, H, I, "fp8_block128", 51)
+    r = oracle.route(a["logits"], k)
+    out = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"],
+                         quant="fp8_block128", s_gate_up=w["s_gate_up"], s_down=w["s_down"])
+    x = torch.from_numpy(bf16_bits_to_f32(a["x"])).reshape(T, H // 128, 128)
+    sx = torch_scale(x.abs().amax(dim=2))
+    xa = (torch_e4m3(x / sx[:, :, None]) * sx.double()[:, :, None]).reshape(T, H)
+
+    def deq(q, s):
+        Ee, K, N = q.shape
+        v = torch.from_numpy(q).view(torch.float8_e4m3fn).double().reshape(Ee, K // 128, 128, N // 128, 128)
+        return (v * torch.from_numpy(s).double()[:, :, None, :, None]).reshape(Ee, K, N)
+
+    wgu, wdn = deq(w["w_gate_up"], w["s_gate_up"]), deq(w["w_down"], w["s_down"])
+    gu = torch.einsum("th,ehn->ten", xa, wgu)
+    h = (F.silu(gu[..., :I]) * gu[..., I:]).float().reshape(T, E, I // 128, 128)
+    sh = torch_scale(h.abs().amax(dim=3))
+    hq = (torch_e4m3(h / sh[..., None]) * sh.double()[..., None]).reshape(T, E, I)
+    Y = torch.einsum("tei,eih->teh", hq, wdn)
+    ref = combine_dense(Y, r["topk_ids"], r["topk_weights"]).numpy()
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+def test_quantisation_matters():
+    """The FP8 oracle is not the bf16 oracle on dequantised weights: dropping the
+    activation quantisation moves the result by far more than the FP8 parity
+    tolerance, so the emulated quantisation is load-bearing."""
+    T, H, I, E, k = 16, 256, 128, 4, 2
+    a = random_activations(T, H, E, 60)
+    w = random_weights(E, H, I, "fp8_block128", 61)
+    r = oracle.route(a["logits"], k)
+    q = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"],
+                       quant="fp8_block128", s_gate_up=w["s_gate_up"], s_down=w["s_down"])
+    x = torch.from_numpy(bf16_bits_to_f32(a["x"])).double()
+
+    def deq(qq, s):
+        Ee, K, N = qq.shape
+        v = torch.from_numpy(qq).view(torch.float8_e4m3fn).double().reshape(Ee, K // 128, 128, N // 128, 128)
+        return (v * torch.from_numpy(s).double()[:, :, None, :, None]).reshape(Ee, K, N)
+
+    Y = dense_experts(x, deq(w["w_gate_up"], w["s_gate_up"]), deq(w["w_down"], w["s_down"]))
+    plain = combine_dense(Y, r["topk_ids"], r["topk_weights"]).numpy()
+    assert rel_l2(q, plain) > 1e-2
