@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE FFN forward (routing + grouped expert GEMMs + combine)
+on one MI355X.
+
+One step = moe_route + moe_forward over one batch whose inputs already sit in
+HBM.  The headline line is the large-T bf16 prefill layer (T=8192, H=2048,
+I=768, E=128, top-8, Zipf-skewed routing): value = tokens/s.  The same JSON
+line carries
+  * roofline: the dominant kernel (the grouped Gate/Up GEMM), its algorithmic
+    flops per launch over its average duration, measured with HIP events the
+    library records on its own stream during the timed steps;
+  * decode: µs/layer at B=1..4 (bf16 route-direct path, H=2048 I=768 E=128),
+    cold HBM (a 1 GiB buffer is rewritten between iterations), with the HBM
+    fraction of its dominant kernel;
+  * fp8: the FP8 per-tensor decode (B=1..4, H=4096 I=192 E=192) and the FP8
+    128x128-blockwise prefill (T=4096, H=4096, I=512) -- skipped with --quick;
+  * cpu_baseline: the CPU oracle on a bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s (large T) + µs/layer at B=1-4; % of HBM BW / MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dev_inputs(torch, a, wl):
+    x = torch.from_numpy(a["x"].view(np.int16)).cuda().view(torch.bfloat16)
+    lg = torch.from_numpy(a["logits"]).cuda()
+    return x, lg
+
+
+def dev_weights(torch, moe, w, quant):
+    if quant == "bf16":
+        gu = torch.from_numpy(w["w_gate_up"].view(np.int16)).cuda()
+        dn = torch.from_numpy(w["w_down"].view(np.int16)).cuda()
+        scales = None
+    else:
+        gu = torch.from_numpy(w["w_gate_up"]).cuda()
+        dn = torch.from_numpy(w["w_down"]).cuda()
+        scales = (torch.from_numpy(w["s_gate_up"]).cuda(), torch.from_numpy(w["s_down"]).cuda())
+    pgu, pd = moe.pack_weights(gu, dn, quant)
+    torch.cuda.synchronize()
+    del gu, dn
+    return pgu, pd, scales
+
+
+class Layer:
+    """Preallocated routes, output and workspaces for repeated steps."""
+
+    def __init__(self, torch, moe, wl, T, x, lg, weights, path="auto"):
+        self.torch, self.moe, self.wl, self.T = torch, moe, wl, T
+        self.x, self.lg = x, lg
+        self.pgu, self.pd, self.scales = weights
+        self.path = moe.select_path(T, wl.H, wl.I, wl.E, wl.k, wl.quant, path)
+        self.routes = moe.Routes(T, wl.E, wl.k, x.device)
+        self.out = torch.empty((T, wl.H), dtype=torch.bfloat16, device=x.device)
+        n = moe.forward_workspace_size(T, wl.H, wl.I, wl.E, wl.k, wl.quant, self.path)
+        self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+        rn = moe.route_workspace_size(T, wl.E, wl.k)
+        self.rws = torch.empty(rn, dtype=torch.uint8, device=x.device) if rn else None
+
+    def step(self, events=None, lg=None):
+        self.moe.route(self.lg if lg is None else lg, self.wl.k, out=self.routes, workspace=self.rws)
+        return self.moe.forward(self.x, self.routes, self.pgu, self.pd, quant=self.wl.quant,
+                                scales=self.scales, out=self.out, path=self.path, workspace=self.ws,
+                                events=events)
+
+
+def stage_times(torch, ev_sets, names):
+    """Average ms per stage over the recorded steps."""
+    n = len(names)
+    tot = np.zeros(n)
+    for evs in ev_sets:
+        for i in range(n):
+            tot[i] += evs[i].elapsed_time(evs[i + 1])
+    return {names[i]: tot[i] / len(ev_sets) for i in range(n)}
+
+
+def bench_prefill(torch, moe, name, steps, warmup):
+    from workloads import WORKLOADS, workload_inputs, workload_weights
+    wl = WORKLOADS[name]
+    a = workload_inputs(name)
+    w = workload_weights(name)
+    x, lg = dev_inputs(torch, a, wl)
+    layer = Layer(torch, moe, wl, wl.T, x, lg, dev_weights(torch, moe, w, wl.quant))
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
+    for evs in ev_sets:                       # create the events before the timed region
+        for e in evs:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    names = None
+    for evs in ev_sets:
+        _, names = layer.step(events=evs)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = stage_times(torch, ev_sets, names)
+    counts = layer.routes.expert_counts.cpu().numpy()
+    return dict(wl=wl, dt=dt, stages_ms=st, path=layer.path, counts=counts, layer=layer, host=(a, w))
+
+
+def roofline_gemm(wl, stages_ms, peak):
+    R = wl.T * wl.k
+    flops = 4.0 * R * wl.H * wl.I            # Gate/Up: 2 flops x R rows x H x 2I
+    t = stages_ms["gate_up"] / 1e3
+    achieved = flops / t / 1e12
+    return dict(kernel="grouped_gemm_kernel (Gate/Up + SwiGLU)", bound="mfma", achieved=round(achieved, 2),
+                peak=peak, unit="TFLOP/s", frac=round(achieved / peak, 4), traffic=None,
+                flops_per_launch=flops, avg_launch_us=round(stages_ms["gate_up"] * 1e3, 2))
+
+
+def bench_decode(torch, moe, name, batches, iters, nsets=32):
+    """Cold-HBM decode latency: a 1 GiB rewrite between iterations, 32 rotating routing sets."""
+    from workloads import WORKLOADS, random_activations, workload_weights
+    wl = WORKLOADS[name]
+    w = workload_weights(name)
+    weights = dev_weights(torch, moe, w, wl.quant)
+    evict = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    elem = 2 if wl.quant == "bf16" else 1
+    res = {}
+    for B in batches:
+        sets = [random_activations(B, wl.H, wl.E, 10000 + i) for i in range(nsets)]
+        xs = [dev_inputs(torch, s, wl) for s in sets]
+        layer = Layer(torch, moe, wl, B, xs[0][0], xs[0][1], weights)
+        ev_sets, distinct = [], []
+        for it in range(iters + 2):
+            layer.x, layer.lg = xs[it % nsets]
+            evict.fill_(it & 0xff)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+            for e in evs:
+                e.record()
+            _, names = layer.step(events=evs)
+            if it >= 2:
+                ev_sets.append((evs, names))
+        torch.cuda.synchronize()
+        for it in range(nsets):
+            ids = moe.route(xs[it][1], wl.k).topk_ids.cpu().numpy()
+            distinct.append(len(np.unique(ids)))
+        fwd, dom = [], []
+        for evs, names in ev_sets:
+            dname = "rd_gate_up" if "rd_gate_up" in names else "gate_up"
+            i = names.index(dname)
+            fwd.append(evs[0].elapsed_time(evs[len(names)]))
+            dom.append(evs[i].elapsed_time(evs[i + 1]))
+        t_fwd = float(np.median(fwd)) * 1e3      # us
+        t_dom = float(np.median(dom)) * 1e3
+        D = float(np.mean(distinct))
+        w_bytes = D * 3 * wl.H * wl.I * elem
+        dom_bytes = D * 2 * wl.H * wl.I * elem + B * wl.H * elem   # Gate/Up weights + activations
+        res[B] = dict(us_per_layer=round(t_fwd, 2), tokens_per_s=round(B / (t_fwd * 1e-6), 1),
+                      path=layer.path, distinct_experts=round(D, 2),
+                      hbm_frac_layer=round(w_bytes / (t_fwd * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
+                      dominant=dict(kernel=dname, bound="hbm", avg_launch_us=round(t_dom, 2),
+                                    achieved=round(dom_bytes / (t_dom * 1e-6) / 1e9, 1),
+                                    peak=PEAK_HBM_GBS, unit="GB/s",
+                                    frac=round(dom_bytes / (t_dom * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)))
+        log(f"decode {name} B={B}: {t_fwd:.2f} us/layer, {res[B]['dominant']['kernel']} "
+            f"{res[B]['dominant']['achieved']} GB/s")
+    del evict
+    return res
+
+
+def cpu_baseline(a, w, wl, budget_s=15.0):
+    import oracle
+    lg, x = a["logits"], a["x"]
+    t0 = time.perf_counter()
+    r = oracle.route(lg, wl.k)
+    oracle.forward(x, r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"], quant=wl.quant,
+                   s_gate_up=w["s_gate_up"], s_down=w["s_down"], tokens=np.arange(32, dtype=np.int32))
+    probe = time.perf_counter() - t0
+    n = int(min(wl.T, max(64, 32 * budget_s / max(probe, 1e-3))))
+    tok = np.arange(n, dtype=np.int32)
+    t0 = time.perf_counter()
+    r = oracle.route(lg, wl.k)
+    oracle.forward(x, r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"], quant=wl.quant,
+                   s_gate_up=w["s_gate_up"], s_down=w["s_down"], tokens=tok)
+    dt = time.perf_counter() - t0
+    return dict(value=round(n / dt, 2), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"routing of all {wl.T} tokens + layer output of the first {n} tokens "
+                       f"of {wl.name} (fp64 C oracle, OpenMP), {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-iters", type=int, default=200)
+    ap.add_argument("--quick", action="store_true", help="headline line only (no fp8 extras)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the layer's expert/tensor sharding is described in DESIGN.md but not built); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import routing_grouped_expert_index_amd as moe
+    torch.cuda.set_device(0)
+
+    log("prefill bf16 T=8192 ...")
+    pf = bench_prefill(torch, moe, "prefill_bf16", args.steps, args.warmup)
+    wl = pf["wl"]
+    ms = pf["dt"] / args.steps * 1e3
+    value = wl.T * args.steps / pf["dt"]
+    roof = roofline_gemm(wl, pf["stages_ms"], PEAK_BF16_TFLOPS)
+    log(f"prefill bf16: {ms:.3f} ms/step, {value:.4g} tokens/s, gate_up {roof['achieved']} TFLOP/s")
+    line = dict(metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="bf16",
+                data="synthetic: seeded N(0,1) bf16 activations, N(0,1)+Zipf-bias router logits, "
+                     "N(0,0.02) bf16 expert weights",
+                config=dict(workload="prefill_bf16", T=wl.T, H=wl.H, I=wl.I, E=wl.E, top_k=wl.k,
+                            path=pf["path"], routing="softmax top-8 renormalised, Zipf-skewed load",
+                            max_expert_rows=int(pf["counts"].max()), min_expert_rows=int(pf["counts"].min())),
+                roofline=roof,
+                stages_us={k: round(v * 1e3, 2) for k, v in pf["stages_ms"].items()})
+    a, w = pf["host"]
+    del pf["layer"]
+    torch.cuda.empty_cache()
+
+    log("decode bf16 B=1..4 (cold HBM) ...")
+    line["decode"] = dict(workload="decode_bf16 H=2048 I=768 E=128 top-8", timing="cold HBM, median of "
+                          f"{args.decode_iters}, forward span between HIP events",
+                          batches=bench_decode(torch, moe, "decode_bf16", (1, 2, 3, 4), args.decode_iters))
+    torch.cuda.empty_cache()
+    if not args.quick:
+        log("decode fp8 per-tensor B=1..4 ...")
+        line["decode_fp8_per_tensor"] = dict(
+            workload="decode_fp8_tensor H=4096 I=192 E=192 top-8",
+            batches=bench_decode(torch, moe, "decode_fp8_tensor", (1, 2, 3, 4), args.decode_iters))
+        torch.cuda.empty_cache()
+        log("prefill fp8 block128 T=4096 ...")
+        p5 = bench_prefill(torch, moe, "prefill_fp8_block", args.steps, args.warmup)
+        w5 = p5["wl"]
+        r5 = roofline_gemm(w5, p5["stages_ms"], PEAK_FP8_TFLOPS)
+        line["prefill_fp8_block128"] = dict(
+            workload="prefill_fp8_block T=4096 H=4096 I=512 E=128 top-8",
+            tokens_per_s=round(w5.T * args.steps / p5["dt"], 1),
+            ms_per_step=round(p5["dt"] / args.steps * 1e3, 4), roofline=r5,
+            stages_us={k: round(v * 1e3, 2) for k, v in p5["stages_ms"].items()})
+        del p5
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(a, w, wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

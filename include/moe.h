@@ -1,0 +1,162 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE FFN forward library.
+ *
+ * The library computes the forward pass of a token-choice Mixture-of-Experts
+ * SwiGLU FFN layer on one GPU:
+ *
+ *   routing   top-k over the router logits, softmax gates renormalised over the
+ *             k picks, then the routes grouped by expert: per-expert counts,
+ *             their exclusive prefix and a stable permutation of route ids
+ *             ("Port necessary FBGEMM MoE kernels", Summary: index_shuffling;
+ *              "perf: add small-batch route MMA for MoE", Motivation:
+ *              count/sort and prefix of the grouped pipeline);
+ *   forward   Gate/Up projection, SwiGLU, optional FP8 requantisation, Down
+ *             projection and the top-k weighted combine, either over the
+ *             expert-grouped routes (grouped GEMMs) or straight from the routes
+ *             for small decode batches ("perf: add small-batch route MMA for
+ *             MoE", Summary, Motivation and Dispatch).
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a device pointer (HIP global memory of the current
+ *     device) unless stated otherwise; every buffer is allocated and owned by
+ *     the caller.  The library never allocates or frees device memory, never
+ *     synchronises the stream and never copies device data to the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued on it in order, so calls can be captured in a HIP
+ *     graph.
+ *   - Return value: MOE_OK (0) or a negative moe_status.  On error nothing has
+ *     been enqueued (argument checks run before any launch) except for
+ *     MOE_ERR_HIP, which reports a failed launch.  moe_last_error() gives a
+ *     message for the calling thread's last error.
+ *   - Device contents are never validated (that would need a synchronisation):
+ *     routes that moe_route did not produce (for example ids >= E) give
+ *     undefined results.
+ *   - Pointers must be 16-byte aligned.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, k > E, negative sizes, ... */
+    MOE_ERR_UNSUPPORTED = -2,   /* shape or quantisation this build does not handle */
+    MOE_ERR_WORKSPACE = -3,     /* workspace smaller than the *_workspace_size query */
+    MOE_ERR_HIP = -4            /* a kernel launch failed */
+} moe_status;
+
+typedef enum {
+    MOE_BF16 = 0,               /* bf16 x and weights, fp32 accumulation */
+    MOE_FP8_PER_TENSOR = 1,     /* e4m3 weights with one fp32 scale per expert tensor;
+                                   x and h quantised on device with one scale each */
+    MOE_FP8_BLOCK128 = 2        /* e4m3 weights with fp32 scales per 128x128 block;
+                                   x and h quantised per row per 128 channels */
+} moe_quant;
+
+typedef enum {
+    MOE_PATH_AUTO = 0,          /* the dispatch rule picks (see moe_select_path) */
+    MOE_PATH_GROUPED = 1,       /* sort by expert, grouped MFMA GEMMs */
+    MOE_PATH_ROUTE_DIRECT = 2   /* per-route weight streaming, no sort or gather */
+} moe_path;
+
+/* Routes of T tokens over E experts, k per token.  Device arrays, int32 unless
+ * noted, all caller-allocated:
+ *   topk_ids       [T,k]  slot j = the j-th largest logit; equal logits (exact
+ *                         fp32 equality, -0 == +0) go to the lower expert id
+ *   topk_weights   [T,k]  fp32 gates: softmax over all E renormalised over the
+ *                         k picks (= exp(l_j - max) / sum over picks)
+ *   expert_counts  [E]    routes per expert
+ *   expert_offsets [E+1]  exclusive prefix of the counts; offsets[E] = T*k
+ *   perm           [T*k]  route ids r = t*k + j ordered by (expert, r)
+ *   route_pos      [T*k]  inverse of perm: perm[route_pos[r]] = r           */
+typedef struct {
+    int32_t *topk_ids;
+    float *topk_weights;
+    int32_t *expert_counts;
+    int32_t *expert_offsets;
+    int32_t *perm;
+    int32_t *route_pos;
+    int32_t T, E, k;
+} moe_routes;
+
+/* FP8 weight scales (device fp32 arrays; NULL members for MOE_BF16), in the
+ * layout of the UNPACKED weights:
+ *   per-tensor: w_gate_up_scale [E], w_down_scale [E]
+ *   block128:   w_gate_up_scale [E][H/128][2I/128], w_down_scale [E][I/128][H/128] */
+typedef struct {
+    const float *w_gate_up_scale;
+    const float *w_down_scale;
+} moe_scales;
+
+/* Bytes of workspace moe_route needs (0 is a valid answer: pass ws = NULL). */
+size_t moe_route_workspace_size(int T, int E, int k);
+
+/* Routing ("perf: add small-batch route MMA for MoE", Summary: routes are
+ * token/top-k; "Port necessary FBGEMM MoE kernels", Summary: index_shuffling).
+ * logits: fp32 [T,E], row-major.  Requires 1 <= k <= E <= 512, T >= 0 and
+ * T*k < 2^31; out->T/E/k are set by this call.  T = 0 writes zero counts and
+ * offsets.  NaN logits are not supported. */
+int moe_route(const float *logits, int T, int E, int k, moe_routes *out,
+              void *ws, size_t ws_bytes, void *stream);
+
+/* Weight re-layout, once per weight set (not per forward call).
+ *   w_gate_up [E][H][2I] (gate = columns [0,I), up = columns [I,2I)) and
+ *   w_down [E][I][H], bf16 (2 bytes) or e4m3 codes (1 byte), row-major
+ * -> packed_gate_up and packed_down, each the same size as its source, K
+ * (the reduction dimension) contiguous, gate and up columns interleaved in
+ * groups of 16.  moe_forward reads only the packed form.  Scales are not
+ * re-laid out. */
+int moe_pack_weights(const void *w_gate_up, const void *w_down, int E, int H, int I,
+                     int quant, void *packed_gate_up, void *packed_down, void *stream);
+
+/* The path MOE_PATH_AUTO takes for this shape, or a negative moe_status if
+ * the requested path cannot run it.  Host-only; no GPU call. */
+int moe_select_path(int T, int H, int I, int E, int k, int quant, int path);
+
+/* Bytes of workspace moe_forward needs for this shape, quantisation and path. */
+size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int quant, int path);
+
+/* Layer forward ("perf: add small-batch route MMA for MoE", Motivation and
+ * Summary; "Port necessary FBGEMM MoE kernels", Summary: scatter_add):
+ *   out[t] = sum_j topk_weights[t,j] * FFN_{topk_ids[t,j]}(x[t])
+ *   FFN_e(v) = (silu(v W_gate[e]) * (v W_up[e])) W_down[e]
+ * x: bf16 [T,H]; out: bf16 [T,H], fully overwritten; routes: from moe_route
+ * (same T, E, k); weights: packed by moe_pack_weights.
+ * FP8: x is quantised on device (per-tensor: one scale amax/448 for all of x;
+ * block128: per token per 128 channels); the SwiGLU output h is requantised
+ * the same way before Down (per-tensor: one scale for all T*k rows).
+ * The combine sums the k routes of a token in a fixed order in fp32 and
+ * rounds to bf16 once: repeated calls give identical bits.
+ * Shapes: H % 128 == 0, I % 64 == 0 (block128: I % 128 == 0); the
+ * route-direct path also needs H*elem <= 8192 bytes and I*elem <= 2048 bytes. */
+int moe_forward(const void *x, const moe_routes *routes, const void *packed_gate_up,
+                const void *packed_down, const moe_scales *scales, void *out, int H, int I,
+                int quant, int path, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_forward with stage timing for profilers and benchmarks: the same
+ * kernels, plus hipEventRecord(stage_events[i], stream) before the first
+ * launch and after each launch (no synchronisation).  stage_events holds
+ * n_events caller-created hipEvent_t handles; recording stops when they run
+ * out.  *n_stages receives the number of launches and stage_names (may be
+ * NULL) a comma-separated list of their names, e.g.
+ * "init,gate_up,down,combine" for the bf16 grouped path. */
+int moe_forward_profiled(const void *x, const moe_routes *routes, const void *packed_gate_up,
+                         const void *packed_down, const moe_scales *scales, void *out, int H,
+                         int I, int quant, int path, void *ws, size_t ws_bytes, void *stream,
+                         void **stage_events, int n_events, int *n_stages,
+                         const char **stage_names);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

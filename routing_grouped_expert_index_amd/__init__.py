@@ -1,0 +1,213 @@
+"""MI355X (gfx950) MoE FFN forward: Python binding of the C ABI in include/moe.h.
+
+This module only marshals arguments: torch supplies device memory and the
+stream, and every step of the layer runs in the HIP kernels of
+``libmoe_mi355x.so``.  There is no fallback: if the library is not built, or
+no GPU is present, the calls raise.
+
+    routes = route(logits, k)                         # top-k + grouping by expert
+    gu, dn = pack_weights(w_gate_up, w_down, quant)   # once per weight set
+    out = forward(x, routes, gu, dn, quant=..., scales=(s_gu, s_d), path="auto")
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_DIR, "libmoe_mi355x.so")
+
+QUANT = {"bf16": 0, "fp8_per_tensor": 1, "fp8_block128": 2}
+PATH = {"auto": 0, "grouped": 1, "route_direct": 2}
+PATH_NAME = {v: k for k, v in PATH.items()}
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
+          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
+
+EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_pack_weights", "moe_select_path",
+            "moe_forward_workspace_size", "moe_forward", "moe_forward_profiled", "moe_last_error"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _CRoutes(ctypes.Structure):
+    _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
+                ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p), ("route_pos", ctypes.c_void_p),
+                ("T", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32)]
+
+
+class _CScales(ctypes.Structure):
+    _fields_ = [("w_gate_up_scale", ctypes.c_void_p), ("w_down_scale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.moe_route_workspace_size.restype = sz
+    L.moe_route_workspace_size.argtypes = [i32, i32, i32]
+    L.moe_route.restype = i32
+    L.moe_route.argtypes = [P, i32, i32, i32, ctypes.POINTER(_CRoutes), P, sz, P]
+    L.moe_pack_weights.restype = i32
+    L.moe_pack_weights.argtypes = [P, P, i32, i32, i32, i32, P, P, P]
+    L.moe_select_path.restype = i32
+    L.moe_select_path.argtypes = [i32] * 7
+    L.moe_forward_workspace_size.restype = sz
+    L.moe_forward_workspace_size.argtypes = [i32] * 7
+    L.moe_forward.restype = i32
+    L.moe_forward.argtypes = [P, ctypes.POINTER(_CRoutes), P, P, ctypes.POINTER(_CScales), P, i32,
+                              i32, i32, i32, P, sz, P]
+    L.moe_forward_profiled.restype = i32
+    L.moe_forward_profiled.argtypes = L.moe_forward.argtypes + [ctypes.POINTER(ctypes.c_void_p), i32,
+                                                               ctypes.POINTER(ctypes.c_int),
+                                                               ctypes.POINTER(ctypes.c_char_p)]
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise MoeError(rc, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need_cuda(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Routes:
+    """Device routing arrays of T tokens over E experts (see moe_routes in moe.h)."""
+
+    def __init__(self, T: int, E: int, k: int, device):
+        i32 = dict(dtype=torch.int32, device=device)
+        self.T, self.E, self.k = T, E, k
+        self.topk_ids = torch.empty((T, k), **i32)
+        self.topk_weights = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.expert_counts = torch.empty(E, **i32)
+        self.expert_offsets = torch.empty(E + 1, **i32)
+        self.perm = torch.empty(T * k, **i32)
+        self.route_pos = torch.empty(T * k, **i32)
+
+    def c_struct(self) -> _CRoutes:
+        return _CRoutes(self.topk_ids.data_ptr(), self.topk_weights.data_ptr(),
+                        self.expert_counts.data_ptr(), self.expert_offsets.data_ptr(),
+                        self.perm.data_ptr(), self.route_pos.data_ptr(), self.T, self.E, self.k)
+
+
+def route_workspace_size(T: int, E: int, k: int) -> int:
+    return int(lib().moe_route_workspace_size(T, E, k))
+
+
+def route(logits: torch.Tensor, k: int, out: Routes | None = None,
+          workspace: torch.Tensor | None = None, stream=None) -> Routes:
+    """Top-k routing of fp32 logits [T, E] and its grouped form (moe_route)."""
+    _need_cuda(logits, "logits")
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be float32 [T, E]")
+    T, E = logits.shape
+    out = out if out is not None else Routes(T, E, k, logits.device)
+    need = route_workspace_size(T, E, k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    cs = out.c_struct()
+    _check(lib().moe_route(_ptr(logits), T, E, k, ctypes.byref(cs), _ptr(workspace),
+                           0 if workspace is None else workspace.numel(),
+                           _stream(logits.device, stream)))
+    return out
+
+
+def pack_weights(w_gate_up: torch.Tensor, w_down: torch.Tensor, quant: str = "bf16", stream=None):
+    """Re-lay [E,H,2I] and [E,I,H] weights into the packed K-contiguous form (moe_pack_weights)."""
+    _need_cuda(w_gate_up, "w_gate_up")
+    _need_cuda(w_down, "w_down")
+    E, H, I2 = w_gate_up.shape
+    I = I2 // 2
+    if tuple(w_down.shape) != (E, I, H):
+        raise ValueError("w_down must be [E, I, H]")
+    pgu = torch.empty_like(w_gate_up)
+    pd = torch.empty_like(w_down)
+    _check(lib().moe_pack_weights(_ptr(w_gate_up), _ptr(w_down), E, H, I, QUANT[quant], _ptr(pgu),
+                                  _ptr(pd), _stream(w_gate_up.device, stream)))
+    return pgu, pd
+
+
+def select_path(T, H, I, E, k, quant="bf16", path="auto") -> str:
+    rc = lib().moe_select_path(T, H, I, E, k, QUANT[quant], PATH[path])
+    _check(rc if rc < 0 else 0)
+    return PATH_NAME[rc]
+
+
+def forward_workspace_size(T, H, I, E, k, quant="bf16", path="auto") -> int:
+    return int(lib().moe_forward_workspace_size(T, H, I, E, k, QUANT[quant], PATH[path]))
+
+
+def forward(x: torch.Tensor, routes: Routes, packed_gate_up: torch.Tensor, packed_down: torch.Tensor,
+            quant: str = "bf16", scales=None, out: torch.Tensor | None = None, path: str = "auto",
+            workspace: torch.Tensor | None = None, stream=None, events=None):
+    """Layer output bf16 [T, H] (moe_forward).
+
+    With events (a list of torch.cuda.Event(enable_timing=True)) it calls
+    moe_forward_profiled instead, which records events[0] before the first
+    launch and events[i] after launch i, and returns (out, stage_names)."""
+    _need_cuda(x, "x")
+    if x.element_size() != 2 or x.dim() != 2:
+        raise ValueError("x must be a bf16 [T, H] tensor")
+    T, H = x.shape
+    I = packed_down.shape[1] if packed_down.dim() == 3 else None
+    if packed_down.dim() != 3 or packed_down.shape[2] != H:
+        raise ValueError("packed_down must be [E, I, H] (the shape of the unpacked tensor)")
+    if routes.T != T:
+        raise ValueError("routes and x disagree on T")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    need = forward_workspace_size(T, H, I, routes.E, routes.k, quant, path)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    cs = routes.c_struct()
+    sc = _CScales(None, None)
+    if scales is not None:
+        sc = _CScales(scales[0].data_ptr(), scales[1].data_ptr())
+    args = (_ptr(x), ctypes.byref(cs), _ptr(packed_gate_up), _ptr(packed_down), ctypes.byref(sc),
+            _ptr(out), H, I, QUANT[quant], PATH[path], _ptr(workspace), workspace.numel(),
+            _stream(x.device, stream))
+    if events is None:
+        _check(lib().moe_forward(*args))
+        return out
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    for ev in events:
+        if not ev.cuda_event:
+            ev.record(st)           # torch creates the underlying event on first record
+    handles = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
+    n = ctypes.c_int(0)
+    names = ctypes.c_char_p()
+    _check(lib().moe_forward_profiled(*args, handles, len(events), ctypes.byref(n), ctypes.byref(names)))
+    return out, names.value.decode().split(",")[: n.value]

@@ -1,0 +1,246 @@
+// Small kernels of the MoE forward on gfx950: per-call initialisation and the
+// device-built tile map of the grouped path, FP8 activation quantisation, the
+// Down-input requantisation, and the deterministic top-k combine.
+//
+// Tile map ("perf: add small-batch route MMA for MoE", Motivation: prefix/task
+// map; Code changes: task-map bound tightened to the non-empty workload;
+// "[mxfp8 moe training] add per group blocked scale kernels", Summary: per-group
+// start rows computed on device with no device-to-host sync): expert e owns
+// ceil(count_e / 128) row tiles; the tiles of all experts are listed in expert
+// order with their first sorted row, and the count of listed tiles is left in
+// device memory.  GEMM grids are launched at the bound ceil(R/128) + min(E, R)
+// and workgroups past the count exit at once.
+//
+// Combine ("Port necessary FBGEMM MoE kernels", Summary: scatter_add_dense_tokens;
+// "perf: add small-batch route MMA for MoE", Code changes: reduce contiguous
+// route-order outputs): out[t] = sum_{j=0..k-1} w[t,j] * y[t*k + j], summed in
+// fp32 in ascending j and rounded to bf16 once -- no atomics, so two runs give
+// the same bits.
+#include "common.cuh"
+#include "launch.h"
+
+namespace moe {
+
+int grouped_max_tiles(int R, int E) { return ceil_div(R, kGemmBM) + (E < R ? E : R); }
+
+__global__ void __launch_bounds__(kMaxExperts)
+forward_init_kernel(int E, const int32_t* __restrict__ offsets, int build_tiles,
+                    int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                    uint32_t* __restrict__ amax) {
+    __shared__ int32_t wsum[kMaxExperts / kWave];
+    const int e = threadIdx.x, lane = lane_id(), wave = e / kWave;
+    if (amax && e < 2) amax[e] = 0u;
+    if (!build_tiles) return;
+    int nt = 0, o0 = 0;
+    if (e < E) {
+        o0 = offsets[e];
+        nt = ceil_div(offsets[e + 1] - o0, kGemmBM);
+    }
+    int incl = nt;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int start = before + incl - nt;
+    for (int i = 0; i < nt; ++i) {
+        tiles[2 * (start + i)] = e;
+        tiles[2 * (start + i) + 1] = o0 + i * kGemmBM;
+    }
+    if (e == blockDim.x - 1) ntiles[0] = before + incl;
+}
+
+hipError_t launch_forward_init(const FwdPlan& p, bool build_tiles, hipStream_t st) {
+    hipLaunchKernelGGL(forward_init_kernel, dim3(1), dim3(kMaxExperts), 0, st, p.E, p.offsets,
+                       build_tiles ? 1 : 0, p.tiles, p.ntiles, p.amax);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- FP8 quant --
+
+template <typename TIn>
+__device__ __forceinline__ void load8(const TIn* p, float v[8]);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float v[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+
+__device__ __forceinline__ void store8_e4m3(uint8_t* q, const float v[8], float s) {
+    uint2 w;
+    w.x = f32x4_to_e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+    w.y = f32x4_to_e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
+    *reinterpret_cast<uint2*>(q) = w;
+}
+
+// Per row, per 128 columns: s = amax/448, q = e4m3(v / s).  16 threads per group.
+template <typename TIn>
+__global__ void __launch_bounds__(256)
+quant_block128_kernel(const TIn* __restrict__ in, int rows, int cols, uint8_t* __restrict__ q,
+                      float* __restrict__ scales) {
+    const int groups_per_row = cols / 128;
+    const long g = (long)blockIdx.x * 16 + threadIdx.x / 16;
+    if (g >= (long)rows * groups_per_row) return;
+    const int sub = threadIdx.x & 15;
+    const long row = g / groups_per_row;
+    const int c = (int)(g % groups_per_row);
+    const long base = row * cols + (long)c * 128 + sub * 8;
+    float v[8];
+    load8<TIn>(in + base, v);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+    const float s = scale_from_amax(a);
+    store8_e4m3(q + base, v, s);
+    if (sub == 0) scales[row * groups_per_row + c] = s;
+}
+
+// amax over n values (n % 8 == 0), folded into *amax_bits with atomicMax on
+// the bit pattern (non-negative floats order like their bits).
+template <typename TIn>
+__global__ void __launch_bounds__(256)
+amax_kernel(const TIn* __restrict__ in, long n, uint32_t* __restrict__ amax_bits) {
+    float a = 0.0f;
+    for (long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n;
+         i += (long)gridDim.x * blockDim.x * 8) {
+        float v[8];
+        load8<TIn>(in + i, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[j]));
+    }
+    a = wave_max(a);
+    if (lane_id() == 0) atomicMax(amax_bits, __float_as_uint(a));
+}
+
+template <typename TIn>
+__global__ void __launch_bounds__(256)
+quant_tensor_kernel(const TIn* __restrict__ in, long n, const uint32_t* __restrict__ amax_bits,
+                    uint8_t* __restrict__ q, float* __restrict__ scale_out) {
+    const float s = scale_from_amax(__uint_as_float(*amax_bits));
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+    for (long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n;
+         i += (long)gridDim.x * blockDim.x * 8) {
+        float v[8];
+        load8<TIn>(in + i, v);
+        store8_e4m3(q + i, v, s);
+    }
+}
+
+// One workgroup does amax and quantisation of a small tensor in one launch.
+template <typename TIn>
+__global__ void __launch_bounds__(1024)
+quant_tensor_small_kernel(const TIn* __restrict__ in, long n, uint8_t* __restrict__ q,
+                          float* __restrict__ scale_out) {
+    __shared__ float part[1024 / kWave];
+    float a = 0.0f;
+    for (long i = (long)threadIdx.x * 8; i < n; i += (long)blockDim.x * 8) {
+        float v[8];
+        load8<TIn>(in + i, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[j]));
+    }
+    a = wave_max(a);
+    if (lane_id() == 0) part[threadIdx.x / kWave] = a;
+    __syncthreads();
+    a = 0.0f;
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) a = fmaxf(a, part[w]);
+    const float s = scale_from_amax(a);
+    if (threadIdx.x == 0) *scale_out = s;
+    for (long i = (long)threadIdx.x * 8; i < n; i += (long)blockDim.x * 8) {
+        float v[8];
+        load8<TIn>(in + i, v);
+        store8_e4m3(q + i, v, s);
+    }
+}
+
+constexpr long kSmallQuant = 1L << 16;
+
+hipError_t launch_quant_x(const FwdPlan& p, hipStream_t st) {
+    const long n = (long)p.T * p.H;
+    if (p.quant == Q_FP8_BLOCK) {
+        const long groups = (long)p.T * (p.H / 128);
+        hipLaunchKernelGGL(quant_block128_kernel<uint16_t>, dim3((unsigned)ceil_div((int)groups, 16)),
+                           dim3(256), 0, st, p.x, p.T, p.H, p.xq, p.sx);
+        return hipGetLastError();
+    }
+    if (n <= kSmallQuant) {
+        hipLaunchKernelGGL(quant_tensor_small_kernel<uint16_t>, dim3(1), dim3(1024), 0, st, p.x, n,
+                           p.xq, &p.scal[0]);
+        return hipGetLastError();
+    }
+    const unsigned grid = (unsigned)std::min<long>(2048, (n / 8 + 255) / 256);
+    hipLaunchKernelGGL(amax_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, p.x, n, &p.amax[0]);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(quant_tensor_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, p.x, n,
+                       &p.amax[0], p.xq, &p.scal[0]);
+    return hipGetLastError();
+}
+
+// h (fp32 [R, I]) -> e4m3 codes.  Per-tensor uses the amax the Gate/Up kernels
+// folded into amax[1]; blockwise computes each row's 128-column groups here.
+hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st) {
+    const long n = (long)p.R * p.I;
+    const float* h = static_cast<const float*>(p.h);
+    if (p.quant == Q_FP8_BLOCK) {
+        const long groups = (long)p.R * (p.I / 128);
+        hipLaunchKernelGGL(quant_block128_kernel<float>, dim3((unsigned)ceil_div((int)groups, 16)),
+                           dim3(256), 0, st, h, p.R, p.I, p.hq, p.sh);
+        return hipGetLastError();
+    }
+    const unsigned grid = (unsigned)std::min<long>(2048, std::max<long>(1, (n / 8 + 255) / 256));
+    hipLaunchKernelGGL(quant_tensor_kernel<float>, dim3(grid), dim3(256), 0, st, h, n, &p.amax[1],
+                       p.hq, &p.scal[1]);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ combine --
+
+__global__ void __launch_bounds__(256)
+combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, int H, int k,
+               uint16_t* __restrict__ out) {
+    const int t = blockIdx.x;
+    const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+    if (c >= H) return;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        const float w = tw[(size_t)t * k + j];
+        float v[8];
+        load8<uint16_t>(y + ((size_t)t * k + j) * H + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(out + (size_t)t * H + c) = o;
+}
+
+hipError_t launch_combine(const FwdPlan& p, hipStream_t st) {
+    dim3 grid(p.T, ceil_div(p.H / 8, 256));
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, p.y, p.tw, p.H, p.k, p.out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

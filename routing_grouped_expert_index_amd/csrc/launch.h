@@ -1,0 +1,77 @@
+// Internal launch interface between the host library (moe_api.cpp) and the
+// gfx950 kernels.  Not part of the public C ABI (include/moe.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;
+constexpr int kRouteSmallMaxRoutes = 4096;
+
+struct RouteOut {
+    int32_t* ids;
+    float* weights;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* route_pos;
+};
+
+// ---- routing (route.hip)
+size_t route_workspace_bytes(int T, int E, int k);
+hipError_t launch_route(const float* logits, int T, int E, int k, const RouteOut& o, void* ws,
+                        hipStream_t st);
+
+// ---- weight packing (pack.hip)
+hipError_t launch_pack_gate_up(const void* src, void* dst, int E, int H, int I, int elem_bytes,
+                               hipStream_t st);
+hipError_t launch_pack_down(const void* src, void* dst, int E, int H, int I, int elem_bytes,
+                            hipStream_t st);
+
+// ---- forward pieces
+enum Quant { Q_BF16 = 0, Q_FP8_TENSOR = 1, Q_FP8_BLOCK = 2 };
+
+struct FwdPlan {
+    // problem
+    int T, H, I, E, k, R;
+    int quant;
+    // inputs
+    const uint16_t* x;          // bf16 [T, H]
+    const int32_t* ids;         // [T, k]
+    const float* tw;            // [T, k]
+    const int32_t* offsets;     // [E + 1]
+    const int32_t* perm;        // [R]
+    const void* wgu;            // packed [E][2I][H]
+    const void* wd;             // packed [E][H][I]
+    const float* s_gu;          // per-tensor [E] | block [E][H/128][2I/128]
+    const float* s_d;           // per-tensor [E] | block [E][I/128][H/128]
+    uint16_t* out;              // bf16 [T, H]
+    // workspace carve-up (null where unused)
+    int32_t* tiles;             // [max_tiles] (expert << 16 | tile-in-expert) pairs as int2
+    int32_t* ntiles;            // [1]
+    uint32_t* amax;             // [2]: x amax bits, h amax bits (per-tensor)
+    float* scal;                // [2]: s_x, s_h (per-tensor)
+    uint8_t* xq;                // e4m3 [T, H]
+    float* sx;                  // block: [T, H/128]
+    void* h;                    // bf16 [R, I] (bf16) | fp32 [R, I] (fp8 paths, before requant)
+    uint8_t* hq;                // e4m3 [R, I]
+    float* sh;                  // block: [R, I/128]
+    uint16_t* y;                // bf16 [R, H] (grouped path, route order)
+    int max_tiles;
+};
+
+constexpr int kGemmBM = 128;
+
+int grouped_max_tiles(int R, int E);
+hipError_t launch_forward_init(const FwdPlan& p, bool build_tiles, hipStream_t st);
+hipError_t launch_quant_x(const FwdPlan& p, hipStream_t st);
+hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st);
+hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st);
+hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st);
+hipError_t launch_combine(const FwdPlan& p, hipStream_t st);
+hipError_t launch_route_direct_gate_up(const FwdPlan& p, hipStream_t st);
+hipError_t launch_route_direct_down(const FwdPlan& p, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,294 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace sizing and carving, the route-direct / grouped dispatch rule, and
+// the launch sequence of each path.  No allocation, no synchronisation, no
+// device-to-host copy.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+// Dispatch: the route-direct path wins while the batch is so small that most
+// experts receive no route ("perf: add small-batch route MMA for MoE", Motivation
+// and Dispatch: production range batch 1-4 at top-k 8).  The rule here keeps
+// that range, expressed in routes: T <= 4 and T*k <= E/2.
+constexpr int kRouteDirectMaxTokens = 4;
+
+bool rd_shape_ok(int H, int I, int quant) {
+    const int elem = quant == MOE_BF16 ? 2 : 1;
+    return (long)H * elem <= 8192 && (long)I * elem <= 2048;
+}
+
+int check_shape(int T, int H, int I, int E, int k, int quant) {
+    if (T < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "T=%d H=%d I=%d: sizes must be positive (T >= 0)", T, H, I);
+    if (k < 1 || E < k || E > moe::kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "need 1 <= k <= E <= %d (k=%d, E=%d)", moe::kMaxExperts, k, E);
+    if (quant < MOE_BF16 || quant > MOE_FP8_BLOCK128) return fail(MOE_ERR_INVALID_ARG, "unknown quant %d", quant);
+    if ((long)T * k >= (1L << 31) || (long)T * H >= (1L << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "T*k and T*H must fit in int32");
+    if (H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "H=%d: H must be a multiple of 128", H);
+    if (I % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "I=%d: I must be a multiple of 64", I);
+    if (quant == MOE_FP8_BLOCK128 && I % 128 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "I=%d: block128 needs I a multiple of 128", I);
+    if ((long)E * H * 2 * I >= (1L << 40)) return fail(MOE_ERR_UNSUPPORTED, "weights too large");
+    return MOE_OK;
+}
+
+int resolve_path(int T, int H, int I, int E, int k, int quant, int path) {
+    if (path == MOE_PATH_AUTO) {
+        const bool small = T <= kRouteDirectMaxTokens && 2L * T * k <= E;
+        return (small && rd_shape_ok(H, I, quant)) ? MOE_PATH_ROUTE_DIRECT : MOE_PATH_GROUPED;
+    }
+    if (path == MOE_PATH_GROUPED) return path;
+    if (path == MOE_PATH_ROUTE_DIRECT) {
+        if (!rd_shape_ok(H, I, quant))
+            return fail(MOE_ERR_UNSUPPORTED, "route-direct path: H*elem <= 8192 and I*elem <= 2048 bytes");
+        return path;
+    }
+    return fail(MOE_ERR_INVALID_ARG, "unknown path %d", path);
+}
+
+struct Layout {
+    size_t tiles, ntiles, amax, scal, xq, sx, h, hq, sh, y, total;
+};
+
+Layout layout(int T, int H, int I, int E, int k, int quant, int path) {
+    Layout L{};
+    const size_t R = (size_t)T * k;
+    const bool grouped = path == MOE_PATH_GROUPED;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align256(bytes);
+        return bytes ? at : (size_t)-1;
+    };
+    L.tiles = take(grouped ? sizeof(int32_t) * 2 * (size_t)moe::grouped_max_tiles((int)R, E) : 0);
+    L.ntiles = take(grouped ? sizeof(int32_t) : 0);
+    L.amax = take(2 * sizeof(uint32_t));
+    L.scal = take(2 * sizeof(float));
+    L.xq = take(quant != MOE_BF16 ? (size_t)T * H : 0);
+    L.sx = take(quant == MOE_FP8_BLOCK128 ? sizeof(float) * (size_t)T * (H / 128) : 0);
+    size_t hbytes = 0;
+    if (quant == MOE_BF16) hbytes = R * I * 2;
+    else if (quant == MOE_FP8_PER_TENSOR || !grouped) hbytes = R * I * 4;
+    L.h = take(hbytes);
+    L.hq = take(quant != MOE_BF16 ? R * I : 0);
+    L.sh = take(quant == MOE_FP8_BLOCK128 ? sizeof(float) * R * (I / 128) : 0);
+    L.y = take(grouped ? R * H * 2 : 0);
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return off == (size_t)-1 ? nullptr : reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return MOE_OK;
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_route_workspace_size(int T, int E, int k) {
+    if (T < 0 || k < 1 || E < k || E > moe::kMaxExperts) return 0;
+    return moe::route_workspace_bytes(T, E, k);
+}
+
+int moe_route(const float* logits, int T, int E, int k, moe_routes* out, void* ws, size_t ws_bytes,
+              void* stream) {
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    if (T < 0 || k < 1 || E < k || E > moe::kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "need T >= 0 and 1 <= k <= E <= %d (T=%d k=%d E=%d)",
+                    moe::kMaxExperts, T, k, E);
+    if ((long)T * k >= (1L << 31) || (long)T * E >= (1L << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "T*k and T*E must fit in int32");
+    if (!out->expert_counts || !out->expert_offsets || (T > 0 && (!logits || !out->topk_ids ||
+        !out->topk_weights || !out->perm || !out->route_pos)))
+        return fail(MOE_ERR_INVALID_ARG, "null pointer among logits / routes members");
+    const void* ptrs[] = {logits, out->topk_ids, out->topk_weights, out->expert_counts,
+                          out->expert_offsets, out->perm, out->route_pos};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    const size_t need = moe::route_workspace_bytes(T, E, k);
+    if (ws_bytes < need || (need && !ws))
+        return fail(MOE_ERR_WORKSPACE, "route workspace: need %zu bytes, got %zu", need, ws_bytes);
+    out->T = T;
+    out->E = E;
+    out->k = k;
+    const moe::RouteOut o{out->topk_ids, out->topk_weights, out->expert_counts, out->expert_offsets,
+                          out->perm, out->route_pos};
+    const int rc = hip_status(moe::launch_route(logits, T, E, k, o, ws, static_cast<hipStream_t>(stream)),
+                              "moe_route launch");
+    return rc == MOE_OK ? ok() : rc;
+}
+
+int moe_pack_weights(const void* w_gate_up, const void* w_down, int E, int H, int I, int quant,
+                     void* packed_gate_up, void* packed_down, void* stream) {
+    if (E < 1 || E > moe::kMaxExperts || H <= 0 || I <= 0)
+        return fail(MOE_ERR_INVALID_ARG, "bad sizes E=%d H=%d I=%d", E, H, I);
+    if (quant < MOE_BF16 || quant > MOE_FP8_BLOCK128) return fail(MOE_ERR_INVALID_ARG, "unknown quant %d", quant);
+    if (I % 16 != 0) return fail(MOE_ERR_UNSUPPORTED, "I must be a multiple of 16");
+    if (!w_gate_up || !w_down || !packed_gate_up || !packed_down)
+        return fail(MOE_ERR_INVALID_ARG, "null weight pointer");
+    if (w_gate_up == packed_gate_up || w_down == packed_down)
+        return fail(MOE_ERR_INVALID_ARG, "packing cannot run in place");
+    const int elem = quant == MOE_BF16 ? 2 : 1;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = hip_status(moe::launch_pack_gate_up(w_gate_up, packed_gate_up, E, H, I, elem, st), "pack gate_up");
+    if (rc != MOE_OK) return rc;
+    rc = hip_status(moe::launch_pack_down(w_down, packed_down, E, H, I, elem, st), "pack down");
+    return rc == MOE_OK ? ok() : rc;
+}
+
+int moe_select_path(int T, int H, int I, int E, int k, int quant, int path) {
+    const int rc = check_shape(T, H, I, E, k, quant);
+    if (rc != MOE_OK) return rc;
+    return resolve_path(T, H, I, E, k, quant, path);
+}
+
+size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int quant, int path) {
+    if (check_shape(T, H, I, E, k, quant) != MOE_OK) return 0;
+    const int p = resolve_path(T, H, I, E, k, quant, path);
+    if (p < 0) return 0;
+    return layout(T, H, I, E, k, quant, p).total;
+}
+
+static int forward_impl(const void* x, const moe_routes* routes, const void* packed_gate_up,
+                        const void* packed_down, const moe_scales* scales, void* out, int H, int I,
+                        int quant, int path, void* ws, size_t ws_bytes, void* stream,
+                        void** events, int n_events, int* n_stages, const char** stage_names) {
+    if (!routes) return fail(MOE_ERR_INVALID_ARG, "routes is NULL");
+    const int T = routes->T, E = routes->E, k = routes->k;
+    int rc = check_shape(T, H, I, E, k, quant);
+    if (rc != MOE_OK) return rc;
+    const int p = resolve_path(T, H, I, E, k, quant, path);
+    if (p < 0) return p;
+    if (T == 0) {
+        if (n_stages) *n_stages = 0;
+        if (stage_names) *stage_names = "";
+        return ok();
+    }
+    if (!x || !out || !packed_gate_up || !packed_down || !routes->topk_ids || !routes->topk_weights)
+        return fail(MOE_ERR_INVALID_ARG, "null pointer among x / out / weights / routes");
+    if (p == MOE_PATH_GROUPED && (!routes->expert_offsets || !routes->perm))
+        return fail(MOE_ERR_INVALID_ARG, "grouped path needs routes->expert_offsets and routes->perm");
+    if (quant != MOE_BF16 && (!scales || !scales->w_gate_up_scale || !scales->w_down_scale))
+        return fail(MOE_ERR_INVALID_ARG, "FP8 quantisation needs both weight scale arrays");
+    const void* ptrs[] = {x, out, packed_gate_up, packed_down, routes->topk_ids, routes->topk_weights,
+                          routes->expert_offsets, routes->perm, ws};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    const Layout L = layout(T, H, I, E, k, quant, p);
+    if (ws_bytes < L.total || !ws)
+        return fail(MOE_ERR_WORKSPACE, "forward workspace: need %zu bytes, got %zu", L.total, ws_bytes);
+
+    moe::FwdPlan P{};
+    P.T = T; P.H = H; P.I = I; P.E = E; P.k = k; P.R = T * k; P.quant = quant;
+    P.x = static_cast<const uint16_t*>(x);
+    P.ids = routes->topk_ids;
+    P.tw = routes->topk_weights;
+    P.offsets = routes->expert_offsets;
+    P.perm = routes->perm;
+    P.wgu = packed_gate_up;
+    P.wd = packed_down;
+    P.s_gu = quant != MOE_BF16 ? scales->w_gate_up_scale : nullptr;
+    P.s_d = quant != MOE_BF16 ? scales->w_down_scale : nullptr;
+    P.out = static_cast<uint16_t*>(out);
+    P.tiles = at<int32_t>(ws, L.tiles);
+    P.ntiles = at<int32_t>(ws, L.ntiles);
+    P.amax = at<uint32_t>(ws, L.amax);
+    P.scal = at<float>(ws, L.scal);
+    P.xq = at<uint8_t>(ws, L.xq);
+    P.sx = at<float>(ws, L.sx);
+    P.h = at<void>(ws, L.h);
+    P.hq = at<uint8_t>(ws, L.hq);
+    P.sh = at<float>(ws, L.sh);
+    P.y = at<uint16_t>(ws, L.y);
+    P.max_tiles = moe::grouped_max_tiles(P.R, E);
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool grouped = p == MOE_PATH_GROUPED;
+    int stage = 0;
+    static thread_local char names[256];
+    names[0] = '\0';
+    auto mark = [&](const char* name) {
+        if (events && stage < n_events) (void)hipEventRecord(static_cast<hipEvent_t>(events[stage]), st);
+        if (name) {
+            if (names[0]) strncat(names, ",", sizeof names - strlen(names) - 1);
+            strncat(names, name, sizeof names - strlen(names) - 1);
+        }
+        ++stage;
+    };
+    mark(nullptr);
+#define MOE_STEP(call, what)                                            \
+    do {                                                                \
+        if ((rc = hip_status((call), what)) != MOE_OK) return rc;       \
+        mark(what);                                                     \
+    } while (0)
+    if (grouped || quant == MOE_FP8_PER_TENSOR) MOE_STEP(moe::launch_forward_init(P, grouped, st), "init");
+    if (quant != MOE_BF16) MOE_STEP(moe::launch_quant_x(P, st), "quant_x");
+    if (grouped) {
+        MOE_STEP(moe::launch_grouped_gate_up(P, st), "gate_up");
+        if (quant == MOE_FP8_PER_TENSOR) MOE_STEP(moe::launch_quant_h(P, st), "quant_h");
+        MOE_STEP(moe::launch_grouped_down(P, st), "down");
+        MOE_STEP(moe::launch_combine(P, st), "combine");
+    } else {
+        MOE_STEP(moe::launch_route_direct_gate_up(P, st), "rd_gate_up");
+        if (quant != MOE_BF16) MOE_STEP(moe::launch_quant_h(P, st), "quant_h");
+        MOE_STEP(moe::launch_route_direct_down(P, st), "rd_down_combine");
+    }
+#undef MOE_STEP
+    if (n_stages) *n_stages = stage - 1;
+    if (stage_names) *stage_names = names;
+    return ok();
+}
+
+int moe_forward(const void* x, const moe_routes* routes, const void* packed_gate_up,
+                const void* packed_down, const moe_scales* scales, void* out, int H, int I,
+                int quant, int path, void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, ws,
+                        ws_bytes, stream, nullptr, 0, nullptr, nullptr);
+}
+
+int moe_forward_profiled(const void* x, const moe_routes* routes, const void* packed_gate_up,
+                         const void* packed_down, const moe_scales* scales, void* out, int H, int I,
+                         int quant, int path, void* ws, size_t ws_bytes, void* stream,
+                         void** stage_events, int n_events, int* n_stages, const char** stage_names) {
+    if (n_events < 0 || (n_events > 0 && !stage_events))
+        return fail(MOE_ERR_INVALID_ARG, "stage_events must hold n_events handles");
+    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, ws,
+                        ws_bytes, stream, stage_events, n_events, n_stages, stage_names);
+}
+
+}  // extern "C"

@@ -1,0 +1,316 @@
+// Routing for the MoE forward on gfx950: top-k with renormalised softmax gates,
+// then the grouped form of the routes -- per-expert counts, their exclusive
+// prefix, and a stable permutation of the route ids r = t*k + j by expert
+// ("Port necessary FBGEMM MoE kernels", Summary: index_shuffling;
+//  "perf: add small-batch route MMA for MoE", Motivation: count/sort, prefix).
+//
+// Design:
+//  * one wavefront per token; each lane keeps ceil(E/64) logits in registers
+//    and the k picks are k wave-wide (value, id) arg-max reductions, ties to
+//    the lower id (values are compared as floats, so -0 == +0);
+//  * counting sort without global atomics: workgroup histograms in LDS, a
+//    column scan over workgroups, then a stable scatter in which each wave
+//    ranks its routes with a ballot-based match (one ballot per key bit);
+//  * a single-workgroup fused kernel serves small T*k (decode) in one launch.
+#include "common.cuh"
+#include "launch.h"
+
+namespace moe {
+
+// Picks the k largest logits of one token (row) with one wave.  Lane 0 writes
+// ids[0..k) and the gates w[0..k).  Gates: exp(l_j - m) / sum_i exp(l_i - m)
+// over the picks, m = the largest logit (the full softmax denominator cancels
+// in the renormalisation).
+template <int VPL>
+__device__ void topk_one_token(const float* __restrict__ row, int E, int k,
+                               int32_t* __restrict__ ids, float* __restrict__ w,
+                               int32_t* __restrict__ ids_lds, int32_t* __restrict__ cnt_lds) {
+    const int lane = lane_id();
+    float v[VPL];
+    uint32_t avail = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+        v[i] = 0.0f;
+        if (e < E) {
+            v[i] = row[e] + 0.0f;   // -0 -> +0 (comparisons treat them equal anyway)
+            avail |= 1u << i;
+        }
+    }
+    float m = 0.0f, S = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        float bv = 0.0f;
+        int bi = -1;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            if ((avail >> i) & 1u) {
+                if (bi < 0 || v[i] > bv) { bv = v[i]; bi = lane + kWave * i; }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
+            const bool take = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
+            if (take) { bv = ov; bi = oi; }
+        }
+        if ((bi & (kWave - 1)) == lane) avail &= ~(1u << (bi / kWave));
+        if (j == 0) m = bv;
+        const float ej = expf(bv - m);
+        S += ej;                    // same order in every lane
+        if (lane == 0) {
+            ids[j] = bi;
+            w[j] = ej;
+            if (ids_lds) ids_lds[j] = bi;
+            if (cnt_lds) atomicAdd(&cnt_lds[bi], 1);
+        }
+    }
+    if (lane == 0) {
+        for (int j = 0; j < k; ++j) w[j] = w[j] / S;   // lane 0 re-reads its own stores
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Small T*k: everything in one workgroup of 16 waves.
+constexpr int kSmallWaves = 16;
+
+template <int VPL>
+__global__ void __launch_bounds__(kSmallWaves * kWave)
+route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int nbits,
+                   int32_t* __restrict__ ids, float* __restrict__ weights,
+                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                   int32_t* __restrict__ perm, int32_t* __restrict__ route_pos) {
+    extern __shared__ int32_t lds[];
+    const int R = T * k;
+    int32_t* sid = lds;                          // [R]
+    int32_t* wcnt = sid + R;                     // [16][E]
+    int32_t* base = wcnt + kSmallWaves * E;      // [E + 1]
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+
+    for (int i = tid; i < kSmallWaves * E; i += blockDim.x) wcnt[i] = 0;
+    for (int t = wave; t < T; t += kSmallWaves)
+        topk_one_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
+                            weights + (size_t)t * k, sid + t * k, nullptr);
+    __syncthreads();
+
+    const int per = ceil_div(R, kSmallWaves);
+    const int lo = min(R, wave * per), hi = min(R, lo + per);
+    for (int r = lo + lane; r < hi; r += kWave) atomicAdd(&wcnt[wave * E + sid[r]], 1);
+    __syncthreads();
+
+    // per expert: exclusive prefix over the waves' ranges (route order)
+    for (int e = tid; e < E; e += blockDim.x) {
+        int run = 0;
+        for (int w = 0; w < kSmallWaves; ++w) {
+            const int c = wcnt[w * E + e];
+            wcnt[w * E + e] = run;
+            run += c;
+        }
+        base[e] = run;                           // count, scanned below
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // exclusive scan of the E counts, 8 per lane (E <= 512)
+        int c[8], s = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = lane * 8 + i;
+            c[i] = e < E ? base[e] : 0;
+            s += c[i];
+        }
+        int incl = s;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        int run = incl - s;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = lane * 8 + i;
+            if (e < E) {
+                counts[e] = c[i];
+                offsets[e] = run;
+                base[e] = run;
+            }
+            run += c[i];
+        }
+        if (lane == kWave - 1) { offsets[E] = run; base[E] = run; }
+    }
+    __syncthreads();
+
+    // stable scatter: each wave walks its own range in order
+    for (int s0 = lo; s0 < hi; s0 += kWave) {
+        const int r = s0 + lane;
+        if (r < hi) {
+            const int key = sid[r];
+            const uint64_t peers = match_any(key, nbits);
+            const int rank = __popcll(peers & lanemask_lt());
+            const int p = base[key] + wcnt[wave * E + key] + rank;
+            perm[p] = r;
+            route_pos[r] = p;
+            if (lane == 63 - __clzll(peers)) wcnt[wave * E + key] += __popcll(peers);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Large T*k: three kernels, 64 tokens per workgroup of 4 waves.
+constexpr int kTokPerBlock = 64;
+constexpr int kBigWaves = 4;
+
+template <int VPL>
+__global__ void __launch_bounds__(kBigWaves * kWave)
+route_topk_hist_kernel(const float* __restrict__ logits, int T, int E, int k,
+                       int32_t* __restrict__ ids, float* __restrict__ weights,
+                       int32_t* __restrict__ block_hist) {
+    __shared__ int32_t cnt[kMaxExperts];
+    const int tid = threadIdx.x, wave = tid / kWave;
+    const int t0 = blockIdx.x * kTokPerBlock, t1 = min(T, t0 + kTokPerBlock);
+    for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    for (int t = t0 + wave; t < t1; t += kBigWaves)
+        topk_one_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
+                            weights + (size_t)t * k, nullptr, cnt);
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) block_hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Column scan over workgroups (per expert) and the exclusive prefix over experts.
+__global__ void __launch_bounds__(kMaxExperts)
+route_scan_kernel(int nblk, int E, int R, int32_t* __restrict__ block_hist,
+                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+    __shared__ int32_t wsum[kMaxExperts / kWave];
+    const int e = threadIdx.x, lane = lane_id(), wave = e / kWave;
+    int run = 0;
+    if (e < E) {
+        int b = 0;
+        for (; b + 4 <= nblk; b += 4) {
+            const int c0 = block_hist[(size_t)(b + 0) * E + e];
+            const int c1 = block_hist[(size_t)(b + 1) * E + e];
+            const int c2 = block_hist[(size_t)(b + 2) * E + e];
+            const int c3 = block_hist[(size_t)(b + 3) * E + e];
+            block_hist[(size_t)(b + 0) * E + e] = run;
+            block_hist[(size_t)(b + 1) * E + e] = run + c0;
+            block_hist[(size_t)(b + 2) * E + e] = run + c0 + c1;
+            block_hist[(size_t)(b + 3) * E + e] = run + c0 + c1 + c2;
+            run += c0 + c1 + c2 + c3;
+        }
+        for (; b < nblk; ++b) {
+            const int c = block_hist[(size_t)b * E + e];
+            block_hist[(size_t)b * E + e] = run;
+            run += c;
+        }
+        counts[e] = run;
+    }
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    if (e < E) offsets[e] = before + incl - run;
+    if (e == 0) offsets[E] = R;
+}
+
+__global__ void __launch_bounds__(kBigWaves * kWave)
+route_scatter_kernel(int T, int E, int k, int nbits, const int32_t* __restrict__ ids,
+                     const int32_t* __restrict__ block_hist, const int32_t* __restrict__ offsets,
+                     int32_t* __restrict__ perm, int32_t* __restrict__ route_pos) {
+    __shared__ int32_t wcnt[kBigWaves * kMaxExperts];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    const int r0 = blockIdx.x * kTokPerBlock * k;
+    const int r1 = min(T, (blockIdx.x + 1) * kTokPerBlock) * k;
+    const int per = ceil_div(r1 - r0, kBigWaves);
+    const int lo = min(r1, r0 + wave * per), hi = min(r1, lo + per);
+    for (int i = tid; i < kBigWaves * E; i += blockDim.x) wcnt[i] = 0;
+    __syncthreads();
+    for (int r = lo + lane; r < hi; r += kWave) atomicAdd(&wcnt[wave * E + ids[r]], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) {
+        int run = offsets[e] + block_hist[(size_t)blockIdx.x * E + e];
+        for (int w = 0; w < kBigWaves; ++w) {
+            const int c = wcnt[w * E + e];
+            wcnt[w * E + e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    for (int s0 = lo; s0 < hi; s0 += kWave) {
+        const int r = s0 + lane;
+        if (r < hi) {
+            const int key = ids[r];
+            const uint64_t peers = match_any(key, nbits);
+            const int rank = __popcll(peers & lanemask_lt());
+            const int p = wcnt[wave * E + key] + rank;
+            perm[p] = r;
+            route_pos[r] = p;
+            if (lane == 63 - __clzll(peers)) wcnt[wave * E + key] += __popcll(peers);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+
+static int bits_for(int E) {
+    int b = 0;
+    while ((1 << b) < E) ++b;
+    return b;
+}
+
+size_t route_small_lds_bytes(int T, int E, int k) {
+    return sizeof(int32_t) * ((size_t)T * k + (size_t)kSmallWaves * E + E + 1);
+}
+
+bool route_use_small(int T, int E, int k) {
+    return (size_t)T * k <= kRouteSmallMaxRoutes && route_small_lds_bytes(T, E, k) <= 64 * 1024;
+}
+
+size_t route_workspace_bytes(int T, int E, int k) {
+    if (T == 0 || route_use_small(T, E, k)) return 0;
+    return sizeof(int32_t) * (size_t)ceil_div(T, kTokPerBlock) * E;
+}
+
+#define MOE_VPL_DISPATCH(E, KERNEL, ...)                                   \
+    ((E) <= 64 ? (KERNEL<1>)(__VA_ARGS__)                                  \
+     : (E) <= 128 ? (KERNEL<2>)(__VA_ARGS__)                               \
+     : (E) <= 256 ? (KERNEL<4>)(__VA_ARGS__) : (KERNEL<8>)(__VA_ARGS__))
+
+template <int VPL>
+static hipError_t launch_small(const float* logits, int T, int E, int k, const RouteOut& o,
+                               hipStream_t st) {
+    const size_t lds = route_small_lds_bytes(T, E, k);
+    hipLaunchKernelGGL(route_small_kernel<VPL>, dim3(1), dim3(kSmallWaves * kWave), lds, st,
+                       logits, T, E, k, bits_for(E), o.ids, o.weights, o.counts, o.offsets,
+                       o.perm, o.route_pos);
+    return hipGetLastError();
+}
+
+template <int VPL>
+static hipError_t launch_topk_hist(const float* logits, int T, int E, int k, const RouteOut& o,
+                                   int32_t* hist, hipStream_t st) {
+    hipLaunchKernelGGL(route_topk_hist_kernel<VPL>, dim3(ceil_div(T, kTokPerBlock)),
+                       dim3(kBigWaves * kWave), 0, st, logits, T, E, k, o.ids, o.weights, hist);
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, const RouteOut& o,
+                        void* ws, hipStream_t st) {
+    if (route_use_small(T, E, k)) return MOE_VPL_DISPATCH(E, launch_small, logits, T, E, k, o, st);
+    const int nblk = ceil_div(T, kTokPerBlock);
+    int32_t* hist = static_cast<int32_t*>(ws);
+    hipError_t err = MOE_VPL_DISPATCH(E, launch_topk_hist, logits, T, E, k, o, hist, st);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kMaxExperts), 0, st, nblk, E, T * k, hist,
+                       o.counts, o.offsets);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(kBigWaves * kWave), 0, st, T, E, k,
+                       bits_for(E), o.ids, hist, o.offsets, o.perm, o.route_pos);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,197 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Routing (ids, counts, offsets, perm, route_pos) must match bit for bit and the
+gates to 1e-6; outputs within max-abs 2e-2 and rel-L2 1e-2 (bf16) or rel-L2
+2e-2 and cosine >= 0.999 (fp8), compared with the fp64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (DEV, WORKLOADS, bf16_dev, check_out, check_routing, moe, oracle, oracle_out,
+                         random_activations, random_weights, routes_np, run, say, weights_dev,
+                         workload_dev, workload_inputs, workload_weights)
+from workloads import tie_heavy_logits
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ routing --
+ROUTE_CASES = [
+    # (T, E, k, kind)  -- small fused kernel and the three-kernel path, ragged sizes
+    (64, 16, 8, "normal"), (1, 128, 8, "normal"), (4, 128, 8, "normal"), (8, 192, 8, "normal"),
+    (8192, 128, 8, "zipf"), (4096, 128, 8, "normal"), (513, 64, 2, "normal"), (1000, 512, 20, "normal"),
+    (3, 512, 512, "normal"), (5000, 7, 7, "normal"), (2000, 64, 8, "ties"), (300, 16, 8, "ties"),
+    (0, 16, 4, "normal"), (1, 1, 1, "normal"), (777, 1, 1, "normal"), (65, 3, 2, "ties"),
+]
+
+
+@pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
+def test_route_parity(T, E, k, kind):
+    say(f"route T={T} E={E} k={k} {kind}")
+    if kind == "ties":
+        lg = tie_heavy_logits(T, E, seed=T + E)
+    else:
+        lg = random_activations(T, 8, E, seed=1000 + T + E, logits="zipf" if kind == "zipf" else "normal")["logits"]
+    r = moe.route(torch.from_numpy(lg).to(DEV), k)
+    torch.cuda.synchronize()
+    check_routing(routes_np(r), oracle.route(lg, k))
+
+
+def test_route_equal_logits_all_experts():
+    T, E = 50, 32
+    lg = np.zeros((T, E), np.float32)
+    r = routes_np(moe.route(torch.from_numpy(lg).to(DEV), E))
+    assert np.array_equal(r["topk_ids"], np.tile(np.arange(E, dtype=np.int32), (T, 1)))
+    assert np.all(r["topk_weights"] == np.float32(1.0 / E))
+    check_routing(r, oracle.route(lg, E))
+
+
+# -------------------------------------------------------------- forward ------
+def _compare(name, x, lg, k, dev_w, host_w, quant, path, tokens=None):
+    r, out = run(x, lg, k, dev_w, quant, path)
+    ref_r = oracle.route(lg, k)
+    check_routing(routes_np(r), ref_r)
+    ref = oracle_out(x, ref_r, host_w, quant, tokens)
+    got = out.float().cpu().numpy()
+    if tokens is not None:
+        got = got[tokens]
+    return check_out(got, ref, "bf16" if quant == "bf16" else "fp8", f"{name} {path}")
+
+
+@pytest.mark.parametrize("path", ["auto", "grouped", "route_direct"])
+def test_tiny_bf16(path):
+    name = "tiny_bf16"
+    a = workload_inputs(name)
+    _compare(name, a["x"], a["logits"], WORKLOADS[name].k, workload_dev(name), workload_weights(name),
+             "bf16", path)
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
+@pytest.mark.parametrize("path", ["auto", "grouped"])
+def test_decode_bf16(B, path):
+    name = "decode_bf16"
+    a = workload_inputs(name, batch=B)
+    _compare(f"{name} B={B}", a["x"], a["logits"], 8, workload_dev(name), workload_weights(name), "bf16", path)
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("path", ["auto", "grouped", "route_direct"])
+def test_decode_fp8_per_tensor(B, path):
+    name = "decode_fp8_tensor"
+    a = workload_inputs(name, batch=B)
+    _compare(f"{name} B={B}", a["x"], a["logits"], 8, workload_dev(name), workload_weights(name),
+             "fp8_per_tensor", path)
+
+
+def _sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    t = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, n, replace=False)]))
+    return t.astype(np.int32)
+
+
+def test_prefill_bf16_sampled():
+    name = "prefill_bf16"
+    a = workload_inputs(name)
+    tok = _sample_tokens(WORKLOADS[name].T, 61, 7)
+    _compare(name, a["x"], a["logits"], 8, workload_dev(name), workload_weights(name), "bf16", "auto", tok)
+
+
+def test_prefill_fp8_block_sampled():
+    name = "prefill_fp8_block"
+    a = workload_inputs(name)
+    tok = _sample_tokens(WORKLOADS[name].T, 61, 8)
+    _compare(name, a["x"], a["logits"], 8, workload_dev(name), workload_weights(name), "fp8_block128",
+             "auto", tok)
+
+
+# -------------------------------------------------------------- edge cases --
+EDGE = [
+    # (T, H, I, E, k, quant, logits, tag)
+    (37, 256, 128, 8, 2, "bf16", "normal", "ragged tiles"),
+    (300, 256, 128, 4, 1, "bf16", "normal", "multi-tile experts"),
+    (5, 256, 64, 1, 1, "bf16", "normal", "E=1"),
+    (9, 128, 64, 6, 6, "bf16", "normal", "k=E"),
+    (1, 256, 128, 64, 8, "bf16", "normal", "T=1 most experts empty"),
+    (200, 256, 128, 16, 4, "bf16", "hot", "all routes to few experts"),
+    (20, 256, 192, 12, 3, "fp8_per_tensor", "normal", "per-tensor I%128!=0"),
+    (150, 384, 256, 8, 2, "fp8_per_tensor", "normal", "per-tensor multi-tile"),
+    (70, 256, 256, 6, 2, "fp8_block128", "normal", "block128 ragged"),
+    (3, 512, 128, 32, 4, "fp8_block128", "normal", "block128 decode"),
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,quant,kind,tag", EDGE)
+@pytest.mark.parametrize("path", ["grouped", "route_direct"])
+def test_edge_cases(T, H, I, E, k, quant, kind, tag, path):
+    say(f"edge {tag}: T={T} H={H} I={I} E={E} k={k} {quant} {path}")
+    a = random_activations(T, H, E, seed=T * 7 + E)
+    lg = a["logits"]
+    if kind == "hot":
+        lg = lg.copy()
+        lg[:, :k] += 50.0       # every token picks experts 0..k-1
+    w = random_weights(E, H, I, quant, seed=E * 13 + I)
+    _compare(tag, a["x"], lg, k, weights_dev(w, quant), w, quant, path)
+
+
+def test_empty_batch():
+    w = random_weights(4, 128, 64, "bf16", seed=3)
+    pgu, pd, _ = weights_dev(w, "bf16")
+    r = moe.route(torch.zeros((0, 4), dtype=torch.float32, device=DEV), 2)
+    out = moe.forward(torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV), r, pgu, pd)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 128)
+    assert r.expert_counts.cpu().tolist() == [0] * 4
+    assert r.expert_offsets.cpu().tolist() == [0] * 5
+
+
+# ------------------------------------------------------------- determinism --
+@pytest.mark.parametrize("name,path", [("prefill_bf16", "auto"), ("decode_fp8_tensor", "auto"),
+                                       ("decode_bf16", "grouped"), ("prefill_fp8_block", "auto")])
+def test_two_runs_bitwise_equal(name, path):
+    wl = WORKLOADS[name]
+    a = workload_inputs(name, batch=4 if wl.batches else None)
+    _, o1 = run(a["x"], a["logits"], wl.k, workload_dev(name), wl.quant, path)
+    _, o2 = run(a["x"], a["logits"], wl.k, workload_dev(name), wl.quant, path)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "decode_fp8_tensor", "tiny_bf16"])
+def test_graph_replay_bitwise_equal(name):
+    wl = WORKLOADS[name]
+    a = workload_inputs(name, batch=4 if wl.batches else None)
+    pgu, pd, scales = workload_dev(name)
+    lg = torch.from_numpy(a["logits"]).to(DEV)
+    x = bf16_dev(a["x"])
+    T = x.shape[0]
+    routes = moe.Routes(T, wl.E, wl.k, DEV)
+    out = torch.empty((T, wl.H), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(256, moe.forward_workspace_size(T, wl.H, wl.I, wl.E, wl.k, wl.quant)),
+                     dtype=torch.uint8, device=DEV)
+    rws_n = moe.route_workspace_size(T, wl.E, wl.k)
+    rws = torch.empty(max(rws_n, 256), dtype=torch.uint8, device=DEV) if rws_n else None
+
+    def step():
+        moe.route(lg, wl.k, out=routes, workspace=rws)
+        moe.forward(x, routes, pgu, pd, quant=wl.quant, scales=scales, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        step()      # eager work between replays
+        torch.cuda.synchronize()
