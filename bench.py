@@ -199,6 +199,27 @@ def cpu_baseline(a, w, wl, budget_s=15.0):
                        f"of {wl.name} (fp64 C oracle, OpenMP), {dt:.1f} s")
 
 
+def profile_only(torch, moe, args):
+    """Short runs of single workloads for rocprofv3 counter passes."""
+    for name in args.only.split(","):
+        if name == "copy":
+            src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(args.steps):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"copy: {args.steps} x 1 GiB device-to-device copies")
+        elif name.startswith("prefill"):
+            pf = bench_prefill(torch, moe, name, args.steps, args.warmup)
+            log(f"{name}: {pf['dt'] / args.steps * 1e3:.3f} ms/step, stages us "
+                f"{ {k: round(v * 1e3, 1) for k, v in pf['stages_ms'].items()} }")
+            del pf
+        else:
+            res = bench_decode(torch, moe, name, (1, 2, 3, 4), args.decode_iters)
+            log(f"{name}: { {b: r['us_per_layer'] for b, r in res.items()} }")
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +228,10 @@ def main():
     ap.add_argument("--decode-iters", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline line only (no fp8 extras)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="profiling runs: comma list of prefill_bf16, prefill_fp8_block, decode_bf16, "
+                         "decode_fp8_tensor, copy (a plain 1 GiB device copy, the traffic-counter "
+                         "reference); prints per-stage times instead of the JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -217,6 +242,8 @@ def main():
     import torch
     import routing_grouped_expert_index_amd as moe
     torch.cuda.set_device(0)
+    if args.only:
+        return profile_only(torch, moe, args)
 
     log("prefill bf16 T=8192 ...")
     pf = bench_prefill(torch, moe, "prefill_bf16", args.steps, args.warmup)

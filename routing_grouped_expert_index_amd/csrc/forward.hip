@@ -127,8 +127,14 @@ amax_kernel(const TIn* __restrict__ in, long n, uint32_t* __restrict__ amax_bits
 #pragma unroll
         for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[j]));
     }
+    __shared__ float part[256 / kWave];
     a = wave_max(a);
-    if (lane_id() == 0) atomicMax(amax_bits, __float_as_uint(a));
+    if (lane_id() == 0) part[threadIdx.x / kWave] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < (int)(blockDim.x / kWave); ++w) a = fmaxf(a, part[w]);
+        atomicMax(amax_bits, __float_as_uint(a));   // one atomic per workgroup
+    }
 }
 
 template <typename TIn>
@@ -196,8 +202,8 @@ hipError_t launch_quant_x(const FwdPlan& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-// h (fp32 [R, I]) -> e4m3 codes.  Per-tensor uses the amax the Gate/Up kernels
-// folded into amax[1]; blockwise computes each row's 128-column groups here.
+// h (fp32 [R, I]) -> e4m3 codes: per-tensor with one scale over all routes,
+// blockwise per row per 128 columns.
 hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st) {
     const long n = (long)p.R * p.I;
     const float* h = static_cast<const float*>(p.h);
@@ -207,10 +213,23 @@ hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st) {
                            dim3(256), 0, st, h, p.R, p.I, p.hq, p.sh);
         return hipGetLastError();
     }
-    const unsigned grid = (unsigned)std::min<long>(2048, std::max<long>(1, (n / 8 + 255) / 256));
+    if (n <= kSmallQuant) {
+        hipLaunchKernelGGL(quant_tensor_small_kernel<float>, dim3(1), dim3(1024), 0, st, h, n, p.hq,
+                           &p.scal[1]);
+        return hipGetLastError();
+    }
+    const unsigned grid = (unsigned)std::min<long>(2048, (n / 8 + 255) / 256);
+    hipLaunchKernelGGL(amax_kernel<float>, dim3(grid), dim3(256), 0, st, h, n, &p.amax[1]);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(quant_tensor_kernel<float>, dim3(grid), dim3(256), 0, st, h, n, &p.amax[1],
                        p.hq, &p.scal[1]);
     return hipGetLastError();
+}
+
+bool forward_needs_amax(const FwdPlan& p) {
+    return p.quant == Q_FP8_TENSOR &&
+           ((long)p.T * p.H > kSmallQuant || (long)p.R * p.I > kSmallQuant);
 }
 
 // ------------------------------------------------------------------ combine --

@@ -27,6 +27,8 @@
 #include "common.cuh"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace moe {
 
 enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_F32 = 1, EPI_SWIGLU_Q128 = 2, EPI_Y_BF16 = 3 };
@@ -51,25 +53,47 @@ struct GemmArgs {
     void* C;                // output
     long ldc;               // output row stride in elements
     float* cscale;          // Q128: [R][I/128]
-    uint32_t* amax;         // F32: amax bits
     int max_tiles;
 };
 
-constexpr int kLdsRow = 144;   // 128 data bytes + 16 pad
+// LDS tile layout: a K step of a tile row is 128 bytes = 8 chunks of 16 bytes;
+// chunk c of row r lives at r*128 + ((c ^ (r & 7)) * 16).  The XOR spreads the
+// 16-byte MFMA operand reads of 8 consecutive rows over all 32 banks.
+constexpr int kRowB = 128;
+constexpr int kStages = 3;
+
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowB + ((c ^ (r & 7)) << 4); }
+
+// 16 zero bytes: the source of K-tail chunks past the end of a row.
+__device__ __attribute__((aligned(16))) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
+
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with vmcnt <= N and lgkmcnt == 0 (expcnt untouched)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
+}
 
 template <bool FP8, bool GATHER, int SC, int EPI, int BM, int BN, int WM, int WN>
 struct Gemm {
     static constexpr int NT = 64 * WM * WN;
+    static constexpr int NW = WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int MI = TM / 16, NI = TN / 16;
-    static constexpr int CA = BM * 8 / NT, CB = BN * 8 / NT;   // 16-byte chunks per thread
-    static constexpr int STAGE = (BM + BN) * kLdsRow + (SC == SC_BLOCK ? BM * 4 : 0);
-    static constexpr int LDS = 2 * STAGE;
-    static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/thread mismatch");
+    static constexpr int DA = BM / 8 / NW, DB = BN / 8 / NW;   // 1 KB DMA loads per wave per stage
+    static constexpr int DS = SC == SC_BLOCK ? 1 : 0;          // + one row-scale load
+    static constexpr int DMA = DA + DB + DS;
+    static constexpr int STAGE = (BM + BN) * kRowB + DS * NW * 256;
+    static constexpr int SWT = SC == SC_BLOCK ? 64 * (BN / 16) * 4 : 0;   // K up to 64 blocks
+    static constexpr int LDS = kStages * STAGE + SWT;
+    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile/wave mismatch");
     static_assert(MI >= 1 && NI >= 2 && NI % 2 == 0, "wave tile");
+    static_assert(NW * 64 >= BM, "row scales: one lane per tile row");
 };
 
-template <bool FP8, bool GATHER, int SC, int EPI, int BM, int BN, int WM, int WN>
+template <bool FP8, bool GATHER, int SC, int EPI, int BM, int BN, int WM, int WN, bool KTAIL>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_kernel(const GemmArgs g) {
     using G = Gemm<FP8, GATHER, SC, EPI, BM, BN, WM, WN>;
@@ -78,13 +102,20 @@ grouped_gemm_kernel(const GemmArgs g) {
     const int wm = wave / WN, wn = wave % WN;
     const int NTN = g.N / BN;
     const int total = g.ntiles[0] * NTN;
-    const int KT = (g.Kb + 127) / 128;   // a partial last step is zero-filled (per-tensor I % 128 != 0)
+    const int KT = (g.Kb + 127) / 128;   // a partial last step reads zeros past the row end
 
-    // XCD-aware contiguous ranges of the real tile space
+    // XCD-aware contiguous ranges of the real tile space: one range per XCD
+    // (fewer ranges when the grid has fewer than 8 workgroups, so that every
+    // range has at least one workgroup walking it)
     const int nwg = gridDim.x;
-    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-    const int per_xcd_wg = nwg / 8 + (xcd < nwg % 8 ? 1 : 0);
-    const int lo = (int)((long)total * xcd / 8), hi = (int)((long)total * (xcd + 1) / 8);
+    const int nx = nwg < 8 ? nwg : 8;
+    const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
+    const int per_xcd_wg = nwg / nx + (xcd < nwg % nx ? 1 : 0);
+    const int lo = (int)((long)total * xcd / nx), hi = (int)((long)total * (xcd + 1) / nx);
+
+    // this lane's place in every 1 KB DMA block: row lane/8 of the block, physical
+    // chunk lane%8, which holds logical chunk (lane%8) ^ (lane/8)
+    const int dma_row = lane / 8, dma_chunk = (lane % 8) ^ (lane / 8);
 
     for (int L = lo + slot; L < hi; L += per_xcd_wg) {
         const int mt = L / NTN, nt = L % NTN;
@@ -92,40 +123,43 @@ grouped_gemm_kernel(const GemmArgs g) {
         const int rows = min(BM, g.offsets[e + 1] - row0);
         const int n0 = nt * BN;
 
-        // per-thread global pointers (fixed over K)
-        const uint8_t* ap[G::CA];
-        bool av[G::CA];
+        // per-lane DMA source rows (fixed over K); rows past the expert's end
+        // re-read the tile's first row (finite data; their outputs are dropped)
+        const uint8_t* ap[G::DA];
 #pragma unroll
-        for (int i = 0; i < G::CA; ++i) {
-            const int c = tid + G::NT * i, r = c / 8;
-            av[i] = r < rows;
-            long src = row0 + (av[i] ? r : 0);
+        for (int i = 0; i < G::DA; ++i) {
+            const int r = (wave * G::DA + i) * 8 + dma_row;
+            long src = row0 + (r < rows ? r : 0);
             if (GATHER) src = g.perm[src] / g.k;
-            ap[i] = g.A + src * g.lda + (c % 8) * 16;
+            ap[i] = g.A + src * g.lda + dma_chunk * 16;
         }
-        const uint8_t* bp[G::CB];
+        const uint8_t* bp[G::DB];
 #pragma unroll
-        for (int i = 0; i < G::CB; ++i) {
-            const int c = tid + G::NT * i;
-            bp[i] = g.B + ((long)e * g.N + n0 + c / 8) * g.Kb + (c % 8) * 16;
+        for (int i = 0; i < G::DB; ++i) {
+            const int r = (wave * G::DB + i) * 8 + dma_row;
+            bp[i] = g.B + ((long)e * g.N + n0 + r) * g.Kb + dma_chunk * 16;
         }
         const float* sap = nullptr;
-        if (SC == SC_BLOCK && tid < BM) {
-            long src = row0 + (tid < rows ? tid : 0);
+        if constexpr (SC == SC_BLOCK) {
+            const int r = wave * 64 + lane;          // lanes past BM fetch a valid, unused row
+            long src = row0 + (r < rows ? r : 0);
             if (GATHER) src = g.perm[src] / g.k;
             sap = g.sa + src * g.sa_ld;
         }
-        // weight-scale block columns of this wave's 16-wide column groups
-        int swcol[G::NI];
-#pragma unroll
-        for (int ni = 0; ni < G::NI; ++ni) {
-            const int pc = n0 + wn * G::TN + ni * 16;
-            int oc = pc;
-            if (EPI != EPI_Y_BF16) {
-                const int grp = pc / 16;
-                oc = (grp & 1) ? g.I + 16 * (grp >> 1) : 16 * (grp >> 1);
+        // blockwise FP8: the tile's weight-scale table [KT][BN/16] goes to LDS once
+        // per tile (read back in the K loop without global loads in flight)
+        float* SWT = reinterpret_cast<float*>(smem + kStages * G::STAGE);
+        if constexpr (SC == SC_BLOCK) {
+            constexpr int GR = BN / 16;
+            for (int i = tid; i < KT * GR; i += G::NT) {
+                const int kt = i / GR, pc = n0 + (i % GR) * 16;
+                int oc = pc;
+                if (EPI != EPI_Y_BF16) {
+                    const int grp = pc / 16;
+                    oc = (grp & 1) ? g.I + 16 * (grp >> 1) : 16 * (grp >> 1);
+                }
+                SWT[i] = g.sw[((long)e * KT + kt) * g.nb_orig + oc / 128];
             }
-            swcol[ni] = oc / 128;
         }
 
         f32x4 acc[G::MI][G::NI];
@@ -134,115 +168,134 @@ grouped_gemm_kernel(const GemmArgs g) {
 #pragma unroll
             for (int ni = 0; ni < G::NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        u32x4 ra[G::CA], rb[G::CB];
-        float rsa = 0.0f;
-        auto gload = [&](int kt) {
+        // one stage: G::DMA direct global->LDS loads per wave
+        auto issue = [&](int kt) {
+            uint8_t* st = smem + (kt % kStages) * G::STAGE;
+            const bool kin = !KTAIL || kt * 128 + dma_chunk * 16 < g.Kb;
 #pragma unroll
-            for (int i = 0; i < G::CA; ++i) {
-                const bool kin = kt * 128 + ((tid + G::NT * i) % 8) * 16 < g.Kb;
-                ra[i] = (av[i] && kin) ? *reinterpret_cast<const u32x4*>(ap[i] + kt * 128) : u32x4{0, 0, 0, 0};
+            for (int i = 0; i < G::DA; ++i) {
+                const void* src = kin ? static_cast<const void*>(ap[i] + kt * 128)
+                                      : static_cast<const void*>(kZero16);
+                __builtin_amdgcn_global_load_lds(src, MOE_LDS(st + (wave * G::DA + i) * 1024), 16, 0, 0);
             }
 #pragma unroll
-            for (int i = 0; i < G::CB; ++i) {
-                const bool kin = kt * 128 + ((tid + G::NT * i) % 8) * 16 < g.Kb;
-                rb[i] = kin ? *reinterpret_cast<const u32x4*>(bp[i] + kt * 128) : u32x4{0, 0, 0, 0};
+            for (int i = 0; i < G::DB; ++i) {
+                const void* src = kin ? static_cast<const void*>(bp[i] + kt * 128)
+                                      : static_cast<const void*>(kZero16);
+                __builtin_amdgcn_global_load_lds(src, MOE_LDS(st + BM * kRowB + (wave * G::DB + i) * 1024),
+                                                 16, 0, 0);
             }
-            if (SC == SC_BLOCK && tid < BM) rsa = tid < rows ? sap[kt] : 0.0f;
+            if constexpr (SC == SC_BLOCK)
+                __builtin_amdgcn_global_load_lds(sap + kt, MOE_LDS(st + (BM + BN) * kRowB + wave * 256), 4, 0, 0);
         };
-        auto sstore = [&](int stage) {
-            uint8_t* As = smem + stage * G::STAGE;
-            uint8_t* Bs = As + BM * kLdsRow;
-#pragma unroll
-            for (int i = 0; i < G::CA; ++i) {
-                const int c = tid + G::NT * i;
-                *reinterpret_cast<u32x4*>(As + (c / 8) * kLdsRow + (c % 8) * 16) = ra[i];
-            }
-#pragma unroll
-            for (int i = 0; i < G::CB; ++i) {
-                const int c = tid + G::NT * i;
-                *reinterpret_cast<u32x4*>(Bs + (c / 8) * kLdsRow + (c % 8) * 16) = rb[i];
-            }
-            if (SC == SC_BLOCK && tid < BM)
-                reinterpret_cast<float*>(Bs + BN * kLdsRow)[tid] = rsa;
-        };
-
-        gload(0);
-        sstore(0);
-        __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < KT) gload(kt + 1);
-            const uint8_t* As = smem + cur * G::STAGE;
-            const uint8_t* Bs = As + BM * kLdsRow;
+        // Fragments of one K step are read from LDS in two halves (bf16: the two
+        // 32-deep MFMA K slices; fp8: the two halves of the wave's columns, with
+        // the A fragments kept per step parity).  The next half is always read
+        // while the current half's MFMAs run, so LDS latency stays hidden.
+        bf16x8 fa[2][G::MI], fb[2][G::NI];
+        i32x8 qa[2][G::MI], qb[G::NI];
+        f32x4 sav[2][G::MI];
+        constexpr int NH = G::NI / 2;
+        auto load_half = [&](auto Pc, int stage, int h) {
+            constexpr int P = decltype(Pc)::value;
+            const uint8_t* As = smem + stage * G::STAGE;
+            const uint8_t* Bs = As + BM * kRowB;
             if constexpr (!FP8) {
+                const int c = h * 4 + lane / 16;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int kb = kk * 64 + (lane / 16) * 16;
-                    bf16x8 af[G::MI], bfr[G::NI];
+                for (int mi = 0; mi < G::MI; ++mi)
+                    fa[h][mi] = *reinterpret_cast<const bf16x8*>(As + swz(wm * G::TM + mi * 16 + lane % 16, c));
 #pragma unroll
-                    for (int mi = 0; mi < G::MI; ++mi)
-                        af[mi] = *reinterpret_cast<const bf16x8*>(
-                            As + (wm * G::TM + mi * 16 + lane % 16) * kLdsRow + kb);
-#pragma unroll
-                    for (int ni = 0; ni < G::NI; ++ni)
-                        bfr[ni] = *reinterpret_cast<const bf16x8*>(
-                            Bs + (wn * G::TN + ni * 16 + lane % 16) * kLdsRow + kb);
-#pragma unroll
-                    for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                        for (int ni = 0; ni < G::NI; ++ni)
-                            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni],
-                                                                                 acc[mi][ni], 0, 0, 0);
-                }
+                for (int ni = 0; ni < G::NI; ++ni)
+                    fb[h][ni] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * G::TN + ni * 16 + lane % 16, c));
             } else {
-                const int kb = (lane / 16) * 32;
-                i32x8 af[G::MI], bfr[G::NI];
-#pragma unroll
-                for (int mi = 0; mi < G::MI; ++mi) {
-                    const uint8_t* p = As + (wm * G::TM + mi * 16 + lane % 16) * kLdsRow + kb;
-                    const u32x4 lo4 = *reinterpret_cast<const u32x4*>(p);
-                    const u32x4 hi4 = *reinterpret_cast<const u32x4*>(p + 16);
-                    af[mi] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                                   (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-                }
-#pragma unroll
-                for (int ni = 0; ni < G::NI; ++ni) {
-                    const uint8_t* p = Bs + (wn * G::TN + ni * 16 + lane % 16) * kLdsRow + kb;
-                    const u32x4 lo4 = *reinterpret_cast<const u32x4*>(p);
-                    const u32x4 hi4 = *reinterpret_cast<const u32x4*>(p + 16);
-                    bfr[ni] = i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                                    (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-                }
-                if constexpr (SC == SC_BLOCK) {
-                    const float* SA = reinterpret_cast<const float*>(Bs + BN * kLdsRow);
-                    float swv[G::NI];
-#pragma unroll
-                    for (int ni = 0; ni < G::NI; ++ni)
-                        swv[ni] = g.sw[((long)e * KT + kt) * g.nb_orig + swcol[ni]];
+                const int c0 = (lane / 16) * 2;
+                auto rd32 = [&](const uint8_t* base, int r) {
+                    const u32x4 lo4 = *reinterpret_cast<const u32x4*>(base + swz(r, c0));
+                    const u32x4 hi4 = *reinterpret_cast<const u32x4*>(base + swz(r, c0 + 1));
+                    return i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                                 (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+                };
+                if (h == 0) {
 #pragma unroll
                     for (int mi = 0; mi < G::MI; ++mi) {
-                        const f32x4 sav = *reinterpret_cast<const f32x4*>(
-                            SA + wm * G::TM + mi * 16 + (lane / 16) * 4);
-#pragma unroll
-                        for (int ni = 0; ni < G::NI; ++ni) {
-                            const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                af[mi], bfr[ni], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) acc[mi][ni][q] = fmaf(p[q], sav[q] * swv[ni], acc[mi][ni][q]);
-                        }
+                        qa[P][mi] = rd32(As, wm * G::TM + mi * 16 + lane % 16);
+                        if constexpr (SC == SC_BLOCK)
+                            sav[P][mi] = *reinterpret_cast<const f32x4*>(
+                                reinterpret_cast<const float*>(Bs + BN * kRowB) + wm * G::TM + mi * 16 + (lane / 16) * 4);
                     }
+#pragma unroll
+                    for (int ni = 0; ni < NH; ++ni) qb[ni] = rd32(Bs, wn * G::TN + ni * 16 + lane % 16);
                 } else {
 #pragma unroll
-                    for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                        for (int ni = 0; ni < G::NI; ++ni)
-                            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                af[mi], bfr[ni], acc[mi][ni], 0, 0, 0, 0, 0, 0);
+                    for (int ni = NH; ni < G::NI; ++ni) qb[ni] = rd32(Bs, wn * G::TN + ni * 16 + lane % 16);
                 }
             }
-            if (kt + 1 < KT) sstore(cur ^ 1);
-            __syncthreads();
+        };
+        auto mfma_half = [&](auto Pc, int kt, int h) {
+            constexpr int P = decltype(Pc)::value;
+            if constexpr (!FP8) {
+#pragma unroll
+                for (int mi = 0; mi < G::MI; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < G::NI; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[h][mi], fb[h][ni], acc[mi][ni], 0, 0, 0);
+            } else {
+                const float* swt = SWT + kt * (BN / 16) + wn * G::TN / 16;
+#pragma unroll
+                for (int mi = 0; mi < G::MI; ++mi)
+#pragma unroll
+                    for (int nj = 0; nj < NH; ++nj) {
+                        const int ni = h * NH + nj;
+                        if constexpr (SC == SC_BLOCK) {
+                            const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                qa[P][mi], qb[ni], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                            const float sw = swt[ni];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                acc[mi][ni][q] = fmaf(p[q], sav[P][mi][q] * sw, acc[mi][ni][q]);
+                        } else {
+                            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                qa[P][mi], qb[ni], acc[mi][ni], 0, 0, 0, 0, 0, 0);
+                        }
+                    }
+            }
+        };
+        // one K step: half 1 of kt is read, half 0 of kt computes, then (barrier)
+        // stage kt is released, kt+3 is requested and half 0 of kt+1 is read
+        // while half 1 of kt computes
+        auto step = [&](auto Pc, int kt) {
+            constexpr int P = decltype(Pc)::value;
+            std::integral_constant<int, P ^ 1> Qc;
+            load_half(Pc, kt % kStages, 1);
+            mfma_half(Pc, kt, 0);
+            if (kt + 1 < KT) {
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);   // keep this step's LDS reads above
+                if (kt + 2 < KT) wait_vm_lgkm<G::DMA>();  // stage kt+1 landed (this wave)
+                else wait_vm_lgkm<0>();
+                __builtin_amdgcn_s_barrier();             // ... for every wave; stage kt is free
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                if (kt + 3 < KT) issue(kt + 3);
+                load_half(Qc, (kt + 1) % kStages, 0);
+            }
+            mfma_half(Pc, kt, 1);
+        };
+
+        // three-stage ring, three steps requested ahead
+        issue(0);
+        if (KT > 1) issue(1);
+        if (KT > 2) issue(2);
+        if (KT > 2) wait_vm_lgkm<2 * G::DMA>();
+        else if (KT > 1) wait_vm_lgkm<G::DMA>();
+        else wait_vm_lgkm<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        load_half(std::integral_constant<int, 0>{}, 0, 0);
+        for (int kt = 0; kt < KT; kt += 2) {
+            step(std::integral_constant<int, 0>{}, kt);
+            if (kt + 1 < KT) step(std::integral_constant<int, 1>{}, kt + 1);
         }
+        __syncthreads();   // the epilogue reuses the stage buffers
 
         if constexpr (SC == SC_TENSOR) {
             const float f = g.sa[0] * g.sw[e];
@@ -296,7 +349,7 @@ grouped_gemm_kernel(const GemmArgs g) {
             const int hc0 = (n0 + wn * G::TN) / 2;
             const int hl0 = wn * G::TN / 2;
             if constexpr (EPI == EPI_SWIGLU_F32) {
-                float am = 0.0f;
+                // fp32 h; its per-tensor scale is taken over all routes afterwards
                 float* H = static_cast<float*>(g.C);
 #pragma unroll
                 for (int mi = 0; mi < G::MI; ++mi)
@@ -305,14 +358,10 @@ grouped_gemm_kernel(const GemmArgs g) {
                         const int r = rbase + mi * 16 + q;
                         if (r < rows) {
 #pragma unroll
-                            for (int p = 0; p < G::NI / 2; ++p) {
+                            for (int p = 0; p < G::NI / 2; ++p)
                                 H[(long)(row0 + r) * g.ldc + hc0 + p * 16 + lane % 16] = H_AT(mi, p, q);
-                                am = fmaxf(am, fabsf(H_AT(mi, p, q)));
-                            }
                         }
                     }
-                am = wave_max(am);
-                if (lane == 0) atomicMax(g.amax, __float_as_uint(am));
             } else if constexpr (EPI == EPI_SWIGLU_BF16) {
                 constexpr int HW = BN / 2;               // h columns per tile
                 constexpr int ROWB = HW * 2 + 16;
@@ -408,10 +457,10 @@ static int num_cus() {
     return g_num_cus;
 }
 
-template <bool FP8, bool GATHER, int SC, int EPI, int BM, int BN, int WM, int WN>
+template <bool FP8, bool GATHER, int SC, int EPI, int BM, int BN, int WM, int WN, bool KTAIL = false>
 static hipError_t run_gemm(const GemmArgs& a, int wg_per_cu, hipStream_t st) {
     using G = Gemm<FP8, GATHER, SC, EPI, BM, BN, WM, WN>;
-    auto kern = grouped_gemm_kernel<FP8, GATHER, SC, EPI, BM, BN, WM, WN>;
+    auto kern = grouped_gemm_kernel<FP8, GATHER, SC, EPI, BM, BN, WM, WN, KTAIL>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -424,6 +473,18 @@ static hipError_t run_gemm(const GemmArgs& a, int wg_per_cu, hipStream_t st) {
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(G::NT), G::LDS, st, a);
     return hipGetLastError();
+}
+
+// 128 x 256 tiles (4 waves of 64 x 128, one workgroup per CU) where the
+// output width allows, 128 x 128 tiles (4 waves of 64 x 64, two per CU) otherwise.
+template <bool FP8, bool GATHER, int SC, int EPI>
+static hipError_t run_any(const GemmArgs& a, hipStream_t st) {
+    if (a.N % 256 == 0) return run_gemm<FP8, GATHER, SC, EPI, 128, 256, 2, 2>(a, 1, st);
+    if constexpr (EPI == EPI_SWIGLU_Q128) {
+        return hipErrorInvalidValue;
+    } else {
+        return run_gemm<FP8, GATHER, SC, EPI, 128, 128, 2, 2>(a, 1, st);
+    }
 }
 
 static GemmArgs gate_up_args(const FwdPlan& p, int elem) {
@@ -453,20 +514,19 @@ hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st) {
         GemmArgs a = gate_up_args(p, 2);
         a.C = p.h;
         a.ldc = p.I;
-        return run_gemm<false, true, SC_NONE, EPI_SWIGLU_BF16, 128, 128, 2, 2>(a, 2, st);
+        return run_any<false, true, SC_NONE, EPI_SWIGLU_BF16>(a, st);
     }
     if (p.quant == Q_FP8_TENSOR) {
         GemmArgs a = gate_up_args(p, 1);
         a.C = p.h;
         a.ldc = p.I;
-        a.amax = &p.amax[1];
-        return run_gemm<true, true, SC_TENSOR, EPI_SWIGLU_F32, 128, 128, 2, 2>(a, 2, st);
+        return run_any<true, true, SC_TENSOR, EPI_SWIGLU_F32>(a, st);
     }
     GemmArgs a = gate_up_args(p, 1);
     a.C = p.hq;
     a.ldc = p.I;
     a.cscale = p.sh;
-    return run_gemm<true, true, SC_BLOCK, EPI_SWIGLU_Q128, 128, 256, 2, 2>(a, 1, st);
+    return run_any<true, true, SC_BLOCK, EPI_SWIGLU_Q128>(a, st);
 }
 
 hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
@@ -491,9 +551,14 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     a.C = p.y;
     a.ldc = p.H;
     a.max_tiles = p.max_tiles;
-    if (p.quant == Q_BF16) return run_gemm<false, false, SC_NONE, EPI_Y_BF16, 128, 128, 2, 2>(a, 2, st);
-    if (p.quant == Q_FP8_TENSOR) return run_gemm<true, false, SC_TENSOR, EPI_Y_BF16, 128, 128, 2, 2>(a, 2, st);
-    return run_gemm<true, false, SC_BLOCK, EPI_Y_BF16, 128, 128, 2, 2>(a, 1, st);
+    if (p.quant == Q_BF16) return run_any<false, false, SC_NONE, EPI_Y_BF16>(a, st);
+    if (p.quant == Q_FP8_TENSOR) {
+        if (a.Kb % 128 != 0)   // I % 128 != 0: the last K step reads zeros past the row end
+            return a.N % 256 == 0 ? run_gemm<true, false, SC_TENSOR, EPI_Y_BF16, 128, 256, 2, 2, true>(a, 1, st)
+                                  : run_gemm<true, false, SC_TENSOR, EPI_Y_BF16, 128, 128, 2, 2, true>(a, 1, st);
+        return run_any<true, false, SC_TENSOR, EPI_Y_BF16>(a, st);
+    }
+    return run_any<true, false, SC_BLOCK, EPI_Y_BF16>(a, st);
 }
 
 }  // namespace moe

@@ -68,6 +68,7 @@ int grouped_max_tiles(int R, int E);
 hipError_t launch_forward_init(const FwdPlan& p, bool build_tiles, hipStream_t st);
 hipError_t launch_quant_x(const FwdPlan& p, hipStream_t st);
 hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st);
+bool forward_needs_amax(const FwdPlan& p);   // the amax words must start at zero
 hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st);
 hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st);
 hipError_t launch_combine(const FwdPlan& p, hipStream_t st);

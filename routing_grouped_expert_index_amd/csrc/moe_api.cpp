@@ -55,6 +55,8 @@ int check_shape(int T, int H, int I, int E, int k, int quant) {
     if (I % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "I=%d: I must be a multiple of 64", I);
     if (quant == MOE_FP8_BLOCK128 && I % 128 != 0)
         return fail(MOE_ERR_UNSUPPORTED, "I=%d: block128 needs I a multiple of 128", I);
+    if (quant == MOE_FP8_BLOCK128 && (H > 8192 || I > 8192))
+        return fail(MOE_ERR_UNSUPPORTED, "block128: H and I up to 8192 (64 scale blocks along K)");
     if ((long)E * H * 2 * I >= (1L << 40)) return fail(MOE_ERR_UNSUPPORTED, "weights too large");
     return MOE_OK;
 }
@@ -256,7 +258,7 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
         if ((rc = hip_status((call), what)) != MOE_OK) return rc;       \
         mark(what);                                                     \
     } while (0)
-    if (grouped || quant == MOE_FP8_PER_TENSOR) MOE_STEP(moe::launch_forward_init(P, grouped, st), "init");
+    if (grouped || moe::forward_needs_amax(P)) MOE_STEP(moe::launch_forward_init(P, grouped, st), "init");
     if (quant != MOE_BF16) MOE_STEP(moe::launch_quant_x(P, st), "quant_x");
     if (grouped) {
         MOE_STEP(moe::launch_grouped_gate_up(P, st), "gate_up");

@@ -17,27 +17,31 @@
 
 namespace moe {
 
-// Picks the k largest logits of one token (row) with one wave.  Lane 0 writes
-// ids[0..k) and the gates w[0..k).  Gates: exp(l_j - m) / sum_i exp(l_i - m)
-// over the picks, m = the largest logit (the full softmax denominator cancels
-// in the renormalisation).
+// Picks the k largest logits of one token (row) with one wave.  Gates:
+// exp(l_j - m) / sum over the picks of exp(l_i - m), m = the largest logit (the
+// full softmax denominator cancels in the renormalisation).  The lane that owns
+// a picked logit remembers its slot j and writes ids[j] and w[j] itself, so no
+// value travels back through memory; the sum over the picks is a wave-wide
+// butterfly, which gives every lane the same bits.
 template <int VPL>
 __device__ void topk_one_token(const float* __restrict__ row, int E, int k,
                                int32_t* __restrict__ ids, float* __restrict__ w,
                                int32_t* __restrict__ ids_lds, int32_t* __restrict__ cnt_lds) {
     const int lane = lane_id();
     float v[VPL];
+    int slot[VPL];
     uint32_t avail = 0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e = lane + kWave * i;
         v[i] = 0.0f;
+        slot[i] = -1;
         if (e < E) {
             v[i] = row[e] + 0.0f;   // -0 -> +0 (comparisons treat them equal anyway)
             avail |= 1u << i;
         }
     }
-    float m = 0.0f, S = 0.0f;
+    float m = 0.0f;
     for (int j = 0; j < k; ++j) {
         float bv = 0.0f;
         int bi = -1;
@@ -54,19 +58,25 @@ __device__ void topk_one_token(const float* __restrict__ row, int E, int k,
             const bool take = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
             if (take) { bv = ov; bi = oi; }
         }
-        if ((bi & (kWave - 1)) == lane) avail &= ~(1u << (bi / kWave));
         if (j == 0) m = bv;
-        const float ej = expf(bv - m);
-        S += ej;                    // same order in every lane
-        if (lane == 0) {
-            ids[j] = bi;
-            w[j] = ej;
-            if (ids_lds) ids_lds[j] = bi;
-            if (cnt_lds) atomicAdd(&cnt_lds[bi], 1);
-        }
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (bi == lane + kWave * i) { avail &= ~(1u << i); slot[i] = j; }
     }
-    if (lane == 0) {
-        for (int j = 0; j < k; ++j) w[j] = w[j] / S;   // lane 0 re-reads its own stores
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        if (slot[i] >= 0) part += expf(v[i] - m);
+    const float S = wave_sum(part);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        if (slot[i] >= 0) {
+            const int e = lane + kWave * i, j = slot[i];
+            ids[j] = e;
+            w[j] = expf(v[i] - m) / S;
+            if (ids_lds) ids_lds[j] = e;
+            if (cnt_lds) atomicAdd(&cnt_lds[e], 1);
+        }
     }
 }
 
@@ -157,10 +167,11 @@ route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int nb
 // ----------------------------------------------------------------------------
 // Large T*k: three kernels, 64 tokens per workgroup of 4 waves.
 constexpr int kTokPerBlock = 64;
-constexpr int kBigWaves = 4;
+constexpr int kBigWaves = 4;          // scatter kernel
+constexpr int kTopkWaves = 16;        // top-k kernel: 4 tokens per wave
 
 template <int VPL>
-__global__ void __launch_bounds__(kBigWaves * kWave)
+__global__ void __launch_bounds__(kTopkWaves * kWave)
 route_topk_hist_kernel(const float* __restrict__ logits, int T, int E, int k,
                        int32_t* __restrict__ ids, float* __restrict__ weights,
                        int32_t* __restrict__ block_hist) {
@@ -169,7 +180,7 @@ route_topk_hist_kernel(const float* __restrict__ logits, int T, int E, int k,
     const int t0 = blockIdx.x * kTokPerBlock, t1 = min(T, t0 + kTokPerBlock);
     for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
-    for (int t = t0 + wave; t < t1; t += kBigWaves)
+    for (int t = t0 + wave; t < t1; t += kTopkWaves)
         topk_one_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
                             weights + (size_t)t * k, nullptr, cnt);
     __syncthreads();
@@ -177,33 +188,58 @@ route_topk_hist_kernel(const float* __restrict__ logits, int T, int E, int k,
 }
 
 // Column scan over workgroups (per expert) and the exclusive prefix over experts.
-__global__ void __launch_bounds__(kMaxExperts)
+// P = 1024 / E' threads share a column (E' = E rounded up to a power of two):
+// each sums a contiguous run of workgroup rows, the P partial sums are scanned
+// in LDS, and each thread then rewrites its run as a running prefix.
+constexpr int kScanThreads = 1024;
+
+__global__ void __launch_bounds__(kScanThreads)
 route_scan_kernel(int nblk, int E, int R, int32_t* __restrict__ block_hist,
                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-    __shared__ int32_t wsum[kMaxExperts / kWave];
-    const int e = threadIdx.x, lane = lane_id(), wave = e / kWave;
-    int run = 0;
+    __shared__ int32_t part[kScanThreads];
+    __shared__ int32_t wsum[kScanThreads / kWave];
+    int Ep = 1;
+    while (Ep < E) Ep <<= 1;
+    const int P = kScanThreads / Ep;
+    const int e = threadIdx.x % Ep, p = threadIdx.x / Ep;
+    const int per = ceil_div(nblk, P);
+    const int b0 = min(nblk, p * per), b1 = min(nblk, b0 + per);
+    int sum = 0;
     if (e < E) {
-        int b = 0;
-        for (; b + 4 <= nblk; b += 4) {
-            const int c0 = block_hist[(size_t)(b + 0) * E + e];
-            const int c1 = block_hist[(size_t)(b + 1) * E + e];
-            const int c2 = block_hist[(size_t)(b + 2) * E + e];
-            const int c3 = block_hist[(size_t)(b + 3) * E + e];
-            block_hist[(size_t)(b + 0) * E + e] = run;
-            block_hist[(size_t)(b + 1) * E + e] = run + c0;
-            block_hist[(size_t)(b + 2) * E + e] = run + c0 + c1;
-            block_hist[(size_t)(b + 3) * E + e] = run + c0 + c1 + c2;
-            run += c0 + c1 + c2 + c3;
+        for (int b = b0; b < b1; b += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = b + i < b1 ? block_hist[(size_t)(b + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sum += c[i];
         }
-        for (; b < nblk; ++b) {
-            const int c = block_hist[(size_t)b * E + e];
-            block_hist[(size_t)b * E + e] = run;
-            run += c;
-        }
-        counts[e] = run;
     }
-    int incl = run;
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    // exclusive prefix of this thread's run within its column, and the column total
+    int before = 0, total = 0;
+    for (int q = 0; q < P; ++q) {
+        const int v = part[q * Ep + e];
+        if (q < p) before += v;
+        total += v;
+    }
+    if (e < E) {
+        int run = before;
+        for (int b = b0; b < b1; b += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = b + i < b1 ? block_hist[(size_t)(b + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (b + i < b1) block_hist[(size_t)(b + i) * E + e] = run;
+                run += c[i];
+            }
+        }
+    }
+    // exclusive prefix over experts (threads p == 0 hold the column totals)
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int t = (p == 0 && e < E) ? total : 0;
+    int incl = t;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const int o = __shfl_up(incl, off);
@@ -211,10 +247,13 @@ route_scan_kernel(int nblk, int E, int R, int32_t* __restrict__ block_hist,
     }
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    if (e < E) offsets[e] = before + incl - run;
-    if (e == 0) offsets[E] = R;
+    if (p == 0 && e < E) {
+        int wb = 0;
+        for (int w = 0; w < wave; ++w) wb += wsum[w];
+        counts[e] = total;
+        offsets[e] = wb + incl - t;
+    }
+    if (threadIdx.x == 0) offsets[E] = R;
 }
 
 __global__ void __launch_bounds__(kBigWaves * kWave)
@@ -294,7 +333,7 @@ template <int VPL>
 static hipError_t launch_topk_hist(const float* logits, int T, int E, int k, const RouteOut& o,
                                    int32_t* hist, hipStream_t st) {
     hipLaunchKernelGGL(route_topk_hist_kernel<VPL>, dim3(ceil_div(T, kTokPerBlock)),
-                       dim3(kBigWaves * kWave), 0, st, logits, T, E, k, o.ids, o.weights, hist);
+                       dim3(kTopkWaves * kWave), 0, st, logits, T, E, k, o.ids, o.weights, hist);
     return hipGetLastError();
 }
 
@@ -305,7 +344,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, const RouteOut
     int32_t* hist = static_cast<int32_t*>(ws);
     hipError_t err = MOE_VPL_DISPATCH(E, launch_topk_hist, logits, T, E, k, o, hist, st);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kMaxExperts), 0, st, nblk, E, T * k, hist,
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, nblk, E, T * k, hist,
                        o.counts, o.offsets);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(kBigWaves * kWave), 0, st, T, E, k,

@@ -14,7 +14,7 @@
 //  * Gate/Up: one wave per (route, JW h columns) streams 2*JW packed weight
 //    rows (K-contiguous) with 16-byte lane loads, dots them with x (or its e4m3
 //    codes) in fp32, reduces across the wave, applies SwiGLU and stores h
-//    (bf16, or fp32 plus a global amax for the per-tensor requantisation);
+//    (bf16, or fp32 for the FP8 requantisation that follows);
 //  * Down + combine: a workgroup of 4 waves owns 4 output columns of one token;
 //    wave w handles slots j = w, w+4, ...; 16 lanes share one weight row.  The
 //    four per-wave partial sums are added in wave order, so the top-k combine
@@ -58,7 +58,6 @@ struct RdArgs {
     const uint8_t* h;        // bf16 h [R][I] (bf16) or e4m3 hq [R][I] (fp8), Down input
     const float* sh;         // block: [R][I/128]; tensor: &s_h
     void* hout;              // Gate/Up output: bf16 [R][I] or fp32 [R][I]
-    uint32_t* amax;          // per-tensor h amax bits
     uint16_t* out;           // [T][H]
     int T, H, I, E, k;
 };
@@ -125,7 +124,6 @@ rd_gate_up_kernel(const RdArgs a) {
 #pragma unroll
         for (int q = 0; q < 2 * JW; ++q) acc[q] *= f;
     }
-    float am = 0.0f;
     if (lane < JW) {
         float hv = 0.0f;
 #pragma unroll
@@ -136,14 +134,9 @@ rd_gate_up_kernel(const RdArgs a) {
             if constexpr (!FP8) {
                 static_cast<uint16_t*>(a.hout)[(long)r * a.I + j] = f32_to_bf16(hv);
             } else {
-                static_cast<float*>(a.hout)[(long)r * a.I + j] = hv;
-                am = fabsf(hv);
+                static_cast<float*>(a.hout)[(long)r * a.I + j] = hv;   // requantised afterwards
             }
         }
-    }
-    if (SC == 1) {
-        am = wave_max(am);
-        if (lane == 0) atomicMax(a.amax, __float_as_uint(am));
     }
 }
 
@@ -218,7 +211,6 @@ static RdArgs rd_args(const FwdPlan& p) {
     a.h = fp8 ? p.hq : static_cast<const uint8_t*>(p.h);
     a.sh = p.quant == Q_FP8_BLOCK ? p.sh : &p.scal[1];
     a.hout = p.h;
-    a.amax = &p.amax[1];
     a.out = p.out;
     a.T = p.T; a.H = p.H; a.I = p.I; a.E = p.E; a.k = p.k;
     return a;

@@ -118,6 +118,10 @@ EDGE = [
     (150, 384, 256, 8, 2, "fp8_per_tensor", "normal", "per-tensor multi-tile"),
     (70, 256, 256, 6, 2, "fp8_block128", "normal", "block128 ragged"),
     (3, 512, 128, 32, 4, "fp8_block128", "normal", "block128 decode"),
+    # grids of fewer than 8 workgroups with several n-tiles (every tile range must be walked)
+    (5, 256, 192, 1, 1, "bf16", "normal", "small grid, 3 n-tiles"),
+    (3, 256, 384, 1, 1, "fp8_block128", "normal", "small grid block128"),
+    (2, 384, 192, 1, 1, "fp8_per_tensor", "normal", "small grid per-tensor"),
 ]
 
 
