@@ -76,6 +76,19 @@ __device__ __forceinline__ void wait_vm_lgkm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
 }
 
+// Scheduling hint for one straight-line region: groups of (1 VMEM load, 1 DS read,
+// 2 MFMAs) while they last, so loads and LDS reads issue between matrix ops.
+template <int NV, int ND, int NM>
+__device__ __forceinline__ void interleave_hint() {
+    if constexpr (NV > 0 || ND > 0 || NM > 0) {
+        if constexpr (NV > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if constexpr (ND > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        constexpr int m = NM >= 2 ? 2 : NM;
+        if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+        interleave_hint<(NV > 0 ? NV - 1 : 0), (ND > 0 ? ND - 1 : 0), NM - m>();
+    }
+}
+
 template <bool FP8, bool GATHER, int SC, int EPI, int BM, int BN, int WM, int WN>
 struct Gemm {
     static constexpr int NT = 64 * WM * WN;
@@ -169,24 +182,25 @@ grouped_gemm_kernel(const GemmArgs g) {
             for (int ni = 0; ni < G::NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // one stage: G::DMA direct global->LDS loads per wave
-        auto issue = [&](int kt) {
-            uint8_t* st = smem + (kt % kStages) * G::STAGE;
-            const bool kin = !KTAIL || kt * 128 + dma_chunk * 16 < g.Kb;
+        // request the data of K step skt into ring slot `slot`
+        auto issue = [&](int skt, int slot) {
+            uint8_t* st = smem + slot * G::STAGE;
+            const bool kin = !KTAIL || skt * 128 + dma_chunk * 16 < g.Kb;
 #pragma unroll
             for (int i = 0; i < G::DA; ++i) {
-                const void* src = kin ? static_cast<const void*>(ap[i] + kt * 128)
+                const void* src = kin ? static_cast<const void*>(ap[i] + skt * 128)
                                       : static_cast<const void*>(kZero16);
                 __builtin_amdgcn_global_load_lds(src, MOE_LDS(st + (wave * G::DA + i) * 1024), 16, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < G::DB; ++i) {
-                const void* src = kin ? static_cast<const void*>(bp[i] + kt * 128)
+                const void* src = kin ? static_cast<const void*>(bp[i] + skt * 128)
                                       : static_cast<const void*>(kZero16);
                 __builtin_amdgcn_global_load_lds(src, MOE_LDS(st + BM * kRowB + (wave * G::DB + i) * 1024),
                                                  16, 0, 0);
             }
             if constexpr (SC == SC_BLOCK)
-                __builtin_amdgcn_global_load_lds(sap + kt, MOE_LDS(st + (BM + BN) * kRowB + wave * 256), 4, 0, 0);
+                __builtin_amdgcn_global_load_lds(sap + skt, MOE_LDS(st + (BM + BN) * kRowB + wave * 256), 4, 0, 0);
         };
         // Fragments of one K step are read from LDS in two halves (bf16: the two
         // 32-deep MFMA K slices; fp8: the two halves of the wave's columns, with
@@ -264,30 +278,34 @@ grouped_gemm_kernel(const GemmArgs g) {
         // one K step: half 1 of kt is read, half 0 of kt computes, then (barrier)
         // stage kt is released, kt+3 is requested and half 0 of kt+1 is read
         // while half 1 of kt computes
+        // DS reads and LDS-DMA issues are spread between the MFMAs so the matrix
+        // core keeps working while the memory pipes are fed
+        constexpr int kDsHalf = FP8 ? 2 * G::NI / 2 + 2 * G::MI : G::MI + G::NI;   // ds_reads of half 0
+        constexpr int kDsHalf1 = FP8 ? 2 * (G::NI - G::NI / 2) : G::MI + G::NI;    // ds_reads of half 1
+        constexpr int kMfmaHalf = FP8 ? G::MI * (G::NI / 2) : G::MI * G::NI;
         auto step = [&](auto Pc, int kt) {
             constexpr int P = decltype(Pc)::value;
             std::integral_constant<int, P ^ 1> Qc;
             load_half(Pc, kt % kStages, 1);
             mfma_half(Pc, kt, 0);
-            if (kt + 1 < KT) {
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);   // keep this step's LDS reads above
-                if (kt + 2 < KT) wait_vm_lgkm<G::DMA>();  // stage kt+1 landed (this wave)
-                else wait_vm_lgkm<0>();
-                __builtin_amdgcn_s_barrier();             // ... for every wave; stage kt is free
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-                if (kt + 3 < KT) issue(kt + 3);
-                load_half(Qc, (kt + 1) % kStages, 0);
-            }
+            interleave_hint<0, kDsHalf1, kMfmaHalf>();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);   // keep this step's LDS reads above
+            wait_vm_lgkm<G::DMA>();                    // stage kt+1 landed (this wave)
+            __builtin_amdgcn_s_barrier();             // ... for every wave; slot kt is free
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            // always one stage per step: past the end the last step is re-read into
+            // the free slot, so the wait above is the same for every step
+            issue(min(kt + 3, KT - 1), (kt + 3) % kStages);
+            load_half(Qc, (kt + 1) % kStages, 0);
             mfma_half(Pc, kt, 1);
+            interleave_hint<G::DMA, kDsHalf, kMfmaHalf>();
         };
 
         // three-stage ring, three steps requested ahead
-        issue(0);
-        if (KT > 1) issue(1);
-        if (KT > 2) issue(2);
-        if (KT > 2) wait_vm_lgkm<2 * G::DMA>();
-        else if (KT > 1) wait_vm_lgkm<G::DMA>();
-        else wait_vm_lgkm<0>();
+        issue(0, 0);
+        issue(min(1, KT - 1), 1);
+        issue(min(2, KT - 1), 2);
+        wait_vm_lgkm<2 * G::DMA>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         load_half(std::integral_constant<int, 0>{}, 0, 0);
@@ -475,11 +493,17 @@ static hipError_t run_gemm(const GemmArgs& a, int wg_per_cu, hipStream_t st) {
     return hipGetLastError();
 }
 
-// 128 x 256 tiles (4 waves of 64 x 128, one workgroup per CU) where the
-// output width allows, 128 x 128 tiles (4 waves of 64 x 64, two per CU) otherwise.
+// 128 x 256 tiles (8 waves of 64 x 64: two waves per SIMD, so one wave's MFMAs
+// run while the other issues its loads) where the output width allows,
+// 128 x 128 tiles (4 waves of 64 x 64) otherwise.
 template <bool FP8, bool GATHER, int SC, int EPI>
 static hipError_t run_any(const GemmArgs& a, hipStream_t st) {
-    if (a.N % 256 == 0) return run_gemm<FP8, GATHER, SC, EPI, 128, 256, 2, 2>(a, 1, st);
+    if (a.N % 256 == 0) {
+        if constexpr (SC == SC_BLOCK)   // per-block rescale needs more registers: 4 waves of 64 x 128
+            return run_gemm<FP8, GATHER, SC, EPI, 128, 256, 2, 2>(a, 1, st);
+        else
+            return run_gemm<FP8, GATHER, SC, EPI, 128, 256, 2, 4>(a, 1, st);
+    }
     if constexpr (EPI == EPI_SWIGLU_Q128) {
         return hipErrorInvalidValue;
     } else {
@@ -554,7 +578,7 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     if (p.quant == Q_BF16) return run_any<false, false, SC_NONE, EPI_Y_BF16>(a, st);
     if (p.quant == Q_FP8_TENSOR) {
         if (a.Kb % 128 != 0)   // I % 128 != 0: the last K step reads zeros past the row end
-            return a.N % 256 == 0 ? run_gemm<true, false, SC_TENSOR, EPI_Y_BF16, 128, 256, 2, 2, true>(a, 1, st)
+            return a.N % 256 == 0 ? run_gemm<true, false, SC_TENSOR, EPI_Y_BF16, 128, 256, 2, 4, true>(a, 1, st)
                                   : run_gemm<true, false, SC_TENSOR, EPI_Y_BF16, 128, 128, 2, 2, true>(a, 1, st);
         return run_any<true, false, SC_TENSOR, EPI_Y_BF16>(a, st);
     }
