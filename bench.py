@@ -10,8 +10,8 @@ line carries
     flops per launch over its average duration, measured with HIP events the
     library records on its own stream during the timed steps;
   * decode: µs/layer at B=1..4 (bf16 route-direct path, H=2048 I=768 E=128),
-    cold HBM (a 1 GiB buffer is rewritten between iterations), with the HBM
-    fraction of its dominant kernel;
+    cold HBM (a 1 GiB buffer is read between iterations, so no expert weight
+    is left in the L2s or the MALL), with the HBM fraction of its dominant kernel;
   * fp8: the FP8 per-tensor decode (B=1..4, H=4096 I=192 E=192) and the FP8
     128x128-blockwise prefill (T=4096, H=4096, I=512) -- skipped with --quick;
   * cpu_baseline: the CPU oracle on a bounded sample of the headline workload.
@@ -118,23 +118,51 @@ def bench_prefill(torch, moe, name, steps, warmup):
     return dict(wl=wl, dt=dt, stages_ms=st, path=layer.path, counts=counts, layer=layer, host=(a, w))
 
 
+# HBM traffic of one Gate/Up launch from two rocprofv3 counter passes (FETCH_SIZE,
+# WRITE_SIZE; KiB per dispatch), each scaled by what the counter reads for a
+# plain 1 GiB copy kernel: FETCH_SIZE reads 524303 KiB for 1 GiB read (x2.0),
+# WRITE_SIZE reads exactly 1 GiB (x1.0).  Valid only for the GEMM source the
+# counters were taken on; any edit to it turns the figure into null.
+FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524303.0, 1.0
+COUNTER_TRAFFIC = {
+    "prefill_bf16": dict(gemm_sha256="0efb599a9c267a38cffd38bc5fcaf0118daba9bdaec52bdeac12d8bd5b119e98",
+                         fetch_kib=823863.0, write_kib=98304.0),
+}
+
+
+def counter_traffic(name):
+    import hashlib
+    rec = COUNTER_TRAFFIC.get(name)
+    if rec is None:
+        return None
+    src = os.path.join(ROOT, "routing_grouped_expert_index_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["gemm_sha256"]:
+            return None
+    return round((rec["fetch_kib"] * FETCH_SCALE + rec["write_kib"] * WRITE_SCALE) * 1024.0)
+
+
 def roofline_gemm(wl, stages_ms, peak):
     R = wl.T * wl.k
     flops = 4.0 * R * wl.H * wl.I            # Gate/Up: 2 flops x R rows x H x 2I
     t = stages_ms["gate_up"] / 1e3
     achieved = flops / t / 1e12
     return dict(kernel="grouped_gemm_kernel (Gate/Up + SwiGLU)", bound="mfma", achieved=round(achieved, 2),
-                peak=peak, unit="TFLOP/s", frac=round(achieved / peak, 4), traffic=None,
+                peak=peak, unit="TFLOP/s", frac=round(achieved / peak, 4),
+                traffic=counter_traffic(wl.name), traffic_unit="bytes per launch",
                 flops_per_launch=flops, avg_launch_us=round(stages_ms["gate_up"] * 1e3, 2))
 
 
 def bench_decode(torch, moe, name, batches, iters, nsets=32):
-    """Cold-HBM decode latency: a 1 GiB rewrite between iterations, 32 rotating routing sets."""
+    """Cold-HBM decode latency: a 1 GiB read between iterations, 32 rotating routing sets."""
     from workloads import WORKLOADS, random_activations, workload_weights
     wl = WORKLOADS[name]
     w = workload_weights(name)
     weights = dev_weights(torch, moe, w, wl.quant)
-    evict = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # eviction by READING 1 GiB (more than the 256 MB MALL and the L2s): a written
+    # eviction buffer leaves dirty lines whose write-back would compete with the
+    # layer's reads and halve the measured bandwidth
+    evict = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
     elem = 2 if wl.quant == "bf16" else 1
     res = {}
     for B in batches:
@@ -144,7 +172,7 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
         ev_sets, distinct = [], []
         for it in range(iters + 2):
             layer.x, layer.lg = xs[it % nsets]
-            evict.fill_(it & 0xff)
+            evict.amax()
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
             for e in evs:
                 e.record()
@@ -203,16 +231,18 @@ def profile_only(torch, moe, args):
     """Short runs of single workloads for rocprofv3 counter passes."""
     for name in args.only.split(","):
         if name == "copy":
-            src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+            # a plain copy kernel of known size (1 GiB read + 1 GiB written per launch):
+            # the reference that scales the FETCH_SIZE / WRITE_SIZE counters
+            src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
             dst = torch.empty_like(src)
             for _ in range(args.steps):
-                dst.copy_(src)
+                torch.mul(src, 1, out=dst)
             torch.cuda.synchronize()
-            log(f"copy: {args.steps} x 1 GiB device-to-device copies")
+            log(f"copy: {args.steps} x 1 GiB elementwise copy kernels")
         elif name.startswith("prefill"):
             pf = bench_prefill(torch, moe, name, args.steps, args.warmup)
             log(f"{name}: {pf['dt'] / args.steps * 1e3:.3f} ms/step, stages us "
-                f"{ {k: round(v * 1e3, 1) for k, v in pf['stages_ms'].items()} }")
+                f"{ {k: round(float(v) * 1e3, 1) for k, v in pf['stages_ms'].items()} }")
             del pf
         else:
             res = bench_decode(torch, moe, name, (1, 2, 3, 4), args.decode_iters)
