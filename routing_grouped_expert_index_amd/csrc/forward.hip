@@ -12,10 +12,11 @@
 // and workgroups past the count exit at once.
 //
 // Combine ("Port necessary FBGEMM MoE kernels", Summary: scatter_add_dense_tokens;
-// "perf: add small-batch route MMA for MoE", Code changes: reduce contiguous
-// route-order outputs): out[t] = sum_{j=0..k-1} w[t,j] * y[t*k + j], summed in
-// fp32 in ascending j and rounded to bf16 once -- no atomics, so two runs give
-// the same bits.
+// "perf: add small-batch route MMA for MoE", Code changes: top-k reduction):
+// out[t] = sum_{j=0..k-1} w[t,j] * y[route_pos[t*k + j]], where y holds the Down
+// outputs in sorted (expert) order and route_pos is the inverse of the sort,
+// summed in fp32 in ascending j and rounded to bf16 once -- no atomics, so two
+// runs give the same bits.
 #include "common.cuh"
 #include "launch.h"
 
@@ -227,16 +228,11 @@ hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-bool forward_needs_amax(const FwdPlan& p) {
-    return p.quant == Q_FP8_TENSOR &&
-           ((long)p.T * p.H > kSmallQuant || (long)p.R * p.I > kSmallQuant);
-}
-
 // ------------------------------------------------------------------ combine --
 
 __global__ void __launch_bounds__(256)
-combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, int H, int k,
-               uint16_t* __restrict__ out) {
+combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, const int32_t* __restrict__ route_pos,
+               int H, int k, uint16_t* __restrict__ out) {
     const int t = blockIdx.x;
     const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
     if (c >= H) return;
@@ -246,7 +242,7 @@ combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, int
     for (int j = 0; j < k; ++j) {
         const float w = tw[(size_t)t * k + j];
         float v[8];
-        load8<uint16_t>(y + ((size_t)t * k + j) * H + c, v);
+        load8<uint16_t>(y + (size_t)route_pos[(size_t)t * k + j] * H + c, v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
     }
@@ -258,7 +254,7 @@ combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, int
 
 hipError_t launch_combine(const FwdPlan& p, hipStream_t st) {
     dim3 grid(p.T, ceil_div(p.H / 8, 256));
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, p.y, p.tw, p.H, p.k, p.out);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, p.y, p.tw, p.route_pos, p.H, p.k, p.out);
     return hipGetLastError();
 }
 

@@ -1,469 +1,318 @@
-// Grouped expert GEMMs of the MoE forward on gfx950 (MFMA).
+// Grouped expert GEMMs of the MoE forward on gfx950: bf16 and FP8 per-tensor.
 //
 // "perf: add small-batch route MMA for MoE", Motivation: after the routes are
 // grouped by expert, a Gate/Up grouped GEMM, the activation (SwiGLU) with
 // optional FP8 quantisation, and a Down grouped GEMM; Summary: FP8 per-tensor
-// and 128x128 blockwise scaling.
+// scaling.
 //
-// One kernel template serves both projections and all three number formats:
-//  * tiles: BM=128 sorted rows of one expert (from the device-built tile map)
-//    x BN packed output columns; K is walked 128 bytes at a time (64 bf16 or
-//    128 e4m3 values), staged through LDS in two stages, rows padded to 144 B
-//    so the 16-byte MFMA operand reads are bank-conflict free;
-//  * the Gate/Up A operand is gathered on the fly: sorted row i reads token
-//    perm[i] / k of x (or of its e4m3 codes), so no gathered copy is written;
-//  * MFMA: bf16 v_mfma_f32_16x16x32_bf16, e4m3 v_mfma_f32_16x16x128_f8f6f4;
-//    every lane loads A and B with the same K layout, so the instruction's
-//    internal K order does not matter;
-//  * blockwise FP8: one K step is one 128-deep scale block, so each MFMA
-//    partial is rescaled by s_a[row] * s_w[block] in fp32 before accumulation;
-//  * persistent, XCD-aware schedule: workgroup w runs on XCD w % 8 (round-robin
-//    dispatch); each XCD walks a contiguous range of the (m-tile, n-tile) space,
-//    so the 12-16 n-tiles of an m-tile and neighbouring m-tiles of one expert
-//    share that XCD's L2;
-//  * epilogues: SwiGLU to bf16 h; SwiGLU to fp32 h plus a global amax (the
-//    per-tensor Down-input scale); SwiGLU with per-row 128-column e4m3
-//    requantisation; Down output written as bf16 to route order perm[i].
-#include "common.cuh"
-#include "launch.h"
-
-#include <type_traits>
+// Tile: 128 sorted rows of one expert (from the device-built tile map) x 512
+// packed weight rows; eight waves, two per SIMD, each owning 64 weight rows and
+// all 128 token rows, i.e. a 2 x 4 grid of 32x32 MFMA blocks (128 fp32
+// accumulators per lane, which the compiler keeps in AGPRs).  Two waves per
+// SIMD matter twice: a SIMD's MFMAs keep running while one wave waits, and the
+// vector-memory throughput a CU sustains grows with the number of waves issuing
+// loads (about 13 B/clk per CU from L2 with one wave per SIMD, twice that with
+// two).
+//  * K advances in 64-byte slices (32 bf16 or 64 e4m3 values).
+//  * Token rows move by direct global->LDS DMA into a 5-stage ring, four
+//    slices ahead; the Gate/Up A operand is gathered on the fly (sorted row i
+//    reads token perm[i] / k), so no gathered copy is ever written.
+//  * Weight rows are not shared between waves, so they skip LDS: each wave loads
+//    its own 32x32 operand blocks straight into registers (a 4-slot ring, three
+//    slices ahead) from the packed layout, where each wave-wide 16-byte load is
+//    one contiguous kilobyte.
+//  * MFMA: bf16 v_mfma_f32_32x32x16_bf16 (two per slice and block), e4m3
+//    v_mfma_f32_32x32x64_f8f6f4 (one per slice and block).  Both operands of an
+//    MFMA take the same K values in each lane, so the instruction's internal K
+//    order does not matter.
+//  * Epilogue straight from the accumulators: the packed column permutation
+//    gives each lane 32 contiguous output columns (Down) or the gate and up
+//    values of 16 contiguous h columns (Gate/Up), written as 16-byte stores
+//    in sorted row order (the combine finds a route's Down row through the
+//    inverse permutation).
+#include "gemm_common.cuh"
+#include "layout.cuh"
 
 namespace moe {
 
-enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_F32 = 1, EPI_SWIGLU_Q128 = 2, EPI_Y_BF16 = 3 };
-enum Scale { SC_NONE = 0, SC_TENSOR = 1, SC_BLOCK = 2 };
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-struct GemmArgs {
-    const uint8_t* A;       // row-major, lda bytes per row
-    long lda;
-    const int32_t* perm;    // gather: sorted row i -> token perm[i] / k; Down: output row perm[i]
-    int k;
-    const uint8_t* B;       // packed [E][N][K]
-    int N;                  // packed output columns
-    int Kb;                 // K in bytes (multiple of 128)
-    const int32_t* tiles;   // [max_tiles][2] (expert, first sorted row)
-    const int32_t* ntiles;
-    const int32_t* offsets; // [E+1]
-    const float* sa;        // tensor: &scalar; block: [rows][sa_ld]
-    int sa_ld;
-    const float* sw;        // tensor: [E]; block: [E][K/128][nb_orig]
-    int nb_orig;
-    int I;                  // Gate/Up: h width (column un-interleave)
-    void* C;                // output
-    long ldc;               // output row stride in elements
-    float* cscale;          // Q128: [R][I/128]
-    int max_tiles;
-};
+namespace g32 {
+constexpr int BM = 128;                     // token rows per tile
+constexpr int WROWS = 64;                   // packed weight rows per wave
+constexpr int NWAVE = 8;
+constexpr int NT = 64 * NWAVE;
+constexpr int BN = WROWS * NWAVE;           // packed weight rows per tile
+constexpr int STAGES = 5;                   // token ring: slices s .. s+4
+constexpr int STAGE_B = BM * kSliceBytes;   // 8 KB
+constexpr int LDS = STAGES * STAGE_B;
+// VMEM instructions per wave and slice: weight loads, token DMA
+constexpr int WLOADS = 4, DMAS = 1;
+// At the top of step s (after its weight loads) the token DMA of slice s,
+// issued in step s-4 (or the prologue), is followed by at least the weights
+// and DMA of steps s-3 .. s-1 and the weights of step s.
+constexpr int WAIT_STEP = 4 * WLOADS + 3 * DMAS;
+// Before the MFMAs of step s: the weights of slice s, requested in step s-3
+// (or the prologue), are followed by at least the prologue's later weights
+// (8), the weights and DMA of step s (5): 13 operations.
+constexpr int WAIT_W = 2 * WLOADS + WLOADS + DMAS;
+}  // namespace g32
 
-// LDS tile layout: a K step of a tile row is 128 bytes = 8 chunks of 16 bytes;
-// chunk c of row r lives at r*128 + ((c ^ (r & 7)) * 16).  The XOR spreads the
-// 16-byte MFMA operand reads of 8 consecutive rows over all 32 banks.
-constexpr int kRowB = 128;
-constexpr int kStages = 3;
-
-__device__ __forceinline__ int swz(int r, int c) { return r * kRowB + ((c ^ (r & 7)) << 4); }
-
-// 16 zero bytes: the source of K-tail chunks past the end of a row.
-__device__ __attribute__((aligned(16))) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
-
-#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// s_waitcnt with vmcnt <= N and lgkmcnt == 0 (expcnt untouched)
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
-}
-
-// Scheduling hint for one straight-line region: groups of (1 VMEM load, 1 DS read,
-// 2 MFMAs) while they last, so loads and LDS reads issue between matrix ops.
-template <int NV, int ND, int NM>
-__device__ __forceinline__ void interleave_hint() {
-    if constexpr (NV > 0 || ND > 0 || NM > 0) {
-        if constexpr (NV > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        if constexpr (ND > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        constexpr int m = NM >= 2 ? 2 : NM;
-        if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
-        interleave_hint<(NV > 0 ? NV - 1 : 0), (ND > 0 ? ND - 1 : 0), NM - m>();
-    }
-}
-
-template <bool FP8, bool GATHER, int SC, int EPI, int BM, int BN, int WM, int WN>
-struct Gemm {
-    static constexpr int NT = 64 * WM * WN;
-    static constexpr int NW = WM * WN;
-    static constexpr int TM = BM / WM, TN = BN / WN;
-    static constexpr int MI = TM / 16, NI = TN / 16;
-    static constexpr int DA = BM / 8 / NW, DB = BN / 8 / NW;   // 1 KB DMA loads per wave per stage
-    static constexpr int DS = SC == SC_BLOCK ? 1 : 0;          // + one row-scale load
-    static constexpr int DMA = DA + DB + DS;
-    static constexpr int STAGE = (BM + BN) * kRowB + DS * NW * 256;
-    static constexpr int SWT = SC == SC_BLOCK ? 64 * (BN / 16) * 4 : 0;   // K up to 64 blocks
-    static constexpr int LDS = kStages * STAGE + SWT;
-    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile/wave mismatch");
-    static_assert(MI >= 1 && NI >= 2 && NI % 2 == 0, "wave tile");
-    static_assert(NW * 64 >= BM, "row scales: one lane per tile row");
-};
-
-template <bool FP8, bool GATHER, int SC, int EPI, int BM, int BN, int WM, int WN, bool KTAIL>
-__global__ void __launch_bounds__(64 * WM * WN)
-grouped_gemm_kernel(const GemmArgs g) {
-    using G = Gemm<FP8, GATHER, SC, EPI, BM, BN, WM, WN>;
+template <bool FP8, bool GATHER, int SC, int EPI>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm32_kernel(const GemmArgs g) {
+    using namespace g32;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
-    const int wm = wave / WN, wn = wave % WN;
-    const int NTN = g.N / BN;
-    const int total = g.ntiles[0] * NTN;
-    const int KT = (g.Kb + 127) / 128;   // a partial last step reads zeros past the row end
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int j = lane & 31, hh = lane >> 5;
+    const int NTN = (g.N + BN - 1) / BN;
+    const int ntm = ld_const(g.ntiles, 0);
+    const int NSL = g.Kb / kSliceBytes;
+    const long gstride = 32L * g.Kb;               // bytes between 32-row blocks
+    const XcdRange xr = xcd_range(ntm * NTN);
+    int L = xr.first;
+    if (L >= xr.hi) return;
 
-    // XCD-aware contiguous ranges of the real tile space: one range per XCD
-    // (fewer ranges when the grid has fewer than 8 workgroups, so that every
-    // range has at least one workgroup walking it)
-    const int nwg = gridDim.x;
-    const int nx = nwg < 8 ? nwg : 8;
-    const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
-    const int per_xcd_wg = nwg / nx + (xcd < nwg % nx ? 1 : 0);
-    const int lo = (int)((long)total * xcd / nx), hi = (int)((long)total * (xcd + 1) / nx);
-
-    // this lane's place in every 1 KB DMA block: row lane/8 of the block, physical
-    // chunk lane%8, which holds logical chunk (lane%8) ^ (lane/8)
-    const int dma_row = lane / 8, dma_chunk = (lane % 8) ^ (lane / 8);
-
-    for (int L = lo + slot; L < hi; L += per_xcd_wg) {
-        const int mt = L / NTN, nt = L % NTN;
-        const int e = g.tiles[2 * mt], row0 = g.tiles[2 * mt + 1];
-        const int rows = min(BM, g.offsets[e + 1] - row0);
-        const int n0 = nt * BN;
-
-        // per-lane DMA source rows (fixed over K); rows past the expert's end
-        // re-read the tile's first row (finite data; their outputs are dropped)
-        const uint8_t* ap[G::DA];
+    // tile L -> (expert, first sorted row, valid rows, this wave's first packed row)
+    auto decode = [&](int Lx, int& e_, int& row0_, int& rows_, int& wn0_) __attribute__((always_inline)) {
+        int nt, mt;
+        if (g.order) { mt = Lx / NTN; nt = Lx - mt * NTN; }     // row tile major
+        else { nt = Lx / ntm; mt = Lx - nt * ntm; }             // column tile major
+        e_ = ld_const(g.tiles, 2 * mt);
+        row0_ = ld_const(g.tiles, 2 * mt + 1);
+        rows_ = min(BM, ld_const(g.offsets, e_ + 1) - row0_);
+        wn0_ = nt * BN + wave * WROWS;
+    };
+    // token DMA: this wave fills tile rows 16*wave + lane/4, physical chunk
+    // lane%4, which holds logical chunk (lane%4) ^ (row/4 % 4); padding rows
+    // re-read a valid row.  The wave's 16 source rows are read with scalar
+    // loads (a vector load here would need a vmcnt wait that drains the
+    // prefetch) and each lane picks its own.
+    const int dma_r = 16 * wave + (lane >> 2);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto src_row = [&](int row0_, int rows_) __attribute__((always_inline)) {
+        int sel = 0;
 #pragma unroll
-        for (int i = 0; i < G::DA; ++i) {
-            const int r = (wave * G::DA + i) * 8 + dma_row;
-            long src = row0 + (r < rows ? r : 0);
-            if (GATHER) src = g.perm[src] / g.k;
-            ap[i] = g.A + src * g.lda + dma_chunk * 16;
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * wave_u + i;
+            const int idx = row0_ + (r < rows_ ? r : 0);
+            const int v = GATHER ? ld_const(g.perm, idx) : idx;
+            sel = (lane >> 2) == i ? v : sel;
         }
-        const uint8_t* bp[G::DB];
+        return (long)(GATHER ? sel / g.k : sel);
+    };
+    auto make_ap = [&](long src) __attribute__((always_inline)) {
+        return g.A + src * g.lda + (((lane & 3) ^ ((dma_r >> 2) & 3)) * 16);
+    };
+    // idle waves (past N) load a valid block, so every wave issues the same loads
+    auto make_wp = [&](int e_, int wn0_) __attribute__((always_inline)) {
+        return g.B + (long)e_ * g.N * g.Kb + (long)((wn0_ < g.N ? wn0_ : 0) / 32) * gstride + lane * 16;
+    };
+
+    int e, row0, rows, wn0;
+    decode(L, e, row0, rows, wn0);
+    const uint8_t* ap = make_ap(src_row(row0, rows));
+    const uint8_t* wp = make_wp(e, wn0);
+
+    f32x16 acc[2][4];
+    u32x4 w[4][2][2];     // [slot][block f][half q]
+
+    auto wload = [&](const uint8_t* wp_, int s, int slot) __attribute__((always_inline)) {
+        const uint8_t* p = wp_ + (long)s * 2048;
 #pragma unroll
-        for (int i = 0; i < G::DB; ++i) {
-            const int r = (wave * G::DB + i) * 8 + dma_row;
-            bp[i] = g.B + ((long)e * g.N + n0 + r) * g.Kb + dma_chunk * 16;
-        }
-        const float* sap = nullptr;
-        if constexpr (SC == SC_BLOCK) {
-            const int r = wave * 64 + lane;          // lanes past BM fetch a valid, unused row
-            long src = row0 + (r < rows ? r : 0);
-            if (GATHER) src = g.perm[src] / g.k;
-            sap = g.sa + src * g.sa_ld;
-        }
-        // blockwise FP8: the tile's weight-scale table [KT][BN/16] goes to LDS once
-        // per tile (read back in the K loop without global loads in flight)
-        float* SWT = reinterpret_cast<float*>(smem + kStages * G::STAGE);
-        if constexpr (SC == SC_BLOCK) {
-            constexpr int GR = BN / 16;
-            for (int i = tid; i < KT * GR; i += G::NT) {
-                const int kt = i / GR, pc = n0 + (i % GR) * 16;
-                int oc = pc;
-                if (EPI != EPI_Y_BF16) {
-                    const int grp = pc / 16;
-                    oc = (grp & 1) ? g.I + 16 * (grp >> 1) : 16 * (grp >> 1);
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                w[slot][f][q] = *reinterpret_cast<const u32x4*>(p + f * gstride + q * 1024);
+    };
+    auto dma = [&](const uint8_t* ap_, int s, int stage) __attribute__((always_inline)) {
+        __builtin_amdgcn_global_load_lds(ap_ + s * kSliceBytes, MOE_LDS(smem + stage * STAGE_B + wave * 1024),
+                                         16, 0, 0);
+    };
+    // a tile's first requests: token DMA of slices 0..3, weights of slices 0..2
+    auto prologue = [&](const uint8_t* ap_, const uint8_t* wp_) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dma(ap_, min(u, NSL - 1), u);
+        __builtin_amdgcn_sched_barrier(0);
+        wload(wp_, 0, 0);
+        wload(wp_, min(1, NSL - 1), 1);
+        wload(wp_, min(2, NSL - 1), 2);
+    };
+    // token operand of block m, K half q (16 bytes: chunk 2hh + q of row 32m + j)
+    auto tok = [&](const uint8_t* st, int m, int q) __attribute__((always_inline)) {
+        const int r = 32 * m + j, c = 2 * hh + q;
+        return *reinterpret_cast<const u32x4*>(st + r * kSliceBytes + ((c ^ ((r >> 2) & 3)) << 4));
+    };
+    auto mma = [&](int slot, int stage) __attribute__((always_inline)) {
+        const uint8_t* st = smem + stage * STAGE_B;
+        if constexpr (!FP8) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const bf16x8 b = __builtin_bit_cast(bf16x8, tok(st, m, q));
+#pragma unroll
+                    for (int f = 0; f < 2; ++f)
+                        acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, w[slot][f][q]), b, acc[f][m], 0, 0, 0);
                 }
-                SWT[i] = g.sw[((long)e * KT + kt) * g.nb_orig + oc / 128];
-            }
-        }
-
-        f32x4 acc[G::MI][G::NI];
+        } else {
 #pragma unroll
-        for (int mi = 0; mi < G::MI; ++mi)
+            for (int m = 0; m < 4; ++m) {
+                const u32x4 b0 = tok(st, m, 0), b1 = tok(st, m, 1);
+                const i32x8 bv{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                               (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
 #pragma unroll
-            for (int ni = 0; ni < G::NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        // one stage: G::DMA direct global->LDS loads per wave
-        // request the data of K step skt into ring slot `slot`
-        auto issue = [&](int skt, int slot) {
-            uint8_t* st = smem + slot * G::STAGE;
-            const bool kin = !KTAIL || skt * 128 + dma_chunk * 16 < g.Kb;
-#pragma unroll
-            for (int i = 0; i < G::DA; ++i) {
-                const void* src = kin ? static_cast<const void*>(ap[i] + skt * 128)
-                                      : static_cast<const void*>(kZero16);
-                __builtin_amdgcn_global_load_lds(src, MOE_LDS(st + (wave * G::DA + i) * 1024), 16, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < G::DB; ++i) {
-                const void* src = kin ? static_cast<const void*>(bp[i] + skt * 128)
-                                      : static_cast<const void*>(kZero16);
-                __builtin_amdgcn_global_load_lds(src, MOE_LDS(st + BM * kRowB + (wave * G::DB + i) * 1024),
-                                                 16, 0, 0);
-            }
-            if constexpr (SC == SC_BLOCK)
-                __builtin_amdgcn_global_load_lds(sap + skt, MOE_LDS(st + (BM + BN) * kRowB + wave * 256), 4, 0, 0);
-        };
-        // Fragments of one K step are read from LDS in two halves (bf16: the two
-        // 32-deep MFMA K slices; fp8: the two halves of the wave's columns, with
-        // the A fragments kept per step parity).  The next half is always read
-        // while the current half's MFMAs run, so LDS latency stays hidden.
-        bf16x8 fa[2][G::MI], fb[2][G::NI];
-        i32x8 qa[2][G::MI], qb[G::NI];
-        f32x4 sav[2][G::MI];
-        constexpr int NH = G::NI / 2;
-        auto load_half = [&](auto Pc, int stage, int h) {
-            constexpr int P = decltype(Pc)::value;
-            const uint8_t* As = smem + stage * G::STAGE;
-            const uint8_t* Bs = As + BM * kRowB;
-            if constexpr (!FP8) {
-                const int c = h * 4 + lane / 16;
-#pragma unroll
-                for (int mi = 0; mi < G::MI; ++mi)
-                    fa[h][mi] = *reinterpret_cast<const bf16x8*>(As + swz(wm * G::TM + mi * 16 + lane % 16, c));
-#pragma unroll
-                for (int ni = 0; ni < G::NI; ++ni)
-                    fb[h][ni] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * G::TN + ni * 16 + lane % 16, c));
-            } else {
-                const int c0 = (lane / 16) * 2;
-                auto rd32 = [&](const uint8_t* base, int r) {
-                    const u32x4 lo4 = *reinterpret_cast<const u32x4*>(base + swz(r, c0));
-                    const u32x4 hi4 = *reinterpret_cast<const u32x4*>(base + swz(r, c0 + 1));
-                    return i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                                 (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-                };
-                if (h == 0) {
-#pragma unroll
-                    for (int mi = 0; mi < G::MI; ++mi) {
-                        qa[P][mi] = rd32(As, wm * G::TM + mi * 16 + lane % 16);
-                        if constexpr (SC == SC_BLOCK)
-                            sav[P][mi] = *reinterpret_cast<const f32x4*>(
-                                reinterpret_cast<const float*>(Bs + BN * kRowB) + wm * G::TM + mi * 16 + (lane / 16) * 4);
-                    }
-#pragma unroll
-                    for (int ni = 0; ni < NH; ++ni) qb[ni] = rd32(Bs, wn * G::TN + ni * 16 + lane % 16);
-                } else {
-#pragma unroll
-                    for (int ni = NH; ni < G::NI; ++ni) qb[ni] = rd32(Bs, wn * G::TN + ni * 16 + lane % 16);
+                for (int f = 0; f < 2; ++f) {
+                    const u32x4 a0 = w[slot][f][0], a1 = w[slot][f][1];
+                    const i32x8 av{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                    acc[f][m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[f][m], 0, 0, 0, 0,
+                                                                                 0, 0);
                 }
             }
-        };
-        auto mfma_half = [&](auto Pc, int kt, int h) {
-            constexpr int P = decltype(Pc)::value;
-            if constexpr (!FP8) {
-#pragma unroll
-                for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < G::NI; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[h][mi], fb[h][ni], acc[mi][ni], 0, 0, 0);
-            } else {
-                const float* swt = SWT + kt * (BN / 16) + wn * G::TN / 16;
-#pragma unroll
-                for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                    for (int nj = 0; nj < NH; ++nj) {
-                        const int ni = h * NH + nj;
-                        if constexpr (SC == SC_BLOCK) {
-                            const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                qa[P][mi], qb[ni], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                            const float sw = swt[ni];
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                acc[mi][ni][q] = fmaf(p[q], sav[P][mi][q] * sw, acc[mi][ni][q]);
-                        } else {
-                            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                qa[P][mi], qb[ni], acc[mi][ni], 0, 0, 0, 0, 0, 0);
-                        }
-                    }
-            }
-        };
-        // one K step: half 1 of kt is read, half 0 of kt computes, then (barrier)
-        // stage kt is released, kt+3 is requested and half 0 of kt+1 is read
-        // while half 1 of kt computes
-        // DS reads and LDS-DMA issues are spread between the MFMAs so the matrix
-        // core keeps working while the memory pipes are fed
-        constexpr int kDsHalf = FP8 ? 2 * G::NI / 2 + 2 * G::MI : G::MI + G::NI;   // ds_reads of half 0
-        constexpr int kDsHalf1 = FP8 ? 2 * (G::NI - G::NI / 2) : G::MI + G::NI;    // ds_reads of half 1
-        constexpr int kMfmaHalf = FP8 ? G::MI * (G::NI / 2) : G::MI * G::NI;
-        auto step = [&](auto Pc, int kt) {
-            constexpr int P = decltype(Pc)::value;
-            std::integral_constant<int, P ^ 1> Qc;
-            load_half(Pc, kt % kStages, 1);
-            mfma_half(Pc, kt, 0);
-            interleave_hint<0, kDsHalf1, kMfmaHalf>();
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);   // keep this step's LDS reads above
-            wait_vm_lgkm<G::DMA>();                    // stage kt+1 landed (this wave)
-            __builtin_amdgcn_s_barrier();             // ... for every wave; slot kt is free
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            // always one stage per step: past the end the last step is re-read into
-            // the free slot, so the wait above is the same for every step
-            issue(min(kt + 3, KT - 1), (kt + 3) % kStages);
-            load_half(Qc, (kt + 1) % kStages, 0);
-            mfma_half(Pc, kt, 1);
-            interleave_hint<G::DMA, kDsHalf, kMfmaHalf>();
-        };
-
-        // three-stage ring, three steps requested ahead
-        issue(0, 0);
-        issue(min(1, KT - 1), 1);
-        issue(min(2, KT - 1), 2);
-        wait_vm_lgkm<2 * G::DMA>();
+        }
+    };
+    // The hand-counted waits assume this VMEM order in every step: weight
+    // loads, then (after the barrier) the token DMA, with no later load hoisted
+    // above the DMA -- a load moved above it would leave fewer than WAIT_STEP
+    // loads behind the DMA being waited for.  Scheduling barriers pin that
+    // order.  (Extra loads issued later, like the next tile's indices or the
+    // epilogue's stores, only add operations behind a DMA and keep the waits
+    // sufficient.)
+    // One K slice s: weights of s+3 requested; (barrier) tokens of s landed
+    // everywhere and every wave is done with stage s-1; DMA of s+4 requested
+    // into that stage; MFMAs of s, reading tokens from LDS.  Requests past the
+    // end repeat the last slice, so every step waits for the same count.
+    // (MFMAs of idle waves and of the padding rows run on valid data and are
+    // dropped; a branch around them would make the compiler drain every load
+    // first.)
+    auto step = [&](auto Uc, int s, bool last) __attribute__((always_inline)) {
+        constexpr int U = decltype(Uc)::value;
+        wload(wp, min(s + 3, NSL - 1), (U + 3) & 3);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_lgkm<WAIT_STEP>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        load_half(std::integral_constant<int, 0>{}, 0, 0);
-        for (int kt = 0; kt < KT; kt += 2) {
-            step(std::integral_constant<int, 0>{}, kt);
-            if (kt + 1 < KT) step(std::integral_constant<int, 1>{}, kt + 1);
-        }
-        __syncthreads();   // the epilogue reuses the stage buffers
+        __builtin_amdgcn_sched_barrier(0);
+        dma(ap, min(s + 4, NSL - 1), (s + 4) % STAGES);
+        __builtin_amdgcn_sched_barrier(0);
+        // the weights of s were requested in step s-3 (or the prologue): at
+        // least WAIT_W loads follow them
+        wait_vm_only<WAIT_W>();
+        if (!last) mma(U, s % STAGES);
+        else if (s < NSL) mma(U, s % STAGES);
+    };
 
-        if constexpr (SC == SC_TENSOR) {
-            const float f = g.sa[0] * g.sw[e];
-#pragma unroll
-            for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < G::NI; ++ni)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[mi][ni][q] *= f;
+    prologue(ap, wp);
+    for (;;) {
+        // the next tile's indices are loaded now; their latency hides under this
+        // tile's K loop
+        const int Ln = L + xr.stride;
+        const bool more = Ln < xr.hi;
+        int ne = 0, nrow0 = 0, nrows = 1, nwn0 = 0;
+        long nsrc = 0;
+        if (more) {
+            decode(Ln, ne, nrow0, nrows, nwn0);
+            nsrc = src_row(nrow0, nrows);
         }
+
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[f][m][i] = 0.0f;
+        int s = 0;
+        for (; s + 4 <= NSL; s += 4) {
+            step(std::integral_constant<int, 0>{}, s, false);
+            step(std::integral_constant<int, 1>{}, s + 1, false);
+            step(std::integral_constant<int, 2>{}, s + 2, false);
+            step(std::integral_constant<int, 3>{}, s + 3, false);
+        }
+        if (s < NSL) {   // 1-3 slices left
+            step(std::integral_constant<int, 0>{}, s, true);
+            step(std::integral_constant<int, 1>{}, s + 1, true);
+            step(std::integral_constant<int, 2>{}, s + 2, true);
+        }
+        // Every wave is done reading this tile's ring, so the next tile's
+        // requests may go out before this tile's stores.  DMA left in flight from
+        // this tile's last steps lands in issue order, before the new requests.
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkm_only();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // (after the last tile the requests repeat this tile's valid data: an
+        // unconditional prologue keeps the loop's wait counts exact)
+        const uint8_t* nap = more ? make_ap(nsrc) : ap;
+        const uint8_t* nwp = more ? make_wp(ne, nwn0) : wp;
+        prologue(nap, nwp);
+        __builtin_amdgcn_sched_barrier(0);
 
         // ------------------------------------------------------------ epilogue
-        // accumulator (mi, ni, q) of this lane: tile row wm*TM + mi*16 + (lane/16)*4 + q,
-        // tile column wn*TN + ni*16 + lane%16
-        const int rbase = wm * G::TM + (lane / 16) * 4;
-        if constexpr (EPI == EPI_Y_BF16) {
-            constexpr int ROWB = BN * 2 + 16;
-            uint8_t* Ys = smem;
+        if (wn0 < g.N) {
+            float fs = 1.0f;
+            if constexpr (SC == SC_TENSOR) fs = ld_const(g.sa, 0) * ld_const(g.sw, e);
+            // acc[f][m][i]: token row 32m + j, packed row wn0 + 32f + 8(i/4) + 4hh + i%4
 #pragma unroll
-            for (int mi = 0; mi < G::MI; ++mi)
+            for (int m = 0; m < 4; ++m) {
+                const int r = 32 * m + j;
+                if (r >= rows) continue;
+                if constexpr (EPI == EPI_Y_BF16) {
+                    // output columns wn0 + 32hh + 16f + i of sorted row row0 + r
+                    uint16_t* base = static_cast<uint16_t*>(g.C) + (long)(row0 + r) * g.ldc + wn0 + 32 * hh;
 #pragma unroll
-                for (int ni = 0; ni < G::NI; ++ni)
+                    for (int f = 0; f < 2; ++f)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<uint16_t*>(Ys + (rbase + mi * 16 + q) * ROWB +
-                                                     (wn * G::TN + ni * 16 + lane % 16) * 2) =
-                            f32_to_bf16(acc[mi][ni][q]);
-            __syncthreads();
-            constexpr int CPR = BN * 2 / 16;   // 16-byte chunks per row
-            for (int c = tid; c < BM * CPR; c += G::NT) {
-                const int r = c / CPR, cc = c % CPR;
-                if (r < rows) {
-                    const long dst_row = g.perm[row0 + r];
-                    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.C) + dst_row * g.ldc + n0 + cc * 8) =
-                        *reinterpret_cast<const u32x4*>(Ys + r * ROWB + cc * 16);
-                }
-            }
-            __syncthreads();
-        } else {
-            // SwiGLU: accumulator pairs (2p gate, 2p+1 up) share lane and register slot
-            // h overwrites the gate accumulator (keeps register pressure down)
+                        for (int hv = 0; hv < 2; ++hv) {
+                            u32x4 v;
 #pragma unroll
-            for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                for (int p = 0; p < G::NI / 2; ++p)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        acc[mi][2 * p][q] = silu(acc[mi][2 * p][q]) * acc[mi][2 * p + 1][q];
-#define H_AT(mi, p, q) acc[mi][2 * (p)][q]
-            // h columns of this wave: hc0 + p*16 + lane%16 (global), tile-local hl0 + ...
-            const int hc0 = (n0 + wn * G::TN) / 2;
-            const int hl0 = wn * G::TN / 2;
-            if constexpr (EPI == EPI_SWIGLU_F32) {
-                // fp32 h; its per-tensor scale is taken over all routes afterwards
-                float* H = static_cast<float*>(g.C);
-#pragma unroll
-                for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r = rbase + mi * 16 + q;
-                        if (r < rows) {
-#pragma unroll
-                            for (int p = 0; p < G::NI / 2; ++p)
-                                H[(long)(row0 + r) * g.ldc + hc0 + p * 16 + lane % 16] = H_AT(mi, p, q);
+                            for (int t = 0; t < 4; ++t)
+                                v[t] = pack_bf16x2(acc[f][m][8 * hv + 2 * t] * fs, acc[f][m][8 * hv + 2 * t + 1] * fs);
+                            *reinterpret_cast<u32x4*>(base + 16 * f + 8 * hv) = v;
                         }
+                } else {
+                    // h columns wn0/2 + 16hh + i: gate acc[0], up acc[1]
+                    const long hrow = row0 + r;
+                    const int hc = wn0 / 2 + 16 * hh;
+                    float hv[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) hv[i] = silu(acc[0][m][i] * fs) * (acc[1][m][i] * fs);
+                    if constexpr (EPI == EPI_SWIGLU_BF16) {
+                        uint16_t* base = static_cast<uint16_t*>(g.C) + hrow * g.ldc + hc;
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            u32x4 v;
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) v[t] = pack_bf16x2(hv[8 * h2 + 2 * t], hv[8 * h2 + 2 * t + 1]);
+                            *reinterpret_cast<u32x4*>(base + 8 * h2) = v;
+                        }
+                    } else {   // EPI_SWIGLU_F32: fp32 h; the per-tensor scale is taken over all routes afterwards
+                        float* base = static_cast<float*>(g.C) + hrow * g.ldc + hc;
+#pragma unroll
+                        for (int h4 = 0; h4 < 4; ++h4)
+                            *reinterpret_cast<f32x4*>(base + 4 * h4) =
+                                f32x4{hv[4 * h4], hv[4 * h4 + 1], hv[4 * h4 + 2], hv[4 * h4 + 3]};
                     }
-            } else if constexpr (EPI == EPI_SWIGLU_BF16) {
-                constexpr int HW = BN / 2;               // h columns per tile
-                constexpr int ROWB = HW * 2 + 16;
-                uint8_t* Hs = smem;
-#pragma unroll
-                for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                    for (int p = 0; p < G::NI / 2; ++p)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            *reinterpret_cast<uint16_t*>(Hs + (rbase + mi * 16 + q) * ROWB +
-                                                         (hl0 + p * 16 + lane % 16) * 2) =
-                                f32_to_bf16(H_AT(mi, p, q));
-                __syncthreads();
-                constexpr int CPR = HW * 2 / 16;
-                for (int c = tid; c < BM * CPR; c += G::NT) {
-                    const int r = c / CPR, cc = c % CPR;
-                    if (r < rows)
-                        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.C) + (long)(row0 + r) * g.ldc +
-                                                  n0 / 2 + cc * 8) =
-                            *reinterpret_cast<const u32x4*>(Hs + r * ROWB + cc * 16);
                 }
-                __syncthreads();
-            } else {  // EPI_SWIGLU_Q128: the tile holds exactly one 128-column h block
-                static_assert(BN == 256, "Q128 epilogue needs 128 h columns per tile");
-                constexpr int ROWB = 128 + 16;
-                float* RA = reinterpret_cast<float*>(smem);          // [WN][BM]
-                uint8_t* Qs = smem + WN * BM * 4;
-                float rowmax[G::MI][4];
-#pragma unroll
-                for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float a = 0.0f;
-#pragma unroll
-                        for (int p = 0; p < G::NI / 2; ++p) a = fmaxf(a, fabsf(H_AT(mi, p, q)));
-#pragma unroll
-                        for (int off = 8; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-                        rowmax[mi][q] = a;
-                    }
-                if (lane % 16 == 0) {
-#pragma unroll
-                    for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) RA[wn * BM + rbase + mi * 16 + q] = rowmax[mi][q];
-                }
-                __syncthreads();
-#pragma unroll
-                for (int mi = 0; mi < G::MI; ++mi)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r = rbase + mi * 16 + q;
-                        float a = 0.0f;
-#pragma unroll
-                        for (int w = 0; w < WN; ++w) a = fmaxf(a, RA[w * BM + r]);
-                        const float s = scale_from_amax(a);
-#pragma unroll
-                        for (int p = 0; p < G::NI / 2; ++p)
-                            Qs[r * ROWB + hl0 + p * 16 + lane % 16] =
-                                (uint8_t)(f32x2_to_e4m3x2(H_AT(mi, p, q) / s, 0.0f) & 0xffu);
-                        if (wn == 0 && lane % 16 == 0 && r < rows)
-                            g.cscale[(long)(row0 + r) * (g.I / 128) + n0 / 256] = s;
-                    }
-                __syncthreads();
-                for (int c = tid; c < BM * 8; c += G::NT) {
-                    const int r = c / 8, cc = c % 8;
-                    if (r < rows)
-                        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(g.C) + (long)(row0 + r) * g.ldc +
-                                                  n0 / 2 + cc * 16) =
-                            *reinterpret_cast<const u32x4*>(Qs + r * ROWB + cc * 16);
-                }
-                __syncthreads();
             }
         }
+        if (!more) break;
+        L = Ln;
+        e = ne;
+        row0 = nrow0;
+        rows = nrows;
+        wn0 = nwn0;
+        ap = nap;
+        wp = nwp;
     }
 }
-
-#undef H_AT
 
 // ----------------------------------------------------------------------------
 
 static int g_num_cus = 0;
 
-static int num_cus() {
+int gemm_num_cus() {
     if (g_num_cus == 0) {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
@@ -475,40 +324,13 @@ static int num_cus() {
     return g_num_cus;
 }
 
-template <bool FP8, bool GATHER, int SC, int EPI, int BM, int BN, int WM, int WN, bool KTAIL = false>
-static hipError_t run_gemm(const GemmArgs& a, int wg_per_cu, hipStream_t st) {
-    using G = Gemm<FP8, GATHER, SC, EPI, BM, BN, WM, WN>;
-    auto kern = grouped_gemm_kernel<FP8, GATHER, SC, EPI, BM, BN, WM, WN, KTAIL>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
-        if (err != hipSuccess) return err;
-        attr_set = true;
-    }
-    const long total_bound = (long)a.max_tiles * (a.N / BN);
-    long grid = std::min<long>(total_bound, (long)num_cus() * wg_per_cu);
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(G::NT), G::LDS, st, a);
-    return hipGetLastError();
-}
-
-// 128 x 256 tiles (8 waves of 64 x 64: two waves per SIMD, so one wave's MFMAs
-// run while the other issues its loads) where the output width allows,
-// 128 x 128 tiles (4 waves of 64 x 64) otherwise.
 template <bool FP8, bool GATHER, int SC, int EPI>
-static hipError_t run_any(const GemmArgs& a, hipStream_t st) {
-    if (a.N % 256 == 0) {
-        if constexpr (SC == SC_BLOCK)   // per-block rescale needs more registers: 4 waves of 64 x 128
-            return run_gemm<FP8, GATHER, SC, EPI, 128, 256, 2, 2>(a, 1, st);
-        else
-            return run_gemm<FP8, GATHER, SC, EPI, 128, 256, 2, 4>(a, 1, st);
-    }
-    if constexpr (EPI == EPI_SWIGLU_Q128) {
-        return hipErrorInvalidValue;
-    } else {
-        return run_gemm<FP8, GATHER, SC, EPI, 128, 128, 2, 2>(a, 1, st);
-    }
+static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st) {
+    const long total_bound = (long)a.max_tiles * ((a.N + g32::BN - 1) / g32::BN);
+    long grid = std::min<long>(total_bound, (long)gemm_num_cus());
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI>), dim3((unsigned)grid), dim3(g32::NT), g32::LDS, st, a);
+    return hipGetLastError();
 }
 
 static GemmArgs gate_up_args(const FwdPlan& p, int elem) {
@@ -538,19 +360,19 @@ hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st) {
         GemmArgs a = gate_up_args(p, 2);
         a.C = p.h;
         a.ldc = p.I;
-        return run_any<false, true, SC_NONE, EPI_SWIGLU_BF16>(a, st);
+        return run_gemm32<false, true, SC_NONE, EPI_SWIGLU_BF16>(a, st);
     }
     if (p.quant == Q_FP8_TENSOR) {
         GemmArgs a = gate_up_args(p, 1);
         a.C = p.h;
         a.ldc = p.I;
-        return run_any<true, true, SC_TENSOR, EPI_SWIGLU_F32>(a, st);
+        return run_gemm32<true, true, SC_TENSOR, EPI_SWIGLU_F32>(a, st);
     }
     GemmArgs a = gate_up_args(p, 1);
     a.C = p.hq;
     a.ldc = p.I;
     a.cscale = p.sh;
-    return run_any<true, true, SC_BLOCK, EPI_SWIGLU_Q128>(a, st);
+    return launch_block_gate_up(a, st);
 }
 
 hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
@@ -575,14 +397,9 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     a.C = p.y;
     a.ldc = p.H;
     a.max_tiles = p.max_tiles;
-    if (p.quant == Q_BF16) return run_any<false, false, SC_NONE, EPI_Y_BF16>(a, st);
-    if (p.quant == Q_FP8_TENSOR) {
-        if (a.Kb % 128 != 0)   // I % 128 != 0: the last K step reads zeros past the row end
-            return a.N % 256 == 0 ? run_gemm<true, false, SC_TENSOR, EPI_Y_BF16, 128, 256, 2, 4, true>(a, 1, st)
-                                  : run_gemm<true, false, SC_TENSOR, EPI_Y_BF16, 128, 128, 2, 2, true>(a, 1, st);
-        return run_any<true, false, SC_TENSOR, EPI_Y_BF16>(a, st);
-    }
-    return run_any<true, false, SC_BLOCK, EPI_Y_BF16>(a, st);
+    if (p.quant == Q_BF16) return run_gemm32<false, false, SC_NONE, EPI_Y_BF16>(a, st);
+    if (p.quant == Q_FP8_TENSOR) return run_gemm32<true, false, SC_TENSOR, EPI_Y_BF16>(a, st);
+    return launch_block_down(a, st);
 }
 
 }  // namespace moe

@@ -1,0 +1,90 @@
+// Pieces shared by the two grouped-GEMM kernels (gemm.hip: bf16 and FP8
+// per-tensor; gemm_block.hip: FP8 128x128-blockwise).
+#pragma once
+#include "common.cuh"
+#include "launch.h"
+
+namespace moe {
+
+enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_F32 = 1, EPI_SWIGLU_Q128 = 2, EPI_Y_BF16 = 3 };
+enum Scale { SC_NONE = 0, SC_TENSOR = 1, SC_BLOCK = 2 };
+
+struct GemmArgs {
+    const uint8_t* A;       // row-major activations, lda bytes per row
+    long lda;
+    const int32_t* perm;    // gather: sorted row i -> token perm[i] / k; Down: output row perm[i]
+    int k;
+    const uint8_t* B;       // packed weights (layout.cuh), N packed rows, Kb bytes of K
+    int N;
+    int Kb;
+    const int32_t* tiles;   // [max_tiles][2] (expert, first sorted row)
+    const int32_t* ntiles;
+    const int32_t* offsets; // [E+1]
+    const float* sa;        // tensor: &scalar; block: [rows][sa_ld]
+    int sa_ld;
+    const float* sw;        // tensor: [E]; block: [E][K/128][nb_orig]
+    int nb_orig;
+    int I;                  // Gate/Up: h width
+    void* C;                // output
+    long ldc;               // output row stride in elements
+    float* cscale;          // Q128: [R][I/128]
+    int max_tiles;
+    int order;              // tile order: 0 column tile major, 1 row tile major
+};
+
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Read-only tables (tile map, offsets) are read through the constant address
+// space: with a uniform index that gives scalar loads, which count on lgkmcnt
+// and leave the hand-counted vmcnt waits of the GEMM loop undisturbed.
+__device__ __forceinline__ int32_t ld_const(const int32_t* p, long i) {
+    return ((const __attribute__((address_space(4))) int32_t*)(p))[i];
+}
+__device__ __forceinline__ float ld_const(const float* p, long i) {
+    return ((const __attribute__((address_space(4))) float*)(p))[i];
+}
+
+// s_waitcnt with vmcnt <= N and lgkmcnt == 0 (expcnt untouched)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
+}
+
+// s_waitcnt with vmcnt <= N only
+template <int N>
+__device__ __forceinline__ void wait_vm_only() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// s_waitcnt with lgkmcnt == 0 only
+__device__ __forceinline__ void wait_lgkm_only() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+
+// Persistent schedule: workgroup w runs on XCD w % 8 (round-robin dispatch);
+// each XCD walks one contiguous range of the tile space, so neighbouring tiles
+// share that XCD's L2.  With fewer than 8 workgroups there are fewer ranges, so
+// every range has a workgroup walking it.
+struct XcdRange {
+    int lo, hi, first, stride;
+};
+__device__ __forceinline__ XcdRange xcd_range(int total) {
+    const int nwg = gridDim.x;
+    const int nx = nwg < 8 ? nwg : 8;
+    const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
+    XcdRange r;
+    r.stride = nwg / nx + (xcd < nwg % nx ? 1 : 0);
+    r.lo = (int)((long)total * xcd / nx);
+    r.hi = (int)((long)total * (xcd + 1) / nx);
+    r.first = r.lo + slot;
+    return r;
+}
+
+int gemm_num_cus();
+
+hipError_t launch_block_gate_up(const GemmArgs& a, hipStream_t st);
+hipError_t launch_block_down(const GemmArgs& a, hipStream_t st);
+
+}  // namespace moe

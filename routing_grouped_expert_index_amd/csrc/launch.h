@@ -43,6 +43,7 @@ struct FwdPlan {
     const float* tw;            // [T, k]
     const int32_t* offsets;     // [E + 1]
     const int32_t* perm;        // [R]
+    const int32_t* route_pos;   // [R] inverse of perm
     const void* wgu;            // packed [E][2I][H]
     const void* wd;             // packed [E][H][I]
     const float* s_gu;          // per-tensor [E] | block [E][H/128][2I/128]
@@ -58,7 +59,7 @@ struct FwdPlan {
     void* h;                    // bf16 [R, I] (bf16) | fp32 [R, I] (fp8 paths, before requant)
     uint8_t* hq;                // e4m3 [R, I]
     float* sh;                  // block: [R, I/128]
-    uint16_t* y;                // bf16 [R, H] (grouped path, route order)
+    uint16_t* y;                // bf16 [R, H] (grouped path, sorted order)
     int max_tiles;
 };
 
@@ -68,7 +69,6 @@ int grouped_max_tiles(int R, int E);
 hipError_t launch_forward_init(const FwdPlan& p, bool build_tiles, hipStream_t st);
 hipError_t launch_quant_x(const FwdPlan& p, hipStream_t st);
 hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st);
-bool forward_needs_amax(const FwdPlan& p);   // the amax words must start at zero
 hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st);
 hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st);
 hipError_t launch_combine(const FwdPlan& p, hipStream_t st);

@@ -203,12 +203,12 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
     }
     if (!x || !out || !packed_gate_up || !packed_down || !routes->topk_ids || !routes->topk_weights)
         return fail(MOE_ERR_INVALID_ARG, "null pointer among x / out / weights / routes");
-    if (p == MOE_PATH_GROUPED && (!routes->expert_offsets || !routes->perm))
-        return fail(MOE_ERR_INVALID_ARG, "grouped path needs routes->expert_offsets and routes->perm");
+    if (p == MOE_PATH_GROUPED && (!routes->expert_offsets || !routes->perm || !routes->route_pos))
+        return fail(MOE_ERR_INVALID_ARG, "grouped path needs routes->expert_offsets, perm and route_pos");
     if (quant != MOE_BF16 && (!scales || !scales->w_gate_up_scale || !scales->w_down_scale))
         return fail(MOE_ERR_INVALID_ARG, "FP8 quantisation needs both weight scale arrays");
     const void* ptrs[] = {x, out, packed_gate_up, packed_down, routes->topk_ids, routes->topk_weights,
-                          routes->expert_offsets, routes->perm, ws};
+                          routes->expert_offsets, routes->perm, routes->route_pos, ws};
     for (const void* q : ptrs)
         if (q && !aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
     const Layout L = layout(T, H, I, E, k, quant, p);
@@ -222,6 +222,7 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
     P.tw = routes->topk_weights;
     P.offsets = routes->expert_offsets;
     P.perm = routes->perm;
+    P.route_pos = routes->route_pos;
     P.wgu = packed_gate_up;
     P.wd = packed_down;
     P.s_gu = quant != MOE_BF16 ? scales->w_gate_up_scale : nullptr;
@@ -258,16 +259,18 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
         if ((rc = hip_status((call), what)) != MOE_OK) return rc;       \
         mark(what);                                                     \
     } while (0)
-    if (grouped || moe::forward_needs_amax(P)) MOE_STEP(moe::launch_forward_init(P, grouped, st), "init");
-    if (quant != MOE_BF16) MOE_STEP(moe::launch_quant_x(P, st), "quant_x");
     if (grouped) {
+        MOE_STEP(moe::launch_forward_init(P, true, st), "init");
+        if (quant != MOE_BF16) MOE_STEP(moe::launch_quant_x(P, st), "quant_x");
         MOE_STEP(moe::launch_grouped_gate_up(P, st), "gate_up");
         if (quant == MOE_FP8_PER_TENSOR) MOE_STEP(moe::launch_quant_h(P, st), "quant_h");
         MOE_STEP(moe::launch_grouped_down(P, st), "down");
         MOE_STEP(moe::launch_combine(P, st), "combine");
     } else {
+        // per-tensor FP8 quantises inside the route-direct kernels
+        if (quant == MOE_FP8_BLOCK128) MOE_STEP(moe::launch_quant_x(P, st), "quant_x");
         MOE_STEP(moe::launch_route_direct_gate_up(P, st), "rd_gate_up");
-        if (quant != MOE_BF16) MOE_STEP(moe::launch_quant_h(P, st), "quant_h");
+        if (quant == MOE_FP8_BLOCK128) MOE_STEP(moe::launch_quant_h(P, st), "quant_h");
         MOE_STEP(moe::launch_route_direct_down(P, st), "rd_down_combine");
     }
 #undef MOE_STEP

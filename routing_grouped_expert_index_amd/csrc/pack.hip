@@ -1,56 +1,65 @@
-// One-time re-layout of the expert weights into the form the forward kernels
-// stream: every matrix is stored with its reduction (K) dimension contiguous,
-// so MFMA operands and GEMV lanes read 16-byte runs along K.
+// One-time re-layout of the expert weights into the packed form every forward
+// kernel reads (layout.cuh): per expert, K-sliced 2 KB blocks of 32 output
+// columns in MFMA operand-lane order, with the output columns permuted inside
+// groups of 64 so that each MFMA result lane holds contiguous outputs.
 //
-//  w_gate_up [E][H][2I]  ->  packed [E][2I][H]: packed row n' holds column
-//     c(n') of the source, where each group of 32 packed rows interleaves 16
-//     gate columns and the 16 up columns of the same h outputs:
-//        n' = 32*g + s, s < 16  -> gate column 16*g + s
-//                       s >= 16 -> up column   I + 16*g + (s - 16)
-//     so a 16-column MFMA block is all gate or all up and the SwiGLU pairs
-//     sit in the same lane of neighbouring accumulator tiles.
-//  w_down    [E][I][H]   ->  packed [E][H][I] (plain transpose).
+//  w_gate_up [E][H][2I] -> packed gate/up matrix (N = 2I, K = H)
+//  w_down    [E][I][H]  -> packed down matrix    (N = H,  K = I)
 //
-// The element is moved bit for bit (bf16 or e4m3); scales are not re-laid out.
+// Elements move bit for bit (bf16 or e4m3); scales keep the caller's layout.
 #include "common.cuh"
 #include "launch.h"
+#include "layout.cuh"
 
 namespace moe {
 
+constexpr int kPackSlicesPerWG = 8;
+
+// one workgroup: expert e, one 64-row permutation group, up to 8 K slices
 template <typename T, bool GATE_UP>
 __global__ void __launch_bounds__(256)
-pack_kernel(const T* __restrict__ src, T* __restrict__ dst, int K, int N, int I) {
-    // dst[e][n'][k] = src[e][k][col(n')]; one 64x64 (k, n') tile per workgroup
-    __shared__ T tile[64][65];
-    const int e = blockIdx.z;
-    const int k0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+pack_kernel(const T* __restrict__ src, uint8_t* __restrict__ dst, int K, int N, int I) {
+    constexpr int elem = sizeof(T);
+    constexpr int KS = kSliceBytes / elem;          // K values per slice
+    __shared__ T tile[KS][kGroupRows + 1];
+    const int e = blockIdx.x, G = blockIdx.y;
+    const int Kb = K * elem, NSL = Kb / kSliceBytes;
     const T* s = src + (size_t)e * K * N;
-    T* d = dst + (size_t)e * K * N;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int i = ty; i < 64; i += 4) {
-        const int np = n0 + tx, k = k0 + i;
-        if (np < N && k < K) {
-            int col = np;
-            if (GATE_UP) {
-                const int g = np >> 5, sl = np & 31;
-                col = sl < 16 ? 16 * g + sl : I + 16 * g + (sl - 16);
-            }
-            tile[i][tx] = s[(size_t)k * N + col];
+    uint8_t* d = dst + (size_t)e * N * Kb;
+    const int tid = threadIdx.x;
+    for (int sl = blockIdx.z * kPackSlicesPerWG; sl < min(NSL, (blockIdx.z + 1) * kPackSlicesPerWG); ++sl) {
+        // source tile: KS rows of K, the group's 64 source columns
+        for (int i = tid; i < KS * kGroupRows; i += 256) {
+            const int kl = i / kGroupRows, cl = i % kGroupRows;
+            int col;
+            if (GATE_UP) col = cl < 32 ? 32 * G + cl : I + 32 * G + (cl - 32);
+            else col = kGroupRows * G + cl;
+            tile[kl][cl] = s[(size_t)(sl * KS + kl) * N + col];
         }
-    }
-    __syncthreads();
-    for (int i = ty; i < 64; i += 4) {
-        const int np = n0 + i, k = k0 + tx;
-        if (np < N && k < K) d[(size_t)np * K + k] = tile[tx][i];
+        __syncthreads();
+        // 2 blocks (32 packed rows each) x 2 halves x 64 lanes of 16 bytes
+        for (int pc = tid; pc < 256; pc += 256) {
+            const int lane = pc & 63, q = (pc >> 6) & 1, gl = pc >> 7;
+            const int hh = lane >> 5, j = lane & 31;
+            const int p = 32 * gl + j;                                  // packed row in the group
+            const int cl = GATE_UP ? gate_up_col_of_packed(p, 32) : down_col_of_packed(p);
+            const int k0 = (32 * hh + 16 * q) / elem;
+            union { T v[16 / elem]; u32x4 u; } piece;
+#pragma unroll
+            for (int t = 0; t < 16 / elem; ++t) piece.v[t] = tile[k0 + t][cl];
+            const int g32 = 2 * G + gl;
+            *reinterpret_cast<u32x4*>(d + (((long)g32 * NSL + sl) * 2 + q) * 1024 + lane * 16) = piece.u;
+        }
+        __syncthreads();
     }
 }
 
 template <typename T, bool GATE_UP>
-static hipError_t launch_pack(const void* src, void* dst, int E, int K, int N, int I,
-                              hipStream_t st) {
-    dim3 grid(ceil_div(K, 64), ceil_div(N, 64), E);
-    hipLaunchKernelGGL((pack_kernel<T, GATE_UP>), grid, dim3(256), 0, st,
-                       static_cast<const T*>(src), static_cast<T*>(dst), K, N, I);
+static hipError_t launch_pack(const void* src, void* dst, int E, int K, int N, int I, hipStream_t st) {
+    const int NSL = K * (int)sizeof(T) / kSliceBytes;
+    dim3 grid(E, N / kGroupRows, ceil_div(NSL, kPackSlicesPerWG));
+    hipLaunchKernelGGL((pack_kernel<T, GATE_UP>), grid, dim3(256), 0, st, static_cast<const T*>(src),
+                       static_cast<uint8_t*>(dst), K, N, I);
     return hipGetLastError();
 }
 

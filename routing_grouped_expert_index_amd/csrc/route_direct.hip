@@ -8,190 +8,308 @@
 // quantisation, then Down, then a contiguous top-k reduction.
 //
 // On MI355X this path is bound by HBM: each route streams 3*H*I weight
-// elements and does 2 flops per element, so there is nothing for the matrix
-// cores to gain.  The kernels are built to keep as many 16-byte weight loads
-// in flight as possible:
-//  * Gate/Up: one wave per (route, JW h columns) streams 2*JW packed weight
-//    rows (K-contiguous) with 16-byte lane loads, dots them with x (or its e4m3
-//    codes) in fp32, reduces across the wave, applies SwiGLU and stores h
-//    (bf16, or fp32 for the FP8 requantisation that follows);
-//  * Down + combine: a workgroup of 4 waves owns 4 output columns of one token;
-//    wave w handles slots j = w, w+4, ...; 16 lanes share one weight row.  The
-//    four per-wave partial sums are added in wave order, so the top-k combine
-//    has a fixed summation order and needs no atomics and no y round trip.
+// elements and does 2 flops per element, so the matrix cores have nothing to
+// gain; the kernels keep as many contiguous weight loads in flight as they can.
+// Weights are read in the packed layout (layout.cuh) as whole 2 KB blocks of
+// 32 rows x 64 K bytes, one contiguous kilobyte per wave-wide load; lane
+// l = 32*hh + j accumulates row j over K bytes [32hh, 32hh+32) of every slice
+// and the two halves are added at the end.
+//  * Gate/Up: a workgroup owns (route, 32 h columns): the gate block and the up
+//    block of those columns; its NW waves split K, their partial sums meet in
+//    LDS in wave order, then SwiGLU and the h store (bf16, or fp32 ahead of the
+//    FP8 requantisation).
+//  * Down + combine: a workgroup owns (token, 32 output columns); its waves take
+//    (slot, K part) items in a fixed order, weight each route by its gate, and
+//    the wave partials are added in wave order: the top-k combine has a fixed
+//    summation order, needs no atomics and no y round trip.
+//  * FP8 per-tensor: the activation scales are whole-tensor maxima (x over
+//    [T, H], h over [T*k, I]); each workgroup takes the maximum itself (the
+//    tensors are a few kilobytes at decode sizes) and quantises its operands
+//    on the fly, so the path is two launches with nothing in between.
+//  * FP8 blockwise: x and h arrive quantised with their per-128 scales; each
+//    64-byte K slice lies in one scale block.
 #include "common.cuh"
 #include "launch.h"
+#include "layout.cuh"
 
 namespace moe {
 
-// dot of 16 bytes of weights with 16 bytes of activations
-template <bool FP8>
-__device__ __forceinline__ float dot16(const u32x4& w, const u32x4& a) {
-    float s = 0.0f;
-    if constexpr (!FP8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s = fmaf(__uint_as_float(w[i] << 16), __uint_as_float(a[i] << 16), s);
-            s = fmaf(__uint_as_float(w[i] & 0xffff0000u), __uint_as_float(a[i] & 0xffff0000u), s);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s = fmaf(e4m3_to_f32<0>(w[i]), e4m3_to_f32<0>(a[i]), s);
-            s = fmaf(e4m3_to_f32<1>(w[i]), e4m3_to_f32<1>(a[i]), s);
-            s = fmaf(e4m3_to_f32<2>(w[i]), e4m3_to_f32<2>(a[i]), s);
-            s = fmaf(e4m3_to_f32<3>(w[i]), e4m3_to_f32<3>(a[i]), s);
-        }
-    }
-    return s;
-}
+enum RdQuant { RD_BF16 = 0, RD_TENSOR = 1, RD_BLOCK = 2 };
 
 struct RdArgs {
-    const uint8_t* act;      // x bf16 [T,H] or xq e4m3 [T,H]
-    const float* sx;         // block: [T][H/128]; tensor: &s_x
+    const uint8_t* act;      // x bf16 [T,H] (bf16, per-tensor) or e4m3 codes [T,H] (block)
+    const float* sx;         // block: [T][H/128]
     const int32_t* ids;      // [T*k]
     const float* tw;         // [T*k]
-    const uint8_t* wgu;      // packed [E][2I][H]
-    const uint8_t* wd;       // packed [E][H][I]
+    const uint8_t* wgu;      // packed Gate/Up
+    const uint8_t* wd;       // packed Down
     const float* s_gu;
     const float* s_d;
-    const uint8_t* h;        // bf16 h [R][I] (bf16) or e4m3 hq [R][I] (fp8), Down input
-    const float* sh;         // block: [R][I/128]; tensor: &s_h
-    void* hout;              // Gate/Up output: bf16 [R][I] or fp32 [R][I]
+    const uint8_t* h;        // Down input: bf16 [R][I] | fp32 [R][I] (per-tensor) | e4m3 [R][I] (block)
+    const float* sh;         // block: [R][I/128]
+    void* hout;              // Gate/Up output: bf16 [R][I] | fp32 [R][I]
     uint16_t* out;           // [T][H]
     int T, H, I, E, k;
 };
 
-// ---------------------------------------------------------------- Gate/Up --
-template <bool FP8, int SC, int NCH, int JW>
-__global__ void __launch_bounds__(256)
-rd_gate_up_kernel(const RdArgs a) {
-    const int lane = lane_id(), wave = threadIdx.x / 64;
-    const int r = blockIdx.x;
-    const int j0 = (blockIdx.y * 4 + wave) * JW;
-    if (j0 >= a.I) return;
-    const int t = r / a.k, e = a.ids[r];
-    const int elem = FP8 ? 1 : 2;
-    const long Kb = (long)a.H * elem;
-    const int chunks = (int)(Kb / 16);
-    const uint8_t* xa = a.act + (long)t * Kb;
+// 8 values from 16 bytes of bf16
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4& w, float v[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
 
-    const uint8_t* wrow[2 * JW];
+// 16 values from 16 bytes of e4m3
+__device__ __forceinline__ void e4m3x16_to_f32(const u32x4& w, float v[16]) {
 #pragma unroll
-    for (int q = 0; q < JW; ++q) {
-        const int j = j0 + q;
-        const long gate_row = 32L * (j / 16) + (j % 16);
-        wrow[2 * q] = a.wgu + ((long)e * 2 * a.I + gate_row) * Kb;
-        wrow[2 * q + 1] = a.wgu + ((long)e * 2 * a.I + gate_row + 16) * Kb;
+    for (int i = 0; i < 4; ++i) {
+        v[4 * i] = e4m3_to_f32<0>(w[i]);
+        v[4 * i + 1] = e4m3_to_f32<1>(w[i]);
+        v[4 * i + 2] = e4m3_to_f32<2>(w[i]);
+        v[4 * i + 3] = e4m3_to_f32<3>(w[i]);
     }
-    u32x4 wv[2 * JW][NCH], xv[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = lane + 64 * i;
-        const bool ok = c < chunks;
-#pragma unroll
-        for (int q = 0; q < 2 * JW; ++q)
-            wv[q][i] = ok ? *reinterpret_cast<const u32x4*>(wrow[q] + c * 16) : u32x4{0, 0, 0, 0};
-        xv[i] = ok ? *reinterpret_cast<const u32x4*>(xa + c * 16) : u32x4{0, 0, 0, 0};
-    }
-    float acc[2 * JW];
-#pragma unroll
-    for (int q = 0; q < 2 * JW; ++q) acc[q] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = lane + 64 * i;
-        if constexpr (SC == 2) {
-            if (c < chunks) {
-                const int kb = c / 8;   // 16 e4m3 per chunk, 128 per block
-                const float s_a = a.sx[(long)t * (a.H / 128) + kb];
-#pragma unroll
-                for (int q = 0; q < 2 * JW; ++q) {
-                    const int j = j0 + q / 2;
-                    const int col = (q & 1) ? a.I + j : j;
-                    const float s_w = a.s_gu[((long)e * (a.H / 128) + kb) * (2 * a.I / 128) + col / 128];
-                    acc[q] = fmaf(dot16<FP8>(wv[q][i], xv[i]), s_a * s_w, acc[q]);
-                }
-            }
+}
+
+// v -> its e4m3 value under scale s (the code, decoded exactly; the caller
+// multiplies the dot product by s afterwards)
+__device__ __forceinline__ float e4m3_round(float v, float s) {
+    return e4m3_to_f32<0>(f32x2_to_e4m3x2(v / s, 0.0f));
+}
+
+// workgroup-wide max |v| over n values of T (bf16 bits or fp32), n % 8 == 0
+template <typename T, int NW>
+__device__ __forceinline__ float block_amax(const T* p, long n, float* sred) {
+    float m = 0.0f;
+    for (long i = (long)threadIdx.x * 8; i < n; i += 64L * NW * 8) {
+        float v[8];
+        if constexpr (sizeof(T) == 2) {
+            bf16x8_to_f32(*reinterpret_cast<const u32x4*>(p + i), v);
         } else {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(p + i);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(p + i + 4);
 #pragma unroll
-            for (int q = 0; q < 2 * JW; ++q) acc[q] += dot16<FP8>(wv[q][i], xv[i]);
+            for (int q = 0; q < 4; ++q) { v[q] = a[q]; v[4 + q] = b[q]; }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+    }
+    m = wave_max(m);
+    if (lane_id() == 0) sred[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, sred[w]);
+    return m;
+}
+
+// The lane's 32 activation K bytes of slice s as fp32 values (bf16: 16 values,
+// fp8: 32 e4m3 values, decoded), from a row of activations.
+template <int Q>
+__device__ __forceinline__ void act_slice(const uint8_t* row, int s, int hh, float xs, float v[32]) {
+    if constexpr (Q == RD_BF16) {
+        const uint8_t* p = row + s * 64 + hh * 32;
+        bf16x8_to_f32(*reinterpret_cast<const u32x4*>(p), v);
+        bf16x8_to_f32(*reinterpret_cast<const u32x4*>(p + 16), v + 8);
+    } else if constexpr (Q == RD_TENSOR) {
+        // bf16 source, K values 64s + 32hh + [0, 32), quantised with scale xs
+        const uint8_t* p = row + (s * 64 + hh * 32) * 2;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float t[8];
+            bf16x8_to_f32(*reinterpret_cast<const u32x4*>(p + 16 * c), t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[8 * c + i] = e4m3_round(t[i], xs);
+        }
+    } else {
+        const uint8_t* p = row + s * 64 + hh * 32;
+        e4m3x16_to_f32(*reinterpret_cast<const u32x4*>(p), v);
+        e4m3x16_to_f32(*reinterpret_cast<const u32x4*>(p + 16), v + 16);
+    }
+}
+
+// Same for an fp32 row (the per-tensor Down input h), quantised with scale hs.
+__device__ __forceinline__ void act_slice_f32(const float* row, int s, int hh, float hs, float v[32]) {
+    const float* p = row + s * 64 + hh * 32;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(p + 4 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * c + i] = e4m3_round(t[i], hs);
+    }
+}
+
+// dot of the lane's two weight halves of one slice with its activation values
+template <int Q>
+__device__ __forceinline__ float dot_slice(const u32x4 w[2], const float v[32]) {
+    float acc = 0.0f;
+    if constexpr (Q == RD_BF16) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float wf[8];
+            bf16x8_to_f32(w[q], wf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = fmaf(wf[i], v[8 * q + i], acc);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float wf[16];
+            e4m3x16_to_f32(w[q], wf);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc = fmaf(wf[i], v[16 * q + i], acc);
         }
     }
-#pragma unroll
-    for (int q = 0; q < 2 * JW; ++q) acc[q] = wave_sum(acc[q]);
-    if (SC == 1) {
-        const float f = a.sx[0] * a.s_gu[e];
-#pragma unroll
-        for (int q = 0; q < 2 * JW; ++q) acc[q] *= f;
+    return acc;
+}
+
+// ---------------------------------------------------------------- Gate/Up --
+template <int Q, int NW, int U>
+__global__ void __launch_bounds__(64 * NW)
+rd_gate_up_kernel(const RdArgs a) {
+    __shared__ float red[NW][2][32];
+    __shared__ float sred[NW];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int j = lane & 31, hh = lane >> 5;
+    const int r = blockIdx.x, pr = blockIdx.y;
+    const int G = pr;                            // 64-row group: gate block 2G, up block 2G+1
+    const int t = r / a.k, e = a.ids[r];
+    constexpr int elem = Q == RD_BF16 ? 2 : 1;
+    const int Kb = a.H * elem, NSL = Kb / kSliceBytes, per = NSL / NW, s0 = wave * per;
+    const long gstride = 32L * Kb;
+    const uint8_t* wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + lane * 16;
+    const uint8_t* wu = wg + gstride;
+    const uint8_t* xrow = a.act + (long)t * a.H * (Q == RD_BLOCK ? 1 : 2);
+
+    float xs = 1.0f;
+    if constexpr (Q == RD_TENSOR)
+        xs = scale_from_amax(block_amax<uint16_t, NW>(reinterpret_cast<const uint16_t*>(a.act),
+                                                       (long)a.T * a.H, sred));
+    int cg = 0, cu = 0;           // blockwise: scale columns of the gate and up blocks
+    if constexpr (Q == RD_BLOCK) {
+        cg = (32 * G) / 128;
+        cu = (a.I + 32 * G) / 128;
     }
-    if (lane < JW) {
-        float hv = 0.0f;
+
+    float accg = 0.0f, accu = 0.0f;
+    for (int s = s0; s < s0 + per; s += U) {
+        u32x4 vg[U][2], vu[U][2];
 #pragma unroll
-        for (int q = 0; q < JW; ++q)
-            if (q == lane) hv = silu(acc[2 * q]) * acc[2 * q + 1];
-        const int j = j0 + lane;
-        if (j < a.I) {
-            if constexpr (!FP8) {
-                static_cast<uint16_t*>(a.hout)[(long)r * a.I + j] = f32_to_bf16(hv);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                vg[u][q] = *reinterpret_cast<const u32x4*>(wg + (long)(s + u) * 2048 + q * 1024);
+                vu[u][q] = *reinterpret_cast<const u32x4*>(wu + (long)(s + u) * 2048 + q * 1024);
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v[32];
+            act_slice<Q>(xrow, s + u, hh, xs, v);
+            const float dg = dot_slice<Q>(vg[u], v), du = dot_slice<Q>(vu[u], v);
+            if constexpr (Q == RD_BLOCK) {
+                const int kb = (s + u) / 2;   // 128-deep scale block
+                const float sa = a.sx[(long)t * (a.H / 128) + kb];
+                const float* swr = a.s_gu + ((long)e * (a.H / 128) + kb) * (2 * a.I / 128);
+                accg = fmaf(dg, sa * swr[cg], accg);
+                accu = fmaf(du, sa * swr[cu], accu);
             } else {
-                static_cast<float*>(a.hout)[(long)r * a.I + j] = hv;   // requantised afterwards
+                accg += dg;
+                accu += du;
             }
         }
+    }
+    accg += __shfl_xor(accg, 32);
+    accu += __shfl_xor(accu, 32);
+    if (hh == 0) {
+        red[wave][0][j] = accg;
+        red[wave][1][j] = accu;
+    }
+    __syncthreads();
+    if (wave == 0 && hh == 0) {
+        float gv = 0.0f, uv = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            gv += red[w][0][j];
+            uv += red[w][1][j];
+        }
+        if constexpr (Q == RD_TENSOR) {
+            const float fsc = xs * a.s_gu[e];
+            gv *= fsc;
+            uv *= fsc;
+        }
+        const float hv = silu(gv) * uv;
+        // row j of the pair's blocks is h column 32G + 16hh' + 4a + b, j = 8a + 4hh' + b
+        const int c = 32 * G + 16 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3);
+        if constexpr (Q == RD_BF16)
+            static_cast<uint16_t*>(a.hout)[(long)r * a.I + c] = f32_to_bf16(hv);
+        else
+            static_cast<float*>(a.hout)[(long)r * a.I + c] = hv;
     }
 }
 
 // ------------------------------------------------------------ Down+combine --
-template <bool FP8, int SC, int NCH>
-__global__ void __launch_bounds__(256)
+template <int Q, int NW, int KP, int U>
+__global__ void __launch_bounds__(64 * NW)
 rd_down_combine_kernel(const RdArgs a) {
-    __shared__ float part[4][4];
-    const int lane = lane_id(), wave = threadIdx.x / 64;
-    const int t = blockIdx.x;
-    const int grp = lane / 16, sub = lane % 16;
-    const int n = blockIdx.y * 4 + grp;          // output column of this 16-lane group
-    const int elem = FP8 ? 1 : 2;
-    const long Kb = (long)a.I * elem;
-    const int chunks = (int)(Kb / 16);
-    float o = 0.0f;
-    for (int j = wave; j < a.k; j += 4) {
-        const int r = t * a.k + j;
-        const int e = a.ids[r];
-        const uint8_t* wrow = a.wd + ((long)e * a.H + n) * Kb;
-        const uint8_t* hrow = a.h + (long)r * Kb;
-        u32x4 wv[NCH], hv[NCH];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = sub + 16 * i;
-            const bool ok = c < chunks;
-            wv[i] = ok ? *reinterpret_cast<const u32x4*>(wrow + c * 16) : u32x4{0, 0, 0, 0};
-            hv[i] = ok ? *reinterpret_cast<const u32x4*>(hrow + c * 16) : u32x4{0, 0, 0, 0};
-        }
+    __shared__ float red[NW][32];
+    __shared__ float sred[NW];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int hh = lane >> 5;
+    const int t = blockIdx.x, g32 = blockIdx.y;
+    constexpr int elem = Q == RD_BF16 ? 2 : 1;
+    const int Kb = a.I * elem, NSL = Kb / kSliceBytes, per = NSL / KP;
+    const int n0 = down_col_of_packed(32 * g32);   // all 32 rows lie in one 128-column block
+
+    float hs = 1.0f;
+    if constexpr (Q == RD_TENSOR)
+        hs = scale_from_amax(block_amax<float, NW>(reinterpret_cast<const float*>(a.h),
+                                                    (long)a.T * a.k * a.I, sred));
+    float acc = 0.0f;
+    const int items = a.k * KP;
+    for (int it = wave; it < items; it += NW) {
+        const int jj = it / KP, kp = it - jj * KP;
+        const int r = t * a.k + jj, e = a.ids[r];
+        const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + lane * 16;
+        const uint8_t* hrow = a.h + (long)r * a.I * (Q == RD_TENSOR ? 4 : elem);
         float y = 0.0f;
+        for (int s = kp * per; s < (kp + 1) * per; s += U) {
+            u32x4 vw[U][2];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = sub + 16 * i;
-            if constexpr (SC == 2) {
-                if (c < chunks) {
-                    const int kb = c / 8;
-                    const float s = a.sh[(long)r * (a.I / 128) + kb] *
-                                    a.s_d[((long)e * (a.I / 128) + kb) * (a.H / 128) + n / 128];
-                    y = fmaf(dot16<FP8>(wv[i], hv[i]), s, y);
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    vw[u][q] = *reinterpret_cast<const u32x4*>(wb + (long)(s + u) * 2048 + q * 1024);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float v[32];
+                if constexpr (Q == RD_TENSOR)
+                    act_slice_f32(reinterpret_cast<const float*>(hrow), s + u, hh, hs, v);
+                else
+                    act_slice<Q>(hrow, s + u, hh, 1.0f, v);
+                const float d = dot_slice<Q>(vw[u], v);
+                if constexpr (Q == RD_BLOCK) {
+                    const int kb = (s + u) / 2;
+                    const float sc = a.sh[(long)r * (a.I / 128) + kb] *
+                                     a.s_d[((long)e * (a.I / 128) + kb) * (a.H / 128) + n0 / 128];
+                    y = fmaf(d, sc, y);
+                } else {
+                    y += d;
                 }
-            } else {
-                y += dot16<FP8>(wv[i], hv[i]);
             }
         }
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) y += __shfl_xor(y, off);
-        if (SC == 1) y *= a.sh[0] * a.s_d[e];
-        o = fmaf(a.tw[r], y, o);
+        float gw = a.tw[r];
+        if constexpr (Q == RD_TENSOR) gw *= hs * a.s_d[e];
+        acc = fmaf(gw, y, acc);
     }
-    if (sub == 0) part[wave][grp] = o;
+    acc += __shfl_xor(acc, 32);
+    if (hh == 0) red[wave][lane] = acc;
     __syncthreads();
-    if (threadIdx.x < 4) {
-        const int g2 = threadIdx.x;
-        const float s = ((part[0][g2] + part[1][g2]) + part[2][g2]) + part[3][g2];
-        a.out[(long)t * a.H + blockIdx.y * 4 + g2] = f32_to_bf16(s);
+    if (wave == 0 && hh == 0) {
+        float o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) o += red[w][lane];
+        a.out[(long)t * a.H + down_col_of_packed(32 * g32 + lane)] = f32_to_bf16(o);
     }
 }
 
@@ -199,74 +317,104 @@ rd_down_combine_kernel(const RdArgs a) {
 
 static RdArgs rd_args(const FwdPlan& p) {
     RdArgs a{};
-    const bool fp8 = p.quant != Q_BF16;
-    a.act = fp8 ? p.xq : reinterpret_cast<const uint8_t*>(p.x);
-    a.sx = p.quant == Q_FP8_BLOCK ? p.sx : &p.scal[0];
+    a.act = p.quant == Q_FP8_BLOCK ? p.xq : reinterpret_cast<const uint8_t*>(p.x);
+    a.sx = p.sx;
     a.ids = p.ids;
     a.tw = p.tw;
     a.wgu = static_cast<const uint8_t*>(p.wgu);
     a.wd = static_cast<const uint8_t*>(p.wd);
     a.s_gu = p.s_gu;
     a.s_d = p.s_d;
-    a.h = fp8 ? p.hq : static_cast<const uint8_t*>(p.h);
-    a.sh = p.quant == Q_FP8_BLOCK ? p.sh : &p.scal[1];
+    a.h = p.quant == Q_FP8_BLOCK ? p.hq : static_cast<const uint8_t*>(p.h);
+    a.sh = p.sh;
     a.hout = p.h;
     a.out = p.out;
     a.T = p.T; a.H = p.H; a.I = p.I; a.E = p.E; a.k = p.k;
     return a;
 }
 
-template <bool FP8, int SC, int JW>
-static hipError_t rd_gu(const RdArgs& a, int nch, hipStream_t st) {
-    dim3 grid(a.T * a.k, ceil_div(a.I, 4 * JW));
-    switch (nch) {
-        case 1: hipLaunchKernelGGL((rd_gate_up_kernel<FP8, SC, 1, JW>), grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((rd_gate_up_kernel<FP8, SC, 2, JW>), grid, dim3(256), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((rd_gate_up_kernel<FP8, SC, 4, JW>), grid, dim3(256), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((rd_gate_up_kernel<FP8, SC, 8, JW>), grid, dim3(256), 0, st, a); break;
-        default: return hipErrorInvalidValue;
+static int largest_unroll(int n) { return n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1); }
+
+// Waves per Gate/Up workgroup: enough waves in total to keep HBM busy (about
+// 2048), K split evenly (NSL % NW == 0), at most 16.
+static int rd_waves(long groups, int NSL) {
+    int nw = 1;
+    while (nw < 16 && groups * nw * 2 <= 2048 && NSL % (nw * 2) == 0) nw *= 2;
+    return nw;
+}
+
+template <int Q, int NW>
+static hipError_t rd_gu_nw(const RdArgs& a, int U, hipStream_t st) {
+    dim3 grid(a.T * a.k, a.I / 32);
+    switch (U) {
+        case 4: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 4>), grid, dim3(64 * NW), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 2>), grid, dim3(64 * NW), 0, st, a); break;
+        default: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 1>), grid, dim3(64 * NW), 0, st, a); break;
     }
     return hipGetLastError();
 }
 
-static int pow2_at_least(int v) {
-    int p = 1;
-    while (p < v) p <<= 1;
-    return p;
+template <int Q>
+static hipError_t rd_gu(const RdArgs& a, hipStream_t st) {
+    const int elem = Q == RD_BF16 ? 2 : 1;
+    const int NSL = a.H * elem / kSliceBytes;
+    const int nw = rd_waves((long)a.T * a.k * (a.I / 32), NSL);
+    const int U = largest_unroll(NSL / nw);
+    switch (nw) {
+        case 1: return rd_gu_nw<Q, 1>(a, U, st);
+        case 2: return rd_gu_nw<Q, 2>(a, U, st);
+        case 4: return rd_gu_nw<Q, 4>(a, U, st);
+        case 8: return rd_gu_nw<Q, 8>(a, U, st);
+        default: return rd_gu_nw<Q, 16>(a, U, st);
+    }
 }
 
 hipError_t launch_route_direct_gate_up(const FwdPlan& p, hipStream_t st) {
     const RdArgs a = rd_args(p);
-    const int elem = p.quant == Q_BF16 ? 2 : 1;
-    const int nch = pow2_at_least(ceil_div(p.H * elem / 16, 64));
-    if (nch > 8) return hipErrorInvalidValue;
-    const bool wide = (long)p.T * p.k * p.I >= 8192;   // enough waves: 2 h columns per wave
-    if (p.quant == Q_BF16) return wide ? rd_gu<false, 0, 2>(a, nch, st) : rd_gu<false, 0, 1>(a, nch, st);
-    if (p.quant == Q_FP8_TENSOR) return wide ? rd_gu<true, 1, 2>(a, nch, st) : rd_gu<true, 1, 1>(a, nch, st);
-    return wide ? rd_gu<true, 2, 2>(a, nch, st) : rd_gu<true, 2, 1>(a, nch, st);
+    if (p.quant == Q_BF16) return rd_gu<RD_BF16>(a, st);
+    if (p.quant == Q_FP8_TENSOR) return rd_gu<RD_TENSOR>(a, st);
+    return rd_gu<RD_BLOCK>(a, st);
 }
 
-template <bool FP8, int SC>
-static hipError_t rd_dn(const RdArgs& a, int nch, hipStream_t st) {
-    dim3 grid(a.T, a.H / 4);
-    switch (nch) {
-        case 1: hipLaunchKernelGGL((rd_down_combine_kernel<FP8, SC, 1>), grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((rd_down_combine_kernel<FP8, SC, 2>), grid, dim3(256), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((rd_down_combine_kernel<FP8, SC, 4>), grid, dim3(256), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((rd_down_combine_kernel<FP8, SC, 8>), grid, dim3(256), 0, st, a); break;
-        default: return hipErrorInvalidValue;
+template <int Q, int NW, int KP>
+static hipError_t rd_dn_kp(const RdArgs& a, int U, hipStream_t st) {
+    dim3 grid(a.T, a.H / 32);
+    switch (U) {
+        case 4: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 4>), grid, dim3(64 * NW), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 2>), grid, dim3(64 * NW), 0, st, a); break;
+        default: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 1>), grid, dim3(64 * NW), 0, st, a); break;
     }
     return hipGetLastError();
 }
 
+template <int Q, int NW>
+static hipError_t rd_dn_nw(const RdArgs& a, int kp, int NSL, hipStream_t st) {
+    const int U = largest_unroll(NSL / kp);
+    switch (kp) {
+        case 1: return rd_dn_kp<Q, NW, 1>(a, U, st);
+        case 2: return rd_dn_kp<Q, NW, 2>(a, U, st);
+        default: return rd_dn_kp<Q, NW, 4>(a, U, st);
+    }
+}
+
+// K parts per route: up to 4, dividing NSL, while (slot, part) items <= 16;
+// 16 waves per workgroup when the grid is small and there are items for all
+template <int Q>
+static hipError_t rd_dn(const RdArgs& a, hipStream_t st) {
+    const int elem = Q == RD_BF16 ? 2 : 1;
+    const int NSL = a.I * elem / kSliceBytes;
+    int kp = 1;
+    while (kp < 4 && NSL % (kp * 2) == 0 && a.k * kp * 2 <= 16) kp *= 2;
+    const long wgs = (long)a.T * (a.H / 32);
+    if (wgs * 8 < 2048 && a.k * kp >= 16) return rd_dn_nw<Q, 16>(a, kp, NSL, st);
+    return rd_dn_nw<Q, 8>(a, kp, NSL, st);
+}
+
 hipError_t launch_route_direct_down(const FwdPlan& p, hipStream_t st) {
     const RdArgs a = rd_args(p);
-    const int elem = p.quant == Q_BF16 ? 2 : 1;
-    const int nch = pow2_at_least(ceil_div(p.I * elem / 16, 16));
-    if (nch > 8) return hipErrorInvalidValue;
-    if (p.quant == Q_BF16) return rd_dn<false, 0>(a, nch, st);
-    if (p.quant == Q_FP8_TENSOR) return rd_dn<true, 1>(a, nch, st);
-    return rd_dn<true, 2>(a, nch, st);
+    if (p.quant == Q_BF16) return rd_dn<RD_BF16>(a, st);
+    if (p.quant == Q_FP8_TENSOR) return rd_dn<RD_TENSOR>(a, st);
+    return rd_dn<RD_BLOCK>(a, st);
 }
 
 }  // namespace moe
