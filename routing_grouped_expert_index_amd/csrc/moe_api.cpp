@@ -39,9 +39,12 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 // that range, expressed in routes: T <= 4 and T*k <= E/2.
 constexpr int kRouteDirectMaxTokens = 4;
 
-bool rd_shape_ok(int H, int I, int quant) {
+// Route-direct kernels stage one activation row (H * elem bytes) in LDS, and
+// for per-tensor FP8 also the k rows of quantised h of a token (k * I bytes).
+bool rd_shape_ok(int H, int I, int k, int quant) {
     const int elem = quant == MOE_BF16 ? 2 : 1;
-    return (long)H * elem <= 8192 && (long)I * elem <= 2048;
+    if ((long)H * elem > 8192 || (long)I * elem > 2048) return false;
+    return quant != MOE_FP8_PER_TENSOR || (long)k * I <= 32768;
 }
 
 int check_shape(int T, int H, int I, int E, int k, int quant) {
@@ -64,12 +67,13 @@ int check_shape(int T, int H, int I, int E, int k, int quant) {
 int resolve_path(int T, int H, int I, int E, int k, int quant, int path) {
     if (path == MOE_PATH_AUTO) {
         const bool small = T <= kRouteDirectMaxTokens && 2L * T * k <= E;
-        return (small && rd_shape_ok(H, I, quant)) ? MOE_PATH_ROUTE_DIRECT : MOE_PATH_GROUPED;
+        return (small && rd_shape_ok(H, I, k, quant)) ? MOE_PATH_ROUTE_DIRECT : MOE_PATH_GROUPED;
     }
     if (path == MOE_PATH_GROUPED) return path;
     if (path == MOE_PATH_ROUTE_DIRECT) {
-        if (!rd_shape_ok(H, I, quant))
-            return fail(MOE_ERR_UNSUPPORTED, "route-direct path: H*elem <= 8192 and I*elem <= 2048 bytes");
+        if (!rd_shape_ok(H, I, k, quant))
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "route-direct path: H*elem <= 8192 and I*elem <= 2048 bytes (per-tensor FP8: k*I <= 32768)");
         return path;
     }
     return fail(MOE_ERR_INVALID_ARG, "unknown path %d", path);

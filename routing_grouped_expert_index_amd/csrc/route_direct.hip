@@ -32,6 +32,9 @@
 #include "launch.h"
 #include "layout.cuh"
 
+#include <algorithm>
+#include <initializer_list>
+
 namespace moe {
 
 enum RdQuant { RD_BF16 = 0, RD_TENSOR = 1, RD_BLOCK = 2 };
@@ -72,11 +75,6 @@ __device__ __forceinline__ void e4m3x16_to_f32(const u32x4& w, float v[16]) {
     }
 }
 
-// v -> its e4m3 value under scale s (the code, decoded exactly; the caller
-// multiplies the dot product by s afterwards)
-__device__ __forceinline__ float e4m3_round(float v, float s) {
-    return e4m3_to_f32<0>(f32x2_to_e4m3x2(v / s, 0.0f));
-}
 
 // workgroup-wide max |v| over n values of T (bf16 bits or fp32), n % 8 == 0
 template <typename T, int NW>
@@ -104,47 +102,68 @@ __device__ __forceinline__ float block_amax(const T* p, long n, float* sred) {
     return m;
 }
 
-// The lane's 32 activation K bytes of slice s as fp32 values (bf16: 16 values,
-// fp8: 32 e4m3 values, decoded), from a row of activations.
-template <int Q>
-__device__ __forceinline__ void act_slice(const uint8_t* row, int s, int hh, float xs, float v[32]) {
-    if constexpr (Q == RD_BF16) {
-        const uint8_t* p = row + s * 64 + hh * 32;
-        bf16x8_to_f32(*reinterpret_cast<const u32x4*>(p), v);
-        bf16x8_to_f32(*reinterpret_cast<const u32x4*>(p + 16), v + 8);
-    } else if constexpr (Q == RD_TENSOR) {
-        // bf16 source, K values 64s + 32hh + [0, 32), quantised with scale xs
-        const uint8_t* p = row + (s * 64 + hh * 32) * 2;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float t[8];
-            bf16x8_to_f32(*reinterpret_cast<const u32x4*>(p + 16 * c), t);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[8 * c + i] = e4m3_round(t[i], xs);
-        }
+// Activation rows are staged in LDS once per workgroup (every lane of a
+// 32-row weight block needs the same activation values): bf16 values, or e4m3
+// codes (quantised here for per-tensor FP8, copied for blockwise).
+constexpr int kRdActBytes = 8192;          // one activation row: H * elem <= 8192
+constexpr int kRdHBytes = 32768;           // per-tensor Down: the token's k rows of h codes
+
+// The lane's 32 activation bytes of slice s from an LDS row, as fp32 values
+// (bf16: 16 values; e4m3: 32 values).
+template <bool FP8>
+__device__ __forceinline__ void lds_act_slice(const uint8_t* row, int s, int hh, float v[32]) {
+    const uint8_t* p = row + s * 64 + hh * 32;
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(p + 16);
+    if constexpr (!FP8) {
+        bf16x8_to_f32(w0, v);
+        bf16x8_to_f32(w1, v + 8);
     } else {
-        const uint8_t* p = row + s * 64 + hh * 32;
-        e4m3x16_to_f32(*reinterpret_cast<const u32x4*>(p), v);
-        e4m3x16_to_f32(*reinterpret_cast<const u32x4*>(p + 16), v + 16);
+        e4m3x16_to_f32(w0, v);
+        e4m3x16_to_f32(w1, v + 16);
     }
 }
 
-// Same for an fp32 row (the per-tensor Down input h), quantised with scale hs.
-__device__ __forceinline__ void act_slice_f32(const float* row, int s, int hh, float hs, float v[32]) {
-    const float* p = row + s * 64 + hh * 32;
+// Global-memory variant for activation rows that are not staged (bf16 and
+// blockwise Down inputs).
+template <bool FP8>
+__device__ __forceinline__ void glb_act_slice(const uint8_t* row, int s, int hh, float v[32]) {
+    lds_act_slice<FP8>(row, s, hh, v);
+}
+
+// copy n bytes (n % 16 == 0) of a global row into LDS, whole workgroup
+template <int NW>
+__device__ __forceinline__ void stage_row(uint8_t* dst, const uint8_t* src, int n) {
+    for (int i = threadIdx.x * 16; i < n; i += 64 * NW * 16)
+        *reinterpret_cast<u32x4*>(dst + i) = *reinterpret_cast<const u32x4*>(src + i);
+}
+
+// quantise n values (n % 8 == 0) of a bf16 (or fp32) row with scale s into e4m3
+// codes in LDS, whole workgroup
+template <typename T, int NW>
+__device__ __forceinline__ void quant_row(uint8_t* dst, const T* src, int n, float s) {
+    for (int i = threadIdx.x * 8; i < n; i += 64 * NW * 8) {
+        float v[8];
+        if constexpr (sizeof(T) == 2) {
+            bf16x8_to_f32(*reinterpret_cast<const u32x4*>(src + i), v);
+        } else {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(src + i);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(src + i + 4);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(p + 4 * c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[4 * c + i] = e4m3_round(t[i], hs);
+            for (int q = 0; q < 4; ++q) { v[q] = a[q]; v[4 + q] = b[q]; }
+        }
+        uint2 c;
+        c.x = f32x4_to_e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+        c.y = f32x4_to_e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
+        *reinterpret_cast<uint2*>(dst + i) = c;
     }
 }
 
 // dot of the lane's two weight halves of one slice with its activation values
-template <int Q>
+template <bool FP8>
 __device__ __forceinline__ float dot_slice(const u32x4 w[2], const float v[32]) {
     float acc = 0.0f;
-    if constexpr (Q == RD_BF16) {
+    if constexpr (!FP8) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             float wf[8];
@@ -168,24 +187,41 @@ __device__ __forceinline__ float dot_slice(const u32x4 w[2], const float v[32]) 
 template <int Q, int NW, int U>
 __global__ void __launch_bounds__(64 * NW)
 rd_gate_up_kernel(const RdArgs a) {
+    constexpr bool FP8 = Q != RD_BF16;
+    __shared__ __attribute__((aligned(16))) uint8_t xrow[kRdActBytes];
     __shared__ float red[NW][2][32];
     __shared__ float sred[NW];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int j = lane & 31, hh = lane >> 5;
-    const int r = blockIdx.x, pr = blockIdx.y;
-    const int G = pr;                            // 64-row group: gate block 2G, up block 2G+1
+    const int r = blockIdx.x, G = blockIdx.y;   // route; 64-row group (gate block 2G, up block 2G+1)
     const int t = r / a.k, e = a.ids[r];
-    constexpr int elem = Q == RD_BF16 ? 2 : 1;
+    constexpr int elem = FP8 ? 1 : 2;
     const int Kb = a.H * elem, NSL = Kb / kSliceBytes, per = NSL / NW, s0 = wave * per;
     const long gstride = 32L * Kb;
     const uint8_t* wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + lane * 16;
     const uint8_t* wu = wg + gstride;
-    const uint8_t* xrow = a.act + (long)t * a.H * (Q == RD_BLOCK ? 1 : 2);
+
+    u32x4 vg[U][2], vu[U][2];
+    auto load_batch = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                vg[u][q] = *reinterpret_cast<const u32x4*>(wg + (long)(s + u) * 2048 + q * 1024);
+                vu[u][q] = *reinterpret_cast<const u32x4*>(wu + (long)(s + u) * 2048 + q * 1024);
+            }
+    };
+    load_batch(s0);   // the weight stream starts before the activation row is staged
 
     float xs = 1.0f;
-    if constexpr (Q == RD_TENSOR)
-        xs = scale_from_amax(block_amax<uint16_t, NW>(reinterpret_cast<const uint16_t*>(a.act),
-                                                       (long)a.T * a.H, sred));
+    if constexpr (Q == RD_TENSOR) {
+        const uint16_t* x = reinterpret_cast<const uint16_t*>(a.act);
+        xs = scale_from_amax(block_amax<uint16_t, NW>(x, (long)a.T * a.H, sred));
+        quant_row<uint16_t, NW>(xrow, x + (long)t * a.H, a.H, xs);
+    } else {
+        stage_row<NW>(xrow, a.act + (long)t * Kb, Kb);
+    }
+    __syncthreads();
     int cg = 0, cu = 0;           // blockwise: scale columns of the gate and up blocks
     if constexpr (Q == RD_BLOCK) {
         cg = (32 * G) / 128;
@@ -194,19 +230,12 @@ rd_gate_up_kernel(const RdArgs a) {
 
     float accg = 0.0f, accu = 0.0f;
     for (int s = s0; s < s0 + per; s += U) {
-        u32x4 vg[U][2], vu[U][2];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                vg[u][q] = *reinterpret_cast<const u32x4*>(wg + (long)(s + u) * 2048 + q * 1024);
-                vu[u][q] = *reinterpret_cast<const u32x4*>(wu + (long)(s + u) * 2048 + q * 1024);
-            }
+        if (s != s0) load_batch(s);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float v[32];
-            act_slice<Q>(xrow, s + u, hh, xs, v);
-            const float dg = dot_slice<Q>(vg[u], v), du = dot_slice<Q>(vu[u], v);
+            lds_act_slice<FP8>(xrow, s + u, hh, v);
+            const float dg = dot_slice<FP8>(vg[u], v), du = dot_slice<FP8>(vu[u], v);
             if constexpr (Q == RD_BLOCK) {
                 const int kb = (s + u) / 2;   // 128-deep scale block
                 const float sa = a.sx[(long)t * (a.H / 128) + kb];
@@ -252,26 +281,31 @@ rd_gate_up_kernel(const RdArgs a) {
 template <int Q, int NW, int KP, int U>
 __global__ void __launch_bounds__(64 * NW)
 rd_down_combine_kernel(const RdArgs a) {
+    constexpr bool FP8 = Q != RD_BF16;
+    __shared__ __attribute__((aligned(16))) uint8_t hrows[Q == RD_TENSOR ? kRdHBytes : 16];
     __shared__ float red[NW][32];
     __shared__ float sred[NW];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int hh = lane >> 5;
     const int t = blockIdx.x, g32 = blockIdx.y;
-    constexpr int elem = Q == RD_BF16 ? 2 : 1;
+    constexpr int elem = FP8 ? 1 : 2;
     const int Kb = a.I * elem, NSL = Kb / kSliceBytes, per = NSL / KP;
     const int n0 = down_col_of_packed(32 * g32);   // all 32 rows lie in one 128-column block
 
     float hs = 1.0f;
-    if constexpr (Q == RD_TENSOR)
-        hs = scale_from_amax(block_amax<float, NW>(reinterpret_cast<const float*>(a.h),
-                                                    (long)a.T * a.k * a.I, sred));
+    if constexpr (Q == RD_TENSOR) {
+        const float* h = reinterpret_cast<const float*>(a.h);
+        hs = scale_from_amax(block_amax<float, NW>(h, (long)a.T * a.k * a.I, sred));
+        quant_row<float, NW>(hrows, h + (long)t * a.k * a.I, a.k * a.I, hs);
+        __syncthreads();
+    }
     float acc = 0.0f;
     const int items = a.k * KP;
     for (int it = wave; it < items; it += NW) {
         const int jj = it / KP, kp = it - jj * KP;
         const int r = t * a.k + jj, e = a.ids[r];
         const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + lane * 16;
-        const uint8_t* hrow = a.h + (long)r * a.I * (Q == RD_TENSOR ? 4 : elem);
+        const uint8_t* hrow = Q == RD_TENSOR ? hrows + (long)jj * Kb : a.h + (long)r * Kb;
         float y = 0.0f;
         for (int s = kp * per; s < (kp + 1) * per; s += U) {
             u32x4 vw[U][2];
@@ -284,10 +318,10 @@ rd_down_combine_kernel(const RdArgs a) {
             for (int u = 0; u < U; ++u) {
                 float v[32];
                 if constexpr (Q == RD_TENSOR)
-                    act_slice_f32(reinterpret_cast<const float*>(hrow), s + u, hh, hs, v);
+                    lds_act_slice<true>(hrow, s + u, hh, v);
                 else
-                    act_slice<Q>(hrow, s + u, hh, 1.0f, v);
-                const float d = dot_slice<Q>(vw[u], v);
+                    glb_act_slice<FP8>(hrow, s + u, hh, v);
+                const float d = dot_slice<FP8>(vw[u], v);
                 if constexpr (Q == RD_BLOCK) {
                     const int kb = (s + u) / 2;
                     const float sc = a.sh[(long)r * (a.I / 128) + kb] *
@@ -333,13 +367,20 @@ static RdArgs rd_args(const FwdPlan& p) {
     return a;
 }
 
-static int largest_unroll(int n) { return n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1); }
+// Slices per load batch: the largest of 8, 6, 4, 3, 2, 1 that divides the
+// wave's slice count n and is at most cap (the loops walk n in steps of U and
+// must never step past the last slice).
+static int largest_unroll(int n, int cap) {
+    for (int u : {8, 6, 4, 3, 2})
+        if (u <= cap && n % u == 0) return u;
+    return 1;
+}
 
-// Waves per Gate/Up workgroup: enough waves in total to keep HBM busy (about
-// 2048), K split evenly (NSL % NW == 0), at most 16.
+// Waves per Gate/Up workgroup: enough waves in total to keep many weight
+// loads in flight at small batch (about 4096), K split evenly, at most 16.
 static int rd_waves(long groups, int NSL) {
     int nw = 1;
-    while (nw < 16 && groups * nw * 2 <= 2048 && NSL % (nw * 2) == 0) nw *= 2;
+    while (nw < 16 && groups * nw * 2 <= 4096 && NSL % (nw * 2) == 0) nw *= 2;
     return nw;
 }
 
@@ -347,7 +388,10 @@ template <int Q, int NW>
 static hipError_t rd_gu_nw(const RdArgs& a, int U, hipStream_t st) {
     dim3 grid(a.T * a.k, a.I / 32);
     switch (U) {
+        case 8: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 8>), grid, dim3(64 * NW), 0, st, a); break;
+        case 6: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 6>), grid, dim3(64 * NW), 0, st, a); break;
         case 4: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 4>), grid, dim3(64 * NW), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 3>), grid, dim3(64 * NW), 0, st, a); break;
         case 2: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 2>), grid, dim3(64 * NW), 0, st, a); break;
         default: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 1>), grid, dim3(64 * NW), 0, st, a); break;
     }
@@ -359,7 +403,10 @@ static hipError_t rd_gu(const RdArgs& a, hipStream_t st) {
     const int elem = Q == RD_BF16 ? 2 : 1;
     const int NSL = a.H * elem / kSliceBytes;
     const int nw = rd_waves((long)a.T * a.k * (a.I / 32), NSL);
-    const int U = largest_unroll(NSL / nw);
+    // at most 16 weight loads per batch; 16-wave groups (128 VGPRs) decoding
+    // e4m3 keep two slices per batch to stay clear of spills
+    const int U = largest_unroll(NSL / nw, Q != RD_BF16 && nw == 16 ? 2 : 4);
+    if (NSL % nw != 0 || (NSL / nw) % U != 0) return hipErrorInvalidValue;
     switch (nw) {
         case 1: return rd_gu_nw<Q, 1>(a, U, st);
         case 2: return rd_gu_nw<Q, 2>(a, U, st);
@@ -380,7 +427,10 @@ template <int Q, int NW, int KP>
 static hipError_t rd_dn_kp(const RdArgs& a, int U, hipStream_t st) {
     dim3 grid(a.T, a.H / 32);
     switch (U) {
+        case 8: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 8>), grid, dim3(64 * NW), 0, st, a); break;
+        case 6: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 6>), grid, dim3(64 * NW), 0, st, a); break;
         case 4: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 4>), grid, dim3(64 * NW), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 3>), grid, dim3(64 * NW), 0, st, a); break;
         case 2: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 2>), grid, dim3(64 * NW), 0, st, a); break;
         default: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 1>), grid, dim3(64 * NW), 0, st, a); break;
     }
@@ -389,7 +439,9 @@ static hipError_t rd_dn_kp(const RdArgs& a, int U, hipStream_t st) {
 
 template <int Q, int NW>
 static hipError_t rd_dn_nw(const RdArgs& a, int kp, int NSL, hipStream_t st) {
-    const int U = largest_unroll(NSL / kp);
+    // 128 VGPRs at 16 waves: e4m3 decoding keeps fewer slices per batch
+    const int U = largest_unroll(NSL / kp, NW == 16 && Q != RD_BF16 ? (Q == RD_TENSOR ? 4 : 2) : 8);
+    if (NSL % kp != 0 || (NSL / kp) % U != 0) return hipErrorInvalidValue;
     switch (kp) {
         case 1: return rd_dn_kp<Q, NW, 1>(a, U, st);
         case 2: return rd_dn_kp<Q, NW, 2>(a, U, st);
