@@ -134,8 +134,7 @@ size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int quant, 
  * The combine sums the k routes of a token in a fixed order in fp32 and
  * rounds to bf16 once: repeated calls give identical bits.
  * Shapes: H % 128 == 0, I % 64 == 0 (block128: I % 128 == 0); the
- * route-direct path also needs H*elem <= 8192 bytes and I*elem <= 2048 bytes
- * (per-tensor FP8 also k*I <= 32768). */
+ * route-direct path also needs H*elem <= 8192 bytes and I*elem <= 2048 bytes. */
 int moe_forward(const void *x, const moe_routes *routes, const void *packed_gate_up,
                 const void *packed_down, const moe_scales *scales, void *out, int H, int I,
                 int quant, int path, void *ws, size_t ws_bytes, void *stream);

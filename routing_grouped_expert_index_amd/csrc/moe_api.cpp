@@ -39,12 +39,12 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 // that range, expressed in routes: T <= 4 and T*k <= E/2.
 constexpr int kRouteDirectMaxTokens = 4;
 
-// Route-direct kernels stage one activation row (H * elem bytes) in LDS, and
-// for per-tensor FP8 also the k rows of quantised h of a token (k * I bytes).
+// Route-direct kernels stage one activation row in LDS: H * elem <= 8192 bytes
+// for Gate/Up, I * elem <= 2048 bytes for Down.
 bool rd_shape_ok(int H, int I, int k, int quant) {
     const int elem = quant == MOE_BF16 ? 2 : 1;
-    if ((long)H * elem > 8192 || (long)I * elem > 2048) return false;
-    return quant != MOE_FP8_PER_TENSOR || (long)k * I <= 32768;
+    (void)k;
+    return (long)H * elem <= 8192 && (long)I * elem <= 2048;
 }
 
 int check_shape(int T, int H, int I, int E, int k, int quant) {
@@ -73,14 +73,14 @@ int resolve_path(int T, int H, int I, int E, int k, int quant, int path) {
     if (path == MOE_PATH_ROUTE_DIRECT) {
         if (!rd_shape_ok(H, I, k, quant))
             return fail(MOE_ERR_UNSUPPORTED,
-                        "route-direct path: H*elem <= 8192 and I*elem <= 2048 bytes (per-tensor FP8: k*I <= 32768)");
+                        "route-direct path: H*elem <= 8192 and I*elem <= 2048 bytes");
         return path;
     }
     return fail(MOE_ERR_INVALID_ARG, "unknown path %d", path);
 }
 
 struct Layout {
-    size_t tiles, ntiles, amax, scal, xq, sx, h, hq, sh, y, total;
+    size_t tiles, ntiles, amax, scal, xq, sx, h, hq, sh, y, rd_hmax, rd_part, rd_cnt, total;
 };
 
 Layout layout(int T, int H, int I, int E, int k, int quant, int path) {
@@ -106,6 +106,10 @@ Layout layout(int T, int H, int I, int E, int k, int quant, int path) {
     L.hq = take(quant != MOE_BF16 ? R * I : 0);
     L.sh = take(quant == MOE_FP8_BLOCK128 ? sizeof(float) * R * (I / 128) : 0);
     L.y = take(grouped ? R * H * 2 : 0);
+    const size_t rd_blocks = grouped ? 0 : (size_t)T * (H / 32);
+    L.rd_hmax = take(!grouped && quant == MOE_FP8_PER_TENSOR ? sizeof(float) * R * (I / 32) : 0);
+    L.rd_part = take(rd_blocks * sizeof(float) * 32 * (size_t)(grouped ? 0 : moe::rd_down_items(T, H, I, k, quant)));
+    L.rd_cnt = take(rd_blocks * sizeof(int32_t));
     L.total = off;
     return L;
 }
@@ -242,6 +246,9 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
     P.hq = at<uint8_t>(ws, L.hq);
     P.sh = at<float>(ws, L.sh);
     P.y = at<uint16_t>(ws, L.y);
+    P.rd_hmax = at<float>(ws, L.rd_hmax);
+    P.rd_part = at<float>(ws, L.rd_part);
+    P.rd_cnt = at<int32_t>(ws, L.rd_cnt);
     P.max_tiles = moe::grouped_max_tiles(P.R, E);
 
     hipStream_t st = static_cast<hipStream_t>(stream);

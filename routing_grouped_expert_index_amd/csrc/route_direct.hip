@@ -18,14 +18,18 @@
 //    block of those columns; its NW waves split K, their partial sums meet in
 //    LDS in wave order, then SwiGLU and the h store (bf16, or fp32 ahead of the
 //    FP8 requantisation).
-//  * Down + combine: a workgroup owns (token, 32 output columns); its waves take
-//    (slot, K part) items in a fixed order, weight each route by its gate, and
-//    the wave partials are added in wave order: the top-k combine has a fixed
-//    summation order, needs no atomics and no y round trip.
-//  * FP8 per-tensor: the activation scales are whole-tensor maxima (x over
-//    [T, H], h over [T*k, I]); each workgroup takes the maximum itself (the
-//    tensors are a few kilobytes at decode sizes) and quantises its operands
-//    on the fly, so the path is two launches with nothing in between.
+//  * Down + combine: a workgroup owns (token, 32 output columns, item), an item
+//    being one route slot and one of KP parts of its K range, so that a batch
+//    of one token still spreads over about a thousand workgroups.  Each writes
+//    its gate-weighted partial sums to the workspace and takes a ticket from a
+//    device-scope counter; the last of the output block's workgroups to arrive
+//    adds all partials in item order and writes the bf16 output.  The order of
+//    the sum never depends on arrival order, so two runs give the same bits.
+//  * FP8 per-tensor: the activation scales are whole-tensor maxima.  Each
+//    Gate/Up workgroup takes the maximum of x over [T, H] itself (a few
+//    kilobytes at decode sizes) and records the maximum of its 32 h values; the
+//    Down workgroups reduce those few hundred maxima.  So the path is two
+//    launches with nothing in between.
 //  * FP8 blockwise: x and h arrive quantised with their per-128 scales; each
 //    64-byte K slice lies in one scale block.
 #include "common.cuh"
@@ -51,6 +55,9 @@ struct RdArgs {
     const uint8_t* h;        // Down input: bf16 [R][I] | fp32 [R][I] (per-tensor) | e4m3 [R][I] (block)
     const float* sh;         // block: [R][I/128]
     void* hout;              // Gate/Up output: bf16 [R][I] | fp32 [R][I]
+    float* hmax;             // per-tensor: max |h| per Gate/Up workgroup [R][I/32]
+    float* part;             // Down partial sums [T*H/32][items][32]
+    int32_t* cnt;            // Down arrival counters [T*H/32], zeroed by the Gate/Up kernel
     uint16_t* out;           // [T][H]
     int T, H, I, E, k;
 };
@@ -106,7 +113,6 @@ __device__ __forceinline__ float block_amax(const T* p, long n, float* sred) {
 // 32-row weight block needs the same activation values): bf16 values, or e4m3
 // codes (quantised here for per-tensor FP8, copied for blockwise).
 constexpr int kRdActBytes = 8192;          // one activation row: H * elem <= 8192
-constexpr int kRdHBytes = 32768;           // per-tensor Down: the token's k rows of h codes
 
 // The lane's 32 activation bytes of slice s from an LDS row, as fp32 values
 // (bf16: 16 values; e4m3: 32 values).
@@ -122,13 +128,6 @@ __device__ __forceinline__ void lds_act_slice(const uint8_t* row, int s, int hh,
         e4m3x16_to_f32(w0, v);
         e4m3x16_to_f32(w1, v + 16);
     }
-}
-
-// Global-memory variant for activation rows that are not staged (bf16 and
-// blockwise Down inputs).
-template <bool FP8>
-__device__ __forceinline__ void glb_act_slice(const uint8_t* row, int s, int hh, float v[32]) {
-    lds_act_slice<FP8>(row, s, hh, v);
 }
 
 // copy n bytes (n % 16 == 0) of a global row into LDS, whole workgroup
@@ -198,6 +197,8 @@ rd_gate_up_kernel(const RdArgs a) {
     constexpr int elem = FP8 ? 1 : 2;
     const int Kb = a.H * elem, NSL = Kb / kSliceBytes, per = NSL / NW, s0 = wave * per;
     const long gstride = 32L * Kb;
+    if (r == 0 && G == 0)   // the Down kernel that follows counts arrivals from zero
+        for (int i = threadIdx.x; i < a.T * (a.H / 32); i += 64 * NW) a.cnt[i] = 0;
     const uint8_t* wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + lane * 16;
     const uint8_t* wu = wg + gstride;
 
@@ -212,6 +213,7 @@ rd_gate_up_kernel(const RdArgs a) {
             }
     };
     load_batch(s0);   // the weight stream starts before the activation row is staged
+    __builtin_amdgcn_sched_barrier(0);   // keep the whole batch in flight (no sinking below the activations)
 
     float xs = 1.0f;
     if constexpr (Q == RD_TENSOR) {
@@ -230,7 +232,10 @@ rd_gate_up_kernel(const RdArgs a) {
 
     float accg = 0.0f, accu = 0.0f;
     for (int s = s0; s < s0 + per; s += U) {
-        if (s != s0) load_batch(s);
+        if (s != s0) {
+            load_batch(s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float v[32];
@@ -268,6 +273,12 @@ rd_gate_up_kernel(const RdArgs a) {
             uv *= fsc;
         }
         const float hv = silu(gv) * uv;
+        if constexpr (Q == RD_TENSOR) {   // this workgroup's share of the h amax
+            float m = fabsf(hv);
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+            if (j == 0) a.hmax[(long)r * (a.I / 32) + G] = m;
+        }
         // row j of the pair's blocks is h column 32G + 16hh' + 4a + b, j = 8a + 4hh' + b
         const int c = 32 * G + 16 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3);
         if constexpr (Q == RD_BF16)
@@ -280,70 +291,121 @@ rd_gate_up_kernel(const RdArgs a) {
 // ------------------------------------------------------------ Down+combine --
 template <int Q, int NW, int KP, int U>
 __global__ void __launch_bounds__(64 * NW)
-rd_down_combine_kernel(const RdArgs a) {
+rd_down_part_kernel(const RdArgs a) {
     constexpr bool FP8 = Q != RD_BF16;
-    __shared__ __attribute__((aligned(16))) uint8_t hrows[Q == RD_TENSOR ? kRdHBytes : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t hrow_s[Q == RD_TENSOR ? 2048 : 16];
     __shared__ float red[NW][32];
-    __shared__ float sred[NW];
+    __shared__ int last_s;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int hh = lane >> 5;
-    const int t = blockIdx.x, g32 = blockIdx.y;
+    const int nb = a.H / 32;
+    const int tb = blockIdx.x, t = tb / nb, g32 = tb - t * nb;
+    const int items = a.k * KP, it = blockIdx.y;
+    const int jj = it / KP, kp = it - jj * KP;
+    const int r = t * a.k + jj, e = a.ids[r];
     constexpr int elem = FP8 ? 1 : 2;
-    const int Kb = a.I * elem, NSL = Kb / kSliceBytes, per = NSL / KP;
+    const int Kb = a.I * elem, NSL = Kb / kSliceBytes, spw = NSL / KP / NW;
+    const int s0 = kp * (NSL / KP) + wave * spw;
     const int n0 = down_col_of_packed(32 * g32);   // all 32 rows lie in one 128-column block
+    const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + lane * 16;
 
-    float hs = 1.0f;
-    if constexpr (Q == RD_TENSOR) {
-        const float* h = reinterpret_cast<const float*>(a.h);
-        hs = scale_from_amax(block_amax<float, NW>(h, (long)a.T * a.k * a.I, sred));
-        quant_row<float, NW>(hrows, h + (long)t * a.k * a.I, a.k * a.I, hs);
-        __syncthreads();
-    }
-    float acc = 0.0f;
-    const int items = a.k * KP;
-    for (int it = wave; it < items; it += NW) {
-        const int jj = it / KP, kp = it - jj * KP;
-        const int r = t * a.k + jj, e = a.ids[r];
-        const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + lane * 16;
-        const uint8_t* hrow = Q == RD_TENSOR ? hrows + (long)jj * Kb : a.h + (long)r * Kb;
-        float y = 0.0f;
-        for (int s = kp * per; s < (kp + 1) * per; s += U) {
-            u32x4 vw[U][2];
+    u32x4 vw[U][2];
+    u32x4 va[U][2];   // activation slices of the batch (rows not staged in LDS)
+    const uint8_t* hg = a.h + (long)r * Kb + hh * 32;
+    auto load_batch = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                vw[u][q] = *reinterpret_cast<const u32x4*>(wb + (long)(s + u) * 2048 + q * 1024);
+        if constexpr (Q != RD_TENSOR) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
-                    vw[u][q] = *reinterpret_cast<const u32x4*>(wb + (long)(s + u) * 2048 + q * 1024);
+                    va[u][q] = *reinterpret_cast<const u32x4*>(hg + (s + u) * 64 + q * 16);
+        }
+    };
+    load_batch(s0);   // the weight stream starts before the h row is prepared
+    __builtin_amdgcn_sched_barrier(0);   // keep the whole batch in flight (no sinking below the activations)
+
+    float hs = 1.0f;
+    const uint8_t* hrow = hrow_s;
+    if constexpr (Q == RD_TENSOR) {
+        // whole-tensor h amax from the Gate/Up workgroups' maxima, then this
+        // route's h row quantised into LDS
+        float m = 0.0f;
+        const int nmax = a.T * a.k * (a.I / 32);
+        for (int i = threadIdx.x; i < nmax; i += 64 * NW) m = fmaxf(m, a.hmax[i]);
+        m = wave_max(m);
+        if (lane == 0) red[wave][0] = m;
+        __syncthreads();
+        m = 0.0f;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float v[32];
-                if constexpr (Q == RD_TENSOR)
-                    lds_act_slice<true>(hrow, s + u, hh, v);
-                else
-                    glb_act_slice<FP8>(hrow, s + u, hh, v);
-                const float d = dot_slice<FP8>(vw[u], v);
-                if constexpr (Q == RD_BLOCK) {
-                    const int kb = (s + u) / 2;
-                    const float sc = a.sh[(long)r * (a.I / 128) + kb] *
-                                     a.s_d[((long)e * (a.I / 128) + kb) * (a.H / 128) + n0 / 128];
-                    y = fmaf(d, sc, y);
-                } else {
-                    y += d;
-                }
+        for (int w = 0; w < NW; ++w) m = fmaxf(m, red[w][0]);
+        hs = scale_from_amax(m);
+        quant_row<float, NW>(hrow_s, reinterpret_cast<const float*>(a.h) + (long)r * a.I, a.I, hs);
+        __syncthreads();
+    }
+
+    float y = 0.0f;
+    for (int s = s0; s < s0 + spw; s += U) {
+        if (s != s0) {
+            load_batch(s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v[32];
+            if constexpr (Q == RD_TENSOR) {
+                lds_act_slice<true>(hrow, s + u, hh, v);
+            } else if constexpr (FP8) {
+                e4m3x16_to_f32(va[u][0], v);
+                e4m3x16_to_f32(va[u][1], v + 16);
+            } else {
+                bf16x8_to_f32(va[u][0], v);
+                bf16x8_to_f32(va[u][1], v + 8);
+            }
+            const float d = dot_slice<FP8>(vw[u], v);
+            if constexpr (Q == RD_BLOCK) {
+                const int kb = (s + u) / 2;
+                const float sc = a.sh[(long)r * (a.I / 128) + kb] *
+                                 a.s_d[((long)e * (a.I / 128) + kb) * (a.H / 128) + n0 / 128];
+                y = fmaf(d, sc, y);
+            } else {
+                y += d;
             }
         }
-        float gw = a.tw[r];
-        if constexpr (Q == RD_TENSOR) gw *= hs * a.s_d[e];
-        acc = fmaf(gw, y, acc);
     }
-    acc += __shfl_xor(acc, 32);
-    if (hh == 0) red[wave][lane] = acc;
+    y += __shfl_xor(y, 32);
+    if (hh == 0) red[wave][lane] = y;
     __syncthreads();
+    // Partials and the ticket use device-scope atomic stores, loads and adds,
+    // which are performed at the device-coherent level without the whole-L2
+    // write-back a device-scope fence costs on this multi-XCD GPU; the wave's
+    // partial stores have completed (vmcnt 0) before it takes its ticket.
+    float* part = a.part + (long)tb * items * 32;
+    if (wave == 0) {
+        if (hh == 0) {
+            float o = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) o += red[w][lane];
+            float gw = a.tw[r];
+            if constexpr (Q == RD_TENSOR) gw *= hs * a.s_d[e];
+            __hip_atomic_store(part + it * 32 + lane, gw * o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0)
+        if (lane == 0)
+            last_s = __hip_atomic_fetch_add(a.cnt + tb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == items - 1;
+    }
+    __syncthreads();
+    if (!last_s) return;
     if (wave == 0 && hh == 0) {
         float o = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) o += red[w][lane];
+        for (int i = 0; i < items; ++i)   // fixed order
+            o += __hip_atomic_load(part + i * 32 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         a.out[(long)t * a.H + down_col_of_packed(32 * g32 + lane)] = f32_to_bf16(o);
+        if (lane == 0) __hip_atomic_store(a.cnt + tb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -362,6 +424,9 @@ static RdArgs rd_args(const FwdPlan& p) {
     a.h = p.quant == Q_FP8_BLOCK ? p.hq : static_cast<const uint8_t*>(p.h);
     a.sh = p.sh;
     a.hout = p.h;
+    a.hmax = p.rd_hmax;
+    a.part = p.rd_part;
+    a.cnt = p.rd_cnt;
     a.out = p.out;
     a.T = p.T; a.H = p.H; a.I = p.I; a.E = p.E; a.k = p.k;
     return a;
@@ -423,50 +488,68 @@ hipError_t launch_route_direct_gate_up(const FwdPlan& p, hipStream_t st) {
     return rd_gu<RD_BLOCK>(a, st);
 }
 
+// Down split: K parts per route (1, 2 or 4, dividing NSL) only while the grid
+// stays small (every item of an output block takes a ticket from the same
+// counter, and those atomics serialise), then waves per workgroup (1, 2 or 4)
+// until each wave streams at most 8 slices, then the batch size.
+struct RdDownCfg {
+    int kp, nw, U;
+};
+static RdDownCfg rd_down_cfg(int T, int H, int I, int k, int quant) {
+    const int elem = quant == Q_BF16 ? 2 : 1;
+    const int NSL = I * elem / kSliceBytes;
+    const long tb = (long)T * (H / 32);
+    RdDownCfg c{1, 1, 1};
+    while (c.kp < 4 && NSL % (c.kp * 2) == 0 && tb * k * c.kp * 2 <= 256) c.kp *= 2;
+    const int per = NSL / c.kp;
+    while (c.nw < 4 && per % (c.nw * 2) == 0 && per / c.nw > 8) c.nw *= 2;
+    c.U = largest_unroll(per / c.nw, 8);
+    return c;
+}
+
+int rd_down_items(int T, int H, int I, int k, int quant) { return k * rd_down_cfg(T, H, I, k, quant).kp; }
+
 template <int Q, int NW, int KP>
 static hipError_t rd_dn_kp(const RdArgs& a, int U, hipStream_t st) {
-    dim3 grid(a.T, a.H / 32);
+    dim3 grid(a.T * (a.H / 32), a.k * KP);
     switch (U) {
-        case 8: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 8>), grid, dim3(64 * NW), 0, st, a); break;
-        case 6: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 6>), grid, dim3(64 * NW), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 4>), grid, dim3(64 * NW), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 3>), grid, dim3(64 * NW), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 2>), grid, dim3(64 * NW), 0, st, a); break;
-        default: hipLaunchKernelGGL((rd_down_combine_kernel<Q, NW, KP, 1>), grid, dim3(64 * NW), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 8>), grid, dim3(64 * NW), 0, st, a); break;
+        case 6: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 6>), grid, dim3(64 * NW), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 4>), grid, dim3(64 * NW), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 3>), grid, dim3(64 * NW), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 2>), grid, dim3(64 * NW), 0, st, a); break;
+        default: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 1>), grid, dim3(64 * NW), 0, st, a); break;
     }
     return hipGetLastError();
 }
 
 template <int Q, int NW>
-static hipError_t rd_dn_nw(const RdArgs& a, int kp, int NSL, hipStream_t st) {
-    // 128 VGPRs at 16 waves: e4m3 decoding keeps fewer slices per batch
-    const int U = largest_unroll(NSL / kp, NW == 16 && Q != RD_BF16 ? (Q == RD_TENSOR ? 4 : 2) : 8);
-    if (NSL % kp != 0 || (NSL / kp) % U != 0) return hipErrorInvalidValue;
-    switch (kp) {
-        case 1: return rd_dn_kp<Q, NW, 1>(a, U, st);
-        case 2: return rd_dn_kp<Q, NW, 2>(a, U, st);
-        default: return rd_dn_kp<Q, NW, 4>(a, U, st);
+static hipError_t rd_dn_nw(const RdArgs& a, const RdDownCfg& c, hipStream_t st) {
+    switch (c.kp) {
+        case 1: return rd_dn_kp<Q, NW, 1>(a, c.U, st);
+        case 2: return rd_dn_kp<Q, NW, 2>(a, c.U, st);
+        default: return rd_dn_kp<Q, NW, 4>(a, c.U, st);
     }
 }
 
-// K parts per route: up to 4, dividing NSL, while (slot, part) items <= 16;
-// 16 waves per workgroup when the grid is small and there are items for all
 template <int Q>
-static hipError_t rd_dn(const RdArgs& a, hipStream_t st) {
+static hipError_t rd_dn(const RdArgs& a, int quant, hipStream_t st) {
     const int elem = Q == RD_BF16 ? 2 : 1;
     const int NSL = a.I * elem / kSliceBytes;
-    int kp = 1;
-    while (kp < 4 && NSL % (kp * 2) == 0 && a.k * kp * 2 <= 16) kp *= 2;
-    const long wgs = (long)a.T * (a.H / 32);
-    if (wgs * 8 < 2048 && a.k * kp >= 16) return rd_dn_nw<Q, 16>(a, kp, NSL, st);
-    return rd_dn_nw<Q, 8>(a, kp, NSL, st);
+    const RdDownCfg c = rd_down_cfg(a.T, a.H, a.I, a.k, quant);
+    if (NSL % (c.kp * c.nw) != 0 || (NSL / c.kp / c.nw) % c.U != 0) return hipErrorInvalidValue;
+    switch (c.nw) {
+        case 1: return rd_dn_nw<Q, 1>(a, c, st);
+        case 2: return rd_dn_nw<Q, 2>(a, c, st);
+        default: return rd_dn_nw<Q, 4>(a, c, st);
+    }
 }
 
 hipError_t launch_route_direct_down(const FwdPlan& p, hipStream_t st) {
     const RdArgs a = rd_args(p);
-    if (p.quant == Q_BF16) return rd_dn<RD_BF16>(a, st);
-    if (p.quant == Q_FP8_TENSOR) return rd_dn<RD_TENSOR>(a, st);
-    return rd_dn<RD_BLOCK>(a, st);
+    if (p.quant == Q_BF16) return rd_dn<RD_BF16>(a, p.quant, st);
+    if (p.quant == Q_FP8_TENSOR) return rd_dn<RD_TENSOR>(a, p.quant, st);
+    return rd_dn<RD_BLOCK>(a, p.quant, st);
 }
 
 }  // namespace moe
