@@ -154,7 +154,11 @@ def roofline_gemm(wl, stages_ms, peak):
 
 
 def bench_decode(torch, moe, name, batches, iters, nsets=32):
-    """Cold-HBM decode latency: a 1 GiB read between iterations, 32 rotating routing sets."""
+    """Cold-HBM decode latency of one layer (moe_route + moe_forward), 32 rotating
+    routing sets, a 1 GiB read before each iteration.  Three timings per batch:
+    stream launches bracketed by two HIP events; the same step captured once in
+    a HIP graph and replayed; and a run with events between the stages for the
+    dominant kernel's own duration."""
     from workloads import WORKLOADS, random_activations, workload_weights
     wl = WORKLOADS[name]
     w = workload_weights(name)
@@ -168,10 +172,43 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
     for B in batches:
         sets = [random_activations(B, wl.H, wl.E, 10000 + i) for i in range(nsets)]
         xs = [dev_inputs(torch, s, wl) for s in sets]
-        layer = Layer(torch, moe, wl, B, xs[0][0], xs[0][1], weights)
-        ev_sets, distinct = [], []
+        layer = Layer(torch, moe, wl, B, xs[0][0].clone(), xs[0][1].clone(), weights)
+
+        def load(it):
+            layer.x.copy_(xs[it % nsets][0])
+            layer.lg.copy_(xs[it % nsets][1])
+
+        def timed(run):
+            ts = []
+            for it in range(iters + 2):
+                load(it)
+                evict.amax()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                run()
+                e1.record()
+                if it >= 2:
+                    ts.append((e0, e1))
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3   # us
+
+        t_fwd = timed(layer.step)
+        # the step captured once (as a serving loop would) and replayed
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            layer.step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.step()
+        t_graph = timed(g.replay)
+        del g
+        # stage events: the dominant kernel's duration
+        ev_sets = []
         for it in range(iters + 2):
-            layer.x, layer.lg = xs[it % nsets]
+            load(it)
             evict.amax()
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
             for e in evs:
@@ -180,29 +217,30 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
             if it >= 2:
                 ev_sets.append((evs, names))
         torch.cuda.synchronize()
+        distinct = []
         for it in range(nsets):
             ids = moe.route(xs[it][1], wl.k).topk_ids.cpu().numpy()
             distinct.append(len(np.unique(ids)))
-        fwd, dom = [], []
+        dom = []
         for evs, names in ev_sets:
             dname = "rd_gate_up" if "rd_gate_up" in names else "gate_up"
             i = names.index(dname)
-            fwd.append(evs[0].elapsed_time(evs[len(names)]))
             dom.append(evs[i].elapsed_time(evs[i + 1]))
-        t_fwd = float(np.median(fwd)) * 1e3      # us
         t_dom = float(np.median(dom)) * 1e3
         D = float(np.mean(distinct))
         w_bytes = D * 3 * wl.H * wl.I * elem
         dom_bytes = D * 2 * wl.H * wl.I * elem + B * wl.H * elem   # Gate/Up weights + activations
-        res[B] = dict(us_per_layer=round(t_fwd, 2), tokens_per_s=round(B / (t_fwd * 1e-6), 1),
+        res[B] = dict(us_per_layer=round(t_fwd, 2), us_per_layer_graph=round(t_graph, 2),
+                      tokens_per_s=round(B / (t_fwd * 1e-6), 1),
                       path=layer.path, distinct_experts=round(D, 2),
                       hbm_frac_layer=round(w_bytes / (t_fwd * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
+                      hbm_frac_layer_graph=round(w_bytes / (t_graph * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
                       dominant=dict(kernel=dname, bound="hbm", avg_launch_us=round(t_dom, 2),
                                     achieved=round(dom_bytes / (t_dom * 1e-6) / 1e9, 1),
                                     peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(dom_bytes / (t_dom * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)))
-        log(f"decode {name} B={B}: {t_fwd:.2f} us/layer, {res[B]['dominant']['kernel']} "
-            f"{res[B]['dominant']['achieved']} GB/s")
+        log(f"decode {name} B={B}: {t_fwd:.2f} us/layer ({t_graph:.2f} graph), "
+            f"{res[B]['dominant']['kernel']} {t_dom:.2f} us {res[B]['dominant']['achieved']} GB/s")
     del evict
     return res
 
@@ -298,7 +336,9 @@ def main():
 
     log("decode bf16 B=1..4 (cold HBM) ...")
     line["decode"] = dict(workload="decode_bf16 H=2048 I=768 E=128 top-8", timing="cold HBM, median of "
-                          f"{args.decode_iters}, forward span between HIP events",
+                          f"{args.decode_iters}; us_per_layer: moe_route + moe_forward launched on "
+                          "the stream between two HIP events; _graph: the same step replayed from "
+                          "a HIP graph; dominant: the kernel between stage events",
                           batches=bench_decode(torch, moe, "decode_bf16", (1, 2, 3, 4), args.decode_iters))
     torch.cuda.empty_cache()
     if not args.quick:

@@ -17,12 +17,49 @@
 
 namespace moe {
 
-// Picks the k largest logits of one token (row) with one wave.  Gates:
+// Row permutations of DPP (lane i of a row of 16 reads lane ...)
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]: i ^ 1
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]: i ^ 2
+constexpr int kDppRowMirror = 0x140;    // 15 - i
+constexpr int kDppHalfMirror = 0x141;   // 7 - i within each half row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float readlane_f32(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Max and sum over the 64 lanes of a fully active wave, the same bits in every
+// lane: symmetric exchanges inside each row of 16 (xor 1, xor 2, half-row
+// mirror, row mirror), then the four row results read as scalars.
+__device__ __forceinline__ float wave_max_full(float v) {
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+    return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+                 fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_full(float v) {
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    v += dpp_f32<kDppRowMirror>(v);
+    return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+
+// Picks the k largest logits of one token (row) with one whole wave.  Pick j is
+// the largest value left (a wave max), and of the lanes holding it the lowest
+// expert id (ballots, taken in id order: id = lane + 64 i).  Gates:
 // exp(l_j - m) / sum over the picks of exp(l_i - m), m = the largest logit (the
 // full softmax denominator cancels in the renormalisation).  The lane that owns
 // a picked logit remembers its slot j and writes ids[j] and w[j] itself, so no
-// value travels back through memory; the sum over the picks is a wave-wide
-// butterfly, which gives every lane the same bits.
+// value travels back through memory.  Logits are taken as finite (with NaN the
+// picks stay in range but their order is unspecified).
 template <int VPL>
 __device__ void topk_one_token(const float* __restrict__ row, int E, int k,
                                int32_t* __restrict__ ids, float* __restrict__ w,
@@ -34,7 +71,7 @@ __device__ void topk_one_token(const float* __restrict__ row, int E, int k,
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e = lane + kWave * i;
-        v[i] = 0.0f;
+        v[i] = -INFINITY;
         slot[i] = -1;
         if (e < E) {
             v[i] = row[e] + 0.0f;   // -0 -> +0 (comparisons treat them equal anyway)
@@ -43,31 +80,32 @@ __device__ void topk_one_token(const float* __restrict__ row, int E, int k,
     }
     float m = 0.0f;
     for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int bi = -1;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            if ((avail >> i) & 1u) {
-                if (bi < 0 || v[i] > bv) { bv = v[i]; bi = lane + kWave * i; }
-            }
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            const bool take = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
-            if (take) { bv = ov; bi = oi; }
-        }
-        if (j == 0) m = bv;
+        float lm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
-            if (bi == lane + kWave * i) { avail &= ~(1u << i); slot[i] = j; }
+            if ((avail >> i) & 1u) lm = fmaxf(lm, v[i]);
+        const float M = wave_max_full(lm);
+        int win = -1;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const uint64_t b = __ballot(((avail >> i) & 1u) && v[i] == M);
+            if (win < 0 && b != 0) win = __builtin_ctzll(b) + kWave * i;
+        }
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {   // no equal value (NaN): lowest id left
+            const uint64_t b = __ballot((avail >> i) & 1u);
+            if (win < 0 && b != 0) win = __builtin_ctzll(b) + kWave * i;
+        }
+        if (j == 0) m = M;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (win == lane + kWave * i) { avail &= ~(1u << i); slot[i] = j; }
     }
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
         if (slot[i] >= 0) part += expf(v[i] - m);
-    const float S = wave_sum(part);
+    const float S = wave_sum_full(part);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         if (slot[i] >= 0) {
@@ -81,8 +119,14 @@ __device__ void topk_one_token(const float* __restrict__ row, int E, int k,
 }
 
 // ----------------------------------------------------------------------------
-// Small T*k: everything in one workgroup of 16 waves.
+// Small T*k: everything in one workgroup of 16 waves; top-k takes one wave per
+// token, counting and scattering one wave per 64 routes (at most 16).
 constexpr int kSmallWaves = 16;
+
+__host__ __device__ inline int small_sort_waves(int R) {
+    const int n = ceil_div(R, kWave);
+    return n < 1 ? 1 : (n > kSmallWaves ? kSmallWaves : n);
+}
 
 template <int VPL>
 __global__ void __launch_bounds__(kSmallWaves * kWave)
@@ -92,26 +136,28 @@ route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int nb
                    int32_t* __restrict__ perm, int32_t* __restrict__ route_pos) {
     extern __shared__ int32_t lds[];
     const int R = T * k;
+    const int nws = small_sort_waves(R);         // waves that count and scatter
     int32_t* sid = lds;                          // [R]
-    int32_t* wcnt = sid + R;                     // [16][E]
-    int32_t* base = wcnt + kSmallWaves * E;      // [E + 1]
+    int32_t* wcnt = sid + R;                     // [nws][E]
+    int32_t* base = wcnt + nws * E;              // [E + 1]
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
 
-    for (int i = tid; i < kSmallWaves * E; i += blockDim.x) wcnt[i] = 0;
+    for (int i = tid; i < nws * E; i += blockDim.x) wcnt[i] = 0;
     for (int t = wave; t < T; t += kSmallWaves)
         topk_one_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
                             weights + (size_t)t * k, sid + t * k, nullptr);
     __syncthreads();
 
-    const int per = ceil_div(R, kSmallWaves);
-    const int lo = min(R, wave * per), hi = min(R, lo + per);
+    // wave w < nws owns the contiguous route range [lo, hi)
+    const int per = ceil_div(R, nws);
+    const int lo = wave < nws ? min(R, wave * per) : R, hi = min(R, lo + per);
     for (int r = lo + lane; r < hi; r += kWave) atomicAdd(&wcnt[wave * E + sid[r]], 1);
     __syncthreads();
 
     // per expert: exclusive prefix over the waves' ranges (route order)
     for (int e = tid; e < E; e += blockDim.x) {
         int run = 0;
-        for (int w = 0; w < kSmallWaves; ++w) {
+        for (int w = 0; w < nws; ++w) {
             const int c = wcnt[w * E + e];
             wcnt[w * E + e] = run;
             run += c;
@@ -302,7 +348,7 @@ static int bits_for(int E) {
 }
 
 size_t route_small_lds_bytes(int T, int E, int k) {
-    return sizeof(int32_t) * ((size_t)T * k + (size_t)kSmallWaves * E + E + 1);
+    return sizeof(int32_t) * ((size_t)T * k + (size_t)small_sort_waves(T * k) * E + E + 1);
 }
 
 bool route_use_small(int T, int E, int k) {

@@ -195,25 +195,32 @@ rd_gate_up_kernel(const RdArgs a) {
     const int r = blockIdx.x, G = blockIdx.y;   // route; 64-row group (gate block 2G, up block 2G+1)
     const int t = r / a.k, e = a.ids[r];
     constexpr int elem = FP8 ? 1 : 2;
-    const int Kb = a.H * elem, NSL = Kb / kSliceBytes, per = NSL / NW, s0 = wave * per;
+    // wave w takes the U-slice chunks w, w + NW, w + 2 NW, ...: at each step the
+    // waves of the workgroup read one contiguous window of NW * U slices
+    const int Kb = a.H * elem, NSL = Kb / kSliceBytes, per = NSL / NW, s0 = wave * U;
+    constexpr int SB = NW * U;   // slice step between a wave's batches
     const long gstride = 32L * Kb;
     if (r == 0 && G == 0)   // the Down kernel that follows counts arrivals from zero
         for (int i = threadIdx.x; i < a.T * (a.H / 32); i += 64 * NW) a.cnt[i] = 0;
     const uint8_t* wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + lane * 16;
     const uint8_t* wu = wg + gstride;
 
-    u32x4 vg[U][2], vu[U][2];
-    auto load_batch = [&](int s) __attribute__((always_inline)) {
+    // two load buffers: batch b+1 is requested before batch b is computed
+    u32x4 vg[2][U][2], vu[2][U][2];
+    auto load_batch = [&](auto Bc, int s) __attribute__((always_inline)) {
+        constexpr int B = decltype(Bc)::value;
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                vg[u][q] = *reinterpret_cast<const u32x4*>(wg + (long)(s + u) * 2048 + q * 1024);
-                vu[u][q] = *reinterpret_cast<const u32x4*>(wu + (long)(s + u) * 2048 + q * 1024);
+                vg[B][u][q] = *reinterpret_cast<const u32x4*>(wg + (long)(s + u) * 2048 + q * 1024);
+                vu[B][u][q] = *reinterpret_cast<const u32x4*>(wu + (long)(s + u) * 2048 + q * 1024);
             }
+        __builtin_amdgcn_sched_barrier(0);   // the whole batch stays in flight
     };
-    load_batch(s0);   // the weight stream starts before the activation row is staged
-    __builtin_amdgcn_sched_barrier(0);   // keep the whole batch in flight (no sinking below the activations)
+    std::integral_constant<int, 0> B0;
+    std::integral_constant<int, 1> B1;
+    load_batch(B0, s0);   // the weight stream starts before the activation row is staged
 
     float xs = 1.0f;
     if constexpr (Q == RD_TENSOR) {
@@ -231,16 +238,13 @@ rd_gate_up_kernel(const RdArgs a) {
     }
 
     float accg = 0.0f, accu = 0.0f;
-    for (int s = s0; s < s0 + per; s += U) {
-        if (s != s0) {
-            load_batch(s);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    auto compute = [&](auto Bc, int s) __attribute__((always_inline)) {
+        constexpr int B = decltype(Bc)::value;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float v[32];
             lds_act_slice<FP8>(xrow, s + u, hh, v);
-            const float dg = dot_slice<FP8>(vg[u], v), du = dot_slice<FP8>(vu[u], v);
+            const float dg = dot_slice<FP8>(vg[B][u], v), du = dot_slice<FP8>(vu[B][u], v);
             if constexpr (Q == RD_BLOCK) {
                 const int kb = (s + u) / 2;   // 128-deep scale block
                 const float sa = a.sx[(long)t * (a.H / 128) + kb];
@@ -252,6 +256,23 @@ rd_gate_up_kernel(const RdArgs a) {
                 accu += du;
             }
         }
+    };
+    // nb batches of U slices: pairs while more than two remain (batch b+2 goes
+    // into the freed buffer), then the last one or two
+    const int nb = per / U;
+    int s = s0, b = 0;
+    for (; b + 2 < nb; b += 2, s += 2 * SB) {
+        load_batch(B1, s + SB);
+        compute(B0, s);
+        load_batch(B0, s + 2 * SB);
+        compute(B1, s + SB);
+    }
+    if (nb - b == 2) {
+        load_batch(B1, s + SB);
+        compute(B0, s);
+        compute(B1, s + SB);
+    } else {
+        compute(B0, s);
     }
     accg += __shfl_xor(accg, 32);
     accu += __shfl_xor(accu, 32);
@@ -452,11 +473,19 @@ static int rd_waves(long groups, int NSL) {
 template <int Q, int NW>
 static hipError_t rd_gu_nw(const RdArgs& a, int U, hipStream_t st) {
     dim3 grid(a.T * a.k, a.I / 32);
+    // the caller caps U at 4, and at 2 for 16-wave groups
+    if constexpr (NW < 16) {
+        if (U == 4) {
+            hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 4>), grid, dim3(64 * NW), 0, st, a);
+            return hipGetLastError();
+        }
+        if (U == 3) {
+            hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 3>), grid, dim3(64 * NW), 0, st, a);
+            return hipGetLastError();
+        }
+    }
+    if (U > 2) return hipErrorInvalidValue;
     switch (U) {
-        case 8: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 8>), grid, dim3(64 * NW), 0, st, a); break;
-        case 6: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 6>), grid, dim3(64 * NW), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 4>), grid, dim3(64 * NW), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 3>), grid, dim3(64 * NW), 0, st, a); break;
         case 2: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 2>), grid, dim3(64 * NW), 0, st, a); break;
         default: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 1>), grid, dim3(64 * NW), 0, st, a); break;
     }
@@ -468,9 +497,10 @@ static hipError_t rd_gu(const RdArgs& a, hipStream_t st) {
     const int elem = Q == RD_BF16 ? 2 : 1;
     const int NSL = a.H * elem / kSliceBytes;
     const int nw = rd_waves((long)a.T * a.k * (a.I / 32), NSL);
-    // at most 16 weight loads per batch; 16-wave groups (128 VGPRs) decoding
-    // e4m3 keep two slices per batch to stay clear of spills
-    const int U = largest_unroll(NSL / nw, Q != RD_BF16 && nw == 16 ? 2 : 4);
+    // two load batches live in registers: 16-wave groups (128 VGPRs) take at
+    // most 2 bf16 slices (1 e4m3) per batch, smaller groups 4 (2 e4m3), which
+    // keeps every launched variant clear of spills
+    const int U = largest_unroll(NSL / nw, nw == 16 ? (Q != RD_BF16 ? 1 : 2) : (Q != RD_BF16 ? 2 : 4));
     if (NSL % nw != 0 || (NSL / nw) % U != 0) return hipErrorInvalidValue;
     switch (nw) {
         case 1: return rd_gu_nw<Q, 1>(a, U, st);
