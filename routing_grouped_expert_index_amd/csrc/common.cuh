@@ -17,16 +17,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 with round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
 // Two fp32 -> two OCP e4m3fn codes (hardware round-to-nearest-even) in the low
@@ -52,7 +52,8 @@ __device__ __forceinline__ float scale_from_amax(float amax) {
     return amax > 0.0f ? amax / 448.0f : 1.0f;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// z * sigmoid(z) with the hardware reciprocal (about 1 ulp in fp32)
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {

@@ -25,11 +25,12 @@
 //    v_mfma_f32_32x32x64_f8f6f4 (one per slice and block).  Both operands of an
 //    MFMA take the same K values in each lane, so the instruction's internal K
 //    order does not matter.
-//  * Epilogue straight from the accumulators: the packed column permutation
-//    gives each lane 32 contiguous output columns (Down) or the gate and up
-//    values of 16 contiguous h columns (Gate/Up), written as 16-byte stores
-//    in sorted row order (the combine finds a route's Down row through the
-//    inverse permutation).
+//  * Epilogue from the accumulators: the packed column permutation gives each
+//    lane 32 contiguous output columns (Down) or the gate and up values of 16
+//    contiguous h columns (Gate/Up) of one row; each wave stages its rows in
+//    its own LDS area and writes whole 64- or 128-byte row segments in sorted
+//    row order (the combine finds a route's Down row through the inverse
+//    permutation).
 #include "gemm_common.cuh"
 #include "layout.cuh"
 
@@ -46,6 +47,8 @@ constexpr int BN = WROWS * NWAVE;           // packed weight rows per tile
 constexpr int STAGES = 5;                   // token ring: slices s .. s+4
 constexpr int STAGE_B = BM * kSliceBytes;   // 8 KB
 constexpr int LDS = STAGES * STAGE_B;
+constexpr int kEpiStageBytes = 8192;        // per wave: epilogue staging
+constexpr int LDS_TOTAL = LDS + NWAVE * kEpiStageBytes;
 // VMEM instructions per wave and slice: weight loads, token DMA
 constexpr int WLOADS = 4, DMAS = 1;
 // At the top of step s (after its weight loads) the token DMA of slice s,
@@ -101,8 +104,14 @@ gemm32_kernel(const GemmArgs g) {
         }
         return (long)(GATHER ? sel / g.k : sel);
     };
+    // The token DMA is a buffer load (MUBUF) with the LDS bit, not the FLAT
+    // global_load_lds: the compiler treats a pending FLAT access that may touch
+    // LDS as completing out of order and would wait for every LDS read with
+    // lgkmcnt(0).  Offsets are bytes from A (the host keeps A below 2 GB).
+    const __amdgpu_buffer_rsrc_t arsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.A), 0, g.a_bytes, 0x00020000);
     auto make_ap = [&](long src) __attribute__((always_inline)) {
-        return g.A + src * g.lda + (((lane & 3) ^ ((dma_r >> 2) & 3)) * 16);
+        return (uint32_t)(src * g.lda) + (uint32_t)(((lane & 3) ^ ((dma_r >> 2) & 3)) * 16);
     };
     // idle waves (past N) load a valid block, so every wave issues the same loads
     auto make_wp = [&](int e_, int wn0_) __attribute__((always_inline)) {
@@ -111,7 +120,7 @@ gemm32_kernel(const GemmArgs g) {
 
     int e, row0, rows, wn0;
     decode(L, e, row0, rows, wn0);
-    const uint8_t* ap = make_ap(src_row(row0, rows));
+    uint32_t ap = make_ap(src_row(row0, rows));
     const uint8_t* wp = make_wp(e, wn0);
 
     f32x16 acc[2][4];
@@ -125,12 +134,12 @@ gemm32_kernel(const GemmArgs g) {
             for (int q = 0; q < 2; ++q)
                 w[slot][f][q] = *reinterpret_cast<const u32x4*>(p + f * gstride + q * 1024);
     };
-    auto dma = [&](const uint8_t* ap_, int s, int stage) __attribute__((always_inline)) {
-        __builtin_amdgcn_global_load_lds(ap_ + s * kSliceBytes, MOE_LDS(smem + stage * STAGE_B + wave * 1024),
-                                         16, 0, 0);
+    auto dma = [&](uint32_t ap_, int s, int stage) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, MOE_LDS(smem + stage * STAGE_B + wave * 1024), 16,
+                                                 ap_ + (uint32_t)(s * kSliceBytes), 0, 0, 0);
     };
     // a tile's first requests: token DMA of slices 0..3, weights of slices 0..2
-    auto prologue = [&](const uint8_t* ap_, const uint8_t* wp_) __attribute__((always_inline)) {
+    auto prologue = [&](uint32_t ap_, const uint8_t* wp_) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) dma(ap_, min(u, NSL - 1), u);
         __builtin_amdgcn_sched_barrier(0);
@@ -143,23 +152,43 @@ gemm32_kernel(const GemmArgs g) {
         const int r = 32 * m + j, c = 2 * hh + q;
         return *reinterpret_cast<const u32x4*>(st + r * kSliceBytes + ((c ^ ((r >> 2) & 3)) << 4));
     };
+    // The LDS reads of the token operands run ahead of the MFMAs that consume
+    // them (scheduling groups pin the interleave; left alone, the compiler
+    // reuses one register quad and waits for each read right before its MFMAs).
     auto mma = [&](int slot, int stage) __attribute__((always_inline)) {
         const uint8_t* st = smem + stage * STAGE_B;
         if constexpr (!FP8) {
+            // operand kk = 4q + m: K half q of token block m; the two MFMAs of one
+            // accumulator (q = 0, 1) are eight instructions apart
+            u32x4 tb[8];
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int kk = 0; kk < 8; ++kk) tb[kk] = tok(st, kk & 3, kk >> 2);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const bf16x8 b = __builtin_bit_cast(bf16x8, tok(st, m, q));
+            for (int kk = 0; kk < 8; ++kk) {
+                const bf16x8 b = __builtin_bit_cast(bf16x8, tb[kk]);
 #pragma unroll
-                    for (int f = 0; f < 2; ++f)
-                        acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, w[slot][f][q]), b, acc[f][m], 0, 0, 0);
-                }
+                for (int f = 0; f < 2; ++f)
+                    acc[f][kk & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, w[slot][f][kk >> 2]), b, acc[f][kk & 3], 0, 0, 0);
+            }
+            // reads three ahead: R R R, (M M R) x 5, M x 6
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+            for (int kk = 0; kk < 5; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         } else {
+            u32x4 tb[4][2];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const u32x4 b0 = tok(st, m, 0), b1 = tok(st, m, 1);
+                tb[m][0] = tok(st, m, 0);
+                tb[m][1] = tok(st, m, 1);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const u32x4 b0 = tb[m][0], b1 = tb[m][1];
                 const i32x8 bv{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                                (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
 #pragma unroll
@@ -171,6 +200,14 @@ gemm32_kernel(const GemmArgs g) {
                                                                                  0, 0);
                 }
             }
+            // reads one token block ahead: R R R R, (M M R R) x 2, M x 4
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
     };
     // The hand-counted waits assume this VMEM order in every step: weight
@@ -244,57 +281,89 @@ gemm32_kernel(const GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         // (after the last tile the requests repeat this tile's valid data: an
         // unconditional prologue keeps the loop's wait counts exact)
-        const uint8_t* nap = more ? make_ap(nsrc) : ap;
+        const uint32_t nap = more ? make_ap(nsrc) : ap;
         const uint8_t* nwp = more ? make_wp(ne, nwn0) : wp;
         prologue(nap, nwp);
         __builtin_amdgcn_sched_barrier(0);
 
         // ------------------------------------------------------------ epilogue
+        // acc[f][m][i]: token row 32m + j, packed row wn0 + 32f + 8(i/4) + 4hh + i%4.
+        // Each lane holds CPL 16-byte chunks of one output row segment per m:
+        //   Y (bf16):       columns wn0 + 32hh + 16f + 8hv + [0,8)  -> chunk 4hh + 2f + hv
+        //   SwiGLU bf16:    h columns wn0/2 + 16hh + 8h2 + [0,8)     -> chunk 2hh + h2
+        //   SwiGLU fp32:    h columns wn0/2 + 16hh + 4h4 + [0,4)     -> chunk 4hh + h4
+        // Written straight out, one store instruction would touch 32 rows with two
+        // 16-byte pieces each.  Instead the wave stages its segments in its own
+        // LDS area and stores whole segments: each store instruction then covers
+        // 64/CB rows of CB contiguous chunks (128 or 64 bytes per row).
         if (wn0 < g.N) {
+            constexpr int CPL = EPI == EPI_SWIGLU_BF16 ? 2 : 4;   // chunks per lane and row
+            constexpr int CB = 2 * CPL;                             // chunks per row segment
+            constexpr int RPP = kEpiStageBytes / (CB * 16);         // staged rows per phase
+            constexpr int MPP = RPP / 32;                           // m blocks per phase
+            // XOR swizzle of the chunk position: the 8 lanes an LDS cycle serves
+            // land on 8 distinct 16-byte bank groups, for writes and reads
+            auto swz = [](int rr) { return CB == 8 ? (rr & 7) : ((rr >> 1) & 3); };
+            uint8_t* ys = smem + LDS + wave * kEpiStageBytes;
             float fs = 1.0f;
             if constexpr (SC == SC_TENSOR) fs = ld_const(g.sa, 0) * ld_const(g.sw, e);
-            // acc[f][m][i]: token row 32m + j, packed row wn0 + 32f + 8(i/4) + 4hh + i%4
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int r = 32 * m + j;
-                if (r >= rows) continue;
-                if constexpr (EPI == EPI_Y_BF16) {
-                    // output columns wn0 + 32hh + 16f + i of sorted row row0 + r
-                    uint16_t* base = static_cast<uint16_t*>(g.C) + (long)(row0 + r) * g.ldc + wn0 + 32 * hh;
+            for (int ph = 0; ph < 4 / MPP; ++ph) {
 #pragma unroll
-                    for (int f = 0; f < 2; ++f)
+                for (int mm = 0; mm < MPP; ++mm) {
+                    const int m = ph * MPP + mm, rr = 32 * mm + j;
+                    u32x4 ch[CPL];
+                    if constexpr (EPI == EPI_Y_BF16) {
 #pragma unroll
-                        for (int hv = 0; hv < 2; ++hv) {
-                            u32x4 v;
+                        for (int f = 0; f < 2; ++f)
 #pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                v[t] = pack_bf16x2(acc[f][m][8 * hv + 2 * t] * fs, acc[f][m][8 * hv + 2 * t + 1] * fs);
-                            *reinterpret_cast<u32x4*>(base + 16 * f + 8 * hv) = v;
+                            for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+                                for (int t = 0; t < 4; ++t)
+                                    ch[2 * f + hv][t] = pack_bf16x2(acc[f][m][8 * hv + 2 * t] * fs,
+                                                                    acc[f][m][8 * hv + 2 * t + 1] * fs);
+                    } else {
+                        float hv[16];
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) hv[i] = silu(acc[0][m][i] * fs) * (acc[1][m][i] * fs);
+                        if constexpr (EPI == EPI_SWIGLU_BF16) {
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                                for (int t = 0; t < 4; ++t)
+                                    ch[h2][t] = pack_bf16x2(hv[8 * h2 + 2 * t], hv[8 * h2 + 2 * t + 1]);
+                        } else {
+#pragma unroll
+                            for (int h4 = 0; h4 < 4; ++h4)
+#pragma unroll
+                                for (int t = 0; t < 4; ++t) ch[h4][t] = __float_as_uint(hv[4 * h4 + t]);
                         }
-                } else {
-                    // h columns wn0/2 + 16hh + i: gate acc[0], up acc[1]
-                    const long hrow = row0 + r;
-                    const int hc = wn0 / 2 + 16 * hh;
-                    float hv[16];
+                    }
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) hv[i] = silu(acc[0][m][i] * fs) * (acc[1][m][i] * fs);
-                    if constexpr (EPI == EPI_SWIGLU_BF16) {
-                        uint16_t* base = static_cast<uint16_t*>(g.C) + hrow * g.ldc + hc;
+                    for (int u = 0; u < CPL; ++u)
+                        *reinterpret_cast<u32x4*>(ys + rr * (CB * 16) + (((CPL * hh + u) ^ swz(rr)) << 4)) = ch[u];
+                }
+                // LDS operations of one wave execute in order; this only keeps the
+                // compiler from moving the reads above the writes
+                __asm__ volatile("" ::: "memory");
 #pragma unroll
-                        for (int h2 = 0; h2 < 2; ++h2) {
-                            u32x4 v;
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) v[t] = pack_bf16x2(hv[8 * h2 + 2 * t], hv[8 * h2 + 2 * t + 1]);
-                            *reinterpret_cast<u32x4*>(base + 8 * h2) = v;
-                        }
-                    } else {   // EPI_SWIGLU_F32: fp32 h; the per-tensor scale is taken over all routes afterwards
-                        float* base = static_cast<float*>(g.C) + hrow * g.ldc + hc;
-#pragma unroll
-                        for (int h4 = 0; h4 < 4; ++h4)
-                            *reinterpret_cast<f32x4*>(base + 4 * h4) =
-                                f32x4{hv[4 * h4], hv[4 * h4 + 1], hv[4 * h4 + 2], hv[4 * h4 + 3]};
+                for (int t = 0; t < RPP * CB / 64; ++t) {
+                    const int rr = t * (64 / CB) + lane / CB, c = lane % CB;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(ys + rr * (CB * 16) + ((c ^ swz(rr)) << 4));
+                    const int r = ph * RPP + rr;
+                    if (r < rows) {
+                        const long orow = row0 + r;
+                        void* dst;
+                        if constexpr (EPI == EPI_Y_BF16)
+                            dst = static_cast<uint16_t*>(g.C) + orow * g.ldc + wn0 + 8 * c;
+                        else if constexpr (EPI == EPI_SWIGLU_BF16)
+                            dst = static_cast<uint16_t*>(g.C) + orow * g.ldc + wn0 / 2 + 8 * c;
+                        else
+                            dst = static_cast<float*>(g.C) + orow * g.ldc + wn0 / 2 + 4 * c;
+                        *reinterpret_cast<u32x4*>(dst) = v;
                     }
                 }
+                __asm__ volatile("" ::: "memory");
             }
         }
         if (!more) break;
@@ -326,10 +395,11 @@ int gemm_num_cus() {
 
 template <bool FP8, bool GATHER, int SC, int EPI>
 static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st) {
+    if (a.a_bytes <= 0 || a.a_bytes > 0x7fffffffL) return hipErrorInvalidValue;   // 32-bit buffer offsets
     const long total_bound = (long)a.max_tiles * ((a.N + g32::BN - 1) / g32::BN);
     long grid = std::min<long>(total_bound, (long)gemm_num_cus());
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI>), dim3((unsigned)grid), dim3(g32::NT), g32::LDS, st, a);
+    hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI>), dim3((unsigned)grid), dim3(g32::NT), g32::LDS_TOTAL, st, a);
     return hipGetLastError();
 }
 
@@ -352,6 +422,7 @@ static GemmArgs gate_up_args(const FwdPlan& p, int elem) {
     a.nb_orig = 2 * p.I / 128;
     a.I = p.I;
     a.max_tiles = p.max_tiles;
+    a.a_bytes = (long)p.T * a.lda;
     return a;
 }
 
@@ -397,6 +468,7 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     a.C = p.y;
     a.ldc = p.H;
     a.max_tiles = p.max_tiles;
+    a.a_bytes = (long)p.T * p.k * a.lda;
     if (p.quant == Q_BF16) return run_gemm32<false, false, SC_NONE, EPI_Y_BF16>(a, st);
     if (p.quant == Q_FP8_TENSOR) return run_gemm32<true, false, SC_TENSOR, EPI_Y_BF16>(a, st);
     return launch_block_down(a, st);

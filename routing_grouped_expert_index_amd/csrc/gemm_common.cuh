@@ -30,6 +30,7 @@ struct GemmArgs {
     float* cscale;          // Q128: [R][I/128]
     int max_tiles;
     int order;              // tile order: 0 column tile major, 1 row tile major
+    long a_bytes;           // bytes of A addressable by the token loads
 };
 
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
