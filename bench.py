@@ -125,8 +125,8 @@ def bench_prefill(torch, moe, name, steps, warmup):
 # counters were taken on; any edit to it turns the figure into null.
 FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524303.0, 1.0
 COUNTER_TRAFFIC = {
-    "prefill_bf16": dict(gemm_sha256="68e77c1c277af6fb0ea062eaca928b11ae5809afe7fafed6bac00e66914a02bf",
-                         fetch_kib=816970.3, write_kib=98409.6),
+    "prefill_bf16": dict(gemm_sha256="c0575437833c8862a6353079261c133ec21a8a9b7fcaee6b474b54f26a2df348",
+                         fetch_kib=802353.3, write_kib=98355.4),
 }
 
 
