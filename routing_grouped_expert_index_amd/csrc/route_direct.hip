@@ -182,6 +182,30 @@ __device__ __forceinline__ float dot_slice(const u32x4 w[2], const float v[32]) 
     return acc;
 }
 
+// bf16: the lane's 16 weights times the 16 activations of the same K positions,
+// two products per instruction (v_dot2c_f32_bf16) straight from the packed words
+__device__ __forceinline__ float dot_slice_bf16(const u32x4 w[2], const u32x4 x[2], float acc) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        // the words go through scalars: a bit cast taken straight from a vector
+        // element was compiled as a cast of element 0 for every i
+        const uint32_t wv[4] = {w[q][0], w[q][1], w[q][2], w[q][3]};
+        const uint32_t xv[4] = {x[q][0], x[q][1], x[q][2], x[q][3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wv[i]),
+                                                  __builtin_bit_cast(bf16x2_t, xv[i]), acc, false);
+    }
+    return acc;
+}
+
+// the lane's 32 activation bytes of slice s from an LDS row, as packed words
+__device__ __forceinline__ void lds_act_raw(const uint8_t* row, int s, int hh, u32x4 x[2]) {
+    const uint8_t* p = row + s * 64 + hh * 32;
+    x[0] = *reinterpret_cast<const u32x4*>(p);
+    x[1] = *reinterpret_cast<const u32x4*>(p + 16);
+}
+
 // ---------------------------------------------------------------- Gate/Up --
 template <int Q, int NW, int U>
 __global__ void __launch_bounds__(64 * NW)
@@ -242,9 +266,18 @@ rd_gate_up_kernel(const RdArgs a) {
         constexpr int B = decltype(Bc)::value;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float v[32];
-            lds_act_slice<FP8>(xrow, s + u, hh, v);
-            const float dg = dot_slice<FP8>(vg[B][u], v), du = dot_slice<FP8>(vu[B][u], v);
+            float dg, du;
+            if constexpr (!FP8) {
+                u32x4 xw[2];
+                lds_act_raw(xrow, s + u, hh, xw);
+                dg = dot_slice_bf16(vg[B][u], xw, 0.0f);
+                du = dot_slice_bf16(vu[B][u], xw, 0.0f);
+            } else {
+                float v[32];
+                lds_act_slice<FP8>(xrow, s + u, hh, v);
+                dg = dot_slice<FP8>(vg[B][u], v);
+                du = dot_slice<FP8>(vu[B][u], v);
+            }
             if constexpr (Q == RD_BLOCK) {
                 const int kb = (s + u) / 2;   // 128-deep scale block
                 const float sa = a.sx[(long)t * (a.H / 128) + kb];
@@ -377,17 +410,19 @@ rd_down_part_kernel(const RdArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float v[32];
-            if constexpr (Q == RD_TENSOR) {
-                lds_act_slice<true>(hrow, s + u, hh, v);
-            } else if constexpr (FP8) {
-                e4m3x16_to_f32(va[u][0], v);
-                e4m3x16_to_f32(va[u][1], v + 16);
+            float d;
+            if constexpr (!FP8) {
+                d = dot_slice_bf16(vw[u], va[u], 0.0f);
             } else {
-                bf16x8_to_f32(va[u][0], v);
-                bf16x8_to_f32(va[u][1], v + 8);
+                float v[32];
+                if constexpr (Q == RD_TENSOR) {
+                    lds_act_slice<true>(hrow, s + u, hh, v);
+                } else {
+                    e4m3x16_to_f32(va[u][0], v);
+                    e4m3x16_to_f32(va[u][1], v + 16);
+                }
+                d = dot_slice<FP8>(vw[u], v);
             }
-            const float d = dot_slice<FP8>(vw[u], v);
             if constexpr (Q == RD_BLOCK) {
                 const int kb = (s + u) / 2;
                 const float sc = a.sh[(long)r * (a.I / 128) + kb] *
@@ -486,7 +521,11 @@ static hipError_t rd_gu_nw(const RdArgs& a, int U, hipStream_t st) {
     }
     if (U > 2) return hipErrorInvalidValue;
     switch (U) {
-        case 2: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 2>), grid, dim3(64 * NW), 0, st, a); break;
+        case 2:   // (e4m3 16-wave groups take one slice per batch)
+            if constexpr (NW < 16 || Q == RD_BF16)
+                hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 2>), grid, dim3(64 * NW), 0, st, a);
+            else return hipErrorInvalidValue;
+            break;
         default: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 1>), grid, dim3(64 * NW), 0, st, a); break;
     }
     return hipGetLastError();
