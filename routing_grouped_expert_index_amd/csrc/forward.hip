@@ -239,12 +239,35 @@ combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, con
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        const float w = tw[(size_t)t * k + j];
-        float v[8];
-        load8<uint16_t>(y + (size_t)route_pos[(size_t)t * k + j] * H + c, v);
+    // eight slots at a time: their positions and gates (uniform, scalar loads),
+    // then all eight y rows requested before the first one is used; slots past
+    // k re-read slot k-1 and are not added.  The sum still runs in ascending j.
+    const __attribute__((address_space(4))) int32_t* rp =
+        (const __attribute__((address_space(4))) int32_t*)(route_pos + (size_t)t * k);
+    const __attribute__((address_space(4))) float* wp =
+        (const __attribute__((address_space(4))) float*)(tw + (size_t)t * k);
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        int pos[8];
+        float w[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+        for (int jj = 0; jj < 8; ++jj) {
+            const int j = min(j0 + jj, k - 1);
+            pos[jj] = rp[j];
+            w[jj] = wp[j];
+        }
+        u32x4 raw[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) raw[jj] = *reinterpret_cast<const u32x4*>(y + (size_t)pos[jj] * H + c);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            if (j0 + jj < k) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = fmaf(w[jj], __uint_as_float(raw[jj][i] << 16), acc[2 * i]);
+                    acc[2 * i + 1] = fmaf(w[jj], __uint_as_float(raw[jj][i] & 0xffff0000u), acc[2 * i + 1]);
+                }
+            }
+        }
     }
     u32x4 o;
 #pragma unroll

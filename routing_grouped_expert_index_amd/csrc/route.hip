@@ -61,34 +61,47 @@ __device__ __forceinline__ float wave_sum_full(float v) {
 // value travels back through memory.  Logits are taken as finite (with NaN the
 // picks stay in range but their order is unspecified).
 template <int VPL>
-__device__ void topk_one_token(const float* __restrict__ row, int E, int k,
-                               int32_t* __restrict__ ids, float* __restrict__ w,
-                               int32_t* __restrict__ ids_lds, int32_t* __restrict__ cnt_lds) {
-    const int lane = lane_id();
+struct TopkRow {
     float v[VPL];
-    int slot[VPL];
-    uint32_t avail = 0;
+    uint32_t avail;
+};
+
+// the row's logits, lane + 64 i for i < VPL (-0 -> +0; comparisons treat them
+// equal anyway).  The loads are unconditional (a clamped index, masked after):
+// a guarded load compiles to a branch that waits for every load before it.
+template <int VPL>
+__device__ __forceinline__ void topk_load(const float* __restrict__ row, int E, TopkRow<VPL>& r) {
+    const int lane = lane_id();
+    r.avail = 0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e = lane + kWave * i;
-        v[i] = -INFINITY;
-        slot[i] = -1;
-        if (e < E) {
-            v[i] = row[e] + 0.0f;   // -0 -> +0 (comparisons treat them equal anyway)
-            avail |= 1u << i;
-        }
+        const float x = row[e < E ? e : E - 1] + 0.0f;
+        r.v[i] = e < E ? x : -INFINITY;
+        r.avail |= (e < E ? 1u : 0u) << i;
     }
+}
+
+template <int VPL>
+__device__ __forceinline__ void topk_pick(TopkRow<VPL>& r, int k, int32_t* __restrict__ ids,
+                                          float* __restrict__ w, int32_t* __restrict__ ids_lds,
+                                          int32_t* __restrict__ cnt_lds) {
+    const int lane = lane_id();
+    int slot[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) slot[i] = -1;
+    uint32_t avail = r.avail;
     float m = 0.0f;
     for (int j = 0; j < k; ++j) {
         float lm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
-            if ((avail >> i) & 1u) lm = fmaxf(lm, v[i]);
+            if ((avail >> i) & 1u) lm = fmaxf(lm, r.v[i]);
         const float M = wave_max_full(lm);
         int win = -1;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
-            const uint64_t b = __ballot(((avail >> i) & 1u) && v[i] == M);
+            const uint64_t b = __ballot(((avail >> i) & 1u) && r.v[i] == M);
             if (win < 0 && b != 0) win = __builtin_ctzll(b) + kWave * i;
         }
 #pragma unroll
@@ -104,18 +117,35 @@ __device__ void topk_one_token(const float* __restrict__ row, int E, int k,
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-        if (slot[i] >= 0) part += expf(v[i] - m);
+        if (slot[i] >= 0) part += expf(r.v[i] - m);
     const float S = wave_sum_full(part);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         if (slot[i] >= 0) {
             const int e = lane + kWave * i, j = slot[i];
             ids[j] = e;
-            w[j] = expf(v[i] - m) / S;
+            w[j] = expf(r.v[i] - m) / S;
             if (ids_lds) ids_lds[j] = e;
             if (cnt_lds) atomicAdd(&cnt_lds[e], 1);
         }
     }
+}
+
+// Picks the k largest logits of one token (row) with one whole wave.  Pick j is
+// the largest value left (a wave max), and of the lanes holding it the lowest
+// expert id (ballots, taken in id order: id = lane + 64 i).  Gates:
+// exp(l_j - m) / sum over the picks of exp(l_i - m), m = the largest logit (the
+// full softmax denominator cancels in the renormalisation).  The lane that owns
+// a picked logit remembers its slot j and writes ids[j] and w[j] itself, so no
+// value travels back through memory.  Logits are taken as finite (with NaN the
+// picks stay in range but their order is unspecified).
+template <int VPL>
+__device__ void topk_one_token(const float* __restrict__ row, int E, int k,
+                               int32_t* __restrict__ ids, float* __restrict__ w,
+                               int32_t* __restrict__ ids_lds, int32_t* __restrict__ cnt_lds) {
+    TopkRow<VPL> r;
+    topk_load<VPL>(row, E, r);
+    topk_pick<VPL>(r, k, ids, w, ids_lds, cnt_lds);
 }
 
 // ----------------------------------------------------------------------------
@@ -211,10 +241,10 @@ route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int nb
 }
 
 // ----------------------------------------------------------------------------
-// Large T*k: three kernels, 64 tokens per workgroup of 4 waves.
-constexpr int kTokPerBlock = 64;
+// Large T*k: three kernels over blocks of 16 tokens (top-k: one wave per token).
+constexpr int kTokPerBlock = 16;
 constexpr int kBigWaves = 4;          // scatter kernel
-constexpr int kTopkWaves = 16;        // top-k kernel: 4 tokens per wave
+constexpr int kTopkWaves = 16;        // top-k kernel: one token per wave
 
 template <int VPL>
 __global__ void __launch_bounds__(kTopkWaves * kWave)
@@ -226,88 +256,115 @@ route_topk_hist_kernel(const float* __restrict__ logits, int T, int E, int k,
     const int t0 = blockIdx.x * kTokPerBlock, t1 = min(T, t0 + kTokPerBlock);
     for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
-    for (int t = t0 + wave; t < t1; t += kTopkWaves)
-        topk_one_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
-                            weights + (size_t)t * k, nullptr, cnt);
+    // the wave's tokens t0 + wave + 16 i: every row is requested before the first pick
+    constexpr int TPW = kTokPerBlock / kTopkWaves;
+    TopkRow<VPL> rows[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {   // (rows past the block's end re-read its last row, unused)
+        const int t = min(t0 + wave + kTopkWaves * i, t1 - 1);
+        topk_load<VPL>(logits + (size_t)t * E, E, rows[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int t = t0 + wave + kTopkWaves * i;
+        if (t < t1)
+            topk_pick<VPL>(rows[i], k, ids + (size_t)t * k, weights + (size_t)t * k, nullptr, cnt);
+    }
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x) block_hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Column scan over workgroups (per expert) and the exclusive prefix over experts.
-// P = 1024 / E' threads share a column (E' = E rounded up to a power of two):
-// each sums a contiguous run of workgroup rows, the P partial sums are scanned
-// in LDS, and each thread then rewrites its run as a running prefix.
-constexpr int kScanThreads = 1024;
+// Column scan over the workgroup histograms: block b's count of expert e
+// becomes the number of expert e's routes in blocks before b, and counts[e] the
+// column total.  A workgroup owns 8 expert columns; its 32 row groups per
+// column each keep their rows in registers between the two passes (a single
+// workgroup moving the whole histogram would be bound by one CU's bandwidth).
+// The exclusive prefix over experts is taken by the scatter kernel.
+constexpr int kScanCols = 8;
+constexpr int kScanGroups = 32;
+constexpr int kScanRows = 16;   // rows per thread and chunk, loads in flight together
 
-__global__ void __launch_bounds__(kScanThreads)
-route_scan_kernel(int nblk, int E, int R, int32_t* __restrict__ block_hist,
-                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-    __shared__ int32_t part[kScanThreads];
-    __shared__ int32_t wsum[kScanThreads / kWave];
-    int Ep = 1;
-    while (Ep < E) Ep <<= 1;
-    const int P = kScanThreads / Ep;
-    const int e = threadIdx.x % Ep, p = threadIdx.x / Ep;
-    const int per = ceil_div(nblk, P);
+__global__ void __launch_bounds__(kScanCols * kScanGroups)
+route_scan_kernel(int nblk, int E, int32_t* __restrict__ block_hist, int32_t* __restrict__ counts) {
+    __shared__ int32_t part[kScanGroups][kScanCols];
+    const int c = threadIdx.x % kScanCols, p = threadIdx.x / kScanCols;
+    const int e = blockIdx.x * kScanCols + c, ec = min(e, E - 1);
+    const int per = ceil_div(nblk, kScanGroups);
     const int b0 = min(nblk, p * per), b1 = min(nblk, b0 + per);
+    // unconditional loads of clamped rows, masked afterwards (a guarded load
+    // compiles to a branch that waits for everything before it)
     int sum = 0;
-    if (e < E) {
-        for (int b = b0; b < b1; b += 16) {
-            int c[16];
+    for (int b = b0; b < b1; b += kScanRows) {
+        int v[kScanRows];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) c[i] = b + i < b1 ? block_hist[(size_t)(b + i) * E + e] : 0;
+        for (int i = 0; i < kScanRows; ++i) v[i] = block_hist[(size_t)min(b + i, nblk - 1) * E + ec];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sum += c[i];
-        }
+        for (int i = 0; i < kScanRows; ++i) sum += b + i < b1 ? v[i] : 0;
     }
-    part[threadIdx.x] = sum;
+    part[p][c] = sum;
     __syncthreads();
-    // exclusive prefix of this thread's run within its column, and the column total
     int before = 0, total = 0;
-    for (int q = 0; q < P; ++q) {
-        const int v = part[q * Ep + e];
-        if (q < p) before += v;
-        total += v;
+    for (int q = 0; q < kScanGroups; ++q) {
+        const int x = part[q][c];
+        if (q < p) before += x;
+        total += x;
     }
+    __syncthreads();   // every thread has read its rows before any is rewritten
     if (e < E) {
         int run = before;
-        for (int b = b0; b < b1; b += 16) {
-            int c[16];
+        for (int b = b0; b < b1; b += kScanRows) {
+            int v[kScanRows];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) c[i] = b + i < b1 ? block_hist[(size_t)(b + i) * E + e] : 0;
+            for (int i = 0; i < kScanRows; ++i) v[i] = block_hist[(size_t)min(b + i, nblk - 1) * E + e];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (b + i < b1) block_hist[(size_t)(b + i) * E + e] = run;
-                run += c[i];
+            for (int i = 0; i < kScanRows; ++i) {
+                if (b + i < b1) {
+                    block_hist[(size_t)(b + i) * E + e] = run;
+                    run += v[i];
+                }
             }
         }
+        if (p == 0) counts[e] = total;
     }
-    // exclusive prefix over experts (threads p == 0 hold the column totals)
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const int t = (p == 0 && e < E) ? total : 0;
-    int incl = t;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    if (lane == kWave - 1) wsum[wave] = incl;
-    __syncthreads();
-    if (p == 0 && e < E) {
-        int wb = 0;
-        for (int w = 0; w < wave; ++w) wb += wsum[w];
-        counts[e] = total;
-        offsets[e] = wb + incl - t;
-    }
-    if (threadIdx.x == 0) offsets[E] = R;
 }
 
 __global__ void __launch_bounds__(kBigWaves * kWave)
 route_scatter_kernel(int T, int E, int k, int nbits, const int32_t* __restrict__ ids,
-                     const int32_t* __restrict__ block_hist, const int32_t* __restrict__ offsets,
-                     int32_t* __restrict__ perm, int32_t* __restrict__ route_pos) {
+                     const int32_t* __restrict__ block_hist, const int32_t* __restrict__ counts,
+                     int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                     int32_t* __restrict__ route_pos) {
     __shared__ int32_t wcnt[kBigWaves * kMaxExperts];
+    __shared__ int32_t base[kMaxExperts];
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    if (wave == 0) {
+        // exclusive prefix of the E counts, 8 per lane (E <= 512); workgroup 0
+        // publishes it as the expert offsets
+        int cv[8], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = lane * 8 + i;
+            cv[i] = counts[e < E ? e : E - 1];
+            cv[i] = e < E ? cv[i] : 0;
+            sum += cv[i];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        int run = incl - sum;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = lane * 8 + i;
+            if (e < E) {
+                base[e] = run;
+                if (blockIdx.x == 0) offsets[e] = run;
+            }
+            run += cv[i];
+        }
+        if (blockIdx.x == 0 && lane == kWave - 1) offsets[E] = run;
+    }
     const int r0 = blockIdx.x * kTokPerBlock * k;
     const int r1 = min(T, (blockIdx.x + 1) * kTokPerBlock) * k;
     const int per = ceil_div(r1 - r0, kBigWaves);
@@ -317,7 +374,7 @@ route_scatter_kernel(int T, int E, int k, int nbits, const int32_t* __restrict__
     for (int r = lo + lane; r < hi; r += kWave) atomicAdd(&wcnt[wave * E + ids[r]], 1);
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x) {
-        int run = offsets[e] + block_hist[(size_t)blockIdx.x * E + e];
+        int run = base[e] + block_hist[(size_t)blockIdx.x * E + e];
         for (int w = 0; w < kBigWaves; ++w) {
             const int c = wcnt[w * E + e];
             wcnt[w * E + e] = run;
@@ -390,11 +447,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, const RouteOut
     int32_t* hist = static_cast<int32_t*>(ws);
     hipError_t err = MOE_VPL_DISPATCH(E, launch_topk_hist, logits, T, E, k, o, hist, st);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, nblk, E, T * k, hist,
-                       o.counts, o.offsets);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(ceil_div(E, kScanCols)), dim3(kScanCols * kScanGroups), 0, st,
+                       nblk, E, hist, o.counts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(kBigWaves * kWave), 0, st, T, E, k,
-                       bits_for(E), o.ids, hist, o.offsets, o.perm, o.route_pos);
+                       bits_for(E), o.ids, hist, o.counts, o.offsets, o.perm, o.route_pos);
     return hipGetLastError();
 }
 
