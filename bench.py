@@ -192,6 +192,24 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
             torch.cuda.synchronize()
             return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3   # us
 
+        # route and forward separately: one event between the two calls
+        tr, tf = [], []
+        for it in range(iters + 2):
+            load(it)
+            evict.amax()
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            moe.route(layer.lg, wl.k, out=layer.routes, workspace=layer.rws)
+            e1.record()
+            moe.forward(layer.x, layer.routes, layer.pgu, layer.pd, quant=wl.quant, scales=layer.scales,
+                        out=layer.out, path=layer.path, workspace=layer.ws)
+            e2.record()
+            if it >= 2:
+                tr.append((e0, e1))
+                tf.append((e1, e2))
+        torch.cuda.synchronize()
+        t_route_only = float(np.median([a.elapsed_time(b) for a, b in tr])) * 1e3
+        t_fwd_only = float(np.median([a.elapsed_time(b) for a, b in tf])) * 1e3
         t_fwd = timed(layer.step)
         # the step captured once (as a serving loop would) and replayed
         s = torch.cuda.Stream()
@@ -204,6 +222,17 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
         with torch.cuda.graph(g):
             layer.step()
         t_graph = timed(g.replay)
+        # warm: the captured step replayed back to back, weights left in the caches
+        nwarm = 200
+        for _ in range(10):
+            g.replay()
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record()
+        for _ in range(nwarm):
+            g.replay()
+        w1.record()
+        torch.cuda.synchronize()
+        t_graph_warm = w0.elapsed_time(w1) / nwarm * 1e3
         del g
         # stage events: the dominant kernel's duration
         ev_sets = []
@@ -230,17 +259,73 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
         D = float(np.mean(distinct))
         w_bytes = D * 3 * wl.H * wl.I * elem
         dom_bytes = D * 2 * wl.H * wl.I * elem + B * wl.H * elem   # Gate/Up weights + activations
-        res[B] = dict(us_per_layer=round(t_fwd, 2), us_per_layer_graph=round(t_graph, 2),
+        res[B] = dict(us_per_layer=round(t_fwd, 2), us_route=round(t_route_only, 2),
+                      us_forward=round(t_fwd_only, 2), us_per_layer_graph=round(t_graph, 2),
+                      us_per_layer_graph_warm=round(t_graph_warm, 2),
                       tokens_per_s=round(B / (t_fwd * 1e-6), 1),
                       path=layer.path, distinct_experts=round(D, 2),
+                      hbm_frac_forward=round(w_bytes / (t_fwd_only * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
                       hbm_frac_layer=round(w_bytes / (t_fwd * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
                       hbm_frac_layer_graph=round(w_bytes / (t_graph * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
                       dominant=dict(kernel=dname, bound="hbm", avg_launch_us=round(t_dom, 2),
                                     achieved=round(dom_bytes / (t_dom * 1e-6) / 1e9, 1),
                                     peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(dom_bytes / (t_dom * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)))
-        log(f"decode {name} B={B}: {t_fwd:.2f} us/layer ({t_graph:.2f} graph), "
+        log(f"decode {name} B={B}: {t_fwd:.2f} us/layer (route {t_route_only:.2f} + forward {t_fwd_only:.2f}; "
+            f"graph {t_graph:.2f}, warm graph {t_graph_warm:.2f}), "
             f"{res[B]['dominant']['kernel']} {t_dom:.2f} us {res[B]['dominant']['achieved']} GB/s")
+    del evict
+    return res
+
+
+def layer_fractions(wl, t_step, peak_tflops):
+    """The whole step against the dense MFMA peak and against HBM: algorithmic flops
+    6*R*H*I; the HBM floor with the gather fused = every expert's weights once, x
+    once (FP8: and its quantised copy written and read), h and y written and read
+    once, out written once."""
+    R = wl.T * wl.k
+    elem_w = 2 if wl.quant == "bf16" else 1
+    flops = 6.0 * R * wl.H * wl.I
+    h_b = 2 if wl.quant == "bf16" else 1
+    bytes_floor = (wl.E * 3 * wl.H * wl.I * elem_w + wl.T * wl.H * 2 + 2 * R * wl.I * h_b
+                   + 2 * R * wl.H * 2 + wl.T * wl.H * 2)
+    if wl.quant != "bf16":
+        bytes_floor += 2 * wl.T * wl.H        # the quantised x, written and read once
+    mf = flops / t_step / (peak_tflops * 1e12)
+    hf = bytes_floor / t_step / (PEAK_HBM_GBS * 1e9)
+    return dict(flops=flops, bytes_floor=bytes_floor, mfma_frac=round(mf, 4), hbm_frac=round(hf, 4),
+                bound_frac=round(max(mf, hf), 4), us_per_step=round(t_step * 1e6, 2))
+
+
+def bench_crossover(torch, moe, name, batches, iters, nsets=16):
+    """Cold route+forward latency with the path forced each way, for the dispatch rule."""
+    from workloads import WORKLOADS, random_activations, workload_weights
+    wl = WORKLOADS[name]
+    weights = dev_weights(torch, moe, workload_weights(name), wl.quant)
+    evict = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    res = {}
+    for B in batches:
+        xs = [dev_inputs(torch, random_activations(B, wl.H, wl.E, 10000 + i), wl) for i in range(nsets)]
+        row = {}
+        for path in ("grouped", "route_direct"):
+            layer = Layer(torch, moe, wl, B, xs[0][0].clone(), xs[0][1].clone(), weights, path=path)
+            ts = []
+            for it in range(iters + 2):
+                layer.x.copy_(xs[it % nsets][0])
+                layer.lg.copy_(xs[it % nsets][1])
+                evict.amax()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                layer.step()
+                e1.record()
+                if it >= 2:
+                    ts.append((e0, e1))
+            torch.cuda.synchronize()
+            row[path] = round(float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3, 2)
+        row["auto"] = moe.select_path(B, wl.H, wl.I, wl.E, wl.k, wl.quant, "auto")
+        res[B] = row
+        log(f"crossover {name} B={B}: grouped {row['grouped']} us, route_direct {row['route_direct']} us, "
+            f"auto takes {row['auto']}")
     del evict
     return res
 
@@ -277,6 +362,8 @@ def profile_only(torch, moe, args):
                 torch.mul(src, 1, out=dst)
             torch.cuda.synchronize()
             log(f"copy: {args.steps} x 1 GiB elementwise copy kernels")
+        elif name.startswith("crossover_"):
+            bench_crossover(torch, moe, name[len("crossover_"):], range(1, 17), 30)
         elif name.startswith("prefill"):
             pf = bench_prefill(torch, moe, name, args.steps, args.warmup)
             log(f"{name}: {pf['dt'] / args.steps * 1e3:.3f} ms/step, stages us "
@@ -329,6 +416,7 @@ def main():
                             path=pf["path"], routing="softmax top-8 renormalised, Zipf-skewed load",
                             max_expert_rows=int(pf["counts"].max()), min_expert_rows=int(pf["counts"].min())),
                 roofline=roof,
+                layer=layer_fractions(wl, pf["dt"] / args.steps, PEAK_BF16_TFLOPS),
                 stages_us={k: round(v * 1e3, 2) for k, v in pf["stages_ms"].items()})
     a, w = pf["host"]
     del pf["layer"]
@@ -337,11 +425,19 @@ def main():
     log("decode bf16 B=1..4 (cold HBM) ...")
     line["decode"] = dict(workload="decode_bf16 H=2048 I=768 E=128 top-8", timing="cold HBM, median of "
                           f"{args.decode_iters}; us_per_layer: moe_route + moe_forward launched on "
-                          "the stream between two HIP events; _graph: the same step replayed from "
-                          "a HIP graph; dominant: the kernel between stage events",
+                          "the stream between two HIP events (us_route, us_forward: the two calls "
+                          "separately); _graph: the same step replayed from a HIP graph, cold; "
+                          "_graph_warm: replayed back to back with the weights cached; dominant: "
+                          "the kernel between stage events",
                           batches=bench_decode(torch, moe, "decode_bf16", (1, 2, 3, 4), args.decode_iters))
     torch.cuda.empty_cache()
     if not args.quick:
+        log("dispatch crossover (cold, forced paths) ...")
+        line["crossover"] = dict(
+            timing="cold HBM, moe_route + moe_forward between two HIP events, median",
+            decode_fp8_tensor=bench_crossover(torch, moe, "decode_fp8_tensor", range(1, 17), 30),
+            decode_bf16=bench_crossover(torch, moe, "decode_bf16", range(1, 17), 30))
+        torch.cuda.empty_cache()
         log("decode fp8 per-tensor B=1..4 ...")
         line["decode_fp8_per_tensor"] = dict(
             workload="decode_fp8_tensor H=4096 I=192 E=192 top-8",
@@ -355,6 +451,7 @@ def main():
             workload="prefill_fp8_block T=4096 H=4096 I=512 E=128 top-8",
             tokens_per_s=round(w5.T * args.steps / p5["dt"], 1),
             ms_per_step=round(p5["dt"] / args.steps * 1e3, 4), roofline=r5,
+            layer=layer_fractions(w5, p5["dt"] / args.steps, PEAK_FP8_TFLOPS),
             stages_us={k: round(v * 1e3, 2) for k, v in p5["stages_ms"].items()})
         del p5
         torch.cuda.empty_cache()

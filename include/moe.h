@@ -116,7 +116,10 @@ int moe_pack_weights(const void *w_gate_up, const void *w_down, int E, int H, in
                      int quant, void *packed_gate_up, void *packed_down, void *stream);
 
 /* The path MOE_PATH_AUTO takes for this shape, or a negative moe_status if
- * the requested path cannot run it.  Host-only; no GPU call. */
+ * the requested path cannot run it.  Host-only; no GPU call.
+ * ("perf: add small-batch route MMA for MoE", Dispatch.)  AUTO takes the
+ * route-direct path while T*k <= 3E/4 and T <= 16 and the shape fits it
+ * (the bound measured on MI355X with both paths forced), else grouped. */
 int moe_select_path(int T, int H, int I, int E, int k, int quant, int path);
 
 /* Bytes of workspace moe_forward needs for this shape, quantisation and path. */

@@ -33,11 +33,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-// Dispatch: the route-direct path wins while the batch is so small that most
+// Dispatch: the route-direct path wins while the batch is so small that many
 // experts receive no route ("perf: add small-batch route MMA for MoE", Motivation
-// and Dispatch: production range batch 1-4 at top-k 8).  The rule here keeps
-// that range, expressed in routes: T <= 4 and T*k <= E/2.
-constexpr int kRouteDirectMaxTokens = 4;
+// and Dispatch).  The bound comes from measuring both paths, forced, at batch
+// 1-16 and top-k 8 on this GPU (cold weights): with E=128, H=2048, I=768 bf16
+// route-direct is faster up to about 112 routes (0.85 E); with E=192, H=4096,
+// I=192 FP8 per-tensor still at 128 routes (0.67 E, the largest measured).
+// Rule: T*k <= 3E/4 and T <= 16 (the measured range).
+constexpr int kRouteDirectMaxTokens = 16;
 
 // Route-direct kernels stage one activation row in LDS: H * elem <= 8192 bytes
 // for Gate/Up, I * elem <= 2048 bytes for Down.
@@ -66,7 +69,7 @@ int check_shape(int T, int H, int I, int E, int k, int quant) {
 
 int resolve_path(int T, int H, int I, int E, int k, int quant, int path) {
     if (path == MOE_PATH_AUTO) {
-        const bool small = T <= kRouteDirectMaxTokens && 2L * T * k <= E;
+        const bool small = T <= kRouteDirectMaxTokens && 4L * T * k <= 3L * E;
         return (small && rd_shape_ok(H, I, k, quant)) ? MOE_PATH_ROUTE_DIRECT : MOE_PATH_GROUPED;
     }
     if (path == MOE_PATH_GROUPED) return path;

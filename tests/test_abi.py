@@ -27,11 +27,14 @@ def test_library_exports_every_declared_function():
 
 
 def test_select_path_rules():
-    # decode batches below the expert count go route-direct, prefill goes grouped
+    # route-direct while T*k <= 3E/4 and T <= 16 (the measured crossover), prefill goes grouped
     assert moe.select_path(1, 2048, 768, 128, 8) == "route_direct"
     assert moe.select_path(4, 2048, 768, 128, 8) == "route_direct"
+    assert moe.select_path(12, 2048, 768, 128, 8) == "route_direct"     # 96 routes = 3E/4
+    assert moe.select_path(13, 2048, 768, 128, 8) == "grouped"
     assert moe.select_path(4, 4096, 192, 192, 8, "fp8_per_tensor") == "route_direct"
-    assert moe.select_path(5, 4096, 192, 192, 8, "fp8_per_tensor") == "grouped"
+    assert moe.select_path(16, 4096, 192, 192, 8, "fp8_per_tensor") == "route_direct"
+    assert moe.select_path(17, 4096, 192, 192, 8, "fp8_per_tensor") == "grouped"   # past 16 tokens
     assert moe.select_path(8192, 2048, 768, 128, 8) == "grouped"
     assert moe.select_path(64, 256, 512, 16, 8) == "grouped"
     assert moe.select_path(1, 2048, 768, 128, 8, "bf16", "grouped") == "grouped"
