@@ -60,6 +60,7 @@ struct RdArgs {
     int32_t* cnt;            // Down arrival counters [T*H/32], zeroed by the Gate/Up kernel
     uint16_t* out;           // [T][H]
     int T, H, I, E, k;
+    int kp;                  // per-block Down: K parts per route slot
 };
 
 // 8 values from 16 bytes of bf16
@@ -465,6 +466,123 @@ rd_down_part_kernel(const RdArgs a) {
     }
 }
 
+// ------------------------------------------------------- Down, per block --
+// When one output block's Down weights are small (k slots x 32 rows x I
+// elements, at most 64 KB), a workgroup owns (token, 32 output columns) with
+// all k route slots: its waves take (slot, K part) pieces, request each piece's
+// weight slices at once, and the pieces meet in LDS in a fixed order -- no
+// partial sums in memory and no arrival counter.  Larger blocks take the split
+// form above, which spreads them over more CUs (one CU streams about 20 GB/s).
+constexpr int kRdBlockWaves = 16;
+constexpr int kRdBlockMaxSlices = 12;         // per piece, held in registers (bf16)
+constexpr int kRdBlockMaxSlicesFp8 = 4;       // e4m3 (decoding needs more registers)
+constexpr int kRdBlockMaxItems = 64;
+constexpr int kRdBlockStage = kRdBlockMaxSlices * kSliceBytes;   // staged activations per wave
+constexpr long kRdBlockMaxBytes = 64 * 1024;  // one block's Down weights
+
+template <int Q>
+__global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const RdArgs a) {
+    constexpr bool FP8 = Q != RD_BF16;
+    constexpr int elem = FP8 ? 1 : 2;
+    constexpr int MS = FP8 ? kRdBlockMaxSlicesFp8 : kRdBlockMaxSlices;
+    __shared__ __attribute__((aligned(16))) uint8_t hst_all[kRdBlockWaves * kRdBlockStage];
+    __shared__ float red[kRdBlockMaxItems * 32];
+    const int nw = blockDim.x >> 6;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int j = lane & 31, hh = lane >> 5;
+    const int nb = a.H / 32, t = blockIdx.x / nb, g32 = blockIdx.x - t * nb;
+    const int Kb = a.I * elem, NSL = Kb / kSliceBytes;
+    const int KP = a.kp, spw = NSL / KP, items = a.k * KP;
+    uint8_t* hst = hst_all + wave * kRdBlockStage;
+    float hs = 1.0f;
+    if constexpr (Q == RD_TENSOR) {
+        // the whole-tensor h scale from the Gate/Up workgroups' maxima (loads of
+        // clamped indices, masked after: a guarded load waits for all before it)
+        const int nmax = a.T * a.k * (a.I / 32);
+        float m = 0.0f;
+        for (int base = 0; base < nmax; base += 512) {
+            float mv[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) mv[q] = a.hmax[min(base + lane + 64 * q, nmax - 1)];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) m = base + lane + 64 * q < nmax ? fmaxf(m, mv[q]) : m;
+        }
+        hs = scale_from_amax(wave_max(m));
+    }
+    for (int it = wave; it < items; it += nw) {
+        const int jj = it / KP, kp = it - jj * KP;
+        const int r = t * a.k + jj, e = a.ids[r];
+        const int s0 = kp * spw;
+        const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + (long)s0 * 2048 + lane * 16;
+        u32x4 vw[MS][2];
+#pragma unroll
+        for (int u = 0; u < MS; ++u)
+            if (u < spw)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    vw[u][q] = *reinterpret_cast<const u32x4*>(wb + u * 2048 + q * 1024);
+        __builtin_amdgcn_sched_barrier(0);
+        // the piece's activations into this wave's LDS area: bf16 h copied,
+        // per-tensor fp32 h quantised into e4m3 codes (clamped loads, masked)
+        if constexpr (Q == RD_TENSOR) {
+            const float* hp = reinterpret_cast<const float*>(a.h) + (long)r * a.I + s0 * 64;
+            const int ng = spw * 16;   // groups of 4 values
+            constexpr int GPL = (MS * 16 + 63) / 64;
+            f32x4 hv[GPL];
+#pragma unroll
+            for (int q = 0; q < GPL; ++q)
+                hv[q] = *reinterpret_cast<const f32x4*>(hp + 4 * min(lane + 64 * q, ng - 1));
+#pragma unroll
+            for (int q = 0; q < GPL; ++q) {
+                const int gi = lane + 64 * q;
+                if (gi < ng)
+                    reinterpret_cast<uint32_t*>(hst)[gi] =
+                        f32x4_to_e4m3x4(hv[q][0] / hs, hv[q][1] / hs, hv[q][2] / hs, hv[q][3] / hs);
+            }
+        } else {
+            const u32x4* hp = reinterpret_cast<const u32x4*>(a.h + (long)r * Kb + s0 * 64);
+            const int nq = spw * 4;    // 16-byte pieces
+            constexpr int QPL = (MS * 4 + 63) / 64;
+            u32x4 hv[QPL];
+#pragma unroll
+            for (int q = 0; q < QPL; ++q) hv[q] = hp[min(lane + 64 * q, nq - 1)];
+#pragma unroll
+            for (int q = 0; q < QPL; ++q)
+                if (lane + 64 * q < nq) reinterpret_cast<u32x4*>(hst)[lane + 64 * q] = hv[q];
+        }
+        // one wave's LDS accesses execute in order; this keeps the compiler from
+        // moving the reads above the writes
+        __asm__ volatile("" ::: "memory");
+        float y = 0.0f;
+#pragma unroll
+        for (int u = 0; u < MS; ++u) {
+            if (u < spw) {
+                if constexpr (!FP8) {
+                    u32x4 xw[2];
+                    lds_act_raw(hst, u, hh, xw);
+                    y = dot_slice_bf16(vw[u], xw, y);
+                } else {
+                    float v[32];
+                    lds_act_slice<true>(hst, u, hh, v);
+                    y += dot_slice<true>(vw[u], v);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);   // one slice's activations at a time
+        }
+        y += __shfl_xor(y, 32);
+        float gw = a.tw[r];
+        if constexpr (Q == RD_TENSOR) gw *= hs * a.s_d[e];
+        if (hh == 0) red[it * 32 + j] = gw * y;
+        __asm__ volatile("" ::: "memory");
+    }
+    __syncthreads();
+    if (wave == 0 && hh == 0) {
+        float o = 0.0f;
+        for (int it = 0; it < items; ++it) o += red[it * 32 + lane];   // fixed order
+        a.out[(long)t * a.H + down_col_of_packed(32 * g32 + lane)] = f32_to_bf16(o);
+    }
+}
+
 // ----------------------------------------------------------------------------
 
 static RdArgs rd_args(const FwdPlan& p) {
@@ -485,6 +603,7 @@ static RdArgs rd_args(const FwdPlan& p) {
     a.cnt = p.rd_cnt;
     a.out = p.out;
     a.T = p.T; a.H = p.H; a.I = p.I; a.E = p.E; a.k = p.k;
+    a.kp = 1;
     return a;
 }
 
@@ -614,8 +733,37 @@ static hipError_t rd_dn(const RdArgs& a, int quant, hipStream_t st) {
     }
 }
 
+// Per-block Down (bf16, FP8 per-tensor) when a block's weights are small:
+// K parts per slot (1, 2, 4) while k * kp fits 16 waves or a piece would exceed
+// the register budget; waves = min(16, k * kp), looping over pieces.
+struct RdBlockCfg {
+    bool ok;
+    int kp, nw;
+};
+static RdBlockCfg rd_block_cfg(int H, int I, int k, int quant) {
+    RdBlockCfg c{false, 1, 1};
+    if (quant == Q_FP8_BLOCK) return c;
+    const int elem = quant == Q_BF16 ? 2 : 1;
+    const int NSL = I * elem / kSliceBytes, ms = quant == Q_BF16 ? kRdBlockMaxSlices : kRdBlockMaxSlicesFp8;
+    if ((long)k * 32 * I * elem > kRdBlockMaxBytes || NSL < 1) return c;
+    while (c.kp < 4 && NSL % (c.kp * 2) == 0 && (k * c.kp * 2 <= kRdBlockWaves || NSL / c.kp > ms)) c.kp *= 2;
+    if (NSL % c.kp != 0 || NSL / c.kp > ms || k * c.kp > kRdBlockMaxItems) return c;
+    c.nw = k * c.kp < kRdBlockWaves ? k * c.kp : kRdBlockWaves;
+    c.ok = true;
+    (void)H;
+    return c;
+}
+
 hipError_t launch_route_direct_down(const FwdPlan& p, hipStream_t st) {
-    const RdArgs a = rd_args(p);
+    RdArgs a = rd_args(p);
+    const RdBlockCfg bc = rd_block_cfg(p.H, p.I, p.k, p.quant);
+    if (bc.ok) {
+        a.kp = bc.kp;
+        const dim3 grid((unsigned)((long)p.T * (p.H / 32))), block(64 * bc.nw);
+        if (p.quant == Q_BF16) hipLaunchKernelGGL((rd_down_block_kernel<RD_BF16>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((rd_down_block_kernel<RD_TENSOR>), grid, block, 0, st, a);
+        return hipGetLastError();
+    }
     if (p.quant == Q_BF16) return rd_dn<RD_BF16>(a, p.quant, st);
     if (p.quant == Q_FP8_TENSOR) return rd_dn<RD_TENSOR>(a, p.quant, st);
     return rd_dn<RD_BLOCK>(a, p.quant, st);
