@@ -60,7 +60,7 @@ struct FwdPlan {
     uint8_t* hq;                // e4m3 [R, I]
     float* sh;                  // block: [R, I/128]
     uint16_t* y;                // bf16 [R, H] (grouped path, sorted order)
-    float* rd_hmax;             // route-direct per-tensor: max |h| of each Gate/Up workgroup [R * I/32]
+    float* rd_hmax;             // route-direct per-tensor: max |h| of each Gate/Up workgroup [R * I/32 * split]
     float* rd_part;             // route-direct Down partial sums [T * H/32][items][32]
     int32_t* rd_cnt;            // route-direct Down arrival counters [T * H/32]
     int max_tiles;
@@ -75,6 +75,8 @@ hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st);
 hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st);
 hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st);
 hipError_t launch_combine(const FwdPlan& p, hipStream_t st);
+// workgroups sharing one route-direct Gate/Up 32-row block pair (1, 2 or 4)
+int rd_gate_up_split(int T, int H, int I, int k, int quant);
 hipError_t launch_route_direct_gate_up(const FwdPlan& p, hipStream_t st);
 // (slot, K part) items of one route-direct Down output block
 int rd_down_items(int T, int H, int I, int k, int quant);

@@ -110,7 +110,9 @@ Layout layout(int T, int H, int I, int E, int k, int quant, int path) {
     L.sh = take(quant == MOE_FP8_BLOCK128 ? sizeof(float) * R * (I / 128) : 0);
     L.y = take(grouped ? R * H * 2 : 0);
     const size_t rd_blocks = grouped ? 0 : (size_t)T * (H / 32);
-    L.rd_hmax = take(!grouped && quant == MOE_FP8_PER_TENSOR ? sizeof(float) * R * (I / 32) : 0);
+    L.rd_hmax = take(!grouped && quant == MOE_FP8_PER_TENSOR
+                         ? sizeof(float) * R * (I / 32) * moe::rd_gate_up_split(T, H, I, k, quant)
+                         : 0);
     L.rd_part = take(rd_blocks * sizeof(float) * 32 * (size_t)(grouped ? 0 : moe::rd_down_items(T, H, I, k, quant)));
     L.rd_cnt = take(rd_blocks * sizeof(int32_t));
     L.total = off;

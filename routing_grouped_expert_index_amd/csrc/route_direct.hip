@@ -37,6 +37,7 @@
 #include "layout.cuh"
 
 #include <algorithm>
+#include <atomic>
 #include <initializer_list>
 
 namespace moe {
@@ -61,6 +62,7 @@ struct RdArgs {
     uint16_t* out;           // [T][H]
     int T, H, I, E, k;
     int kp;                  // per-block Down: K parts per route slot
+    int rs;                  // Gate/Up row split (workgroups per 32-row block pair)
 };
 
 // 8 values from 16 bytes of bf16
@@ -218,28 +220,36 @@ rd_gate_up_kernel(const RdArgs a) {
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int j = lane & 31, hh = lane >> 5;
     const int r = blockIdx.x, G = blockIdx.y;   // route; 64-row group (gate block 2G, up block 2G+1)
+    // Row split RS = gridDim.z (1, 2, 4, 8): this workgroup owns rows
+    // [RW rs, RW rs + RW) of both blocks, RW = 32 / RS.  Lane j reads row
+    // RW rs + j % RW of slice RS S + j / RW of each super-slice S (RS
+    // consecutive slices), so one wave-wide load still fetches RS x RW rows x
+    // 32 distinct bytes, and the RS lanes of a row are added at the end.
+    const int lrs = __builtin_ctz(gridDim.z), RS = 1 << lrs, RW = 32 >> lrs, rs = blockIdx.z;
+    const int ls = j >> (5 - lrs), jr = rs * RW + (j & (RW - 1));
     const int t = r / a.k, e = a.ids[r];
     constexpr int elem = FP8 ? 1 : 2;
-    // wave w takes the U-slice chunks w, w + NW, w + 2 NW, ...: at each step the
-    // waves of the workgroup read one contiguous window of NW * U slices
-    const int Kb = a.H * elem, NSL = Kb / kSliceBytes, per = NSL / NW, s0 = wave * U;
-    constexpr int SB = NW * U;   // slice step between a wave's batches
+    // wave w takes the U-super-slice chunks w, w + NW, w + 2 NW, ...: at each
+    // step the waves of the workgroup read one contiguous window
+    const int Kb = a.H * elem, NSL = Kb / kSliceBytes, NSS = NSL >> lrs, per = NSS / NW, s0 = wave * U;
+    constexpr int SB = NW * U;   // super-slice step between a wave's batches
     const long gstride = 32L * Kb;
-    if (r == 0 && G == 0)   // the Down kernel that follows counts arrivals from zero
+    if (r == 0 && G == 0 && rs == 0)   // the Down kernel that follows counts arrivals from zero
         for (int i = threadIdx.x; i < a.T * (a.H / 32); i += 64 * NW) a.cnt[i] = 0;
-    const uint8_t* wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + lane * 16;
+    const uint8_t* wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + (32 * hh + jr) * 16 + ls * 2048;
     const uint8_t* wu = wg + gstride;
 
     // two load buffers: batch b+1 is requested before batch b is computed
     u32x4 vg[2][U][2], vu[2][U][2];
-    auto load_batch = [&](auto Bc, int s) __attribute__((always_inline)) {
+    auto load_batch = [&](auto Bc, int S) __attribute__((always_inline)) {
         constexpr int B = decltype(Bc)::value;
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                vg[B][u][q] = *reinterpret_cast<const u32x4*>(wg + (long)(s + u) * 2048 + q * 1024);
-                vu[B][u][q] = *reinterpret_cast<const u32x4*>(wu + (long)(s + u) * 2048 + q * 1024);
+                const long off = ((long)(S + u) << lrs) * 2048 + q * 1024;
+                vg[B][u][q] = *reinterpret_cast<const u32x4*>(wg + off);
+                vu[B][u][q] = *reinterpret_cast<const u32x4*>(wu + off);
             }
         __builtin_amdgcn_sched_barrier(0);   // the whole batch stays in flight
     };
@@ -263,24 +273,25 @@ rd_gate_up_kernel(const RdArgs a) {
     }
 
     float accg = 0.0f, accu = 0.0f;
-    auto compute = [&](auto Bc, int s) __attribute__((always_inline)) {
+    auto compute = [&](auto Bc, int S) __attribute__((always_inline)) {
         constexpr int B = decltype(Bc)::value;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const int sl = ((S + u) << lrs) + ls;   // this lane's slice
             float dg, du;
             if constexpr (!FP8) {
                 u32x4 xw[2];
-                lds_act_raw(xrow, s + u, hh, xw);
+                lds_act_raw(xrow, sl, hh, xw);
                 dg = dot_slice_bf16(vg[B][u], xw, 0.0f);
                 du = dot_slice_bf16(vu[B][u], xw, 0.0f);
             } else {
                 float v[32];
-                lds_act_slice<FP8>(xrow, s + u, hh, v);
+                lds_act_slice<FP8>(xrow, sl, hh, v);
                 dg = dot_slice<FP8>(vg[B][u], v);
                 du = dot_slice<FP8>(vu[B][u], v);
             }
             if constexpr (Q == RD_BLOCK) {
-                const int kb = (s + u) / 2;   // 128-deep scale block
+                const int kb = sl / 2;   // 128-deep scale block
                 const float sa = a.sx[(long)t * (a.H / 128) + kb];
                 const float* swr = a.s_gu + ((long)e * (a.H / 128) + kb) * (2 * a.I / 128);
                 accg = fmaf(dg, sa * swr[cg], accg);
@@ -291,36 +302,43 @@ rd_gate_up_kernel(const RdArgs a) {
             }
         }
     };
-    // nb batches of U slices: pairs while more than two remain (batch b+2 goes
-    // into the freed buffer), then the last one or two
+    // nb batches of U super-slices: pairs while more than two remain (batch b+2
+    // goes into the freed buffer), then the last one or two
     const int nb = per / U;
-    int s = s0, b = 0;
-    for (; b + 2 < nb; b += 2, s += 2 * SB) {
-        load_batch(B1, s + SB);
-        compute(B0, s);
-        load_batch(B0, s + 2 * SB);
-        compute(B1, s + SB);
+    int S = s0, b = 0;
+    for (; b + 2 < nb; b += 2, S += 2 * SB) {
+        load_batch(B1, S + SB);
+        compute(B0, S);
+        load_batch(B0, S + 2 * SB);
+        compute(B1, S + SB);
     }
     if (nb - b == 2) {
-        load_batch(B1, s + SB);
-        compute(B0, s);
-        compute(B1, s + SB);
+        load_batch(B1, S + SB);
+        compute(B0, S);
+        compute(B1, S + SB);
     } else {
-        compute(B0, s);
+        compute(B0, S);
     }
+    // the two K halves of a lane pair, then the RS slices of a row
     accg += __shfl_xor(accg, 32);
     accu += __shfl_xor(accu, 32);
-    if (hh == 0) {
+    for (int off = 16; off >= RW; off >>= 1) {
+        accg += __shfl_xor(accg, off);
+        accu += __shfl_xor(accu, off);
+    }
+    if (hh == 0 && j < RW) {
         red[wave][0][j] = accg;
         red[wave][1][j] = accu;
     }
     __syncthreads();
     if (wave == 0 && hh == 0) {
         float gv = 0.0f, uv = 0.0f;
+        if (j < RW) {
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            gv += red[w][0][j];
-            uv += red[w][1][j];
+            for (int w = 0; w < NW; ++w) {
+                gv += red[w][0][j];
+                uv += red[w][1][j];
+            }
         }
         if constexpr (Q == RD_TENSOR) {
             const float fsc = xs * a.s_gu[e];
@@ -329,17 +347,19 @@ rd_gate_up_kernel(const RdArgs a) {
         }
         const float hv = silu(gv) * uv;
         if constexpr (Q == RD_TENSOR) {   // this workgroup's share of the h amax
-            float m = fabsf(hv);
+            float m = j < RW ? fabsf(hv) : 0.0f;
 #pragma unroll
             for (int off = 16; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-            if (j == 0) a.hmax[(long)r * (a.I / 32) + G] = m;
+            if (j == 0) a.hmax[((long)r * (a.I / 32) + G) * RS + rs] = m;
         }
-        // row j of the pair's blocks is h column 32G + 16hh' + 4a + b, j = 8a + 4hh' + b
-        const int c = 32 * G + 16 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3);
-        if constexpr (Q == RD_BF16)
-            static_cast<uint16_t*>(a.hout)[(long)r * a.I + c] = f32_to_bf16(hv);
-        else
-            static_cast<float*>(a.hout)[(long)r * a.I + c] = hv;
+        // row jr of the pair's blocks is h column 32G + 16hh' + 4a + b, jr = 8a + 4hh' + b
+        const int c = 32 * G + 16 * ((jr >> 2) & 1) + 4 * (jr >> 3) + (jr & 3);
+        if (j < RW) {
+            if constexpr (Q == RD_BF16)
+                static_cast<uint16_t*>(a.hout)[(long)r * a.I + c] = f32_to_bf16(hv);
+            else
+                static_cast<float*>(a.hout)[(long)r * a.I + c] = hv;
+        }
     }
 }
 
@@ -390,7 +410,7 @@ rd_down_part_kernel(const RdArgs a) {
         // whole-tensor h amax from the Gate/Up workgroups' maxima, then this
         // route's h row quantised into LDS
         float m = 0.0f;
-        const int nmax = a.T * a.k * (a.I / 32);
+        const int nmax = a.T * a.k * (a.I / 32) * a.rs;
         for (int i = threadIdx.x; i < nmax; i += 64 * NW) m = fmaxf(m, a.hmax[i]);
         m = wave_max(m);
         if (lane == 0) red[wave][0] = m;
@@ -498,7 +518,7 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
     if constexpr (Q == RD_TENSOR) {
         // the whole-tensor h scale from the Gate/Up workgroups' maxima (loads of
         // clamped indices, masked after: a guarded load waits for all before it)
-        const int nmax = a.T * a.k * (a.I / 32);
+        const int nmax = a.T * a.k * (a.I / 32) * a.rs;
         float m = 0.0f;
         for (int base = 0; base < nmax; base += 512) {
             float mv[8];
@@ -604,6 +624,7 @@ static RdArgs rd_args(const FwdPlan& p) {
     a.out = p.out;
     a.T = p.T; a.H = p.H; a.I = p.I; a.E = p.E; a.k = p.k;
     a.kp = 1;
+    a.rs = rd_gate_up_split(p.T, p.H, p.I, p.k, p.quant);
     return a;
 }
 
@@ -616,64 +637,137 @@ static int largest_unroll(int n, int cap) {
     return 1;
 }
 
-// Waves per Gate/Up workgroup: enough waves in total to keep many weight
-// loads in flight at small batch (about 4096), K split evenly, at most 16.
-static int rd_waves(long groups, int NSL) {
-    int nw = 1;
-    while (nw < 16 && groups * nw * 2 <= 4096 && NSL % (nw * 2) == 0) nw *= 2;
-    return nw;
+// ---- Gate/Up launch shape
+//
+// Three choices per call: the row split RS (1, 2 or 4 workgroups share a
+// 32-row block pair, each taking RW = 32/RS rows of every slice: at RS = 4
+// one 128-byte line per slice half), the waves per workgroup nw (K split
+// evenly between them) and the slices per load batch U.  One workgroup
+// streams at only a fraction of HBM bandwidth and a decode step is short, so
+// the rule maximises the number of waves in flight (up to about 4096) among
+// the shapes whose whole grid is resident at once: a second round of
+// workgroups would double the kernel's time.  Residency comes from the
+// runtime's occupancy figure for the exact kernel.  Ties keep the smaller
+// split (measured: a split that only repacks the same waves into more,
+// smaller workgroups loses a little).  The blockwise format keeps RS = 1: its
+// scales are per 128-deep block.
+struct RdGuCfg {
+    int rs, nw, U;
+};
+
+// two load batches live in registers: 16-wave groups (128 VGPRs) take at most
+// 2 bf16 slices (1 e4m3) per batch, smaller groups 4 (2 e4m3), which keeps
+// every launched variant clear of spills
+static int rd_gu_unroll(int quant, int nw, int per) {
+    return largest_unroll(per, nw == 16 ? (quant != Q_BF16 ? 1 : 2) : (quant != Q_BF16 ? 2 : 4));
 }
 
 template <int Q, int NW>
-static hipError_t rd_gu_nw(const RdArgs& a, int U, hipStream_t st) {
-    dim3 grid(a.T * a.k, a.I / 32);
-    // the caller caps U at 4, and at 2 for 16-wave groups
+static const void* rd_gu_fn_nw(int U) {
     if constexpr (NW < 16) {
-        if (U == 4) {
-            hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 4>), grid, dim3(64 * NW), 0, st, a);
-            return hipGetLastError();
-        }
-        if (U == 3) {
-            hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 3>), grid, dim3(64 * NW), 0, st, a);
-            return hipGetLastError();
-        }
+        if (U == 4) return reinterpret_cast<const void*>(&rd_gate_up_kernel<Q, NW, 4>);
+        if (U == 3) return reinterpret_cast<const void*>(&rd_gate_up_kernel<Q, NW, 3>);
     }
-    if (U > 2) return hipErrorInvalidValue;
-    switch (U) {
-        case 2:   // (e4m3 16-wave groups take one slice per batch)
-            if constexpr (NW < 16 || Q == RD_BF16)
-                hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 2>), grid, dim3(64 * NW), 0, st, a);
-            else return hipErrorInvalidValue;
-            break;
-        default: hipLaunchKernelGGL((rd_gate_up_kernel<Q, NW, 1>), grid, dim3(64 * NW), 0, st, a); break;
+    if (U == 2) {
+        if constexpr (NW < 16 || Q == RD_BF16) return reinterpret_cast<const void*>(&rd_gate_up_kernel<Q, NW, 2>);
+        return nullptr;   // (e4m3 16-wave groups take one slice per batch)
     }
-    return hipGetLastError();
+    if (U == 1) return reinterpret_cast<const void*>(&rd_gate_up_kernel<Q, NW, 1>);
+    return nullptr;
 }
 
 template <int Q>
-static hipError_t rd_gu(const RdArgs& a, hipStream_t st) {
-    const int elem = Q == RD_BF16 ? 2 : 1;
-    const int NSL = a.H * elem / kSliceBytes;
-    const int nw = rd_waves((long)a.T * a.k * (a.I / 32), NSL);
-    // two load batches live in registers: 16-wave groups (128 VGPRs) take at
-    // most 2 bf16 slices (1 e4m3) per batch, smaller groups 4 (2 e4m3), which
-    // keeps every launched variant clear of spills
-    const int U = largest_unroll(NSL / nw, nw == 16 ? (Q != RD_BF16 ? 1 : 2) : (Q != RD_BF16 ? 2 : 4));
-    if (NSL % nw != 0 || (NSL / nw) % U != 0) return hipErrorInvalidValue;
+static const void* rd_gu_fn_q(int nw, int U) {
     switch (nw) {
-        case 1: return rd_gu_nw<Q, 1>(a, U, st);
-        case 2: return rd_gu_nw<Q, 2>(a, U, st);
-        case 4: return rd_gu_nw<Q, 4>(a, U, st);
-        case 8: return rd_gu_nw<Q, 8>(a, U, st);
-        default: return rd_gu_nw<Q, 16>(a, U, st);
+        case 1: return rd_gu_fn_nw<Q, 1>(U);
+        case 2: return rd_gu_fn_nw<Q, 2>(U);
+        case 4: return rd_gu_fn_nw<Q, 4>(U);
+        case 8: return rd_gu_fn_nw<Q, 8>(U);
+        case 16: return rd_gu_fn_nw<Q, 16>(U);
+        default: return nullptr;
     }
 }
 
+// the instantiated kernel for (quant, nw, U), null for a combination that is
+// not built
+static const void* rd_gu_fn(int quant, int nw, int U) {
+    if (quant == Q_BF16) return rd_gu_fn_q<RD_BF16>(nw, U);
+    if (quant == Q_FP8_TENSOR) return rd_gu_fn_q<RD_TENSOR>(nw, U);
+    return rd_gu_fn_q<RD_BLOCK>(nw, U);
+}
+
+// Workgroups of one kernel resident on the whole device at once, cached per
+// (device, quant, nw, U).  0 when the runtime cannot tell (the shape is then
+// never taken as resident).
+constexpr int kRdMaxDevices = 64;
+static long rd_gu_resident(int quant, int nw, int U) {
+    static std::atomic<int> cus[kRdMaxDevices];
+    static std::atomic<int> occ[kRdMaxDevices][3][5][9];   // 1 + occupancy, 0 = not asked yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kRdMaxDevices) return 0;
+    int lg = 0;
+    while ((1 << lg) < nw) ++lg;
+    if (quant < 0 || quant > 2 || lg > 4 || U < 1 || U > 8) return 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 0;
+        n = c + 1;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    int o = occ[dev][quant][lg][U].load(std::memory_order_relaxed);
+    if (o == 0) {
+        const void* fn = rd_gu_fn(quant, nw, U);
+        int blocks = 0;
+        if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64 * nw, 0) != hipSuccess) blocks = 0;
+        o = blocks + 1;
+        occ[dev][quant][lg][U].store(o, std::memory_order_relaxed);
+    }
+    return (long)(n - 1) * (o - 1);
+}
+
+static RdGuCfg rd_gu_cfg(int T, int H, int I, int k, int quant) {
+    const int NSL = H * (quant == Q_BF16 ? 2 : 1) / kSliceBytes;
+    const long groups = (long)T * k * (I / 32);
+    RdGuCfg best{0, 0, 0};
+    long best_waves = -1;
+    for (int rs = 1; rs <= (quant == Q_FP8_BLOCK ? 1 : 4); rs *= 2) {
+        if (NSL % rs != 0) break;
+        const int NSS = NSL / rs;
+        const long wgs = groups * rs;
+        RdGuCfg c{rs, 1, rd_gu_unroll(quant, 1, NSS)};
+        long waves = 0;   // one-wave groups when no larger shape is resident
+        for (int nw = 16; nw >= 1; nw /= 2) {
+            if (NSS % nw != 0 || wgs * nw > 4096) continue;
+            const int U = rd_gu_unroll(quant, nw, NSS / nw);
+            if (wgs <= rd_gu_resident(quant, nw, U)) {
+                c = RdGuCfg{rs, nw, U};
+                waves = wgs * nw;
+                break;
+            }
+        }
+        if (waves > best_waves) {
+            best = c;
+            best_waves = waves;
+        }
+    }
+    return best;
+}
+
+int rd_gate_up_split(int T, int H, int I, int k, int quant) { return rd_gu_cfg(T, H, I, k, quant).rs; }
+
 hipError_t launch_route_direct_gate_up(const FwdPlan& p, hipStream_t st) {
-    const RdArgs a = rd_args(p);
-    if (p.quant == Q_BF16) return rd_gu<RD_BF16>(a, st);
-    if (p.quant == Q_FP8_TENSOR) return rd_gu<RD_TENSOR>(a, st);
-    return rd_gu<RD_BLOCK>(a, st);
+    RdArgs a = rd_args(p);
+    const RdGuCfg c = rd_gu_cfg(p.T, p.H, p.I, p.k, p.quant);
+    const int NSL = p.H * (p.quant == Q_BF16 ? 2 : 1) / kSliceBytes;
+    // the kernel walks NSL / rs super-slices in nw x U steps and never past the end
+    if (c.rs < 1 || c.rs > 4 || NSL % c.rs != 0 || (NSL / c.rs) % (c.nw * c.U) != 0 ||
+        (p.quant == Q_FP8_BLOCK && c.rs != 1))
+        return hipErrorInvalidValue;
+    const void* fn = rd_gu_fn(p.quant, c.nw, c.U);
+    if (!fn) return hipErrorInvalidValue;
+    void* args[] = {&a};
+    return hipLaunchKernel(fn, dim3(p.T * p.k, p.I / 32, c.rs), dim3(64 * c.nw), args, 0, st);
 }
 
 // Down split: K parts per route (1, 2 or 4, dividing NSL) only while the grid
