@@ -6,8 +6,9 @@
 //
 // Design:
 //  * one wavefront per token; each lane keeps ceil(E/64) logits in registers
-//    and the k picks are k wave-wide (value, id) arg-max reductions, ties to
-//    the lower id (values are compared as floats, so -0 == +0);
+//    and the k picks are k wave-wide arg-max reductions over order-preserving
+//    integer keys of the values, ties to the lower id (-0 is read as +0, so
+//    the two compare equal);
 //  * counting sort without global atomics: workgroup histograms in LDS, a
 //    column scan over workgroups, then a stable scatter in which each wave
 //    ranks its routes with a ballot-based match (one ballot per key bit);
@@ -52,14 +53,24 @@ __device__ __forceinline__ float wave_sum_full(float v) {
     return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
 
-// Picks the k largest logits of one token (row) with one whole wave.  Pick j is
-// the largest value left (a wave max), and of the lanes holding it the lowest
-// expert id (ballots, taken in id order: id = lane + 64 i).  Gates:
-// exp(l_j - m) / sum over the picks of exp(l_i - m), m = the largest logit (the
-// full softmax denominator cancels in the renormalisation).  The lane that owns
-// a picked logit remembers its slot j and writes ids[j] and w[j] itself, so no
-// value travels back through memory.  Logits are taken as finite (with NaN the
-// picks stay in range but their order is unspecified).
+// Inclusive prefix sum over the 64 lanes of a fully active wave: shifts by 1,
+// 2, 4 and 8 inside each row of 16 (lanes shifted in from outside the row read
+// 0), then lane 15 of a row added to the next row (rows 1 and 3) and lane 31 to
+// rows 2 and 3.
+constexpr int kDppRowShr = 0x110;       // + n: lane i reads lane i - n of its row
+constexpr int kDppRowBcast15 = 0x142;   // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143;   // lane 31 to rows 2 and 3
+__device__ __forceinline__ int wave_scan_incl(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 1, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 2, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 4, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 8, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
+    return v;
+}
+
+// One token's logits in a wave: lane l holds ids l + 64 i, i < VPL.
 template <int VPL>
 struct TopkRow {
     float v[VPL];
@@ -82,38 +93,82 @@ __device__ __forceinline__ void topk_load(const float* __restrict__ row, int E, 
     }
 }
 
+// Order-preserving map of a float's bits to an unsigned key: a larger float
+// gives a larger key (-inf lowest, +inf highest among non-NaN values).
+__device__ __forceinline__ uint32_t order_key(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of order_key.
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Max over the 64 lanes of a fully active wave (unsigned): the exchanges of
+// wave_max_full, on integers (no NaN canonicalisation between the steps, and
+// each exchange folds into its max instruction).
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t x, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppRowMirror>(v));
+    return max(max(readlane_u32(v, 0), readlane_u32(v, 16)), max(readlane_u32(v, 32), readlane_u32(v, 48)));
+}
+
+// Picks the k largest logits of one token (row) with one whole wave: slot j
+// holds the j-th largest value, ties to the lower expert id.  Gates:
+// exp(l_j - m) / sum over the picks of exp(l_i - m), m = the largest logit (the
+// full softmax denominator cancels in the renormalisation).  The lane that owns
+// a picked logit writes ids[j] and w[j] itself, so no value travels back
+// through memory.  Logits are taken as finite (with NaN the picks stay in range
+// and distinct but their order is unspecified).
+//
+// Pick j is a wave max over order-preserving integer keys (taken and padding
+// entries hold key 0, real ones at least 1), then of the entries holding that
+// key the lowest id: a ballot per slot, taken in id order (id = lane + 64 i,
+// slot-major).  Some entry always holds the maximum key exactly, so no NaN
+// fallback is needed.
 template <int VPL>
 __device__ __forceinline__ void topk_pick(TopkRow<VPL>& r, int k, int32_t* __restrict__ ids,
                                           float* __restrict__ w, int32_t* __restrict__ ids_lds,
                                           int32_t* __restrict__ cnt_lds) {
     const int lane = lane_id();
+    uint32_t key[VPL];
     int slot[VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) slot[i] = -1;
-    uint32_t avail = r.avail;
-    float m = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        float lm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if ((avail >> i) & 1u) lm = fmaxf(lm, r.v[i]);
-        const float M = wave_max_full(lm);
-        int win = -1;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const uint64_t b = __ballot(((avail >> i) & 1u) && r.v[i] == M);
-            if (win < 0 && b != 0) win = __builtin_ctzll(b) + kWave * i;
-        }
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {   // no equal value (NaN): lowest id left
-            const uint64_t b = __ballot((avail >> i) & 1u);
-            if (win < 0 && b != 0) win = __builtin_ctzll(b) + kWave * i;
-        }
-        if (j == 0) m = M;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if (win == lane + kWave * i) { avail &= ~(1u << i); slot[i] = j; }
+    for (int i = 0; i < VPL; ++i) {
+        key[i] = ((r.avail >> i) & 1u) ? max(order_key(r.v[i]), 1u) : 0u;
+        slot[i] = -1;
     }
+    uint32_t top = 0;
+    for (int j = 0; j < k; ++j) {
+        uint32_t lm = key[0];
+#pragma unroll
+        for (int i = 1; i < VPL; ++i) lm = max(lm, key[i]);
+        const uint32_t M = wave_max_u32(lm);
+        if (j == 0) top = M;
+        int win = 0;
+#pragma unroll
+        for (int i = VPL - 1; i >= 0; --i) {   // the lowest slot holding M wins
+            const uint64_t b = __ballot(key[i] == M);
+            if (b != 0) win = __builtin_ctzll(b) + kWave * i;
+        }
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (win == lane + kWave * i) {
+                key[i] = 0;
+                slot[i] = j;
+            }
+    }
+    const float m = key_to_float(top);
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
@@ -129,23 +184,6 @@ __device__ __forceinline__ void topk_pick(TopkRow<VPL>& r, int k, int32_t* __res
             if (cnt_lds) atomicAdd(&cnt_lds[e], 1);
         }
     }
-}
-
-// Picks the k largest logits of one token (row) with one whole wave.  Pick j is
-// the largest value left (a wave max), and of the lanes holding it the lowest
-// expert id (ballots, taken in id order: id = lane + 64 i).  Gates:
-// exp(l_j - m) / sum over the picks of exp(l_i - m), m = the largest logit (the
-// full softmax denominator cancels in the renormalisation).  The lane that owns
-// a picked logit remembers its slot j and writes ids[j] and w[j] itself, so no
-// value travels back through memory.  Logits are taken as finite (with NaN the
-// picks stay in range but their order is unspecified).
-template <int VPL>
-__device__ void topk_one_token(const float* __restrict__ row, int E, int k,
-                               int32_t* __restrict__ ids, float* __restrict__ w,
-                               int32_t* __restrict__ ids_lds, int32_t* __restrict__ cnt_lds) {
-    TopkRow<VPL> r;
-    topk_load<VPL>(row, E, r);
-    topk_pick<VPL>(r, k, ids, w, ids_lds, cnt_lds);
 }
 
 // ----------------------------------------------------------------------------
@@ -172,10 +210,20 @@ route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int nb
     int32_t* base = wcnt + nws * E;              // [E + 1]
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
 
-    for (int i = tid; i < nws * E; i += blockDim.x) wcnt[i] = 0;
-    for (int t = wave; t < T; t += kSmallWaves)
-        topk_one_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
-                            weights + (size_t)t * k, sid + t * k, nullptr);
+    if (T > 0) {
+        // the first row of every wave is requested before the LDS set-up (waves
+        // past T re-read row T-1 and drop it: an unconditional load is not waited
+        // on early)
+        TopkRow<VPL> row;
+        topk_load<VPL>(logits + (size_t)min(wave, T - 1) * E, E, row);
+        for (int i = tid; i < nws * E; i += blockDim.x) wcnt[i] = 0;
+        for (int t = wave; t < T; t += kSmallWaves) {
+            if (t != wave) topk_load<VPL>(logits + (size_t)t * E, E, row);
+            topk_pick<VPL>(row, k, ids + (size_t)t * k, weights + (size_t)t * k, sid + t * k, nullptr);
+        }
+    } else {   // no routes: zero counts and offsets only (logits may be null)
+        for (int i = tid; i < nws * E; i += blockDim.x) wcnt[i] = 0;
+    }
     __syncthreads();
 
     // wave w < nws owns the contiguous route range [lo, hi)
@@ -204,13 +252,7 @@ route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int nb
             c[i] = e < E ? base[e] : 0;
             s += c[i];
         }
-        int incl = s;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
-        int run = incl - s;
+        int run = wave_scan_incl(s) - s;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int e = lane * 8 + i;
@@ -347,13 +389,7 @@ route_scatter_kernel(int T, int E, int k, int nbits, const int32_t* __restrict__
             cv[i] = e < E ? cv[i] : 0;
             sum += cv[i];
         }
-        int incl = sum;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
-        int run = incl - sum;
+        int run = wave_scan_incl(sum) - sum;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int e = lane * 8 + i;
