@@ -61,7 +61,7 @@ constexpr int WAIT_STEP = 4 * WLOADS + 3 * DMAS;
 constexpr int WAIT_W = 2 * WLOADS + WLOADS + DMAS;
 }  // namespace g32
 
-template <bool FP8, bool GATHER, int SC, int EPI>
+template <bool FP8, bool GATHER, int SC, int EPI, bool SHORT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm32_kernel(const GemmArgs g) {
     using namespace g32;
@@ -114,6 +114,17 @@ gemm32_kernel(const GemmArgs g) {
         return (uint32_t)(src * g.lda) + (uint32_t)(((lane & 3) ^ ((dma_r >> 2) & 3)) * 16);
     };
     // idle waves (past N) load a valid block, so every wave issues the same loads
+    // Epilogue stores are buffer stores through a resource covering C: the
+    // rows a wave must not write (tile padding, waves past N) get an offset
+    // past the end, which the range check drops, so every wave issues the same
+    // SX stores per tile and the K loop's waits can count them (below).
+    const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(g.C, 0, g.c_bytes, 0x00020000);
+    constexpr uint32_t kDropped = 0x80000000u;                // >= c_bytes (host: c_bytes < 2 GB)
+    constexpr int CPL = EPI == EPI_SWIGLU_BF16 ? 2 : 4;       // chunks per lane and row
+    constexpr int CB = 2 * CPL;                               // chunks per row segment
+    constexpr int RPP = kEpiStageBytes / (CB * 16);           // staged rows per phase
+    constexpr int MPP = RPP / 32;                             // m blocks per phase
+    constexpr int SX = (4 / MPP) * (RPP * CB / 64);           // store instructions per wave and tile
     auto make_wp = [&](int e_, int wn0_) __attribute__((always_inline)) {
         return g.B + (long)e_ * g.N * g.Kb + (long)((wn0_ < g.N ? wn0_ : 0) / 32) * gstride + lane * 16;
     };
@@ -224,11 +235,18 @@ gemm32_kernel(const GemmArgs g) {
     // (MFMAs of idle waves and of the padding rows run on valid data and are
     // dropped; a branch around them would make the compiler drain every load
     // first.)
-    auto step = [&](auto Uc, int s, bool last) __attribute__((always_inline)) {
+    //
+    // A tile's SX epilogue stores are issued after the next tile's prologue, so
+    // in the next tile's first four steps they sit between the awaited prologue
+    // requests and the newer ones: those steps count them (XS, and XW for the
+    // weights of slices 0-2).  vmcnt completes in issue order, so the stores are
+    // waited for only at step 4, whose token DMA was issued after them.
+    auto step = [&](auto Uc, int s, bool last, auto Xs, auto Xw) __attribute__((always_inline)) {
         constexpr int U = decltype(Uc)::value;
+        constexpr int XS = decltype(Xs)::value, XW = decltype(Xw)::value;
         wload(wp, min(s + 3, NSL - 1), (U + 3) & 3);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm_lgkm<WAIT_STEP>();
+        wait_vm_lgkm<WAIT_STEP + XS>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         __builtin_amdgcn_sched_barrier(0);
@@ -236,12 +254,18 @@ gemm32_kernel(const GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         // the weights of s were requested in step s-3 (or the prologue): at
         // least WAIT_W loads follow them
-        wait_vm_only<WAIT_W>();
+        wait_vm_only<WAIT_W + XW>();
         if (!last) mma(U, s % STAGES);
         else if (s < NSL) mma(U, s % STAGES);
     };
 
     prologue(ap, wp);
+    // the first tile has no epilogue before it: SX dropped stores take its place
+    // so that every tile's first steps see the same request counts
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < SX; ++i) __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, crsrc, kDropped, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     for (;;) {
         // the next tile's indices are loaded now; their latency hides under this
         // tile's K loop
@@ -260,17 +284,30 @@ gemm32_kernel(const GemmArgs g) {
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[f][m][i] = 0.0f;
-        int s = 0;
-        for (; s + 4 <= NSL; s += 4) {
-            step(std::integral_constant<int, 0>{}, s, false);
-            step(std::integral_constant<int, 1>{}, s + 1, false);
-            step(std::integral_constant<int, 2>{}, s + 2, false);
-            step(std::integral_constant<int, 3>{}, s + 3, false);
-        }
-        if (s < NSL) {   // 1-3 slices left
-            step(std::integral_constant<int, 0>{}, s, true);
-            step(std::integral_constant<int, 1>{}, s + 1, true);
-            step(std::integral_constant<int, 2>{}, s + 2, true);
+        std::integral_constant<int, 0> X0;
+        std::integral_constant<int, SX> XE;
+        if constexpr (!SHORT) {   // NSL >= 4
+            // the first four steps count the previous epilogue's stores
+            step(std::integral_constant<int, 0>{}, 0, false, XE, XE);
+            step(std::integral_constant<int, 1>{}, 1, false, XE, XE);
+            step(std::integral_constant<int, 2>{}, 2, false, XE, XE);
+            step(std::integral_constant<int, 3>{}, 3, false, XE, X0);   // weights of 3: step 0
+            int s = 4;
+            for (; s + 4 <= NSL; s += 4) {
+                step(std::integral_constant<int, 0>{}, s, false, X0, X0);
+                step(std::integral_constant<int, 1>{}, s + 1, false, X0, X0);
+                step(std::integral_constant<int, 2>{}, s + 2, false, X0, X0);
+                step(std::integral_constant<int, 3>{}, s + 3, false, X0, X0);
+            }
+            if (s < NSL) {   // 1-3 slices left
+                step(std::integral_constant<int, 0>{}, s, true, X0, X0);
+                step(std::integral_constant<int, 1>{}, s + 1, true, X0, X0);
+                step(std::integral_constant<int, 2>{}, s + 2, true, X0, X0);
+            }
+        } else {   // 1-3 slices: every step is among the first four
+            step(std::integral_constant<int, 0>{}, 0, true, XE, XE);
+            step(std::integral_constant<int, 1>{}, 1, true, XE, XE);
+            step(std::integral_constant<int, 2>{}, 2, true, XE, XE);
         }
         // Every wave is done reading this tile's ring, so the next tile's
         // requests may go out before this tile's stores.  DMA left in flight from
@@ -296,11 +333,17 @@ gemm32_kernel(const GemmArgs g) {
         // 16-byte pieces each.  Instead the wave stages its segments in its own
         // LDS area and stores whole segments: each store instruction then covers
         // 64/CB rows of CB contiguous chunks (128 or 64 bytes per row).
-        if (wn0 < g.N) {
-            constexpr int CPL = EPI == EPI_SWIGLU_BF16 ? 2 : 4;   // chunks per lane and row
-            constexpr int CB = 2 * CPL;                             // chunks per row segment
-            constexpr int RPP = kEpiStageBytes / (CB * 16);         // staged rows per phase
-            constexpr int MPP = RPP / 32;                           // m blocks per phase
+        {
+            // this lane's store offset for staged row lane/CB of phase 0, and how
+            // many rows past it are valid (none for waves past N): a store of
+            // row rr is kept while rr - lane/CB < rlim
+            constexpr int EB = EPI == EPI_SWIGLU_F32 ? 4 : 2;           // bytes per element
+            constexpr int CE = 16 / EB;                                  // elements per chunk
+            const int c0 = EPI == EPI_Y_BF16 ? wn0 : wn0 / 2;
+            const uint32_t lane_off =
+                ((uint32_t)(row0 + lane / CB) * (uint32_t)g.ldc + (uint32_t)(c0 + CE * (lane % CB))) * EB;
+            const int rlim = wn0 < g.N ? rows - lane / CB : 0;
+            const uint32_t row_bytes = (uint32_t)g.ldc * EB;
             // XOR swizzle of the chunk position: the 8 lanes an LDS cycle serves
             // land on 8 distinct 16-byte bank groups, for writes and reads
             auto swz = [](int rr) { return CB == 8 ? (rr & 7) : ((rr >> 1) & 3); };
@@ -350,18 +393,10 @@ gemm32_kernel(const GemmArgs g) {
                 for (int t = 0; t < RPP * CB / 64; ++t) {
                     const int rr = t * (64 / CB) + lane / CB, c = lane % CB;
                     const u32x4 v = *reinterpret_cast<const u32x4*>(ys + rr * (CB * 16) + ((c ^ swz(rr)) << 4));
-                    const int r = ph * RPP + rr;
-                    if (r < rows) {
-                        const long orow = row0 + r;
-                        void* dst;
-                        if constexpr (EPI == EPI_Y_BF16)
-                            dst = static_cast<uint16_t*>(g.C) + orow * g.ldc + wn0 + 8 * c;
-                        else if constexpr (EPI == EPI_SWIGLU_BF16)
-                            dst = static_cast<uint16_t*>(g.C) + orow * g.ldc + wn0 / 2 + 8 * c;
-                        else
-                            dst = static_cast<float*>(g.C) + orow * g.ldc + wn0 / 2 + 4 * c;
-                        *reinterpret_cast<u32x4*>(dst) = v;
-                    }
+                    const int dr = t * (64 / CB);   // rows past lane/CB (plus the phase's)
+                    const int rp = ph * RPP + dr;
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        v, crsrc, rp < rlim ? lane_off + (uint32_t)rp * row_bytes : kDropped, 0, 0);
                 }
                 __asm__ volatile("" ::: "memory");
             }
@@ -395,11 +430,19 @@ int gemm_num_cus() {
 
 template <bool FP8, bool GATHER, int SC, int EPI>
 static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st) {
-    if (a.a_bytes <= 0 || a.a_bytes > 0x7fffffffL) return hipErrorInvalidValue;   // 32-bit buffer offsets
+    const bool short_k = a.Kb / kSliceBytes < 4;
+    // 32-bit buffer offsets; C also keeps 0x80000000 free as the dropped-store offset
+    if (a.a_bytes <= 0 || a.a_bytes > 0x7fffffffL || a.c_bytes <= 0 || a.c_bytes > 0x7fffffffL)
+        return hipErrorInvalidValue;
     const long total_bound = (long)a.max_tiles * ((a.N + g32::BN - 1) / g32::BN);
     long grid = std::min<long>(total_bound, (long)gemm_num_cus());
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI>), dim3((unsigned)grid), dim3(g32::NT), g32::LDS_TOTAL, st, a);
+    if (short_k)
+        hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI, true>), dim3((unsigned)grid), dim3(g32::NT),
+                           g32::LDS_TOTAL, st, a);
+    else
+        hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI, false>), dim3((unsigned)grid), dim3(g32::NT),
+                           g32::LDS_TOTAL, st, a);
     return hipGetLastError();
 }
 
@@ -431,12 +474,14 @@ hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st) {
         GemmArgs a = gate_up_args(p, 2);
         a.C = p.h;
         a.ldc = p.I;
+        a.c_bytes = (long)p.T * p.k * p.I * 2;
         return run_gemm32<false, true, SC_NONE, EPI_SWIGLU_BF16>(a, st);
     }
     if (p.quant == Q_FP8_TENSOR) {
         GemmArgs a = gate_up_args(p, 1);
         a.C = p.h;
         a.ldc = p.I;
+        a.c_bytes = (long)p.T * p.k * p.I * 4;
         return run_gemm32<true, true, SC_TENSOR, EPI_SWIGLU_F32>(a, st);
     }
     GemmArgs a = gate_up_args(p, 1);
@@ -467,6 +512,7 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     a.I = p.I;
     a.C = p.y;
     a.ldc = p.H;
+    a.c_bytes = (long)p.T * p.k * p.H * 2;
     a.max_tiles = p.max_tiles;
     a.a_bytes = (long)p.T * p.k * a.lda;
     if (p.quant == Q_BF16) return run_gemm32<false, false, SC_NONE, EPI_Y_BF16>(a, st);

@@ -31,6 +31,7 @@ struct GemmArgs {
     int max_tiles;
     int order;              // tile order: 0 column tile major, 1 row tile major
     long a_bytes;           // bytes of A addressable by the token loads
+    long c_bytes;           // bytes of C addressable by the epilogue stores
 };
 
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
