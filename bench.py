@@ -125,8 +125,8 @@ def bench_prefill(torch, moe, name, steps, warmup):
 # counters were taken on; any edit to it turns the figure into null.
 FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524303.0, 1.0
 COUNTER_TRAFFIC = {
-    "prefill_bf16": dict(gemm_sha256="c0575437833c8862a6353079261c133ec21a8a9b7fcaee6b474b54f26a2df348",
-                         fetch_kib=802353.3, write_kib=98355.4),
+    "prefill_bf16": dict(gemm_sha256="fe0ff0b03b1b028d4cec9c72d56426decc6c9526786eb6e0807214b20c694dfd",
+                         fetch_kib=797737.7, write_kib=98323.6),
 }
 
 
