@@ -92,7 +92,12 @@ def stage_times(torch, ev_sets, names):
     return {names[i]: tot[i] / len(ev_sets) for i in range(n)}
 
 
-def bench_prefill(torch, moe, name, steps, warmup):
+def bench_prefill(torch, moe, name, steps, warmup, stage_steps=10):
+    """Prefill throughput: `steps` timed steps (moe_route + moe_forward) whose only
+    instrumentation is the pair of HIP events around the Gate/Up launch (the
+    roofline kernel; every recorded event costs the stream a few microseconds),
+    then `stage_steps` untimed steps with events between all stages for the
+    per-stage breakdown."""
     from workloads import WORKLOADS, workload_inputs, workload_weights
     wl = WORKLOADS[name]
     a = workload_inputs(name)
@@ -101,21 +106,30 @@ def bench_prefill(torch, moe, name, steps, warmup):
     layer = Layer(torch, moe, wl, wl.T, x, lg, dev_weights(torch, moe, w, wl.quant))
     for _ in range(warmup):
         layer.step()
+    _, names = layer.step(events=[torch.cuda.Event(enable_timing=True) for _ in range(8)])
+    g = names.index("gate_up")
     torch.cuda.synchronize()
-    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
-    for evs in ev_sets:                       # create the events before the timed region
-        for e in evs:
-            e.record()
+    gu_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in gu_pairs:                   # create the events before the timed region
+        e0.record()
+        e1.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    names = None
-    for evs in ev_sets:
-        _, names = layer.step(events=evs)
+    for e0, e1 in gu_pairs:
+        evs = [None] * (len(names) + 1)
+        evs[g], evs[g + 1] = e0, e1
+        layer.step(events=evs)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    gate_up_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in gu_pairs]))
+    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(stage_steps)]
+    for evs in ev_sets:
+        layer.step(events=evs)
+    torch.cuda.synchronize()
     st = stage_times(torch, ev_sets, names)
     counts = layer.routes.expert_counts.cpu().numpy()
-    return dict(wl=wl, dt=dt, stages_ms=st, path=layer.path, counts=counts, layer=layer, host=(a, w))
+    return dict(wl=wl, dt=dt, stages_ms=st, gate_up_ms=gate_up_ms, path=layer.path, counts=counts,
+                layer=layer, host=(a, w))
 
 
 # HBM traffic of one Gate/Up launch from two rocprofv3 counter passes (FETCH_SIZE,
@@ -142,15 +156,15 @@ def counter_traffic(name):
     return round((rec["fetch_kib"] * FETCH_SCALE + rec["write_kib"] * WRITE_SCALE) * 1024.0)
 
 
-def roofline_gemm(wl, stages_ms, peak):
+def roofline_gemm(wl, gate_up_ms, peak):
     R = wl.T * wl.k
     flops = 4.0 * R * wl.H * wl.I            # Gate/Up: 2 flops x R rows x H x 2I
-    t = stages_ms["gate_up"] / 1e3
+    t = gate_up_ms / 1e3
     achieved = flops / t / 1e12
     return dict(kernel="grouped_gemm_kernel (Gate/Up + SwiGLU)", bound="mfma", achieved=round(achieved, 2),
                 peak=peak, unit="TFLOP/s", frac=round(achieved / peak, 4),
                 traffic=counter_traffic(wl.name), traffic_unit="bytes per launch",
-                flops_per_launch=flops, avg_launch_us=round(stages_ms["gate_up"] * 1e3, 2))
+                flops_per_launch=flops, avg_launch_us=round(gate_up_ms * 1e3, 2))
 
 
 def bench_decode(torch, moe, name, batches, iters, nsets=32):
@@ -378,8 +392,10 @@ def profile_only(torch, moe, args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the part leaves its idle clock state only after a few tens of milliseconds of
+    # load: 5 warm-up steps (4 ms) left the first timed steps 8-10% slow
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-iters", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline line only (no fp8 extras)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -405,7 +421,7 @@ def main():
     wl = pf["wl"]
     ms = pf["dt"] / args.steps * 1e3
     value = wl.T * args.steps / pf["dt"]
-    roof = roofline_gemm(wl, pf["stages_ms"], PEAK_BF16_TFLOPS)
+    roof = roofline_gemm(wl, pf["gate_up_ms"], PEAK_BF16_TFLOPS)
     log(f"prefill bf16: {ms:.3f} ms/step, {value:.4g} tokens/s, gate_up {roof['achieved']} TFLOP/s")
     line = dict(metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
                 warmup=args.warmup, ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak",
@@ -446,7 +462,7 @@ def main():
         log("prefill fp8 block128 T=4096 ...")
         p5 = bench_prefill(torch, moe, "prefill_fp8_block", args.steps, args.warmup)
         w5 = p5["wl"]
-        r5 = roofline_gemm(w5, p5["stages_ms"], PEAK_FP8_TFLOPS)
+        r5 = roofline_gemm(w5, p5["gate_up_ms"], PEAK_FP8_TFLOPS)
         line["prefill_fp8_block128"] = dict(
             workload="prefill_fp8_block T=4096 H=4096 I=512 E=128 top-8",
             tokens_per_s=round(w5.T * args.steps / p5["dt"], 1),

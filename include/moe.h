@@ -146,7 +146,9 @@ int moe_forward(const void *x, const moe_routes *routes, const void *packed_gate
  * kernels, plus hipEventRecord(stage_events[i], stream) before the first
  * launch and after each launch (no synchronisation).  stage_events holds
  * n_events caller-created hipEvent_t handles; recording stops when they run
- * out.  *n_stages receives the number of launches and stage_names (may be
+ * out, and a NULL entry records nothing at that point (each recorded event
+ * costs the stream a few microseconds, so a caller timing one stage passes
+ * only the two handles around it).  *n_stages receives the number of launches and stage_names (may be
  * NULL) a comma-separated list of their names, e.g.
  * "init,gate_up,down,combine" for the bf16 grouped path. */
 int moe_forward_profiled(const void *x, const moe_routes *routes, const void *packed_gate_up,

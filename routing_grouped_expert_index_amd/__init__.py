@@ -175,9 +175,10 @@ def forward(x: torch.Tensor, routes: Routes, packed_gate_up: torch.Tensor, packe
             workspace: torch.Tensor | None = None, stream=None, events=None):
     """Layer output bf16 [T, H] (moe_forward).
 
-    With events (a list of torch.cuda.Event(enable_timing=True)) it calls
-    moe_forward_profiled instead, which records events[0] before the first
-    launch and events[i] after launch i, and returns (out, stage_names)."""
+    With events (a list of torch.cuda.Event(enable_timing=True) or None) it
+    calls moe_forward_profiled instead, which records events[0] before the
+    first launch and events[i] after launch i (None entries record nothing),
+    and returns (out, stage_names)."""
     _need_cuda(x, "x")
     if x.element_size() != 2 or x.dim() != 2:
         raise ValueError("x must be a bf16 [T, H] tensor")
@@ -204,9 +205,9 @@ def forward(x: torch.Tensor, routes: Routes, packed_gate_up: torch.Tensor, packe
         return out
     st = stream if stream is not None else torch.cuda.current_stream(x.device)
     for ev in events:
-        if not ev.cuda_event:
+        if ev is not None and not ev.cuda_event:
             ev.record(st)           # torch creates the underlying event on first record
-    handles = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
+    handles = (ctypes.c_void_p * len(events))(*[ev.cuda_event if ev is not None else None for ev in events])
     n = ctypes.c_int(0)
     names = ctypes.c_char_p()
     _check(lib().moe_forward_profiled(*args, handles, len(events), ctypes.byref(n), ctypes.byref(names)))

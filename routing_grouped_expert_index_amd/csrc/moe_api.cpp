@@ -262,7 +262,8 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
     static thread_local char names[256];
     names[0] = '\0';
     auto mark = [&](const char* name) {
-        if (events && stage < n_events) (void)hipEventRecord(static_cast<hipEvent_t>(events[stage]), st);
+        if (events && stage < n_events && events[stage])
+            (void)hipEventRecord(static_cast<hipEvent_t>(events[stage]), st);
         if (name) {
             if (names[0]) strncat(names, ",", sizeof names - strlen(names) - 1);
             strncat(names, name, sizeof names - strlen(names) - 1);
