@@ -1,9 +1,11 @@
-// Grouped expert GEMMs of the MoE forward on gfx950: bf16 and FP8 per-tensor.
+// Grouped expert GEMMs of the MoE forward on gfx950: bf16, FP8 per-tensor and
+// FP8 with 128x128 block scales.
 //
 // "perf: add small-batch route MMA for MoE", Motivation: after the routes are
 // grouped by expert, a Gate/Up grouped GEMM, the activation (SwiGLU) with
 // optional FP8 quantisation, and a Down grouped GEMM; Summary: FP8 per-tensor
-// scaling.
+// and 128x128 blockwise scaling, the Down-input quantisation fused into the
+// Gate/Up epilogue.
 //
 // Tile: 128 sorted rows of one expert (from the device-built tile map) x 512
 // packed weight rows; eight waves, two per SIMD, each owning 64 weight rows and
@@ -124,15 +126,53 @@ gemm32_kernel(const GemmArgs g) {
     constexpr int CB = 2 * CPL;                               // chunks per row segment
     constexpr int RPP = kEpiStageBytes / (CB * 16);           // staged rows per phase
     constexpr int MPP = RPP / 32;                             // m blocks per phase
-    constexpr int SX = (4 / MPP) * (RPP * CB / 64);           // store instructions per wave and tile
+    // store instructions per wave and tile (Q128: four rows of codes, four of scales)
+    constexpr int SX = EPI == EPI_SWIGLU_Q128 ? 8 : (4 / MPP) * (RPP * CB / 64);
     auto make_wp = [&](int e_, int wn0_) __attribute__((always_inline)) {
         return g.B + (long)e_ * g.N * g.Kb + (long)((wn0_ < g.N ? wn0_ : 0) / 32) * gstride + lane * 16;
     };
 
+    // 128x128-blockwise e4m3: every 128-deep K block kb has its own activation
+    // scale per token row and weight scale per 128 output columns.  The
+    // accumulators are kept in units of the current block's scale: at the first
+    // slice of block kb they are multiplied by s(kb-1)/s(kb) (per token row and
+    // weight half, all positive), the MFMAs keep accumulating in place, and after
+    // the K loop they are multiplied by s(KT-1).  The tile's activation scales
+    // come into LDS ([KT/4][BM][4] floats) by a DMA issued before the tile's
+    // prologue: older than every request the K loop waits for, so in-order
+    // completion lands them before the first step and no wait counts change.
+    constexpr bool BLK = SC == SC_BLOCK;
+    const int KT = NSL / 2;
+    float* sat = reinterpret_cast<float*>(smem + LDS_TOTAL);
+    const __amdgpu_buffer_rsrc_t srsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g.sa), 0, BLK ? g.sa_bytes : 0, 0x00020000);
+    // this lane's row (16 wave + lane/4, source row src) and scale blocks 4t + lane%4
+    auto table = [&](long src) __attribute__((always_inline)) {
+        if constexpr (BLK) {
+            for (int t = 0; t < (KT + 3) / 4; ++t) {
+                const int kb = min(4 * t + (lane & 3), KT - 1);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, MOE_LDS(sat + t * 4 * BM + wave * 64), 4,
+                                                         (uint32_t)((src * g.sa_ld + kb) * 4), 0, 0, 0);
+            }
+        }
+    };
+    // the 128-column weight-scale blocks of this wave's two 32-row halves
+    auto col_blocks = [&](int wn0_, int& c0, int& c1) __attribute__((always_inline)) {
+        const int P = wn0_ < g.N ? wn0_ : 0;
+        if constexpr (EPI == EPI_Y_BF16) {
+            c0 = c1 = down_col_of_packed(P) / 128;
+        } else {
+            c0 = gate_up_col_of_packed(P, g.I) / 128;
+            c1 = gate_up_col_of_packed(P + 32, g.I) / 128;
+        }
+    };
+
     int e, row0, rows, wn0;
     decode(L, e, row0, rows, wn0);
-    uint32_t ap = make_ap(src_row(row0, rows));
+    const long src0 = src_row(row0, rows);
+    uint32_t ap = make_ap(src0);
     const uint8_t* wp = make_wp(e, wn0);
+    table(src0);
 
     f32x16 acc[2][4];
     u32x4 w[4][2][2];     // [slot][block f][half q]
@@ -221,6 +261,31 @@ gemm32_kernel(const GemmArgs g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
     };
+    // Block kb's scales: sa of the lane's token rows from the LDS table, sw of
+    // the wave's two halves by scalar loads.  Nothing is kept across steps: the
+    // previous block's scales are read again (registers are the K loop's limit).
+    int cb0 = 0, cb1 = 0;
+    auto sa_of = [&](int kb, int m) __attribute__((always_inline)) {
+        return sat[(kb >> 2) * 4 * BM + (32 * m + j) * 4 + (kb & 3)];
+    };
+    auto sw_of = [&](int kb, int c) __attribute__((always_inline)) {
+        return ld_const(g.sw, ((long)e * KT + kb) * g.nb_orig + c);
+    };
+    // into block kb's units (the first block of a tile: factor 1)
+    auto rescale = [&](int kb) __attribute__((always_inline)) {
+        const int kp = kb > 0 ? kb - 1 : 0;
+        const float r0 = sw_of(kp, cb0) / sw_of(kb, cb0), r1 = sw_of(kp, cb1) / sw_of(kb, cb1);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float rm = sa_of(kp, m) / sa_of(kb, m);
+            const float a0 = rm * r0, a1 = rm * r1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                acc[0][m][i] *= a0;
+                acc[1][m][i] *= a1;
+            }
+        }
+    };
     // The hand-counted waits assume this VMEM order in every step: weight
     // loads, then (after the barrier) the token DMA, with no later load hoisted
     // above the DMA -- a load moved above it would leave fewer than WAIT_STEP
@@ -255,6 +320,12 @@ gemm32_kernel(const GemmArgs g) {
         // the weights of s were requested in step s-3 (or the prologue): at
         // least WAIT_W loads follow them
         wait_vm_only<WAIT_W + XW>();
+        if constexpr (BLK) {   // first slice of a 128-deep K block
+            if constexpr ((U & 1) == 0) {
+                if (!last || s < NSL) rescale(s >> 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if (!last) mma(U, s % STAGES);
         else if (s < NSL) mma(U, s % STAGES);
     };
@@ -284,6 +355,7 @@ gemm32_kernel(const GemmArgs g) {
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[f][m][i] = 0.0f;
+        if constexpr (BLK) col_blocks(wn0, cb0, cb1);
         std::integral_constant<int, 0> X0;
         std::integral_constant<int, SX> XE;
         if constexpr (!SHORT) {   // NSL >= 4
@@ -309,12 +381,26 @@ gemm32_kernel(const GemmArgs g) {
             step(std::integral_constant<int, 1>{}, 1, true, XE, XE);
             step(std::integral_constant<int, 2>{}, 2, true, XE, XE);
         }
+        if constexpr (BLK) {   // out of the last block's units
+            const float w0 = sw_of(KT - 1, cb0), w1 = sw_of(KT - 1, cb1);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float sa = sa_of(KT - 1, m);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    acc[0][m][i] *= sa * w0;
+                    acc[1][m][i] *= sa * w1;
+                }
+            }
+        }
         // Every wave is done reading this tile's ring, so the next tile's
         // requests may go out before this tile's stores.  DMA left in flight from
         // this tile's last steps lands in issue order, before the new requests.
         __builtin_amdgcn_sched_barrier(0);
         wait_lgkm_only();
         __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        table(more ? nsrc : src0);   // (every wave is past its last read of this tile's scales)
         __builtin_amdgcn_sched_barrier(0);
         // (after the last tile the requests repeat this tile's valid data: an
         // unconditional prologue keeps the loop's wait counts exact)
@@ -333,7 +419,63 @@ gemm32_kernel(const GemmArgs g) {
         // 16-byte pieces each.  Instead the wave stages its segments in its own
         // LDS area and stores whole segments: each store instruction then covers
         // 64/CB rows of CB contiguous chunks (128 or 64 bytes per row).
-        {
+        //   SwiGLU Q128:    h columns wn0/2 + 16hh + [0,16), one 16-byte chunk of
+        //                   e4m3 codes per row, stored straight out (see below)
+        if constexpr (EPI == EPI_SWIGLU_Q128) {
+            // h = silu(gate) * up in place of the gate accumulators.  A 128-column
+            // h block is 256 packed rows: waves 4b..4b+3 of the tile.  Per token
+            // row each wave takes the amax of its 32 columns, the four waves of a
+            // block meet in LDS, and each lane then quantises its 16 values with
+            // the row's block scale (amax/448) and stores them as one 16-byte
+            // chunk; the first wave of the block stores the scale.
+            const bool live = wn0 < g.N;
+            float* RA = reinterpret_cast<float*>(smem + LDS);     // [NWAVE][BM]
+            const int hb = (live ? wn0 : 0) / 256;                // h block of this wave
+            const int hc0 = (live ? wn0 : 0) / 2 + 16 * hh;       // this lane's first h column
+            const __amdgpu_buffer_rsrc_t qsrc = __builtin_amdgcn_make_buffer_rsrc(g.cscale, 0, g.cs_bytes, 0x00020000);
+            const int nbh = g.I / 128;
+            float amx[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    acc[0][m][i] = silu(acc[0][m][i]) * acc[1][m][i];
+                    a = fmaxf(a, fabsf(acc[0][m][i]));
+                }
+                amx[m] = fmaxf(a, __shfl_xor(a, 32));
+            }
+            if (hh == 0) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) RA[wave * BM + 32 * m + j] = amx[m];
+            }
+            __asm__ volatile("" ::: "memory");
+            wait_lgkm_only();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            __asm__ volatile("" ::: "memory");
+            const int grp = wave & ~3;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 32 * m + j;
+                const float a = fmaxf(fmaxf(RA[grp * BM + r], RA[(grp + 1) * BM + r]),
+                                      fmaxf(RA[(grp + 2) * BM + r], RA[(grp + 3) * BM + r]));
+                const float sc = scale_from_amax(a);
+                u32x4 q;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    q[t] = f32x4_to_e4m3x4(acc[0][m][4 * t] / sc, acc[0][m][4 * t + 1] / sc,
+                                           acc[0][m][4 * t + 2] / sc, acc[0][m][4 * t + 3] / sc);
+                const bool ok = live && r < rows;
+                const uint32_t orow = (uint32_t)(row0 + r);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    q, crsrc, ok ? orow * (uint32_t)g.ldc + (uint32_t)hc0 : kDropped, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint(sc), qsrc,
+                    ok && hh == 0 && (wave & 3) == 0 ? (orow * (uint32_t)nbh + (uint32_t)hb) * 4u : kDropped, 0, 0);
+            }
+            // (the next tile's epilogue rewrites RA only after its K loop's barriers)
+        } else {
             // this lane's store offset for staged row lane/CB of phase 0, and how
             // many rows past it are valid (none for waves past N): a store of
             // row rr is kept while rr - lane/CB < rlim
@@ -431,6 +573,17 @@ int gemm_num_cus() {
 template <bool FP8, bool GATHER, int SC, int EPI>
 static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st) {
     const bool short_k = a.Kb / kSliceBytes < 4;
+    size_t lds = g32::LDS_TOTAL;
+    if constexpr (SC == SC_BLOCK) {
+        // e4m3 K in whole 128-deep scale blocks; the tile's activation scales,
+        // [KT/4][128][4] floats, sit behind the epilogue staging (KT <= 64: 32 KB)
+        const int KT = a.Kb / 128;
+        if (a.Kb % 128 != 0 || KT < 1 || KT > 64 || a.sa_bytes <= 0 || a.sa_bytes > 0x7fffffffL)
+            return hipErrorInvalidValue;
+        if (EPI == EPI_SWIGLU_Q128 && (a.I % 128 != 0 || a.cs_bytes <= 0 || a.cs_bytes > 0x7fffffffL))
+            return hipErrorInvalidValue;
+        lds += (size_t)((KT + 3) / 4) * 4 * g32::BM * sizeof(float);
+    }
     // 32-bit buffer offsets; C also keeps 0x80000000 free as the dropped-store offset
     if (a.a_bytes <= 0 || a.a_bytes > 0x7fffffffL || a.c_bytes <= 0 || a.c_bytes > 0x7fffffffL)
         return hipErrorInvalidValue;
@@ -438,11 +591,11 @@ static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st) {
     long grid = std::min<long>(total_bound, (long)gemm_num_cus());
     if (grid < 1) grid = 1;
     if (short_k)
-        hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI, true>), dim3((unsigned)grid), dim3(g32::NT),
-                           g32::LDS_TOTAL, st, a);
+        hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI, true>), dim3((unsigned)grid), dim3(g32::NT), lds,
+                           st, a);
     else
-        hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI, false>), dim3((unsigned)grid), dim3(g32::NT),
-                           g32::LDS_TOTAL, st, a);
+        hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI, false>), dim3((unsigned)grid), dim3(g32::NT), lds,
+                           st, a);
     return hipGetLastError();
 }
 
@@ -487,8 +640,11 @@ hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st) {
     GemmArgs a = gate_up_args(p, 1);
     a.C = p.hq;
     a.ldc = p.I;
+    a.c_bytes = (long)p.T * p.k * p.I;
     a.cscale = p.sh;
-    return launch_block_gate_up(a, st);
+    a.cs_bytes = (long)p.T * p.k * (p.I / 128) * 4;
+    a.sa_bytes = (long)p.T * (p.H / 128) * 4;
+    return run_gemm32<true, true, SC_BLOCK, EPI_SWIGLU_Q128>(a, st);
 }
 
 hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
@@ -517,7 +673,8 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     a.a_bytes = (long)p.T * p.k * a.lda;
     if (p.quant == Q_BF16) return run_gemm32<false, false, SC_NONE, EPI_Y_BF16>(a, st);
     if (p.quant == Q_FP8_TENSOR) return run_gemm32<true, false, SC_TENSOR, EPI_Y_BF16>(a, st);
-    return launch_block_down(a, st);
+    a.sa_bytes = (long)p.T * p.k * (p.I / 128) * 4;
+    return run_gemm32<true, false, SC_BLOCK, EPI_Y_BF16>(a, st);
 }
 
 }  // namespace moe

@@ -1,5 +1,5 @@
-// Pieces shared by the two grouped-GEMM kernels (gemm.hip: bf16 and FP8
-// per-tensor; gemm_block.hip: FP8 128x128-blockwise).
+// Pieces of the grouped-GEMM kernel (gemm.hip: bf16, FP8 per-tensor and FP8
+// 128x128-blockwise).
 #pragma once
 #include "common.cuh"
 #include "launch.h"
@@ -32,6 +32,8 @@ struct GemmArgs {
     int order;              // tile order: 0 column tile major, 1 row tile major
     long a_bytes;           // bytes of A addressable by the token loads
     long c_bytes;           // bytes of C addressable by the epilogue stores
+    long sa_bytes;          // block: bytes of sa (activation scales)
+    long cs_bytes;          // Q128: bytes of cscale
 };
 
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -86,7 +88,5 @@ __device__ __forceinline__ XcdRange xcd_range(int total) {
 
 int gemm_num_cus();
 
-hipError_t launch_block_gate_up(const GemmArgs& a, hipStream_t st);
-hipError_t launch_block_down(const GemmArgs& a, hipStream_t st);
 
 }  // namespace moe
