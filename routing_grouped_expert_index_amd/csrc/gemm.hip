@@ -271,13 +271,16 @@ gemm32_kernel(const GemmArgs g) {
     auto sw_of = [&](int kb, int c) __attribute__((always_inline)) {
         return ld_const(g.sw, ((long)e * KT + kb) * g.nb_orig + c);
     };
-    // into block kb's units (the first block of a tile: factor 1)
+    // into block kb's units (the first block of a tile: factor 1); the ratios
+    // use the hardware reciprocal (about 1 ulp): a few 1e-7 relative over a
+    // whole K, and an IEEE division's temporaries would spill the K loop
     auto rescale = [&](int kb) __attribute__((always_inline)) {
         const int kp = kb > 0 ? kb - 1 : 0;
-        const float r0 = sw_of(kp, cb0) / sw_of(kb, cb0), r1 = sw_of(kp, cb1) / sw_of(kb, cb1);
+        const float r0 = sw_of(kp, cb0) * __builtin_amdgcn_rcpf(sw_of(kb, cb0));
+        const float r1 = sw_of(kp, cb1) * __builtin_amdgcn_rcpf(sw_of(kb, cb1));
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const float rm = sa_of(kp, m) / sa_of(kb, m);
+            const float rm = sa_of(kp, m) * __builtin_amdgcn_rcpf(sa_of(kb, m));
             const float a0 = rm * r0, a1 = rm * r1;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -381,16 +384,16 @@ gemm32_kernel(const GemmArgs g) {
             step(std::integral_constant<int, 1>{}, 1, true, XE, XE);
             step(std::integral_constant<int, 2>{}, 2, true, XE, XE);
         }
-        if constexpr (BLK) {   // out of the last block's units
+        // out of the last block's units: the epilogue's conversion multiplies by
+        // fsb[f][m] (read now: the next tile's scales overwrite the table below)
+        float fsb[2][4];
+        if constexpr (BLK) {
             const float w0 = sw_of(KT - 1, cb0), w1 = sw_of(KT - 1, cb1);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const float sa = sa_of(KT - 1, m);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    acc[0][m][i] *= sa * w0;
-                    acc[1][m][i] *= sa * w1;
-                }
+                fsb[0][m] = sa * w0;
+                fsb[1][m] = sa * w1;
             }
         }
         // Every wave is done reading this tile's ring, so the next tile's
@@ -434,16 +437,20 @@ gemm32_kernel(const GemmArgs g) {
             const int hc0 = (live ? wn0 : 0) / 2 + 16 * hh;       // this lane's first h column
             const __amdgpu_buffer_rsrc_t qsrc = __builtin_amdgcn_make_buffer_rsrc(g.cscale, 0, g.cs_bytes, 0x00020000);
             const int nbh = g.I / 128;
+            // one row block at a time (scheduling barriers keep the compiler from
+            // widening the SiLU and division work over all 64 values: the next
+            // tile's weight loads are in flight and hold 48 registers)
             float amx[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 float a = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    acc[0][m][i] = silu(acc[0][m][i]) * acc[1][m][i];
+                    acc[0][m][i] = silu(acc[0][m][i] * fsb[0][m]) * (acc[1][m][i] * fsb[1][m]);
                     a = fmaxf(a, fabsf(acc[0][m][i]));
                 }
                 amx[m] = fmaxf(a, __shfl_xor(a, 32));
+                __builtin_amdgcn_sched_barrier(0);
             }
             if (hh == 0) {
 #pragma unroll
@@ -473,6 +480,7 @@ gemm32_kernel(const GemmArgs g) {
                 __builtin_amdgcn_raw_buffer_store_b32(
                     __float_as_uint(sc), qsrc,
                     ok && hh == 0 && (wave & 3) == 0 ? (orow * (uint32_t)nbh + (uint32_t)hb) * 4u : kDropped, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // (the next tile's epilogue rewrites RA only after its K loop's barriers)
         } else {
@@ -492,6 +500,11 @@ gemm32_kernel(const GemmArgs g) {
             uint8_t* ys = smem + LDS + wave * kEpiStageBytes;
             float fs = 1.0f;
             if constexpr (SC == SC_TENSOR) fs = ld_const(g.sa, 0) * ld_const(g.sw, e);
+            // per accumulator block: the tensor scale, or the last K block's scales
+            auto fsc = [&](int f, int m) __attribute__((always_inline)) {
+                if constexpr (BLK) return fsb[f][m];
+                else return fs;
+            };
 #pragma unroll
             for (int ph = 0; ph < 4 / MPP; ++ph) {
 #pragma unroll
@@ -505,8 +518,8 @@ gemm32_kernel(const GemmArgs g) {
                             for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
                                 for (int t = 0; t < 4; ++t)
-                                    ch[2 * f + hv][t] = pack_bf16x2(acc[f][m][8 * hv + 2 * t] * fs,
-                                                                    acc[f][m][8 * hv + 2 * t + 1] * fs);
+                                    ch[2 * f + hv][t] = pack_bf16x2(acc[f][m][8 * hv + 2 * t] * fsc(f, m),
+                                                                    acc[f][m][8 * hv + 2 * t + 1] * fsc(f, m));
                     } else {
                         float hv[16];
 #pragma unroll
