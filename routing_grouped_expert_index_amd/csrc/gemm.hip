@@ -156,7 +156,9 @@ gemm32_kernel(const GemmArgs g) {
             }
         }
     };
-    // the 128-column weight-scale blocks of this wave's two 32-row halves
+    // the 128-column weight-scale blocks of this wave's two 32-row halves, made
+    // visibly wave-uniform (wn0 comes from threadIdx): the weight scales are
+    // then scalar loads, not vector loads whose waits would drain the K loop
     auto col_blocks = [&](int wn0_, int& c0, int& c1) __attribute__((always_inline)) {
         const int P = wn0_ < g.N ? wn0_ : 0;
         if constexpr (EPI == EPI_Y_BF16) {
@@ -165,6 +167,8 @@ gemm32_kernel(const GemmArgs g) {
             c0 = gate_up_col_of_packed(P, g.I) / 128;
             c1 = gate_up_col_of_packed(P + 32, g.I) / 128;
         }
+        c0 = __builtin_amdgcn_readfirstlane(c0);
+        c1 = __builtin_amdgcn_readfirstlane(c1);
     };
 
     int e, row0, rows, wn0;
@@ -206,7 +210,11 @@ gemm32_kernel(const GemmArgs g) {
     // The LDS reads of the token operands run ahead of the MFMAs that consume
     // them (scheduling groups pin the interleave; left alone, the compiler
     // reuses one register quad and waits for each read right before its MFMAs).
-    auto mma = [&](int slot, int stage) __attribute__((always_inline)) {
+    // (blockwise e4m3, first slice of a K block: each accumulator block is
+    // multiplied by fac[f][m] just before its MFMA, so the multiplies of the next
+    // block run under the current MFMA)
+    auto mma = [&](auto Rc, int slot, int stage, const float (&fac)[2][4]) __attribute__((always_inline)) {
+        constexpr bool RS = decltype(Rc)::value;
         const uint8_t* st = smem + stage * STAGE_B;
         if constexpr (!FP8) {
             // operand kk = 4q + m: K half q of token block m; the two MFMAs of one
@@ -247,18 +255,36 @@ gemm32_kernel(const GemmArgs g) {
                     const u32x4 a0 = w[slot][f][0], a1 = w[slot][f][1];
                     const i32x8 av{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                                    (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                    if constexpr (RS) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[f][m][i] *= fac[f][m];
+                    }
                     acc[f][m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[f][m], 0, 0, 0, 0,
                                                                                  0, 0);
                 }
             }
-            // reads one token block ahead: R R R R, (M M R R) x 2, M x 4
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            if constexpr (!RS) {
+                // reads one token block ahead: R R R R, (M M R R) x 2, M x 4
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                for (int m = 0; m < 2; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            } else {
+                // R R R R, (V16 M V16 M R R) x 2, (V16 M V16 M) x 2
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+                    if (m < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
     };
     // Block kb's scales: sa of the lane's token rows from the LDS table, sw of
@@ -271,22 +297,18 @@ gemm32_kernel(const GemmArgs g) {
     auto sw_of = [&](int kb, int c) __attribute__((always_inline)) {
         return ld_const(g.sw, ((long)e * KT + kb) * g.nb_orig + c);
     };
-    // into block kb's units (the first block of a tile: factor 1); the ratios
+    // factors into block kb's units (the first block of a tile: 1); the ratios
     // use the hardware reciprocal (about 1 ulp): a few 1e-7 relative over a
     // whole K, and an IEEE division's temporaries would spill the K loop
-    auto rescale = [&](int kb) __attribute__((always_inline)) {
+    auto block_factors = [&](int kb, float (&fac)[2][4]) __attribute__((always_inline)) {
         const int kp = kb > 0 ? kb - 1 : 0;
         const float r0 = sw_of(kp, cb0) * __builtin_amdgcn_rcpf(sw_of(kb, cb0));
         const float r1 = sw_of(kp, cb1) * __builtin_amdgcn_rcpf(sw_of(kb, cb1));
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const float rm = sa_of(kp, m) * __builtin_amdgcn_rcpf(sa_of(kb, m));
-            const float a0 = rm * r0, a1 = rm * r1;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                acc[0][m][i] *= a0;
-                acc[1][m][i] *= a1;
-            }
+            fac[0][m] = rm * r0;
+            fac[1][m] = rm * r1;
         }
     };
     // The hand-counted waits assume this VMEM order in every step: weight
@@ -322,15 +344,15 @@ gemm32_kernel(const GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         // the weights of s were requested in step s-3 (or the prologue): at
         // least WAIT_W loads follow them
+        // blockwise: the first slice of a K block carries the rescale (its scales
+        // are read before the weight wait, the table landed before step 0)
+        constexpr bool RS = BLK && (U & 1) == 0;
+        std::integral_constant<bool, RS> Rc;
+        float fac[2][4];
+        if constexpr (RS) block_factors(min(s >> 1, KT - 1), fac);
         wait_vm_only<WAIT_W + XW>();
-        if constexpr (BLK) {   // first slice of a 128-deep K block
-            if constexpr ((U & 1) == 0) {
-                if (!last || s < NSL) rescale(s >> 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (!last) mma(U, s % STAGES);
-        else if (s < NSL) mma(U, s % STAGES);
+        if (!last) mma(Rc, U, s % STAGES, fac);
+        else if (s < NSL) mma(Rc, U, s % STAGES, fac);
     };
 
     prologue(ap, wp);
