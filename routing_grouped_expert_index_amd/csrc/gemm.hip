@@ -256,14 +256,15 @@ gemm32_kernel(const GemmArgs g) {
                     const i32x8 av{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                                    (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
                     if constexpr (RS) {
+                        const float a = fac[0][m] * fac[1][f];
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) acc[f][m][i] *= fac[f][m];
+                        for (int i = 0; i < 16; ++i) acc[f][m][i] *= a;
                     }
                     acc[f][m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[f][m], 0, 0, 0, 0,
                                                                                  0, 0);
                 }
             }
-            if constexpr (!RS) {
+            if constexpr (!BLK) {
                 // reads one token block ahead: R R R R, (M M R R) x 2, M x 4
                 __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -272,17 +273,32 @@ gemm32_kernel(const GemmArgs g) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            } else {
-                // R R R R, (V16 M V16 M R R) x 2, (V16 M V16 M) x 2
+            } else if constexpr (EPI == EPI_Y_BF16) {
+                // blockwise Down: the same, on K-block starts each M preceded by
+                // its block's 16 multiplies: R R R R, (V M V M R R) x 2, (V M V M) x 2
                 __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
 #pragma unroll
                     for (int f = 0; f < 2; ++f) {
-                        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                        if constexpr (RS) __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     }
                     if (m < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+            } else {
+                // blockwise Gate/Up (its requantising epilogue leaves the K loop the
+                // fewest registers): the next token block only, R R, (M M R R) x 3,
+                // M M, with the multiplies on K-block starts as above
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        if constexpr (RS) __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+                    if (m < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 }
             }
         }
@@ -300,16 +316,16 @@ gemm32_kernel(const GemmArgs g) {
     // factors into block kb's units (the first block of a tile: 1); the ratios
     // use the hardware reciprocal (about 1 ulp): a few 1e-7 relative over a
     // whole K, and an IEEE division's temporaries would spill the K loop
+    // fac[0][m]: the token rows' ratio; fac[1][0..1]: the two halves' weight
+    // ratios (wave-uniform, held in scalar registers)
     auto block_factors = [&](int kb, float (&fac)[2][4]) __attribute__((always_inline)) {
         const int kp = kb > 0 ? kb - 1 : 0;
-        const float r0 = sw_of(kp, cb0) * __builtin_amdgcn_rcpf(sw_of(kb, cb0));
-        const float r1 = sw_of(kp, cb1) * __builtin_amdgcn_rcpf(sw_of(kb, cb1));
+        fac[1][0] = __int_as_float(__builtin_amdgcn_readfirstlane(
+            __float_as_int(sw_of(kp, cb0) * __builtin_amdgcn_rcpf(sw_of(kb, cb0)))));
+        fac[1][1] = __int_as_float(__builtin_amdgcn_readfirstlane(
+            __float_as_int(sw_of(kp, cb1) * __builtin_amdgcn_rcpf(sw_of(kb, cb1)))));
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float rm = sa_of(kp, m) * __builtin_amdgcn_rcpf(sa_of(kb, m));
-            fac[0][m] = rm * r0;
-            fac[1][m] = rm * r1;
-        }
+        for (int m = 0; m < 4; ++m) fac[0][m] = sa_of(kp, m) * __builtin_amdgcn_rcpf(sa_of(kb, m));
     };
     // The hand-counted waits assume this VMEM order in every step: weight
     // loads, then (after the barrier) the token DMA, with no later load hoisted
@@ -407,16 +423,13 @@ gemm32_kernel(const GemmArgs g) {
             step(std::integral_constant<int, 2>{}, 2, true, XE, XE);
         }
         // out of the last block's units: the epilogue's conversion multiplies by
-        // fsb[f][m] (read now: the next tile's scales overwrite the table below)
-        float fsb[2][4];
+        // sal[m] * swl[f] (read now: the next tile's scales overwrite the table below)
+        float sal[4], swl0 = 1.0f, swl1 = 1.0f;   // (the weight scales stay scalar)
         if constexpr (BLK) {
-            const float w0 = sw_of(KT - 1, cb0), w1 = sw_of(KT - 1, cb1);
+            swl0 = sw_of(KT - 1, cb0);
+            swl1 = sw_of(KT - 1, cb1);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float sa = sa_of(KT - 1, m);
-                fsb[0][m] = sa * w0;
-                fsb[1][m] = sa * w1;
-            }
+            for (int m = 0; m < 4; ++m) sal[m] = sa_of(KT - 1, m);
         }
         // Every wave is done reading this tile's ring, so the next tile's
         // requests may go out before this tile's stores.  DMA left in flight from
@@ -425,7 +438,7 @@ gemm32_kernel(const GemmArgs g) {
         wait_lgkm_only();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        table(more ? nsrc : src0);   // (every wave is past its last read of this tile's scales)
+        if (more) table(nsrc);   // (every wave is past its last read of this tile's scales)
         __builtin_amdgcn_sched_barrier(0);
         // (after the last tile the requests repeat this tile's valid data: an
         // unconditional prologue keeps the loop's wait counts exact)
@@ -468,7 +481,7 @@ gemm32_kernel(const GemmArgs g) {
                 float a = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    acc[0][m][i] = silu(acc[0][m][i] * fsb[0][m]) * (acc[1][m][i] * fsb[1][m]);
+                    acc[0][m][i] = silu(acc[0][m][i] * (sal[m] * swl0)) * (acc[1][m][i] * (sal[m] * swl1));
                     a = fmaxf(a, fabsf(acc[0][m][i]));
                 }
                 amx[m] = fmaxf(a, __shfl_xor(a, 32));
@@ -524,7 +537,7 @@ gemm32_kernel(const GemmArgs g) {
             if constexpr (SC == SC_TENSOR) fs = ld_const(g.sa, 0) * ld_const(g.sw, e);
             // per accumulator block: the tensor scale, or the last K block's scales
             auto fsc = [&](int f, int m) __attribute__((always_inline)) {
-                if constexpr (BLK) return fsb[f][m];
+                if constexpr (BLK) return sal[m] * (f ? swl1 : swl0);
                 else return fs;
             };
 #pragma unroll
