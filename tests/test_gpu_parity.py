@@ -11,7 +11,8 @@ import torch
 from gpu_helpers import (DEV, WORKLOADS, bf16_dev, check_out, check_routing, moe, oracle, oracle_out,
                          random_activations, random_weights, routes_np, run, say, weights_dev,
                          workload_dev, workload_inputs, workload_weights)
-from workloads import tie_heavy_logits
+from workloads import (_normal_per_expert, bf16_bits_to_f32, quantise_weight_block128, tie_heavy_logits,
+                       to_bf16_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -199,3 +200,24 @@ def test_graph_replay_bitwise_equal(name):
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
         step()      # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", ["grouped", "route_direct"])
+def test_block128_wide_scale_range(path):
+    """Blockwise FP8 with 128-channel K blocks whose magnitudes differ by up to 1e4 (activations
+    1e-2..1e2, weights 0.1..10 per K block): the blockwise GEMMs keep their accumulators in the
+    current K block's scale units, so consecutive blocks' scale ratios are far from 1.  Gate/Up
+    has 8 K blocks, Down 3, and the second Gate/Up column tile has waves past N."""
+    T, H, I, E, k = 37, 1024, 384, 6, 2
+    say(f"block128 wide scale range T={T} H={H} I={I} E={E} k={k} {path}")
+    a = random_activations(T, H, E, seed=91)
+    fx = np.array([1e-2, 1.0, 1e2, 1e-1, 10.0, 1.0, 3e-2, 30.0], np.float32)
+    x_bits = to_bf16_bits(bf16_bits_to_f32(a["x"]) * np.repeat(fx, 128)[None, :])
+    gw = np.array([0.1, 10.0, 1.0, 0.3, 3.0, 1.0, 10.0, 0.1], np.float32)
+    wgu = _normal_per_expert((E, H, 2 * I), 17, 0, 0.02) * np.repeat(gw, 128)[None, :, None]
+    wd = _normal_per_expert((E, I, H), 17, 1, 0.02) * np.repeat(gw[:3], 128)[None, :, None]
+    qgu, sgu = quantise_weight_block128(wgu)
+    qd, sd = quantise_weight_block128(wd)
+    w = dict(w_gate_up=qgu, w_down=qd, s_gate_up=sgu, s_down=sd)
+    _compare("block128 wide scale range", x_bits, a["logits"], k, weights_dev(w, "fp8_block128"), w,
+             "fp8_block128", path)
