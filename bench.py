@@ -139,8 +139,8 @@ def bench_prefill(torch, moe, name, steps, warmup, stage_steps=10):
 # counters were taken on; any edit to it turns the figure into null.
 FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524303.0, 1.0
 COUNTER_TRAFFIC = {
-    "prefill_bf16": dict(gemm_sha256="fe0ff0b03b1b028d4cec9c72d56426decc6c9526786eb6e0807214b20c694dfd",
-                         fetch_kib=797737.7, write_kib=98323.6),
+    "prefill_bf16": dict(gemm_sha256="aca150c9403721117daa99b4b6c7ef0f376b3946d3a8571bcdb237f510b77749",
+                         fetch_kib=801640.3, write_kib=98329.8),
 }
 
 
