@@ -58,6 +58,9 @@ def _load():
     lib.oracle_forward.restype = i32
     lib.oracle_forward.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P, P,
                                    i32, P, i32, P]
+    lib.oracle_forward_ep.restype = i32
+    lib.oracle_forward_ep.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P, P,
+                                      i32, i32, i32, P, i32, P]
     lib.oracle_quantise_activations.restype = i32
     lib.oracle_quantise_activations.argtypes = [P, i32, i32, i32, P, P]
     _lib = lib
@@ -126,12 +129,15 @@ def route(logits, k):
 
 
 def forward(x_bf16, topk_ids, topk_weights, w_gate_up, w_down, quant="bf16",
-            s_gate_up=None, s_down=None, tokens=None):
+            s_gate_up=None, s_down=None, tokens=None, expert_begin=0):
     """Layer output (float64 [n_tok, H]) for the listed tokens (all if None).
 
     x_bf16: uint16 bf16 bits [T,H]; w_gate_up [E,H,2I] and w_down [E,I,H] as
     uint16 bf16 bits (quant "bf16") or uint8 e4m3 codes with fp32 scales:
-    per-tensor [E] each, block128 [E,H/128,2I/128] and [E,I/128,H/128]."""
+    per-tensor [E] each, block128 [E,H/128,2I/128] and [E,I/128,H/128].
+    Expert-parallel slice: the weights hold experts [expert_begin,
+    expert_begin + E) and routes to other experts contribute nothing (the
+    per-tensor h scale then covers the local routes only)."""
     q = QUANT[quant]
     x = _c(x_bf16, np.uint16)
     T, H = x.shape
@@ -150,8 +156,9 @@ def forward(x_bf16, topk_ids, topk_weights, w_gate_up, w_down, quant="bf16",
     tok = None if tokens is None else _c(tokens, np.int32)
     n_tok = T if tok is None else tok.size
     out = np.zeros((n_tok, H), np.float64)
-    rc = _load().oracle_forward(_ptr(x), T, H, I, E, k, _ptr(ids), _ptr(tw), _ptr(wgu), _ptr(wd),
-                                _ptr(sgu), _ptr(sd), q, _ptr(tok), n_tok, _ptr(out))
+    rc = _load().oracle_forward_ep(_ptr(x), T, H, I, E, k, _ptr(ids), _ptr(tw), _ptr(wgu), _ptr(wd),
+                                   _ptr(sgu), _ptr(sd), q, int(expert_begin), E, _ptr(tok), n_tok,
+                                   _ptr(out))
     if rc != 0:
         raise ValueError("oracle_forward rejected the inputs")
     return out

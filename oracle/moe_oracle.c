@@ -258,11 +258,34 @@ static void down(const orc_layer *L, int e, const double *h, double *y) {
  * Gate/Up pass over all T tokens first, whatever tok lists.
  * Returns 0, or -1 on an unsupported shape or an allocation failure.
  */
+int oracle_forward_ep(const uint16_t *x, int T, int H, int I, int E, int k,
+                      const int32_t *ids, const float *weights,
+                      const void *w_gu, const void *w_d,
+                      const float *s_gu, const float *s_d, int quant, int e0, int n_local,
+                      const int32_t *tok, int n_tok, double *out);
+
 int oracle_forward(const uint16_t *x, int T, int H, int I, int E, int k,
                    const int32_t *ids, const float *weights,
                    const void *w_gu, const void *w_d,
                    const float *s_gu, const float *s_d, int quant,
                    const int32_t *tok, int n_tok, double *out) {
+    return oracle_forward_ep(x, T, H, I, E, k, ids, weights, w_gu, w_d, s_gu, s_d, quant, 0, E, tok,
+                             n_tok, out);
+}
+
+/*
+ * Expert-parallel form [P3 Summary: the fast path "preserves EP routing" and
+ * "shared output"]: the weights and scales hold experts [e0, e0 + n_local)
+ * only (expert e at index e - e0); routes to other experts contribute nothing,
+ * so out[t] is the gate-weighted sum over token t's local routes.  The
+ * per-tensor h scale is the amax over the local routes' h, the only h such a
+ * call sees.  (Adding the sum into an existing output is left to the caller.)
+ */
+int oracle_forward_ep(const uint16_t *x, int T, int H, int I, int E, int k,
+                      const int32_t *ids, const float *weights,
+                      const void *w_gu, const void *w_d,
+                      const float *s_gu, const float *s_d, int quant, int e0, int n_local,
+                      const int32_t *tok, int n_tok, double *out) {
     orc_layer L;
     uint8_t *q_x = NULL;
     float *s_x_blk = NULL, *h_all = NULL, s_h = 1.0f;
@@ -271,6 +294,7 @@ int oracle_forward(const uint16_t *x, int T, int H, int I, int E, int k,
     long i;
     (void)E;
     if (quant < 0 || quant > 2) return -1;
+    if (e0 < 0 || n_local < 1) return -1;
     if (quant == ORC_FP8_BLOCK128 && (H % 128 || I % 128)) return -1;
     memset(&L, 0, sizeof L);
     L.T = T; L.H = H; L.I = I; L.E = E; L.k = k; L.quant = quant;
@@ -304,11 +328,14 @@ int oracle_forward(const uint16_t *x, int T, int H, int I, int E, int k,
 
     /* per-tensor Down-input requantisation needs every route's h first */
     if (quant == ORC_FP8_PER_TENSOR) {
-        long R = (long)T * k;
+        long R = (long)T * k, nl = 0, r;
+        long *slot = (long *)malloc(sizeof(long) * (size_t)(R > 0 ? R : 1));   /* route -> local h row */
         uint8_t *q_h;
-        h_all = (float *)malloc(sizeof(float) * (size_t)R * I);
-        q_h = (uint8_t *)malloc((size_t)R * I);
-        if (!h_all || !q_h) { free(h_all); free(q_h); free(q_x); return -1; }
+        if (!slot) { free(q_x); return -1; }
+        for (r = 0; r < R; ++r) slot[r] = (ids[r] >= e0 && ids[r] < e0 + n_local) ? nl++ : -1;
+        h_all = (float *)malloc(sizeof(float) * (size_t)(nl > 0 ? nl : 1) * I);
+        q_h = (uint8_t *)malloc((size_t)(nl > 0 ? nl : 1) * I);
+        if (!h_all || !q_h) { free(h_all); free(q_h); free(q_x); free(slot); return -1; }
 #pragma omp parallel for schedule(dynamic)
         for (ti = 0; ti < T; ++ti) {
             double *a = (double *)malloc(sizeof(double) * (size_t)H);
@@ -317,20 +344,24 @@ int oracle_forward(const uint16_t *x, int T, int H, int I, int E, int k,
             int j, n;
             activation(&L, ti, a);
             for (j = 0; j < k; ++j) {
-                long r = (long)ti * k + j;
-                gate_up_swiglu(&L, ids[r], a, hr, acc);
+                long rr = (long)ti * k + j;
+                if (slot[rr] < 0) continue;
+                gate_up_swiglu(&L, ids[rr] - e0, a, hr, acc);
                 /* the quantiser sees h as fp32, the width the method holds it in */
-                for (n = 0; n < I; ++n) h_all[r * I + n] = (float)hr[n];
+                for (n = 0; n < I; ++n) h_all[slot[rr] * I + n] = (float)hr[n];
             }
             free(a); free(acc); free(hr);
         }
-        s_h = oracle_quantise_group(h_all, R * I, q_h);
+        s_h = nl > 0 ? oracle_quantise_group(h_all, nl * I, q_h) : 1.0f;
         free(h_all);
         h_all = NULL;
         hq_all = (double *)malloc(sizeof(double) * (size_t)R * I);
-        if (!hq_all) { free(q_h); free(q_x); return -1; }
-        for (i = 0; i < R * I; ++i) hq_all[i] = oracle_e4m3_decode(q_h[i]) * s_h;
+        if (!hq_all) { free(q_h); free(q_x); free(slot); return -1; }
+        for (r = 0; r < R; ++r)
+            for (i = 0; i < I; ++i)
+                hq_all[r * I + i] = slot[r] < 0 ? 0.0 : oracle_e4m3_decode(q_h[slot[r] * I + i]) * s_h;
         free(q_h);
+        free(slot);
     }
 
 #pragma omp parallel for schedule(dynamic) reduction(| : bad)
@@ -349,7 +380,8 @@ int oracle_forward(const uint16_t *x, int T, int H, int I, int E, int k,
             if (quant != ORC_FP8_PER_TENSOR) activation(&L, t, a);
             for (j = 0; j < k; ++j) {
                 long r = (long)t * k + j;
-                int e = ids[r];
+                int e = ids[r] - e0;   /* index into this call's experts */
+                if (e < 0 || e >= n_local) continue;   /* another rank's expert */
                 if (quant == ORC_FP8_PER_TENSOR) {
                     for (n = 0; n < I; ++n) hd[n] = hq_all[r * I + n];
                 } else {

@@ -182,3 +182,97 @@ def test_quantisation_matters():
     Y = dense_experts(x, deq(w["w_gate_up"], w["s_gate_up"]), deq(w["w_down"], w["s_down"]))
     plain = combine_dense(Y, r["topk_ids"], r["topk_weights"]).numpy()
     assert rel_l2(q, plain) > 1e-2
+
+
+# ------------------------------------------------------ expert-parallel slice --
+# A forward call may hold only experts [e0, e0 + n) (P3 Summary: the fast path
+# preserves EP routing and shared output): routes to other experts contribute
+# nothing and the per-tensor h scale covers the local routes only.
+
+def _slice_w(w, e0, n):
+    out = dict(w_gate_up=w["w_gate_up"][e0:e0 + n], w_down=w["w_down"][e0:e0 + n])
+    for key in ("s_gate_up", "s_down"):
+        out[key] = None if w[key] is None else np.ascontiguousarray(w[key][e0:e0 + n])
+    return out
+
+
+def test_ep_slices_brute_force_and_partition_bf16():
+    T, H, I, E, k = 14, 32, 16, 8, 3
+    a = random_activations(T, H, E, 60)
+    w = random_weights(E, H, I, "bf16", 61)
+    r = oracle.route(a["logits"], k)
+    x = torch.from_numpy(bf16_bits_to_f32(a["x"])).double()
+    Y = dense_experts(x, torch.from_numpy(bf16_bits_to_f32(w["w_gate_up"])).double(),
+                      torch.from_numpy(bf16_bits_to_f32(w["w_down"])).double())
+    full = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"])
+    total = np.zeros_like(full)
+    for e0, n in ((0, 3), (3, 4), (7, 1)):
+        ws = _slice_w(w, e0, n)
+        out = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], ws["w_gate_up"], ws["w_down"],
+                             expert_begin=e0)
+        local = (r["topk_ids"] >= e0) & (r["topk_ids"] < e0 + n)
+        ref = combine_dense(Y, r["topk_ids"], np.where(local, r["topk_weights"], 0.0)).numpy()
+        assert np.max(np.abs(out - ref)) <= 1e-12, (e0, n)
+        total += out
+    assert np.max(np.abs(total - full)) <= 1e-12
+
+
+def test_ep_per_tensor_scale_covers_local_routes():
+    T, H, I, E, k = 10, 64, 32, 6, 3
+    e0, n = 2, 3
+    a = random_activations(T, H, E, 62)
+    w = random_weights(E, H, I, "fp8_per_tensor", 63)
+    r = oracle.route(a["logits"], k)
+    ws = _slice_w(w, e0, n)
+    out = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], ws["w_gate_up"], ws["w_down"],
+                         quant="fp8_per_tensor", s_gate_up=ws["s_gate_up"], s_down=ws["s_down"],
+                         expert_begin=e0)
+    x = torch.from_numpy(bf16_bits_to_f32(a["x"]))
+    sx = torch_scale(x.abs().max())
+    xa = torch_e4m3(x / sx) * sx.double()
+    wgu = (torch.from_numpy(w["w_gate_up"]).view(torch.float8_e4m3fn).double()
+           * torch.from_numpy(w["s_gate_up"]).double()[:, None, None])
+    wdn = (torch.from_numpy(w["w_down"]).view(torch.float8_e4m3fn).double()
+           * torch.from_numpy(w["s_down"]).double()[:, None, None])
+    gu = torch.einsum("th,ehn->ten", xa, wgu)
+    h = (F.silu(gu[..., :I]) * gu[..., I:]).float()
+    ids = torch.from_numpy(r["topk_ids"].astype(np.int64))
+    local = (ids >= e0) & (ids < e0 + n)
+    h_routes = torch.gather(h, 1, ids[:, :, None].expand(T, k, I))
+    sh = torch_scale(h_routes[local].abs().max())                     # local routes only
+    hq = torch_e4m3(h_routes / sh) * sh.double()
+    y = torch.einsum("tji,tjih->tjh", hq, wdn[ids])
+    gw = torch.from_numpy(r["topk_weights"]).double() * local.double()
+    ref = (y * gw[:, :, None]).sum(dim=1)
+    assert np.max(np.abs(out - ref.numpy())) <= 1e-12
+    # the scale differs from the whole layer's, so the slice is not a restriction of it
+    assert local.any() and not local.all()
+
+
+def test_ep_block128_partition_sums_to_layer():
+    T, H, I, E, k = 6, 256, 256, 4, 2
+    a = random_activations(T, H, E, 64)
+    w = random_weights(E, H, I, "fp8_block128", 65)
+    r = oracle.route(a["logits"], k)
+    kw = dict(quant="fp8_block128")
+    full = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"],
+                          s_gate_up=w["s_gate_up"], s_down=w["s_down"], **kw)
+    total = np.zeros_like(full)
+    for e0, n in ((0, 1), (1, 3)):
+        ws = _slice_w(w, e0, n)
+        total += oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], ws["w_gate_up"], ws["w_down"],
+                                s_gate_up=ws["s_gate_up"], s_down=ws["s_down"], expert_begin=e0, **kw)
+    assert np.max(np.abs(total - full)) <= 1e-12 * max(1.0, np.max(np.abs(full)))
+
+
+def test_ep_slice_without_routes_is_zero():
+    T, H, I, E, k = 5, 32, 16, 8, 2
+    a = random_activations(T, H, E, 66)
+    lg = a["logits"].copy()
+    lg[:, :k] += 50.0                        # every token picks experts 0..k-1
+    w = random_weights(E, H, I, "bf16", 67)
+    r = oracle.route(lg, k)
+    ws = _slice_w(w, 4, 3)
+    out = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], ws["w_gate_up"], ws["w_down"],
+                         expert_begin=4)
+    assert np.array_equal(out, np.zeros_like(out))
