@@ -142,6 +142,34 @@ int moe_forward(const void *x, const moe_routes *routes, const void *packed_gate
                 const void *packed_down, const moe_scales *scales, void *out, int H, int I,
                 int quant, int path, void *ws, size_t ws_bytes, void *stream);
 
+/* Expert-parallel slice and shared output for moe_forward_ex ("perf: add
+ * small-batch route MMA for MoE", Summary: the fast path preserves EP
+ * routing and shared output).  The routes stay global (moe_route over all E
+ * experts); this call holds experts [expert_begin, expert_begin +
+ * num_experts) only -- packed_gate_up, packed_down and the scales cover
+ * exactly those, expert expert_begin + i at index i -- and computes only the
+ * routes to them:
+ *   sum[t] = sum over j with topk_ids[t,j] in the slice of
+ *            topk_weights[t,j] * FFN_{topk_ids[t,j]}(x[t])
+ * FP8 per-tensor: the h scale is the amax over this call's routes (the only
+ * h it sees); x's scale still covers all of x.
+ * accumulate 0: out = bf16(sum); 1: out = bf16(out + sum), one rounding (a
+ * shared output, e.g. the partial sums of several expert slices). */
+typedef struct {
+    int32_t expert_begin;   /* >= 0 */
+    int32_t num_experts;    /* >= 1, expert_begin + num_experts <= routes->E */
+    int32_t accumulate;     /* 0 or 1 */
+} moe_ep;
+
+/* moe_forward for an expert slice and/or into a shared output; ep may be
+ * NULL (all experts, out overwritten: exactly moe_forward).  The workspace
+ * is moe_forward_workspace_size with the routes' E.  AUTO picks the path
+ * from the routes' T, E and k as for moe_forward.  Invalid ep fields give
+ * MOE_ERR_INVALID_ARG. */
+int moe_forward_ex(const void *x, const moe_routes *routes, const void *packed_gate_up,
+                   const void *packed_down, const moe_scales *scales, void *out, int H, int I,
+                   int quant, int path, const moe_ep *ep, void *ws, size_t ws_bytes, void *stream);
+
 /* moe_forward with stage timing for profilers and benchmarks: the same
  * kernels, plus hipEventRecord(stage_events[i], stream) before the first
  * launch and after each launch (no synchronisation).  stage_events holds

@@ -26,7 +26,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
 EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_pack_weights", "moe_select_path",
-            "moe_forward_workspace_size", "moe_forward", "moe_forward_profiled", "moe_last_error"]
+            "moe_forward_workspace_size", "moe_forward", "moe_forward_ex", "moe_forward_profiled",
+            "moe_last_error"]
 
 
 class MoeError(RuntimeError):
@@ -44,6 +45,11 @@ class _CRoutes(ctypes.Structure):
 
 class _CScales(ctypes.Structure):
     _fields_ = [("w_gate_up_scale", ctypes.c_void_p), ("w_down_scale", ctypes.c_void_p)]
+
+
+class _CEp(ctypes.Structure):
+    _fields_ = [("expert_begin", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("accumulate", ctypes.c_int32)]
 
 
 _lib = None
@@ -72,6 +78,9 @@ def lib():
     L.moe_forward.restype = i32
     L.moe_forward.argtypes = [P, ctypes.POINTER(_CRoutes), P, P, ctypes.POINTER(_CScales), P, i32,
                               i32, i32, i32, P, sz, P]
+    L.moe_forward_ex.restype = i32
+    L.moe_forward_ex.argtypes = L.moe_forward.argtypes[:10] + [ctypes.POINTER(_CEp)] + \
+        L.moe_forward.argtypes[10:]
     L.moe_forward_profiled.restype = i32
     L.moe_forward_profiled.argtypes = L.moe_forward.argtypes + [ctypes.POINTER(ctypes.c_void_p), i32,
                                                                ctypes.POINTER(ctypes.c_int),
@@ -172,8 +181,14 @@ def forward_workspace_size(T, H, I, E, k, quant="bf16", path="auto") -> int:
 
 def forward(x: torch.Tensor, routes: Routes, packed_gate_up: torch.Tensor, packed_down: torch.Tensor,
             quant: str = "bf16", scales=None, out: torch.Tensor | None = None, path: str = "auto",
-            workspace: torch.Tensor | None = None, stream=None, events=None):
+            workspace: torch.Tensor | None = None, stream=None, events=None,
+            expert_begin: int = 0, num_experts: int | None = None, accumulate: bool = False):
     """Layer output bf16 [T, H] (moe_forward).
+
+    expert_begin / num_experts / accumulate select an expert slice and a
+    shared output (moe_forward_ex): the packed weights and scales then hold
+    experts [expert_begin, expert_begin + num_experts) only, the routes stay
+    global, and accumulate=True adds the slice's sum into `out`.
 
     With events (a list of torch.cuda.Event(enable_timing=True) or None) it
     calls moe_forward_profiled instead, which records events[0] before the
@@ -188,6 +203,14 @@ def forward(x: torch.Tensor, routes: Routes, packed_gate_up: torch.Tensor, packe
         raise ValueError("packed_down must be [E, I, H] (the shape of the unpacked tensor)")
     if routes.T != T:
         raise ValueError("routes and x disagree on T")
+    ep = None
+    if expert_begin != 0 or num_experts is not None or accumulate:
+        if events is not None:
+            raise ValueError("stage events are not recorded for an expert slice")
+        if accumulate and out is None:
+            raise ValueError("accumulate needs the output to add into")
+        ep = _CEp(expert_begin, routes.E - expert_begin if num_experts is None else num_experts,
+                  int(bool(accumulate)))
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     need = forward_workspace_size(T, H, I, routes.E, routes.k, quant, path)
@@ -200,6 +223,9 @@ def forward(x: torch.Tensor, routes: Routes, packed_gate_up: torch.Tensor, packe
     args = (_ptr(x), ctypes.byref(cs), _ptr(packed_gate_up), _ptr(packed_down), ctypes.byref(sc),
             _ptr(out), H, I, QUANT[quant], PATH[path], _ptr(workspace), workspace.numel(),
             _stream(x.device, stream))
+    if ep is not None:
+        _check(lib().moe_forward_ex(*args[:10], ctypes.byref(ep), *args[10:]))
+        return out
     if events is None:
         _check(lib().moe_forward(*args))
         return out

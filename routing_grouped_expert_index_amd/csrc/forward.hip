@@ -56,7 +56,9 @@ forward_init_kernel(int E, const int32_t* __restrict__ offsets, int build_tiles,
 }
 
 hipError_t launch_forward_init(const FwdPlan& p, bool build_tiles, hipStream_t st) {
-    hipLaunchKernelGGL(forward_init_kernel, dim3(1), dim3(kMaxExperts), 0, st, p.E, p.offsets,
+    // the tile map covers the expert slice: offsets + e0 for nloc experts, so a
+    // tile names its expert by its index in the slice (the weights' index)
+    hipLaunchKernelGGL(forward_init_kernel, dim3(1), dim3(kMaxExperts), 0, st, p.nloc, p.offsets + p.e0,
                        build_tiles ? 1 : 0, p.tiles, p.ntiles, p.amax);
     return hipGetLastError();
 }
@@ -117,11 +119,29 @@ quant_block128_kernel(const TIn* __restrict__ in, int rows, int cols, uint8_t* _
 
 // amax over n values (n % 8 == 0), folded into *amax_bits with atomicMax on
 // the bit pattern (non-negative floats order like their bits).
+// Element range [lo, hi) of a row-major tensor with `cols` columns: all n
+// elements, or (rows != null) the sorted rows [rows[0], rows[nr]) of an expert
+// slice (its routes are contiguous in sorted order).
+struct ElemRange {
+    const int32_t* rows;
+    int nr, cols;
+};
+__device__ __forceinline__ void elem_range(const ElemRange& g, long n, long& lo, long& hi) {
+    lo = 0;
+    hi = n;
+    if (g.rows) {
+        lo = (long)g.rows[0] * g.cols;
+        hi = (long)g.rows[g.nr] * g.cols;
+    }
+}
+
 template <typename TIn>
 __global__ void __launch_bounds__(256)
-amax_kernel(const TIn* __restrict__ in, long n, uint32_t* __restrict__ amax_bits) {
+amax_kernel(const TIn* __restrict__ in, long n, ElemRange er, uint32_t* __restrict__ amax_bits) {
     float a = 0.0f;
-    for (long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n;
+    long lo, hi;
+    elem_range(er, n, lo, hi);
+    for (long i = lo + ((long)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < hi;
          i += (long)gridDim.x * blockDim.x * 8) {
         float v[8];
         load8<TIn>(in + i, v);
@@ -140,11 +160,13 @@ amax_kernel(const TIn* __restrict__ in, long n, uint32_t* __restrict__ amax_bits
 
 template <typename TIn>
 __global__ void __launch_bounds__(256)
-quant_tensor_kernel(const TIn* __restrict__ in, long n, const uint32_t* __restrict__ amax_bits,
+quant_tensor_kernel(const TIn* __restrict__ in, long n, ElemRange er, const uint32_t* __restrict__ amax_bits,
                     uint8_t* __restrict__ q, float* __restrict__ scale_out) {
     const float s = scale_from_amax(__uint_as_float(*amax_bits));
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
-    for (long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n;
+    long lo, hi;
+    elem_range(er, n, lo, hi);
+    for (long i = lo + ((long)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < hi;
          i += (long)gridDim.x * blockDim.x * 8) {
         float v[8];
         load8<TIn>(in + i, v);
@@ -155,11 +177,13 @@ quant_tensor_kernel(const TIn* __restrict__ in, long n, const uint32_t* __restri
 // One workgroup does amax and quantisation of a small tensor in one launch.
 template <typename TIn>
 __global__ void __launch_bounds__(1024)
-quant_tensor_small_kernel(const TIn* __restrict__ in, long n, uint8_t* __restrict__ q,
+quant_tensor_small_kernel(const TIn* __restrict__ in, long n, ElemRange er, uint8_t* __restrict__ q,
                           float* __restrict__ scale_out) {
     __shared__ float part[1024 / kWave];
     float a = 0.0f;
-    for (long i = (long)threadIdx.x * 8; i < n; i += (long)blockDim.x * 8) {
+    long lo, hi;
+    elem_range(er, n, lo, hi);
+    for (long i = lo + (long)threadIdx.x * 8; i < hi; i += (long)blockDim.x * 8) {
         float v[8];
         load8<TIn>(in + i, v);
 #pragma unroll
@@ -172,7 +196,7 @@ quant_tensor_small_kernel(const TIn* __restrict__ in, long n, uint8_t* __restric
     for (int w = 0; w < (int)(blockDim.x / kWave); ++w) a = fmaxf(a, part[w]);
     const float s = scale_from_amax(a);
     if (threadIdx.x == 0) *scale_out = s;
-    for (long i = (long)threadIdx.x * 8; i < n; i += (long)blockDim.x * 8) {
+    for (long i = lo + (long)threadIdx.x * 8; i < hi; i += (long)blockDim.x * 8) {
         float v[8];
         load8<TIn>(in + i, v);
         store8_e4m3(q + i, v, s);
@@ -189,16 +213,17 @@ hipError_t launch_quant_x(const FwdPlan& p, hipStream_t st) {
                            dim3(256), 0, st, p.x, p.T, p.H, p.xq, p.sx);
         return hipGetLastError();
     }
+    const ElemRange all{nullptr, 0, 0};
     if (n <= kSmallQuant) {
-        hipLaunchKernelGGL(quant_tensor_small_kernel<uint16_t>, dim3(1), dim3(1024), 0, st, p.x, n,
+        hipLaunchKernelGGL(quant_tensor_small_kernel<uint16_t>, dim3(1), dim3(1024), 0, st, p.x, n, all,
                            p.xq, &p.scal[0]);
         return hipGetLastError();
     }
     const unsigned grid = (unsigned)std::min<long>(2048, (n / 8 + 255) / 256);
-    hipLaunchKernelGGL(amax_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, p.x, n, &p.amax[0]);
+    hipLaunchKernelGGL(amax_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, p.x, n, all, &p.amax[0]);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(quant_tensor_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, p.x, n,
+    hipLaunchKernelGGL(quant_tensor_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, p.x, n, all,
                        &p.amax[0], p.xq, &p.scal[0]);
     return hipGetLastError();
 }
@@ -214,28 +239,36 @@ hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st) {
                            dim3(256), 0, st, h, p.R, p.I, p.hq, p.sh);
         return hipGetLastError();
     }
+    // per-tensor: the scale covers the expert slice's routes, sorted rows
+    // [offsets[e0], offsets[e0 + nloc]) (the only rows of h this call writes)
+    const ElemRange local{p.offsets + p.e0, p.nloc, p.I};
     if (n <= kSmallQuant) {
-        hipLaunchKernelGGL(quant_tensor_small_kernel<float>, dim3(1), dim3(1024), 0, st, h, n, p.hq,
+        hipLaunchKernelGGL(quant_tensor_small_kernel<float>, dim3(1), dim3(1024), 0, st, h, n, local, p.hq,
                            &p.scal[1]);
         return hipGetLastError();
     }
     const unsigned grid = (unsigned)std::min<long>(2048, (n / 8 + 255) / 256);
-    hipLaunchKernelGGL(amax_kernel<float>, dim3(grid), dim3(256), 0, st, h, n, &p.amax[1]);
+    hipLaunchKernelGGL(amax_kernel<float>, dim3(grid), dim3(256), 0, st, h, n, local, &p.amax[1]);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(quant_tensor_kernel<float>, dim3(grid), dim3(256), 0, st, h, n, &p.amax[1],
+    hipLaunchKernelGGL(quant_tensor_kernel<float>, dim3(grid), dim3(256), 0, st, h, n, local, &p.amax[1],
                        p.hq, &p.scal[1]);
     return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ combine --
 
+// Expert slice: only routes whose sorted position lies in the slice's rows
+// [rows[0], rows[nr]) were computed (the other rows of y are not written) and
+// enter the sum; with accumulate the old output is added before the rounding.
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, const int32_t* __restrict__ route_pos,
-               int H, int k, uint16_t* __restrict__ out) {
+               int H, int k, const int32_t* __restrict__ rows, int nr, int accumulate, uint16_t* __restrict__ out) {
     const int t = blockIdx.x;
     const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
     if (c >= H) return;
+    const __attribute__((address_space(4))) int32_t* rw = (const __attribute__((address_space(4))) int32_t*)rows;
+    const int lo = rw[0], hi = rw[nr];
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -260,7 +293,7 @@ combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, con
         for (int jj = 0; jj < 8; ++jj) raw[jj] = *reinterpret_cast<const u32x4*>(y + (size_t)pos[jj] * H + c);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            if (j0 + jj < k) {
+            if (j0 + jj < k && pos[jj] >= lo && pos[jj] < hi) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     acc[2 * i] = fmaf(w[jj], __uint_as_float(raw[jj][i] << 16), acc[2 * i]);
@@ -269,15 +302,25 @@ combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, con
             }
         }
     }
+    u32x4* op = reinterpret_cast<u32x4*>(out + (size_t)t * H + c);
+    if (accumulate) {
+        const u32x4 old = *op;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += __uint_as_float(old[i] << 16);
+            acc[2 * i + 1] += __uint_as_float(old[i] & 0xffff0000u);
+        }
+    }
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-    *reinterpret_cast<u32x4*>(out + (size_t)t * H + c) = o;
+    *op = o;
 }
 
 hipError_t launch_combine(const FwdPlan& p, hipStream_t st) {
     dim3 grid(p.T, ceil_div(p.H / 8, 256));
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, p.y, p.tw, p.route_pos, p.H, p.k, p.out);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, p.y, p.tw, p.route_pos, p.H, p.k,
+                       p.offsets + p.e0, p.nloc, p.acc, p.out);
     return hipGetLastError();
 }
 

@@ -659,7 +659,7 @@ static GemmArgs gate_up_args(const FwdPlan& p, int elem) {
     a.Kb = p.H * elem;
     a.tiles = p.tiles;
     a.ntiles = p.ntiles;
-    a.offsets = p.offsets;
+    a.offsets = p.offsets + p.e0;   // the expert slice (the tile map indexes it)
     a.sa = p.quant == Q_FP8_BLOCK ? p.sx : &p.scal[0];
     a.sa_ld = p.H / 128;
     a.sw = p.s_gu;
@@ -708,7 +708,7 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     a.Kb = p.I * elem;
     a.tiles = p.tiles;
     a.ntiles = p.ntiles;
-    a.offsets = p.offsets;
+    a.offsets = p.offsets + p.e0;   // the expert slice (the tile map indexes it)
     a.sa = p.quant == Q_FP8_BLOCK ? p.sh : &p.scal[1];
     a.sa_ld = p.I / 128;
     a.sw = p.s_d;

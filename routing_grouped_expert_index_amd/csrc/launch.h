@@ -64,6 +64,8 @@ struct FwdPlan {
     float* rd_part;             // route-direct Down partial sums [T * H/32][items][32]
     int32_t* rd_cnt;            // route-direct Down arrival counters [T * H/32]
     int max_tiles;
+    // expert slice [e0, e0 + nloc) held by the weights (index e - e0); acc: out += sum
+    int e0, nloc, acc;
 };
 
 constexpr int kGemmBM = 128;

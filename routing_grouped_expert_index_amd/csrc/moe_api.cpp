@@ -201,12 +201,16 @@ size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int quant, 
 
 static int forward_impl(const void* x, const moe_routes* routes, const void* packed_gate_up,
                         const void* packed_down, const moe_scales* scales, void* out, int H, int I,
-                        int quant, int path, void* ws, size_t ws_bytes, void* stream,
+                        int quant, int path, const moe_ep* ep, void* ws, size_t ws_bytes, void* stream,
                         void** events, int n_events, int* n_stages, const char** stage_names) {
     if (!routes) return fail(MOE_ERR_INVALID_ARG, "routes is NULL");
     const int T = routes->T, E = routes->E, k = routes->k;
     int rc = check_shape(T, H, I, E, k, quant);
     if (rc != MOE_OK) return rc;
+    const int e0 = ep ? ep->expert_begin : 0, nloc = ep ? ep->num_experts : E, acc = ep ? ep->accumulate : 0;
+    if (e0 < 0 || nloc < 1 || (long)e0 + nloc > E || (acc != 0 && acc != 1))
+        return fail(MOE_ERR_INVALID_ARG, "expert slice [%d, %d+%d) must lie in [0, %d) and accumulate be 0 or 1",
+                    e0, e0, nloc, E);
     const int p = resolve_path(T, H, I, E, k, quant, path);
     if (p < 0) return p;
     if (T == 0) {
@@ -255,6 +259,9 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
     P.rd_part = at<float>(ws, L.rd_part);
     P.rd_cnt = at<int32_t>(ws, L.rd_cnt);
     P.max_tiles = moe::grouped_max_tiles(P.R, E);
+    P.e0 = e0;
+    P.nloc = nloc;
+    P.acc = acc;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool grouped = p == MOE_PATH_GROUPED;
@@ -299,7 +306,14 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
 int moe_forward(const void* x, const moe_routes* routes, const void* packed_gate_up,
                 const void* packed_down, const moe_scales* scales, void* out, int H, int I,
                 int quant, int path, void* ws, size_t ws_bytes, void* stream) {
-    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, ws,
+    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, nullptr, ws,
+                        ws_bytes, stream, nullptr, 0, nullptr, nullptr);
+}
+
+int moe_forward_ex(const void* x, const moe_routes* routes, const void* packed_gate_up,
+                   const void* packed_down, const moe_scales* scales, void* out, int H, int I,
+                   int quant, int path, const moe_ep* ep, void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, ep, ws,
                         ws_bytes, stream, nullptr, 0, nullptr, nullptr);
 }
 
@@ -309,7 +323,7 @@ int moe_forward_profiled(const void* x, const moe_routes* routes, const void* pa
                          void** stage_events, int n_events, int* n_stages, const char** stage_names) {
     if (n_events < 0 || (n_events > 0 && !stage_events))
         return fail(MOE_ERR_INVALID_ARG, "stage_events must hold n_events handles");
-    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, ws,
+    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, nullptr, ws,
                         ws_bytes, stream, stage_events, n_events, n_stages, stage_names);
 }
 

@@ -63,6 +63,8 @@ struct RdArgs {
     int T, H, I, E, k;
     int kp;                  // per-block Down: K parts per route slot
     int rs;                  // Gate/Up row split (workgroups per 32-row block pair)
+    int e0, nloc;            // expert slice held by the weights (expert e at index e - e0)
+    int acc;                 // out += the layer sum (else out = it)
 };
 
 // 8 values from 16 bytes of bf16
@@ -227,7 +229,7 @@ rd_gate_up_kernel(const RdArgs a) {
     // 32 distinct bytes, and the RS lanes of a row are added at the end.
     const int lrs = __builtin_ctz(gridDim.z), RS = 1 << lrs, RW = 32 >> lrs, rs = blockIdx.z;
     const int ls = j >> (5 - lrs), jr = rs * RW + (j & (RW - 1));
-    const int t = r / a.k, e = a.ids[r];
+    const int t = r / a.k, e = a.ids[r] - a.e0;   // the expert's index in this call's slice
     constexpr int elem = FP8 ? 1 : 2;
     // wave w takes the U-super-slice chunks w, w + NW, w + 2 NW, ...: at each
     // step the waves of the workgroup read one contiguous window
@@ -236,6 +238,12 @@ rd_gate_up_kernel(const RdArgs a) {
     const long gstride = 32L * Kb;
     if (r == 0 && G == 0 && rs == 0)   // the Down kernel that follows counts arrivals from zero
         for (int i = threadIdx.x; i < a.T * (a.H / 32); i += 64 * NW) a.cnt[i] = 0;
+    if ((unsigned)e >= (unsigned)a.nloc) {   // another slice's expert: no h, a zero share of the h amax
+        if constexpr (Q == RD_TENSOR) {
+            if (threadIdx.x == 0) a.hmax[((long)r * (a.I / 32) + G) * RS + rs] = 0.0f;
+        }
+        return;
+    }
     const uint8_t* wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + (32 * hh + jr) * 16 + ls * 2048;
     const uint8_t* wu = wg + gstride;
 
@@ -364,6 +372,37 @@ rd_gate_up_kernel(const RdArgs a) {
 }
 
 // ------------------------------------------------------------ Down+combine --
+// The end of a Down piece: wave 0 publishes the piece's partial v (lanes 0..31)
+// and takes the output block's arrival ticket; the last arrival sums the k*KP
+// partials in a fixed order and writes the block's 32 outputs.  Partials and
+// the ticket use device-scope atomic stores, loads and adds, which are
+// performed at the device-coherent level without the whole-L2 write-back a
+// device-scope fence costs on this multi-XCD GPU; the wave's partial stores
+// have completed (vmcnt 0) before it takes its ticket.  Every thread of the
+// workgroup calls this (it holds a barrier).
+__device__ __forceinline__ void rd_part_publish(const RdArgs& a, int tb, int t, int g32, int it,
+                                                int items, float v, int& last_s) {
+    const int lane = lane_id(), wave = threadIdx.x >> 6, hh = lane >> 5;
+    float* part = a.part + (long)tb * items * 32;
+    if (wave == 0) {
+        if (hh == 0) __hip_atomic_store(part + it * 32 + lane, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0)
+        if (lane == 0)
+            last_s = __hip_atomic_fetch_add(a.cnt + tb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == items - 1;
+    }
+    __syncthreads();
+    if (!last_s) return;
+    if (wave == 0 && hh == 0) {
+        float o = 0.0f;
+        for (int i = 0; i < items; ++i)   // fixed order
+            o += __hip_atomic_load(part + i * 32 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint16_t* op = a.out + (long)t * a.H + down_col_of_packed(32 * g32 + lane);
+        if (a.acc) o += __uint_as_float((uint32_t)*op << 16);   // shared output: one rounding of out + sum
+        *op = f32_to_bf16(o);
+        if (lane == 0) __hip_atomic_store(a.cnt + tb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 template <int Q, int NW, int KP, int U>
 __global__ void __launch_bounds__(64 * NW)
 rd_down_part_kernel(const RdArgs a) {
@@ -377,7 +416,11 @@ rd_down_part_kernel(const RdArgs a) {
     const int tb = blockIdx.x, t = tb / nb, g32 = tb - t * nb;
     const int items = a.k * KP, it = blockIdx.y;
     const int jj = it / KP, kp = it - jj * KP;
-    const int r = t * a.k + jj, e = a.ids[r];
+    const int r = t * a.k + jj, e = a.ids[r] - a.e0;   // index in this call's expert slice
+    if ((unsigned)e >= (unsigned)a.nloc) {   // another slice's expert: a zero partial, no weights
+        rd_part_publish(a, tb, t, g32, it, items, 0.0f, last_s);
+        return;
+    }
     constexpr int elem = FP8 ? 1 : 2;
     const int Kb = a.I * elem, NSL = Kb / kSliceBytes, spw = NSL / KP / NW;
     const int s0 = kp * (NSL / KP) + wave * spw;
@@ -457,33 +500,15 @@ rd_down_part_kernel(const RdArgs a) {
     y += __shfl_xor(y, 32);
     if (hh == 0) red[wave][lane] = y;
     __syncthreads();
-    // Partials and the ticket use device-scope atomic stores, loads and adds,
-    // which are performed at the device-coherent level without the whole-L2
-    // write-back a device-scope fence costs on this multi-XCD GPU; the wave's
-    // partial stores have completed (vmcnt 0) before it takes its ticket.
-    float* part = a.part + (long)tb * items * 32;
-    if (wave == 0) {
-        if (hh == 0) {
-            float o = 0.0f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) o += red[w][lane];
-            float gw = a.tw[r];
-            if constexpr (Q == RD_TENSOR) gw *= hs * a.s_d[e];
-            __hip_atomic_store(part + it * 32 + lane, gw * o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0)
-        if (lane == 0)
-            last_s = __hip_atomic_fetch_add(a.cnt + tb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == items - 1;
-    }
-    __syncthreads();
-    if (!last_s) return;
+    float v = 0.0f;
     if (wave == 0 && hh == 0) {
-        float o = 0.0f;
-        for (int i = 0; i < items; ++i)   // fixed order
-            o += __hip_atomic_load(part + i * 32 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        a.out[(long)t * a.H + down_col_of_packed(32 * g32 + lane)] = f32_to_bf16(o);
-        if (lane == 0) __hip_atomic_store(a.cnt + tb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += red[w][lane];
+        float gw = a.tw[r];
+        if constexpr (Q == RD_TENSOR) gw *= hs * a.s_d[e];
+        v *= gw;
     }
+    rd_part_publish(a, tb, t, g32, it, items, v, last_s);
 }
 
 // ------------------------------------------------------- Down, per block --
@@ -531,7 +556,11 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
     }
     for (int it = wave; it < items; it += nw) {
         const int jj = it / KP, kp = it - jj * KP;
-        const int r = t * a.k + jj, e = a.ids[r];
+        const int r = t * a.k + jj, e = a.ids[r] - a.e0;   // index in this call's expert slice
+        if ((unsigned)e >= (unsigned)a.nloc) {   // another slice's expert: a zero piece
+            if (hh == 0) red[it * 32 + j] = 0.0f;
+            continue;
+        }
         const int s0 = kp * spw;
         const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + (long)s0 * 2048 + lane * 16;
         u32x4 vw[MS][2];
@@ -599,7 +628,9 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
     if (wave == 0 && hh == 0) {
         float o = 0.0f;
         for (int it = 0; it < items; ++it) o += red[it * 32 + lane];   // fixed order
-        a.out[(long)t * a.H + down_col_of_packed(32 * g32 + lane)] = f32_to_bf16(o);
+        uint16_t* op = a.out + (long)t * a.H + down_col_of_packed(32 * g32 + lane);
+        if (a.acc) o += __uint_as_float((uint32_t)*op << 16);   // shared output: one rounding of out + sum
+        *op = f32_to_bf16(o);
     }
 }
 
@@ -625,6 +656,9 @@ static RdArgs rd_args(const FwdPlan& p) {
     a.T = p.T; a.H = p.H; a.I = p.I; a.E = p.E; a.k = p.k;
     a.kp = 1;
     a.rs = rd_gate_up_split(p.T, p.H, p.I, p.k, p.quant);
+    a.e0 = p.e0;
+    a.nloc = p.nloc;
+    a.acc = p.acc;
     return a;
 }
 

@@ -100,6 +100,20 @@ def test_host_validation_before_any_launch():
     # fp8 needs scales
     assert L.moe_forward(good, ctypes.byref(r), good, good, None, good, 2048, 768, 1, 0, good, 1 << 30,
                          None) == -1
+    # expert slices: [expert_begin, expert_begin + num_experts) inside [0, E), accumulate 0 or 1
+    for e0, n, acc in ((-1, 4, 0), (0, 0, 0), (120, 9, 0), (0, 129, 0), (0, 8, 2), (0, 8, -1)):
+        ep = moe._CEp(e0, n, acc)
+        assert L.moe_forward_ex(good, ctypes.byref(r), good, good, None, good, 2048, 768, 0, 0,
+                                ctypes.byref(ep), good, 1 << 30, None) == -1, (e0, n, acc)
+        assert b"expert slice" in L.moe_last_error()
+    r.T = 0
+    for e0, n, acc in ((0, 128, 0), (120, 8, 1), (0, 1, 1)):
+        ep = moe._CEp(e0, n, acc)
+        assert L.moe_forward_ex(None, ctypes.byref(r), None, None, None, None, 2048, 768, 0, 0,
+                                ctypes.byref(ep), None, 0, None) == 0
+    assert L.moe_forward_ex(None, ctypes.byref(r), None, None, None, None, 2048, 768, 0, 0,
+                            None, None, 0, None) == 0
+    r.T = 4
     # packing rejects in-place and null
     assert L.moe_pack_weights(good, good, 4, 256, 64, 0, good, None, None) == -1
     assert L.moe_pack_weights(good, None, 4, 256, 64, 0, good, good, None) == -1
