@@ -6,6 +6,10 @@ calls it.  The arithmetic lives in ``moe_oracle.c`` (plain C, fp64
 accumulation); this module only marshals numpy arrays through ctypes.
 
 Functions and what they follow (page titles and sections):
+  router_logits -- the per-expert router scores of a token, a bias-free linear
+                map x W_r ("Port necessary FBGEMM MoE kernels", Benchmarks: the
+                MoE module of 16 experts, top 8; the router's form is not
+                printed, the linear map is the plain reading).
   route      -- token-choice top-k routing and its grouped form: per-expert
                 counts, exclusive prefix, stable route permutation and its
                 inverse ("Port necessary FBGEMM MoE kernels", Summary: index
@@ -53,6 +57,8 @@ def _load():
     lib.oracle_scale_from_amax.argtypes = [ctypes.c_float]
     lib.oracle_quantise_group.restype = ctypes.c_float
     lib.oracle_quantise_group.argtypes = [P, ctypes.c_long, P]
+    lib.oracle_router_logits.restype = None
+    lib.oracle_router_logits.argtypes = [P, P, i32, i32, i32, P]
     lib.oracle_route.restype = None
     lib.oracle_route.argtypes = [P, i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_forward.restype = i32
@@ -107,6 +113,19 @@ def quantise_group(values):
     q = np.empty(v.size, dtype=np.uint8)
     s = _load().oracle_quantise_group(_ptr(v), v.size, _ptr(q))
     return q, np.float32(s)
+
+
+def router_logits(x_bf16, w_router):
+    """fp32 router scores [T, E] = x [T, H] (bf16 bits) times w_router [H, E]
+    (fp32), summed in double over ascending h and rounded once."""
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_router, np.float32)
+    T, H = x.shape
+    assert w.shape[0] == H
+    E = w.shape[1]
+    out = np.empty((T, E), np.float32)
+    _load().oracle_router_logits(_ptr(x), _ptr(w), T, H, E, _ptr(out))
+    return out
 
 
 def route(logits, k):

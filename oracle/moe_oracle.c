@@ -128,6 +128,29 @@ float oracle_quantise_group(const float *v, long n, uint8_t *q) {
     return s;
 }
 
+/* ---------------------------------------------------------------- router -- */
+
+/* Router scores of a bias-free linear router: logits[t][e] = sum over h of
+ * x[t][h] * w_r[h][e], with x bf16 [T, H] and w_r fp32 [H, E] row-major.  Each
+ * product is exact in double (8 + 24 significand bits); the sum runs over
+ * ascending h in double and is rounded once to fp32.  The pages route each
+ * token by the top-k of its per-expert scores ("Port necessary FBGEMM MoE
+ * kernels", Benchmarks: the MoE module of 16 experts, top 8) without printing
+ * the router itself; this linear map is the plainest reading. */
+void oracle_router_logits(const uint16_t *x, const float *w_r, int T, int H, int E, float *logits) {
+    int t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        int e, h;
+        for (e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (h = 0; h < H; ++h)
+                s += (double)oracle_bf16_decode(x[(long)t * H + h]) * (double)w_r[(long)h * E + e];
+            logits[(long)t * E + e] = (float)s;
+        }
+    }
+}
+
 /* --------------------------------------------------------------- routing -- */
 
 /* Token-choice routing.  For each token: pick k experts greedily by largest

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import random_activations, tie_heavy_logits
+from workloads import bf16_bits_to_f32, random_activations, tie_heavy_logits, to_bf16_bits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
 
@@ -126,3 +126,37 @@ def test_golden_hand_example_routing():
     for key in ("topk_ids", "expert_counts", "expert_offsets", "perm", "route_pos"):
         assert r[key].tolist() == ex[key], key
     assert np.max(np.abs(r["topk_weights"] - np.array(ex["topk_weights"]))) <= ex["tolerance_weights"]
+
+
+# ------------------------------------------------------------------ router --
+def test_router_logits_exact_integer_closed_form():
+    """Integer x (exact in bf16) and W_r in multiples of 2^-6: every partial sum is exact in
+    double and every score fits fp32's significand, so the scores are the integer matrix product
+    (a dropped term, a transposed operand or a wrong index changes them)."""
+    rng = np.random.default_rng(40)
+    T, H, E = 9, 96, 20
+    xi = rng.integers(-16, 17, size=(T, H))
+    wi = rng.integers(-128, 129, size=(H, E))
+    x_bits = to_bf16_bits(xi.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f32(x_bits), xi.astype(np.float32))
+    got = oracle.router_logits(x_bits, (wi / 64.0).astype(np.float32))
+    assert np.array_equal(got.astype(np.float64) * 64.0, (xi @ wi).astype(np.float64))
+
+
+def test_router_logits_one_hot_columns_select_activations():
+    T, H, E = 5, 64, 24
+    x_bits = random_activations(T, H, E, 41)["x"]
+    cols = np.random.default_rng(42).choice(H, E, replace=False)
+    w = np.zeros((H, E), np.float32)
+    w[cols, np.arange(E)] = 1.0
+    assert np.array_equal(oracle.router_logits(x_bits, w), bf16_bits_to_f32(x_bits)[:, cols])
+
+
+def test_router_logits_match_float64_product():
+    """numpy's float64 product (another summation order) rounded to fp32: at most one fp32 ulp
+    apart, and almost always identical."""
+    a = random_activations(64, 256, 16, 1, logits="router")
+    got = oracle.router_logits(a["x"], a["w_router"])
+    ref = (bf16_bits_to_f32(a["x"]).astype(np.float64) @ a["w_router"].astype(np.float64)).astype(np.float32)
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1 and np.mean(ulps == 0) >= 0.99

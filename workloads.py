@@ -7,8 +7,8 @@ oracle receive exactly these arrays.
 
 Recipe (all draws are ``numpy.random.default_rng(seed)`` standard normals):
   * x ~ N(0,1), stored as bf16 (round-to-nearest-even via torch's cast);
-  * router logits ~ N(0,1) fp32, or, for the tiny layer, logits = x @ W_r with
-    W_r ~ N(0, 0.02) fp32 [H, E], accumulated in float64 and stored fp32;
+  * router logits ~ N(0,1) fp32, or, for the tiny layer, a router weight
+    W_r ~ N(0, 0.02) fp32 [H, E] instead (the layer computes its logits x W_r);
   * the prefill-bf16 workload adds a per-expert bias 0.5*ln(1/(e+1)) to its
     logits, giving a Zipf-skewed expert load;
   * expert weights ~ N(0, 0.02), expert e of tensor i drawn from
@@ -132,12 +132,13 @@ def random_weights(E, H, I, quant, seed):
 
 
 def random_activations(T, H, E, seed, logits="normal"):
-    """dict(x bf16 bits [T,H], logits fp32 [T,E])."""
+    """dict(x bf16 bits [T,H], logits fp32 [T,E]); with logits="router",
+    dict(x, w_router fp32 [H,E]) instead."""
     rng = np.random.default_rng(seed)
     x = to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
     if logits == "router":
         wr = (rng.standard_normal((H, E)) * 0.02).astype(np.float32)
-        lg = (bf16_bits_to_f32(x).astype(np.float64) @ wr.astype(np.float64)).astype(np.float32)
+        return dict(x=x, w_router=wr)
     else:
         lg = rng.standard_normal((T, E), dtype=np.float32)
         if logits == "zipf":
