@@ -292,6 +292,56 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
     return res
 
 
+def bench_router(torch, moe, batches, iters, H=2048, E=128, k=8):
+    """Cold-HBM latency of the router scores x W_r plus routing in one call
+    (moe_route_project, W_r fp32 [H, E]) against the two-call alternative
+    (torch's fp32 product, then moe_route) and moe_route alone on given logits."""
+    from workloads import random_activations
+    evict = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    res = {}
+    for B in batches:
+        a = random_activations(B, H, E, 500 + B, logits="router")
+        x = torch.from_numpy(a["x"].view(np.int16)).cuda().view(torch.bfloat16)
+        wr = torch.from_numpy(a["w_router"]).cuda()
+        routes = moe.Routes(B, E, k, x.device)
+        lg = torch.empty((B, E), dtype=torch.float32, device=x.device)
+        ws = torch.zeros(moe.route_project_workspace_size(B, H, E, k), dtype=torch.uint8, device=x.device)
+        rws_n = moe.route_workspace_size(B, E, k)
+        rws = torch.empty(rws_n, dtype=torch.uint8, device=x.device) if rws_n else None
+
+        def fused():
+            moe.route_project(x, wr, k, out=routes, logits=lg, workspace=ws)
+
+        def two_calls():
+            torch.matmul(x.float(), wr, out=lg)
+            moe.route(lg, k, out=routes, workspace=rws)
+
+        def route_only():
+            moe.route(lg, k, out=routes, workspace=rws)
+
+        def timed(run):
+            ts = []
+            for it in range(iters + 2):
+                evict.amax()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                run()
+                e1.record()
+                if it >= 2:
+                    ts.append((e0, e1))
+            torch.cuda.synchronize()
+            return float(np.median([p.elapsed_time(q) for p, q in ts])) * 1e3
+
+        t_f, t_2, t_r = timed(fused), timed(two_calls), timed(route_only)
+        nbytes = H * E * 4 + B * H * 2
+        res[B] = dict(us_route_project=round(t_f, 2), us_matmul_then_route=round(t_2, 2),
+                      us_route_only=round(t_r, 2), bytes=nbytes,
+                      achieved_gbs=round(nbytes / (t_f * 1e-6) / 1e9, 1))
+        log(f"router B={B}: route_project {t_f:.2f} us, matmul + route {t_2:.2f} us, route alone {t_r:.2f} us")
+    del evict
+    return res
+
+
 def layer_fractions(wl, t_step, peak_tflops):
     """The whole step against the dense MFMA peak and against HBM: algorithmic flops
     6*R*H*I; the HBM floor with the gather fused = every expert's weights once, x
@@ -376,6 +426,8 @@ def profile_only(torch, moe, args):
                 torch.mul(src, 1, out=dst)
             torch.cuda.synchronize()
             log(f"copy: {args.steps} x 1 GiB elementwise copy kernels")
+        elif name == "router":
+            bench_router(torch, moe, (1, 2, 3, 4), args.decode_iters)
         elif name.startswith("crossover_"):
             bench_crossover(torch, moe, name[len("crossover_"):], range(1, 17), 30)
         elif name.startswith("prefill"):
@@ -401,7 +453,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
                     help="profiling runs: comma list of prefill_bf16, prefill_fp8_block, decode_bf16, "
-                         "decode_fp8_tensor, copy (a plain 1 GiB device copy, the traffic-counter "
+                         "decode_fp8_tensor, router, copy (a plain 1 GiB device copy, the traffic-counter "
                          "reference); prints per-stage times instead of the JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -446,6 +498,12 @@ def main():
                           "_graph_warm: replayed back to back with the weights cached; dominant: "
                           "the kernel between stage events",
                           batches=bench_decode(torch, moe, "decode_bf16", (1, 2, 3, 4), args.decode_iters))
+    torch.cuda.empty_cache()
+    log("router scores + routing B=1..4 ...")
+    line["router"] = dict(
+        workload="router scores x W_r (fp32 [2048,128]) + top-8 routing, decode_bf16 shapes",
+        timing=f"cold HBM, median of {args.decode_iters}, between two HIP events",
+        batches=bench_router(torch, moe, (1, 2, 3, 4), args.decode_iters))
     torch.cuda.empty_cache()
     if not args.quick:
         log("dispatch crossover (cold, forced paths) ...")

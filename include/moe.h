@@ -105,6 +105,28 @@ size_t moe_route_workspace_size(int T, int E, int k);
 int moe_route(const float *logits, int T, int E, int k, moe_routes *out,
               void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of workspace moe_route_project needs (> 0 for T > 0). */
+size_t moe_route_project_workspace_size(int T, int H, int E, int k);
+
+/* Router scores and routing in one call: logits = x W_r, then exactly what
+ * moe_route computes from those logits.  The pages route every token by the
+ * top-k of its per-expert scores ("Port necessary FBGEMM MoE kernels",
+ * Benchmarks: the MoE module of 16 experts, top 8) without printing the
+ * router; here it is a bias-free linear map.
+ *   x        bf16 [T,H] row-major; H a positive multiple of 64
+ *   w_router fp32 [H,E] row-major
+ *   logits   fp32 [T,E], written: sum over h of x[t,h] * w_router[h,e] in
+ *            fp32, in an order fixed by (T, H, E) -- repeated calls give the
+ *            same bits; the routes are taken from exactly these values
+ *   out      as for moe_route (out->T/E/k are set by this call)
+ * For small T the scores and the routing run in one launch: its workgroups
+ * meet through an arrival counter in the first 256 bytes of ws, which must be
+ * zero before the first call with a given workspace (e.g. zero-filled when
+ * allocated); every call leaves it zero.  Calls that share a workspace must
+ * not run concurrently.  T = 0 writes zero counts and offsets only. */
+int moe_route_project(const void *x, const float *w_router, int T, int H, int E, int k,
+                      float *logits, moe_routes *out, void *ws, size_t ws_bytes, void *stream);
+
 /* Weight re-layout, once per weight set (not per forward call).
  *   w_gate_up [E][H][2I] (gate = columns [0,I), up = columns [I,2I)) and
  *   w_down [E][I][H], bf16 (2 bytes) or e4m3 codes (1 byte), row-major

@@ -25,7 +25,8 @@ PATH_NAME = {v: k for k, v in PATH.items()}
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
-EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_pack_weights", "moe_select_path",
+EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_route_project_workspace_size",
+            "moe_route_project", "moe_pack_weights", "moe_select_path",
             "moe_forward_workspace_size", "moe_forward", "moe_forward_ex", "moe_forward_profiled",
             "moe_last_error"]
 
@@ -70,6 +71,10 @@ def lib():
     L.moe_route.restype = i32
     L.moe_route.argtypes = [P, i32, i32, i32, ctypes.POINTER(_CRoutes), P, sz, P]
     L.moe_pack_weights.restype = i32
+    L.moe_route_project_workspace_size.restype = sz
+    L.moe_route_project_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.moe_route_project.restype = i32
+    L.moe_route_project.argtypes = [P, P, i32, i32, i32, i32, P, ctypes.POINTER(_CRoutes), P, sz, P]
     L.moe_pack_weights.argtypes = [P, P, i32, i32, i32, i32, P, P, P]
     L.moe_select_path.restype = i32
     L.moe_select_path.argtypes = [i32] * 7
@@ -152,6 +157,38 @@ def route(logits: torch.Tensor, k: int, out: Routes | None = None,
                            0 if workspace is None else workspace.numel(),
                            _stream(logits.device, stream)))
     return out
+
+
+def route_project_workspace_size(T: int, H: int, E: int, k: int) -> int:
+    return int(lib().moe_route_project_workspace_size(T, H, E, k))
+
+
+def route_project(x: torch.Tensor, w_router: torch.Tensor, k: int, out: Routes | None = None,
+                  logits: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Router scores x W_r and the routing from them (moe_route_project).
+
+    x bf16 [T, H], w_router fp32 [H, E]; returns (Routes, logits fp32 [T, E]).
+    A workspace passed in must have been zero-filled before its first use (the
+    call leaves its arrival counter at zero)."""
+    _need_cuda(x, "x")
+    _need_cuda(w_router, "w_router")
+    if x.element_size() != 2 or x.dim() != 2:
+        raise ValueError("x must be a bf16 [T, H] tensor")
+    if w_router.dtype != torch.float32 or w_router.dim() != 2 or w_router.shape[0] != x.shape[1]:
+        raise ValueError("w_router must be float32 [H, E]")
+    T, H = x.shape
+    E = w_router.shape[1]
+    out = out if out is not None else Routes(T, E, k, x.device)
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    need = route_project_workspace_size(T, H, E, k)
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    cs = out.c_struct()
+    _check(lib().moe_route_project(_ptr(x), _ptr(w_router), T, H, E, k, _ptr(logits), ctypes.byref(cs),
+                                   _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                   _stream(x.device, stream)))
+    return out, logits
 
 
 def pack_weights(w_gate_up: torch.Tensor, w_down: torch.Tensor, quant: str = "bf16", stream=None):

@@ -24,6 +24,18 @@ size_t route_workspace_bytes(int T, int E, int k);
 hipError_t launch_route(const float* logits, int T, int E, int k, const RouteOut& o, void* ws,
                         hipStream_t st);
 
+// ---- router scores x W_r, then the routing (route.hip)
+constexpr size_t kRpTicketBytes = 256;   // workspace head: the fused kernel's arrival counter
+struct RouteProjectPlan {
+    bool fused;        // scores and routing in one launch
+    int ks, hk, ntb;   // K splits, W_r rows per split, token blocks
+    size_t lds;        // dynamic LDS bytes
+    size_t ws_bytes;   // workspace: ticket + partial scores (fused) or the routing's own
+};
+RouteProjectPlan route_project_plan(int T, int H, int E, int k);
+hipError_t launch_route_project(const uint16_t* x, const float* w_router, int T, int H, int E, int k,
+                                float* logits, const RouteOut& o, void* ws, hipStream_t st);
+
 // ---- weight packing (pack.hip)
 hipError_t launch_pack_gate_up(const void* src, void* dst, int E, int H, int I, int elem_bytes,
                                hipStream_t st);

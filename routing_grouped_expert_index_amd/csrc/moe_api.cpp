@@ -168,6 +168,46 @@ int moe_route(const float* logits, int T, int E, int k, moe_routes* out, void* w
     return rc == MOE_OK ? ok() : rc;
 }
 
+static bool route_project_shape_ok(int T, int H, int E, int k) {
+    return T >= 0 && k >= 1 && E >= k && E <= moe::kMaxExperts && H >= 64 && H % 64 == 0 &&
+           (long)T * k < (1L << 31) && (long)T * E < (1L << 31) && (long)T * H < (1L << 31);
+}
+
+size_t moe_route_project_workspace_size(int T, int H, int E, int k) {
+    if (!route_project_shape_ok(T, H, E, k)) return 0;
+    return moe::route_project_plan(T, H, E, k).ws_bytes;
+}
+
+int moe_route_project(const void* x, const float* w_router, int T, int H, int E, int k, float* logits,
+                      moe_routes* out, void* ws, size_t ws_bytes, void* stream) {
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    if (T < 0 || k < 1 || E < k || E > moe::kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "need T >= 0 and 1 <= k <= E <= %d (T=%d k=%d E=%d)",
+                    moe::kMaxExperts, T, k, E);
+    if (H < 64 || H % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "H must be a positive multiple of 64 (H=%d)", H);
+    if (!route_project_shape_ok(T, H, E, k))
+        return fail(MOE_ERR_UNSUPPORTED, "T*k, T*E and T*H must fit in int32");
+    if (!out->expert_counts || !out->expert_offsets || (T > 0 && (!x || !w_router || !logits ||
+        !out->topk_ids || !out->topk_weights || !out->perm || !out->route_pos)))
+        return fail(MOE_ERR_INVALID_ARG, "null pointer among x / w_router / logits / routes members");
+    const void* ptrs[] = {x, w_router, logits, ws, out->topk_ids, out->topk_weights, out->expert_counts,
+                          out->expert_offsets, out->perm, out->route_pos};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    const size_t need = T > 0 ? moe::route_project_plan(T, H, E, k).ws_bytes : 0;
+    if (ws_bytes < need || (need && !ws))
+        return fail(MOE_ERR_WORKSPACE, "route_project workspace: need %zu bytes, got %zu", need, ws_bytes);
+    out->T = T;
+    out->E = E;
+    out->k = k;
+    const moe::RouteOut o{out->topk_ids, out->topk_weights, out->expert_counts, out->expert_offsets,
+                          out->perm, out->route_pos};
+    const int rc = hip_status(moe::launch_route_project(static_cast<const uint16_t*>(x), w_router, T, H, E, k,
+                                                        logits, o, ws, static_cast<hipStream_t>(stream)),
+                              "moe_route_project launch");
+    return rc == MOE_OK ? ok() : rc;
+}
+
 int moe_pack_weights(const void* w_gate_up, const void* w_down, int E, int H, int I, int quant,
                      void* packed_gate_up, void* packed_down, void* stream) {
     if (E < 1 || E > moe::kMaxExperts || H <= 0 || I <= 0)

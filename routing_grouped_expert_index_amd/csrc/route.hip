@@ -13,6 +13,8 @@
 //    column scan over workgroups, then a stable scatter in which each wave
 //    ranks its routes with a ballot-based match (one ballot per key bit);
 //  * a single-workgroup fused kernel serves small T*k (decode) in one launch.
+#include <algorithm>
+
 #include "common.cuh"
 #include "launch.h"
 
@@ -196,13 +198,18 @@ __host__ __device__ inline int small_sort_waves(int R) {
     return n < 1 ? 1 : (n > kSmallWaves ? kSmallWaves : n);
 }
 
+// The whole routing of T tokens by one workgroup of kSmallWaves waves; `lds`
+// holds route_small_lds_bytes(T, E, k).  `logits` may point to global memory
+// or to LDS.  Every thread of the workgroup calls it (it holds barriers).
 template <int VPL>
-__global__ void __launch_bounds__(kSmallWaves * kWave)
-route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int nbits,
-                   int32_t* __restrict__ ids, float* __restrict__ weights,
-                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                   int32_t* __restrict__ perm, int32_t* __restrict__ route_pos) {
-    extern __shared__ int32_t lds[];
+__device__ __forceinline__ void route_small_body(const float* __restrict__ logits, int T, int E, int k, int nbits,
+                                                 const RouteOut& o, int32_t* lds) {
+    int32_t* __restrict__ ids = o.ids;
+    float* __restrict__ weights = o.weights;
+    int32_t* __restrict__ counts = o.counts;
+    int32_t* __restrict__ offsets = o.offsets;
+    int32_t* __restrict__ perm = o.perm;
+    int32_t* __restrict__ route_pos = o.route_pos;
     const int R = T * k;
     const int nws = small_sort_waves(R);         // waves that count and scatter
     int32_t* sid = lds;                          // [R]
@@ -280,6 +287,13 @@ route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int nb
             if (lane == 63 - __clzll(peers)) wcnt[wave * E + key] += __popcll(peers);
         }
     }
+}
+
+template <int VPL>
+__global__ void __launch_bounds__(kSmallWaves * kWave)
+route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int nbits, const RouteOut o) {
+    extern __shared__ int32_t lds[];
+    route_small_body<VPL>(logits, T, E, k, nbits, o, lds);
 }
 
 // ----------------------------------------------------------------------------
@@ -432,6 +446,180 @@ route_scatter_kernel(int T, int E, int k, int nbits, const int32_t* __restrict__
     }
 }
 
+
+// ------------------------------------------------------------------ router --
+// Router scores logits = x W_r in fp32 (x bf16 [T, H], W_r fp32 [H, E]
+// row-major), optionally followed in the same launch by the routing above.
+//
+// Workgroup (ks, tb) takes tokens [tb TB, tb TB + TB) over the rows
+// [ks hk, ks hk + hk) of W_r, in steps of 64 rows: wave w takes rows 4w..4w+3
+// of a step, lane l holds columns l + 64 i (i < VPL) for the TB tokens (TB VPL
+// <= 16 accumulators), so one W_r row is one coalesced wave load and the token
+// values are wave-uniform (scalar loads).  Each accumulator adds its rows in
+// ascending order; the 16 waves' sums meet in a fixed tree (wave w adds wave
+// w + 8, then w + 4, w + 2, w + 1) and K-split partials are added in
+// ascending ks, so the scores are the same on every run.
+//
+// Fused form (decode-sized T): the workgroups publish their partials and take
+// an arrival ticket (device-scope atomics, stores complete before the ticket,
+// as in the route-direct Down kernel); the last one adds the partials into
+// LDS and the logits output, returns the ticket to zero and routes from LDS.
+constexpr int kRpWaves = kSmallWaves;     // the fused routing runs in the last workgroup
+constexpr int kRpRows = 4;                // W_r rows per wave per step
+constexpr int kRpStep = kRpWaves * kRpRows;
+constexpr int kRpAcc = 16;                // accumulators per lane (tokens x columns)
+constexpr size_t kRpTreeBytes = sizeof(float) * (kRpWaves / 2) * kRpAcc * kWave;
+constexpr size_t kRpMaxLds = 60 * 1024;
+// tokens per workgroup: 16 accumulators, at most 8 tokens (each token's row
+// pointer and two in-flight x words live in scalar registers)
+__host__ __device__ constexpr int rp_tokens(int vpl) { return kRpAcc / vpl < 8 ? kRpAcc / vpl : 8; }
+
+struct RpArgs {
+    const uint16_t* x;   // bf16 [T, H]
+    const float* w;      // fp32 [H, E]
+    int T, H, E, k, nbits;
+    int hk;              // W_r rows per workgroup, a multiple of kRpStep
+    float* logits;       // [T, E]
+    float* part;         // fused: [gridDim.x][T][E] partial scores
+    int32_t* ticket;     // fused: arrival counter, zero between calls
+    RouteOut o;
+};
+
+template <int VPL, bool FUSED>
+__global__ void __launch_bounds__(kRpWaves * kWave)
+router_project_kernel(const RpArgs a) {
+    constexpr int TB = rp_tokens(VPL);
+    extern __shared__ __attribute__((aligned(16))) float rp_lds[];
+    __shared__ int last_s;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int T = a.T, H = a.H, E = a.E;
+    const int ks = blockIdx.x, t0 = blockIdx.y * TB;
+    // token rows (rows past T repeat row T-1; their sums are never written)
+    const uint16_t* xr[TB];
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) xr[tt] = a.x + (size_t)min(t0 + tt, T - 1) * H;
+    int col[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) col[i] = min(lane + kWave * i, E - 1);
+
+    float acc[TB][VPL];
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) acc[tt][i] = 0.0f;
+
+    const int h_end = (ks + 1) * a.hk;
+    float wv[kRpRows][VPL];
+    uint2 xv[TB];
+    auto load_step = [&](int h0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < kRpRows; ++r)
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) wv[r][i] = a.w[(size_t)(h0 + r) * E + col[i]];
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt) xv[tt] = *reinterpret_cast<const uint2*>(xr[tt] + h0);
+    };
+    int h0 = ks * a.hk + wave * kRpRows;
+    load_step(h0);
+    for (; h0 < h_end; h0 += kRpStep) {
+        float wc[kRpRows][VPL];
+        uint2 xc[TB];
+#pragma unroll
+        for (int r = 0; r < kRpRows; ++r)
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) wc[r][i] = wv[r][i];
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt) xc[tt] = xv[tt];
+        if (h0 + kRpStep < h_end) load_step(h0 + kRpStep);   // the next step's rows in flight
+#pragma unroll
+        for (int r = 0; r < kRpRows; ++r)
+#pragma unroll
+            for (int tt = 0; tt < TB; ++tt) {
+                const uint32_t pair = (r < 2) ? xc[tt].x : xc[tt].y;
+                const float xf = __uint_as_float((r & 1) ? (pair & 0xffff0000u) : (pair << 16));
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) acc[tt][i] = fmaf(xf, wc[r][i], acc[tt][i]);
+            }
+    }
+
+    // the waves' sums in a fixed tree through LDS
+    for (int half = kRpWaves / 2; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half) {
+#pragma unroll
+            for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+                for (int i = 0; i < VPL; ++i)
+                    rp_lds[((wave - half) * kRpAcc + tt * VPL + i) * kWave + lane] = acc[tt][i];
+        }
+        __syncthreads();
+        if (wave < half) {
+#pragma unroll
+            for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) acc[tt][i] += rp_lds[(wave * kRpAcc + tt * VPL + i) * kWave + lane];
+        }
+        __syncthreads();
+    }
+
+    if constexpr (!FUSED) {
+        if (wave == 0) {
+#pragma unroll
+            for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int t = t0 + tt, e = lane + kWave * i;
+                    if (t < T && e < E) a.logits[(size_t)t * E + e] = acc[tt][i];
+                }
+        }
+    } else {
+        if (wave == 0) {
+#pragma unroll
+            for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int t = t0 + tt, e = lane + kWave * i;
+                    if (t < T && e < E)
+                        __hip_atomic_store(a.part + ((size_t)ks * T + t) * E + e, acc[tt][i], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+            __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0)
+            if (lane == 0)
+                last_s = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                         (int)(gridDim.x * gridDim.y) - 1;
+        }
+        __syncthreads();
+        if (!last_s) return;
+        // the last workgroup: all partials into LDS at once (8 requests per thread
+        // in flight, clamped indices, masked after), the scores added in ks order
+        // into LDS and the output, then the routing
+        const int n = T * E, KS = gridDim.x, np = KS * n;
+        float* stage = rp_lds;                       // [KS][n]
+        float* lg = rp_lds + ((np + 3) & ~3);        // [n]
+        int32_t* rl = reinterpret_cast<int32_t*>(lg + ((n + 3) & ~3));
+        for (int j0 = threadIdx.x; j0 < np; j0 += 8 * (int)blockDim.x) {
+            float pv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                pv[u] = __hip_atomic_load(a.part + min(j0 + u * (int)blockDim.x, np - 1), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (j0 + u * (int)blockDim.x < np) stage[j0 + u * blockDim.x] = pv[u];
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < n; idx += blockDim.x) {
+            float v = 0.0f;
+            for (int q = 0; q < KS; ++q) v += stage[q * n + idx];
+            lg[idx] = v;
+            a.logits[idx] = v;
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(a.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        route_small_body<VPL>(lg, T, E, a.k, a.nbits, a.o, rl);
+    }
+}
+
 // ----------------------------------------------------------------------------
 
 static int bits_for(int E) {
@@ -463,8 +651,7 @@ static hipError_t launch_small(const float* logits, int T, int E, int k, const R
                                hipStream_t st) {
     const size_t lds = route_small_lds_bytes(T, E, k);
     hipLaunchKernelGGL(route_small_kernel<VPL>, dim3(1), dim3(kSmallWaves * kWave), lds, st,
-                       logits, T, E, k, bits_for(E), o.ids, o.weights, o.counts, o.offsets,
-                       o.perm, o.route_pos);
+                       logits, T, E, k, bits_for(E), o);
     return hipGetLastError();
 }
 
@@ -489,6 +676,63 @@ hipError_t launch_route(const float* logits, int T, int E, int k, const RouteOut
     hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(kBigWaves * kWave), 0, st, T, E, k,
                        bits_for(E), o.ids, hist, o.counts, o.offsets, o.perm, o.route_pos);
     return hipGetLastError();
+}
+
+// ---- router scores (+ routing)
+static int vpl_for(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : 8; }
+
+RouteProjectPlan route_project_plan(int T, int H, int E, int k) {
+    RouteProjectPlan p{};
+    const int TB = rp_tokens(vpl_for(E));
+    p.ntb = ceil_div(T, TB);
+    const size_t lg_bytes = sizeof(float) * (((size_t)T * E + 3) & ~(size_t)3);
+    p.lds = kRpTreeBytes;
+    // the last workgroup stages every partial in LDS next to the scores and the
+    // routing's own arrays: K splits (a divisor of the 64-row steps, at most 64)
+    // as many as fit
+    const size_t fixed = lg_bytes + route_small_lds_bytes(T, E, k);
+    p.fused = T > 0 && route_use_small(T, E, k) && fixed + lg_bytes <= kRpMaxLds;
+    p.ks = 1;
+    if (p.fused) {
+        const int steps = H / kRpStep;
+        const int cap = (int)std::min<size_t>(64, (kRpMaxLds - fixed) / lg_bytes);
+        for (int d = 1; d <= steps && d <= cap; ++d)
+            if (steps % d == 0) p.ks = d;
+        p.lds = std::max(p.lds, fixed + (size_t)p.ks * lg_bytes);
+    }
+    p.hk = H / p.ks;
+    p.ws_bytes = kRpTicketBytes + (p.fused ? sizeof(float) * (size_t)p.ks * T * E
+                                           : route_workspace_bytes(T, E, k));
+    return p;
+}
+
+template <int VPL>
+static hipError_t launch_project(const RpArgs& a, const RouteProjectPlan& p, hipStream_t st) {
+    if (p.fused)
+        hipLaunchKernelGGL((router_project_kernel<VPL, true>), dim3(p.ks, p.ntb), dim3(kRpWaves * kWave), p.lds, st, a);
+    else
+        hipLaunchKernelGGL((router_project_kernel<VPL, false>), dim3(p.ks, p.ntb), dim3(kRpWaves * kWave), p.lds, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_project(const uint16_t* x, const float* w_router, int T, int H, int E, int k,
+                                float* logits, const RouteOut& o, void* ws, hipStream_t st) {
+    if (T == 0) return launch_route(nullptr, 0, E, k, o, nullptr, st);   // counts and offsets only
+    const RouteProjectPlan p = route_project_plan(T, H, E, k);
+    RpArgs a{};
+    a.x = x;
+    a.w = w_router;
+    a.T = T; a.H = H; a.E = E; a.k = k; a.nbits = bits_for(E);
+    a.hk = p.hk;
+    a.logits = logits;
+    a.ticket = static_cast<int32_t*>(ws);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + kRpTicketBytes);
+    a.o = o;
+    const int vpl = vpl_for(E);
+    hipError_t err = vpl == 1 ? launch_project<1>(a, p, st) : vpl == 2 ? launch_project<2>(a, p, st)
+                   : vpl == 4 ? launch_project<4>(a, p, st) : launch_project<8>(a, p, st);
+    if (err != hipSuccess || p.fused) return err;
+    return launch_route(logits, T, E, k, o, static_cast<char*>(ws) + kRpTicketBytes, st);
 }
 
 }  // namespace moe

@@ -114,6 +114,18 @@ def test_host_validation_before_any_launch():
     assert L.moe_forward_ex(None, ctypes.byref(r), None, None, None, None, 2048, 768, 0, 0,
                             None, None, 0, None) == 0
     r.T = 4
+    # router scores + routing: H a positive multiple of 64, k <= E, workspace large enough
+    assert L.moe_route_project(None, None, 4, 2048, 128, 8, None, None, None, 0, None) == -1
+    assert L.moe_route_project(None, None, 4, 100, 128, 8, None, ctypes.byref(r), None, 0, None) == -2
+    assert L.moe_route_project(None, None, 4, 2048, 8, 9, None, ctypes.byref(r), None, 0, None) == -1
+    assert L.moe_route_project(None, None, 4, 2048, 128, 8, None, ctypes.byref(r), None, 0, None) == -1
+    r.expert_counts = r.route_pos = 4096
+    need = L.moe_route_project_workspace_size(4, 2048, 128, 8)
+    assert need >= 256 + 4 * 4 * 128
+    assert L.moe_route_project(good, good, 4, 2048, 128, 8, good, ctypes.byref(r), good, need - 16,
+                               None) == -3
+    assert L.moe_route_project(bad, good, 4, 2048, 128, 8, good, ctypes.byref(r), good, need, None) == -1
+    assert L.moe_route_project_workspace_size(4, 100, 128, 8) == 0
     # packing rejects in-place and null
     assert L.moe_pack_weights(good, good, 4, 256, 64, 0, good, None, None) == -1
     assert L.moe_pack_weights(good, None, 4, 256, 64, 0, good, good, None) == -1

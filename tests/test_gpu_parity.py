@@ -62,10 +62,22 @@ def _compare(name, x, lg, k, dev_w, host_w, quant, path, tokens=None):
 
 @pytest.mark.parametrize("path", ["auto", "grouped", "route_direct"])
 def test_tiny_bf16(path):
+    """The tiny layer end to end: router scores and routing in one call, then the layer; the
+    oracle routes the kernel's fp32 scores (checked against its own) and computes the layer."""
     name = "tiny_bf16"
+    wl = WORKLOADS[name]
     a = workload_inputs(name)
-    _compare(name, a["x"], a["logits"], WORKLOADS[name].k, workload_dev(name), workload_weights(name),
-             "bf16", path)
+    pgu, pd, _ = workload_dev(name)
+    r, lg = moe.route_project(bf16_dev(a["x"]), torch.from_numpy(a["w_router"]).to(DEV), wl.k)
+    out = moe.forward(bf16_dev(a["x"]), r, pgu, pd, path=path)
+    torch.cuda.synchronize()
+    g = lg.cpu().numpy()
+    ref_lg = oracle.router_logits(a["x"], a["w_router"])
+    assert np.max(np.abs(g - ref_lg)) <= 1e-5
+    ref_r = oracle.route(g, wl.k)
+    check_routing(routes_np(r), ref_r)
+    ref = oracle_out(a["x"], ref_r, workload_weights(name), "bf16")
+    check_out(out.float().cpu().numpy(), ref, "bf16", f"{name} {path}")
 
 
 @pytest.mark.parametrize("B", [1, 2, 3, 4])
@@ -166,18 +178,29 @@ def test_graph_replay_bitwise_equal(name):
     wl = WORKLOADS[name]
     a = workload_inputs(name, batch=4 if wl.batches else None)
     pgu, pd, scales = workload_dev(name)
-    lg = torch.from_numpy(a["logits"]).to(DEV)
     x = bf16_dev(a["x"])
     T = x.shape[0]
     routes = moe.Routes(T, wl.E, wl.k, DEV)
     out = torch.empty((T, wl.H), dtype=torch.bfloat16, device=DEV)
     ws = torch.empty(max(256, moe.forward_workspace_size(T, wl.H, wl.I, wl.E, wl.k, wl.quant)),
                      dtype=torch.uint8, device=DEV)
-    rws_n = moe.route_workspace_size(T, wl.E, wl.k)
-    rws = torch.empty(max(rws_n, 256), dtype=torch.uint8, device=DEV) if rws_n else None
+    if "w_router" in a:   # router scores and routing in one launch (arrival counter in rws)
+        wr = torch.from_numpy(a["w_router"]).to(DEV)
+        lg = torch.empty((T, wl.E), dtype=torch.float32, device=DEV)
+        rws = torch.zeros(moe.route_project_workspace_size(T, wl.H, wl.E, wl.k), dtype=torch.uint8, device=DEV)
+
+        def route_step():
+            moe.route_project(x, wr, wl.k, out=routes, logits=lg, workspace=rws)
+    else:
+        lg = torch.from_numpy(a["logits"]).to(DEV)
+        rws_n = moe.route_workspace_size(T, wl.E, wl.k)
+        rws = torch.empty(max(rws_n, 256), dtype=torch.uint8, device=DEV) if rws_n else None
+
+        def route_step():
+            moe.route(lg, wl.k, out=routes, workspace=rws)
 
     def step():
-        moe.route(lg, wl.k, out=routes, workspace=rws)
+        route_step()
         moe.forward(x, routes, pgu, pd, quant=wl.quant, scales=scales, out=out, workspace=ws)
 
     step()
