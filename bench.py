@@ -342,6 +342,91 @@ def bench_router(torch, moe, batches, iters, H=2048, E=128, k=8):
     return res
 
 
+# The route-direct latencies printed by "perf: add small-batch route MMA for MoE"
+# (Performance tables, forced route path, single-op CUDA graph with preallocated
+# output, top-8, on an H20): context for the same shapes here, not a target.
+PAGES_ROUTE_US = {
+    "fp8_per_tensor E=192 H=4096 I=192": [13.243, 16.833, 22.773, 30.663, 35.983, 41.554, 47.259, 54.124],
+    "fp8_block128 E=128 H=2048 I=768": [17.349, 29.863, 40.708, 52.732, 62.510, 73.040, 84.419, 94.352],
+    "fp8_block128 E=128 H=4096 I=512": [19.779, 37.585, 52.295, 63.833, 85.218, 98.465, 111.362, 121.922],
+}
+
+
+def bench_pages_shapes(torch, moe, iters, batches=range(1, 9)):
+    """moe_forward alone (routes given, as the pages time their op) captured in a
+    HIP graph with preallocated output, at the pages' three FP8 decode shapes:
+    replayed cold (a 1 GiB read before each replay) and warm (back to back)."""
+    from workloads import random_activations, random_weights, workload_weights
+    evict = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    shapes = [("fp8_per_tensor E=192 H=4096 I=192", 192, 4096, 192, "fp8_per_tensor",
+               lambda: workload_weights("decode_fp8_tensor")),
+              ("fp8_block128 E=128 H=2048 I=768", 128, 2048, 768, "fp8_block128",
+               lambda: random_weights(128, 2048, 768, "fp8_block128", 6)),
+              ("fp8_block128 E=128 H=4096 I=512", 128, 4096, 512, "fp8_block128",
+               lambda: workload_weights("prefill_fp8_block"))]
+    # leave the idle clock state before the first timing (tens of milliseconds of load)
+    for _ in range(200):
+        evict.amax()
+    torch.cuda.synchronize()
+    res = {}
+    for key, E, H, I, quant, wfn in shapes:
+        pgu, pd, scales = dev_weights(torch, moe, wfn(), quant)
+        out_k = {}
+        for B in batches:
+            a = random_activations(B, H, E, 20000 + B)
+            x = torch.from_numpy(a["x"].view(np.int16)).cuda().view(torch.bfloat16)
+            r = moe.route(torch.from_numpy(a["logits"]).cuda(), 8)
+            out = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+            path = moe.select_path(B, H, I, E, 8, quant)
+            ws = torch.empty(max(256, moe.forward_workspace_size(B, H, I, E, 8, quant, path)),
+                             dtype=torch.uint8, device="cuda")
+
+            def fwd():
+                moe.forward(x, r, pgu, pd, quant=quant, scales=scales, out=out, path=path, workspace=ws)
+
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                fwd()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fwd()
+            ts = []
+            for it in range(iters + 2):
+                evict.amax()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                g.replay()
+                e1.record()
+                if it >= 2:
+                    ts.append((e0, e1))
+            torch.cuda.synchronize()
+            cold = float(np.median([p.elapsed_time(q) for p, q in ts])) * 1e3
+            for _ in range(20):
+                g.replay()
+            w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            nwarm = 200
+            w0.record()
+            for _ in range(nwarm):
+                g.replay()
+            w1.record()
+            torch.cuda.synchronize()
+            warm = w0.elapsed_time(w1) / nwarm * 1e3
+            del g
+            h20 = PAGES_ROUTE_US[key][B - 1]
+            out_k[B] = dict(path=path, us_graph_cold=round(cold, 2), us_graph_warm=round(warm, 2),
+                            pages_h20_us=h20, h20_over_warm=round(h20 / warm, 3),
+                            h20_over_cold=round(h20 / cold, 3))
+            log(f"{key} B={B} ({path}): graph cold {cold:.2f} us, warm {warm:.2f} us (pages, H20: {h20} us)")
+        res[key] = out_k
+        del pgu, pd, scales
+        torch.cuda.empty_cache()
+    del evict
+    return res
+
+
 def layer_fractions(wl, t_step, peak_tflops):
     """The whole step against the dense MFMA peak and against HBM: algorithmic flops
     6*R*H*I; the HBM floor with the gather fused = every expert's weights once, x
@@ -426,6 +511,8 @@ def profile_only(torch, moe, args):
                 torch.mul(src, 1, out=dst)
             torch.cuda.synchronize()
             log(f"copy: {args.steps} x 1 GiB elementwise copy kernels")
+        elif name == "pages_shapes":
+            bench_pages_shapes(torch, moe, args.decode_iters)
         elif name == "router":
             bench_router(torch, moe, (1, 2, 3, 4), args.decode_iters)
         elif name.startswith("crossover_"):
@@ -453,7 +540,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
                     help="profiling runs: comma list of prefill_bf16, prefill_fp8_block, decode_bf16, "
-                         "decode_fp8_tensor, router, copy (a plain 1 GiB device copy, the traffic-counter "
+                         "decode_fp8_tensor, router, pages_shapes, copy (a plain 1 GiB device copy, the traffic-counter "
                          "reference); prints per-stage times instead of the JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -511,6 +598,14 @@ def main():
             timing="cold HBM, moe_route + moe_forward between two HIP events, median",
             decode_fp8_tensor=bench_crossover(torch, moe, "decode_fp8_tensor", range(1, 17), 30),
             decode_bf16=bench_crossover(torch, moe, "decode_bf16", range(1, 17), 30))
+        torch.cuda.empty_cache()
+        log("the pages' FP8 decode shapes, forward alone in a HIP graph ...")
+        line["pages_shapes"] = dict(
+            timing=f"moe_forward alone (routes given) captured in a HIP graph with preallocated output; "
+                   f"cold: median of {args.decode_iters} replays after a 1 GiB read; warm: 200 back-to-back "
+                   "replays. pages_h20_us: the forced route-direct single-op CUDA graph latency the pages "
+                   "print for the same shape on an H20 (context)",
+            shapes=bench_pages_shapes(torch, moe, args.decode_iters))
         torch.cuda.empty_cache()
         log("decode fp8 per-tensor B=1..4 ...")
         line["decode_fp8_per_tensor"] = dict(

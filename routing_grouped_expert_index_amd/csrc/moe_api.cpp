@@ -100,14 +100,14 @@ Layout layout(int T, int H, int I, int E, int k, int quant, int path) {
     L.ntiles = take(grouped ? sizeof(int32_t) : 0);
     L.amax = take(2 * sizeof(uint32_t));
     L.scal = take(2 * sizeof(float));
-    L.xq = take(quant != MOE_BF16 ? (size_t)T * H : 0);
-    L.sx = take(quant == MOE_FP8_BLOCK128 ? sizeof(float) * (size_t)T * (H / 128) : 0);
+    L.xq = take(grouped && quant != MOE_BF16 ? (size_t)T * H : 0);
+    L.sx = take(grouped && quant == MOE_FP8_BLOCK128 ? sizeof(float) * (size_t)T * (H / 128) : 0);
     size_t hbytes = 0;
     if (quant == MOE_BF16) hbytes = R * I * 2;
     else if (quant == MOE_FP8_PER_TENSOR || !grouped) hbytes = R * I * 4;
     L.h = take(hbytes);
-    L.hq = take(quant != MOE_BF16 ? R * I : 0);
-    L.sh = take(quant == MOE_FP8_BLOCK128 ? sizeof(float) * R * (I / 128) : 0);
+    L.hq = take(grouped && quant != MOE_BF16 ? R * I : 0);
+    L.sh = take(grouped && quant == MOE_FP8_BLOCK128 ? sizeof(float) * R * (I / 128) : 0);
     L.y = take(grouped ? R * H * 2 : 0);
     const size_t rd_blocks = grouped ? 0 : (size_t)T * (H / 32);
     L.rd_hmax = take(!grouped && quant == MOE_FP8_PER_TENSOR
@@ -331,10 +331,10 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
         MOE_STEP(moe::launch_grouped_down(P, st), "down");
         MOE_STEP(moe::launch_combine(P, st), "combine");
     } else {
-        // per-tensor FP8 quantises inside the route-direct kernels
-        if (quant == MOE_FP8_BLOCK128) MOE_STEP(moe::launch_quant_x(P, st), "quant_x");
+        // FP8 quantises x and h inside the route-direct kernels (per tensor: from
+        // all of x and the Gate/Up workgroups' h maxima; blockwise: per token or
+        // route row and 128 channels, in the workgroup that uses them)
         MOE_STEP(moe::launch_route_direct_gate_up(P, st), "rd_gate_up");
-        if (quant == MOE_FP8_BLOCK128) MOE_STEP(moe::launch_quant_h(P, st), "quant_h");
         MOE_STEP(moe::launch_route_direct_down(P, st), "rd_down_combine");
     }
 #undef MOE_STEP

@@ -46,7 +46,6 @@ enum RdQuant { RD_BF16 = 0, RD_TENSOR = 1, RD_BLOCK = 2 };
 
 struct RdArgs {
     const uint8_t* act;      // x bf16 [T,H] (bf16, per-tensor) or e4m3 codes [T,H] (block)
-    const float* sx;         // block: [T][H/128]
     const int32_t* ids;      // [T*k]
     const float* tw;         // [T*k]
     const uint8_t* wgu;      // packed Gate/Up
@@ -54,7 +53,6 @@ struct RdArgs {
     const float* s_gu;
     const float* s_d;
     const uint8_t* h;        // Down input: bf16 [R][I] | fp32 [R][I] (per-tensor) | e4m3 [R][I] (block)
-    const float* sh;         // block: [R][I/128]
     void* hout;              // Gate/Up output: bf16 [R][I] | fp32 [R][I]
     float* hmax;             // per-tensor: max |h| per Gate/Up workgroup [R][I/32]
     float* part;             // Down partial sums [T*H/32][items][32]
@@ -163,6 +161,35 @@ __device__ __forceinline__ void quant_row(uint8_t* dst, const T* src, int n, flo
     }
 }
 
+// quantise n values (n % 128 == 0) of a bf16 (or fp32) row per 128-value group
+// into e4m3 codes in LDS, s = amax/448 of the group into sdst[group]; whole
+// workgroup, 16 lanes per group (8 values each)
+template <typename T, int NW>
+__device__ __forceinline__ void quant_row_block128(uint8_t* dst, float* sdst, const T* src, int n) {
+    for (int i = threadIdx.x * 8; i < n; i += 64 * NW * 8) {
+        float v[8];
+        if constexpr (sizeof(T) == 2) {
+            bf16x8_to_f32(*reinterpret_cast<const u32x4*>(src + i), v);
+        } else {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(src + i);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(src + i + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { v[q] = a[q]; v[4 + q] = b[q]; }
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));   // the group's 16 lanes
+        const float sc = scale_from_amax(m);
+        uint2 c;
+        c.x = f32x4_to_e4m3x4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+        c.y = f32x4_to_e4m3x4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
+        *reinterpret_cast<uint2*>(dst + i) = c;
+        if ((threadIdx.x & 15) == 0) sdst[i / 128] = sc;
+    }
+}
+
 // dot of the lane's two weight halves of one slice with its activation values
 template <bool FP8>
 __device__ __forceinline__ float dot_slice(const u32x4 w[2], const float v[32]) {
@@ -217,6 +244,7 @@ __global__ void __launch_bounds__(64 * NW)
 rd_gate_up_kernel(const RdArgs a) {
     constexpr bool FP8 = Q != RD_BF16;
     __shared__ __attribute__((aligned(16))) uint8_t xrow[kRdActBytes];
+    __shared__ float sxs[Q == RD_BLOCK ? kRdActBytes / 128 : 1];   // blockwise: the row's x scales
     __shared__ float red[NW][2][32];
     __shared__ float sred[NW];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -266,10 +294,12 @@ rd_gate_up_kernel(const RdArgs a) {
     load_batch(B0, s0);   // the weight stream starts before the activation row is staged
 
     float xs = 1.0f;
+    const uint16_t* x = reinterpret_cast<const uint16_t*>(a.act);
     if constexpr (Q == RD_TENSOR) {
-        const uint16_t* x = reinterpret_cast<const uint16_t*>(a.act);
         xs = scale_from_amax(block_amax<uint16_t, NW>(x, (long)a.T * a.H, sred));
         quant_row<uint16_t, NW>(xrow, x + (long)t * a.H, a.H, xs);
+    } else if constexpr (Q == RD_BLOCK) {   // the token's codes and per-128 scales, here
+        quant_row_block128<uint16_t, NW>(xrow, sxs, x + (long)t * a.H, a.H);
     } else {
         stage_row<NW>(xrow, a.act + (long)t * Kb, Kb);
     }
@@ -300,7 +330,7 @@ rd_gate_up_kernel(const RdArgs a) {
             }
             if constexpr (Q == RD_BLOCK) {
                 const int kb = sl / 2;   // 128-deep scale block
-                const float sa = a.sx[(long)t * (a.H / 128) + kb];
+                const float sa = sxs[kb];
                 const float* swr = a.s_gu + ((long)e * (a.H / 128) + kb) * (2 * a.I / 128);
                 accg = fmaf(dg, sa * swr[cg], accg);
                 accu = fmaf(du, sa * swr[cu], accu);
@@ -407,7 +437,10 @@ template <int Q, int NW, int KP, int U>
 __global__ void __launch_bounds__(64 * NW)
 rd_down_part_kernel(const RdArgs a) {
     constexpr bool FP8 = Q != RD_BF16;
-    __shared__ __attribute__((aligned(16))) uint8_t hrow_s[Q == RD_TENSOR ? 2048 : 16];
+    // FP8: the route's h row as e4m3 codes (quantised here), blockwise with its
+    // per-128 scales
+    __shared__ __attribute__((aligned(16))) uint8_t hrow_s[FP8 ? 2048 : 16];
+    __shared__ float shs[Q == RD_BLOCK ? 2048 / 128 : 1];
     __shared__ float red[NW][32];
     __shared__ int last_s;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -428,7 +461,7 @@ rd_down_part_kernel(const RdArgs a) {
     const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + lane * 16;
 
     u32x4 vw[U][2];
-    u32x4 va[U][2];   // activation slices of the batch (rows not staged in LDS)
+    u32x4 va[U][2];   // bf16: activation slices of the batch (the row is not staged in LDS)
     const uint8_t* hg = a.h + (long)r * Kb + hh * 32;
     auto load_batch = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
@@ -436,7 +469,7 @@ rd_down_part_kernel(const RdArgs a) {
 #pragma unroll
             for (int q = 0; q < 2; ++q)
                 vw[u][q] = *reinterpret_cast<const u32x4*>(wb + (long)(s + u) * 2048 + q * 1024);
-        if constexpr (Q != RD_TENSOR) {
+        if constexpr (!FP8) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -464,6 +497,9 @@ rd_down_part_kernel(const RdArgs a) {
         hs = scale_from_amax(m);
         quant_row<float, NW>(hrow_s, reinterpret_cast<const float*>(a.h) + (long)r * a.I, a.I, hs);
         __syncthreads();
+    } else if constexpr (Q == RD_BLOCK) {   // the route's h row per 128 channels, here
+        quant_row_block128<float, NW>(hrow_s, shs, reinterpret_cast<const float*>(a.h) + (long)r * a.I, a.I);
+        __syncthreads();
     }
 
     float y = 0.0f;
@@ -479,17 +515,12 @@ rd_down_part_kernel(const RdArgs a) {
                 d = dot_slice_bf16(vw[u], va[u], 0.0f);
             } else {
                 float v[32];
-                if constexpr (Q == RD_TENSOR) {
-                    lds_act_slice<true>(hrow, s + u, hh, v);
-                } else {
-                    e4m3x16_to_f32(va[u][0], v);
-                    e4m3x16_to_f32(va[u][1], v + 16);
-                }
+                lds_act_slice<true>(hrow, s + u, hh, v);
                 d = dot_slice<FP8>(vw[u], v);
             }
             if constexpr (Q == RD_BLOCK) {
                 const int kb = (s + u) / 2;
-                const float sc = a.sh[(long)r * (a.I / 128) + kb] *
+                const float sc = shs[kb] *
                                  a.s_d[((long)e * (a.I / 128) + kb) * (a.H / 128) + n0 / 128];
                 y = fmaf(d, sc, y);
             } else {
@@ -638,16 +669,14 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
 
 static RdArgs rd_args(const FwdPlan& p) {
     RdArgs a{};
-    a.act = p.quant == Q_FP8_BLOCK ? p.xq : reinterpret_cast<const uint8_t*>(p.x);
-    a.sx = p.sx;
+    a.act = reinterpret_cast<const uint8_t*>(p.x);
     a.ids = p.ids;
     a.tw = p.tw;
     a.wgu = static_cast<const uint8_t*>(p.wgu);
     a.wd = static_cast<const uint8_t*>(p.wd);
     a.s_gu = p.s_gu;
     a.s_d = p.s_d;
-    a.h = p.quant == Q_FP8_BLOCK ? p.hq : static_cast<const uint8_t*>(p.h);
-    a.sh = p.sh;
+    a.h = static_cast<const uint8_t*>(p.h);
     a.hout = p.h;
     a.hmax = p.rd_hmax;
     a.part = p.rd_part;
