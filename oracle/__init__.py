@@ -23,6 +23,10 @@ Functions and what they follow (page titles and sections):
   quantise_activations, e4m3_encode/decode, bf16_decode -- the FP8 per-tensor
                 and 128-channel blockwise activation quantisation and the
                 codecs ("perf: add small-batch route MMA for MoE", Summary).
+  mx_scale_byte, quantise_group_mx, quant "fp8_mx32" -- MX FP8: e4m3 codes
+                with one power-of-two (E8M0) scale per 32 values along K
+                ("[mxfp8 moe training] add per group blocked scale kernels",
+                Summary: mxfp8 scales; the OCP MX scale rule).
 """
 import ctypes
 import os
@@ -33,7 +37,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 _lib = None
 
-QUANT = {"bf16": 0, "fp8_per_tensor": 1, "fp8_block128": 2}
+QUANT = {"bf16": 0, "fp8_per_tensor": 1, "fp8_block128": 2, "fp8_mx32": 3}
 
 
 def _load():
@@ -55,6 +59,10 @@ def _load():
     lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
     lib.oracle_scale_from_amax.restype = ctypes.c_float
     lib.oracle_scale_from_amax.argtypes = [ctypes.c_float]
+    lib.oracle_mx_scale_byte.restype = ctypes.c_uint8
+    lib.oracle_mx_scale_byte.argtypes = [ctypes.c_float]
+    lib.oracle_quantise_group_mx.restype = ctypes.c_uint8
+    lib.oracle_quantise_group_mx.argtypes = [P, ctypes.c_long, P]
     lib.oracle_quantise_group.restype = ctypes.c_float
     lib.oracle_quantise_group.argtypes = [P, ctypes.c_long, P]
     lib.oracle_router_logits.restype = None
@@ -168,8 +176,9 @@ def forward(x_bf16, topk_ids, topk_weights, w_gate_up, w_down, quant="bf16",
     wgu = _c(w_gate_up, wdt)
     wd = _c(w_down, wdt)
     assert wd.shape == (E, I, H)
-    sgu = None if q == 0 else _c(s_gate_up, np.float32)
-    sd = None if q == 0 else _c(s_down, np.float32)
+    sdt = np.uint8 if q == 3 else np.float32   # MX: E8M0 scale bytes
+    sgu = None if q == 0 else _c(s_gate_up, sdt)
+    sd = None if q == 0 else _c(s_down, sdt)
     ids = _c(topk_ids, np.int32)
     tw = _c(topk_weights, np.float32)
     tok = None if tokens is None else _c(tokens, np.int32)
@@ -189,7 +198,25 @@ def quantise_activations(x_bf16, quant):
     x = _c(x_bf16, np.uint16)
     T, H = x.shape
     codes = np.empty((T, H), np.uint8)
-    scales = np.empty(1 if q == 1 else T * (H // 128), np.float32)
+    if q == 3:
+        scales = np.empty(T * (H // 32), np.uint8)
+    else:
+        scales = np.empty(1 if q == 1 else T * (H // 128), np.float32)
     if _load().oracle_quantise_activations(_ptr(x), T, H, q, _ptr(codes), _ptr(scales)) != 0:
         raise ValueError("unsupported quantisation")
+    if q == 3:
+        return codes, scales.reshape(T, H // 32)
     return codes, (scales[0] if q == 1 else scales.reshape(T, H // 128))
+
+
+def mx_scale_byte(amax):
+    """E8M0 byte of an MX group whose largest magnitude is amax (fp32)."""
+    return int(_load().oracle_mx_scale_byte(float(np.float32(amax))))
+
+
+def quantise_group_mx(values):
+    """(codes, E8M0 byte) of one MX group of fp32 values."""
+    v = _c(values, np.float32).ravel()
+    q = np.empty(v.size, dtype=np.uint8)
+    b = _load().oracle_quantise_group_mx(_ptr(v), v.size, _ptr(q))
+    return q, int(b)

@@ -36,7 +36,15 @@
  *  - per-tensor: one scale for all of x [T,H] and one for all of h [T*k, I];
  *    blockwise: one scale per token per 128 channels (x) and per route row per
  *    128 channels (h); weight scales are given with the weights;
- *  - the combine sums j = 0..k-1 in ascending order.
+ *  - the combine sums j = 0..k-1 in ascending order;
+ *  - MX ("[mxfp8 moe training] add per group blocked scale kernels", Summary:
+ *    mxfp8 scales): one power-of-two scale per 32 consecutive values along K,
+ *    stored as an E8M0 byte b (scale 2^(b-127)); a group's scale is
+ *    2^(floor(log2 amax) - 8), 8 being the largest exponent of e4m3 (the OCP
+ *    MX rule), byte 0 for an all-zero group, bytes clamped to [0, 254]; codes
+ *    are e4m3(v / scale) as above.  Weights come with their scales per 32 rows
+ *    of K per output column; x is quantised per token and h per route row,
+ *    each per 32 channels.
  */
 #include <math.h>
 #include <stdint.h>
@@ -49,6 +57,7 @@
 #define ORC_BF16 0
 #define ORC_FP8_PER_TENSOR 1
 #define ORC_FP8_BLOCK128 2
+#define ORC_FP8_MX32 3
 
 int oracle_num_threads(void) {
 #ifdef _OPENMP
@@ -113,6 +122,32 @@ uint8_t oracle_e4m3_encode(float f) {
 /* Scale of a quantisation group: amax / 448 in fp32, or 1 for an all-zero group. */
 float oracle_scale_from_amax(float amax) {
     return amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
+/* E8M0 byte of an MX group with largest magnitude amax (see the header). */
+uint8_t oracle_mx_scale_byte(float amax) {
+    int ex, b;
+    if (!(amax > 0.0f)) return 0;
+    frexp((double)amax, &ex);          /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+    b = (ex - 1) - 8 + 127;
+    return (uint8_t)(b < 0 ? 0 : b > 254 ? 254 : b);
+}
+
+double oracle_e8m0_decode(uint8_t b) { return ldexp(1.0, (int)b - 127); }
+
+/* MX-quantise n fp32 values as one group; returns the E8M0 byte.  v / scale is
+ * exact (a power of two), so the codes are those of the values themselves. */
+uint8_t oracle_quantise_group_mx(const float *v, long n, uint8_t *q) {
+    float amax = 0.0f;
+    uint8_t b;
+    long i;
+    for (i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    b = oracle_mx_scale_byte(amax);
+    for (i = 0; i < n; ++i) q[i] = oracle_e4m3_encode((float)((double)v[i] / oracle_e8m0_decode(b)));
+    return b;
 }
 
 /* Quantise n fp32 values with one scale; returns the scale. */
@@ -213,6 +248,7 @@ typedef struct {
     const float *s_d;         /* per-tensor [E]; block128 [E, I/128, H/128] */
     float s_x;                /* per-tensor activation scale */
     const float *s_x_blk;     /* block128 activation scales [T, H/128] */
+    const uint8_t *mx_x;      /* MX activation scale bytes [T, H/32] */
     const uint8_t *q_x;       /* fp8 activation codes [T, H] */
 } orc_layer;
 
@@ -221,6 +257,8 @@ static double w_gu_at(const orc_layer *L, int e, int h, int n) {
     if (L->quant == ORC_BF16) return oracle_bf16_decode(((const uint16_t *)L->w_gu)[idx]);
     {
         double q = oracle_e4m3_decode(((const uint8_t *)L->w_gu)[idx]);
+        if (L->quant == ORC_FP8_MX32)   /* bytes [E][H/32][2I] */
+            return q * oracle_e8m0_decode(((const uint8_t *)L->s_gu)[((long)e * (L->H / 32) + h / 32) * (2L * L->I) + n]);
         if (L->quant == ORC_FP8_PER_TENSOR) return q * L->s_gu[e];
         return q * L->s_gu[((long)e * (L->H / 128) + h / 128) * (2L * L->I / 128) + n / 128];
     }
@@ -231,6 +269,8 @@ static double w_d_at(const orc_layer *L, int e, int i, int n) {
     if (L->quant == ORC_BF16) return oracle_bf16_decode(((const uint16_t *)L->w_d)[idx]);
     {
         double q = oracle_e4m3_decode(((const uint8_t *)L->w_d)[idx]);
+        if (L->quant == ORC_FP8_MX32)   /* bytes [E][I/32][H] */
+            return q * oracle_e8m0_decode(((const uint8_t *)L->s_d)[((long)e * (L->I / 32) + i / 32) * L->H + n]);
         if (L->quant == ORC_FP8_PER_TENSOR) return q * L->s_d[e];
         return q * L->s_d[((long)e * (L->I / 128) + i / 128) * (L->H / 128) + n / 128];
     }
@@ -243,6 +283,8 @@ static void activation(const orc_layer *L, int t, double *a) {
         long idx = (long)t * L->H + h;
         if (L->quant == ORC_BF16) a[h] = oracle_bf16_decode(L->x[idx]);
         else if (L->quant == ORC_FP8_PER_TENSOR) a[h] = oracle_e4m3_decode(L->q_x[idx]) * L->s_x;
+        else if (L->quant == ORC_FP8_MX32)
+            a[h] = oracle_e4m3_decode(L->q_x[idx]) * oracle_e8m0_decode(L->mx_x[(long)t * (L->H / 32) + h / 32]);
         else a[h] = oracle_e4m3_decode(L->q_x[idx]) * L->s_x_blk[(long)t * (L->H / 128) + h / 128];
     }
 }
@@ -312,13 +354,15 @@ int oracle_forward_ep(const uint16_t *x, int T, int H, int I, int E, int k,
     orc_layer L;
     uint8_t *q_x = NULL;
     float *s_x_blk = NULL, *h_all = NULL, s_h = 1.0f;
+    uint8_t *mx_x = NULL;
     double *hq_all = NULL;
     int bad = 0, ti;
     long i;
     (void)E;
-    if (quant < 0 || quant > 2) return -1;
+    if (quant < 0 || quant > 3) return -1;
     if (e0 < 0 || n_local < 1) return -1;
     if (quant == ORC_FP8_BLOCK128 && (H % 128 || I % 128)) return -1;
+    if (quant == ORC_FP8_MX32 && (H % 32 || I % 32)) return -1;
     memset(&L, 0, sizeof L);
     L.T = T; L.H = H; L.I = I; L.E = E; L.k = k; L.quant = quant;
     L.x = x; L.w_gu = w_gu; L.w_d = w_d; L.s_gu = s_gu; L.s_d = s_d;
@@ -334,6 +378,17 @@ int oracle_forward_ep(const uint16_t *x, int T, int H, int I, int E, int k,
             for (i = 0; i < (long)T * H; ++i) xf[i] = oracle_bf16_decode(x[i]);
             L.s_x = oracle_quantise_group(xf, (long)T * H, q_x);
             free(xf);
+        } else if (quant == ORC_FP8_MX32) {
+            int nb = H / 32, t, c, j;
+            mx_x = (uint8_t *)malloc((size_t)T * nb);
+            if (!mx_x) { free(q_x); return -1; }
+            for (t = 0; t < T; ++t)
+                for (c = 0; c < nb; ++c) {
+                    float v[32];
+                    for (j = 0; j < 32; ++j) v[j] = oracle_bf16_decode(x[(long)t * H + c * 32 + j]);
+                    mx_x[(long)t * nb + c] = oracle_quantise_group_mx(v, 32, q_x + (long)t * H + c * 32);
+                }
+            L.mx_x = mx_x;
         } else {
             int nb = H / 128, t, c, j;
             s_x_blk = (float *)malloc(sizeof(float) * (size_t)T * nb);
@@ -418,6 +473,15 @@ int oracle_forward_ep(const uint16_t *x, int T, int H, int I, int E, int k,
                             s = oracle_quantise_group(hf, 128, q);
                             for (n = 0; n < 128; ++n) hd[c * 128 + n] = oracle_e4m3_decode(q[n]) * s;
                         }
+                    } else if (quant == ORC_FP8_MX32) {
+                        uint8_t q[32];
+                        float hf[32];
+                        for (c = 0; c < I / 32; ++c) {
+                            uint8_t b;
+                            for (n = 0; n < 32; ++n) hf[n] = (float)h[c * 32 + n];
+                            b = oracle_quantise_group_mx(hf, 32, q);
+                            for (n = 0; n < 32; ++n) hd[c * 32 + n] = oracle_e4m3_decode(q[n]) * oracle_e8m0_decode(b);
+                        }
                     } else {
                         for (n = 0; n < I; ++n) hd[n] = h[n];
                     }
@@ -429,13 +493,14 @@ int oracle_forward_ep(const uint16_t *x, int T, int H, int I, int E, int k,
         }
         free(a); free(acc); free(hd); free(y); free(h);
     }
-    free(q_x); free(s_x_blk); free(h_all); free(hq_all);
+    free(q_x); free(s_x_blk); free(mx_x); free(h_all); free(hq_all);
     return bad ? -1 : 0;
 }
 
 /* The quantised activations exactly as the method defines them, exposed so
  * the tests can compare codes: per-tensor writes one scale, block128 writes
- * [T, H/128] scales. */
+ * [T, H/128] scales, MX writes [T, H/32] E8M0 bytes (into `scales` viewed as
+ * bytes). */
 int oracle_quantise_activations(const uint16_t *x, int T, int H, int quant,
                                 uint8_t *q, float *scales) {
     long i;
@@ -445,6 +510,17 @@ int oracle_quantise_activations(const uint16_t *x, int T, int H, int quant,
         for (i = 0; i < (long)T * H; ++i) xf[i] = oracle_bf16_decode(x[i]);
         scales[0] = oracle_quantise_group(xf, (long)T * H, q);
         free(xf);
+        return 0;
+    }
+    if (quant == ORC_FP8_MX32) {
+        int t, c, j, nb = H / 32;
+        if (H % 32) return -1;
+        for (t = 0; t < T; ++t)
+            for (c = 0; c < nb; ++c) {
+                float v[32];
+                for (j = 0; j < 32; ++j) v[j] = oracle_bf16_decode(x[(long)t * H + c * 32 + j]);
+                ((uint8_t *)scales)[(long)t * nb + c] = oracle_quantise_group_mx(v, 32, q + (long)t * H + c * 32);
+            }
         return 0;
     }
     if (quant == ORC_FP8_BLOCK128) {

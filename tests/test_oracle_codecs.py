@@ -124,3 +124,35 @@ def test_activation_quantisation_matches_definition(quant):
         assert np.array_equal(scales, s)
         ref = torch.from_numpy((blk / s[:, :, None]).astype(np.float32)).to(torch.float8_e4m3fn)
         assert np.array_equal(codes, ref.view(torch.uint8).numpy().reshape(5, 256))
+
+
+# ---------------------------------------------------------------------- MX --
+def test_mx_scale_rule_landmarks():
+    """E8M0 byte = floor(log2 amax) - 8 + 127 (8 = e4m3's largest exponent): amax 448 and 256
+    keep scale 1, just under 256 halves it, 1.0 gives 2^-8; an all-zero group takes byte 0 and
+    tiny magnitudes clamp at byte 0."""
+    assert oracle.mx_scale_byte(448.0) == 127
+    assert oracle.mx_scale_byte(256.0) == 127
+    assert oracle.mx_scale_byte(511.9) == 127
+    assert oracle.mx_scale_byte(255.9) == 126
+    assert oracle.mx_scale_byte(1.0) == 119
+    assert oracle.mx_scale_byte(0.75) == 118
+    assert oracle.mx_scale_byte(0.0) == 0
+    assert oracle.mx_scale_byte(2.0 ** -130) == 0
+    assert oracle.mx_scale_byte(3.0e38) == 246   # floor(log2) = 127: fp32 never reaches the upper clamp
+
+
+def test_mx_group_codes_and_range():
+    """Every nonzero group's largest |v| / scale lies in [256, 512) (so its code is >= 256 or
+    saturates at 448); the codes are torch's e4m3 cast of v / scale, saturated."""
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        v = (rng.standard_normal(32) * 10.0 ** rng.uniform(-6, 6)).astype(np.float32)
+        q, b = oracle.quantise_group_mx(v)
+        scale = 2.0 ** (b - 127)
+        r = np.max(np.abs(v)) / scale
+        assert 256.0 <= r < 512.0, (trial, r)
+        ref = torch.clamp(torch.from_numpy(v.astype(np.float64) / scale).float(), -448.0, 448.0)
+        assert np.array_equal(q, ref.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    q, b = oracle.quantise_group_mx(np.zeros(32, np.float32))
+    assert b == 0 and not q.any()

@@ -162,6 +162,41 @@ def test_fp8_block128_dense_reformulation():
     assert np.max(np.abs(out - ref)) <= 1e-12
 
 
+def test_fp8_mx32_dense_reformulation():
+    """MX FP8: weights as codes times 2^(b-127) per 32 rows of K and column; x per token and h per
+    route row quantised per 32 channels with the E8M0 rule (torch's frexp and e4m3 cast); the
+    whole layer densely in torch."""
+    T, H, I, E, k = 6, 128, 96, 4, 2
+    a = random_activations(T, H, E, 52)
+    w = random_weights(E, H, I, "fp8_mx32", 53)
+    r = oracle.route(a["logits"], k)
+    out = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"],
+                         quant="fp8_mx32", s_gate_up=w["s_gate_up"], s_down=w["s_down"])
+
+    def mx(v):   # [..., 32] fp32 -> dequantised fp64
+        amax = v.abs().amax(dim=-1)
+        _, ex = torch.frexp(amax)
+        b = torch.where(amax > 0, (ex - 9 + 127).clamp(0, 254), torch.zeros_like(ex)).double()
+        sc = torch.pow(2.0, b - 127)
+        return torch_e4m3((v.double() / sc[..., None]).float()) * sc[..., None]
+
+    x = torch.from_numpy(bf16_bits_to_f32(a["x"])).reshape(T, H // 32, 32)
+    xa = mx(x).reshape(T, H)
+
+    def deq(q, s):
+        Ee, K, N = q.shape
+        v = torch.from_numpy(q).view(torch.float8_e4m3fn).double().reshape(Ee, K // 32, 32, N)
+        return (v * torch.pow(2.0, torch.from_numpy(s).double() - 127)[:, :, None, :]).reshape(Ee, K, N)
+
+    wgu, wdn = deq(w["w_gate_up"], w["s_gate_up"]), deq(w["w_down"], w["s_down"])
+    gu = torch.einsum("th,ehn->ten", xa, wgu)
+    h = (F.silu(gu[..., :I]) * gu[..., I:]).float().reshape(T, E, I // 32, 32)
+    hq = mx(h).reshape(T, E, I)
+    Y = torch.einsum("tei,eih->teh", hq, wdn)
+    ref = combine_dense(Y, r["topk_ids"], r["topk_weights"]).numpy()
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
 def test_quantisation_matters():
     """The FP8 oracle is not the bf16 oracle on dequantised weights: dropping the
     activation quantisation moves the result by far more than the FP8 parity

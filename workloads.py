@@ -15,7 +15,8 @@ Recipe (all draws are ``numpy.random.default_rng(seed)`` standard normals):
     default_rng([seed, i, e]) (i = 0 for w_gate_up, 1 for w_down): w_gate_up [E, H, 2I] (gate in columns [0,I),
     up in [I,2I)) and w_down [E, I, H], stored bf16, or quantised offline to
     e4m3 with fp32 scales amax/448 per expert tensor (per-tensor) or per
-    128x128 block of the stored [K, N] matrix (block128).
+    128x128 block of the stored [K, N] matrix (block128), or with E8M0
+    power-of-two scales per 32 rows of K and output column (MX, fp8_mx32).
 
 Workloads (the shapes of the layers the pages measure):
   tiny_bf16          T=64,   H=256,  I=512, E=16,  k=8  (world-model MoE, E=16 k=8)
@@ -98,6 +99,21 @@ def quantise_weight_block128(w: np.ndarray):
     return q.reshape(E, K, N), s.numpy()
 
 
+def quantise_weight_mx32(w: np.ndarray):
+    """w [E, K, N] fp32 -> (e4m3 codes, E8M0 scale bytes [E, K/32, N]): per 32
+    rows of K and output column, scale 2^(floor(log2 amax) - 8) (byte 0 for an
+    all-zero group), codes e4m3(w / scale) saturated at 448 (offline weight
+    preparation, the MX format's rule)."""
+    E, K, N = w.shape
+    blk = torch.from_numpy(w).view(E, K // 32, 32, N)
+    amax = blk.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)
+    b = torch.where(amax > 0, (ex - 1 - 8 + 127).clamp(0, 254), torch.zeros_like(ex)).to(torch.int32)
+    scale = torch.pow(torch.tensor(2.0, dtype=torch.float64), (b - 127).double()).float()
+    q = _e4m3_cast(blk / scale[:, :, None, :])
+    return q.reshape(E, K, N), b.to(torch.uint8).numpy()
+
+
 def _normal_per_expert(shape, seed, tensor_id, std):
     """[E, ...] fp32 draws; expert e uses default_rng([seed, tensor_id, e]) so the
     experts can be drawn on several threads with a fixed result."""
@@ -126,6 +142,9 @@ def random_weights(E, H, I, quant, seed):
     elif quant == "fp8_block128":
         qgu, sgu = quantise_weight_block128(wgu)
         qd, sd = quantise_weight_block128(wd)
+    elif quant == "fp8_mx32":
+        qgu, sgu = quantise_weight_mx32(wgu)
+        qd, sd = quantise_weight_mx32(wd)
     else:
         raise ValueError(quant)
     return dict(w_gate_up=qgu, w_down=qd, s_gate_up=sgu, s_down=sd)
