@@ -54,6 +54,8 @@ def dev_weights(torch, moe, w, quant):
         gu = torch.from_numpy(w["w_gate_up"]).cuda()
         dn = torch.from_numpy(w["w_down"]).cuda()
         scales = (torch.from_numpy(w["s_gate_up"]).cuda(), torch.from_numpy(w["s_down"]).cuda())
+        if quant == "fp8_mx32":
+            scales = moe.pack_mx_scales(*scales)
     pgu, pd = moe.pack_weights(gu, dn, quant)
     torch.cuda.synchronize()
     del gu, dn
@@ -539,7 +541,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline line only (no fp8 extras)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="profiling runs: comma list of prefill_bf16, prefill_fp8_block, decode_bf16, "
+                    help="profiling runs: comma list of prefill_bf16, prefill_fp8_block, prefill_fp8_mx, decode_bf16, "
                          "decode_fp8_tensor, router, pages_shapes, copy (a plain 1 GiB device copy, the traffic-counter "
                          "reference); prints per-stage times instead of the JSON line")
     args = ap.parse_args()
@@ -623,6 +625,18 @@ def main():
             layer=layer_fractions(w5, p5["dt"] / args.steps, PEAK_FP8_TFLOPS),
             stages_us={k: round(v * 1e3, 2) for k, v in p5["stages_ms"].items()})
         del p5
+        torch.cuda.empty_cache()
+        log("prefill MX fp8 T=4096 ...")
+        p6 = bench_prefill(torch, moe, "prefill_fp8_mx", args.steps, args.warmup)
+        w6 = p6["wl"]
+        line["prefill_fp8_mx32"] = dict(
+            workload="prefill_fp8_mx T=4096 H=4096 I=512 E=128 top-8, MX e4m3 (E8M0 per 32 along K)",
+            tokens_per_s=round(w6.T * args.steps / p6["dt"], 1),
+            ms_per_step=round(p6["dt"] / args.steps * 1e3, 4),
+            roofline=roofline_gemm(w6, p6["gate_up_ms"], PEAK_FP8_TFLOPS),
+            layer=layer_fractions(w6, p6["dt"] / args.steps, PEAK_FP8_TFLOPS),
+            stages_us={k: round(v * 1e3, 2) for k, v in p6["stages_ms"].items()})
+        del p6
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -55,8 +55,12 @@ typedef enum {
     MOE_BF16 = 0,               /* bf16 x and weights, fp32 accumulation */
     MOE_FP8_PER_TENSOR = 1,     /* e4m3 weights with one fp32 scale per expert tensor;
                                    x and h quantised on device with one scale each */
-    MOE_FP8_BLOCK128 = 2        /* e4m3 weights with fp32 scales per 128x128 block;
+    MOE_FP8_BLOCK128 = 2,       /* e4m3 weights with fp32 scales per 128x128 block;
                                    x and h quantised per row per 128 channels */
+    MOE_FP8_MX32 = 3            /* MX: e4m3 weights with one E8M0 (power-of-two) scale
+                                   per 32 rows of K per output column; x and h
+                                   quantised per row per 32 channels; grouped path
+                                   only, H and I multiples of 256 */
 } moe_quant;
 
 typedef enum {
@@ -85,10 +89,12 @@ typedef struct {
     int32_t T, E, k;
 } moe_routes;
 
-/* FP8 weight scales (device fp32 arrays; NULL members for MOE_BF16), in the
- * layout of the UNPACKED weights:
- *   per-tensor: w_gate_up_scale [E], w_down_scale [E]
- *   block128:   w_gate_up_scale [E][H/128][2I/128], w_down_scale [E][I/128][H/128] */
+/* FP8 weight scales (device arrays; NULL members for MOE_BF16):
+ *   per-tensor: fp32 w_gate_up_scale [E], w_down_scale [E]
+ *   block128:   fp32 w_gate_up_scale [E][H/128][2I/128], w_down_scale [E][I/128][H/128]
+ *               (the layout of the unpacked weights)
+ *   MX:         E8M0 bytes re-laid by moe_pack_mx_scales (the members point to
+ *               those bytes; the float type is only the struct's) */
 typedef struct {
     const float *w_gate_up_scale;
     const float *w_down_scale;
@@ -137,6 +143,16 @@ int moe_route_project(const void *x, const float *w_router, int T, int H, int E,
 int moe_pack_weights(const void *w_gate_up, const void *w_down, int E, int H, int I,
                      int quant, void *packed_gate_up, void *packed_down, void *stream);
 
+/* MX scale re-layout, once per weight set ("[mxfp8 moe training] add per group
+ * blocked scale kernels", Summary: scales re-laid for the block-scaled matrix
+ * instruction on device).
+ *   s_gate_up [E][H/32][2I] and s_down [E][I/32][H]: E8M0 bytes, one per 32
+ *   rows of K and output column (2^(b-127)), the layout of the unpacked weights
+ * -> packed_s_gate_up, packed_s_down, each the same size as its source, the
+ * order in which the MX GEMM feeds its scaled MFMAs.  H and I multiples of 256. */
+int moe_pack_mx_scales(const uint8_t *s_gate_up, const uint8_t *s_down, int E, int H, int I,
+                       uint8_t *packed_s_gate_up, uint8_t *packed_s_down, void *stream);
+
 /* The path MOE_PATH_AUTO takes for this shape, or a negative moe_status if
  * the requested path cannot run it.  Host-only; no GPU call.
  * ("perf: add small-batch route MMA for MoE", Dispatch.)  AUTO takes the
@@ -154,8 +170,9 @@ size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int quant, 
  * x: bf16 [T,H]; out: bf16 [T,H], fully overwritten; routes: from moe_route
  * (same T, E, k); weights: packed by moe_pack_weights.
  * FP8: x is quantised on device (per-tensor: one scale amax/448 for all of x;
- * block128: per token per 128 channels); the SwiGLU output h is requantised
- * the same way before Down (per-tensor: one scale for all T*k rows).
+ * block128: per token per 128 channels; MX: per token per 32 channels, E8M0
+ * scale 2^(floor(log2 amax) - 8)); the SwiGLU output h is requantised the
+ * same way before Down (per-tensor: one scale for all T*k rows).
  * The combine sums the k routes of a token in a fixed order in fp32 and
  * rounds to bf16 once: repeated calls give identical bits.
  * Shapes: H % 128 == 0, I % 64 == 0 (block128: I % 128 == 0); the

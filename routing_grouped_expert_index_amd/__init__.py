@@ -19,14 +19,14 @@ import torch
 _DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_DIR, "libmoe_mi355x.so")
 
-QUANT = {"bf16": 0, "fp8_per_tensor": 1, "fp8_block128": 2}
+QUANT = {"bf16": 0, "fp8_per_tensor": 1, "fp8_block128": 2, "fp8_mx32": 3}
 PATH = {"auto": 0, "grouped": 1, "route_direct": 2}
 PATH_NAME = {v: k for k, v in PATH.items()}
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
 EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_route_project_workspace_size",
-            "moe_route_project", "moe_pack_weights", "moe_select_path",
+            "moe_route_project", "moe_pack_weights", "moe_pack_mx_scales", "moe_select_path",
             "moe_forward_workspace_size", "moe_forward", "moe_forward_ex", "moe_forward_profiled",
             "moe_last_error"]
 
@@ -75,6 +75,8 @@ def lib():
     L.moe_route_project_workspace_size.argtypes = [i32, i32, i32, i32]
     L.moe_route_project.restype = i32
     L.moe_route_project.argtypes = [P, P, i32, i32, i32, i32, P, ctypes.POINTER(_CRoutes), P, sz, P]
+    L.moe_pack_mx_scales.restype = i32
+    L.moe_pack_mx_scales.argtypes = [P, P, i32, i32, i32, P, P, P]
     L.moe_pack_weights.argtypes = [P, P, i32, i32, i32, i32, P, P, P]
     L.moe_select_path.restype = i32
     L.moe_select_path.argtypes = [i32] * 7
@@ -203,6 +205,24 @@ def pack_weights(w_gate_up: torch.Tensor, w_down: torch.Tensor, quant: str = "bf
     pd = torch.empty_like(w_down)
     _check(lib().moe_pack_weights(_ptr(w_gate_up), _ptr(w_down), E, H, I, QUANT[quant], _ptr(pgu),
                                   _ptr(pd), _stream(w_gate_up.device, stream)))
+    return pgu, pd
+
+
+def pack_mx_scales(s_gate_up: torch.Tensor, s_down: torch.Tensor, stream=None):
+    """Re-lay MX E8M0 scale bytes [E,H/32,2I] and [E,I/32,H] into the order the MX
+    GEMM reads them (moe_pack_mx_scales); pass the result as `scales`."""
+    _need_cuda(s_gate_up, "s_gate_up")
+    _need_cuda(s_down, "s_down")
+    if s_gate_up.dtype != torch.uint8 or s_down.dtype != torch.uint8:
+        raise ValueError("MX scales are uint8 E8M0 bytes")
+    E, H32, I2 = s_gate_up.shape
+    H, I = H32 * 32, I2 // 2
+    if tuple(s_down.shape) != (E, I // 32, H):
+        raise ValueError("s_down must be [E, I/32, H]")
+    pgu = torch.empty_like(s_gate_up)
+    pd = torch.empty_like(s_down)
+    _check(lib().moe_pack_mx_scales(_ptr(s_gate_up), _ptr(s_down), E, H, I, _ptr(pgu), _ptr(pd),
+                                    _stream(s_gate_up.device, stream)))
     return pgu, pd
 
 

@@ -117,6 +117,39 @@ quant_block128_kernel(const TIn* __restrict__ in, int rows, int cols, uint8_t* _
     if (sub == 0) scales[row * groups_per_row + c] = s;
 }
 
+// MX: per row, per 32 columns, E8M0 byte b = 2^(floor(log2 amax) - 8) (the
+// float exponent field of amax less 8, at least 0) and codes e4m3(v * 2^(127-b))
+// (exact power-of-two scaling).  4 threads per group.  The bytes of a row go in
+// the order the MX GEMM reads them: group c at 8(c/8) + 4(c%2) + (c%8)/2, so
+// dword 2g + hh holds groups 8g + hh, 8g + 2 + hh, 8g + 4 + hh, 8g + 6 + hh.
+template <typename TIn>
+__global__ void __launch_bounds__(256)
+quant_mx32_kernel(const TIn* __restrict__ in, int rows, int cols, uint8_t* __restrict__ q,
+                  uint8_t* __restrict__ scales) {
+    const int gpr = cols / 32;
+    const long g = (long)blockIdx.x * 64 + threadIdx.x / 4;
+    if (g >= (long)rows * gpr) return;
+    const int sub = threadIdx.x & 3;
+    const long row = g / gpr;
+    const int c = (int)(g % gpr);
+    const long base = row * cols + (long)c * 32 + sub * 8;
+    float v[8];
+    load8<TIn>(in + base, v);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    const int ef = (int)((__float_as_uint(a) >> 23) & 255);
+    const uint32_t b = (uint32_t)(ef > 8 ? ef - 8 : 0);
+    const float inv = __uint_as_float((254u - b) << 23);   // 2^(127 - b)
+    uint2 w;
+    w.x = f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    w.y = f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    *reinterpret_cast<uint2*>(q + base) = w;
+    if (sub == 0) scales[row * gpr + 8 * (c >> 3) + 4 * (c & 1) + ((c & 7) >> 1)] = (uint8_t)b;
+}
+
 // amax over n values (n % 8 == 0), folded into *amax_bits with atomicMax on
 // the bit pattern (non-negative floats order like their bits).
 // Element range [lo, hi) of a row-major tensor with `cols` columns: all n
@@ -206,6 +239,12 @@ quant_tensor_small_kernel(const TIn* __restrict__ in, long n, ElemRange er, uint
 constexpr long kSmallQuant = 1L << 16;
 
 hipError_t launch_quant_x(const FwdPlan& p, hipStream_t st) {
+    if (p.quant == Q_FP8_MX) {
+        const long groups = (long)p.T * (p.H / 32);
+        hipLaunchKernelGGL(quant_mx32_kernel<uint16_t>, dim3((unsigned)((groups + 63) / 64)), dim3(256), 0, st,
+                           p.x, p.T, p.H, p.xq, reinterpret_cast<uint8_t*>(p.sx));
+        return hipGetLastError();
+    }
     const long n = (long)p.T * p.H;
     if (p.quant == Q_FP8_BLOCK) {
         const long groups = (long)p.T * (p.H / 128);

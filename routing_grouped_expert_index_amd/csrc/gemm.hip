@@ -1,5 +1,6 @@
-// Grouped expert GEMMs of the MoE forward on gfx950: bf16, FP8 per-tensor and
-// FP8 with 128x128 block scales.
+// Grouped expert GEMMs of the MoE forward on gfx950: bf16, FP8 per-tensor, FP8
+// with 128x128 block scales, and MX FP8 (an E8M0 scale per 32 K values, applied
+// by the scaled MFMA).
 //
 // "perf: add small-batch route MMA for MoE", Motivation: after the routes are
 // grouped by expert, a Gate/Up grouped GEMM, the activation (SwiGLU) with
@@ -127,7 +128,7 @@ gemm32_kernel(const GemmArgs g) {
     constexpr int RPP = kEpiStageBytes / (CB * 16);           // staged rows per phase
     constexpr int MPP = RPP / 32;                             // m blocks per phase
     // store instructions per wave and tile (Q128: four rows of codes, four of scales)
-    constexpr int SX = EPI == EPI_SWIGLU_Q128 ? 8 : (4 / MPP) * (RPP * CB / 64);
+    constexpr int SX = EPI == EPI_SWIGLU_Q128 || EPI == EPI_SWIGLU_MX ? 8 : (4 / MPP) * (RPP * CB / 64);
     auto make_wp = [&](int e_, int wn0_) __attribute__((always_inline)) {
         return g.B + (long)e_ * g.N * g.Kb + (long)((wn0_ < g.N ? wn0_ : 0) / 32) * gstride + lane * 16;
     };
@@ -142,13 +143,26 @@ gemm32_kernel(const GemmArgs g) {
     // prologue: older than every request the K loop waits for, so in-order
     // completion lands them before the first step and no wait counts change.
     constexpr bool BLK = SC == SC_BLOCK;
+    // MX e4m3: one E8M0 scale per 32 K values of every token row and weight
+    // column, applied by the MFMA itself (v_mfma_scale: the scale of K block kb
+    // of row r comes from operand lane r + 32 kb, one byte of a dword picked by
+    // op_sel).  That instruction's K blocks are bytes 0-15 of lanes r and r+32
+    // (block 0) and bytes 16-31 of them (block 1), so for MX the lanes take the
+    // 16-byte chunks hh + 2q of a slice (weights packed that way, tokens read
+    // that way): lane half hh then holds MX block 2s + hh of slice s.  Token
+    // scales of a row are dwords of 4 bytes, dword 2g + hh holding blocks
+    // 8g + 2u + hh (u = slice 4g + u), staged per tile in LDS like the
+    // blockwise table; a wave's weight scales are one dword per lane and
+    // 32-row block per 4 slices, loaded three slices ahead with the weights.
+    constexpr bool MX = SC == SC_MX;
     const int KT = NSL / 2;
     float* sat = reinterpret_cast<float*>(smem + LDS_TOTAL);
     const __amdgpu_buffer_rsrc_t srsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g.sa), 0, BLK ? g.sa_bytes : 0, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g.sa), 0, BLK || MX ? g.sa_bytes : 0, 0x00020000);
     // this lane's row (16 wave + lane/4, source row src) and scale blocks 4t + lane%4
+    // (MX: scale dwords 4t + lane%4)
     auto table = [&](long src) __attribute__((always_inline)) {
-        if constexpr (BLK) {
+        if constexpr (BLK || MX) {
             for (int t = 0; t < (KT + 3) / 4; ++t) {
                 const int kb = min(4 * t + (lane & 3), KT - 1);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, MOE_LDS(sat + t * 4 * BM + wave * 64), 4,
@@ -171,11 +185,30 @@ gemm32_kernel(const GemmArgs g) {
         c1 = __builtin_amdgcn_readfirstlane(c1);
     };
 
+    // MX: the wave's two 32-row blocks' scale dwords of scale group grp (slices
+    // 4 grp .. 4 grp + 3; K is a multiple of 256), into wsn; wsc holds the
+    // current group's
+    const int NB32 = g.N / 32, NG = NSL / 4;
+    // (the block base is made visibly wave-uniform, so it lives in scalar
+    // registers and each load adds only the lane's offset)
+    auto make_wsp = [&](int e_, int wn0_) __attribute__((always_inline)) {
+        const int rb = __builtin_amdgcn_readfirstlane((wn0_ < g.N ? wn0_ : 0) / 32);
+        return g.swx + ((long)e_ * NB32 + rb) * (long)NG * 64;
+    };
+    uint32_t wsn[2] = {0u, 0u}, wsc[2] = {0u, 0u};
+    auto wsload = [&](const uint32_t* wsp_, int grp) __attribute__((always_inline)) {
+        if constexpr (MX) {
+#pragma unroll
+            for (int f = 0; f < 2; ++f) wsn[f] = wsp_[((long)f * NG + min(grp, NG - 1)) * 64 + lane];
+        }
+    };
+
     int e, row0, rows, wn0;
     decode(L, e, row0, rows, wn0);
     const long src0 = src_row(row0, rows);
     uint32_t ap = make_ap(src0);
     const uint8_t* wp = make_wp(e, wn0);
+    const uint32_t* wsp = MX ? make_wsp(e, wn0) : nullptr;
     table(src0);
 
     f32x16 acc[2][4];
@@ -193,18 +226,21 @@ gemm32_kernel(const GemmArgs g) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, MOE_LDS(smem + stage * STAGE_B + wave * 1024), 16,
                                                  ap_ + (uint32_t)(s * kSliceBytes), 0, 0, 0);
     };
-    // a tile's first requests: token DMA of slices 0..3, weights of slices 0..2
-    auto prologue = [&](uint32_t ap_, const uint8_t* wp_) __attribute__((always_inline)) {
+    // a tile's first requests: token DMA of slices 0..3, (MX: the weight scales
+    // of slices 0..3,) weights of slices 0..2
+    auto prologue = [&](uint32_t ap_, const uint8_t* wp_, const uint32_t* wsp_) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) dma(ap_, min(u, NSL - 1), u);
         __builtin_amdgcn_sched_barrier(0);
+        wsload(wsp_, 0);
         wload(wp_, 0, 0);
         wload(wp_, min(1, NSL - 1), 1);
         wload(wp_, min(2, NSL - 1), 2);
     };
-    // token operand of block m, K half q (16 bytes: chunk 2hh + q of row 32m + j)
+    // token operand of block m, K half q (16 bytes: chunk 2hh + q of row 32m + j;
+    // MX: chunk hh + 2q)
     auto tok = [&](const uint8_t* st, int m, int q) __attribute__((always_inline)) {
-        const int r = 32 * m + j, c = 2 * hh + q;
+        const int r = 32 * m + j, c = MX ? hh + 2 * q : 2 * hh + q;
         return *reinterpret_cast<const u32x4*>(st + r * kSliceBytes + ((c ^ ((r >> 2) & 3)) << 4));
     };
     // The LDS reads of the token operands run ahead of the MFMAs that consume
@@ -213,8 +249,10 @@ gemm32_kernel(const GemmArgs g) {
     // (blockwise e4m3, first slice of a K block: each accumulator block is
     // multiplied by fac[f][m] just before its MFMA, so the multiplies of the next
     // block run under the current MFMA)
-    auto mma = [&](auto Rc, int slot, int stage, const float (&fac)[2][4]) __attribute__((always_inline)) {
+    uint32_t tsc[4] = {0u, 0u, 0u, 0u};   // MX: the token rows' scale dwords of the current group
+    auto mma = [&](auto Rc, auto Uc, int stage, const float (&fac)[2][4]) __attribute__((always_inline)) {
         constexpr bool RS = decltype(Rc)::value;
+        constexpr int slot = decltype(Uc)::value;
         const uint8_t* st = smem + stage * STAGE_B;
         if constexpr (!FP8) {
             // operand kk = 4q + m: K half q of token block m; the two MFMAs of one
@@ -260,8 +298,12 @@ gemm32_kernel(const GemmArgs g) {
 #pragma unroll
                         for (int i = 0; i < 16; ++i) acc[f][m][i] *= a;
                     }
-                    acc[f][m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[f][m], 0, 0, 0, 0,
-                                                                                 0, 0);
+                    if constexpr (MX)   // op_sel: the byte of this slice
+                        acc[f][m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            av, bv, acc[f][m], 0, 0, slot, (int)wsc[f], slot, (int)tsc[m]);
+                    else
+                        acc[f][m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[f][m], 0, 0, 0, 0,
+                                                                                     0, 0);
                 }
             }
             if constexpr (!BLK) {
@@ -350,6 +392,9 @@ gemm32_kernel(const GemmArgs g) {
     auto step = [&](auto Uc, int s, bool last, auto Xs, auto Xw) __attribute__((always_inline)) {
         constexpr int U = decltype(Uc)::value;
         constexpr int XS = decltype(Xs)::value, XW = decltype(Xw)::value;
+        // MX: the next scale group's weight scales go out with slice s+3's
+        // weights (older than them, so the weight wait of slice s+3 covers them)
+        if constexpr (MX && U == 1) wsload(wsp, (s + 3) >> 2);
         wload(wp, min(s + 3, NSL - 1), (U + 3) & 3);
         __builtin_amdgcn_sched_barrier(0);
         wait_vm_lgkm<WAIT_STEP + XS>();
@@ -366,12 +411,25 @@ gemm32_kernel(const GemmArgs g) {
         std::integral_constant<bool, RS> Rc;
         float fac[2][4];
         if constexpr (RS) block_factors(min(s >> 1, KT - 1), fac);
+        if constexpr (MX && U == 0) {
+            // a new scale group: the token rows' dwords 2g + hh from the LDS
+            // table (landed before step 0), the weights' from the group's load
+            const uint32_t* st32 = reinterpret_cast<const uint32_t*>(sat);
+            const int d = 2 * min(s >> 2, NG - 1) + hh;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) tsc[m] = st32[(d >> 2) * 4 * BM + (32 * m + j) * 4 + (d & 3)];
+            __builtin_amdgcn_sched_barrier(0);
+        }
         wait_vm_only<WAIT_W + XW>();
-        if (!last) mma(Rc, U, s % STAGES, fac);
-        else if (s < NSL) mma(Rc, U, s % STAGES, fac);
+        if constexpr (MX && U == 0) {
+            wsc[0] = wsn[0];
+            wsc[1] = wsn[1];
+        }
+        if (!last) mma(Rc, Uc, s % STAGES, fac);
+        else if (s < NSL) mma(Rc, Uc, s % STAGES, fac);
     };
 
-    prologue(ap, wp);
+    prologue(ap, wp, wsp);
     // the first tile has no epilogue before it: SX dropped stores take its place
     // so that every tile's first steps see the same request counts
     __builtin_amdgcn_sched_barrier(0);
@@ -444,7 +502,8 @@ gemm32_kernel(const GemmArgs g) {
         // unconditional prologue keeps the loop's wait counts exact)
         const uint32_t nap = more ? make_ap(nsrc) : ap;
         const uint8_t* nwp = more ? make_wp(ne, nwn0) : wp;
-        prologue(nap, nwp);
+        const uint32_t* nwsp = MX && more ? make_wsp(ne, nwn0) : wsp;
+        prologue(nap, nwp, nwsp);
         __builtin_amdgcn_sched_barrier(0);
 
         // ------------------------------------------------------------ epilogue
@@ -459,7 +518,47 @@ gemm32_kernel(const GemmArgs g) {
         // 64/CB rows of CB contiguous chunks (128 or 64 bytes per row).
         //   SwiGLU Q128:    h columns wn0/2 + 16hh + [0,16), one 16-byte chunk of
         //                   e4m3 codes per row, stored straight out (see below)
-        if constexpr (EPI == EPI_SWIGLU_Q128) {
+        if constexpr (EPI == EPI_SWIGLU_MX) {
+            // h = silu(gate) * up (the MFMAs applied every scale).  A wave's 32 h
+            // columns are one MX group per token row, held by the lane pair hh =
+            // 0, 1: its E8M0 byte is 2^(floor(log2 amax) - 8) (the float exponent
+            // field of amax less 8, at least 0), the codes e4m3(h * 2^(127 - b))
+            // (exact power-of-two scaling); each lane stores its 16 codes as one
+            // chunk and lane hh = 0 the byte, at the group's place in the row's
+            // scale layout (byte 8(c/8) + 4(c%2) + (c%8)/2 for group c).
+            const bool live = wn0 < g.N;
+            const int hc0 = (live ? wn0 : 0) / 2 + 16 * hh;      // this lane's first h column
+            const int hg = (live ? wn0 : 0) / 64;                 // the wave's MX group
+            const int spos = 8 * (hg >> 3) + 4 * (hg & 1) + ((hg & 7) >> 1);
+            const __amdgpu_buffer_rsrc_t qsrc = __builtin_amdgcn_make_buffer_rsrc(g.cscale, 0, g.cs_bytes, 0x00020000);
+            const int nbh = g.I / 32;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    acc[0][m][i] = silu(acc[0][m][i]) * acc[1][m][i];
+                    a = fmaxf(a, fabsf(acc[0][m][i]));
+                }
+                a = fmaxf(a, __shfl_xor(a, 32));
+                const int ef = (int)((__float_as_uint(a) >> 23) & 255);
+                const uint32_t b = (uint32_t)(ef > 8 ? ef - 8 : 0);
+                const float inv = __uint_as_float((254u - b) << 23);   // 2^(127 - b), b <= 247
+                u32x4 q;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    q[t] = f32x4_to_e4m3x4(acc[0][m][4 * t] * inv, acc[0][m][4 * t + 1] * inv,
+                                           acc[0][m][4 * t + 2] * inv, acc[0][m][4 * t + 3] * inv);
+                const int r = 32 * m + j;
+                const bool ok = live && r < rows;
+                const uint32_t orow = (uint32_t)(row0 + r);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    q, crsrc, ok ? orow * (uint32_t)g.ldc + (uint32_t)hc0 : kDropped, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b8(
+                    (uint8_t)b, qsrc, ok && hh == 0 ? orow * (uint32_t)nbh + (uint32_t)spos : kDropped, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if constexpr (EPI == EPI_SWIGLU_Q128) {
             // h = silu(gate) * up in place of the gate accumulators.  A 128-column
             // h block is 256 packed rows: waves 4b..4b+3 of the tile.  Per token
             // row each wave takes the amax of its 32 columns, the four waves of a
@@ -599,6 +698,7 @@ gemm32_kernel(const GemmArgs g) {
         wn0 = nwn0;
         ap = nap;
         wp = nwp;
+        wsp = nwsp;
     }
 }
 
@@ -632,6 +732,17 @@ static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st) {
             return hipErrorInvalidValue;
         lds += (size_t)((KT + 3) / 4) * 4 * g32::BM * sizeof(float);
     }
+    if constexpr (SC == SC_MX) {
+        // K in whole 256-deep scale groups (a dword of 4 E8M0 bytes per lane and
+        // 4 slices); the tile's token scale dwords, K/128 per row, sit in LDS
+        // behind the epilogue staging like the blockwise table
+        const int KT = a.Kb / 128;
+        if (a.Kb % 256 != 0 || KT < 2 || KT > 64 || !a.swx || a.sa_bytes <= 0 || a.sa_bytes > 0x7fffffffL)
+            return hipErrorInvalidValue;
+        if (EPI == EPI_SWIGLU_MX && (a.I % 64 != 0 || a.cs_bytes <= 0 || a.cs_bytes > 0x7fffffffL))
+            return hipErrorInvalidValue;
+        lds += (size_t)((KT + 3) / 4) * 4 * g32::BM * sizeof(uint32_t);
+    }
     // 32-bit buffer offsets; C also keeps 0x80000000 free as the dropped-store offset
     if (a.a_bytes <= 0 || a.a_bytes > 0x7fffffffL || a.c_bytes <= 0 || a.c_bytes > 0x7fffffffL)
         return hipErrorInvalidValue;
@@ -660,8 +771,8 @@ static GemmArgs gate_up_args(const FwdPlan& p, int elem) {
     a.tiles = p.tiles;
     a.ntiles = p.ntiles;
     a.offsets = p.offsets + p.e0;   // the expert slice (the tile map indexes it)
-    a.sa = p.quant == Q_FP8_BLOCK ? p.sx : &p.scal[0];
-    a.sa_ld = p.H / 128;
+    a.sa = p.quant == Q_FP8_BLOCK || p.quant == Q_FP8_MX ? p.sx : &p.scal[0];
+    a.sa_ld = p.H / 128;   // floats per row (block), or dwords of 4 E8M0 bytes (MX)
     a.sw = p.s_gu;
     a.nb_orig = 2 * p.I / 128;
     a.I = p.I;
@@ -690,6 +801,12 @@ hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st) {
     a.ldc = p.I;
     a.c_bytes = (long)p.T * p.k * p.I;
     a.cscale = p.sh;
+    if (p.quant == Q_FP8_MX) {   // E8M0 bytes: x [T][H/32] in, h [R][I/32] out
+        a.swx = reinterpret_cast<const uint32_t*>(p.s_gu);
+        a.cs_bytes = (long)p.T * p.k * (p.I / 32);
+        a.sa_bytes = (long)p.T * (p.H / 32);
+        return run_gemm32<true, true, SC_MX, EPI_SWIGLU_MX>(a, st);
+    }
     a.cs_bytes = (long)p.T * p.k * (p.I / 128) * 4;
     a.sa_bytes = (long)p.T * (p.H / 128) * 4;
     return run_gemm32<true, true, SC_BLOCK, EPI_SWIGLU_Q128>(a, st);
@@ -709,7 +826,7 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     a.tiles = p.tiles;
     a.ntiles = p.ntiles;
     a.offsets = p.offsets + p.e0;   // the expert slice (the tile map indexes it)
-    a.sa = p.quant == Q_FP8_BLOCK ? p.sh : &p.scal[1];
+    a.sa = p.quant == Q_FP8_BLOCK || p.quant == Q_FP8_MX ? p.sh : &p.scal[1];
     a.sa_ld = p.I / 128;
     a.sw = p.s_d;
     a.nb_orig = p.H / 128;
@@ -721,6 +838,11 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     a.a_bytes = (long)p.T * p.k * a.lda;
     if (p.quant == Q_BF16) return run_gemm32<false, false, SC_NONE, EPI_Y_BF16>(a, st);
     if (p.quant == Q_FP8_TENSOR) return run_gemm32<true, false, SC_TENSOR, EPI_Y_BF16>(a, st);
+    if (p.quant == Q_FP8_MX) {
+        a.swx = reinterpret_cast<const uint32_t*>(p.s_d);
+        a.sa_bytes = (long)p.T * p.k * (p.I / 32);
+        return run_gemm32<true, false, SC_MX, EPI_Y_BF16>(a, st);
+    }
     a.sa_bytes = (long)p.T * p.k * (p.I / 128) * 4;
     return run_gemm32<true, false, SC_BLOCK, EPI_Y_BF16>(a, st);
 }

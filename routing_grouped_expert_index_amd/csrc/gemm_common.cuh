@@ -1,13 +1,13 @@
-// Pieces of the grouped-GEMM kernel (gemm.hip: bf16, FP8 per-tensor and FP8
-// 128x128-blockwise).
+// Pieces of the grouped-GEMM kernel (gemm.hip: bf16, FP8 per-tensor, FP8
+// 128x128-blockwise and MX FP8).
 #pragma once
 #include "common.cuh"
 #include "launch.h"
 
 namespace moe {
 
-enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_F32 = 1, EPI_SWIGLU_Q128 = 2, EPI_Y_BF16 = 3 };
-enum Scale { SC_NONE = 0, SC_TENSOR = 1, SC_BLOCK = 2 };
+enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_F32 = 1, EPI_SWIGLU_Q128 = 2, EPI_Y_BF16 = 3, EPI_SWIGLU_MX = 4 };
+enum Scale { SC_NONE = 0, SC_TENSOR = 1, SC_BLOCK = 2, SC_MX = 3 };
 
 struct GemmArgs {
     const uint8_t* A;       // row-major activations, lda bytes per row
@@ -20,14 +20,15 @@ struct GemmArgs {
     const int32_t* tiles;   // [max_tiles][2] (expert, first sorted row)
     const int32_t* ntiles;
     const int32_t* offsets; // [E+1]
-    const float* sa;        // tensor: &scalar; block: [rows][sa_ld]
+    const float* sa;        // tensor: &scalar; block: [rows][sa_ld]; MX: E8M0 bytes [rows][4 sa_ld]
     int sa_ld;
     const float* sw;        // tensor: [E]; block: [E][K/128][nb_orig]
+    const uint32_t* swx;    // MX: packed weight scales [E][N/32][K/128][64 lanes] (4 E8M0 bytes each)
     int nb_orig;
     int I;                  // Gate/Up: h width
     void* C;                // output
     long ldc;               // output row stride in elements
-    float* cscale;          // Q128: [R][I/128]
+    float* cscale;          // Q128: [R][I/128]; MX: E8M0 bytes [R][I/32]
     int max_tiles;
     int order;              // tile order: 0 column tile major, 1 row tile major
     long a_bytes;           // bytes of A addressable by the token loads

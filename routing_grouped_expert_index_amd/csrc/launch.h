@@ -41,9 +41,14 @@ hipError_t launch_pack_gate_up(const void* src, void* dst, int E, int H, int I, 
                                hipStream_t st);
 hipError_t launch_pack_down(const void* src, void* dst, int E, int H, int I, int elem_bytes,
                             hipStream_t st);
+// MX: e4m3 codes in the chunk order of the scaled MFMA, and the E8M0 scales
+// [E][K/32][N] re-laid as [E][N/32][K/256][64 lanes] dwords
+hipError_t launch_pack_mx(const void* src, void* dst, int E, int K, int N, int I, bool gate_up, hipStream_t st);
+hipError_t launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, int E, int K, int N, int I, bool gate_up,
+                                 hipStream_t st);
 
 // ---- forward pieces
-enum Quant { Q_BF16 = 0, Q_FP8_TENSOR = 1, Q_FP8_BLOCK = 2 };
+enum Quant { Q_BF16 = 0, Q_FP8_TENSOR = 1, Q_FP8_BLOCK = 2, Q_FP8_MX = 3 };
 
 struct FwdPlan {
     // problem
@@ -58,8 +63,8 @@ struct FwdPlan {
     const int32_t* route_pos;   // [R] inverse of perm
     const void* wgu;            // packed [E][2I][H]
     const void* wd;             // packed [E][H][I]
-    const float* s_gu;          // per-tensor [E] | block [E][H/128][2I/128]
-    const float* s_d;           // per-tensor [E] | block [E][I/128][H/128]
+    const float* s_gu;          // per-tensor [E] | block [E][H/128][2I/128] | MX: packed E8M0 dwords
+    const float* s_d;           // per-tensor [E] | block [E][I/128][H/128] | MX: packed E8M0 dwords
     uint16_t* out;              // bf16 [T, H]
     // workspace carve-up (null where unused)
     int32_t* tiles;             // [max_tiles] (expert << 16 | tile-in-expert) pairs as int2
@@ -67,10 +72,10 @@ struct FwdPlan {
     uint32_t* amax;             // [2]: x amax bits, h amax bits (per-tensor)
     float* scal;                // [2]: s_x, s_h (per-tensor)
     uint8_t* xq;                // e4m3 [T, H]
-    float* sx;                  // block: [T, H/128]
+    float* sx;                  // block: [T, H/128] | MX: E8M0 bytes [T, H/32] (in scale-dword order)
     void* h;                    // bf16 [R, I] (bf16) | fp32 [R, I] (fp8 paths, before requant)
     uint8_t* hq;                // e4m3 [R, I]
-    float* sh;                  // block: [R, I/128]
+    float* sh;                  // block: [R, I/128] | MX: E8M0 bytes [R, I/32] (in scale-dword order)
     uint16_t* y;                // bf16 [R, H] (grouped path, sorted order)
     float* rd_hmax;             // route-direct per-tensor: max |h| of each Gate/Up workgroup [R * I/32 * split]
     float* rd_part;             // route-direct Down partial sums [T * H/32][items][32]

@@ -47,6 +47,7 @@ constexpr int kRouteDirectMaxTokens = 16;
 bool rd_shape_ok(int H, int I, int k, int quant) {
     const int elem = quant == MOE_BF16 ? 2 : 1;
     (void)k;
+    if (quant == MOE_FP8_MX32) return false;   // MX runs on the grouped path only
     return (long)H * elem <= 8192 && (long)I * elem <= 2048;
 }
 
@@ -54,7 +55,7 @@ int check_shape(int T, int H, int I, int E, int k, int quant) {
     if (T < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "T=%d H=%d I=%d: sizes must be positive (T >= 0)", T, H, I);
     if (k < 1 || E < k || E > moe::kMaxExperts)
         return fail(MOE_ERR_INVALID_ARG, "need 1 <= k <= E <= %d (k=%d, E=%d)", moe::kMaxExperts, k, E);
-    if (quant < MOE_BF16 || quant > MOE_FP8_BLOCK128) return fail(MOE_ERR_INVALID_ARG, "unknown quant %d", quant);
+    if (quant < MOE_BF16 || quant > MOE_FP8_MX32) return fail(MOE_ERR_INVALID_ARG, "unknown quant %d", quant);
     if ((long)T * k >= (1L << 31) || (long)T * H >= (1L << 31))
         return fail(MOE_ERR_UNSUPPORTED, "T*k and T*H must fit in int32");
     if (H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "H=%d: H must be a multiple of 128", H);
@@ -63,6 +64,8 @@ int check_shape(int T, int H, int I, int E, int k, int quant) {
         return fail(MOE_ERR_UNSUPPORTED, "I=%d: block128 needs I a multiple of 128", I);
     if (quant == MOE_FP8_BLOCK128 && (H > 8192 || I > 8192))
         return fail(MOE_ERR_UNSUPPORTED, "block128: H and I up to 8192 (64 scale blocks along K)");
+    if (quant == MOE_FP8_MX32 && (H % 256 != 0 || I % 256 != 0 || H > 8192 || I > 8192))
+        return fail(MOE_ERR_UNSUPPORTED, "MX: H and I multiples of 256, up to 8192 (H=%d, I=%d)", H, I);
     if ((long)E * H * 2 * I >= (1L << 40)) return fail(MOE_ERR_UNSUPPORTED, "weights too large");
     return MOE_OK;
 }
@@ -76,7 +79,7 @@ int resolve_path(int T, int H, int I, int E, int k, int quant, int path) {
     if (path == MOE_PATH_ROUTE_DIRECT) {
         if (!rd_shape_ok(H, I, k, quant))
             return fail(MOE_ERR_UNSUPPORTED,
-                        "route-direct path: H*elem <= 8192 and I*elem <= 2048 bytes");
+                        "route-direct path: H*elem <= 8192 and I*elem <= 2048 bytes, not MX");
         return path;
     }
     return fail(MOE_ERR_INVALID_ARG, "unknown path %d", path);
@@ -101,13 +104,15 @@ Layout layout(int T, int H, int I, int E, int k, int quant, int path) {
     L.amax = take(2 * sizeof(uint32_t));
     L.scal = take(2 * sizeof(float));
     L.xq = take(grouped && quant != MOE_BF16 ? (size_t)T * H : 0);
-    L.sx = take(grouped && quant == MOE_FP8_BLOCK128 ? sizeof(float) * (size_t)T * (H / 128) : 0);
+    L.sx = take(grouped && quant == MOE_FP8_BLOCK128 ? sizeof(float) * (size_t)T * (H / 128)
+                : grouped && quant == MOE_FP8_MX32 ? (size_t)T * (H / 32) : 0);
     size_t hbytes = 0;
     if (quant == MOE_BF16) hbytes = R * I * 2;
     else if (quant == MOE_FP8_PER_TENSOR || !grouped) hbytes = R * I * 4;
     L.h = take(hbytes);
     L.hq = take(grouped && quant != MOE_BF16 ? R * I : 0);
-    L.sh = take(grouped && quant == MOE_FP8_BLOCK128 ? sizeof(float) * R * (I / 128) : 0);
+    L.sh = take(grouped && quant == MOE_FP8_BLOCK128 ? sizeof(float) * R * (I / 128)
+                : grouped && quant == MOE_FP8_MX32 ? R * (I / 32) : 0);
     L.y = take(grouped ? R * H * 2 : 0);
     const size_t rd_blocks = grouped ? 0 : (size_t)T * (H / 32);
     L.rd_hmax = take(!grouped && quant == MOE_FP8_PER_TENSOR
@@ -212,17 +217,46 @@ int moe_pack_weights(const void* w_gate_up, const void* w_down, int E, int H, in
                      void* packed_gate_up, void* packed_down, void* stream) {
     if (E < 1 || E > moe::kMaxExperts || H <= 0 || I <= 0)
         return fail(MOE_ERR_INVALID_ARG, "bad sizes E=%d H=%d I=%d", E, H, I);
-    if (quant < MOE_BF16 || quant > MOE_FP8_BLOCK128) return fail(MOE_ERR_INVALID_ARG, "unknown quant %d", quant);
+    if (quant < MOE_BF16 || quant > MOE_FP8_MX32) return fail(MOE_ERR_INVALID_ARG, "unknown quant %d", quant);
     if (I % 16 != 0) return fail(MOE_ERR_UNSUPPORTED, "I must be a multiple of 16");
+    if (quant == MOE_FP8_MX32 && (H % 256 != 0 || I % 256 != 0))
+        return fail(MOE_ERR_UNSUPPORTED, "MX: H and I multiples of 256 (H=%d, I=%d)", H, I);
     if (!w_gate_up || !w_down || !packed_gate_up || !packed_down)
         return fail(MOE_ERR_INVALID_ARG, "null weight pointer");
     if (w_gate_up == packed_gate_up || w_down == packed_down)
         return fail(MOE_ERR_INVALID_ARG, "packing cannot run in place");
     const int elem = quant == MOE_BF16 ? 2 : 1;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    int rc = hip_status(moe::launch_pack_gate_up(w_gate_up, packed_gate_up, E, H, I, elem, st), "pack gate_up");
+    int rc;
+    if (quant == MOE_FP8_MX32) {
+        rc = hip_status(moe::launch_pack_mx(w_gate_up, packed_gate_up, E, H, 2 * I, I, true, st), "pack gate_up");
+        if (rc != MOE_OK) return rc;
+        rc = hip_status(moe::launch_pack_mx(w_down, packed_down, E, I, H, I, false, st), "pack down");
+        return rc == MOE_OK ? ok() : rc;
+    }
+    rc = hip_status(moe::launch_pack_gate_up(w_gate_up, packed_gate_up, E, H, I, elem, st), "pack gate_up");
     if (rc != MOE_OK) return rc;
     rc = hip_status(moe::launch_pack_down(w_down, packed_down, E, H, I, elem, st), "pack down");
+    return rc == MOE_OK ? ok() : rc;
+}
+
+int moe_pack_mx_scales(const uint8_t* s_gate_up, const uint8_t* s_down, int E, int H, int I,
+                       uint8_t* packed_s_gate_up, uint8_t* packed_s_down, void* stream) {
+    if (E < 1 || E > moe::kMaxExperts || H <= 0 || I <= 0)
+        return fail(MOE_ERR_INVALID_ARG, "bad sizes E=%d H=%d I=%d", E, H, I);
+    if (H % 256 != 0 || I % 256 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "MX: H and I multiples of 256 (H=%d, I=%d)", H, I);
+    if (!s_gate_up || !s_down || !packed_s_gate_up || !packed_s_down)
+        return fail(MOE_ERR_INVALID_ARG, "null scale pointer");
+    if (s_gate_up == packed_s_gate_up || s_down == packed_s_down)
+        return fail(MOE_ERR_INVALID_ARG, "packing cannot run in place");
+    if (!aligned16(packed_s_gate_up) || !aligned16(packed_s_down))
+        return fail(MOE_ERR_INVALID_ARG, "packed scale pointers must be 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = hip_status(moe::launch_pack_mx_scales(s_gate_up, packed_s_gate_up, E, H, 2 * I, I, true, st),
+                        "pack gate_up scales");
+    if (rc != MOE_OK) return rc;
+    rc = hip_status(moe::launch_pack_mx_scales(s_down, packed_s_down, E, I, H, I, false, st), "pack down scales");
     return rc == MOE_OK ? ok() : rc;
 }
 

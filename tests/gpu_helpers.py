@@ -32,6 +32,8 @@ def weights_dev(w: dict, quant: str):
         gu = torch.from_numpy(w["w_gate_up"]).to(DEV)
         dn = torch.from_numpy(w["w_down"]).to(DEV)
         scales = (torch.from_numpy(w["s_gate_up"]).to(DEV), torch.from_numpy(w["s_down"]).to(DEV))
+        if quant == "fp8_mx32":
+            scales = moe.pack_mx_scales(*scales)
     pgu, pd = moe.pack_weights(gu, dn, quant)
     torch.cuda.synchronize()
     del gu, dn

@@ -38,6 +38,12 @@ def test_select_path_rules():
     assert moe.select_path(8192, 2048, 768, 128, 8) == "grouped"
     assert moe.select_path(64, 256, 512, 16, 8) == "grouped"
     assert moe.select_path(1, 2048, 768, 128, 8, "bf16", "grouped") == "grouped"
+    # MX FP8 runs on the grouped path only, H and I multiples of 256
+    assert moe.select_path(1, 2048, 768, 128, 8, "fp8_mx32") == "grouped"
+    with pytest.raises(moe.MoeError):
+        moe.select_path(1, 2048, 768, 128, 8, "fp8_mx32", "route_direct")
+    with pytest.raises(moe.MoeError):
+        moe.select_path(64, 2048, 192, 128, 8, "fp8_mx32")
     assert moe.select_path(64, 2048, 768, 128, 8, "bf16", "route_direct") == "route_direct"
 
 

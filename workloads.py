@@ -24,6 +24,7 @@ Workloads (the shapes of the layers the pages measure):
   decode_fp8_tensor  T=B in 1..8, H=4096, I=192, E=192, k=8 (Hunyuan TP8 share)
   prefill_bf16       T=8192, H=2048, I=768, E=128, k=8, Zipf-biased routing
   prefill_fp8_block  T=4096, H=4096, I=512, E=128, k=8, fp8 128x128 blockwise
+  prefill_fp8_mx     the same shape, MX fp8 (E8M0 scale per 32 values along K)
 """
 from __future__ import annotations
 
@@ -61,6 +62,8 @@ WORKLOADS = {
     "prefill_bf16": Workload("prefill_bf16", 8192, 2048, 768, 128, 8, "bf16", 2, 4, "zipf"),
     "prefill_fp8_block": Workload("prefill_fp8_block", 4096, 4096, 512, 128, 8, "fp8_block128",
                                   5, 5),
+    # the same layer shape with MX FP8 weights (E8M0 scale per 32 values along K)
+    "prefill_fp8_mx": Workload("prefill_fp8_mx", 4096, 4096, 512, 128, 8, "fp8_mx32", 7, 5),
 }
 
 
