@@ -411,9 +411,10 @@ gemm32_kernel(const GemmArgs g) {
         std::integral_constant<bool, RS> Rc;
         float fac[2][4];
         if constexpr (RS) block_factors(min(s >> 1, KT - 1), fac);
-        if constexpr (MX && U == 0) {
-            // a new scale group: the token rows' dwords 2g + hh from the LDS
-            // table (landed before step 0), the weights' from the group's load
+        if constexpr (MX) {
+            // the token rows' scale dwords 2g + hh of this slice's group from the
+            // LDS table (landed before step 0; read every step, so they hold no
+            // registers across steps)
             const uint32_t* st32 = reinterpret_cast<const uint32_t*>(sat);
             const int d = 2 * min(s >> 2, NG - 1) + hh;
 #pragma unroll
