@@ -141,8 +141,8 @@ def bench_prefill(torch, moe, name, steps, warmup, stage_steps=10):
 # counters were taken on; any edit to it turns the figure into null.
 FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524303.0, 1.0
 COUNTER_TRAFFIC = {
-    "prefill_bf16": dict(gemm_sha256="aca150c9403721117daa99b4b6c7ef0f376b3946d3a8571bcdb237f510b77749",
-                         fetch_kib=801640.3, write_kib=98329.8),
+    "prefill_bf16": dict(gemm_sha256="0b4c38135dcab7544d90ea6facdbe160de9129dc510abeb242c3d98831e4c177",
+                         fetch_kib=795330.8, write_kib=98316.5),
 }
 
 
@@ -395,17 +395,21 @@ def bench_pages_shapes(torch, moe, iters, batches=range(1, 9)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 fwd()
-            ts = []
-            for it in range(iters + 2):
-                evict.amax()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                g.replay()
-                e1.record()
-                if it >= 2:
-                    ts.append((e0, e1))
-            torch.cuda.synchronize()
-            cold = float(np.median([p.elapsed_time(q) for p, q in ts])) * 1e3
+            def cold_median(run):
+                ts = []
+                for it in range(iters + 2):
+                    evict.amax()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    run()
+                    e1.record()
+                    if it >= 2:
+                        ts.append((e0, e1))
+                torch.cuda.synchronize()
+                return float(np.median([p.elapsed_time(q) for p, q in ts])) * 1e3
+
+            cold = cold_median(g.replay)
+            cold_stream = cold_median(fwd)   # the same launches straight on the stream
             for _ in range(20):
                 g.replay()
             w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -419,9 +423,11 @@ def bench_pages_shapes(torch, moe, iters, batches=range(1, 9)):
             del g
             h20 = PAGES_ROUTE_US[key][B - 1]
             out_k[B] = dict(path=path, us_graph_cold=round(cold, 2), us_graph_warm=round(warm, 2),
-                            pages_h20_us=h20, h20_over_warm=round(h20 / warm, 3),
-                            h20_over_cold=round(h20 / cold, 3))
-            log(f"{key} B={B} ({path}): graph cold {cold:.2f} us, warm {warm:.2f} us (pages, H20: {h20} us)")
+                            us_stream_cold=round(cold_stream, 2), pages_h20_us=h20,
+                            h20_over_warm=round(h20 / warm, 3), h20_over_cold=round(h20 / cold, 3),
+                            h20_over_stream_cold=round(h20 / cold_stream, 3))
+            log(f"{key} B={B} ({path}): graph cold {cold:.2f} us, warm {warm:.2f} us, stream cold "
+                f"{cold_stream:.2f} us (pages, H20: {h20} us)")
         res[key] = out_k
         del pgu, pd, scales
         torch.cuda.empty_cache()
@@ -605,8 +611,9 @@ def main():
         line["pages_shapes"] = dict(
             timing=f"moe_forward alone (routes given) captured in a HIP graph with preallocated output; "
                    f"cold: median of {args.decode_iters} replays after a 1 GiB read; warm: 200 back-to-back "
-                   "replays. pages_h20_us: the forced route-direct single-op CUDA graph latency the pages "
-                   "print for the same shape on an H20 (context)",
+                   "replays; stream_cold: the same launches made straight on the stream, cold. pages_h20_us: "
+                   "the forced route-direct single-op CUDA graph latency the pages print for the same shape "
+                   "on an H20 (context)",
             shapes=bench_pages_shapes(torch, moe, args.decode_iters))
         torch.cuda.empty_cache()
         log("decode fp8 per-tensor B=1..4 ...")
