@@ -227,6 +227,12 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
         t_route_only = float(np.median([a.elapsed_time(b) for a, b in tr])) * 1e3
         t_fwd_only = float(np.median([a.elapsed_time(b) for a, b in tf])) * 1e3
         t_fwd = timed(layer.step)
+        # the routing folded into the first kernel (moe_decode_forward), route-direct only
+        t_fused = None
+        if layer.path == "route_direct":
+            t_fused = timed(lambda: moe.decode_forward(layer.lg, layer.x, wl.k, layer.pgu, layer.pd, quant=wl.quant,
+                                                       scales=layer.scales, out=layer.out, routes=layer.routes,
+                                                       path=layer.path, workspace=layer.ws))
         # the step captured once (as a serving loop would) and replayed
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -275,7 +281,9 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
         D = float(np.mean(distinct))
         w_bytes = D * 3 * wl.H * wl.I * elem
         dom_bytes = D * 2 * wl.H * wl.I * elem + B * wl.H * elem   # Gate/Up weights + activations
-        res[B] = dict(us_per_layer=round(t_fwd, 2), us_route=round(t_route_only, 2),
+        res[B] = dict(us_per_layer=round(t_fwd, 2),
+                      us_per_layer_fused=None if t_fused is None else round(t_fused, 2),
+                      us_route=round(t_route_only, 2),
                       us_forward=round(t_fwd_only, 2), us_per_layer_graph=round(t_graph, 2),
                       us_per_layer_graph_warm=round(t_graph_warm, 2),
                       tokens_per_s=round(B / (t_fwd * 1e-6), 1),
@@ -287,7 +295,7 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
                                     achieved=round(dom_bytes / (t_dom * 1e-6) / 1e9, 1),
                                     peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(dom_bytes / (t_dom * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)))
-        log(f"decode {name} B={B}: {t_fwd:.2f} us/layer (route {t_route_only:.2f} + forward {t_fwd_only:.2f}; "
+        log(f"decode {name} B={B}: {t_fwd:.2f} us/layer, fused {t_fused} (route {t_route_only:.2f} + forward {t_fwd_only:.2f}; "
             f"graph {t_graph:.2f}, warm graph {t_graph_warm:.2f}), "
             f"{res[B]['dominant']['kernel']} {t_dom:.2f} us {res[B]['dominant']['achieved']} GB/s")
     del evict
@@ -589,7 +597,9 @@ def main():
     line["decode"] = dict(workload="decode_bf16 H=2048 I=768 E=128 top-8", timing="cold HBM, median of "
                           f"{args.decode_iters}; us_per_layer: moe_route + moe_forward launched on "
                           "the stream between two HIP events (us_route, us_forward: the two calls "
-                          "separately); _graph: the same step replayed from a HIP graph, cold; "
+                          "separately); us_per_layer_fused: moe_decode_forward, the routing folded into "
+                          "the route-direct Gate/Up kernel (one call); _graph: the same step replayed from "
+                          "a HIP graph, cold; "
                           "_graph_warm: replayed back to back with the weights cached; dominant: "
                           "the kernel between stage events",
                           batches=bench_decode(torch, moe, "decode_bf16", (1, 2, 3, 4), args.decode_iters))

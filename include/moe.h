@@ -209,6 +209,25 @@ int moe_forward_ex(const void *x, const moe_routes *routes, const void *packed_g
                    const void *packed_down, const moe_scales *scales, void *out, int H, int I,
                    int quant, int path, const moe_ep *ep, void *ws, size_t ws_bytes, void *stream);
 
+/* Decode batch in one call: the routing folded into the route-direct Gate/Up
+ * kernel ("perf: add small-batch route MMA for MoE", Summary: the fast path
+ * reads each route's expert straight from the token's top-k; Motivation: the
+ * route-order pipeline starts from the top-k routes).  Every Gate/Up workgroup
+ * takes its route's expert from the top-k of its token's logits (fp32 [T,E],
+ * as moe_route reads them), so no routing launch precedes the layer.
+ *   routes: caller-allocated as for moe_route; this call sets T/E/k and writes
+ *           topk_ids and topk_weights (the same bits moe_route writes);
+ *           expert_counts, expert_offsets, perm and route_pos are not used and
+ *           not written (may be NULL).
+ *   everything else as for moe_forward_ex (ep may be NULL).
+ * The path (AUTO or forced) must be the route-direct one, else
+ * MOE_ERR_UNSUPPORTED: larger batches use moe_route + moe_forward.  The
+ * workspace is moe_forward_workspace_size(T, H, I, E, k, quant, path). */
+int moe_decode_forward(const float *logits, const void *x, int T, int E, int k, moe_routes *routes,
+                       const void *packed_gate_up, const void *packed_down, const moe_scales *scales, void *out,
+                       int H, int I, int quant, int path, const moe_ep *ep, void *ws, size_t ws_bytes,
+                       void *stream);
+
 /* moe_forward with stage timing for profilers and benchmarks: the same
  * kernels, plus hipEventRecord(stage_events[i], stream) before the first
  * launch and after each launch (no synchronisation).  stage_events holds

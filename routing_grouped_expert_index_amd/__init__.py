@@ -27,7 +27,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_route_project_workspace_size",
             "moe_route_project", "moe_pack_weights", "moe_pack_mx_scales", "moe_select_path",
-            "moe_forward_workspace_size", "moe_forward", "moe_forward_ex", "moe_forward_profiled",
+            "moe_forward_workspace_size", "moe_forward", "moe_forward_ex", "moe_decode_forward",
+            "moe_forward_profiled",
             "moe_last_error"]
 
 
@@ -88,6 +89,9 @@ def lib():
     L.moe_forward_ex.restype = i32
     L.moe_forward_ex.argtypes = L.moe_forward.argtypes[:10] + [ctypes.POINTER(_CEp)] + \
         L.moe_forward.argtypes[10:]
+    L.moe_decode_forward.restype = i32
+    L.moe_decode_forward.argtypes = [P, P, i32, i32, i32, ctypes.POINTER(_CRoutes), P, P, ctypes.POINTER(_CScales),
+                                     P, i32, i32, i32, i32, ctypes.POINTER(_CEp), P, sz, P]
     L.moe_forward_profiled.restype = i32
     L.moe_forward_profiled.argtypes = L.moe_forward.argtypes + [ctypes.POINTER(ctypes.c_void_p), i32,
                                                                ctypes.POINTER(ctypes.c_int),
@@ -234,6 +238,41 @@ def select_path(T, H, I, E, k, quant="bf16", path="auto") -> str:
 
 def forward_workspace_size(T, H, I, E, k, quant="bf16", path="auto") -> int:
     return int(lib().moe_forward_workspace_size(T, H, I, E, k, QUANT[quant], PATH[path]))
+
+
+def decode_forward(logits: torch.Tensor, x: torch.Tensor, k: int, packed_gate_up: torch.Tensor,
+                   packed_down: torch.Tensor, quant: str = "bf16", scales=None, out: torch.Tensor | None = None,
+                   routes: Routes | None = None, path: str = "auto", workspace: torch.Tensor | None = None,
+                   stream=None, expert_begin: int = 0, num_experts: int | None = None, accumulate: bool = False):
+    """Routing and the route-direct layer in one call (moe_decode_forward): returns
+    (out, routes); routes carries topk_ids and topk_weights (counts, offsets,
+    perm and route_pos are not written)."""
+    _need_cuda(logits, "logits")
+    _need_cuda(x, "x")
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be float32 [T, E]")
+    T, E = logits.shape
+    if x.element_size() != 2 or x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be a bf16 [T, H] tensor with the logits' T")
+    H = x.shape[1]
+    if packed_down.dim() != 3 or packed_down.shape[2] != H:
+        raise ValueError("packed_down must be [E, I, H] (the shape of the unpacked tensor)")
+    I = packed_down.shape[1]
+    if accumulate and out is None:
+        raise ValueError("accumulate needs the output to add into")
+    routes = routes if routes is not None else Routes(T, E, k, x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    need = forward_workspace_size(T, H, I, E, k, quant, path)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    cs = routes.c_struct()
+    sc = _CScales(None, None) if scales is None else _CScales(scales[0].data_ptr(), scales[1].data_ptr())
+    ep = _CEp(expert_begin, E - expert_begin if num_experts is None else num_experts, int(bool(accumulate)))
+    _check(lib().moe_decode_forward(_ptr(logits), _ptr(x), T, E, k, ctypes.byref(cs), _ptr(packed_gate_up),
+                                    _ptr(packed_down), ctypes.byref(sc), _ptr(out), H, I, QUANT[quant], PATH[path],
+                                    ctypes.byref(ep), _ptr(workspace), workspace.numel(), _stream(x.device, stream)))
+    return out, routes
 
 
 def forward(x: torch.Tensor, routes: Routes, packed_gate_up: torch.Tensor, packed_down: torch.Tensor,

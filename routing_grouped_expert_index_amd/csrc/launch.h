@@ -83,6 +83,11 @@ struct FwdPlan {
     int max_tiles;
     // expert slice [e0, e0 + nloc) held by the weights (index e - e0); acc: out += sum
     int e0, nloc, acc;
+    // route-direct with the routing folded in: logits [T][E]; the Gate/Up kernel
+    // writes each route's id and gate to ids_w / tw_w (ids / tw point there too)
+    const float* logits;
+    int32_t* ids_w;
+    float* tw_w;
 };
 
 constexpr int kGemmBM = 128;

@@ -276,7 +276,8 @@ size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int quant, 
 static int forward_impl(const void* x, const moe_routes* routes, const void* packed_gate_up,
                         const void* packed_down, const moe_scales* scales, void* out, int H, int I,
                         int quant, int path, const moe_ep* ep, void* ws, size_t ws_bytes, void* stream,
-                        void** events, int n_events, int* n_stages, const char** stage_names) {
+                        void** events, int n_events, int* n_stages, const char** stage_names,
+                        const float* logits = nullptr) {
     if (!routes) return fail(MOE_ERR_INVALID_ARG, "routes is NULL");
     const int T = routes->T, E = routes->E, k = routes->k;
     int rc = check_shape(T, H, I, E, k, quant);
@@ -287,6 +288,9 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
                     e0, e0, nloc, E);
     const int p = resolve_path(T, H, I, E, k, quant, path);
     if (p < 0) return p;
+    if (logits && p != MOE_PATH_ROUTE_DIRECT)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_decode_forward runs the route-direct path only (T=%d, E=%d, k=%d)", T, E, k);
+    if (logits && T > 0 && !aligned16(logits)) return fail(MOE_ERR_INVALID_ARG, "logits must be 16-byte aligned");
     if (T == 0) {
         if (n_stages) *n_stages = 0;
         if (stage_names) *stage_names = "";
@@ -336,6 +340,9 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
     P.e0 = e0;
     P.nloc = nloc;
     P.acc = acc;
+    P.logits = logits;
+    P.ids_w = logits ? routes->topk_ids : nullptr;
+    P.tw_w = logits ? routes->topk_weights : nullptr;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool grouped = p == MOE_PATH_GROUPED;
@@ -389,6 +396,19 @@ int moe_forward_ex(const void* x, const moe_routes* routes, const void* packed_g
                    int quant, int path, const moe_ep* ep, void* ws, size_t ws_bytes, void* stream) {
     return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, ep, ws,
                         ws_bytes, stream, nullptr, 0, nullptr, nullptr);
+}
+
+int moe_decode_forward(const float* logits, const void* x, int T, int E, int k, moe_routes* routes,
+                       const void* packed_gate_up, const void* packed_down, const moe_scales* scales, void* out,
+                       int H, int I, int quant, int path, const moe_ep* ep, void* ws, size_t ws_bytes,
+                       void* stream) {
+    if (!routes) return fail(MOE_ERR_INVALID_ARG, "routes is NULL");
+    if (T > 0 && !logits) return fail(MOE_ERR_INVALID_ARG, "logits is NULL");
+    routes->T = T;
+    routes->E = E;
+    routes->k = k;
+    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, ep, ws, ws_bytes,
+                        stream, nullptr, 0, nullptr, nullptr, logits ? logits : nullptr);
 }
 
 int moe_forward_profiled(const void* x, const moe_routes* routes, const void* packed_gate_up,

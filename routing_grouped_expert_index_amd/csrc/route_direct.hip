@@ -35,6 +35,7 @@
 #include "common.cuh"
 #include "launch.h"
 #include "layout.cuh"
+#include "topk.cuh"
 
 #include <algorithm>
 #include <atomic>
@@ -62,6 +63,13 @@ struct RdArgs {
     int kp;                  // per-block Down: K parts per route slot
     int rs;                  // Gate/Up row split (workgroups per 32-row block pair)
     int e0, nloc;            // expert slice held by the weights (expert e at index e - e0)
+    // routing folded into the Gate/Up kernel: with logits set, each Gate/Up
+    // workgroup takes its route's expert from the top-k of its token's logits,
+    // and the first workgroup of a route writes the route's id and gate to
+    // ids_w / tw_w (which the Down kernel then reads as ids / tw)
+    const float* logits;     // fp32 [T][E] or null
+    int32_t* ids_w;
+    float* tw_w;
     int acc;                 // out += the layer sum (else out = it)
 };
 
@@ -247,6 +255,7 @@ rd_gate_up_kernel(const RdArgs a) {
     __shared__ float sxs[Q == RD_BLOCK ? kRdActBytes / 128 : 1];   // blockwise: the row's x scales
     __shared__ float red[NW][2][32];
     __shared__ float sred[NW];
+    __shared__ int s_eg;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int j = lane & 31, hh = lane >> 5;
     const int r = blockIdx.x, G = blockIdx.y;   // route; 64-row group (gate block 2G, up block 2G+1)
@@ -257,7 +266,24 @@ rd_gate_up_kernel(const RdArgs a) {
     // 32 distinct bytes, and the RS lanes of a row are added at the end.
     const int lrs = __builtin_ctz(gridDim.z), RS = 1 << lrs, RW = 32 >> lrs, rs = blockIdx.z;
     const int ls = j >> (5 - lrs), jr = rs * RW + (j & (RW - 1));
-    const int t = r / a.k, e = a.ids[r] - a.e0;   // the expert's index in this call's slice
+    const int t = r / a.k;
+    // With logits, wave 0 takes the route's expert from the token's top-k
+    // while the workgroup stages x, and the weight stream starts after the
+    // barrier that publishes it; otherwise the expert comes from the routes and
+    // the weight stream starts first.
+    const bool from_logits = a.logits != nullptr;
+    if (from_logits && wave == 0) {
+        int eg0;
+        float gate;
+        topk_slot_row(a.logits + (size_t)t * a.E, a.E, a.k, r - t * a.k, eg0, gate);
+        if (lane == 0) {
+            s_eg = eg0;
+            if (G == 0 && rs == 0) {   // one writer per route
+                a.ids_w[r] = eg0;
+                a.tw_w[r] = gate;
+            }
+        }
+    }
     constexpr int elem = FP8 ? 1 : 2;
     // wave w takes the U-super-slice chunks w, w + NW, w + 2 NW, ...: at each
     // step the waves of the workgroup read one contiguous window
@@ -266,14 +292,23 @@ rd_gate_up_kernel(const RdArgs a) {
     const long gstride = 32L * Kb;
     if (r == 0 && G == 0 && rs == 0)   // the Down kernel that follows counts arrivals from zero
         for (int i = threadIdx.x; i < a.T * (a.H / 32); i += 64 * NW) a.cnt[i] = 0;
-    if ((unsigned)e >= (unsigned)a.nloc) {   // another slice's expert: no h, a zero share of the h amax
-        if constexpr (Q == RD_TENSOR) {
-            if (threadIdx.x == 0) a.hmax[((long)r * (a.I / 32) + G) * RS + rs] = 0.0f;
+    int e = 0;
+    const uint8_t *wg = nullptr, *wu = nullptr;
+    // the expert's index in this call's slice and its weight rows; false for
+    // another slice's expert (no h, a zero share of the h amax)
+    auto resolve = [&](int eg) __attribute__((always_inline)) {
+        e = eg - a.e0;
+        if ((unsigned)e >= (unsigned)a.nloc) {
+            if constexpr (Q == RD_TENSOR) {
+                if (threadIdx.x == 0) a.hmax[((long)r * (a.I / 32) + G) * RS + rs] = 0.0f;
+            }
+            return false;
         }
-        return;
-    }
-    const uint8_t* wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + (32 * hh + jr) * 16 + ls * 2048;
-    const uint8_t* wu = wg + gstride;
+        wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + (32 * hh + jr) * 16 + ls * 2048;
+        wu = wg + gstride;
+        return true;
+    };
+    if (!from_logits && !resolve(a.ids[r])) return;
 
     // two load buffers: batch b+1 is requested before batch b is computed
     u32x4 vg[2][U][2], vu[2][U][2];
@@ -291,7 +326,7 @@ rd_gate_up_kernel(const RdArgs a) {
     };
     std::integral_constant<int, 0> B0;
     std::integral_constant<int, 1> B1;
-    load_batch(B0, s0);   // the weight stream starts before the activation row is staged
+    if (!from_logits) load_batch(B0, s0);   // the weight stream starts before the activation row is staged
 
     float xs = 1.0f;
     const uint16_t* x = reinterpret_cast<const uint16_t*>(a.act);
@@ -304,6 +339,10 @@ rd_gate_up_kernel(const RdArgs a) {
         stage_row<NW>(xrow, a.act + (long)t * Kb, Kb);
     }
     __syncthreads();
+    if (from_logits) {   // the expert wave 0 published; then the weight stream
+        if (!resolve(__builtin_amdgcn_readfirstlane(s_eg))) return;
+        load_batch(B0, s0);
+    }
     int cg = 0, cu = 0;           // blockwise: scale columns of the gate and up blocks
     if constexpr (Q == RD_BLOCK) {
         cg = (32 * G) / 128;
@@ -688,6 +727,9 @@ static RdArgs rd_args(const FwdPlan& p) {
     a.e0 = p.e0;
     a.nloc = p.nloc;
     a.acc = p.acc;
+    a.logits = p.logits;
+    a.ids_w = p.ids_w;
+    a.tw_w = p.tw_w;
     return a;
 }
 

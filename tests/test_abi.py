@@ -132,6 +132,13 @@ def test_host_validation_before_any_launch():
                                None) == -3
     assert L.moe_route_project(bad, good, 4, 2048, 128, 8, good, ctypes.byref(r), good, need, None) == -1
     assert L.moe_route_project_workspace_size(4, 100, 128, 8) == 0
+    # the decode entry: logits required for T > 0, route-direct path only
+    assert L.moe_decode_forward(None, good, 4, 128, 8, ctypes.byref(r), good, good, None, good, 2048, 768, 0, 0,
+                                None, good, 1 << 30, None) == -1
+    assert L.moe_decode_forward(good, good, 4, 128, 8, ctypes.byref(r), good, good, None, good, 2048, 768, 0, 1,
+                                None, good, 1 << 30, None) == -2
+    assert L.moe_decode_forward(good, good, 64, 128, 8, ctypes.byref(r), good, good, None, good, 2048, 768, 0, 0,
+                                None, good, 1 << 30, None) == -2
     # packing rejects in-place and null
     assert L.moe_pack_weights(good, good, 4, 256, 64, 0, good, None, None) == -1
     assert L.moe_pack_weights(good, None, 4, 256, 64, 0, good, good, None) == -1
