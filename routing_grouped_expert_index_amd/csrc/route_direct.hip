@@ -878,7 +878,8 @@ hipError_t launch_route_direct_gate_up(const FwdPlan& p, hipStream_t st) {
 // Down split: K parts per route (1, 2 or 4, dividing NSL) only while the grid
 // stays small (every item of an output block takes a ticket from the same
 // counter, and those atomics serialise), then waves per workgroup (1, 2 or 4)
-// until each wave streams at most 8 slices, then the batch size.
+// until each wave streams at most 4 slices (blockwise E=128 decode: 0.8-2.2 us
+// faster than at most 8, bf16 unchanged), then the batch size.
 struct RdDownCfg {
     int kp, nw, U;
 };
@@ -889,7 +890,7 @@ static RdDownCfg rd_down_cfg(int T, int H, int I, int k, int quant) {
     RdDownCfg c{1, 1, 1};
     while (c.kp < 4 && NSL % (c.kp * 2) == 0 && tb * k * c.kp * 2 <= 256) c.kp *= 2;
     const int per = NSL / c.kp;
-    while (c.nw < 4 && per % (c.nw * 2) == 0 && per / c.nw > 8) c.nw *= 2;
+    while (c.nw < 4 && per % (c.nw * 2) == 0 && per / c.nw > 4) c.nw *= 2;
     c.U = largest_unroll(per / c.nw, 8);
     return c;
 }
