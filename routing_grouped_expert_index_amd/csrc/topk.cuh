@@ -95,13 +95,13 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(max(readlane_u32(v, 0), readlane_u32(v, 16)), max(readlane_u32(v, 32), readlane_u32(v, 48)));
 }
 
-// Picks the k largest logits of one token (row) with one whole wave: slot j
-// holds the j-th largest value, ties to the lower expert id.  Gates:
-// exp(l_j - m) / sum over the picks of exp(l_i - m), m = the largest logit (the
-// full softmax denominator cancels in the renormalisation).  The lane that owns
-// a picked logit writes ids[j] and w[j] itself, so no value travels back
-// through memory.  Logits are taken as finite (with NaN the picks stay in range
-// and distinct but their order is unspecified).
+// The k largest logits of one token (row) with one whole wave: slot[i] is the
+// pick (0..k-1) held by the lane's entry i, or -1; pick j is the j-th largest
+// value, ties to the lower expert id.  Gates (computed by the callers):
+// exp(l_j - m) / S, m the largest logit, S the sum over the picks of
+// exp(l_i - m) (the full softmax denominator cancels in the renormalisation).
+// Logits are taken as finite (with NaN the picks stay in range and distinct
+// but their order is unspecified).
 //
 // Pick j is a wave max over order-preserving integer keys (taken and padding
 // entries hold key 0, real ones at least 1), then of the entries holding that
@@ -145,6 +145,9 @@ __device__ __forceinline__ void topk_core(const TopkRow<VPL>& r, int k, int (&sl
     S = wave_sum_full(part);
 }
 
+// topk_core, then the lane that owns a picked logit writes ids[j] and w[j]
+// itself (and the LDS copies when given), so no value travels back through
+// memory.
 template <int VPL>
 __device__ __forceinline__ void topk_pick(TopkRow<VPL>& r, int k, int32_t* __restrict__ ids,
                                           float* __restrict__ w, int32_t* __restrict__ ids_lds,
