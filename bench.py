@@ -142,7 +142,7 @@ def bench_prefill(torch, moe, name, steps, warmup, stage_steps=10):
 FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524303.0, 1.0
 COUNTER_TRAFFIC = {
     "prefill_bf16": dict(gemm_sha256="0b4c38135dcab7544d90ea6facdbe160de9129dc510abeb242c3d98831e4c177",
-                         fetch_kib=795330.8, write_kib=98316.5),
+                         fetch_kib=804602.4, write_kib=98329.5),
 }
 
 
