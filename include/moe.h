@@ -14,7 +14,12 @@
  *             projection and the top-k weighted combine, either over the
  *             expert-grouped routes (grouped GEMMs) or straight from the routes
  *             for small decode batches ("perf: add small-batch route MMA for
- *             MoE", Summary, Motivation and Dispatch).
+ *             MoE", Summary, Motivation and Dispatch);
+ *   also      router scores x W_r fused with the routing (moe_route_project),
+ *             an expert slice and a shared output (moe_forward_ex), a decode
+ *             batch with the routing folded into its first kernel
+ *             (moe_decode_forward), and MX FP8 weights (MOE_FP8_MX32,
+ *             moe_pack_mx_scales).
  *
  * Conventions for every entry point:
  *   - Every pointer is a device pointer (HIP global memory of the current
@@ -32,6 +37,8 @@
  *     routes that moe_route did not produce (for example ids >= E) give
  *     undefined results.
  *   - Pointers must be 16-byte aligned.
+ *   - Calls that share a workspace must be ordered on one stream (or
+ *     otherwise not run at the same time).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -157,7 +164,8 @@ int moe_pack_mx_scales(const uint8_t *s_gate_up, const uint8_t *s_down, int E, i
  * the requested path cannot run it.  Host-only; no GPU call.
  * ("perf: add small-batch route MMA for MoE", Dispatch.)  AUTO takes the
  * route-direct path while T*k <= 3E/4 and T <= 16 and the shape fits it
- * (the bound measured on MI355X with both paths forced), else grouped. */
+ * (the bound measured on MI355X with both paths forced), else grouped; MX
+ * (MOE_FP8_MX32) always takes the grouped path. */
 int moe_select_path(int T, int H, int I, int E, int k, int quant, int path);
 
 /* Bytes of workspace moe_forward needs for this shape, quantisation and path. */
