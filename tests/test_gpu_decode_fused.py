@@ -103,3 +103,45 @@ def test_decode_fused_rejects_grouped_and_empty_batch():
                                 device=DEV), 2, pgu, pd, path="route_direct")
     torch.cuda.synchronize()
     assert out.shape == (0, 128)
+
+
+def test_decode_fused_graph_replay():
+    """Captured in a HIP graph and replayed several times with eager calls between: every replay
+    gives the eager output's bits and the same routes."""
+    name = "decode_fp8_tensor"
+    wl = WORKLOADS[name]
+    a = workload_inputs(name, batch=3)
+    pgu, pd, sc = workload_dev(name)
+    x = bf16_dev(a["x"])
+    lg = torch.from_numpy(a["logits"]).to(DEV)
+    T = x.shape[0]
+    routes = moe.Routes(T, wl.E, wl.k, DEV)
+    out = torch.empty((T, wl.H), dtype=torch.bfloat16, device=DEV)
+    ws = torch.zeros(max(256, moe.forward_workspace_size(T, wl.H, wl.I, wl.E, wl.k, wl.quant)), dtype=torch.uint8,
+                     device=DEV)
+
+    def step():
+        moe.decode_forward(lg, x, wl.k, pgu, pd, quant=wl.quant, scales=sc, out=out, routes=routes, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager, ids = out.clone(), routes.topk_ids.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        out.zero_()
+        routes.topk_ids.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        assert torch.equal(routes.topk_ids, ids)
+        step()
+        torch.cuda.synchronize()

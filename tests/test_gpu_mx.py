@@ -129,3 +129,15 @@ def test_mx_scale_packing_layout():
                     for u in range(4):
                         ref[:, rb, g, lane, u] = src[:, 8 * g + 2 * u + (lane >> 5), col]
         assert np.array_equal(got.cpu().numpy().reshape(-1), ref.reshape(-1))
+
+
+def test_mx_two_runs_bitwise_equal():
+    T, H, I, E, k = 300, 512, 256, 8, 2
+    a = random_activations(T, H, E, seed=450)
+    w = random_weights(E, H, I, "fp8_mx32", seed=451)
+    pgu, pd, sc = weights_dev(w, "fp8_mx32")
+    r = moe.route(torch.from_numpy(a["logits"]).to(DEV), k)
+    o1 = moe.forward(bf16_dev(a["x"]), r, pgu, pd, quant="fp8_mx32", scales=sc)
+    o2 = moe.forward(bf16_dev(a["x"]), r, pgu, pd, quant="fp8_mx32", scales=sc)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
