@@ -560,9 +560,8 @@ def main():
                          "reference); prints per-stage times instead of the JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the layer's expert/tensor sharding is described in DESIGN.md but not built); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the layer's expert and tensor sharding over "
+              "several GPUs is not built; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

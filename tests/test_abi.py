@@ -142,3 +142,14 @@ def test_host_validation_before_any_launch():
     # packing rejects in-place and null
     assert L.moe_pack_weights(good, good, 4, 256, 64, 0, good, None, None) == -1
     assert L.moe_pack_weights(good, None, 4, 256, 64, 0, good, good, None) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with status 2 and a message,
+    before touching torch or the device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
