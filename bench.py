@@ -365,7 +365,8 @@ PAGES_ROUTE_US = {
 def bench_pages_shapes(torch, moe, iters, batches=range(1, 9)):
     """moe_forward alone (routes given, as the pages time their op) captured in a
     HIP graph with preallocated output, at the pages' three FP8 decode shapes:
-    replayed cold (a 1 GiB read before each replay) and warm (back to back)."""
+    replayed cold (a 1 GiB read before each replay) and warm (back to back), and
+    launched straight on the stream, cold and warm (each call between two events)."""
     from workloads import random_activations, random_weights, workload_weights
     evict = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
     shapes = [("fp8_per_tensor E=192 H=4096 I=192", 192, 4096, 192, "fp8_per_tensor",
@@ -403,10 +404,11 @@ def bench_pages_shapes(torch, moe, iters, batches=range(1, 9)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 fwd()
-            def cold_median(run):
+            def cold_median(run, cold=True):
                 ts = []
                 for it in range(iters + 2):
-                    evict.amax()
+                    if cold:
+                        evict.amax()
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record()
                     run()
@@ -418,6 +420,9 @@ def bench_pages_shapes(torch, moe, iters, batches=range(1, 9)):
 
             cold = cold_median(g.replay)
             cold_stream = cold_median(fwd)   # the same launches straight on the stream
+            # stream, warm: no read between the calls, so the weights stay in the caches;
+            # each call timed between its own two events (the device time of its launches)
+            warm_stream = cold_median(fwd, cold=False)
             for _ in range(20):
                 g.replay()
             w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -431,11 +436,12 @@ def bench_pages_shapes(torch, moe, iters, batches=range(1, 9)):
             del g
             h20 = PAGES_ROUTE_US[key][B - 1]
             out_k[B] = dict(path=path, us_graph_cold=round(cold, 2), us_graph_warm=round(warm, 2),
-                            us_stream_cold=round(cold_stream, 2), pages_h20_us=h20,
+                            us_stream_cold=round(cold_stream, 2), us_stream_warm=round(warm_stream, 2),
+                            pages_h20_us=h20, h20_over_stream_warm=round(h20 / warm_stream, 3),
                             h20_over_warm=round(h20 / warm, 3), h20_over_cold=round(h20 / cold, 3),
                             h20_over_stream_cold=round(h20 / cold_stream, 3))
             log(f"{key} B={B} ({path}): graph cold {cold:.2f} us, warm {warm:.2f} us, stream cold "
-                f"{cold_stream:.2f} us (pages, H20: {h20} us)")
+                f"{cold_stream:.2f} us, stream warm {warm_stream:.2f} us (pages, H20: {h20} us)")
         res[key] = out_k
         del pgu, pd, scales
         torch.cuda.empty_cache()
@@ -620,7 +626,9 @@ def main():
         line["pages_shapes"] = dict(
             timing=f"moe_forward alone (routes given) captured in a HIP graph with preallocated output; "
                    f"cold: median of {args.decode_iters} replays after a 1 GiB read; warm: 200 back-to-back "
-                   "replays; stream_cold: the same launches made straight on the stream, cold. pages_h20_us: "
+                   "replays; stream_cold: the same launches made straight on the stream, cold; stream_warm: "
+                   "the same, without the read between calls (weights cache-resident), each call between its "
+                   "own two events, median. pages_h20_us: "
                    "the forced route-direct single-op CUDA graph latency the pages print for the same shape "
                    "on an H20 (context)",
             shapes=bench_pages_shapes(torch, moe, args.decode_iters))
