@@ -754,8 +754,8 @@ static int largest_unroll(int n, int cap) {
 // workgroups would double the kernel's time.  Residency comes from the
 // runtime's occupancy figure for the exact kernel.  Ties keep the smaller
 // split (measured: a split that only repacks the same waves into more,
-// smaller workgroups loses a little).  The blockwise format keeps RS = 1: its
-// scales are per 128-deep block.
+// smaller workgroups loses a little).  The blockwise format splits too: each
+// lane reads the scales of its own slice's 128-deep block.
 struct RdGuCfg {
     int rs, nw, U;
 };
@@ -836,7 +836,7 @@ static RdGuCfg rd_gu_cfg(int T, int H, int I, int k, int quant) {
     const long groups = (long)T * k * (I / 32);
     RdGuCfg best{0, 0, 0};
     long best_waves = -1;
-    for (int rs = 1; rs <= (quant == Q_FP8_BLOCK ? 1 : 4); rs *= 2) {
+    for (int rs = 1; rs <= 4; rs *= 2) {
         if (NSL % rs != 0) break;
         const int NSS = NSL / rs;
         const long wgs = groups * rs;
@@ -866,9 +866,7 @@ hipError_t launch_route_direct_gate_up(const FwdPlan& p, hipStream_t st) {
     const RdGuCfg c = rd_gu_cfg(p.T, p.H, p.I, p.k, p.quant);
     const int NSL = p.H * (p.quant == Q_BF16 ? 2 : 1) / kSliceBytes;
     // the kernel walks NSL / rs super-slices in nw x U steps and never past the end
-    if (c.rs < 1 || c.rs > 4 || NSL % c.rs != 0 || (NSL / c.rs) % (c.nw * c.U) != 0 ||
-        (p.quant == Q_FP8_BLOCK && c.rs != 1))
-        return hipErrorInvalidValue;
+    if (c.rs < 1 || c.rs > 4 || NSL % c.rs != 0 || (NSL / c.rs) % (c.nw * c.U) != 0) return hipErrorInvalidValue;
     const void* fn = rd_gu_fn(p.quant, c.nw, c.U);
     if (!fn) return hipErrorInvalidValue;
     void* args[] = {&a};

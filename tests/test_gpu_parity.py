@@ -131,6 +131,9 @@ EDGE = [
     (150, 384, 256, 8, 2, "fp8_per_tensor", "normal", "per-tensor multi-tile"),
     (70, 256, 256, 6, 2, "fp8_block128", "normal", "block128 ragged"),
     (3, 512, 128, 32, 4, "fp8_block128", "normal", "block128 decode"),
+    # route-direct Gate/Up row split with per-lane 128-block scales (split 2, then 4)
+    (1, 4096, 512, 128, 8, "fp8_block128", "normal", "block128 B=1 row split 2"),
+    (1, 8192, 128, 8, 2, "fp8_block128", "normal", "block128 row split 4"),
     # grids of fewer than 8 workgroups with several n-tiles (every tile range must be walked)
     (5, 256, 192, 1, 1, "bf16", "normal", "small grid, 3 n-tiles"),
     (3, 256, 384, 1, 1, "fp8_block128", "normal", "small grid block128"),
