@@ -56,10 +56,10 @@ def dev_weights(torch, moe, w, quant):
         scales = (torch.from_numpy(w["s_gate_up"]).cuda(), torch.from_numpy(w["s_down"]).cuda())
         if quant == "fp8_mx32":
             scales = moe.pack_mx_scales(*scales)
-    pgu, pd = moe.pack_weights(gu, dn, quant)
+    pw = moe.pack_weights(gu, dn, quant)
     torch.cuda.synchronize()
     del gu, dn
-    return pgu, pd, scales
+    return pw, scales
 
 
 class Layer:
@@ -68,7 +68,7 @@ class Layer:
     def __init__(self, torch, moe, wl, T, x, lg, weights, path="auto"):
         self.torch, self.moe, self.wl, self.T = torch, moe, wl, T
         self.x, self.lg = x, lg
-        self.pgu, self.pd, self.scales = weights
+        self.pw, self.scales = weights
         self.path = moe.select_path(T, wl.H, wl.I, wl.E, wl.k, wl.quant, path)
         self.routes = moe.Routes(T, wl.E, wl.k, x.device)
         self.out = torch.empty((T, wl.H), dtype=torch.bfloat16, device=x.device)
@@ -79,7 +79,7 @@ class Layer:
 
     def step(self, events=None, lg=None):
         self.moe.route(self.lg if lg is None else lg, self.wl.k, out=self.routes, workspace=self.rws)
-        return self.moe.forward(self.x, self.routes, self.pgu, self.pd, quant=self.wl.quant,
+        return self.moe.forward(self.x, self.routes, self.pw, quant=self.wl.quant,
                                 scales=self.scales, out=self.out, path=self.path, workspace=self.ws,
                                 events=events)
 
@@ -217,7 +217,7 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
             e0.record()
             moe.route(layer.lg, wl.k, out=layer.routes, workspace=layer.rws)
             e1.record()
-            moe.forward(layer.x, layer.routes, layer.pgu, layer.pd, quant=wl.quant, scales=layer.scales,
+            moe.forward(layer.x, layer.routes, layer.pw, quant=wl.quant, scales=layer.scales,
                         out=layer.out, path=layer.path, workspace=layer.ws)
             e2.record()
             if it >= 2:
@@ -230,7 +230,7 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
         # the routing folded into the first kernel (moe_decode_forward), route-direct only
         t_fused = None
         if layer.path == "route_direct":
-            t_fused = timed(lambda: moe.decode_forward(layer.lg, layer.x, wl.k, layer.pgu, layer.pd, quant=wl.quant,
+            t_fused = timed(lambda: moe.decode_forward(layer.lg, layer.x, wl.k, layer.pw, quant=wl.quant,
                                                        scales=layer.scales, out=layer.out, routes=layer.routes,
                                                        path=layer.path, workspace=layer.ws))
         # the step captured once (as a serving loop would) and replayed
@@ -381,7 +381,7 @@ def bench_pages_shapes(torch, moe, iters, batches=range(1, 9)):
     torch.cuda.synchronize()
     res = {}
     for key, E, H, I, quant, wfn in shapes:
-        pgu, pd, scales = dev_weights(torch, moe, wfn(), quant)
+        pw, scales = dev_weights(torch, moe, wfn(), quant)
         out_k = {}
         for B in batches:
             a = random_activations(B, H, E, 20000 + B)
@@ -393,7 +393,7 @@ def bench_pages_shapes(torch, moe, iters, batches=range(1, 9)):
                              dtype=torch.uint8, device="cuda")
 
             def fwd():
-                moe.forward(x, r, pgu, pd, quant=quant, scales=scales, out=out, path=path, workspace=ws)
+                moe.forward(x, r, pw, quant=quant, scales=scales, out=out, path=path, workspace=ws)
 
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
@@ -443,7 +443,7 @@ def bench_pages_shapes(torch, moe, iters, batches=range(1, 9)):
             log(f"{key} B={B} ({path}): graph cold {cold:.2f} us, warm {warm:.2f} us, stream cold "
                 f"{cold_stream:.2f} us, stream warm {warm_stream:.2f} us (pages, H20: {h20} us)")
         res[key] = out_k
-        del pgu, pd, scales
+        del pw, scales
         torch.cuda.empty_cache()
     del evict
     return res

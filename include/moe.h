@@ -140,15 +140,33 @@ size_t moe_route_project_workspace_size(int T, int H, int E, int k);
 int moe_route_project(const void *x, const float *w_router, int T, int H, int E, int k,
                       float *logits, moe_routes *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Expert weights as moe_pack_weights re-laid them, with the shape and format
+ * they were packed for.  moe_pack_weights fills every member; the forward
+ * entry points compare E, H, I, quant and tag with the call (E: the routes'
+ * E, or the slice's num_experts) and return MOE_ERR_INVALID_ARG on any
+ * mismatch before anything is enqueued, so raw [E,H,2I] / [E,I,H] weights or
+ * weights packed for another shape cannot reach the kernels by mistake.  The
+ * struct lives in host memory; the two buffers stay owned by the caller. */
+#define MOE_PACKED_TAG 0x4d6f4557u
+typedef struct {
+    const void *gate_up;   /* device: packed Gate/Up weights (E*H*2I elements) */
+    const void *down;      /* device: packed Down weights (E*I*H elements) */
+    int32_t E, H, I;       /* the packed shape */
+    int32_t quant;         /* moe_quant the weights were packed for */
+    uint32_t tag;          /* MOE_PACKED_TAG once moe_pack_weights succeeded */
+} moe_packed_weights;
+
 /* Weight re-layout, once per weight set (not per forward call).
  *   w_gate_up [E][H][2I] (gate = columns [0,I), up = columns [I,2I)) and
  *   w_down [E][I][H], bf16 (2 bytes) or e4m3 codes (1 byte), row-major
  * -> packed_gate_up and packed_down, each the same size as its source, K
  * (the reduction dimension) contiguous, gate and up columns interleaved in
- * groups of 16.  moe_forward reads only the packed form.  Scales are not
- * re-laid out. */
+ * groups of 16.  The forward entry points read only the packed form, through
+ * the descriptor `packed` this call fills (host memory, not NULL; on error its
+ * tag is cleared).  Scales are not re-laid out (MX: moe_pack_mx_scales). */
 int moe_pack_weights(const void *w_gate_up, const void *w_down, int E, int H, int I,
-                     int quant, void *packed_gate_up, void *packed_down, void *stream);
+                     int quant, void *packed_gate_up, void *packed_down,
+                     moe_packed_weights *packed, void *stream);
 
 /* MX scale re-layout, once per weight set ("[mxfp8 moe training] add per group
  * blocked scale kernels", Summary: scales re-laid for the block-scaled matrix
@@ -171,30 +189,72 @@ int moe_select_path(int T, int H, int I, int E, int k, int quant, int path);
 /* Bytes of workspace moe_forward needs for this shape, quantisation and path. */
 size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int quant, int path);
 
+/* Where a forward call leaves its FP8 quantised activations in the workspace,
+ * as byte offsets from ws (-1 where the call keeps no such array).  After a
+ * moe_forward / moe_forward_ex / moe_decode_forward call with this shape,
+ * quantisation and path, and until the next call that uses the workspace:
+ *   x_codes   e4m3 [T,H], the codes the Gate/Up projection consumed (both paths)
+ *   x_scales  per-tensor fp32 [1]; block128 fp32 [T,H/128]; MX E8M0 bytes
+ *             [T,H/32], group c of a row at byte 8(c/8) + 4(c%2) + (c%8)/2
+ *   h_codes   grouped path: e4m3 [T*k,I], row i = the route at sorted position i
+ *   h_scales  per-tensor fp32 [1] (both paths); block128 fp32 [T*k,I/128],
+ *             sorted order (grouped) or route order r = t*k + j (route-direct);
+ *             MX E8M0 [T*k,I/32], sorted order, bytes ordered as x_scales
+ * ("perf: add small-batch route MMA for MoE", Summary: the activation and
+ * Down-input quantisation; exposed so callers and tests can inspect the
+ * codes.)  bf16 has none of them.  Returns MOE_OK or the shape's error. */
+typedef struct {
+    int64_t x_codes, x_scales, h_codes, h_scales;
+} moe_ws_views;
+int moe_forward_workspace_views(int T, int H, int I, int E, int k, int quant, int path, moe_ws_views *out);
+
+/* The launch shape a forward call with these arguments takes (host-only; the
+ * route-direct shape depends on the current device's occupancy figures, so
+ * call it with the device the forward will run on current):
+ *   path            MOE_PATH_GROUPED or MOE_PATH_ROUTE_DIRECT
+ *   gate_up_split   route-direct: workgroups sharing one 32-row block pair of
+ *                   the Gate/Up weights (1, 2 or 4); 0 on the grouped path
+ *   gate_up_waves   route-direct: waves per Gate/Up workgroup
+ *   down_form       route-direct: 0 = K split over workgroups with a
+ *                   last-arriver sum, 1 = one workgroup per output block
+ *   down_parts      route-direct: K parts per route slot of the Down step
+ * ("perf: add small-batch route MMA for MoE", Dispatch: the fast path's
+ * launch depends on the shape.) */
+typedef struct {
+    int32_t path, gate_up_split, gate_up_waves, down_form, down_parts;
+} moe_launch_info;
+int moe_forward_launch_info(int T, int H, int I, int E, int k, int quant, int path, moe_launch_info *out);
+
 /* Layer forward ("perf: add small-batch route MMA for MoE", Motivation and
  * Summary; "Port necessary FBGEMM MoE kernels", Summary: scatter_add):
  *   out[t] = sum_j topk_weights[t,j] * FFN_{topk_ids[t,j]}(x[t])
  *   FFN_e(v) = (silu(v W_gate[e]) * (v W_up[e])) W_down[e]
  * x: bf16 [T,H]; out: bf16 [T,H], fully overwritten; routes: from moe_route
- * (same T, E, k); weights: packed by moe_pack_weights.
+ * (same T, E, k); w: the descriptor moe_pack_weights filled (its E, H, I and
+ * quant must equal the routes' E and this call's H, I and quant).
  * FP8: x is quantised on device (per-tensor: one scale amax/448 for all of x;
  * block128: per token per 128 channels; MX: per token per 32 channels, E8M0
  * scale 2^(floor(log2 amax) - 8)); the SwiGLU output h is requantised the
  * same way before Down (per-tensor: one scale for all T*k rows).
  * The combine sums the k routes of a token in a fixed order in fp32 and
  * rounds to bf16 once: repeated calls give identical bits.
- * Shapes: H % 128 == 0, I % 64 == 0 (block128: I % 128 == 0); the
- * route-direct path also needs H*elem <= 8192 bytes and I*elem <= 2048 bytes. */
-int moe_forward(const void *x, const moe_routes *routes, const void *packed_gate_up,
-                const void *packed_down, const moe_scales *scales, void *out, int H, int I,
+ * Shapes: H % 128 == 0, I % 64 == 0 (block128: I % 128 == 0); T*H < 2^31
+ * and T*k*I < 2^36 (the grouped path addresses x with 32-bit offsets and
+ * every sorted-row buffer -- h, y -- from a 64-bit base per row tile, so
+ * intermediates of many GiB are fine); the route-direct path also needs
+ * H*elem <= 8192 bytes and I*elem <= 2048 bytes.  Shapes outside these limits
+ * give MOE_ERR_UNSUPPORTED before anything is enqueued. */
+int moe_forward(const void *x, const moe_routes *routes, const moe_packed_weights *w,
+                const moe_scales *scales, void *out, int H, int I,
                 int quant, int path, void *ws, size_t ws_bytes, void *stream);
 
 /* Expert-parallel slice and shared output for moe_forward_ex ("perf: add
  * small-batch route MMA for MoE", Summary: the fast path preserves EP
  * routing and shared output).  The routes stay global (moe_route over all E
  * experts); this call holds experts [expert_begin, expert_begin +
- * num_experts) only -- packed_gate_up, packed_down and the scales cover
- * exactly those, expert expert_begin + i at index i -- and computes only the
+ * num_experts) only -- the packed weights (packed with E = num_experts) and
+ * the scales cover exactly those, expert expert_begin + i at index i -- and
+ * computes only the
  * routes to them:
  *   sum[t] = sum over j with topk_ids[t,j] in the slice of
  *            topk_weights[t,j] * FFN_{topk_ids[t,j]}(x[t])
@@ -213,8 +273,8 @@ typedef struct {
  * is moe_forward_workspace_size with the routes' E.  AUTO picks the path
  * from the routes' T, E and k as for moe_forward.  Invalid ep fields give
  * MOE_ERR_INVALID_ARG. */
-int moe_forward_ex(const void *x, const moe_routes *routes, const void *packed_gate_up,
-                   const void *packed_down, const moe_scales *scales, void *out, int H, int I,
+int moe_forward_ex(const void *x, const moe_routes *routes, const moe_packed_weights *w,
+                   const moe_scales *scales, void *out, int H, int I,
                    int quant, int path, const moe_ep *ep, void *ws, size_t ws_bytes, void *stream);
 
 /* Decode batch in one call: the routing folded into the route-direct Gate/Up
@@ -232,7 +292,7 @@ int moe_forward_ex(const void *x, const moe_routes *routes, const void *packed_g
  * MOE_ERR_UNSUPPORTED: larger batches use moe_route + moe_forward.  The
  * workspace is moe_forward_workspace_size(T, H, I, E, k, quant, path). */
 int moe_decode_forward(const float *logits, const void *x, int T, int E, int k, moe_routes *routes,
-                       const void *packed_gate_up, const void *packed_down, const moe_scales *scales, void *out,
+                       const moe_packed_weights *w, const moe_scales *scales, void *out,
                        int H, int I, int quant, int path, const moe_ep *ep, void *ws, size_t ws_bytes,
                        void *stream);
 
@@ -245,8 +305,8 @@ int moe_decode_forward(const float *logits, const void *x, int T, int E, int k, 
  * only the two handles around it).  *n_stages receives the number of launches and stage_names (may be
  * NULL) a comma-separated list of their names, e.g.
  * "init,gate_up,down,combine" for the bf16 grouped path. */
-int moe_forward_profiled(const void *x, const moe_routes *routes, const void *packed_gate_up,
-                         const void *packed_down, const moe_scales *scales, void *out, int H,
+int moe_forward_profiled(const void *x, const moe_routes *routes, const moe_packed_weights *w,
+                         const moe_scales *scales, void *out, int H,
                          int I, int quant, int path, void *ws, size_t ws_bytes, void *stream,
                          void **stage_events, int n_events, int *n_stages,
                          const char **stage_names);

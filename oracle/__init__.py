@@ -20,6 +20,8 @@ Functions and what they follow (page titles and sections):
                 weighted combine ("perf: add small-batch route MMA for MoE",
                 Summary and Motivation; "Port necessary FBGEMM MoE kernels",
                 Summary: scatter_add_dense_tokens).
+  gate_up_h  -- the SwiGLU output of listed routes (the tensor the Down-input
+                quantisation scales are taken over; same passages as forward).
   quantise_activations, e4m3_encode/decode, bf16_decode -- the FP8 per-tensor
                 and 128-channel blockwise activation quantisation and the
                 codecs ("perf: add small-batch route MMA for MoE", Summary).
@@ -77,6 +79,8 @@ def _load():
                                       i32, i32, i32, P, i32, P]
     lib.oracle_quantise_activations.restype = i32
     lib.oracle_quantise_activations.argtypes = [P, i32, i32, i32, P, P]
+    lib.oracle_gate_up_h.restype = i32
+    lib.oracle_gate_up_h.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, i32, P, ctypes.c_long, P]
     _lib = lib
     return lib
 
@@ -207,6 +211,30 @@ def quantise_activations(x_bf16, quant):
     if q == 3:
         return codes, scales.reshape(T, H // 32)
     return codes, (scales[0] if q == 1 else scales.reshape(T, H // 128))
+
+
+def gate_up_h(x_bf16, topk_ids, w_gate_up, quant="bf16", s_gate_up=None, routes=None):
+    """SwiGLU output h (float64 [n, I]) of the listed route ids r = t*k + j (all
+    T*k if None): silu(a W_gate) * (a W_up) with a the token's activation as the
+    Gate/Up projection sees it (x quantised for the FP8 formats) -- the tensor
+    the Down-input quantisation takes its scales over."""
+    q = QUANT[quant]
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    E, H2, I2 = w_gate_up.shape
+    assert H2 == H
+    I = I2 // 2
+    ids = _c(topk_ids, np.int32)
+    k = ids.shape[1]
+    wgu = _c(w_gate_up, np.uint16 if q == 0 else np.uint8)
+    sgu = None if q == 0 else _c(s_gate_up, np.uint8 if q == 3 else np.float32)
+    rt = None if routes is None else _c(routes, np.int32)
+    n = T * k if rt is None else rt.size
+    out = np.zeros((n, I), np.float64)
+    if _load().oracle_gate_up_h(_ptr(x), T, H, I, E, k, _ptr(ids), _ptr(wgu), _ptr(sgu), q, _ptr(rt), n,
+                                _ptr(out)) != 0:
+        raise ValueError("oracle_gate_up_h rejected the inputs")
+    return out
 
 
 def mx_scale_byte(amax):

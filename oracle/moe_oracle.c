@@ -536,3 +536,58 @@ int oracle_quantise_activations(const uint16_t *x, int T, int H, int quant,
     }
     return -1;
 }
+
+/*
+ * The SwiGLU output h = silu(a W_gate) * (a W_up) of the listed routes, in
+ * double, where a is the token's activation as the Gate/Up projection sees it
+ * (bf16 x, or x quantised as oracle_quantise_activations defines it) [P3
+ * Motivation: the Gate/Up GEMM, then the activation; Summary: FP8 activations
+ * before each GEMM].  This is the tensor the Down-input quantisation takes
+ * its scales over (per-tensor: amax over all routes; blockwise: per route row
+ * per 128 channels; MX: per 32), exposed so tests can derive those scales.
+ * routes: n route ids r = t*k + j (NULL: all T*k in order); out [n, I].
+ * Returns 0, or -1 on an unsupported shape or an allocation failure.
+ */
+int oracle_gate_up_h(const uint16_t *x, int T, int H, int I, int E, int k, const int32_t *ids,
+                     const void *w_gu, const float *s_gu, int quant, const int32_t *routes, long n,
+                     double *out) {
+    orc_layer L;
+    uint8_t *q_x = NULL;
+    float *scales = NULL;
+    long R = (long)T * k, ri;
+    int bad = 0;
+    if (quant < 0 || quant > 3 || T < 0) return -1;
+    if ((quant == ORC_FP8_BLOCK128 && H % 128) || (quant == ORC_FP8_MX32 && H % 32)) return -1;
+    memset(&L, 0, sizeof L);
+    L.T = T; L.H = H; L.I = I; L.E = E; L.k = k; L.quant = quant;
+    L.x = x; L.w_gu = w_gu; L.s_gu = s_gu;
+    if (quant != ORC_BF16) {
+        long ns = quant == ORC_FP8_PER_TENSOR ? 1 : quant == ORC_FP8_BLOCK128 ? (long)T * (H / 128) : 0;
+        q_x = (uint8_t *)malloc((size_t)T * H + 1);
+        /* MX scale bytes are held in a float buffer of the same byte count or more */
+        scales = (float *)malloc(sizeof(float) * (size_t)(ns > 0 ? ns : (long)T * (H / 32) / 4 + 1));
+        if (!q_x || !scales || oracle_quantise_activations(x, T, H, quant, q_x, scales) != 0) {
+            free(q_x); free(scales);
+            return -1;
+        }
+        L.q_x = q_x;
+        if (quant == ORC_FP8_PER_TENSOR) L.s_x = scales[0];
+        else if (quant == ORC_FP8_BLOCK128) L.s_x_blk = scales;
+        else L.mx_x = (const uint8_t *)scales;
+    }
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (ri = 0; ri < n; ++ri) {
+        long r = routes ? routes[ri] : ri;
+        double *a = (double *)malloc(sizeof(double) * (size_t)H);
+        double *acc = (double *)malloc(sizeof(double) * 2 * (size_t)I);
+        if (!a || !acc || r < 0 || r >= R || ids[r] < 0 || ids[r] >= E) {
+            bad |= 1;
+        } else {
+            activation(&L, (int)(r / k), a);
+            gate_up_swiglu(&L, ids[r], a, out + ri * (long)I, acc);
+        }
+        free(a); free(acc);
+    }
+    free(q_x); free(scales);
+    return bad ? -1 : 0;
+}

@@ -6,8 +6,8 @@ stream, and every step of the layer runs in the HIP kernels of
 no GPU is present, the calls raise.
 
     routes = route(logits, k)                         # top-k + grouping by expert
-    gu, dn = pack_weights(w_gate_up, w_down, quant)   # once per weight set
-    out = forward(x, routes, gu, dn, quant=..., scales=(s_gu, s_d), path="auto")
+    w = pack_weights(w_gate_up, w_down, quant)        # once per weight set
+    out = forward(x, routes, w, scales=(s_gu, s_d), path="auto")
 """
 from __future__ import annotations
 
@@ -27,9 +27,10 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_route_project_workspace_size",
             "moe_route_project", "moe_pack_weights", "moe_pack_mx_scales", "moe_select_path",
-            "moe_forward_workspace_size", "moe_forward", "moe_forward_ex", "moe_decode_forward",
-            "moe_forward_profiled",
+            "moe_forward_workspace_size", "moe_forward_workspace_views", "moe_forward_launch_info",
+            "moe_forward", "moe_forward_ex", "moe_decode_forward", "moe_forward_profiled",
             "moe_last_error"]
+PACKED_TAG = 0x4D6F4557
 
 
 class MoeError(RuntimeError):
@@ -52,6 +53,22 @@ class _CScales(ctypes.Structure):
 class _CEp(ctypes.Structure):
     _fields_ = [("expert_begin", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("accumulate", ctypes.c_int32)]
+
+
+class _CPacked(ctypes.Structure):
+    _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("E", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("quant", ctypes.c_int32),
+                ("tag", ctypes.c_uint32)]
+
+
+class _CViews(ctypes.Structure):
+    _fields_ = [("x_codes", ctypes.c_int64), ("x_scales", ctypes.c_int64), ("h_codes", ctypes.c_int64),
+                ("h_scales", ctypes.c_int64)]
+
+
+class _CLaunch(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("gate_up_split", ctypes.c_int32), ("gate_up_waves", ctypes.c_int32),
+                ("down_form", ctypes.c_int32), ("down_parts", ctypes.c_int32)]
 
 
 _lib = None
@@ -78,20 +95,24 @@ def lib():
     L.moe_route_project.argtypes = [P, P, i32, i32, i32, i32, P, ctypes.POINTER(_CRoutes), P, sz, P]
     L.moe_pack_mx_scales.restype = i32
     L.moe_pack_mx_scales.argtypes = [P, P, i32, i32, i32, P, P, P]
-    L.moe_pack_weights.argtypes = [P, P, i32, i32, i32, i32, P, P, P]
+    L.moe_pack_weights.argtypes = [P, P, i32, i32, i32, i32, P, P, ctypes.POINTER(_CPacked), P]
+    L.moe_forward_workspace_views.restype = i32
+    L.moe_forward_workspace_views.argtypes = [i32] * 7 + [ctypes.POINTER(_CViews)]
+    L.moe_forward_launch_info.restype = i32
+    L.moe_forward_launch_info.argtypes = [i32] * 7 + [ctypes.POINTER(_CLaunch)]
     L.moe_select_path.restype = i32
     L.moe_select_path.argtypes = [i32] * 7
     L.moe_forward_workspace_size.restype = sz
     L.moe_forward_workspace_size.argtypes = [i32] * 7
     L.moe_forward.restype = i32
-    L.moe_forward.argtypes = [P, ctypes.POINTER(_CRoutes), P, P, ctypes.POINTER(_CScales), P, i32,
-                              i32, i32, i32, P, sz, P]
+    L.moe_forward.argtypes = [P, ctypes.POINTER(_CRoutes), ctypes.POINTER(_CPacked), ctypes.POINTER(_CScales), P,
+                              i32, i32, i32, i32, P, sz, P]
     L.moe_forward_ex.restype = i32
-    L.moe_forward_ex.argtypes = L.moe_forward.argtypes[:10] + [ctypes.POINTER(_CEp)] + \
-        L.moe_forward.argtypes[10:]
+    L.moe_forward_ex.argtypes = L.moe_forward.argtypes[:9] + [ctypes.POINTER(_CEp)] + \
+        L.moe_forward.argtypes[9:]
     L.moe_decode_forward.restype = i32
-    L.moe_decode_forward.argtypes = [P, P, i32, i32, i32, ctypes.POINTER(_CRoutes), P, P, ctypes.POINTER(_CScales),
-                                     P, i32, i32, i32, i32, ctypes.POINTER(_CEp), P, sz, P]
+    L.moe_decode_forward.argtypes = [P, P, i32, i32, i32, ctypes.POINTER(_CRoutes), ctypes.POINTER(_CPacked),
+                                     ctypes.POINTER(_CScales), P, i32, i32, i32, i32, ctypes.POINTER(_CEp), P, sz, P]
     L.moe_forward_profiled.restype = i32
     L.moe_forward_profiled.argtypes = L.moe_forward.argtypes + [ctypes.POINTER(ctypes.c_void_p), i32,
                                                                ctypes.POINTER(ctypes.c_int),
@@ -197,7 +218,20 @@ def route_project(x: torch.Tensor, w_router: torch.Tensor, k: int, out: Routes |
     return out, logits
 
 
-def pack_weights(w_gate_up: torch.Tensor, w_down: torch.Tensor, quant: str = "bf16", stream=None):
+class PackedWeights:
+    """Expert weights re-laid by moe_pack_weights: the two packed device
+    buffers and the C descriptor (shape, format, tag) the forward calls check."""
+
+    def __init__(self, gate_up: torch.Tensor, down: torch.Tensor, desc: _CPacked):
+        self.gate_up, self.down, self.desc = gate_up, down, desc
+
+    E = property(lambda self: self.desc.E)
+    H = property(lambda self: self.desc.H)
+    I = property(lambda self: self.desc.I)
+    quant = property(lambda self: {v: k for k, v in QUANT.items()}[self.desc.quant])
+
+
+def pack_weights(w_gate_up: torch.Tensor, w_down: torch.Tensor, quant: str = "bf16", stream=None) -> PackedWeights:
     """Re-lay [E,H,2I] and [E,I,H] weights into the packed K-contiguous form (moe_pack_weights)."""
     _need_cuda(w_gate_up, "w_gate_up")
     _need_cuda(w_down, "w_down")
@@ -207,9 +241,16 @@ def pack_weights(w_gate_up: torch.Tensor, w_down: torch.Tensor, quant: str = "bf
         raise ValueError("w_down must be [E, I, H]")
     pgu = torch.empty_like(w_gate_up)
     pd = torch.empty_like(w_down)
+    desc = _CPacked()
     _check(lib().moe_pack_weights(_ptr(w_gate_up), _ptr(w_down), E, H, I, QUANT[quant], _ptr(pgu),
-                                  _ptr(pd), _stream(w_gate_up.device, stream)))
-    return pgu, pd
+                                  _ptr(pd), ctypes.byref(desc), _stream(w_gate_up.device, stream)))
+    return PackedWeights(pgu, pd, desc)
+
+
+def _need_packed(w):
+    if not isinstance(w, PackedWeights):
+        raise TypeError("weights must be the PackedWeights that pack_weights returned")
+    return w
 
 
 def pack_mx_scales(s_gate_up: torch.Tensor, s_down: torch.Tensor, stream=None):
@@ -240,8 +281,25 @@ def forward_workspace_size(T, H, I, E, k, quant="bf16", path="auto") -> int:
     return int(lib().moe_forward_workspace_size(T, H, I, E, k, QUANT[quant], PATH[path]))
 
 
-def decode_forward(logits: torch.Tensor, x: torch.Tensor, k: int, packed_gate_up: torch.Tensor,
-                   packed_down: torch.Tensor, quant: str = "bf16", scales=None, out: torch.Tensor | None = None,
+def forward_workspace_views(T, H, I, E, k, quant="bf16", path="auto") -> dict:
+    """Byte offsets into the forward workspace of the quantised x and h codes and
+    scales a call leaves there (moe_forward_workspace_views); None where absent."""
+    v = _CViews()
+    _check(lib().moe_forward_workspace_views(T, H, I, E, k, QUANT[quant], PATH[path], ctypes.byref(v)))
+    return {f: (None if getattr(v, f) < 0 else int(getattr(v, f))) for f, _ in _CViews._fields_}
+
+
+def forward_launch_info(T, H, I, E, k, quant="bf16", path="auto") -> dict:
+    """The launch shape a forward call with these arguments takes (moe_forward_launch_info)."""
+    li = _CLaunch()
+    _check(lib().moe_forward_launch_info(T, H, I, E, k, QUANT[quant], PATH[path], ctypes.byref(li)))
+    d = {f: int(getattr(li, f)) for f, _ in _CLaunch._fields_}
+    d["path"] = PATH_NAME[d["path"]]
+    return d
+
+
+def decode_forward(logits: torch.Tensor, x: torch.Tensor, k: int, weights: PackedWeights,
+                   quant: str | None = None, scales=None, out: torch.Tensor | None = None,
                    routes: Routes | None = None, path: str = "auto", workspace: torch.Tensor | None = None,
                    stream=None, expert_begin: int = 0, num_experts: int | None = None, accumulate: bool = False):
     """Routing and the route-direct layer in one call (moe_decode_forward): returns
@@ -255,9 +313,9 @@ def decode_forward(logits: torch.Tensor, x: torch.Tensor, k: int, packed_gate_up
     if x.element_size() != 2 or x.dim() != 2 or x.shape[0] != T:
         raise ValueError("x must be a bf16 [T, H] tensor with the logits' T")
     H = x.shape[1]
-    if packed_down.dim() != 3 or packed_down.shape[2] != H:
-        raise ValueError("packed_down must be [E, I, H] (the shape of the unpacked tensor)")
-    I = packed_down.shape[1]
+    w = _need_packed(weights)
+    quant = w.quant if quant is None else quant
+    I = w.I
     if accumulate and out is None:
         raise ValueError("accumulate needs the output to add into")
     routes = routes if routes is not None else Routes(T, E, k, x.device)
@@ -269,18 +327,20 @@ def decode_forward(logits: torch.Tensor, x: torch.Tensor, k: int, packed_gate_up
     cs = routes.c_struct()
     sc = _CScales(None, None) if scales is None else _CScales(scales[0].data_ptr(), scales[1].data_ptr())
     ep = _CEp(expert_begin, E - expert_begin if num_experts is None else num_experts, int(bool(accumulate)))
-    _check(lib().moe_decode_forward(_ptr(logits), _ptr(x), T, E, k, ctypes.byref(cs), _ptr(packed_gate_up),
-                                    _ptr(packed_down), ctypes.byref(sc), _ptr(out), H, I, QUANT[quant], PATH[path],
+    _check(lib().moe_decode_forward(_ptr(logits), _ptr(x), T, E, k, ctypes.byref(cs), ctypes.byref(w.desc),
+                                    ctypes.byref(sc), _ptr(out), H, I, QUANT[quant], PATH[path],
                                     ctypes.byref(ep), _ptr(workspace), workspace.numel(), _stream(x.device, stream)))
     return out, routes
 
 
-def forward(x: torch.Tensor, routes: Routes, packed_gate_up: torch.Tensor, packed_down: torch.Tensor,
-            quant: str = "bf16", scales=None, out: torch.Tensor | None = None, path: str = "auto",
+def forward(x: torch.Tensor, routes: Routes, weights: PackedWeights,
+            quant: str | None = None, scales=None, out: torch.Tensor | None = None, path: str = "auto",
             workspace: torch.Tensor | None = None, stream=None, events=None,
             expert_begin: int = 0, num_experts: int | None = None, accumulate: bool = False):
     """Layer output bf16 [T, H] (moe_forward).
 
+    weights: what pack_weights returned; quant defaults to the format they were
+    packed for (a different quant is passed through and rejected by the library).
     expert_begin / num_experts / accumulate select an expert slice and a
     shared output (moe_forward_ex): the packed weights and scales then hold
     experts [expert_begin, expert_begin + num_experts) only, the routes stay
@@ -294,9 +354,9 @@ def forward(x: torch.Tensor, routes: Routes, packed_gate_up: torch.Tensor, packe
     if x.element_size() != 2 or x.dim() != 2:
         raise ValueError("x must be a bf16 [T, H] tensor")
     T, H = x.shape
-    I = packed_down.shape[1] if packed_down.dim() == 3 else None
-    if packed_down.dim() != 3 or packed_down.shape[2] != H:
-        raise ValueError("packed_down must be [E, I, H] (the shape of the unpacked tensor)")
+    w = _need_packed(weights)
+    quant = w.quant if quant is None else quant
+    I = w.I
     if routes.T != T:
         raise ValueError("routes and x disagree on T")
     ep = None
@@ -316,11 +376,11 @@ def forward(x: torch.Tensor, routes: Routes, packed_gate_up: torch.Tensor, packe
     sc = _CScales(None, None)
     if scales is not None:
         sc = _CScales(scales[0].data_ptr(), scales[1].data_ptr())
-    args = (_ptr(x), ctypes.byref(cs), _ptr(packed_gate_up), _ptr(packed_down), ctypes.byref(sc),
+    args = (_ptr(x), ctypes.byref(cs), ctypes.byref(w.desc), ctypes.byref(sc),
             _ptr(out), H, I, QUANT[quant], PATH[path], _ptr(workspace), workspace.numel(),
             _stream(x.device, stream))
     if ep is not None:
-        _check(lib().moe_forward_ex(*args[:10], ctypes.byref(ep), *args[10:]))
+        _check(lib().moe_forward_ex(*args[:9], ctypes.byref(ep), *args[9:]))
         return out
     if events is None:
         _check(lib().moe_forward(*args))

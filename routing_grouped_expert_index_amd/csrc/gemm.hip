@@ -110,19 +110,39 @@ gemm32_kernel(const GemmArgs g) {
     // The token DMA is a buffer load (MUBUF) with the LDS bit, not the FLAT
     // global_load_lds: the compiler treats a pending FLAT access that may touch
     // LDS as completing out of order and would wait for every LDS read with
-    // lgkmcnt(0).  Offsets are bytes from A (the host keeps A below 2 GB).
-    const __amdgpu_buffer_rsrc_t arsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.A), 0, g.a_bytes, 0x00020000);
-    auto make_ap = [&](long src) __attribute__((always_inline)) {
-        return (uint32_t)(src * g.lda) + (uint32_t)(((lane & 3) ^ ((dma_r >> 2) & 3)) * 16);
+    // lgkmcnt(0).  Offsets are unsigned 32-bit byte counts from the resource's
+    // base: the gathered x as a whole (the host keeps it below 4 GiB), or, for
+    // the sorted rows of h, a base at the tile's first row (64-bit address
+    // arithmetic in scalar registers), so h may be any size.
+    auto make_arsrc = [&](int row0_) __attribute__((always_inline)) {
+        long base = 0, left = g.a_bytes;
+        if constexpr (!GATHER) {
+            base = (long)row0_ * g.lda;
+            left -= base;
+        }
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.A) + base, 0,
+                                                 (int)(uint32_t)(left < 0xffffffffL ? left : 0xffffffffL),
+                                                 0x00020000);
+    };
+    auto make_ap = [&](long src, int row0_) __attribute__((always_inline)) {
+        const long rel = GATHER ? src : src - row0_;
+        return (uint32_t)(rel * g.lda) + (uint32_t)(((lane & 3) ^ ((dma_r >> 2) & 3)) * 16);
     };
     // idle waves (past N) load a valid block, so every wave issues the same loads
     // Epilogue stores are buffer stores through a resource covering C: the
     // rows a wave must not write (tile padding, waves past N) get an offset
     // past the end, which the range check drops, so every wave issues the same
     // SX stores per tile and the K loop's waits can count them (below).
-    const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(g.C, 0, g.c_bytes, 0x00020000);
-    constexpr uint32_t kDropped = 0x80000000u;                // >= c_bytes (host: c_bytes < 2 GB)
+    // The resource starts at the tile's first output row (64-bit address
+    // arithmetic in scalar registers) and covers at most 2 GiB, so C may be any
+    // size and offset 2^31 is always past its end.
+    constexpr long EBC = EPI == EPI_SWIGLU_F32 ? 4 : (EPI == EPI_Y_BF16 || EPI == EPI_SWIGLU_BF16) ? 2 : 1;
+    auto make_crsrc = [&](int row0_) __attribute__((always_inline)) {
+        const long base = (long)row0_ * g.ldc * EBC, left = g.c_bytes - base;
+        return __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(g.C) + base, 0,
+                                                 (int)(left < 0x7fffffffL ? left : 0x7fffffffL), 0x00020000);
+    };
+    constexpr uint32_t kDropped = 0x80000000u;                // past the end of every C resource
     constexpr int CPL = EPI == EPI_SWIGLU_BF16 ? 2 : 4;       // chunks per lane and row
     constexpr int CB = 2 * CPL;                               // chunks per row segment
     constexpr int RPP = kEpiStageBytes / (CB * 16);           // staged rows per phase
@@ -206,7 +226,8 @@ gemm32_kernel(const GemmArgs g) {
     int e, row0, rows, wn0;
     decode(L, e, row0, rows, wn0);
     const long src0 = src_row(row0, rows);
-    uint32_t ap = make_ap(src0);
+    __amdgpu_buffer_rsrc_t arsrc = make_arsrc(row0);
+    uint32_t ap = make_ap(src0, row0);
     const uint8_t* wp = make_wp(e, wn0);
     const uint32_t* wsp = MX ? make_wsp(e, wn0) : nullptr;
     table(src0);
@@ -434,8 +455,12 @@ gemm32_kernel(const GemmArgs g) {
     // the first tile has no epilogue before it: SX dropped stores take its place
     // so that every tile's first steps see the same request counts
     __builtin_amdgcn_sched_barrier(0);
+    {
+        const __amdgpu_buffer_rsrc_t crsrc = make_crsrc(0);
 #pragma unroll
-    for (int i = 0; i < SX; ++i) __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, crsrc, kDropped, 0, 0);
+        for (int i = 0; i < SX; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, crsrc, kDropped, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     for (;;) {
         // the next tile's indices are loaded now; their latency hides under this
@@ -501,13 +526,21 @@ gemm32_kernel(const GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         // (after the last tile the requests repeat this tile's valid data: an
         // unconditional prologue keeps the loop's wait counts exact)
-        const uint32_t nap = more ? make_ap(nsrc) : ap;
+        if (!GATHER && more) arsrc = make_arsrc(nrow0);   // (the DMAs of this tile are all issued)
+        const uint32_t nap = more ? make_ap(nsrc, nrow0) : ap;
         const uint8_t* nwp = more ? make_wp(ne, nwn0) : wp;
         const uint32_t* nwsp = MX && more ? make_wsp(ne, nwn0) : wsp;
         prologue(nap, nwp, nwsp);
         __builtin_amdgcn_sched_barrier(0);
 
         // ------------------------------------------------------------ epilogue
+        // (output offsets count from this tile's first row; the lane index is
+        // taken through an opaque copy so that the offsets are computed here,
+        // not hoisted out of the tile loop to occupy registers in the K loop)
+        const __amdgpu_buffer_rsrc_t crsrc = make_crsrc(row0);
+        int lane_e = lane;
+        __asm__ volatile("" : "+v"(lane_e));
+        const int j_e = lane_e & 31;
         // acc[f][m][i]: token row 32m + j, packed row wn0 + 32f + 8(i/4) + 4hh + i%4.
         // Each lane holds CPL 16-byte chunks of one output row segment per m:
         //   Y (bf16):       columns wn0 + 32hh + 16f + 8hv + [0,8)  -> chunk 4hh + 2f + hv
@@ -554,7 +587,7 @@ gemm32_kernel(const GemmArgs g) {
                 const bool ok = live && r < rows;
                 const uint32_t orow = (uint32_t)(row0 + r);
                 __builtin_amdgcn_raw_buffer_store_b128(
-                    q, crsrc, ok ? orow * (uint32_t)g.ldc + (uint32_t)hc0 : kDropped, 0, 0);
+                    q, crsrc, ok ? (uint32_t)(32 * m + j_e) * (uint32_t)g.ldc + (uint32_t)hc0 : kDropped, 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b8(
                     (uint8_t)b, qsrc, ok && hh == 0 ? orow * (uint32_t)nbh + (uint32_t)spos : kDropped, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -611,7 +644,7 @@ gemm32_kernel(const GemmArgs g) {
                 const bool ok = live && r < rows;
                 const uint32_t orow = (uint32_t)(row0 + r);
                 __builtin_amdgcn_raw_buffer_store_b128(
-                    q, crsrc, ok ? orow * (uint32_t)g.ldc + (uint32_t)hc0 : kDropped, 0, 0);
+                    q, crsrc, ok ? (uint32_t)(32 * m + j_e) * (uint32_t)g.ldc + (uint32_t)hc0 : kDropped, 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b32(
                     __float_as_uint(sc), qsrc,
                     ok && hh == 0 && (wave & 3) == 0 ? (orow * (uint32_t)nbh + (uint32_t)hb) * 4u : kDropped, 0, 0);
@@ -626,7 +659,7 @@ gemm32_kernel(const GemmArgs g) {
             constexpr int CE = 16 / EB;                                  // elements per chunk
             const int c0 = EPI == EPI_Y_BF16 ? wn0 : wn0 / 2;
             const uint32_t lane_off =
-                ((uint32_t)(row0 + lane / CB) * (uint32_t)g.ldc + (uint32_t)(c0 + CE * (lane % CB))) * EB;
+                ((uint32_t)(lane_e / CB) * (uint32_t)g.ldc + (uint32_t)(c0 + CE * (lane_e % CB))) * EB;
             const int rlim = wn0 < g.N ? rows - lane / CB : 0;
             const uint32_t row_bytes = (uint32_t)g.ldc * EB;
             // XOR swizzle of the chunk position: the 8 lanes an LDS cycle serves
@@ -744,8 +777,10 @@ static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st) {
             return hipErrorInvalidValue;
         lds += (size_t)((KT + 3) / 4) * 4 * g32::BM * sizeof(uint32_t);
     }
-    // 32-bit buffer offsets; C also keeps 0x80000000 free as the dropped-store offset
-    if (a.a_bytes <= 0 || a.a_bytes > 0x7fffffffL || a.c_bytes <= 0 || a.c_bytes > 0x7fffffffL)
+    // 32-bit offsets into the gathered x (Gate/Up); h and y are addressed from a
+    // base per row tile, so only a row's offsets need 32 bits
+    if (a.a_bytes <= 0 || (GATHER && a.a_bytes > 0xffffffffL) || a.c_bytes <= 0 ||
+        a.lda * g32::BM > 0x7fffffffL || a.ldc * g32::BM * 4 > 0x7fffffffL)
         return hipErrorInvalidValue;
     const long total_bound = (long)a.max_tiles * ((a.N + g32::BN - 1) / g32::BN);
     long grid = std::min<long>(total_bound, (long)gemm_num_cus());

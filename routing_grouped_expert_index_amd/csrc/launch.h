@@ -105,5 +105,10 @@ hipError_t launch_route_direct_gate_up(const FwdPlan& p, hipStream_t st);
 // (slot, K part) items of one route-direct Down output block
 int rd_down_items(int T, int H, int I, int k, int quant);
 hipError_t launch_route_direct_down(const FwdPlan& p, hipStream_t st);
+// the route-direct launch shape for a call (host-only)
+struct RdLaunchInfo {
+    int gu_split, gu_waves, down_form, down_parts;
+};
+RdLaunchInfo rd_launch_info(int T, int H, int I, int k, int quant);
 
 }  // namespace moe

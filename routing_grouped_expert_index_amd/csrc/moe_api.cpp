@@ -58,6 +58,11 @@ int check_shape(int T, int H, int I, int E, int k, int quant) {
     if (quant < MOE_BF16 || quant > MOE_FP8_MX32) return fail(MOE_ERR_INVALID_ARG, "unknown quant %d", quant);
     if ((long)T * k >= (1L << 31) || (long)T * H >= (1L << 31))
         return fail(MOE_ERR_UNSUPPORTED, "T*k and T*H must fit in int32");
+    // The grouped GEMMs address the gathered x (at most 4 GiB when T*H < 2^31)
+    // and the per-row scale tables with 32-bit offsets; h and y are addressed
+    // from a 64-bit base per row tile, so their size is not limited here.
+    if ((long)T * k * I >= (1L << 36))
+        return fail(MOE_ERR_UNSUPPORTED, "T*k*I = %ld must be below 2^36", (long)T * k * I);
     if (H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "H=%d: H must be a multiple of 128", H);
     if (I % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "I=%d: I must be a multiple of 64", I);
     if (quant == MOE_FP8_BLOCK128 && I % 128 != 0)
@@ -103,15 +108,17 @@ Layout layout(int T, int H, int I, int E, int k, int quant, int path) {
     L.ntiles = take(grouped ? sizeof(int32_t) : 0);
     L.amax = take(2 * sizeof(uint32_t));
     L.scal = take(2 * sizeof(float));
-    L.xq = take(grouped && quant != MOE_BF16 ? (size_t)T * H : 0);
-    L.sx = take(grouped && quant == MOE_FP8_BLOCK128 ? sizeof(float) * (size_t)T * (H / 128)
+    // (route-direct: the Gate/Up kernel leaves the codes of each token's x row
+    // here too, for inspection; it reads them from LDS)
+    L.xq = take(quant != MOE_BF16 ? (size_t)T * H : 0);
+    L.sx = take(quant == MOE_FP8_BLOCK128 ? sizeof(float) * (size_t)T * (H / 128)
                 : grouped && quant == MOE_FP8_MX32 ? (size_t)T * (H / 32) : 0);
     size_t hbytes = 0;
     if (quant == MOE_BF16) hbytes = R * I * 2;
     else if (quant == MOE_FP8_PER_TENSOR || !grouped) hbytes = R * I * 4;
     L.h = take(hbytes);
     L.hq = take(grouped && quant != MOE_BF16 ? R * I : 0);
-    L.sh = take(grouped && quant == MOE_FP8_BLOCK128 ? sizeof(float) * R * (I / 128)
+    L.sh = take(quant == MOE_FP8_BLOCK128 ? sizeof(float) * R * (I / 128)
                 : grouped && quant == MOE_FP8_MX32 ? R * (I / 32) : 0);
     L.y = take(grouped ? R * H * 2 : 0);
     const size_t rd_blocks = grouped ? 0 : (size_t)T * (H / 32);
@@ -213,8 +220,8 @@ int moe_route_project(const void* x, const float* w_router, int T, int H, int E,
     return rc == MOE_OK ? ok() : rc;
 }
 
-int moe_pack_weights(const void* w_gate_up, const void* w_down, int E, int H, int I, int quant,
-                     void* packed_gate_up, void* packed_down, void* stream) {
+static int pack_weights_impl(const void* w_gate_up, const void* w_down, int E, int H, int I, int quant,
+                             void* packed_gate_up, void* packed_down, void* stream) {
     if (E < 1 || E > moe::kMaxExperts || H <= 0 || I <= 0)
         return fail(MOE_ERR_INVALID_ARG, "bad sizes E=%d H=%d I=%d", E, H, I);
     if (quant < MOE_BF16 || quant > MOE_FP8_MX32) return fail(MOE_ERR_INVALID_ARG, "unknown quant %d", quant);
@@ -238,6 +245,22 @@ int moe_pack_weights(const void* w_gate_up, const void* w_down, int E, int H, in
     if (rc != MOE_OK) return rc;
     rc = hip_status(moe::launch_pack_down(w_down, packed_down, E, H, I, elem, st), "pack down");
     return rc == MOE_OK ? ok() : rc;
+}
+
+int moe_pack_weights(const void* w_gate_up, const void* w_down, int E, int H, int I, int quant,
+                     void* packed_gate_up, void* packed_down, moe_packed_weights* packed, void* stream) {
+    if (!packed) return fail(MOE_ERR_INVALID_ARG, "packed (the descriptor to fill) is NULL");
+    packed->tag = 0;
+    const int rc = pack_weights_impl(w_gate_up, w_down, E, H, I, quant, packed_gate_up, packed_down, stream);
+    if (rc != MOE_OK) return rc;
+    packed->gate_up = packed_gate_up;
+    packed->down = packed_down;
+    packed->E = E;
+    packed->H = H;
+    packed->I = I;
+    packed->quant = quant;
+    packed->tag = MOE_PACKED_TAG;
+    return ok();
 }
 
 int moe_pack_mx_scales(const uint8_t* s_gate_up, const uint8_t* s_down, int E, int H, int I,
@@ -273,8 +296,43 @@ size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int quant, 
     return layout(T, H, I, E, k, quant, p).total;
 }
 
-static int forward_impl(const void* x, const moe_routes* routes, const void* packed_gate_up,
-                        const void* packed_down, const moe_scales* scales, void* out, int H, int I,
+int moe_forward_workspace_views(int T, int H, int I, int E, int k, int quant, int path, moe_ws_views* out) {
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    out->x_codes = out->x_scales = out->h_codes = out->h_scales = -1;
+    int rc = check_shape(T, H, I, E, k, quant);
+    if (rc != MOE_OK) return rc;
+    const int p = resolve_path(T, H, I, E, k, quant, path);
+    if (p < 0) return p;
+    if (quant == MOE_BF16) return ok();
+    const Layout L = layout(T, H, I, E, k, quant, p);
+    auto off = [](size_t v) { return v == (size_t)-1 ? (int64_t)-1 : (int64_t)v; };
+    out->x_codes = off(L.xq);
+    out->x_scales = quant == MOE_FP8_PER_TENSOR ? off(L.scal) : off(L.sx);
+    out->h_codes = p == MOE_PATH_GROUPED ? off(L.hq) : -1;
+    out->h_scales = quant == MOE_FP8_PER_TENSOR ? off(L.scal) + (int64_t)sizeof(float) : off(L.sh);
+    return ok();
+}
+
+int moe_forward_launch_info(int T, int H, int I, int E, int k, int quant, int path, moe_launch_info* out) {
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    *out = moe_launch_info{};
+    int rc = check_shape(T, H, I, E, k, quant);
+    if (rc != MOE_OK) return rc;
+    const int p = resolve_path(T, H, I, E, k, quant, path);
+    if (p < 0) return p;
+    out->path = p;
+    if (p == MOE_PATH_ROUTE_DIRECT) {
+        const moe::RdLaunchInfo li = moe::rd_launch_info(T, H, I, k, quant);
+        out->gate_up_split = li.gu_split;
+        out->gate_up_waves = li.gu_waves;
+        out->down_form = li.down_form;
+        out->down_parts = li.down_parts;
+    }
+    return ok();
+}
+
+static int forward_impl(const void* x, const moe_routes* routes, const moe_packed_weights* w,
+                        const moe_scales* scales, void* out, int H, int I,
                         int quant, int path, const moe_ep* ep, void* ws, size_t ws_bytes, void* stream,
                         void** events, int n_events, int* n_stages, const char** stage_names,
                         const float* logits = nullptr) {
@@ -286,6 +344,14 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
     if (e0 < 0 || nloc < 1 || (long)e0 + nloc > E || (acc != 0 && acc != 1))
         return fail(MOE_ERR_INVALID_ARG, "expert slice [%d, %d+%d) must lie in [0, %d) and accumulate be 0 or 1",
                     e0, e0, nloc, E);
+    // the packed weights must be the descriptor moe_pack_weights filled, for
+    // this call's experts, shape and format (checked before anything launches)
+    if (w && w->tag != MOE_PACKED_TAG)
+        return fail(MOE_ERR_INVALID_ARG, "w was not filled by moe_pack_weights");
+    if (w && (w->E != nloc || w->H != H || w->I != I || w->quant != quant))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "weights packed for E=%d H=%d I=%d quant=%d, but the call has E=%d H=%d I=%d quant=%d",
+                    w->E, w->H, w->I, w->quant, nloc, H, I, quant);
     const int p = resolve_path(T, H, I, E, k, quant, path);
     if (p < 0) return p;
     if (logits && p != MOE_PATH_ROUTE_DIRECT)
@@ -296,6 +362,9 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
         if (stage_names) *stage_names = "";
         return ok();
     }
+    if (!w) return fail(MOE_ERR_INVALID_ARG, "w (the packed weights) is NULL");
+    const void* packed_gate_up = w->gate_up;
+    const void* packed_down = w->down;
     if (!x || !out || !packed_gate_up || !packed_down || !routes->topk_ids || !routes->topk_weights)
         return fail(MOE_ERR_INVALID_ARG, "null pointer among x / out / weights / routes");
     if (p == MOE_PATH_GROUPED && (!routes->expert_offsets || !routes->perm || !routes->route_pos))
@@ -384,22 +453,22 @@ static int forward_impl(const void* x, const moe_routes* routes, const void* pac
     return ok();
 }
 
-int moe_forward(const void* x, const moe_routes* routes, const void* packed_gate_up,
-                const void* packed_down, const moe_scales* scales, void* out, int H, int I,
+int moe_forward(const void* x, const moe_routes* routes, const moe_packed_weights* w,
+                const moe_scales* scales, void* out, int H, int I,
                 int quant, int path, void* ws, size_t ws_bytes, void* stream) {
-    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, nullptr, ws,
+    return forward_impl(x, routes, w, scales, out, H, I, quant, path, nullptr, ws,
                         ws_bytes, stream, nullptr, 0, nullptr, nullptr);
 }
 
-int moe_forward_ex(const void* x, const moe_routes* routes, const void* packed_gate_up,
-                   const void* packed_down, const moe_scales* scales, void* out, int H, int I,
+int moe_forward_ex(const void* x, const moe_routes* routes, const moe_packed_weights* w,
+                   const moe_scales* scales, void* out, int H, int I,
                    int quant, int path, const moe_ep* ep, void* ws, size_t ws_bytes, void* stream) {
-    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, ep, ws,
+    return forward_impl(x, routes, w, scales, out, H, I, quant, path, ep, ws,
                         ws_bytes, stream, nullptr, 0, nullptr, nullptr);
 }
 
 int moe_decode_forward(const float* logits, const void* x, int T, int E, int k, moe_routes* routes,
-                       const void* packed_gate_up, const void* packed_down, const moe_scales* scales, void* out,
+                       const moe_packed_weights* w, const moe_scales* scales, void* out,
                        int H, int I, int quant, int path, const moe_ep* ep, void* ws, size_t ws_bytes,
                        void* stream) {
     if (!routes) return fail(MOE_ERR_INVALID_ARG, "routes is NULL");
@@ -407,17 +476,17 @@ int moe_decode_forward(const float* logits, const void* x, int T, int E, int k, 
     routes->T = T;
     routes->E = E;
     routes->k = k;
-    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, ep, ws, ws_bytes,
+    return forward_impl(x, routes, w, scales, out, H, I, quant, path, ep, ws, ws_bytes,
                         stream, nullptr, 0, nullptr, nullptr, logits ? logits : nullptr);
 }
 
-int moe_forward_profiled(const void* x, const moe_routes* routes, const void* packed_gate_up,
-                         const void* packed_down, const moe_scales* scales, void* out, int H, int I,
+int moe_forward_profiled(const void* x, const moe_routes* routes, const moe_packed_weights* w,
+                         const moe_scales* scales, void* out, int H, int I,
                          int quant, int path, void* ws, size_t ws_bytes, void* stream,
                          void** stage_events, int n_events, int* n_stages, const char** stage_names) {
     if (n_events < 0 || (n_events > 0 && !stage_events))
         return fail(MOE_ERR_INVALID_ARG, "stage_events must hold n_events handles");
-    return forward_impl(x, routes, packed_gate_up, packed_down, scales, out, H, I, quant, path, nullptr, ws,
+    return forward_impl(x, routes, w, scales, out, H, I, quant, path, nullptr, ws,
                         ws_bytes, stream, stage_events, n_events, n_stages, stage_names);
 }
 

@@ -433,13 +433,21 @@ router_project_kernel(const RpArgs a) {
                         __hip_atomic_store(a.part + ((size_t)ks * T + t) * E + e, acc[tt][i], __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
                 }
+            // partial stores, vmcnt(0), then the ticket: agent-scope atomic
+            // stores are acknowledged by the device-coherent level, so once the
+            // wait returns they are visible to the agent-scope loads of whichever
+            // workgroup draws the last ticket; the signal fences keep the
+            // compiler from moving either memory operation across the wait
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0)
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
             if (lane == 0)
                 last_s = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                          (int)(gridDim.x * gridDim.y) - 1;
         }
         __syncthreads();
         if (!last_s) return;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the partial loads stay after the ticket
         // the last workgroup: all partials into LDS at once (8 requests per thread
         // in flight, clamped indices, masked after), the scores added in ks order
         // into LDS and the output, then the routing

@@ -71,6 +71,13 @@ struct RdArgs {
     int32_t* ids_w;
     float* tw_w;
     int acc;                 // out += the layer sum (else out = it)
+    // FP8 inspection copies in the workspace (null for bf16): each token's x
+    // codes [T][H] and block scales [T][H/128]; per-tensor x and h scales
+    // (scal_out[0], scal_out[1]); blockwise h scales [R][I/128] in route order
+    uint8_t* xq_out;
+    float* sx_out;
+    float* scal_out;
+    float* sh_out;
 };
 
 // 8 values from 16 bytes of bf16
@@ -308,7 +315,12 @@ rd_gate_up_kernel(const RdArgs a) {
         wu = wg + gstride;
         return true;
     };
-    if (!from_logits && !resolve(a.ids[r])) return;
+    // FP8: the workgroup (slot 0, h block 0, split 0) of each token also leaves
+    // the token's codes and scales in the workspace (it runs even when its own
+    // expert lies outside this call's slice)
+    const bool writer = FP8 && a.xq_out != nullptr && G == 0 && rs == 0 && r == t * a.k;
+    const bool mine = from_logits || resolve(a.ids[r]);
+    if (!mine && !writer) return;
 
     // two load buffers: batch b+1 is requested before batch b is computed
     u32x4 vg[2][U][2], vu[2][U][2];
@@ -326,7 +338,7 @@ rd_gate_up_kernel(const RdArgs a) {
     };
     std::integral_constant<int, 0> B0;
     std::integral_constant<int, 1> B1;
-    if (!from_logits) load_batch(B0, s0);   // the weight stream starts before the activation row is staged
+    if (!from_logits && mine) load_batch(B0, s0);   // the weight stream starts before the activation row is staged
 
     float xs = 1.0f;
     const uint16_t* x = reinterpret_cast<const uint16_t*>(a.act);
@@ -339,9 +351,21 @@ rd_gate_up_kernel(const RdArgs a) {
         stage_row<NW>(xrow, a.act + (long)t * Kb, Kb);
     }
     __syncthreads();
+    if (writer) {
+        uint8_t* xq = a.xq_out + (long)t * a.H;
+        for (int i = threadIdx.x * 16; i < a.H; i += 64 * NW * 16)
+            *reinterpret_cast<u32x4*>(xq + i) = *reinterpret_cast<const u32x4*>(xrow + i);
+        if constexpr (Q == RD_BLOCK) {
+            for (int i = threadIdx.x; i < a.H / 128; i += 64 * NW) a.sx_out[(long)t * (a.H / 128) + i] = sxs[i];
+        } else {
+            if (t == 0 && threadIdx.x == 0) a.scal_out[0] = xs;
+        }
+    }
     if (from_logits) {   // the expert wave 0 published; then the weight stream
         if (!resolve(__builtin_amdgcn_readfirstlane(s_eg))) return;
         load_batch(B0, s0);
+    } else if (!mine) {
+        return;
     }
     int cg = 0, cu = 0;           // blockwise: scale columns of the gate and up blocks
     if constexpr (Q == RD_BLOCK) {
@@ -455,12 +479,22 @@ __device__ __forceinline__ void rd_part_publish(const RdArgs& a, int tb, int t, 
     float* part = a.part + (long)tb * items * 32;
     if (wave == 0) {
         if (hh == 0) __hip_atomic_store(part + it * 32 + lane, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // Order: partial stores, then vmcnt(0) (the stores are acknowledged by
+        // the device-coherent level: agent-scope atomic stores bypass the
+        // non-coherent caches), then the ticket.  The signal fences keep the
+        // compiler from moving either memory operation across the wait; the
+        // hardware completes the stores before the wait returns, so any
+        // workgroup that draws the last ticket finds every partial in memory
+        // (its loads are agent-scope atomics too, read at that same level).
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (lane == 0)
             last_s = __hip_atomic_fetch_add(a.cnt + tb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == items - 1;
     }
     __syncthreads();
     if (!last_s) return;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the partial loads stay after the ticket
     if (wave == 0 && hh == 0) {
         float o = 0.0f;
         for (int i = 0; i < items; ++i)   // fixed order
@@ -534,11 +568,14 @@ rd_down_part_kernel(const RdArgs a) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) m = fmaxf(m, red[w][0]);
         hs = scale_from_amax(m);
+        if (tb == 0 && threadIdx.x == 0) a.scal_out[1] = hs;   // (inspection copy; every writer stores the same value)
         quant_row<float, NW>(hrow_s, reinterpret_cast<const float*>(a.h) + (long)r * a.I, a.I, hs);
         __syncthreads();
     } else if constexpr (Q == RD_BLOCK) {   // the route's h row per 128 channels, here
         quant_row_block128<float, NW>(hrow_s, shs, reinterpret_cast<const float*>(a.h) + (long)r * a.I, a.I);
         __syncthreads();
+        if (g32 == 0 && kp == 0)   // inspection copy of the route's h scales
+            for (int i = threadIdx.x; i < a.I / 128; i += 64 * NW) a.sh_out[(long)r * (a.I / 128) + i] = shs[i];
     }
 
     float y = 0.0f;
@@ -623,6 +660,7 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
             for (int q = 0; q < 8; ++q) m = base + lane + 64 * q < nmax ? fmaxf(m, mv[q]) : m;
         }
         hs = scale_from_amax(wave_max(m));
+        if (blockIdx.x == 0 && threadIdx.x == 0) a.scal_out[1] = hs;   // inspection copy
     }
     for (int it = wave; it < items; it += nw) {
         const int jj = it / KP, kp = it - jj * KP;
@@ -730,6 +768,10 @@ static RdArgs rd_args(const FwdPlan& p) {
     a.logits = p.logits;
     a.ids_w = p.ids_w;
     a.tw_w = p.tw_w;
+    a.xq_out = p.xq;
+    a.sx_out = p.sx;
+    a.scal_out = p.scal;
+    a.sh_out = p.sh;
     return a;
 }
 
@@ -950,6 +992,22 @@ static RdBlockCfg rd_block_cfg(int H, int I, int k, int quant) {
     c.ok = true;
     (void)H;
     return c;
+}
+
+RdLaunchInfo rd_launch_info(int T, int H, int I, int k, int quant) {
+    RdLaunchInfo li{};
+    const RdGuCfg c = rd_gu_cfg(T, H, I, k, quant);
+    li.gu_split = c.rs;
+    li.gu_waves = c.nw;
+    const RdBlockCfg bc = rd_block_cfg(H, I, k, quant);
+    if (bc.ok) {
+        li.down_form = 1;
+        li.down_parts = bc.kp;
+    } else {
+        li.down_form = 0;
+        li.down_parts = rd_down_cfg(T, H, I, k, quant).kp;
+    }
+    return li;
 }
 
 hipError_t launch_route_direct_down(const FwdPlan& p, hipStream_t st) {

@@ -34,10 +34,10 @@ def weights_dev(w: dict, quant: str):
         scales = (torch.from_numpy(w["s_gate_up"]).to(DEV), torch.from_numpy(w["s_down"]).to(DEV))
         if quant == "fp8_mx32":
             scales = moe.pack_mx_scales(*scales)
-    pgu, pd = moe.pack_weights(gu, dn, quant)
+    pw = moe.pack_weights(gu, dn, quant)
     torch.cuda.synchronize()
     del gu, dn
-    return pgu, pd, scales
+    return pw, scales
 
 
 @functools.lru_cache(maxsize=1)
@@ -47,9 +47,9 @@ def workload_dev(name: str):
 
 
 def run(x_bits, logits, k, dev_w, quant, path="auto"):
-    pgu, pd, scales = dev_w
+    pw, scales = dev_w
     r = moe.route(torch.from_numpy(np.ascontiguousarray(logits)).to(DEV), k)
-    out = moe.forward(bf16_dev(x_bits), r, pgu, pd, quant=quant, scales=scales, path=path)
+    out = moe.forward(bf16_dev(x_bits), r, pw, quant=quant, scales=scales, path=path)
     torch.cuda.synchronize()
     return r, out
 
@@ -97,3 +97,43 @@ def oracle_out(x_bits, ref_routes, w, quant, tokens=None):
 __all__ = ["DEV", "say", "bf16_dev", "weights_dev", "workload_dev", "run", "routes_np", "check_routing",
            "check_out", "oracle_out", "metrics", "random_activations", "random_weights", "workload_inputs",
            "workload_weights", "WORKLOADS", "oracle", "moe"]
+
+
+def tile_cover_tokens(ref_routes: dict, k: int, bm: int = 128, blk: int = 32) -> np.ndarray:
+    """Tokens whose outputs, compared in full, check at least one row of every
+    32-row MFMA block of every 128-row tile of the grouped GEMMs' tile map (each
+    expert's tiles start at its offset), plus the first and last sorted row of
+    every expert.  A token covers the blocks its k routes' sorted positions fall
+    in.  Greedy: experts' first and last rows first, then the last row of every
+    block not yet covered."""
+    off = ref_routes["expert_offsets"].astype(np.int64)
+    perm = ref_routes["perm"].astype(np.int64)
+    route_pos = ref_routes["route_pos"].astype(np.int64)
+    starts = []
+    for e in range(len(off) - 1):
+        for r0 in range(off[e], off[e + 1], bm):
+            starts.extend(range(r0, min(r0 + bm, off[e + 1]), blk))
+    starts = np.array(starts, np.int64)
+    if starts.size == 0:
+        return np.zeros(0, np.int32)
+    ends = np.append(starts[1:], off[-1])
+    covered = np.zeros(starts.size, bool)
+    chosen = []
+
+    def take(pos):
+        t = int(perm[pos] // k)
+        chosen.append(t)
+        covered[np.searchsorted(starts, route_pos[t * k:(t + 1) * k], side="right") - 1] = True
+
+    for e in range(len(off) - 1):
+        if off[e + 1] > off[e]:
+            take(off[e])
+            take(off[e + 1] - 1)
+    for b in range(starts.size):
+        if not covered[b]:
+            take(ends[b] - 1)
+    assert covered.all()
+    return np.unique(np.array(chosen, np.int32))
+
+
+__all__.append("tile_cover_tokens")

@@ -14,12 +14,12 @@ pytestmark = pytest.mark.gpu
 
 
 def _both(x_bits, lg, k, dev_w, quant, **kw):
-    pgu, pd, sc = dev_w
+    pw, sc = dev_w
     x = bf16_dev(x_bits)
     lgd = torch.from_numpy(np.ascontiguousarray(lg)).to(DEV)
     r = moe.route(lgd, k)
-    ref = moe.forward(x, r, pgu, pd, quant=quant, scales=sc, path="route_direct", **kw)
-    out, rf = moe.decode_forward(lgd, x, k, pgu, pd, quant=quant, scales=sc, path="route_direct", **kw)
+    ref = moe.forward(x, r, pw, quant=quant, scales=sc, path="route_direct", **kw)
+    out, rf = moe.decode_forward(lgd, x, k, pw, quant=quant, scales=sc, path="route_direct", **kw)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "fused output differs from route + forward"
     assert torch.equal(rf.topk_ids, r.topk_ids)
@@ -81,12 +81,12 @@ def test_decode_fused_expert_slice_accumulate():
     start = torch.randn((T, H), device=DEV).to(torch.bfloat16)
     o1 = start.clone()
     o2 = start.clone()
-    pgu, pd, _ = weights_dev(ws, "bf16")
+    pw, _ = weights_dev(ws, "bf16")
     lgd = torch.from_numpy(a["logits"]).to(DEV)
     r = moe.route(lgd, k)
-    moe.forward(bf16_dev(a["x"]), r, pgu, pd, out=o1, path="route_direct", expert_begin=e0, num_experts=n,
+    moe.forward(bf16_dev(a["x"]), r, pw, out=o1, path="route_direct", expert_begin=e0, num_experts=n,
                 accumulate=True)
-    moe.decode_forward(lgd, bf16_dev(a["x"]), k, pgu, pd, out=o2, path="route_direct", expert_begin=e0,
+    moe.decode_forward(lgd, bf16_dev(a["x"]), k, pw, out=o2, path="route_direct", expert_begin=e0,
                        num_experts=n, accumulate=True)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
@@ -94,13 +94,13 @@ def test_decode_fused_expert_slice_accumulate():
 
 def test_decode_fused_rejects_grouped_and_empty_batch():
     w = random_weights(4, 128, 64, "bf16", seed=520)
-    pgu, pd, _ = weights_dev(w, "bf16")
+    pw, _ = weights_dev(w, "bf16")
     x = torch.zeros((40, 128), dtype=torch.bfloat16, device=DEV)
     lg = torch.zeros((40, 4), dtype=torch.float32, device=DEV)
     with pytest.raises(moe.MoeError):
-        moe.decode_forward(lg, x, 2, pgu, pd)               # AUTO picks grouped for 80 routes over 4 experts
+        moe.decode_forward(lg, x, 2, pw)               # AUTO picks grouped for 80 routes over 4 experts
     out, r = moe.decode_forward(torch.zeros((0, 4), device=DEV), torch.zeros((0, 128), dtype=torch.bfloat16,
-                                device=DEV), 2, pgu, pd, path="route_direct")
+                                device=DEV), 2, pw, path="route_direct")
     torch.cuda.synchronize()
     assert out.shape == (0, 128)
 
@@ -111,7 +111,7 @@ def test_decode_fused_graph_replay():
     name = "decode_fp8_tensor"
     wl = WORKLOADS[name]
     a = workload_inputs(name, batch=3)
-    pgu, pd, sc = workload_dev(name)
+    pw, sc = workload_dev(name)
     x = bf16_dev(a["x"])
     lg = torch.from_numpy(a["logits"]).to(DEV)
     T = x.shape[0]
@@ -121,7 +121,7 @@ def test_decode_fused_graph_replay():
                      device=DEV)
 
     def step():
-        moe.decode_forward(lg, x, wl.k, pgu, pd, quant=wl.quant, scales=sc, out=out, routes=routes, workspace=ws)
+        moe.decode_forward(lg, x, wl.k, pw, quant=wl.quant, scales=sc, out=out, routes=routes, workspace=ws)
 
     step()
     torch.cuda.synchronize()

@@ -54,9 +54,9 @@ def test_ep_slices_and_shared_output(T, H, I, quant, path):
     total = np.zeros((T, H))
     for e0, n in SLICES:
         w_s = _slice_w(w, e0, n)
-        pgu, pd, sc = weights_dev(w_s, quant)
-        got = moe.forward(x, r, pgu, pd, quant=quant, scales=sc, path=path, expert_begin=e0, num_experts=n)
-        moe.forward(x, r, pgu, pd, quant=quant, scales=sc, out=shared, path=path, expert_begin=e0,
+        pw, sc = weights_dev(w_s, quant)
+        got = moe.forward(x, r, pw, quant=quant, scales=sc, path=path, expert_begin=e0, num_experts=n)
+        moe.forward(x, r, pw, quant=quant, scales=sc, out=shared, path=path, expert_begin=e0,
                     num_experts=n, accumulate=True)
         torch.cuda.synchronize()
         ref = _oracle_slice(a["x"], ref_r, w_s, quant, e0)
@@ -75,11 +75,11 @@ def test_ep_full_slice_equals_layer(path):
     T, H, I, E, k = 5, 512, 256, 16, 4
     a = random_activations(T, H, E, seed=310)
     w = random_weights(E, H, I, "fp8_per_tensor", seed=311)
-    pgu, pd, sc = weights_dev(w, "fp8_per_tensor")
+    pw, sc = weights_dev(w, "fp8_per_tensor")
     r, _ = _routes(a["logits"], k)
     x = bf16_dev(a["x"])
-    o1 = moe.forward(x, r, pgu, pd, quant="fp8_per_tensor", scales=sc, path=path)
-    o2 = moe.forward(x, r, pgu, pd, quant="fp8_per_tensor", scales=sc, path=path, expert_begin=0,
+    o1 = moe.forward(x, r, pw, quant="fp8_per_tensor", scales=sc, path=path)
+    o2 = moe.forward(x, r, pw, quant="fp8_per_tensor", scales=sc, path=path, expert_begin=0,
                      num_experts=E)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
@@ -94,12 +94,12 @@ def test_ep_accumulate_onto_existing_output(path):
     a = random_activations(T, H, E, seed=320)
     w = random_weights(E, H, I, "bf16", seed=321)
     w_s = _slice_w(w, e0, n)
-    pgu, pd, _ = weights_dev(w_s, "bf16")
+    pw, _ = weights_dev(w_s, "bf16")
     r, ref_r = _routes(a["logits"], k)
     rng = np.random.default_rng(322)
     start = to_bf16_bits(rng.normal(0.0, 0.05, (T, H)).astype(np.float32))
     out = bf16_dev(start)
-    moe.forward(bf16_dev(a["x"]), r, pgu, pd, out=out, path=path, expert_begin=e0, num_experts=n,
+    moe.forward(bf16_dev(a["x"]), r, pw, out=out, path=path, expert_begin=e0, num_experts=n,
                 accumulate=True)
     torch.cuda.synchronize()
     ref = bf16_bits_to_f32(start).astype(np.float64) + _oracle_slice(a["x"], ref_r, w_s, "bf16", e0)
@@ -117,15 +117,15 @@ def test_ep_slice_without_routes(quant, path):
     lg = a["logits"].copy()
     lg[:, :k] += 50.0
     w = random_weights(E, H, I, quant, seed=331)
-    pgu, pd, sc = weights_dev(_slice_w(w, e0, n), quant)
+    pw, sc = weights_dev(_slice_w(w, e0, n), quant)
     r, ref_r = _routes(lg, k)
     assert not np.any(ref_r["topk_ids"] >= e0)
     x = bf16_dev(a["x"])
-    got = moe.forward(x, r, pgu, pd, quant=quant, scales=sc, path=path, expert_begin=e0, num_experts=n)
+    got = moe.forward(x, r, pw, quant=quant, scales=sc, path=path, expert_begin=e0, num_experts=n)
     rng = np.random.default_rng(332)
     start = to_bf16_bits(rng.uniform(0.5, 1.0, (T, H)).astype(np.float32))   # no -0.0
     out = bf16_dev(start)
-    moe.forward(x, r, pgu, pd, quant=quant, scales=sc, out=out, path=path, expert_begin=e0, num_experts=n,
+    moe.forward(x, r, pw, quant=quant, scales=sc, out=out, path=path, expert_begin=e0, num_experts=n,
                 accumulate=True)
     torch.cuda.synchronize()
     assert torch.count_nonzero(got.float()).item() == 0

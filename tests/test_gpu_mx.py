@@ -6,16 +6,16 @@ import pytest
 import torch
 
 from gpu_helpers import DEV, bf16_dev, check_out, check_routing, moe, oracle, oracle_out, random_activations, \
-    random_weights, routes_np, say, weights_dev
+    random_weights, routes_np, say, tile_cover_tokens, weights_dev
 from workloads import _normal_per_expert, bf16_bits_to_f32, quantise_weight_mx32, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
 
 def _layer(x_bits, lg, k, w, tokens=None, **kw):
-    pgu, pd, sc = weights_dev(w, "fp8_mx32")
+    pw, sc = weights_dev(w, "fp8_mx32")
     r = moe.route(torch.from_numpy(np.ascontiguousarray(lg)).to(DEV), k)
-    out = moe.forward(bf16_dev(x_bits), r, pgu, pd, quant="fp8_mx32", scales=sc, **kw)
+    out = moe.forward(bf16_dev(x_bits), r, pw, quant="fp8_mx32", scales=sc, **kw)
     torch.cuda.synchronize()
     ref_r = oracle.route(lg, k)
     check_routing(routes_np(r), ref_r)
@@ -48,17 +48,18 @@ def test_mx_forward_parity(T, H, I, E, k, tag):
     check_out(got, ref, "fp8", tag)
 
 
-def test_mx_prefill_sampled():
-    """The blockwise prefill layer's shape (T=4096, H=4096, I=512, E=128, top-8) in MX, sampled
-    tokens against the oracle."""
+def test_mx_prefill_every_tile():
+    """The blockwise prefill layer's shape (T=4096, H=4096, I=512, E=128, top-8) in MX: the
+    whole output of tokens that put a compared row in every 32-row block of every row tile
+    (and each expert's first and last sorted row), against the oracle."""
     T, H, I, E, k = 4096, 4096, 512, 128, 8
     say(f"mx prefill T={T} H={H} I={I} E={E} k={k}")
     a = random_activations(T, H, E, seed=410)
     w = random_weights(E, H, I, "fp8_mx32", seed=411)
-    rng = np.random.default_rng(412)
-    tok = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, 45, replace=False)])).astype(np.int32)
+    tok = tile_cover_tokens(oracle.route(a["logits"], k), k)
+    say(f"  {tok.size} tokens cover every tile block")
     got, ref = _layer(a["x"], a["logits"], k, w, tokens=tok)
-    check_out(got, ref, "fp8", "mx prefill sampled")
+    check_out(got, ref, "fp8", "mx prefill every tile")
 
 
 def test_mx_wide_scale_range():
@@ -88,8 +89,8 @@ def test_mx_expert_slices_accumulate():
     total = np.zeros((T, H))
     for e0, n in ((0, 3), (3, 5)):
         ws = {key: (None if w[key] is None else np.ascontiguousarray(w[key][e0:e0 + n])) for key in w}
-        pgu, pd, sc = weights_dev(ws, "fp8_mx32")
-        moe.forward(bf16_dev(a["x"]), r, pgu, pd, quant="fp8_mx32", scales=sc, out=shared, expert_begin=e0,
+        pw, sc = weights_dev(ws, "fp8_mx32")
+        moe.forward(bf16_dev(a["x"]), r, pw, quant="fp8_mx32", scales=sc, out=shared, expert_begin=e0,
                     num_experts=n, accumulate=True)
         total += oracle.forward(a["x"], ref_r["topk_ids"], ref_r["topk_weights"], ws["w_gate_up"], ws["w_down"],
                                 quant="fp8_mx32", s_gate_up=ws["s_gate_up"], s_down=ws["s_down"],
@@ -135,9 +136,9 @@ def test_mx_two_runs_bitwise_equal():
     T, H, I, E, k = 300, 512, 256, 8, 2
     a = random_activations(T, H, E, seed=450)
     w = random_weights(E, H, I, "fp8_mx32", seed=451)
-    pgu, pd, sc = weights_dev(w, "fp8_mx32")
+    pw, sc = weights_dev(w, "fp8_mx32")
     r = moe.route(torch.from_numpy(a["logits"]).to(DEV), k)
-    o1 = moe.forward(bf16_dev(a["x"]), r, pgu, pd, quant="fp8_mx32", scales=sc)
-    o2 = moe.forward(bf16_dev(a["x"]), r, pgu, pd, quant="fp8_mx32", scales=sc)
+    o1 = moe.forward(bf16_dev(a["x"]), r, pw, quant="fp8_mx32", scales=sc)
+    o2 = moe.forward(bf16_dev(a["x"]), r, pw, quant="fp8_mx32", scales=sc)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from gpu_helpers import (DEV, WORKLOADS, bf16_dev, check_out, check_routing, moe, oracle, oracle_out,
-                         random_activations, random_weights, routes_np, run, say, weights_dev,
+                         random_activations, random_weights, routes_np, run, say, tile_cover_tokens, weights_dev,
                          workload_dev, workload_inputs, workload_weights)
 from workloads import (_normal_per_expert, bf16_bits_to_f32, quantise_weight_block128, tie_heavy_logits,
                        to_bf16_bits)
@@ -67,17 +67,30 @@ def test_tiny_bf16(path):
     name = "tiny_bf16"
     wl = WORKLOADS[name]
     a = workload_inputs(name)
-    pgu, pd, _ = workload_dev(name)
+    pw, _ = workload_dev(name)
     r, lg = moe.route_project(bf16_dev(a["x"]), torch.from_numpy(a["w_router"]).to(DEV), wl.k)
-    out = moe.forward(bf16_dev(a["x"]), r, pgu, pd, path=path)
+    out = moe.forward(bf16_dev(a["x"]), r, pw, path=path)
     torch.cuda.synchronize()
     g = lg.cpu().numpy()
     ref_lg = oracle.router_logits(a["x"], a["w_router"])
     assert np.max(np.abs(g - ref_lg)) <= 1e-5
     ref_r = oracle.route(g, wl.k)
     check_routing(routes_np(r), ref_r)
+    # the kernel's scores pick the same routes as the oracle's own scores (no near-tie flips)
+    check_routing(ref_r, oracle.route(ref_lg, wl.k))
     ref = oracle_out(a["x"], ref_r, workload_weights(name), "bf16")
     check_out(out.float().cpu().numpy(), ref, "bf16", f"{name} {path}")
+
+
+@pytest.mark.parametrize("path", ["auto", "grouped", "route_direct"])
+def test_tiny_bf16_host_logits(path):
+    """The tiny layer with its router scores computed by the oracle on the host and fed to
+    moe_route: every value the reference uses comes from the host, none from the GPU."""
+    name = "tiny_bf16"
+    wl = WORKLOADS[name]
+    a = workload_inputs(name)
+    lg = oracle.router_logits(a["x"], a["w_router"])
+    _compare(f"{name} host logits", a["x"], lg, wl.k, workload_dev(name), workload_weights(name), "bf16", path)
 
 
 @pytest.mark.parametrize("B", [1, 2, 3, 4])
@@ -103,19 +116,31 @@ def _sample_tokens(T, n, seed):
     return t.astype(np.int32)
 
 
-def test_prefill_bf16_sampled():
-    name = "prefill_bf16"
+@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_fp8_block"])
+def test_prefill_every_tile(name):
+    """Full-size prefill (the benchmarked launch): the whole output of a set of tokens that
+    puts at least one compared row in every 32-row block of every 128-row tile of both grouped
+    GEMMs (and each expert's first and last sorted row), on the oracle's own routing."""
+    wl = WORKLOADS[name]
     a = workload_inputs(name)
-    tok = _sample_tokens(WORKLOADS[name].T, 61, 7)
-    _compare(name, a["x"], a["logits"], 8, workload_dev(name), workload_weights(name), "bf16", "auto", tok)
+    tok = tile_cover_tokens(oracle.route(a["logits"], wl.k), wl.k)
+    say(f"{name}: {tok.size} tokens cover every tile block")
+    _compare(name, a["x"], a["logits"], wl.k, workload_dev(name), workload_weights(name), wl.quant, "auto", tok)
 
 
-def test_prefill_fp8_block_sampled():
-    name = "prefill_fp8_block"
-    a = workload_inputs(name)
-    tok = _sample_tokens(WORKLOADS[name].T, 61, 8)
-    _compare(name, a["x"], a["logits"], 8, workload_dev(name), workload_weights(name), "fp8_block128",
-             "auto", tok)
+@pytest.mark.parametrize("quant", ["bf16", "fp8_block128"])
+def test_large_t_intermediates_past_4gib(quant):
+    """T=70000, k=E=8: the sorted Down output y is 70000*8*2048*2 = 2.3 GB (past the 2^31
+    byte offsets of a single buffer resource), so its row tiles are addressed from 64-bit
+    bases; compared on the first and last tokens (the highest y rows of every expert) and a
+    random sample, routing bit-exact."""
+    T, H, I, E, k = 70000, 2048, 256, 8, 8
+    say(f"large T={T} H={H} I={I} E={E} k={k} {quant}")
+    a = random_activations(T, H, E, seed=77)
+    w = random_weights(E, H, I, quant, seed=78)
+    assert moe.select_path(T, H, I, E, k, quant) == "grouped"
+    tok = np.unique(np.concatenate([np.arange(4), np.arange(T - 40, T), _sample_tokens(T, 40, 79)])).astype(np.int32)
+    _compare(f"large T {quant}", a["x"], a["logits"], k, weights_dev(w, quant), w, quant, "grouped", tok)
 
 
 # -------------------------------------------------------------- edge cases --
@@ -141,10 +166,18 @@ EDGE = [
 ]
 
 
+# route-direct Gate/Up row split each row-split case exists to exercise
+EXPECT_SPLIT = {"block128 B=1 row split 2": 2, "block128 row split 4": 4}
+
+
 @pytest.mark.parametrize("T,H,I,E,k,quant,kind,tag", EDGE)
 @pytest.mark.parametrize("path", ["grouped", "route_direct"])
 def test_edge_cases(T, H, I, E, k, quant, kind, tag, path):
     say(f"edge {tag}: T={T} H={H} I={I} E={E} k={k} {quant} {path}")
+    if path == "route_direct" and tag in EXPECT_SPLIT:
+        li = moe.forward_launch_info(T, H, I, E, k, quant, path)
+        say(f"  launch {li}")
+        assert li["gate_up_split"] == EXPECT_SPLIT[tag], li
     a = random_activations(T, H, E, seed=T * 7 + E)
     lg = a["logits"]
     if kind == "hot":
@@ -156,9 +189,9 @@ def test_edge_cases(T, H, I, E, k, quant, kind, tag, path):
 
 def test_empty_batch():
     w = random_weights(4, 128, 64, "bf16", seed=3)
-    pgu, pd, _ = weights_dev(w, "bf16")
+    pw, _ = weights_dev(w, "bf16")
     r = moe.route(torch.zeros((0, 4), dtype=torch.float32, device=DEV), 2)
-    out = moe.forward(torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV), r, pgu, pd)
+    out = moe.forward(torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV), r, pw)
     torch.cuda.synchronize()
     assert out.shape == (0, 128)
     assert r.expert_counts.cpu().tolist() == [0] * 4
@@ -180,7 +213,7 @@ def test_two_runs_bitwise_equal(name, path):
 def test_graph_replay_bitwise_equal(name):
     wl = WORKLOADS[name]
     a = workload_inputs(name, batch=4 if wl.batches else None)
-    pgu, pd, scales = workload_dev(name)
+    pw, scales = workload_dev(name)
     x = bf16_dev(a["x"])
     T = x.shape[0]
     routes = moe.Routes(T, wl.E, wl.k, DEV)
@@ -204,7 +237,7 @@ def test_graph_replay_bitwise_equal(name):
 
     def step():
         route_step()
-        moe.forward(x, routes, pgu, pd, quant=wl.quant, scales=scales, out=out, workspace=ws)
+        moe.forward(x, routes, pw, quant=wl.quant, scales=scales, out=out, workspace=ws)
 
     step()
     torch.cuda.synchronize()

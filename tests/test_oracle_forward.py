@@ -311,3 +311,50 @@ def test_ep_slice_without_routes_is_zero():
     out = oracle.forward(a["x"], r["topk_ids"], r["topk_weights"], ws["w_gate_up"], ws["w_down"],
                          expert_begin=4)
     assert np.array_equal(out, np.zeros_like(out))
+
+
+@pytest.mark.parametrize("quant", ["bf16", "fp8_per_tensor", "fp8_block128", "fp8_mx32"])
+def test_gate_up_h_dense_reformulation(quant):
+    """oracle.gate_up_h: the SwiGLU output of each route, against torch's dense product of the
+    activation (quantised with torch's own e4m3 cast for the FP8 formats) and every expert's
+    Gate/Up weight, gathered at the routed (token, expert) pairs; a listed subset of routes
+    returns exactly those rows."""
+    T, H, I, E, k = 6, 256, 128, 5, 2
+    a = random_activations(T, H, E, 60)
+    w = random_weights(E, H, I, quant, 61)
+    r = oracle.route(a["logits"], k)
+    h = oracle.gate_up_h(a["x"], r["topk_ids"], w["w_gate_up"], quant, w["s_gate_up"])
+    x = torch.from_numpy(bf16_bits_to_f32(a["x"]))
+    if quant == "bf16":
+        xa = x.double()
+        wgu = torch.from_numpy(bf16_bits_to_f32(w["w_gate_up"])).double()
+    else:
+        q = torch.from_numpy(w["w_gate_up"]).view(torch.float8_e4m3fn).double()
+        s = torch.from_numpy(w["s_gate_up"])
+        if quant == "fp8_per_tensor":
+            sx = torch_scale(x.abs().max())
+            xa = torch_e4m3(x / sx) * sx.double()
+            wgu = q * s.double()[:, None, None]
+        elif quant == "fp8_block128":
+            xb = x.reshape(T, H // 128, 128)
+            sx = torch_scale(xb.abs().amax(dim=2))
+            xa = (torch_e4m3(xb / sx[:, :, None]) * sx.double()[:, :, None]).reshape(T, H)
+            wgu = (q.reshape(E, H // 128, 128, 2 * I // 128, 128)
+                   * s.double()[:, :, None, :, None]).reshape(E, H, 2 * I)
+        else:
+            xb = x.reshape(T, H // 32, 32)
+            amax = xb.abs().amax(dim=-1)
+            _, ex = torch.frexp(amax)
+            b = torch.where(amax > 0, (ex - 9 + 127).clamp(0, 254), torch.zeros_like(ex)).double()
+            sc = torch.pow(2.0, b - 127)
+            xa = (torch_e4m3((xb.double() / sc[..., None]).float()) * sc[..., None]).reshape(T, H)
+            wgu = (q.reshape(E, H // 32, 32, 2 * I) * torch.pow(2.0, s.double() - 127)[:, :, None, :]).reshape(
+                E, H, 2 * I)
+    gu = torch.einsum("th,ehn->ten", xa, wgu)
+    dense = (F.silu(gu[..., :I]) * gu[..., I:]).numpy()            # [T, E, I]
+    ids = r["topk_ids"]
+    ref = np.stack([dense[t, ids[t, j]] for t in range(T) for j in range(k)])
+    assert np.max(np.abs(h - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+    sub = np.array([5, 0, 11], np.int32)
+    assert np.array_equal(oracle.gate_up_h(a["x"], ids, w["w_gate_up"], quant, w["s_gate_up"], routes=sub),
+                          h[sub])
