@@ -296,6 +296,24 @@ int moe_decode_forward(const float *logits, const void *x, int T, int E, int k, 
                        int H, int I, int quant, int path, const moe_ep *ep, void *ws, size_t ws_bytes,
                        void *stream);
 
+/* moe_decode_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same launches and results as moe_decode_forward, with the
+ * workspace taken from a 16 MiB device array inside this library (each GPU
+ * the library runs on holds its own copy until the process ends; the call
+ * itself allocates nothing).  A call whose workspace
+ * (moe_forward_workspace_size for its shape, route-direct path) exceeds
+ * 16 MiB returns MOE_ERR_UNSUPPORTED before anything is enqueued; every
+ * decode batch up to 16 tokens at the layer shapes measured here needs
+ * under 6 MiB.  All calls on one GPU share that array: calls that overlap
+ * on one GPU (other streams, other threads) race; order them on one stream.
+ * The array keeps the last call's contents; nothing in it needs to start at
+ * zero (the kernels reset their own counters each call).  Arguments and
+ * errors otherwise as for moe_decode_forward. */
+int moe_decode_forward_noalloc(const float *logits, const void *x, int T, int E, int k, moe_routes *routes,
+                               const moe_packed_weights *w, const moe_scales *scales, void *out,
+                               int H, int I, int quant, int path, const moe_ep *ep, void *stream);
+
 /* moe_forward with stage timing for profilers and benchmarks: the same
  * kernels, plus hipEventRecord(stage_events[i], stream) before the first
  * launch and after each launch (no synchronisation).  stage_events holds

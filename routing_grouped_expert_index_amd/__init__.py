@@ -28,7 +28,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
 EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_route_project_workspace_size",
             "moe_route_project", "moe_pack_weights", "moe_pack_mx_scales", "moe_select_path",
             "moe_forward_workspace_size", "moe_forward_workspace_views", "moe_forward_launch_info",
-            "moe_forward", "moe_forward_ex", "moe_decode_forward", "moe_forward_profiled",
+            "moe_forward", "moe_forward_ex", "moe_decode_forward", "moe_decode_forward_noalloc",
+            "moe_forward_profiled",
             "moe_last_error"]
 PACKED_TAG = 0x4D6F4557
 
@@ -113,6 +114,8 @@ def lib():
     L.moe_decode_forward.restype = i32
     L.moe_decode_forward.argtypes = [P, P, i32, i32, i32, ctypes.POINTER(_CRoutes), ctypes.POINTER(_CPacked),
                                      ctypes.POINTER(_CScales), P, i32, i32, i32, i32, ctypes.POINTER(_CEp), P, sz, P]
+    L.moe_decode_forward_noalloc.restype = i32
+    L.moe_decode_forward_noalloc.argtypes = L.moe_decode_forward.argtypes[:14] + [P]
     L.moe_forward_profiled.restype = i32
     L.moe_forward_profiled.argtypes = L.moe_forward.argtypes + [ctypes.POINTER(ctypes.c_void_p), i32,
                                                                ctypes.POINTER(ctypes.c_int),
@@ -331,6 +334,28 @@ def decode_forward(logits: torch.Tensor, x: torch.Tensor, k: int, weights: Packe
                                     ctypes.byref(sc), _ptr(out), H, I, QUANT[quant], PATH[path],
                                     ctypes.byref(ep), _ptr(workspace), workspace.numel(), _stream(x.device, stream)))
     return out, routes
+
+
+def decode_forward_noalloc(logits: torch.Tensor, x: torch.Tensor, k: int, weights: PackedWeights,
+                           out: torch.Tensor, routes: Routes, quant: str | None = None, scales=None,
+                           path: str = "auto", stream=None, expert_begin: int = 0, num_experts: int | None = None,
+                           accumulate: bool = False):
+    """decode_forward with the library's own static workspace (moe_decode_forward_noalloc):
+    the caller passes preallocated `out` and `routes`; the call allocates nothing."""
+    _need_cuda(logits, "logits")
+    _need_cuda(x, "x")
+    _need_cuda(out, "out")
+    T, E = logits.shape
+    H = x.shape[1]
+    w = _need_packed(weights)
+    quant = w.quant if quant is None else quant
+    cs = routes.c_struct()
+    sc = _CScales(None, None) if scales is None else _CScales(scales[0].data_ptr(), scales[1].data_ptr())
+    ep = _CEp(expert_begin, E - expert_begin if num_experts is None else num_experts, int(bool(accumulate)))
+    _check(lib().moe_decode_forward_noalloc(_ptr(logits), _ptr(x), T, E, k, ctypes.byref(cs), ctypes.byref(w.desc),
+                                            ctypes.byref(sc), _ptr(out), H, w.I, QUANT[quant], PATH[path],
+                                            ctypes.byref(ep), _stream(x.device, stream)))
+    return out
 
 
 def forward(x: torch.Tensor, routes: Routes, weights: PackedWeights,

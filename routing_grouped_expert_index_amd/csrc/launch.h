@@ -8,6 +8,9 @@
 namespace moe {
 
 constexpr int kMaxExperts = 512;
+
+// Records a message for moe_last_error() on the calling thread; returns code.
+int set_error(int code, const char* fmt, ...);
 constexpr int kRouteSmallMaxRoutes = 4096;
 
 struct RouteOut {

@@ -143,6 +143,16 @@ int hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace moe {
+int set_error(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
