@@ -193,7 +193,9 @@ size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int quant, 
  * as byte offsets from ws (-1 where the call keeps no such array).  After a
  * moe_forward / moe_forward_ex / moe_decode_forward call with this shape,
  * quantisation and path, and until the next call that uses the workspace:
- *   x_codes   e4m3 [T,H], the codes the Gate/Up projection consumed (both paths)
+ *   x_codes   e4m3 [T,H], the codes the Gate/Up projection consumed (both paths;
+ *             route-direct: rows of tokens with a route into the call's
+ *             expert slice, or every row with the routing folded in)
  *   x_scales  per-tensor fp32 [1]; block128 fp32 [T,H/128]; MX E8M0 bytes
  *             [T,H/32], group c of a row at byte 8(c/8) + 4(c%2) + (c%8)/2
  *   h_codes   grouped path: e4m3 [T*k,I], row i = the route at sorted position i

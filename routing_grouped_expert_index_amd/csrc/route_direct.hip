@@ -127,6 +127,24 @@ __device__ __forceinline__ float block_amax(const T* p, long n, float* sred) {
     return m;
 }
 
+// workgroup-wide max of one value per thread (sred: NW floats of LDS)
+template <int NW>
+__device__ __forceinline__ float block_max(float m, float* sred) {
+    m = wave_max(m);
+    if (lane_id() == 0) sred[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, sred[w]);
+    return m;
+}
+
+// wave-uniform 32-bit load through the constant address space (a scalar load:
+// it counts on lgkmcnt, so waiting for it never waits for vector loads)
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int i) {
+    return ((const __attribute__((address_space(4))) int32_t*)(p))[__builtin_amdgcn_readfirstlane(i)];
+}
+
 // Activation rows are staged in LDS once per workgroup (every lane of a
 // 32-row weight block needs the same activation values): bf16 values, or e4m3
 // codes (quantised here for per-tensor FP8, copied for blockwise).
@@ -279,6 +297,30 @@ rd_gate_up_kernel(const RdArgs a) {
     // barrier that publishes it; otherwise the expert comes from the routes and
     // the weight stream starts first.
     const bool from_logits = a.logits != nullptr;
+    // The activation values go out before anything else (vector loads complete
+    // in issue order, so waiting for them later never waits for the weight
+    // stream behind them): this thread's 16-byte chunks c = threadIdx.x + p NT
+    // of the token's bf16 row and, for the per-tensor scale, of all of x
+    // (clamped indices, masked when used).  Workgroups of fewer than 4 waves
+    // would need too many registers for the row and read it after the weights.
+    constexpr int NT = 64 * NW;
+    constexpr bool PRE = NW >= 4;
+    constexpr int RP = PRE ? (kRdActBytes * 2 / 16 + NT - 1) / NT : 1;   // bf16 row: H <= 8192 values
+    constexpr int AP = Q == RD_TENSOR && PRE ? 16384 / 8 / NT : 1;      // all of x while T H <= 16384
+    const uint16_t* x = reinterpret_cast<const uint16_t*>(a.act);
+    const int rch = a.H / 8;                     // 16-byte chunks in the row
+    const long ach = (long)a.T * a.H / 8;        // ... in all of x
+    u32x4 xr[RP], xa[AP];
+    if constexpr (PRE) {
+        const u32x4* xt = reinterpret_cast<const u32x4*>(x + (long)t * a.H);
+#pragma unroll
+        for (int p = 0; p < RP; ++p) xr[p] = xt[min((int)threadIdx.x + p * NT, rch - 1)];
+        if constexpr (Q == RD_TENSOR) {
+#pragma unroll
+            for (int p = 0; p < AP; ++p)
+                xa[p] = reinterpret_cast<const u32x4*>(x)[min((long)threadIdx.x + p * NT, ach - 1)];
+        }
+    }
     if (from_logits && wave == 0) {
         int eg0;
         float gate;
@@ -315,12 +357,18 @@ rd_gate_up_kernel(const RdArgs a) {
         wu = wg + gstride;
         return true;
     };
-    // FP8: the workgroup (slot 0, h block 0, split 0) of each token also leaves
-    // the token's codes and scales in the workspace (it runs even when its own
-    // expert lies outside this call's slice)
-    const bool writer = FP8 && a.xq_out != nullptr && G == 0 && rs == 0 && r == t * a.k;
-    const bool mine = from_logits || resolve(a.ids[r]);
-    if (!mine && !writer) return;
+    // FP8: one workgroup of each token (h block 0, split 0, and the token's
+    // first slot whose expert lies in this call's slice; with the routing
+    // folded in, slot 0, before it learns its expert) also leaves the token's
+    // codes and scales in the workspace
+    const bool mine = from_logits || resolve(ld_uniform(a.ids, r));
+    if (!mine) return;
+    bool writer = FP8 && a.xq_out != nullptr && G == 0 && rs == 0;
+    if (writer && !from_logits)
+        for (int jj = 0; jj < r - t * a.k; ++jj)
+            writer = writer && (unsigned)(ld_uniform(a.ids, t * a.k + jj) - a.e0) >= (unsigned)a.nloc;
+    else if (writer)
+        writer = r == t * a.k;
 
     // two load buffers: batch b+1 is requested before batch b is computed
     u32x4 vg[2][U][2], vu[2][U][2];
@@ -338,19 +386,87 @@ rd_gate_up_kernel(const RdArgs a) {
     };
     std::integral_constant<int, 0> B0;
     std::integral_constant<int, 1> B1;
-    if (!from_logits && mine) load_batch(B0, s0);   // the weight stream starts before the activation row is staged
-
     float xs = 1.0f;
-    const uint16_t* x = reinterpret_cast<const uint16_t*>(a.act);
-    if constexpr (Q == RD_TENSOR) {
-        xs = scale_from_amax(block_amax<uint16_t, NW>(x, (long)a.T * a.H, sred));
-        quant_row<uint16_t, NW>(xrow, x + (long)t * a.H, a.H, xs);
-    } else if constexpr (Q == RD_BLOCK) {   // the token's codes and per-128 scales, here
-        quant_row_block128<uint16_t, NW>(xrow, sxs, x + (long)t * a.H, a.H);
+    // the activation row staged in LDS (x quantised for FP8): written out twice
+    // below, once per mode, so that no branch joins between the weight loads
+    // and the first use of the preloaded activations (a join would make the
+    // compiler wait for every load issued on either side)
+    auto stage_x = [&]() __attribute__((always_inline)) {
+    if constexpr (!PRE) {
+        if constexpr (Q == RD_TENSOR) {
+            xs = scale_from_amax(block_amax<uint16_t, NW>(x, (long)a.T * a.H, sred));
+            quant_row<uint16_t, NW>(xrow, x + (long)t * a.H, a.H, xs);
+        } else if constexpr (Q == RD_BLOCK) {   // the token's codes and per-128 scales, here
+            quant_row_block128<uint16_t, NW>(xrow, sxs, x + (long)t * a.H, a.H);
+        } else {
+            stage_row<NW>(xrow, a.act + (long)t * Kb, Kb);
+        }
+    } else if constexpr (Q == RD_TENSOR) {
+        // the x amax from the preloaded chunks (and any beyond them), then the
+        // row's codes from its preloaded chunks
+        float m = 0.0f;
+#pragma unroll
+        for (int p = 0; p < AP; ++p) {
+            float v[8];
+            bf16x8_to_f32(xa[p], v);
+            float mp = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) mp = fmaxf(mp, fabsf(v[q]));
+            m = (long)threadIdx.x + p * NT < ach ? fmaxf(m, mp) : m;
+        }
+        for (long c = (long)threadIdx.x + AP * NT; c < ach; c += NT) {
+            float v[8];
+            bf16x8_to_f32(reinterpret_cast<const u32x4*>(x)[c], v);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+        }
+        xs = scale_from_amax(block_max<NW>(m, sred));
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            const int c = threadIdx.x + p * NT;
+            float v[8];
+            bf16x8_to_f32(xr[p], v);
+            uint2 q8;
+            q8.x = f32x4_to_e4m3x4(v[0] / xs, v[1] / xs, v[2] / xs, v[3] / xs);
+            q8.y = f32x4_to_e4m3x4(v[4] / xs, v[5] / xs, v[6] / xs, v[7] / xs);
+            if (c < rch) *reinterpret_cast<uint2*>(xrow + 8 * c) = q8;
+        }
+    } else if constexpr (Q == RD_BLOCK) {
+        // per 128 values (16 lanes of 8): amax over the group, s = amax/448, codes
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            const int c = threadIdx.x + p * NT;
+            float v[8];
+            bf16x8_to_f32(xr[p], v);
+            float m = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));   // the group's 16 lanes
+            const float sc = scale_from_amax(m);
+            uint2 q8;
+            q8.x = f32x4_to_e4m3x4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+            q8.y = f32x4_to_e4m3x4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
+            if (c < rch) {
+                *reinterpret_cast<uint2*>(xrow + 8 * c) = q8;
+                if ((threadIdx.x & 15) == 0) sxs[c / 16] = sc;
+            }
+        }
     } else {
-        stage_row<NW>(xrow, a.act + (long)t * Kb, Kb);
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            const int c = threadIdx.x + p * NT;
+            if (c < rch) reinterpret_cast<u32x4*>(xrow)[c] = xr[p];
+        }
     }
     __syncthreads();
+    };
+    if (!from_logits) {
+        load_batch(B0, s0);   // the weight stream goes out right behind the activations
+        stage_x();
+    } else {
+        stage_x();
+    }
     if (writer) {
         uint8_t* xq = a.xq_out + (long)t * a.H;
         for (int i = threadIdx.x * 16; i < a.H; i += 64 * NW * 16)
@@ -364,8 +480,6 @@ rd_gate_up_kernel(const RdArgs a) {
     if (from_logits) {   // the expert wave 0 published; then the weight stream
         if (!resolve(__builtin_amdgcn_readfirstlane(s_eg))) return;
         load_batch(B0, s0);
-    } else if (!mine) {
-        return;
     }
     int cg = 0, cu = 0;           // blockwise: scale columns of the gate and up blocks
     if constexpr (Q == RD_BLOCK) {
@@ -637,6 +751,8 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
     constexpr bool FP8 = Q != RD_BF16;
     constexpr int elem = FP8 ? 1 : 2;
     constexpr int MS = FP8 ? kRdBlockMaxSlicesFp8 : kRdBlockMaxSlices;
+    constexpr int GPL = (MS * 16 + 63) / 64;   // fp32 h (per-tensor): groups of 4 values per lane
+    constexpr int QPL = (MS * 4 + 63) / 64;    // bf16 h: 16-byte pieces per lane
     __shared__ __attribute__((aligned(16))) uint8_t hst_all[kRdBlockWaves * kRdBlockStage];
     __shared__ float red[kRdBlockMaxItems * 32];
     const int nw = blockDim.x >> 6;
@@ -646,10 +762,51 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
     const int Kb = a.I * elem, NSL = Kb / kSliceBytes;
     const int KP = a.kp, spw = NSL / KP, items = a.k * KP;
     uint8_t* hst = hst_all + wave * kRdBlockStage;
+
+    // One piece (route slot, K part): its weight slices and its activations are
+    // requested together (clamped indices, masked after: a guarded load waits
+    // for all before it); the slot's expert comes by a scalar load, so the
+    // weight addresses wait only for that.
+    u32x4 vw[MS][2];
+    f32x4 hf[GPL];
+    u32x4 hb[QPL];
+    int r = 0, e = 0, s0 = 0;
+    bool live = false;
+    auto issue = [&](int it) __attribute__((always_inline)) {
+        const int jj = it / KP, kp = it - jj * KP;
+        r = t * a.k + jj;
+        s0 = kp * spw;
+        if constexpr (Q == RD_TENSOR) {
+            const float* hp = reinterpret_cast<const float*>(a.h) + (long)r * a.I + s0 * 64;
+            const int ng = spw * 16;
+#pragma unroll
+            for (int q = 0; q < GPL; ++q) hf[q] = *reinterpret_cast<const f32x4*>(hp + 4 * min(lane + 64 * q, ng - 1));
+        } else {
+            const u32x4* hp = reinterpret_cast<const u32x4*>(a.h + (long)r * Kb + s0 * 64);
+            const int nq = spw * 4;
+#pragma unroll
+            for (int q = 0; q < QPL; ++q) hb[q] = hp[min(lane + 64 * q, nq - 1)];
+        }
+        e = ld_uniform(a.ids, r) - a.e0;   // index in this call's expert slice
+        live = (unsigned)e < (unsigned)a.nloc;
+        if (live) {
+            const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + (long)s0 * 2048 + lane * 16;
+#pragma unroll
+            for (int u = 0; u < MS; ++u)
+                if (u < spw)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        vw[u][q] = *reinterpret_cast<const u32x4*>(wb + u * 2048 + q * 1024);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // the wave's first piece goes out before the h scale's inputs
+    if (wave < items) issue(wave);
+
     float hs = 1.0f;
     if constexpr (Q == RD_TENSOR) {
         // the whole-tensor h scale from the Gate/Up workgroups' maxima (loads of
-        // clamped indices, masked after: a guarded load waits for all before it)
+        // clamped indices, masked after)
         const int nmax = a.T * a.k * (a.I / 32) * a.rs;
         float m = 0.0f;
         for (int base = 0; base < nmax; base += 512) {
@@ -663,49 +820,27 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
         if (blockIdx.x == 0 && threadIdx.x == 0) a.scal_out[1] = hs;   // inspection copy
     }
     for (int it = wave; it < items; it += nw) {
-        const int jj = it / KP, kp = it - jj * KP;
-        const int r = t * a.k + jj, e = a.ids[r] - a.e0;   // index in this call's expert slice
-        if ((unsigned)e >= (unsigned)a.nloc) {   // another slice's expert: a zero piece
+        if (it != wave) issue(it);
+        if (!live) {   // another slice's expert: a zero piece
             if (hh == 0) red[it * 32 + j] = 0.0f;
             continue;
         }
-        const int s0 = kp * spw;
-        const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + (long)s0 * 2048 + lane * 16;
-        u32x4 vw[MS][2];
-#pragma unroll
-        for (int u = 0; u < MS; ++u)
-            if (u < spw)
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    vw[u][q] = *reinterpret_cast<const u32x4*>(wb + u * 2048 + q * 1024);
-        __builtin_amdgcn_sched_barrier(0);
         // the piece's activations into this wave's LDS area: bf16 h copied,
-        // per-tensor fp32 h quantised into e4m3 codes (clamped loads, masked)
+        // per-tensor fp32 h quantised into e4m3 codes
         if constexpr (Q == RD_TENSOR) {
-            const float* hp = reinterpret_cast<const float*>(a.h) + (long)r * a.I + s0 * 64;
-            const int ng = spw * 16;   // groups of 4 values
-            constexpr int GPL = (MS * 16 + 63) / 64;
-            f32x4 hv[GPL];
-#pragma unroll
-            for (int q = 0; q < GPL; ++q)
-                hv[q] = *reinterpret_cast<const f32x4*>(hp + 4 * min(lane + 64 * q, ng - 1));
+            const int ng = spw * 16;
 #pragma unroll
             for (int q = 0; q < GPL; ++q) {
                 const int gi = lane + 64 * q;
                 if (gi < ng)
                     reinterpret_cast<uint32_t*>(hst)[gi] =
-                        f32x4_to_e4m3x4(hv[q][0] / hs, hv[q][1] / hs, hv[q][2] / hs, hv[q][3] / hs);
+                        f32x4_to_e4m3x4(hf[q][0] / hs, hf[q][1] / hs, hf[q][2] / hs, hf[q][3] / hs);
             }
         } else {
-            const u32x4* hp = reinterpret_cast<const u32x4*>(a.h + (long)r * Kb + s0 * 64);
-            const int nq = spw * 4;    // 16-byte pieces
-            constexpr int QPL = (MS * 4 + 63) / 64;
-            u32x4 hv[QPL];
-#pragma unroll
-            for (int q = 0; q < QPL; ++q) hv[q] = hp[min(lane + 64 * q, nq - 1)];
+            const int nq = spw * 4;
 #pragma unroll
             for (int q = 0; q < QPL; ++q)
-                if (lane + 64 * q < nq) reinterpret_cast<u32x4*>(hst)[lane + 64 * q] = hv[q];
+                if (lane + 64 * q < nq) reinterpret_cast<u32x4*>(hst)[lane + 64 * q] = hb[q];
         }
         // one wave's LDS accesses execute in order; this keeps the compiler from
         // moving the reads above the writes
