@@ -71,6 +71,17 @@ gemm32_kernel(const GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int j = lane & 31, hh = lane >> 5;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // The lane index through an opaque copy at each use: addresses built from
+    // it (scale tables, epilogue offsets, the weight-row pointer) are then
+    // computed where they are used instead of being hoisted out of the loops
+    // and held across the K loop (the long-K FP8 instantiations run at the
+    // 256-register limit).
+    auto lane_o = [&]() __attribute__((always_inline)) {
+        int lo = lane;
+        __asm__ volatile("" : "+v"(lo));
+        return lo;
+    };
     const int NTN = (g.N + BN - 1) / BN;
     const int ntm = ld_const(g.ntiles, 0);
     const int NSL = g.Kb / kSliceBytes;
@@ -87,7 +98,7 @@ gemm32_kernel(const GemmArgs g) {
         e_ = ld_const(g.tiles, 2 * mt);
         row0_ = ld_const(g.tiles, 2 * mt + 1);
         rows_ = min(BM, ld_const(g.offsets, e_ + 1) - row0_);
-        wn0_ = nt * BN + wave * WROWS;
+        wn0_ = nt * BN + wave_u * WROWS;   // wave-uniform (scalar registers)
     };
     // token DMA: this wave fills tile rows 16*wave + lane/4, physical chunk
     // lane%4, which holds logical chunk (lane%4) ^ (row/4 % 4); padding rows
@@ -95,7 +106,6 @@ gemm32_kernel(const GemmArgs g) {
     // loads (a vector load here would need a vmcnt wait that drains the
     // prefetch) and each lane picks its own.
     const int dma_r = 16 * wave + (lane >> 2);
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto src_row = [&](int row0_, int rows_) __attribute__((always_inline)) {
         int sel = 0;
 #pragma unroll
@@ -105,7 +115,9 @@ gemm32_kernel(const GemmArgs g) {
             const int v = GATHER ? ld_const(g.perm, idx) : idx;
             sel = (lane >> 2) == i ? v : sel;
         }
-        return (long)(GATHER ? sel / g.k : sel);
+        // (the division by k as a multiply-shift from the host: a divide here
+        // would hold a reciprocal in a register through the K loop)
+        return GATHER ? (int)(((uint64_t)(uint32_t)sel * g.kdiv_m) >> g.kdiv_s) : sel;
     };
     // The token DMA is a buffer load (MUBUF) with the LDS bit, not the FLAT
     // global_load_lds: the compiler treats a pending FLAT access that may touch
@@ -124,7 +136,7 @@ gemm32_kernel(const GemmArgs g) {
                                                  (int)(uint32_t)(left < 0xffffffffL ? left : 0xffffffffL),
                                                  0x00020000);
     };
-    auto make_ap = [&](long src, int row0_) __attribute__((always_inline)) {
+    auto make_ap = [&](int src, int row0_) __attribute__((always_inline)) {
         const long rel = GATHER ? src : src - row0_;
         return (uint32_t)(rel * g.lda) + (uint32_t)(((lane & 3) ^ ((dma_r >> 2) & 3)) * 16);
     };
@@ -150,7 +162,7 @@ gemm32_kernel(const GemmArgs g) {
     // store instructions per wave and tile (Q128: four rows of codes, four of scales)
     constexpr int SX = EPI == EPI_SWIGLU_Q128 || EPI == EPI_SWIGLU_MX ? 8 : (4 / MPP) * (RPP * CB / 64);
     auto make_wp = [&](int e_, int wn0_) __attribute__((always_inline)) {
-        return g.B + (long)e_ * g.N * g.Kb + (long)((wn0_ < g.N ? wn0_ : 0) / 32) * gstride + lane * 16;
+        return g.B + (long)e_ * g.N * g.Kb + (long)((wn0_ < g.N ? wn0_ : 0) / 32) * gstride + lane_o() * 16;
     };
 
     // 128x128-blockwise e4m3: every 128-deep K block kb has its own activation
@@ -181,12 +193,12 @@ gemm32_kernel(const GemmArgs g) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g.sa), 0, BLK || MX ? g.sa_bytes : 0, 0x00020000);
     // this lane's row (16 wave + lane/4, source row src) and scale blocks 4t + lane%4
     // (MX: scale dwords 4t + lane%4)
-    auto table = [&](long src) __attribute__((always_inline)) {
+    auto table = [&](int src) __attribute__((always_inline)) {
         if constexpr (BLK || MX) {
             for (int t = 0; t < (KT + 3) / 4; ++t) {
-                const int kb = min(4 * t + (lane & 3), KT - 1);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, MOE_LDS(sat + t * 4 * BM + wave * 64), 4,
-                                                         (uint32_t)((src * g.sa_ld + kb) * 4), 0, 0, 0);
+                const int kb = min(4 * t + (lane_o() & 3), KT - 1);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, MOE_LDS(sat + t * 4 * BM + wave_u * 64), 4,
+                                                         (uint32_t)(((long)src * g.sa_ld + kb) * 4), 0, 0, 0);
             }
         }
     };
@@ -225,7 +237,7 @@ gemm32_kernel(const GemmArgs g) {
 
     int e, row0, rows, wn0;
     decode(L, e, row0, rows, wn0);
-    const long src0 = src_row(row0, rows);
+    const int src0 = src_row(row0, rows);
     __amdgpu_buffer_rsrc_t arsrc = make_arsrc(row0);
     uint32_t ap = make_ap(src0, row0);
     const uint8_t* wp = make_wp(e, wn0);
@@ -336,23 +348,10 @@ gemm32_kernel(const GemmArgs g) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            } else if constexpr (EPI == EPI_Y_BF16) {
-                // blockwise Down: the same, on K-block starts each M preceded by
-                // its block's 16 multiplies: R R R R, (V M V M R R) x 2, (V M V M) x 2
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                    for (int f = 0; f < 2; ++f) {
-                        if constexpr (RS) __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    }
-                    if (m < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                }
             } else {
-                // blockwise Gate/Up (its requantising epilogue leaves the K loop the
-                // fewest registers): the next token block only, R R, (M M R R) x 3,
-                // M M, with the multiplies on K-block starts as above
+                // blockwise (the K loop runs at the register limit): the next
+                // token block only, R R, (M M R R) x 3, M M, on K-block starts
+                // each M preceded by its block's 16 multiplies
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -370,8 +369,10 @@ gemm32_kernel(const GemmArgs g) {
     // the wave's two halves by scalar loads.  Nothing is kept across steps: the
     // previous block's scales are read again (registers are the K loop's limit).
     int cb0 = 0, cb1 = 0;
+    // the lane's row within a 32-row block (opaque: see lane_o)
+    auto jrow = [&]() __attribute__((always_inline)) { return lane_o() & 31; };
     auto sa_of = [&](int kb, int m) __attribute__((always_inline)) {
-        return sat[(kb >> 2) * 4 * BM + (32 * m + j) * 4 + (kb & 3)];
+        return sat[(kb >> 2) * 4 * BM + (32 * m + jrow()) * 4 + (kb & 3)];
     };
     auto sw_of = [&](int kb, int c) __attribute__((always_inline)) {
         return ld_const(g.sw, ((long)e * KT + kb) * g.nb_orig + c);
@@ -439,7 +440,7 @@ gemm32_kernel(const GemmArgs g) {
             const uint32_t* st32 = reinterpret_cast<const uint32_t*>(sat);
             const int d = 2 * min(s >> 2, NG - 1) + hh;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) tsc[m] = st32[(d >> 2) * 4 * BM + (32 * m + j) * 4 + (d & 3)];
+            for (int m = 0; m < 4; ++m) tsc[m] = st32[(d >> 2) * 4 * BM + (32 * m + jrow()) * 4 + (d & 3)];
             __builtin_amdgcn_sched_barrier(0);
         }
         wait_vm_only<WAIT_W + XW>();
@@ -468,7 +469,7 @@ gemm32_kernel(const GemmArgs g) {
         const int Ln = L + xr.stride;
         const bool more = Ln < xr.hi;
         int ne = 0, nrow0 = 0, nrows = 1, nwn0 = 0;
-        long nsrc = 0;
+        int nsrc = 0;
         if (more) {
             decode(Ln, ne, nrow0, nrows, nwn0);
             nsrc = src_row(nrow0, nrows);
@@ -534,12 +535,9 @@ gemm32_kernel(const GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
 
         // ------------------------------------------------------------ epilogue
-        // (output offsets count from this tile's first row; the lane index is
-        // taken through an opaque copy so that the offsets are computed here,
-        // not hoisted out of the tile loop to occupy registers in the K loop)
+        // (output offsets count from this tile's first row)
         const __amdgpu_buffer_rsrc_t crsrc = make_crsrc(row0);
-        int lane_e = lane;
-        __asm__ volatile("" : "+v"(lane_e));
+        const int lane_e = lane_o();
         const int j_e = lane_e & 31;
         // acc[f][m][i]: token row 32m + j, packed row wn0 + 32f + 8(i/4) + 4hh + i%4.
         // Each lane holds CPL 16-byte chunks of one output row segment per m:
@@ -622,7 +620,7 @@ gemm32_kernel(const GemmArgs g) {
             }
             if (hh == 0) {
 #pragma unroll
-                for (int m = 0; m < 4; ++m) RA[wave * BM + 32 * m + j] = amx[m];
+                for (int m = 0; m < 4; ++m) RA[wave * BM + 32 * m + j_e] = amx[m];
             }
             __asm__ volatile("" ::: "memory");
             wait_lgkm_only();
@@ -633,8 +631,9 @@ gemm32_kernel(const GemmArgs g) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r = 32 * m + j;
-                const float a = fmaxf(fmaxf(RA[grp * BM + r], RA[(grp + 1) * BM + r]),
-                                      fmaxf(RA[(grp + 2) * BM + r], RA[(grp + 3) * BM + r]));
+                const int re = 32 * m + j_e;
+                const float a = fmaxf(fmaxf(RA[grp * BM + re], RA[(grp + 1) * BM + re]),
+                                      fmaxf(RA[(grp + 2) * BM + re], RA[(grp + 3) * BM + re]));
                 const float sc = scale_from_amax(a);
                 u32x4 q;
 #pragma unroll
@@ -794,6 +793,16 @@ static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// n / d == (n * m) >> s for every n < 2^31 and 1 <= d <= 2^10, with
+// s = 31 + ceil(log2 d) and m = ceil(2^s / d) < 2^32: the error n (m - 2^s/d) / 2^s
+// is below n / 2^s < 1/d, so the floor is exact.
+static void div_magic(int d, uint32_t& m, int& s) {
+    int l = 0;
+    while ((1 << l) < d) ++l;
+    s = 31 + l;
+    m = (uint32_t)(((1ULL << s) + (uint64_t)d - 1) / (uint64_t)d);
+}
+
 static GemmArgs gate_up_args(const FwdPlan& p, int elem) {
     GemmArgs a{};
     const bool fp8 = p.quant != Q_BF16;
@@ -801,6 +810,7 @@ static GemmArgs gate_up_args(const FwdPlan& p, int elem) {
     a.lda = (long)p.H * elem;
     a.perm = p.perm;
     a.k = p.k;
+    div_magic(p.k, a.kdiv_m, a.kdiv_s);
     a.B = static_cast<const uint8_t*>(p.wgu);
     a.N = 2 * p.I;
     a.Kb = p.H * elem;

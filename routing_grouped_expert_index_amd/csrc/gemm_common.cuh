@@ -14,6 +14,8 @@ struct GemmArgs {
     long lda;
     const int32_t* perm;    // gather: sorted row i -> token perm[i] / k; Down: output row perm[i]
     int k;
+    uint32_t kdiv_m;        // perm[i] / k == (perm[i] * kdiv_m) >> kdiv_s (exact: perm[i] < 2^31)
+    int kdiv_s;
     const uint8_t* B;       // packed weights (layout.cuh), N packed rows, Kb bytes of K
     int N;
     int Kb;
