@@ -518,7 +518,8 @@ def cpu_baseline(a, w, wl, budget_s=15.0):
     dt = time.perf_counter() - t0
     return dict(value=round(n / dt, 2), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
                 sample=f"routing of all {wl.T} tokens + layer output of the first {n} tokens "
-                       f"of {wl.name} (fp64 C oracle, OpenMP), {dt:.1f} s")
+                       f"of {wl.name} (fp64 C oracle, gcc -O3 -fopenmp without -march=native so the library "
+                       f"runs on any x86-64 host; no tuning), {dt:.1f} s")
 
 
 def profile_only(torch, moe, args):
@@ -666,6 +667,41 @@ def main():
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(a, w, wl)
     print(json.dumps(line), flush=True)
+    recap(line)
+
+
+# Time budgets of the targets (≥60% of HBM for the decode forward at B=1..4,
+# ≥50% of dense MFMA for a prefill layer), from the bytes and flops each moves.
+DECODE_BUDGET_US = {"decode": [15.7, 30.5, 44.3, 57.3], "decode_fp8_per_tensor": [3.94, 7.71, 11.32, 14.79]}
+PREFILL_BUDGET_US = {"prefill_bf16": 494.8, "prefill_fp8_block128": 164.9, "prefill_fp8_mx32": 164.9}
+
+
+def recap(line):
+    """Compact stderr lines after the JSON line: every target next to its measurement."""
+    for key, name in (("decode", "decode bf16 E128 H2048 I768"),
+                      ("decode_fp8_per_tensor", "decode fp8 per-tensor E192 H4096 I192")):
+        if key not in line:
+            continue
+        for B, r in line[key]["batches"].items():
+            budget = DECODE_BUDGET_US[key][int(B) - 1]
+            log(f"recap {name} B={B}: forward {r['us_forward']} us (budget {budget}) = "
+                f"{r['hbm_frac_forward']:.3f} of HBM over {r['distinct_experts']} experts' weights; "
+                f"route+forward {r['us_per_layer']} us; one call {r['us_per_layer_fused']} us; "
+                f"{r['dominant']['kernel']} {r['dominant']['avg_launch_us']} us = {r['dominant']['frac']:.3f} of HBM")
+    rows = [("prefill_bf16", line.get("layer"), line.get("roofline"), line.get("ms_per_step"), line.get("value"))]
+    for key in ("prefill_fp8_block128", "prefill_fp8_mx32"):
+        if key in line:
+            rows.append((key, line[key]["layer"], line[key]["roofline"], line[key]["ms_per_step"],
+                         line[key]["tokens_per_s"]))
+    for key, lay, roof, ms, tps in rows:
+        if lay is None:
+            continue
+        log(f"recap {key}: {ms * 1e3:.1f} us/layer (budget {PREFILL_BUDGET_US[key]}), {tps:.4g} tokens/s; layer "
+            f"{lay['mfma_frac']:.3f} of MFMA, {lay['hbm_frac']:.3f} of HBM; Gate/Up {roof['avg_launch_us']} us = "
+            f"{roof['frac']:.3f} of MFMA peak")
+    cb = line.get("cpu_baseline")
+    if cb:
+        log(f"recap cpu oracle: {cb['value']} {cb['unit']} on {cb['cores']} threads ({cb['sample']})")
 
 
 if __name__ == "__main__":
