@@ -226,6 +226,20 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
         torch.cuda.synchronize()
         t_route_only = float(np.median([a.elapsed_time(b) for a, b in tr])) * 1e3
         t_fwd_only = float(np.median([a.elapsed_time(b) for a, b in tf])) * 1e3
+        # the forward's device span: events attached to its first and last kernel
+        # dispatches (moe_forward_timed), the figure a kernel trace reports
+        td = []
+        for it in range(iters + 2):
+            load(it)
+            evict.amax()
+            moe.route(layer.lg, wl.k, out=layer.routes, workspace=layer.rws)
+            d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            moe.forward(layer.x, layer.routes, layer.pw, quant=wl.quant, scales=layer.scales, out=layer.out,
+                        path=layer.path, workspace=layer.ws, device_events=(d0, d1))
+            if it >= 2:
+                td.append((d0, d1))
+        torch.cuda.synchronize()
+        t_fwd_dev = float(np.median([a.elapsed_time(b) for a, b in td])) * 1e3
         t_fwd = timed(layer.step)
         # the routing folded into the first kernel (moe_decode_forward), route-direct only
         t_fused = None
@@ -288,14 +302,17 @@ def bench_decode(torch, moe, name, batches, iters, nsets=32):
                       us_per_layer_graph_warm=round(t_graph_warm, 2),
                       tokens_per_s=round(B / (t_fwd * 1e-6), 1),
                       path=layer.path, distinct_experts=round(D, 2),
+                      us_forward_device=round(t_fwd_dev, 2),
                       hbm_frac_forward=round(w_bytes / (t_fwd_only * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
+                      hbm_frac_forward_device=round(w_bytes / (t_fwd_dev * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
                       hbm_frac_layer=round(w_bytes / (t_fwd * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
                       hbm_frac_layer_graph=round(w_bytes / (t_graph * 1e-6) / (PEAK_HBM_GBS * 1e9), 4),
                       dominant=dict(kernel=dname, bound="hbm", avg_launch_us=round(t_dom, 2),
                                     achieved=round(dom_bytes / (t_dom * 1e-6) / 1e9, 1),
                                     peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(dom_bytes / (t_dom * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)))
-        log(f"decode {name} B={B}: {t_fwd:.2f} us/layer, fused {t_fused} (route {t_route_only:.2f} + forward {t_fwd_only:.2f}; "
+        log(f"decode {name} B={B}: {t_fwd:.2f} us/layer, fused {t_fused} (route {t_route_only:.2f} + forward "
+            f"{t_fwd_only:.2f}, forward device span {t_fwd_dev:.2f}; "
             f"graph {t_graph:.2f}, warm graph {t_graph_warm:.2f}), "
             f"{res[B]['dominant']['kernel']} {t_dom:.2f} us {res[B]['dominant']['achieved']} GB/s")
     del evict
@@ -603,7 +620,10 @@ def main():
     line["decode"] = dict(workload="decode_bf16 H=2048 I=768 E=128 top-8", timing="cold HBM, median of "
                           f"{args.decode_iters}; us_per_layer: moe_route + moe_forward launched on "
                           "the stream between two HIP events (us_route, us_forward: the two calls "
-                          "separately); us_per_layer_fused: moe_decode_forward, the routing folded into "
+                          "separately); us_forward_device: moe_forward's device span, first kernel start "
+                          "to last kernel end, from events attached to those dispatches (moe_forward_timed), "
+                          "hbm_frac_forward_device over it; us_per_layer_fused: moe_decode_forward, the "
+                          "routing folded into "
                           "the route-direct Gate/Up kernel (one call); _graph: the same step replayed from "
                           "a HIP graph, cold; "
                           "_graph_warm: replayed back to back with the weights cached; dominant: "
@@ -684,8 +704,9 @@ def recap(line):
             continue
         for B, r in line[key]["batches"].items():
             budget = DECODE_BUDGET_US[key][int(B) - 1]
-            log(f"recap {name} B={B}: forward {r['us_forward']} us (budget {budget}) = "
-                f"{r['hbm_frac_forward']:.3f} of HBM over {r['distinct_experts']} experts' weights; "
+            log(f"recap {name} B={B}: forward {r['us_forward']} us stream / {r['us_forward_device']} us device "
+                f"(budget {budget}) = {r['hbm_frac_forward']:.3f} / {r['hbm_frac_forward_device']:.3f} of HBM over "
+                f"{r['distinct_experts']} experts' weights; "
                 f"route+forward {r['us_per_layer']} us; one call {r['us_per_layer_fused']} us; "
                 f"{r['dominant']['kernel']} {r['dominant']['avg_launch_us']} us = {r['dominant']['frac']:.3f} of HBM")
     rows = [("prefill_bf16", line.get("layer"), line.get("roofline"), line.get("ms_per_step"), line.get("value"))]

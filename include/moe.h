@@ -316,6 +316,19 @@ int moe_decode_forward_noalloc(const float *logits, const void *x, int T, int E,
                                const moe_packed_weights *w, const moe_scales *scales, void *out,
                                int H, int I, int quant, int path, const moe_ep *ep, void *stream);
 
+/* moe_forward with its device time: exactly moe_forward's launches, with
+ * ev_start attached to the first kernel's dispatch (recorded when that kernel
+ * starts) and ev_end to the last kernel's (recorded when it ends) --
+ * hipExtLaunchKernel's dispatch events, so no marker packet sits between the
+ * kernels.  hipEventElapsedTime(ev_start, ev_end) is then the span from the
+ * first kernel's start to the last kernel's end on the device, the quantity
+ * a kernel trace reports.  Both events are caller-created hipEvent_t handles
+ * (either may be NULL); T = 0 launches nothing and records neither.
+ * (For benchmarks: "perf: add small-batch route MMA for MoE", Performance.) */
+int moe_forward_timed(const void *x, const moe_routes *routes, const moe_packed_weights *w,
+                      const moe_scales *scales, void *out, int H, int I, int quant, int path,
+                      void *ws, size_t ws_bytes, void *stream, void *ev_start, void *ev_end);
+
 /* moe_forward with stage timing for profilers and benchmarks: the same
  * kernels, plus hipEventRecord(stage_events[i], stream) before the first
  * launch and after each launch (no synchronisation).  stage_events holds

@@ -29,7 +29,7 @@ EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_route_project_workspac
             "moe_route_project", "moe_pack_weights", "moe_pack_mx_scales", "moe_select_path",
             "moe_forward_workspace_size", "moe_forward_workspace_views", "moe_forward_launch_info",
             "moe_forward", "moe_forward_ex", "moe_decode_forward", "moe_decode_forward_noalloc",
-            "moe_forward_profiled",
+            "moe_forward_profiled", "moe_forward_timed",
             "moe_last_error"]
 PACKED_TAG = 0x4D6F4557
 
@@ -116,6 +116,8 @@ def lib():
                                      ctypes.POINTER(_CScales), P, i32, i32, i32, i32, ctypes.POINTER(_CEp), P, sz, P]
     L.moe_decode_forward_noalloc.restype = i32
     L.moe_decode_forward_noalloc.argtypes = L.moe_decode_forward.argtypes[:14] + [P]
+    L.moe_forward_timed.restype = i32
+    L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [P, P]
     L.moe_forward_profiled.restype = i32
     L.moe_forward_profiled.argtypes = L.moe_forward.argtypes + [ctypes.POINTER(ctypes.c_void_p), i32,
                                                                ctypes.POINTER(ctypes.c_int),
@@ -361,7 +363,8 @@ def decode_forward_noalloc(logits: torch.Tensor, x: torch.Tensor, k: int, weight
 def forward(x: torch.Tensor, routes: Routes, weights: PackedWeights,
             quant: str | None = None, scales=None, out: torch.Tensor | None = None, path: str = "auto",
             workspace: torch.Tensor | None = None, stream=None, events=None,
-            expert_begin: int = 0, num_experts: int | None = None, accumulate: bool = False):
+            expert_begin: int = 0, num_experts: int | None = None, accumulate: bool = False,
+            device_events=None):
     """Layer output bf16 [T, H] (moe_forward).
 
     weights: what pack_weights returned; quant defaults to the format they were
@@ -374,7 +377,11 @@ def forward(x: torch.Tensor, routes: Routes, weights: PackedWeights,
     With events (a list of torch.cuda.Event(enable_timing=True) or None) it
     calls moe_forward_profiled instead, which records events[0] before the
     first launch and events[i] after launch i (None entries record nothing),
-    and returns (out, stage_names)."""
+    and returns (out, stage_names).
+
+    With device_events=(start, end) (torch.cuda.Event(enable_timing=True)) it
+    calls moe_forward_timed: start/end are attached to the first and last kernel
+    dispatches, so start.elapsed_time(end) is the forward's device span."""
     _need_cuda(x, "x")
     if x.element_size() != 2 or x.dim() != 2:
         raise ValueError("x must be a bf16 [T, H] tensor")
@@ -406,6 +413,14 @@ def forward(x: torch.Tensor, routes: Routes, weights: PackedWeights,
             _stream(x.device, stream))
     if ep is not None:
         _check(lib().moe_forward_ex(*args[:9], ctypes.byref(ep), *args[9:]))
+        return out
+    if device_events is not None:
+        st = stream if stream is not None else torch.cuda.current_stream(x.device)
+        for ev in device_events:
+            if not ev.cuda_event:
+                ev.record(st)       # torch creates the underlying event on first record
+        _check(lib().moe_forward_timed(*args, ctypes.c_void_p(device_events[0].cuda_event),
+                                       ctypes.c_void_p(device_events[1].cuda_event)))
         return out
     if events is None:
         _check(lib().moe_forward(*args))

@@ -17,6 +17,8 @@
 // outputs in sorted (expert) order and route_pos is the inverse of the sort,
 // summed in fp32 in ascending j and rounded to bf16 once -- no atomics, so two
 // runs give the same bits.
+#include <hip/hip_ext.h>
+
 #include "common.cuh"
 #include "launch.h"
 
@@ -58,8 +60,8 @@ forward_init_kernel(int E, const int32_t* __restrict__ offsets, int build_tiles,
 hipError_t launch_forward_init(const FwdPlan& p, bool build_tiles, hipStream_t st) {
     // the tile map covers the expert slice: offsets + e0 for nloc experts, so a
     // tile names its expert by its index in the slice (the weights' index)
-    hipLaunchKernelGGL(forward_init_kernel, dim3(1), dim3(kMaxExperts), 0, st, p.nloc, p.offsets + p.e0,
-                       build_tiles ? 1 : 0, p.tiles, p.ntiles, p.amax);
+    hipExtLaunchKernelGGL(forward_init_kernel, dim3(1), dim3(kMaxExperts), 0, st, p.ev_first_start, nullptr, 0,
+                          p.nloc, p.offsets + p.e0, build_tiles ? 1 : 0, p.tiles, p.ntiles, p.amax);
     return hipGetLastError();
 }
 
@@ -358,8 +360,8 @@ combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, con
 
 hipError_t launch_combine(const FwdPlan& p, hipStream_t st) {
     dim3 grid(p.T, ceil_div(p.H / 8, 256));
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, p.y, p.tw, p.route_pos, p.H, p.k,
-                       p.offsets + p.e0, p.nloc, p.acc, p.out);
+    hipExtLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, nullptr, p.ev_last_end, 0, p.y, p.tw, p.route_pos,
+                          p.H, p.k, p.offsets + p.e0, p.nloc, p.acc, p.out);
     return hipGetLastError();
 }
 

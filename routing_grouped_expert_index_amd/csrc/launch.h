@@ -91,6 +91,10 @@ struct FwdPlan {
     const float* logits;
     int32_t* ids_w;
     float* tw_w;
+    // timing: events attached to the first kernel's dispatch (its start) and
+    // the last kernel's dispatch (its end), or null
+    hipEvent_t ev_first_start;
+    hipEvent_t ev_last_end;
 };
 
 constexpr int kGemmBM = 128;

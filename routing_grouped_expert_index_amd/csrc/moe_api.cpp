@@ -345,7 +345,7 @@ static int forward_impl(const void* x, const moe_routes* routes, const moe_packe
                         const moe_scales* scales, void* out, int H, int I,
                         int quant, int path, const moe_ep* ep, void* ws, size_t ws_bytes, void* stream,
                         void** events, int n_events, int* n_stages, const char** stage_names,
-                        const float* logits = nullptr) {
+                        const float* logits = nullptr, void* ev_start = nullptr, void* ev_end = nullptr) {
     if (!routes) return fail(MOE_ERR_INVALID_ARG, "routes is NULL");
     const int T = routes->T, E = routes->E, k = routes->k;
     int rc = check_shape(T, H, I, E, k, quant);
@@ -422,6 +422,8 @@ static int forward_impl(const void* x, const moe_routes* routes, const moe_packe
     P.logits = logits;
     P.ids_w = logits ? routes->topk_ids : nullptr;
     P.tw_w = logits ? routes->topk_weights : nullptr;
+    P.ev_first_start = static_cast<hipEvent_t>(ev_start);
+    P.ev_last_end = static_cast<hipEvent_t>(ev_end);
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool grouped = p == MOE_PATH_GROUPED;
@@ -488,6 +490,13 @@ int moe_decode_forward(const float* logits, const void* x, int T, int E, int k, 
     routes->k = k;
     return forward_impl(x, routes, w, scales, out, H, I, quant, path, ep, ws, ws_bytes,
                         stream, nullptr, 0, nullptr, nullptr, logits ? logits : nullptr);
+}
+
+int moe_forward_timed(const void* x, const moe_routes* routes, const moe_packed_weights* w,
+                      const moe_scales* scales, void* out, int H, int I, int quant, int path, void* ws,
+                      size_t ws_bytes, void* stream, void* ev_start, void* ev_end) {
+    return forward_impl(x, routes, w, scales, out, H, I, quant, path, nullptr, ws, ws_bytes, stream, nullptr, 0,
+                        nullptr, nullptr, nullptr, ev_start, ev_end);
 }
 
 int moe_forward_profiled(const void* x, const moe_routes* routes, const moe_packed_weights* w,

@@ -32,6 +32,8 @@
 //    launches with nothing in between.
 //  * FP8 blockwise: x and h arrive quantised with their per-128 scales; each
 //    64-byte K slice lies in one scale block.
+#include <hip/hip_ext.h>
+
 #include "common.cuh"
 #include "launch.h"
 #include "layout.cuh"
@@ -1047,7 +1049,8 @@ hipError_t launch_route_direct_gate_up(const FwdPlan& p, hipStream_t st) {
     const void* fn = rd_gu_fn(p.quant, c.nw, c.U);
     if (!fn) return hipErrorInvalidValue;
     void* args[] = {&a};
-    return hipLaunchKernel(fn, dim3(p.T * p.k, p.I / 32, c.rs), dim3(64 * c.nw), args, 0, st);
+    return hipExtLaunchKernel(fn, dim3(p.T * p.k, p.I / 32, c.rs), dim3(64 * c.nw), args, 0, st, p.ev_first_start,
+                              nullptr, 0);
 }
 
 // Down split: K parts per route (1, 2 or 4, dividing NSL) only while the grid
@@ -1073,38 +1076,38 @@ static RdDownCfg rd_down_cfg(int T, int H, int I, int k, int quant) {
 int rd_down_items(int T, int H, int I, int k, int quant) { return k * rd_down_cfg(T, H, I, k, quant).kp; }
 
 template <int Q, int NW, int KP>
-static hipError_t rd_dn_kp(const RdArgs& a, int U, hipStream_t st) {
+static hipError_t rd_dn_kp(const RdArgs& a, int U, hipStream_t st, hipEvent_t ev) {
     dim3 grid(a.T * (a.H / 32), a.k * KP);
     switch (U) {
-        case 8: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 8>), grid, dim3(64 * NW), 0, st, a); break;
-        case 6: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 6>), grid, dim3(64 * NW), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 4>), grid, dim3(64 * NW), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 3>), grid, dim3(64 * NW), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 2>), grid, dim3(64 * NW), 0, st, a); break;
-        default: hipLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 1>), grid, dim3(64 * NW), 0, st, a); break;
+        case 8: hipExtLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 8>), grid, dim3(64 * NW), 0, st, nullptr, ev, 0, a); break;
+        case 6: hipExtLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 6>), grid, dim3(64 * NW), 0, st, nullptr, ev, 0, a); break;
+        case 4: hipExtLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 4>), grid, dim3(64 * NW), 0, st, nullptr, ev, 0, a); break;
+        case 3: hipExtLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 3>), grid, dim3(64 * NW), 0, st, nullptr, ev, 0, a); break;
+        case 2: hipExtLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 2>), grid, dim3(64 * NW), 0, st, nullptr, ev, 0, a); break;
+        default: hipExtLaunchKernelGGL((rd_down_part_kernel<Q, NW, KP, 1>), grid, dim3(64 * NW), 0, st, nullptr, ev, 0, a); break;
     }
     return hipGetLastError();
 }
 
 template <int Q, int NW>
-static hipError_t rd_dn_nw(const RdArgs& a, const RdDownCfg& c, hipStream_t st) {
+static hipError_t rd_dn_nw(const RdArgs& a, const RdDownCfg& c, hipStream_t st, hipEvent_t ev) {
     switch (c.kp) {
-        case 1: return rd_dn_kp<Q, NW, 1>(a, c.U, st);
-        case 2: return rd_dn_kp<Q, NW, 2>(a, c.U, st);
-        default: return rd_dn_kp<Q, NW, 4>(a, c.U, st);
+        case 1: return rd_dn_kp<Q, NW, 1>(a, c.U, st, ev);
+        case 2: return rd_dn_kp<Q, NW, 2>(a, c.U, st, ev);
+        default: return rd_dn_kp<Q, NW, 4>(a, c.U, st, ev);
     }
 }
 
 template <int Q>
-static hipError_t rd_dn(const RdArgs& a, int quant, hipStream_t st) {
+static hipError_t rd_dn(const RdArgs& a, int quant, hipStream_t st, hipEvent_t ev) {
     const int elem = Q == RD_BF16 ? 2 : 1;
     const int NSL = a.I * elem / kSliceBytes;
     const RdDownCfg c = rd_down_cfg(a.T, a.H, a.I, a.k, quant);
     if (NSL % (c.kp * c.nw) != 0 || (NSL / c.kp / c.nw) % c.U != 0) return hipErrorInvalidValue;
     switch (c.nw) {
-        case 1: return rd_dn_nw<Q, 1>(a, c, st);
-        case 2: return rd_dn_nw<Q, 2>(a, c, st);
-        default: return rd_dn_nw<Q, 4>(a, c, st);
+        case 1: return rd_dn_nw<Q, 1>(a, c, st, ev);
+        case 2: return rd_dn_nw<Q, 2>(a, c, st, ev);
+        default: return rd_dn_nw<Q, 4>(a, c, st, ev);
     }
 }
 
@@ -1151,13 +1154,15 @@ hipError_t launch_route_direct_down(const FwdPlan& p, hipStream_t st) {
     if (bc.ok) {
         a.kp = bc.kp;
         const dim3 grid((unsigned)((long)p.T * (p.H / 32))), block(64 * bc.nw);
-        if (p.quant == Q_BF16) hipLaunchKernelGGL((rd_down_block_kernel<RD_BF16>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((rd_down_block_kernel<RD_TENSOR>), grid, block, 0, st, a);
+        if (p.quant == Q_BF16)
+            hipExtLaunchKernelGGL((rd_down_block_kernel<RD_BF16>), grid, block, 0, st, nullptr, p.ev_last_end, 0, a);
+        else
+            hipExtLaunchKernelGGL((rd_down_block_kernel<RD_TENSOR>), grid, block, 0, st, nullptr, p.ev_last_end, 0, a);
         return hipGetLastError();
     }
-    if (p.quant == Q_BF16) return rd_dn<RD_BF16>(a, p.quant, st);
-    if (p.quant == Q_FP8_TENSOR) return rd_dn<RD_TENSOR>(a, p.quant, st);
-    return rd_dn<RD_BLOCK>(a, p.quant, st);
+    if (p.quant == Q_BF16) return rd_dn<RD_BF16>(a, p.quant, st, p.ev_last_end);
+    if (p.quant == Q_FP8_TENSOR) return rd_dn<RD_TENSOR>(a, p.quant, st, p.ev_last_end);
+    return rd_dn<RD_BLOCK>(a, p.quant, st, p.ev_last_end);
 }
 
 }  // namespace moe

@@ -280,3 +280,22 @@ def test_block128_wide_scale_range(path):
     w = dict(w_gate_up=qgu, w_down=qd, s_gate_up=sgu, s_down=sd)
     _compare("block128 wide scale range", x_bits, a["logits"], k, weights_dev(w, "fp8_block128"), w,
              "fp8_block128", path)
+
+
+@pytest.mark.parametrize("name,B,path", [("decode_fp8_tensor", 2, "route_direct"), ("decode_bf16", 3, "grouped")])
+def test_forward_timed_same_bits(name, B, path):
+    """moe_forward_timed runs moe_forward's launches with events attached to the first and last
+    dispatch: the same output bits, and a positive device span."""
+    wl = WORKLOADS[name]
+    a = workload_inputs(name, batch=B)
+    pw, sc = workload_dev(name)
+    x = bf16_dev(a["x"])
+    r = moe.route(torch.from_numpy(a["logits"]).to(DEV), wl.k)
+    ref = moe.forward(x, r, pw, scales=sc, path=path)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = moe.forward(x, r, pw, scales=sc, path=path, device_events=(d0, d1))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    span = d0.elapsed_time(d1)
+    say(f"  {name} B={B} {path}: device span {span * 1e3:.2f} us")
+    assert 0.0 < span < 10.0
