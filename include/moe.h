@@ -182,8 +182,8 @@ int moe_pack_mx_scales(const uint8_t *s_gate_up, const uint8_t *s_down, int E, i
  * the requested path cannot run it.  Host-only; no GPU call.
  * ("perf: add small-batch route MMA for MoE", Dispatch.)  AUTO takes the
  * route-direct path while T*k <= 3E/4 and T <= 16 and the shape fits it
- * (the bound measured on MI355X with both paths forced), else grouped; MX
- * (MOE_FP8_MX32) always takes the grouped path. */
+ * (the bound measured on MI355X with both paths forced), else grouped; the
+ * same rule for every quantisation, MX included. */
 int moe_select_path(int T, int H, int I, int E, int k, int quant, int path);
 
 /* Bytes of workspace moe_forward needs for this shape, quantisation and path. */
@@ -201,7 +201,8 @@ size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int quant, 
  *   h_codes   grouped path: e4m3 [T*k,I], row i = the route at sorted position i
  *   h_scales  per-tensor fp32 [1] (both paths); block128 fp32 [T*k,I/128],
  *             sorted order (grouped) or route order r = t*k + j (route-direct);
- *             MX E8M0 [T*k,I/32], sorted order, bytes ordered as x_scales
+ *             MX E8M0 [T*k,I/32], sorted order (grouped) or route order
+ *             (route-direct), bytes ordered as x_scales
  * ("perf: add small-batch route MMA for MoE", Summary: the activation and
  * Down-input quantisation; exposed so callers and tests can inspect the
  * codes.)  bf16 has none of them.  Returns MOE_OK or the shape's error. */

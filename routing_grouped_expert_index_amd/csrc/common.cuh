@@ -52,6 +52,23 @@ __device__ __forceinline__ float scale_from_amax(float amax) {
     return amax > 0.0f ? amax / 448.0f : 1.0f;
 }
 
+// MX (E8M0 scale per 32 values): the byte of a group whose largest magnitude
+// is amax is floor(log2 amax) - 8 + 127 -- the float exponent field less 8, 8
+// being the largest exponent of e4m3 -- at least 0 (also for amax = 0 or
+// subnormal); the group's codes are e4m3(v * 2^(127 - b)), an exact scaling.
+__device__ __forceinline__ uint32_t mx_byte(float amax) {
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 255);
+    return (uint32_t)(ef > 8 ? ef - 8 : 0);
+}
+__device__ __forceinline__ float mx_inv(uint32_t b) { return __uint_as_float((254u - b) << 23); }
+// 2^(b - 127) as fp32 (b = 0: the subnormal 2^-127; b <= 254)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+    return __uint_as_float(b ? b << 23 : 0x00400000u);
+}
+// Position of group c's byte in a row of MX scale bytes as the MX GEMM reads
+// them: dword 2g + hh holds groups 8g + hh, 8g + 2 + hh, 8g + 4 + hh, 8g + 6 + hh.
+__device__ __forceinline__ int mx_scale_pos(int c) { return 8 * (c >> 3) + 4 * (c & 1) + ((c & 7) >> 1); }
+
 // z * sigmoid(z) with the hardware reciprocal (about 1 ulp in fp32)
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 

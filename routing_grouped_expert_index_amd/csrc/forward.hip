@@ -142,14 +142,13 @@ quant_mx32_kernel(const TIn* __restrict__ in, int rows, int cols, uint8_t* __res
     for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
     a = fmaxf(a, __shfl_xor(a, 1));
     a = fmaxf(a, __shfl_xor(a, 2));
-    const int ef = (int)((__float_as_uint(a) >> 23) & 255);
-    const uint32_t b = (uint32_t)(ef > 8 ? ef - 8 : 0);
-    const float inv = __uint_as_float((254u - b) << 23);   // 2^(127 - b)
+    const uint32_t b = mx_byte(a);
+    const float inv = mx_inv(b);   // 2^(127 - b)
     uint2 w;
     w.x = f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     w.y = f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     *reinterpret_cast<uint2*>(q + base) = w;
-    if (sub == 0) scales[row * gpr + 8 * (c >> 3) + 4 * (c & 1) + ((c & 7) >> 1)] = (uint8_t)b;
+    if (sub == 0) scales[row * gpr + mx_scale_pos(c)] = (uint8_t)b;
 }
 
 // amax over n values (n % 8 == 0), folded into *amax_bits with atomicMax on

@@ -573,9 +573,8 @@ gemm32_kernel(const GemmArgs g) {
                     a = fmaxf(a, fabsf(acc[0][m][i]));
                 }
                 a = fmaxf(a, __shfl_xor(a, 32));
-                const int ef = (int)((__float_as_uint(a) >> 23) & 255);
-                const uint32_t b = (uint32_t)(ef > 8 ? ef - 8 : 0);
-                const float inv = __uint_as_float((254u - b) << 23);   // 2^(127 - b), b <= 247
+                const uint32_t b = mx_byte(a);
+                const float inv = mx_inv(b);   // 2^(127 - b), b <= 246
                 u32x4 q;
 #pragma unroll
                 for (int t = 0; t < 4; ++t)

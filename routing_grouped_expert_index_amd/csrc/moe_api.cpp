@@ -9,7 +9,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "launch.h"
 
 namespace {
@@ -47,7 +47,6 @@ constexpr int kRouteDirectMaxTokens = 16;
 bool rd_shape_ok(int H, int I, int k, int quant) {
     const int elem = quant == MOE_BF16 ? 2 : 1;
     (void)k;
-    if (quant == MOE_FP8_MX32) return false;   // MX runs on the grouped path only
     return (long)H * elem <= 8192 && (long)I * elem <= 2048;
 }
 
@@ -84,7 +83,7 @@ int resolve_path(int T, int H, int I, int E, int k, int quant, int path) {
     if (path == MOE_PATH_ROUTE_DIRECT) {
         if (!rd_shape_ok(H, I, k, quant))
             return fail(MOE_ERR_UNSUPPORTED,
-                        "route-direct path: H*elem <= 8192 and I*elem <= 2048 bytes, not MX");
+                        "route-direct path: H*elem <= 8192 and I*elem <= 2048 bytes");
         return path;
     }
     return fail(MOE_ERR_INVALID_ARG, "unknown path %d", path);
@@ -112,14 +111,14 @@ Layout layout(int T, int H, int I, int E, int k, int quant, int path) {
     // here too, for inspection; it reads them from LDS)
     L.xq = take(quant != MOE_BF16 ? (size_t)T * H : 0);
     L.sx = take(quant == MOE_FP8_BLOCK128 ? sizeof(float) * (size_t)T * (H / 128)
-                : grouped && quant == MOE_FP8_MX32 ? (size_t)T * (H / 32) : 0);
+                : quant == MOE_FP8_MX32 ? (size_t)T * (H / 32) : 0);
     size_t hbytes = 0;
     if (quant == MOE_BF16) hbytes = R * I * 2;
     else if (quant == MOE_FP8_PER_TENSOR || !grouped) hbytes = R * I * 4;
     L.h = take(hbytes);
     L.hq = take(grouped && quant != MOE_BF16 ? R * I : 0);
     L.sh = take(quant == MOE_FP8_BLOCK128 ? sizeof(float) * R * (I / 128)
-                : grouped && quant == MOE_FP8_MX32 ? R * (I / 32) : 0);
+                : quant == MOE_FP8_MX32 ? R * (I / 32) : 0);
     L.y = take(grouped ? R * H * 2 : 0);
     const size_t rd_blocks = grouped ? 0 : (size_t)T * (H / 32);
     L.rd_hmax = take(!grouped && quant == MOE_FP8_PER_TENSOR
@@ -454,8 +453,9 @@ static int forward_impl(const void* x, const moe_routes* routes, const moe_packe
         MOE_STEP(moe::launch_combine(P, st), "combine");
     } else {
         // FP8 quantises x and h inside the route-direct kernels (per tensor: from
-        // all of x and the Gate/Up workgroups' h maxima; blockwise: per token or
-        // route row and 128 channels, in the workgroup that uses them)
+        // all of x and the Gate/Up workgroups' h maxima; blockwise and MX: per
+        // token or route row and 128 or 32 channels, in the workgroup that uses
+        // them)
         MOE_STEP(moe::launch_route_direct_gate_up(P, st), "rd_gate_up");
         MOE_STEP(moe::launch_route_direct_down(P, st), "rd_down_combine");
     }

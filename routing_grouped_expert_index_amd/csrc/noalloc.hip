@@ -7,7 +7,7 @@
 #include <atomic>
 #include <mutex>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "launch.h"
 
 namespace moe {

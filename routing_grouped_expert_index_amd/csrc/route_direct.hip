@@ -30,8 +30,18 @@
 //    kilobytes at decode sizes) and records the maximum of its 32 h values; the
 //    Down workgroups reduce those few hundred maxima.  So the path is two
 //    launches with nothing in between.
-//  * FP8 blockwise: x and h arrive quantised with their per-128 scales; each
-//    64-byte K slice lies in one scale block.
+//  * FP8 blockwise: x and h are quantised per token (route row) and 128
+//    channels in the workgroups that use them; each 64-byte K slice lies in one
+//    scale block.
+//  * MX ("[mxfp8 moe training] add per group blocked scale kernels", Summary:
+//    mxfp8 scales): x and h are quantised per 32 channels with an E8M0 byte in
+//    the workgroups that use them.  The weights are packed in the scaled MFMA's
+//    chunk order, so a lane's two 16-byte pieces of a slice belong to its two
+//    MX blocks (K [16hh, 16hh+16) of block 2s, [32+16hh, 48+16hh) of block
+//    2s+1); each piece's dot product takes its block's weight and activation
+//    scales.  The weight scale bytes come from the dwords moe_pack_mx_scales
+//    lays out for the grouped GEMM: dword (32-row block, slice group g, lane
+//    32hh' + j) holds row j's scales of blocks 8g + 2u + hh' in byte u.
 #include <hip/hip_ext.h>
 
 #include "common.cuh"
@@ -45,17 +55,17 @@
 
 namespace moe {
 
-enum RdQuant { RD_BF16 = 0, RD_TENSOR = 1, RD_BLOCK = 2 };
+enum RdQuant { RD_BF16 = 0, RD_TENSOR = 1, RD_BLOCK = 2, RD_MX = 3 };
 
 struct RdArgs {
-    const uint8_t* act;      // x bf16 [T,H] (bf16, per-tensor) or e4m3 codes [T,H] (block)
+    const uint8_t* act;      // x bf16 [T,H]
     const int32_t* ids;      // [T*k]
     const float* tw;         // [T*k]
     const uint8_t* wgu;      // packed Gate/Up
     const uint8_t* wd;       // packed Down
-    const float* s_gu;
+    const float* s_gu;       // weight scales (MX: the packed E8M0 dwords)
     const float* s_d;
-    const uint8_t* h;        // Down input: bf16 [R][I] | fp32 [R][I] (per-tensor) | e4m3 [R][I] (block)
+    const uint8_t* h;        // Down input: bf16 [R][I] | fp32 [R][I] (FP8, quantised by the Down kernel)
     void* hout;              // Gate/Up output: bf16 [R][I] | fp32 [R][I]
     float* hmax;             // per-tensor: max |h| per Gate/Up workgroup [R][I/32]
     float* part;             // Down partial sums [T*H/32][items][32]
@@ -74,8 +84,10 @@ struct RdArgs {
     float* tw_w;
     int acc;                 // out += the layer sum (else out = it)
     // FP8 inspection copies in the workspace (null for bf16): each token's x
-    // codes [T][H] and block scales [T][H/128]; per-tensor x and h scales
-    // (scal_out[0], scal_out[1]); blockwise h scales [R][I/128] in route order
+    // codes [T][H] and block scales [T][H/128] (MX: E8M0 bytes [T][H/32] in
+    // the MX GEMM's byte order); per-tensor x and h scales (scal_out[0],
+    // scal_out[1]); blockwise h scales [R][I/128] (MX: bytes [R][I/32]) in
+    // route order
     uint8_t* xq_out;
     float* sx_out;
     float* scal_out;
@@ -225,6 +237,64 @@ __device__ __forceinline__ void quant_row_block128(uint8_t* dst, float* sdst, co
     }
 }
 
+// quantise n values (n % 32 == 0) of a bf16 (or fp32) row per 32-value MX
+// group: the group's E8M0 byte (mx_byte of its amax) into sdst[group] and
+// codes e4m3(v * 2^(127 - b)) into dst in LDS; whole workgroup, 4 lanes per
+// group (8 values each)
+template <typename T, int NW>
+__device__ __forceinline__ void quant_row_mx32(uint8_t* dst, uint8_t* sdst, const T* src, int n) {
+    for (int i = threadIdx.x * 8; i < n; i += 64 * NW * 8) {
+        float v[8];
+        if constexpr (sizeof(T) == 2) {
+            bf16x8_to_f32(*reinterpret_cast<const u32x4*>(src + i), v);
+        } else {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(src + i);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(src + i + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { v[q] = a[q]; v[4 + q] = b[q]; }
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+        m = fmaxf(m, __shfl_xor(m, 1));   // the group's 4 lanes
+        m = fmaxf(m, __shfl_xor(m, 2));
+        const uint32_t b = mx_byte(m);
+        const float inv = mx_inv(b);
+        uint2 c;
+        c.x = f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        c.y = f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        *reinterpret_cast<uint2*>(dst + i) = c;
+        if ((threadIdx.x & 3) == 0) sdst[i / 32] = (uint8_t)b;
+    }
+}
+
+// MX: the dot of one 16-byte piece of e4m3 weights with 16 e4m3 activations
+__device__ __forceinline__ float dot16_e4m3(const u32x4& w, const u32x4& x) {
+    float wf[16], xf[16];
+    e4m3x16_to_f32(w, wf);
+    e4m3x16_to_f32(x, xf);
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc = fmaf(wf[i], xf[i], acc);
+    return acc;
+}
+
+// MX: the lane's two weight pieces of a slice (blocks 2s and 2s+1) times the
+// activation codes of the same K positions, each scaled by its blocks'
+// weight scale (byte `sh` of dword ws[q]) and activation scale byte sa[q]
+__device__ __forceinline__ float dot_slice_mx(const u32x4 w[2], const uint8_t* act, int s, int hh,
+                                              const uint32_t ws[2], const uint8_t* sa, int sh) {
+    const uint8_t* p = act + s * 64 + hh * 16;
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(p + 32 * q);
+        const float sc = e8m0_to_f32((ws[q] >> sh) & 255u) * e8m0_to_f32(sa[2 * s + q]);
+        acc = fmaf(dot16_e4m3(w[q], x), sc, acc);
+    }
+    return acc;
+}
+
 // dot of the lane's two weight halves of one slice with its activation values
 template <bool FP8>
 __device__ __forceinline__ float dot_slice(const u32x4 w[2], const float v[32]) {
@@ -280,6 +350,7 @@ rd_gate_up_kernel(const RdArgs a) {
     constexpr bool FP8 = Q != RD_BF16;
     __shared__ __attribute__((aligned(16))) uint8_t xrow[kRdActBytes];
     __shared__ float sxs[Q == RD_BLOCK ? kRdActBytes / 128 : 1];   // blockwise: the row's x scales
+    __shared__ uint8_t sxb[Q == RD_MX ? kRdActBytes / 32 : 4];     // MX: the row's x scale bytes
     __shared__ float red[NW][2][32];
     __shared__ float sred[NW];
     __shared__ int s_eg;
@@ -345,6 +416,10 @@ rd_gate_up_kernel(const RdArgs a) {
         for (int i = threadIdx.x; i < a.T * (a.H / 32); i += 64 * NW) a.cnt[i] = 0;
     int e = 0;
     const uint8_t *wg = nullptr, *wu = nullptr;
+    // MX: this lane's row in the scale dwords of the gate and up blocks
+    // (dwords [slice group][64 lanes]; piece q of a slice reads lane jr + 32q)
+    const uint32_t *swg = nullptr, *swu = nullptr;
+    const int NG = a.H / 256;
     // the expert's index in this call's slice and its weight rows; false for
     // another slice's expert (no h, a zero share of the h amax)
     auto resolve = [&](int eg) __attribute__((always_inline)) {
@@ -357,6 +432,10 @@ rd_gate_up_kernel(const RdArgs a) {
         }
         wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + (32 * hh + jr) * 16 + ls * 2048;
         wu = wg + gstride;
+        if constexpr (Q == RD_MX) {
+            swg = reinterpret_cast<const uint32_t*>(a.s_gu) + ((long)e * (2 * a.I / 32) + 2 * G) * NG * 64 + jr;
+            swu = swg + NG * 64;
+        }
         return true;
     };
     // FP8: one workgroup of each token (h block 0, split 0, and the token's
@@ -373,7 +452,9 @@ rd_gate_up_kernel(const RdArgs a) {
         writer = r == t * a.k;
 
     // two load buffers: batch b+1 is requested before batch b is computed
+    // (MX: with each slice's scale dwords of its two pieces)
     u32x4 vg[2][U][2], vu[2][U][2];
+    uint32_t mg[Q == RD_MX ? 2 : 1][U][2], mu[Q == RD_MX ? 2 : 1][U][2];
     auto load_batch = [&](auto Bc, int S) __attribute__((always_inline)) {
         constexpr int B = decltype(Bc)::value;
 #pragma unroll
@@ -383,6 +464,11 @@ rd_gate_up_kernel(const RdArgs a) {
                 const long off = ((long)(S + u) << lrs) * 2048 + q * 1024;
                 vg[B][u][q] = *reinterpret_cast<const u32x4*>(wg + off);
                 vu[B][u][q] = *reinterpret_cast<const u32x4*>(wu + off);
+                if constexpr (Q == RD_MX) {
+                    const int g = ((((S + u) << lrs) + ls) >> 2) * 64 + 32 * q;
+                    mg[B][u][q] = swg[g];
+                    mu[B][u][q] = swu[g];
+                }
             }
         __builtin_amdgcn_sched_barrier(0);   // the whole batch stays in flight
     };
@@ -400,6 +486,8 @@ rd_gate_up_kernel(const RdArgs a) {
             quant_row<uint16_t, NW>(xrow, x + (long)t * a.H, a.H, xs);
         } else if constexpr (Q == RD_BLOCK) {   // the token's codes and per-128 scales, here
             quant_row_block128<uint16_t, NW>(xrow, sxs, x + (long)t * a.H, a.H);
+        } else if constexpr (Q == RD_MX) {      // ... per-32 E8M0 bytes
+            quant_row_mx32<uint16_t, NW>(xrow, sxb, x + (long)t * a.H, a.H);
         } else {
             stage_row<NW>(xrow, a.act + (long)t * Kb, Kb);
         }
@@ -454,6 +542,28 @@ rd_gate_up_kernel(const RdArgs a) {
                 if ((threadIdx.x & 15) == 0) sxs[c / 16] = sc;
             }
         }
+    } else if constexpr (Q == RD_MX) {
+        // per 32 values (4 lanes of 8): the E8M0 byte of the group's amax, codes
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+            const int c = threadIdx.x + p * NT;
+            float v[8];
+            bf16x8_to_f32(xr[p], v);
+            float m = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+            m = fmaxf(m, __shfl_xor(m, 1));   // the group's 4 lanes
+            m = fmaxf(m, __shfl_xor(m, 2));
+            const uint32_t bx = mx_byte(m);
+            const float inv = mx_inv(bx);
+            uint2 q8;
+            q8.x = f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+            q8.y = f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+            if (c < rch) {
+                *reinterpret_cast<uint2*>(xrow + 8 * c) = q8;
+                if ((threadIdx.x & 3) == 0) sxb[c / 4] = (uint8_t)bx;
+            }
+        }
     } else {
 #pragma unroll
         for (int p = 0; p < RP; ++p) {
@@ -475,6 +585,9 @@ rd_gate_up_kernel(const RdArgs a) {
             *reinterpret_cast<u32x4*>(xq + i) = *reinterpret_cast<const u32x4*>(xrow + i);
         if constexpr (Q == RD_BLOCK) {
             for (int i = threadIdx.x; i < a.H / 128; i += 64 * NW) a.sx_out[(long)t * (a.H / 128) + i] = sxs[i];
+        } else if constexpr (Q == RD_MX) {
+            uint8_t* so = reinterpret_cast<uint8_t*>(a.sx_out) + (long)t * (a.H / 32);
+            for (int i = threadIdx.x; i < a.H / 32; i += 64 * NW) so[mx_scale_pos(i)] = sxb[i];
         } else {
             if (t == 0 && threadIdx.x == 0) a.scal_out[0] = xs;
         }
@@ -495,8 +608,12 @@ rd_gate_up_kernel(const RdArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int sl = ((S + u) << lrs) + ls;   // this lane's slice
-            float dg, du;
-            if constexpr (!FP8) {
+            float dg = 0.0f, du = 0.0f;
+            if constexpr (Q == RD_MX) {   // the scales are inside the products
+                const int sh = 8 * (sl & 3);
+                dg = dot_slice_mx(vg[B][u], xrow, sl, hh, mg[B][u], sxb, sh);
+                du = dot_slice_mx(vu[B][u], xrow, sl, hh, mu[B][u], sxb, sh);
+            } else if constexpr (!FP8) {
                 u32x4 xw[2];
                 lds_act_raw(xrow, sl, hh, xw);
                 dg = dot_slice_bf16(vg[B][u], xw, 0.0f);
@@ -627,9 +744,10 @@ __global__ void __launch_bounds__(64 * NW)
 rd_down_part_kernel(const RdArgs a) {
     constexpr bool FP8 = Q != RD_BF16;
     // FP8: the route's h row as e4m3 codes (quantised here), blockwise with its
-    // per-128 scales
+    // per-128 scales, MX with its per-32 E8M0 bytes
     __shared__ __attribute__((aligned(16))) uint8_t hrow_s[FP8 ? 2048 : 16];
     __shared__ float shs[Q == RD_BLOCK ? 2048 / 128 : 1];
+    __shared__ uint8_t shb[Q == RD_MX ? 2048 / 32 : 4];
     __shared__ float red[NW][32];
     __shared__ int last_s;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -648,16 +766,23 @@ rd_down_part_kernel(const RdArgs a) {
     const int s0 = kp * (NSL / KP) + wave * spw;
     const int n0 = down_col_of_packed(32 * g32);   // all 32 rows lie in one 128-column block
     const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + lane * 16;
+    // MX: row j's scale dwords of this 32-row block (piece q of a slice: lane j + 32q)
+    const uint32_t* swd = Q == RD_MX ? reinterpret_cast<const uint32_t*>(a.s_d) +
+                                           ((long)e * nb + g32) * (a.I / 256) * 64 + (lane & 31)
+                                     : nullptr;
 
     u32x4 vw[U][2];
+    uint32_t mw[Q == RD_MX ? U : 1][2];
     u32x4 va[U][2];   // bf16: activation slices of the batch (the row is not staged in LDS)
     const uint8_t* hg = a.h + (long)r * Kb + hh * 32;
     auto load_batch = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 2; ++q) {
                 vw[u][q] = *reinterpret_cast<const u32x4*>(wb + (long)(s + u) * 2048 + q * 1024);
+                if constexpr (Q == RD_MX) mw[u][q] = swd[((s + u) >> 2) * 64 + 32 * q];
+            }
         if constexpr (!FP8) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -692,6 +817,13 @@ rd_down_part_kernel(const RdArgs a) {
         __syncthreads();
         if (g32 == 0 && kp == 0)   // inspection copy of the route's h scales
             for (int i = threadIdx.x; i < a.I / 128; i += 64 * NW) a.sh_out[(long)r * (a.I / 128) + i] = shs[i];
+    } else if constexpr (Q == RD_MX) {     // ... per 32 channels
+        quant_row_mx32<float, NW>(hrow_s, shb, reinterpret_cast<const float*>(a.h) + (long)r * a.I, a.I);
+        __syncthreads();
+        if (g32 == 0 && kp == 0) {
+            uint8_t* so = reinterpret_cast<uint8_t*>(a.sh_out) + (long)r * (a.I / 32);
+            for (int i = threadIdx.x; i < a.I / 32; i += 64 * NW) so[mx_scale_pos(i)] = shb[i];
+        }
     }
 
     float y = 0.0f;
@@ -703,7 +835,9 @@ rd_down_part_kernel(const RdArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float d;
-            if constexpr (!FP8) {
+            if constexpr (Q == RD_MX) {
+                d = dot_slice_mx(vw[u], hrow, s + u, hh, mw[u], shb, 8 * ((s + u) & 3));
+            } else if constexpr (!FP8) {
                 d = dot_slice_bf16(vw[u], va[u], 0.0f);
             } else {
                 float v[32];
@@ -977,6 +1111,7 @@ static const void* rd_gu_fn_q(int nw, int U) {
 static const void* rd_gu_fn(int quant, int nw, int U) {
     if (quant == Q_BF16) return rd_gu_fn_q<RD_BF16>(nw, U);
     if (quant == Q_FP8_TENSOR) return rd_gu_fn_q<RD_TENSOR>(nw, U);
+    if (quant == Q_FP8_MX) return rd_gu_fn_q<RD_MX>(nw, U);
     return rd_gu_fn_q<RD_BLOCK>(nw, U);
 }
 
@@ -986,12 +1121,12 @@ static const void* rd_gu_fn(int quant, int nw, int U) {
 constexpr int kRdMaxDevices = 64;
 static long rd_gu_resident(int quant, int nw, int U) {
     static std::atomic<int> cus[kRdMaxDevices];
-    static std::atomic<int> occ[kRdMaxDevices][3][5][9];   // 1 + occupancy, 0 = not asked yet
+    static std::atomic<int> occ[kRdMaxDevices][4][5][9];   // 1 + occupancy, 0 = not asked yet
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kRdMaxDevices) return 0;
     int lg = 0;
     while ((1 << lg) < nw) ++lg;
-    if (quant < 0 || quant > 2 || lg > 4 || U < 1 || U > 8) return 0;
+    if (quant < 0 || quant > 3 || lg > 4 || U < 1 || U > 8) return 0;
     int n = cus[dev].load(std::memory_order_relaxed);
     if (n == 0) {
         int c = 0;
@@ -1120,7 +1255,7 @@ struct RdBlockCfg {
 };
 static RdBlockCfg rd_block_cfg(int H, int I, int k, int quant) {
     RdBlockCfg c{false, 1, 1};
-    if (quant == Q_FP8_BLOCK) return c;
+    if (quant == Q_FP8_BLOCK || quant == Q_FP8_MX) return c;
     const int elem = quant == Q_BF16 ? 2 : 1;
     const int NSL = I * elem / kSliceBytes, ms = quant == Q_BF16 ? kRdBlockMaxSlices : kRdBlockMaxSlicesFp8;
     if ((long)k * 32 * I * elem > kRdBlockMaxBytes || NSL < 1) return c;
@@ -1162,6 +1297,7 @@ hipError_t launch_route_direct_down(const FwdPlan& p, hipStream_t st) {
     }
     if (p.quant == Q_BF16) return rd_dn<RD_BF16>(a, p.quant, st, p.ev_last_end);
     if (p.quant == Q_FP8_TENSOR) return rd_dn<RD_TENSOR>(a, p.quant, st, p.ev_last_end);
+    if (p.quant == Q_FP8_MX) return rd_dn<RD_MX>(a, p.quant, st, p.ev_last_end);
     return rd_dn<RD_BLOCK>(a, p.quant, st, p.ev_last_end);
 }
 

@@ -38,10 +38,13 @@ def test_select_path_rules():
     assert moe.select_path(8192, 2048, 768, 128, 8) == "grouped"
     assert moe.select_path(64, 256, 512, 16, 8) == "grouped"
     assert moe.select_path(1, 2048, 768, 128, 8, "bf16", "grouped") == "grouped"
-    # MX FP8 runs on the grouped path only, H and I multiples of 256
-    assert moe.select_path(1, 2048, 768, 128, 8, "fp8_mx32") == "grouped"
+    # MX FP8 follows the same rule (H and I multiples of 256, I <= 2048 on route-direct)
+    assert moe.select_path(1, 2048, 768, 128, 8, "fp8_mx32") == "route_direct"
+    assert moe.select_path(13, 2048, 768, 128, 8, "fp8_mx32") == "grouped"
+    assert moe.select_path(1, 2048, 768, 128, 8, "fp8_mx32", "route_direct") == "route_direct"
+    assert moe.select_path(1, 2048, 4096, 128, 8, "fp8_mx32") == "grouped"      # I past 2048 bytes
     with pytest.raises(moe.MoeError):
-        moe.select_path(1, 2048, 768, 128, 8, "fp8_mx32", "route_direct")
+        moe.select_path(1, 2048, 4096, 128, 8, "fp8_mx32", "route_direct")
     with pytest.raises(moe.MoeError):
         moe.select_path(64, 2048, 192, 128, 8, "fp8_mx32")
     assert moe.select_path(64, 2048, 768, 128, 8, "bf16", "route_direct") == "route_direct"

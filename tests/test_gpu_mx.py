@@ -1,6 +1,6 @@
 """GPU parity of MX FP8 (e4m3 with an E8M0 power-of-two scale per 32 values along K) on the
-grouped path, against the oracle's MX forward ("[mxfp8 moe training] add per group blocked scale
-kernels", Summary: mxfp8 scales); tolerance as for the other FP8 modes."""
+grouped and route-direct paths, against the oracle's MX forward ("[mxfp8 moe training] add per
+group blocked scale kernels", Summary: mxfp8 scales); tolerance as for the other FP8 modes."""
 import numpy as np
 import pytest
 import torch
@@ -35,17 +35,68 @@ MX_CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["grouped", "route_direct"])
 @pytest.mark.parametrize("T,H,I,E,k,tag", MX_CASES)
-def test_mx_forward_parity(T, H, I, E, k, tag):
-    say(f"mx {tag}: T={T} H={H} I={I} E={E} k={k}")
+def test_mx_forward_parity(T, H, I, E, k, tag, path):
+    say(f"mx {tag} {path}: T={T} H={H} I={I} E={E} k={k}")
     a = random_activations(T, H, E, seed=400 + T)
     lg = a["logits"]
     if tag == "hot experts":
         lg = lg.copy()
         lg[:, :k] += 50.0
     w = random_weights(E, H, I, "fp8_mx32", seed=401 + I)
-    got, ref = _layer(a["x"], lg, k, w)
-    check_out(got, ref, "fp8", tag)
+    got, ref = _layer(a["x"], lg, k, w, path=path)
+    check_out(got, ref, "fp8", f"{tag} {path}")
+
+
+_DECODE_W = {}
+
+
+def _decode_weights(H, I, E):
+    """One MX weight set per decode shape, kept while consecutive cases use it."""
+    if (H, I, E) not in _DECODE_W:
+        _DECODE_W.clear()
+        w = random_weights(E, H, I, "fp8_mx32", seed=460 + I)
+        _DECODE_W[(H, I, E)] = (w, weights_dev(w, "fp8_mx32"))
+    return _DECODE_W[(H, I, E)]
+
+
+MX_DECODE = [(H, I, B) for H, I in ((2048, 768), (4096, 512)) for B in range(1, 9)]
+
+
+@pytest.mark.parametrize("H,I,B", MX_DECODE)
+def test_mx_route_direct_decode(H, I, B):
+    """Route-direct MX at decode batches B = 1..8, E=128, top-8 (the shapes of the bf16 and
+    blockwise decode layers): every launch shape the batch sizes select (row splits, waves per
+    workgroup, Down K parts), the whole output against the oracle."""
+    E, k = 128, 8
+    w, (pw, sc) = _decode_weights(H, I, E)
+    a = random_activations(B, H, E, seed=470 + B)
+    li = moe.forward_launch_info(B, H, I, E, k, "fp8_mx32", "route_direct")
+    say(f"mx route-direct decode B={B} H={H} I={I}: {li}")
+    r = moe.route(torch.from_numpy(a["logits"]).to(DEV), k)
+    out = moe.forward(bf16_dev(a["x"]), r, pw, quant="fp8_mx32", scales=sc, path="route_direct")
+    torch.cuda.synchronize()
+    ref_r = oracle.route(a["logits"], k)
+    check_routing(routes_np(r), ref_r)
+    check_out(out.float().cpu().numpy(), oracle_out(a["x"], ref_r, w, "fp8_mx32"), "fp8",
+              f"mx decode B={B}")
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_mx_decode_forward_folded_routing(B):
+    """moe_decode_forward in MX: the routing taken inside the Gate/Up kernel from host logits."""
+    H, I, E, k = 2048, 768, 128, 8
+    w, (pw, sc) = _decode_weights(H, I, E)
+    a = random_activations(B, H, E, seed=480 + B)
+    say(f"mx decode_forward B={B}")
+    out, r = moe.decode_forward(torch.from_numpy(a["logits"]).to(DEV), bf16_dev(a["x"]), k, pw,
+                                quant="fp8_mx32", scales=sc, path="route_direct")
+    torch.cuda.synchronize()
+    ref_r = oracle.route(a["logits"], k)
+    assert np.array_equal(r.topk_ids.cpu().numpy().reshape(B, k), ref_r["topk_ids"])
+    check_out(out.float().cpu().numpy(), oracle_out(a["x"], ref_r, w, "fp8_mx32"), "fp8",
+              f"mx decode_forward B={B}")
 
 
 def test_mx_prefill_every_tile():
@@ -62,7 +113,8 @@ def test_mx_prefill_every_tile():
     check_out(got, ref, "fp8", "mx prefill every tile")
 
 
-def test_mx_wide_scale_range():
+@pytest.mark.parametrize("path", ["grouped", "route_direct"])
+def test_mx_wide_scale_range(path):
     """Per-32 magnitudes spanning 1e4 along K in x and in the weights: every MX block takes a very
     different E8M0 byte, so a scale applied to the wrong 32 values shows."""
     T, H, I, E, k = 29, 512, 256, 4, 2
@@ -75,11 +127,12 @@ def test_mx_wide_scale_range():
     qgu, sgu = quantise_weight_mx32(wgu)
     qd, sd = quantise_weight_mx32(wd)
     w = dict(w_gate_up=qgu, w_down=qd, s_gate_up=sgu, s_down=sd)
-    got, ref = _layer(x_bits, a["logits"], k, w)
-    check_out(got, ref, "fp8", "mx wide scale range")
+    got, ref = _layer(x_bits, a["logits"], k, w, path=path)
+    check_out(got, ref, "fp8", f"mx wide scale range {path}")
 
 
-def test_mx_expert_slices_accumulate():
+@pytest.mark.parametrize("path", ["grouped", "route_direct"])
+def test_mx_expert_slices_accumulate(path):
     T, H, I, E, k = 40, 256, 256, 8, 2
     a = random_activations(T, H, E, seed=430)
     w = random_weights(E, H, I, "fp8_mx32", seed=431)
@@ -91,12 +144,12 @@ def test_mx_expert_slices_accumulate():
         ws = {key: (None if w[key] is None else np.ascontiguousarray(w[key][e0:e0 + n])) for key in w}
         pw, sc = weights_dev(ws, "fp8_mx32")
         moe.forward(bf16_dev(a["x"]), r, pw, quant="fp8_mx32", scales=sc, out=shared, expert_begin=e0,
-                    num_experts=n, accumulate=True)
+                    num_experts=n, accumulate=True, path=path)
         total += oracle.forward(a["x"], ref_r["topk_ids"], ref_r["topk_weights"], ws["w_gate_up"], ws["w_down"],
                                 quant="fp8_mx32", s_gate_up=ws["s_gate_up"], s_down=ws["s_down"],
                                 expert_begin=e0)
     torch.cuda.synchronize()
-    check_out(shared.float().cpu().numpy(), total, "fp8", "mx slices accumulated")
+    check_out(shared.float().cpu().numpy(), total, "fp8", f"mx slices accumulated {path}")
 
 
 def test_mx_scale_packing_layout():

@@ -124,6 +124,8 @@ CASES = [
     (3, 1024, 256, 16, 4, "fp8_block128", "route_direct", False),
     (3, 1024, 256, 16, 4, "fp8_block128", "route_direct", True),
     (150, 1024, 256, 16, 4, "fp8_mx32", "grouped", False),
+    (3, 1024, 256, 16, 4, "fp8_mx32", "route_direct", False),
+    (3, 1024, 256, 16, 4, "fp8_mx32", "route_direct", True),
 ]
 
 
