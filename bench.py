@@ -641,6 +641,7 @@ def main():
         line["crossover"] = dict(
             timing="cold HBM, moe_route + moe_forward between two HIP events, median",
             decode_fp8_tensor=bench_crossover(torch, moe, "decode_fp8_tensor", range(1, 17), 30),
+            decode_fp8_mx=bench_crossover(torch, moe, "decode_fp8_mx", range(1, 17), 30),
             decode_bf16=bench_crossover(torch, moe, "decode_bf16", range(1, 17), 30))
         torch.cuda.empty_cache()
         log("the pages' FP8 decode shapes, forward alone in a HIP graph ...")
@@ -658,6 +659,11 @@ def main():
         line["decode_fp8_per_tensor"] = dict(
             workload="decode_fp8_tensor H=4096 I=192 E=192 top-8",
             batches=bench_decode(torch, moe, "decode_fp8_tensor", (1, 2, 3, 4), args.decode_iters))
+        torch.cuda.empty_cache()
+        log("decode MX fp8 B=1..4 ...")
+        line["decode_fp8_mx32"] = dict(
+            workload="decode_fp8_mx H=4096 I=512 E=128 top-8, MX e4m3 (E8M0 per 32 along K)",
+            batches=bench_decode(torch, moe, "decode_fp8_mx", (1, 2, 3, 4), args.decode_iters))
         torch.cuda.empty_cache()
         log("prefill fp8 block128 T=4096 ...")
         p5 = bench_prefill(torch, moe, "prefill_fp8_block", args.steps, args.warmup)

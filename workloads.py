@@ -25,6 +25,7 @@ Workloads (the shapes of the layers the pages measure):
   prefill_bf16       T=8192, H=2048, I=768, E=128, k=8, Zipf-biased routing
   prefill_fp8_block  T=4096, H=4096, I=512, E=128, k=8, fp8 128x128 blockwise
   prefill_fp8_mx     the same shape, MX fp8 (E8M0 scale per 32 values along K)
+  decode_fp8_mx      T=B in 1..8 with prefill_fp8_mx's weights (MX decode)
 """
 from __future__ import annotations
 
@@ -64,6 +65,9 @@ WORKLOADS = {
                                   5, 5),
     # the same layer shape with MX FP8 weights (E8M0 scale per 32 values along K)
     "prefill_fp8_mx": Workload("prefill_fp8_mx", 4096, 4096, 512, 128, 8, "fp8_mx32", 7, 5),
+    # decode batches over the same MX layer
+    "decode_fp8_mx": Workload("decode_fp8_mx", 8, 4096, 512, 128, 8, "fp8_mx32", 7, 700,
+                              batches=(1, 2, 3, 4, 5, 6, 7, 8)),
 }
 
 
