@@ -135,14 +135,17 @@ def bench_prefill(torch, moe, name, steps, warmup, stage_steps=10):
 
 
 # HBM traffic of one Gate/Up launch from two rocprofv3 counter passes (FETCH_SIZE,
-# WRITE_SIZE; KiB per dispatch), each scaled by what the counter reads for a
-# plain 1 GiB copy kernel: FETCH_SIZE reads 524303 KiB for 1 GiB read (x2.0),
-# WRITE_SIZE reads exactly 1 GiB (x1.0).  Valid only for the GEMM source the
-# counters were taken on; any edit to it turns the figure into null.
-FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524303.0, 1.0
+# WRITE_SIZE; KiB per dispatch, median over the run's launches), each scaled by
+# what the counter reads for a plain 1 GiB copy kernel in the same run:
+# FETCH_SIZE reads 524300.5 KiB for 1 GiB read (x2.0), WRITE_SIZE exactly 1 GiB
+# (x1.0).  Valid only for the GEMM source the counters were taken on; any edit
+# to it turns the figure into null.
+FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524300.5, 1.0
+_GEMM_SHA = "89782dec031ea208e1a3cf19809c0ec6861455a490c473f5b2f861ec4586baed"
 COUNTER_TRAFFIC = {
-    "prefill_bf16": dict(gemm_sha256="0b4c38135dcab7544d90ea6facdbe160de9129dc510abeb242c3d98831e4c177",
-                         fetch_kib=804602.4, write_kib=98329.5),
+    "prefill_bf16": dict(gemm_sha256=_GEMM_SHA, fetch_kib=795007.8, write_kib=98312.4),
+    "prefill_fp8_block": dict(gemm_sha256=_GEMM_SHA, fetch_kib=381936.7, write_kib=17424.7),
+    "prefill_fp8_mx": dict(gemm_sha256=_GEMM_SHA, fetch_kib=419999.2, write_kib=17500.1),
 }
 
 
