@@ -331,14 +331,17 @@ int moe_forward_timed(const void *x, const moe_routes *routes, const moe_packed_
                       void *ws, size_t ws_bytes, void *stream, void *ev_start, void *ev_end);
 
 /* moe_forward with stage timing for profilers and benchmarks: the same
- * kernels, plus hipEventRecord(stage_events[i], stream) before the first
- * launch and after each launch (no synchronisation).  stage_events holds
- * n_events caller-created hipEvent_t handles; recording stops when they run
- * out, and a NULL entry records nothing at that point (each recorded event
- * costs the stream a few microseconds, so a caller timing one stage passes
- * only the two handles around it).  *n_stages receives the number of launches and stage_names (may be
- * NULL) a comma-separated list of their names, e.g.
- * "init,gate_up,down,combine" for the bf16 grouped path. */
+ * kernels, with stage_events[0] attached to the first kernel's dispatch
+ * (recorded when it starts) and stage_events[i] to the dispatch of stage i's
+ * last kernel (recorded when it ends), through hipExtLaunchKernel, so no
+ * marker packet sits between two kernels and the timing does not slow the
+ * stream; stage_events[i] - stage_events[i-1] is then stage i's device time
+ * (from the end of the previous stage, the kernels running back to back).
+ * stage_events holds n_events caller-created hipEvent_t handles; stages past
+ * them and NULL entries take no event.  No synchronisation.  *n_stages
+ * receives the number of stages and stage_names (may be NULL) a
+ * comma-separated list of their names, e.g. "init,gate_up,down,combine" for
+ * the bf16 grouped path. */
 int moe_forward_profiled(const void *x, const moe_routes *routes, const moe_packed_weights *w,
                          const moe_scales *scales, void *out, int H,
                          int I, int quant, int path, void *ws, size_t ws_bytes, void *stream,

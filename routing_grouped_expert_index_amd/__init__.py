@@ -375,9 +375,10 @@ def forward(x: torch.Tensor, routes: Routes, weights: PackedWeights,
     global, and accumulate=True adds the slice's sum into `out`.
 
     With events (a list of torch.cuda.Event(enable_timing=True) or None) it
-    calls moe_forward_profiled instead, which records events[0] before the
-    first launch and events[i] after launch i (None entries record nothing),
-    and returns (out, stage_names).
+    calls moe_forward_profiled instead, which attaches events[0] to the first
+    kernel's start and events[i] to the end of stage i's last kernel (None
+    entries take no event; no marker packet between kernels), and returns
+    (out, stage_names).
 
     With device_events=(start, end) (torch.cuda.Event(enable_timing=True)) it
     calls moe_forward_timed: start/end are attached to the first and last kernel

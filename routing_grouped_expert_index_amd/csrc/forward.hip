@@ -60,7 +60,7 @@ forward_init_kernel(int E, const int32_t* __restrict__ offsets, int build_tiles,
 hipError_t launch_forward_init(const FwdPlan& p, bool build_tiles, hipStream_t st) {
     // the tile map covers the expert slice: offsets + e0 for nloc experts, so a
     // tile names its expert by its index in the slice (the weights' index)
-    hipExtLaunchKernelGGL(forward_init_kernel, dim3(1), dim3(kMaxExperts), 0, st, p.ev_first_start, nullptr, 0,
+    hipExtLaunchKernelGGL(forward_init_kernel, dim3(1), dim3(kMaxExperts), 0, st, p.ev_first_start, p.ev_stage_end, 0,
                           p.nloc, p.offsets + p.e0, build_tiles ? 1 : 0, p.tiles, p.ntiles, p.amax);
     return hipGetLastError();
 }
@@ -242,29 +242,29 @@ constexpr long kSmallQuant = 1L << 16;
 hipError_t launch_quant_x(const FwdPlan& p, hipStream_t st) {
     if (p.quant == Q_FP8_MX) {
         const long groups = (long)p.T * (p.H / 32);
-        hipLaunchKernelGGL(quant_mx32_kernel<uint16_t>, dim3((unsigned)((groups + 63) / 64)), dim3(256), 0, st,
-                           p.x, p.T, p.H, p.xq, reinterpret_cast<uint8_t*>(p.sx));
+        hipExtLaunchKernelGGL(quant_mx32_kernel<uint16_t>, dim3((unsigned)((groups + 63) / 64)), dim3(256), 0, st,
+                              nullptr, p.ev_stage_end, 0, p.x, p.T, p.H, p.xq, reinterpret_cast<uint8_t*>(p.sx));
         return hipGetLastError();
     }
     const long n = (long)p.T * p.H;
     if (p.quant == Q_FP8_BLOCK) {
         const long groups = (long)p.T * (p.H / 128);
-        hipLaunchKernelGGL(quant_block128_kernel<uint16_t>, dim3((unsigned)ceil_div((int)groups, 16)),
-                           dim3(256), 0, st, p.x, p.T, p.H, p.xq, p.sx);
+        hipExtLaunchKernelGGL(quant_block128_kernel<uint16_t>, dim3((unsigned)ceil_div((int)groups, 16)),
+                              dim3(256), 0, st, nullptr, p.ev_stage_end, 0, p.x, p.T, p.H, p.xq, p.sx);
         return hipGetLastError();
     }
     const ElemRange all{nullptr, 0, 0};
     if (n <= kSmallQuant) {
-        hipLaunchKernelGGL(quant_tensor_small_kernel<uint16_t>, dim3(1), dim3(1024), 0, st, p.x, n, all,
-                           p.xq, &p.scal[0]);
+        hipExtLaunchKernelGGL(quant_tensor_small_kernel<uint16_t>, dim3(1), dim3(1024), 0, st, nullptr,
+                              p.ev_stage_end, 0, p.x, n, all, p.xq, &p.scal[0]);
         return hipGetLastError();
     }
     const unsigned grid = (unsigned)std::min<long>(2048, (n / 8 + 255) / 256);
     hipLaunchKernelGGL(amax_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, p.x, n, all, &p.amax[0]);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(quant_tensor_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, p.x, n, all,
-                       &p.amax[0], p.xq, &p.scal[0]);
+    hipExtLaunchKernelGGL(quant_tensor_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, nullptr, p.ev_stage_end, 0,
+                          p.x, n, all, &p.amax[0], p.xq, &p.scal[0]);
     return hipGetLastError();
 }
 
@@ -275,24 +275,24 @@ hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st) {
     const float* h = static_cast<const float*>(p.h);
     if (p.quant == Q_FP8_BLOCK) {
         const long groups = (long)p.R * (p.I / 128);
-        hipLaunchKernelGGL(quant_block128_kernel<float>, dim3((unsigned)ceil_div((int)groups, 16)),
-                           dim3(256), 0, st, h, p.R, p.I, p.hq, p.sh);
+        hipExtLaunchKernelGGL(quant_block128_kernel<float>, dim3((unsigned)ceil_div((int)groups, 16)),
+                              dim3(256), 0, st, nullptr, p.ev_stage_end, 0, h, p.R, p.I, p.hq, p.sh);
         return hipGetLastError();
     }
     // per-tensor: the scale covers the expert slice's routes, sorted rows
     // [offsets[e0], offsets[e0 + nloc]) (the only rows of h this call writes)
     const ElemRange local{p.offsets + p.e0, p.nloc, p.I};
     if (n <= kSmallQuant) {
-        hipLaunchKernelGGL(quant_tensor_small_kernel<float>, dim3(1), dim3(1024), 0, st, h, n, local, p.hq,
-                           &p.scal[1]);
+        hipExtLaunchKernelGGL(quant_tensor_small_kernel<float>, dim3(1), dim3(1024), 0, st, nullptr,
+                              p.ev_stage_end, 0, h, n, local, p.hq, &p.scal[1]);
         return hipGetLastError();
     }
     const unsigned grid = (unsigned)std::min<long>(2048, (n / 8 + 255) / 256);
     hipLaunchKernelGGL(amax_kernel<float>, dim3(grid), dim3(256), 0, st, h, n, local, &p.amax[1]);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(quant_tensor_kernel<float>, dim3(grid), dim3(256), 0, st, h, n, local, &p.amax[1],
-                       p.hq, &p.scal[1]);
+    hipExtLaunchKernelGGL(quant_tensor_kernel<float>, dim3(grid), dim3(256), 0, st, nullptr, p.ev_stage_end, 0,
+                          h, n, local, &p.amax[1], p.hq, &p.scal[1]);
     return hipGetLastError();
 }
 
@@ -359,7 +359,7 @@ combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ tw, con
 
 hipError_t launch_combine(const FwdPlan& p, hipStream_t st) {
     dim3 grid(p.T, ceil_div(p.H / 8, 256));
-    hipExtLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, nullptr, p.ev_last_end, 0, p.y, p.tw, p.route_pos,
+    hipExtLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, nullptr, p.ev_stage_end, 0, p.y, p.tw, p.route_pos,
                           p.H, p.k, p.offsets + p.e0, p.nloc, p.acc, p.out);
     return hipGetLastError();
 }

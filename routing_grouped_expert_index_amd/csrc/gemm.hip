@@ -34,6 +34,8 @@
 //    its own LDS area and writes whole 64- or 128-byte row segments in sorted
 //    row order (the combine finds a route's Down row through the inverse
 //    permutation).
+#include <hip/hip_ext.h>
+
 #include "gemm_common.cuh"
 #include "layout.cuh"
 
@@ -751,7 +753,7 @@ int gemm_num_cus() {
 }
 
 template <bool FP8, bool GATHER, int SC, int EPI>
-static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st) {
+static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st, hipEvent_t ev_end) {
     const bool short_k = a.Kb / kSliceBytes < 4;
     size_t lds = g32::LDS_TOTAL;
     if constexpr (SC == SC_BLOCK) {
@@ -784,11 +786,11 @@ static hipError_t run_gemm32(const GemmArgs& a, hipStream_t st) {
     long grid = std::min<long>(total_bound, (long)gemm_num_cus());
     if (grid < 1) grid = 1;
     if (short_k)
-        hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI, true>), dim3((unsigned)grid), dim3(g32::NT), lds,
-                           st, a);
+        hipExtLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI, true>), dim3((unsigned)grid), dim3(g32::NT), lds,
+                              st, nullptr, ev_end, 0, a);
     else
-        hipLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI, false>), dim3((unsigned)grid), dim3(g32::NT), lds,
-                           st, a);
+        hipExtLaunchKernelGGL((gemm32_kernel<FP8, GATHER, SC, EPI, false>), dim3((unsigned)grid), dim3(g32::NT), lds,
+                              st, nullptr, ev_end, 0, a);
     return hipGetLastError();
 }
 
@@ -832,14 +834,14 @@ hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st) {
         a.C = p.h;
         a.ldc = p.I;
         a.c_bytes = (long)p.T * p.k * p.I * 2;
-        return run_gemm32<false, true, SC_NONE, EPI_SWIGLU_BF16>(a, st);
+        return run_gemm32<false, true, SC_NONE, EPI_SWIGLU_BF16>(a, st, p.ev_stage_end);
     }
     if (p.quant == Q_FP8_TENSOR) {
         GemmArgs a = gate_up_args(p, 1);
         a.C = p.h;
         a.ldc = p.I;
         a.c_bytes = (long)p.T * p.k * p.I * 4;
-        return run_gemm32<true, true, SC_TENSOR, EPI_SWIGLU_F32>(a, st);
+        return run_gemm32<true, true, SC_TENSOR, EPI_SWIGLU_F32>(a, st, p.ev_stage_end);
     }
     GemmArgs a = gate_up_args(p, 1);
     a.C = p.hq;
@@ -850,11 +852,11 @@ hipError_t launch_grouped_gate_up(const FwdPlan& p, hipStream_t st) {
         a.swx = reinterpret_cast<const uint32_t*>(p.s_gu);
         a.cs_bytes = (long)p.T * p.k * (p.I / 32);
         a.sa_bytes = (long)p.T * (p.H / 32);
-        return run_gemm32<true, true, SC_MX, EPI_SWIGLU_MX>(a, st);
+        return run_gemm32<true, true, SC_MX, EPI_SWIGLU_MX>(a, st, p.ev_stage_end);
     }
     a.cs_bytes = (long)p.T * p.k * (p.I / 128) * 4;
     a.sa_bytes = (long)p.T * (p.H / 128) * 4;
-    return run_gemm32<true, true, SC_BLOCK, EPI_SWIGLU_Q128>(a, st);
+    return run_gemm32<true, true, SC_BLOCK, EPI_SWIGLU_Q128>(a, st, p.ev_stage_end);
 }
 
 hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
@@ -881,15 +883,15 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     a.c_bytes = (long)p.T * p.k * p.H * 2;
     a.max_tiles = p.max_tiles;
     a.a_bytes = (long)p.T * p.k * a.lda;
-    if (p.quant == Q_BF16) return run_gemm32<false, false, SC_NONE, EPI_Y_BF16>(a, st);
-    if (p.quant == Q_FP8_TENSOR) return run_gemm32<true, false, SC_TENSOR, EPI_Y_BF16>(a, st);
+    if (p.quant == Q_BF16) return run_gemm32<false, false, SC_NONE, EPI_Y_BF16>(a, st, p.ev_stage_end);
+    if (p.quant == Q_FP8_TENSOR) return run_gemm32<true, false, SC_TENSOR, EPI_Y_BF16>(a, st, p.ev_stage_end);
     if (p.quant == Q_FP8_MX) {
         a.swx = reinterpret_cast<const uint32_t*>(p.s_d);
         a.sa_bytes = (long)p.T * p.k * (p.I / 32);
-        return run_gemm32<true, false, SC_MX, EPI_Y_BF16>(a, st);
+        return run_gemm32<true, false, SC_MX, EPI_Y_BF16>(a, st, p.ev_stage_end);
     }
     a.sa_bytes = (long)p.T * p.k * (p.I / 128) * 4;
-    return run_gemm32<true, false, SC_BLOCK, EPI_Y_BF16>(a, st);
+    return run_gemm32<true, false, SC_BLOCK, EPI_Y_BF16>(a, st, p.ev_stage_end);
 }
 
 }  // namespace moe

@@ -91,10 +91,12 @@ struct FwdPlan {
     const float* logits;
     int32_t* ids_w;
     float* tw_w;
-    // timing: events attached to the first kernel's dispatch (its start) and
-    // the last kernel's dispatch (its end), or null
+    // timing, through events attached to kernel dispatches (hipExtLaunchKernel:
+    // no marker packet between kernels): ev_first_start to the forward's first
+    // kernel (recorded when it starts), ev_stage_end to the current stage's
+    // last kernel (recorded when it ends); null when not timed
     hipEvent_t ev_first_start;
-    hipEvent_t ev_last_end;
+    hipEvent_t ev_stage_end;
 };
 
 constexpr int kGemmBM = 128;

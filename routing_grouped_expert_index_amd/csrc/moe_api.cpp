@@ -421,8 +421,12 @@ static int forward_impl(const void* x, const moe_routes* routes, const moe_packe
     P.logits = logits;
     P.ids_w = logits ? routes->topk_ids : nullptr;
     P.tw_w = logits ? routes->topk_weights : nullptr;
-    P.ev_first_start = static_cast<hipEvent_t>(ev_start);
-    P.ev_last_end = static_cast<hipEvent_t>(ev_end);
+    // Timing events are attached to kernel dispatches (hipExtLaunchKernel), so
+    // no marker packet sits between two kernels: profiled calls put events[0]
+    // on the first kernel's start and events[i] on the end of stage i's last
+    // kernel; timed calls put ev_start on the first kernel's start and ev_end
+    // on the last kernel's end.
+    P.ev_first_start = static_cast<hipEvent_t>(events && n_events > 0 ? events[0] : ev_start);
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool grouped = p == MOE_PATH_GROUPED;
@@ -430,34 +434,37 @@ static int forward_impl(const void* x, const moe_routes* routes, const moe_packe
     static thread_local char names[256];
     names[0] = '\0';
     auto mark = [&](const char* name) {
-        if (events && stage < n_events && events[stage])
-            (void)hipEventRecord(static_cast<hipEvent_t>(events[stage]), st);
         if (name) {
             if (names[0]) strncat(names, ",", sizeof names - strlen(names) - 1);
             strncat(names, name, sizeof names - strlen(names) - 1);
         }
         ++stage;
     };
+    auto stage_end = [&](bool last) -> hipEvent_t {
+        if (events) return stage < n_events ? static_cast<hipEvent_t>(events[stage]) : nullptr;
+        return last ? static_cast<hipEvent_t>(ev_end) : nullptr;
+    };
     mark(nullptr);
-#define MOE_STEP(call, what)                                            \
+#define MOE_STEP(call, what, last)                                      \
     do {                                                                \
+        P.ev_stage_end = stage_end(last);                               \
         if ((rc = hip_status((call), what)) != MOE_OK) return rc;       \
         mark(what);                                                     \
     } while (0)
     if (grouped) {
-        MOE_STEP(moe::launch_forward_init(P, true, st), "init");
-        if (quant != MOE_BF16) MOE_STEP(moe::launch_quant_x(P, st), "quant_x");
-        MOE_STEP(moe::launch_grouped_gate_up(P, st), "gate_up");
-        if (quant == MOE_FP8_PER_TENSOR) MOE_STEP(moe::launch_quant_h(P, st), "quant_h");
-        MOE_STEP(moe::launch_grouped_down(P, st), "down");
-        MOE_STEP(moe::launch_combine(P, st), "combine");
+        MOE_STEP(moe::launch_forward_init(P, true, st), "init", false);
+        if (quant != MOE_BF16) MOE_STEP(moe::launch_quant_x(P, st), "quant_x", false);
+        MOE_STEP(moe::launch_grouped_gate_up(P, st), "gate_up", false);
+        if (quant == MOE_FP8_PER_TENSOR) MOE_STEP(moe::launch_quant_h(P, st), "quant_h", false);
+        MOE_STEP(moe::launch_grouped_down(P, st), "down", false);
+        MOE_STEP(moe::launch_combine(P, st), "combine", true);
     } else {
         // FP8 quantises x and h inside the route-direct kernels (per tensor: from
         // all of x and the Gate/Up workgroups' h maxima; blockwise and MX: per
         // token or route row and 128 or 32 channels, in the workgroup that uses
         // them)
-        MOE_STEP(moe::launch_route_direct_gate_up(P, st), "rd_gate_up");
-        MOE_STEP(moe::launch_route_direct_down(P, st), "rd_down_combine");
+        MOE_STEP(moe::launch_route_direct_gate_up(P, st), "rd_gate_up", false);
+        MOE_STEP(moe::launch_route_direct_down(P, st), "rd_down_combine", true);
     }
 #undef MOE_STEP
     if (n_stages) *n_stages = stage - 1;

@@ -1185,7 +1185,7 @@ hipError_t launch_route_direct_gate_up(const FwdPlan& p, hipStream_t st) {
     if (!fn) return hipErrorInvalidValue;
     void* args[] = {&a};
     return hipExtLaunchKernel(fn, dim3(p.T * p.k, p.I / 32, c.rs), dim3(64 * c.nw), args, 0, st, p.ev_first_start,
-                              nullptr, 0);
+                              p.ev_stage_end, 0);
 }
 
 // Down split: K parts per route (1, 2 or 4, dividing NSL) only while the grid
@@ -1290,15 +1290,15 @@ hipError_t launch_route_direct_down(const FwdPlan& p, hipStream_t st) {
         a.kp = bc.kp;
         const dim3 grid((unsigned)((long)p.T * (p.H / 32))), block(64 * bc.nw);
         if (p.quant == Q_BF16)
-            hipExtLaunchKernelGGL((rd_down_block_kernel<RD_BF16>), grid, block, 0, st, nullptr, p.ev_last_end, 0, a);
+            hipExtLaunchKernelGGL((rd_down_block_kernel<RD_BF16>), grid, block, 0, st, nullptr, p.ev_stage_end, 0, a);
         else
-            hipExtLaunchKernelGGL((rd_down_block_kernel<RD_TENSOR>), grid, block, 0, st, nullptr, p.ev_last_end, 0, a);
+            hipExtLaunchKernelGGL((rd_down_block_kernel<RD_TENSOR>), grid, block, 0, st, nullptr, p.ev_stage_end, 0, a);
         return hipGetLastError();
     }
-    if (p.quant == Q_BF16) return rd_dn<RD_BF16>(a, p.quant, st, p.ev_last_end);
-    if (p.quant == Q_FP8_TENSOR) return rd_dn<RD_TENSOR>(a, p.quant, st, p.ev_last_end);
-    if (p.quant == Q_FP8_MX) return rd_dn<RD_MX>(a, p.quant, st, p.ev_last_end);
-    return rd_dn<RD_BLOCK>(a, p.quant, st, p.ev_last_end);
+    if (p.quant == Q_BF16) return rd_dn<RD_BF16>(a, p.quant, st, p.ev_stage_end);
+    if (p.quant == Q_FP8_TENSOR) return rd_dn<RD_TENSOR>(a, p.quant, st, p.ev_stage_end);
+    if (p.quant == Q_FP8_MX) return rd_dn<RD_MX>(a, p.quant, st, p.ev_stage_end);
+    return rd_dn<RD_BLOCK>(a, p.quant, st, p.ev_stage_end);
 }
 
 }  // namespace moe

@@ -299,3 +299,27 @@ def test_forward_timed_same_bits(name, B, path):
     span = d0.elapsed_time(d1)
     say(f"  {name} B={B} {path}: device span {span * 1e3:.2f} us")
     assert 0.0 < span < 10.0
+
+
+@pytest.mark.parametrize("name,B,path", [("decode_fp8_tensor", 2, "route_direct"), ("decode_bf16", 3, "grouped"),
+                                         ("prefill_fp8_block", None, "grouped")])
+def test_forward_profiled_stage_events(name, B, path):
+    """moe_forward_profiled attaches its events to the kernel dispatches: the same output bits as
+    moe_forward, every stage a positive device time, and the stages adding up to the span from
+    the first kernel's start to the last kernel's end (events[-1] - events[0])."""
+    wl = WORKLOADS[name]
+    a = workload_inputs(name, batch=B)
+    pw, sc = workload_dev(name)
+    x = bf16_dev(a["x"])
+    r = moe.route(torch.from_numpy(a["logits"]).to(DEV), wl.k)
+    ref = moe.forward(x, r, pw, scales=sc, path=path)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    out, names = moe.forward(x, r, pw, scales=sc, path=path, events=evs)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    n = len(names)
+    stages = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+    total = evs[0].elapsed_time(evs[n])
+    say(f"  {name} {path}: {dict(zip(names, [round(s * 1e3, 2) for s in stages]))} us, span {total * 1e3:.2f} us")
+    assert all(s > 0.0 for s in stages)
+    assert abs(sum(stages) - total) <= 1e-3 * total + 1e-6
