@@ -241,7 +241,7 @@ int moe_forward_launch_info(int T, int H, int I, int E, int k, int quant, int pa
  * same way before Down (per-tensor: one scale for all T*k rows).
  * The combine sums the k routes of a token in a fixed order in fp32 and
  * rounds to bf16 once: repeated calls give identical bits.
- * Shapes: H % 128 == 0, I % 64 == 0 (block128: I % 128 == 0); T*H < 2^31
+ * Shapes: H % 64 == 0, I % 64 == 0 (block128: both % 128; MX: both % 256); T*H < 2^31
  * and T*k*I < 2^36 (the grouped path addresses x with 32-bit offsets and
  * every sorted-row buffer -- h, y -- from a 64-bit base per row tile, so
  * intermediates of many GiB are fine); the route-direct path also needs

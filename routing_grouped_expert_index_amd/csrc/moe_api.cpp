@@ -62,7 +62,9 @@ int check_shape(int T, int H, int I, int E, int k, int quant) {
     // from a 64-bit base per row tile, so their size is not limited here.
     if ((long)T * k * I >= (1L << 36))
         return fail(MOE_ERR_UNSUPPORTED, "T*k*I = %ld must be below 2^36", (long)T * k * I);
-    if (H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "H=%d: H must be a multiple of 128", H);
+    if (H % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "H=%d: H must be a multiple of 64", H);
+    if (quant == MOE_FP8_BLOCK128 && H % 128 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "H=%d: block128 needs H a multiple of 128", H);
     if (I % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "I=%d: I must be a multiple of 64", I);
     if (quant == MOE_FP8_BLOCK128 && I % 128 != 0)
         return fail(MOE_ERR_UNSUPPORTED, "I=%d: block128 needs I a multiple of 128", I);

@@ -48,12 +48,16 @@ def test_select_path_rules():
     with pytest.raises(moe.MoeError):
         moe.select_path(64, 2048, 192, 128, 8, "fp8_mx32")
     assert moe.select_path(64, 2048, 768, 128, 8, "bf16", "route_direct") == "route_direct"
+    # H a multiple of 64 (not of 128) for bf16 and per-tensor FP8
+    assert moe.select_path(1, 2112, 768, 128, 8) == "route_direct"
+    assert moe.select_path(512, 2112, 768, 128, 8, "fp8_per_tensor") == "grouped"
 
 
 @pytest.mark.parametrize("args,code", [
     ((1, 2048, 768, 4, 8, "bf16", "auto"), -1),      # k > E
     ((1, 2048, 768, 600, 8, "bf16", "auto"), -1),    # E > 512
-    ((1, 2000, 768, 128, 8, "bf16", "auto"), -2),    # H % 128
+    ((1, 2000, 768, 128, 8, "bf16", "auto"), -2),    # H % 64
+    ((1, 2112, 768, 128, 8, "fp8_block128", "auto"), -2),   # block128 needs H % 128
     ((1, 2048, 96, 128, 8, "bf16", "auto"), -2),     # I % 64
     ((1, 2048, 192, 128, 8, "fp8_block128", "auto"), -2),   # block128 needs I % 128
     ((1, 16384, 768, 128, 8, "bf16", "route_direct"), -2),  # route-direct shape limit

@@ -163,6 +163,11 @@ EDGE = [
     (5, 256, 192, 1, 1, "bf16", "normal", "small grid, 3 n-tiles"),
     (3, 256, 384, 1, 1, "fp8_block128", "normal", "small grid block128"),
     (2, 384, 192, 1, 1, "fp8_per_tensor", "normal", "small grid per-tensor"),
+    # H a multiple of 64 but not of 128 (the Down GEMM's last 512-column tile mostly past H)
+    (13, 192, 128, 8, 2, "bf16", "normal", "H=192"),
+    (150, 192, 256, 8, 2, "bf16", "normal", "H=192 multi-tile"),
+    (7, 320, 192, 6, 3, "fp8_per_tensor", "normal", "H=320 per-tensor"),
+    (90, 576, 128, 10, 4, "fp8_per_tensor", "normal", "H=576 per-tensor multi-tile"),
 ]
 
 
