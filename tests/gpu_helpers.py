@@ -99,41 +99,3 @@ __all__ = ["DEV", "say", "bf16_dev", "weights_dev", "workload_dev", "run", "rout
            "workload_weights", "WORKLOADS", "oracle", "moe"]
 
 
-def tile_cover_tokens(ref_routes: dict, k: int, bm: int = 128, blk: int = 32) -> np.ndarray:
-    """Tokens whose outputs, compared in full, check at least one row of every
-    32-row MFMA block of every 128-row tile of the grouped GEMMs' tile map (each
-    expert's tiles start at its offset), plus the first and last sorted row of
-    every expert.  A token covers the blocks its k routes' sorted positions fall
-    in.  Greedy: experts' first and last rows first, then the last row of every
-    block not yet covered."""
-    off = ref_routes["expert_offsets"].astype(np.int64)
-    perm = ref_routes["perm"].astype(np.int64)
-    route_pos = ref_routes["route_pos"].astype(np.int64)
-    starts = []
-    for e in range(len(off) - 1):
-        for r0 in range(off[e], off[e + 1], bm):
-            starts.extend(range(r0, min(r0 + bm, off[e + 1]), blk))
-    starts = np.array(starts, np.int64)
-    if starts.size == 0:
-        return np.zeros(0, np.int32)
-    ends = np.append(starts[1:], off[-1])
-    covered = np.zeros(starts.size, bool)
-    chosen = []
-
-    def take(pos):
-        t = int(perm[pos] // k)
-        chosen.append(t)
-        covered[np.searchsorted(starts, route_pos[t * k:(t + 1) * k], side="right") - 1] = True
-
-    for e in range(len(off) - 1):
-        if off[e + 1] > off[e]:
-            take(off[e])
-            take(off[e + 1] - 1)
-    for b in range(starts.size):
-        if not covered[b]:
-            take(ends[b] - 1)
-    assert covered.all()
-    return np.unique(np.array(chosen, np.int32))
-
-
-__all__.append("tile_cover_tokens")
