@@ -212,7 +212,7 @@ def test_two_runs_bitwise_equal(name, path):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["decode_bf16", "decode_fp8_tensor", "tiny_bf16"])
+@pytest.mark.parametrize("name", ["decode_bf16", "decode_fp8_tensor", "decode_fp8_mx", "tiny_bf16"])
 def test_graph_replay_bitwise_equal(name):
     wl = WORKLOADS[name]
     a = workload_inputs(name, batch=4 if wl.batches else None)

@@ -28,7 +28,8 @@ def _pair(lg_np, x_bits, k, pw, sc, E, H):
     return out
 
 
-@pytest.mark.parametrize("name,batches", [("decode_bf16", (4, 2)), ("decode_fp8_tensor", (8, 3))])
+@pytest.mark.parametrize("name,batches", [("decode_bf16", (4, 2)), ("decode_fp8_tensor", (8, 3)),
+                                          ("decode_fp8_mx", (3, 1))])
 def test_noalloc_matches_decode_forward(name, batches):
     wl = WORKLOADS[name]
     pw, sc = workload_dev(name)
