@@ -141,11 +141,11 @@ def bench_prefill(torch, moe, name, steps, warmup, stage_steps=10):
 # (x1.0).  Valid only for the GEMM source the counters were taken on; any edit
 # to it turns the figure into null.
 FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524300.5, 1.0
-_GEMM_SHA = "89782dec031ea208e1a3cf19809c0ec6861455a490c473f5b2f861ec4586baed"
+_GEMM_SHA = "22f00a45b5e998a7001fdb26709be0f7b155d4390017758f0cfd6c1caae60755"
 COUNTER_TRAFFIC = {
-    "prefill_bf16": dict(gemm_sha256=_GEMM_SHA, fetch_kib=795007.8, write_kib=98312.4),
-    "prefill_fp8_block": dict(gemm_sha256=_GEMM_SHA, fetch_kib=381936.7, write_kib=17424.7),
-    "prefill_fp8_mx": dict(gemm_sha256=_GEMM_SHA, fetch_kib=419999.2, write_kib=17500.1),
+    "prefill_bf16": dict(gemm_sha256=_GEMM_SHA, fetch_kib=802743.1, write_kib=98325.1),
+    "prefill_fp8_block": dict(gemm_sha256=_GEMM_SHA, fetch_kib=382233.2, write_kib=17437.0),
+    "prefill_fp8_mx": dict(gemm_sha256=_GEMM_SHA, fetch_kib=421366.2, write_kib=17504.0),
 }
 
 

@@ -36,6 +36,8 @@
 //    permutation).
 #include <hip/hip_ext.h>
 
+#include <atomic>
+
 #include "gemm_common.cuh"
 #include "layout.cuh"
 
@@ -738,18 +740,19 @@ gemm32_kernel(const GemmArgs g) {
 
 // ----------------------------------------------------------------------------
 
-static int g_num_cus = 0;
-
+// compute units of the current device, asked once per device (the persistent
+// grid's size; 256 if the runtime cannot tell)
 int gemm_num_cus() {
-    if (g_num_cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            g_num_cus = n;
-        else
-            g_num_cus = 256;
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cus[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return g_num_cus;
+    return n;
 }
 
 template <bool FP8, bool GATHER, int SC, int EPI>
