@@ -25,6 +25,14 @@ Functions and what they follow (page titles and sections):
   quantise_activations, e4m3_encode/decode, bf16_decode -- the FP8 per-tensor
                 and 128-channel blockwise activation quantisation and the
                 codecs ("perf: add small-batch route MMA for MoE", Summary).
+  backward_mx -- the layer's gradients (input, gates, both expert weights)
+                for an upstream gradient under the MX training recipe: every
+                backward product on MX operands quantised along its own
+                reduction dimension, the weight gradients' operands along each
+                expert's routes ("[mxfp8 moe training] add per group blocked
+                scale kernels", Summary and stacked pull requests: the dim1
+                cast in the backward, per-group padded scale rows); exact=True
+                is the same calculus with no quantiser.
   mx_scale_byte, quantise_group_mx, quant "fp8_mx32" -- MX FP8: e4m3 codes
                 with one power-of-two (E8M0) scale per 32 values along K
                 ("[mxfp8 moe training] add per group blocked scale kernels",
@@ -81,6 +89,9 @@ def _load():
     lib.oracle_quantise_activations.argtypes = [P, i32, i32, i32, P, P]
     lib.oracle_gate_up_h.restype = i32
     lib.oracle_gate_up_h.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, i32, P, ctypes.c_long, P]
+    lib.oracle_backward_mx.restype = i32
+    lib.oracle_backward_mx.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P, i32, P, i32, P, i32,
+                                       P, P, P, P]
     _lib = lib
     return lib
 
@@ -248,3 +259,39 @@ def quantise_group_mx(values):
     q = np.empty(v.size, dtype=np.uint8)
     b = _load().oracle_quantise_group_mx(_ptr(v), v.size, _ptr(q))
     return q, int(b)
+
+
+def backward_mx(x_bf16, topk_ids, topk_weights, w_gate_up, w_down, dout_bf16, exact=False,
+                tokens=None, experts=None):
+    """Gradients of the layer for the upstream gradient dout (bf16 bits [T,H]).
+
+    w_gate_up [E,H,2I] and w_down [E,I,H] are bf16 master weights (uint16
+    bits); the MX forward and backward quantise them as each product needs.
+    Returns dict(dx [n_tok,H], dgate [n_tok,k], dw_gate_up [n_exp,H,2I],
+    dw_down [n_exp,I,H]) in float64 for the listed tokens and experts (all
+    when None)."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    E, H2, I2 = w_gate_up.shape
+    assert H2 == H and I2 % 2 == 0
+    I = I2 // 2
+    k = topk_ids.shape[1]
+    wgu = _c(w_gate_up, np.uint16)
+    wd = _c(w_down, np.uint16)
+    assert wd.shape == (E, I, H)
+    do = _c(dout_bf16, np.uint16)
+    assert do.shape == (T, H)
+    ids = _c(topk_ids, np.int32)
+    tw = _c(topk_weights, np.float32)
+    tok = _c(np.arange(T) if tokens is None else tokens, np.int32)
+    exps = _c(np.arange(E) if experts is None else experts, np.int32)
+    dx = np.zeros((tok.size, H), np.float64)
+    dg = np.zeros((tok.size, k), np.float64)
+    dwg = np.zeros((exps.size, H, I2), np.float64)
+    dwd = np.zeros((exps.size, I, H), np.float64)
+    rc = _load().oracle_backward_mx(_ptr(x), T, H, I, E, k, _ptr(ids), _ptr(tw), _ptr(wgu), _ptr(wd),
+                                    _ptr(do), int(bool(exact)), _ptr(tok), tok.size, _ptr(exps),
+                                    exps.size, _ptr(dx), _ptr(dg), _ptr(dwg), _ptr(dwd))
+    if rc != 0:
+        raise ValueError("oracle_backward_mx rejected the inputs")
+    return {"dx": dx, "dgate": dg, "dw_gate_up": dwg, "dw_down": dwd}

@@ -591,3 +591,317 @@ int oracle_gate_up_h(const uint16_t *x, int T, int H, int I, int E, int k, const
     free(q_x); free(scales);
     return bad ? -1 : 0;
 }
+
+/* ------------------------------------------------------------- backward -- */
+
+/*
+ * Gradients of the layer for an upstream gradient dout [T, H] (bf16), under
+ * the MX training recipe of [P2] ("[mxfp8 moe training] add per group blocked
+ * scale kernels": Summary and its stacked pull requests -- the "dim1" cast in
+ * the backward, per-expert 3-D weight scales, per-group padded scale rows).
+ * The gradients themselves are the chain rule through the forward above;
+ * the readings taken where the pages are silent:
+ *  - the forward is the MX forward with the weights quantised from bf16
+ *    master weights along K (W_gate_up along H per output column, W_down
+ *    along I), x per token along H and h per route along I;
+ *  - every backward product takes MX operands quantised along its own
+ *    reduction dimension, 32 values per scale: the input-gradient products
+ *    along the forward's output dimension (dy and W_down along H, dGU =
+ *    [dgate | dup] and W_gate_up along 2I), the weight-gradient products along
+ *    the routes of one expert in ascending route order (the stable sort's
+ *    order), 32 routes per group, an expert's last group padded with zeros;
+ *  - the quantisers pass gradients through unchanged (straight-through);
+ *  - the quantisers see fp32 values: dy = fp32(gate) * fp32(dout) rounded to
+ *    fp32, h = fp32(silu(g) u), dGU rounded to fp32, x as its bf16 value;
+ *  - silu'(g) = sigma(g) (1 + g (1 - sigma(g)));
+ *  - dgate_r = sum over n of dout[t][n] y_r[n], y_r the route's Down output
+ *    before the gate weighting; dx[t] = the sum of the token's route input
+ *    gradients over j ascending.
+ * exact = 1 switches every quantiser off (the bf16 inputs in double
+ * throughout): the plain calculus, which the tests compare with autograd.
+ *
+ * x, dout: bf16 [T, H]; ids, weights: [T, k]; w_gu bf16 [E, H, 2I]; w_d bf16
+ * [E, I, H].  tok (n_tok distinct tokens) selects the rows of dx [n_tok, H]
+ * and dgate [n_tok, k]; exps (n_exp experts) the slabs of dw_gu [n_exp, H, 2I]
+ * and dw_d [n_exp, I, H].  Returns 0, or -1 on a bad argument or allocation
+ * failure.
+ */
+static void mx_group_deq(const float *v, double *out) {
+    uint8_t q[32];
+    uint8_t b = oracle_quantise_group_mx(v, 32, q);
+    double s = oracle_e8m0_decode(b);
+    int j;
+    for (j = 0; j < 32; ++j) out[j] = oracle_e4m3_decode(q[j]) * s;
+}
+
+/* n values of a row (n a multiple of 32), each group of 32 MX-quantised and
+ * returned dequantised; v holds fp32 values */
+static void mx_row_deq(const float *v, long n, double *out) {
+    long c;
+    for (c = 0; c < n; c += 32) mx_group_deq(v + c, out + c);
+}
+
+static double silu_d(double z) { return z / (1.0 + exp(-z)); }
+
+int oracle_backward_mx(const uint16_t *x, int T, int H, int I, int E, int k,
+                       const int32_t *ids, const float *weights,
+                       const uint16_t *w_gu, const uint16_t *w_d, const uint16_t *dout, int exact,
+                       const int32_t *tok, int n_tok, const int32_t *exps, int n_exp,
+                       double *dx, double *dgate, double *dw_gu, double *dw_d) {
+    long R = (long)T * k, r;
+    int I2 = 2 * I, bad = 0, e, i;
+    double *xa = NULL, *da = NULL;
+    long *slot = NULL;
+    int *exp_slot = NULL;
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || n_tok < 0 || n_exp < 0) return -1;
+    if (!exact && (H % 32 || I % 32)) return -1;
+    slot = (long *)malloc(sizeof(long) * (size_t)(R > 0 ? R : 1));
+    exp_slot = (int *)malloc(sizeof(int) * (size_t)E);
+    xa = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * H);
+    da = (double *)malloc(sizeof(double) * (size_t)(n_tok > 0 ? n_tok : 1) * k * H);
+    if (!slot || !exp_slot || !xa || !da) { bad = 1; goto done; }
+    for (r = 0; r < R; ++r) {
+        slot[r] = -1;
+        if (ids[r] < 0 || ids[r] >= E) { bad = 1; goto done; }
+    }
+    for (i = 0; i < n_tok; ++i) {
+        int j;
+        if (tok[i] < 0 || tok[i] >= T) { bad = 1; goto done; }
+        for (j = 0; j < k; ++j) slot[(long)tok[i] * k + j] = (long)i * k + j;
+    }
+    for (e = 0; e < E; ++e) exp_slot[e] = -1;
+    for (i = 0; i < n_exp; ++i) {
+        if (exps[i] < 0 || exps[i] >= E) { bad = 1; goto done; }
+        exp_slot[exps[i]] = i;
+    }
+    /* the Gate/Up input: x quantised per token along H (MX), or x itself */
+    {
+        int t, c;
+        for (t = 0; t < T; ++t) {
+            float v[32];
+            for (c = 0; c < H; c += 32) {
+                int j;
+                for (j = 0; j < 32 && c + j < H; ++j) v[j] = oracle_bf16_decode(x[(long)t * H + c + j]);
+                if (exact) for (j = 0; j < 32 && c + j < H; ++j) xa[(long)t * H + c + j] = v[j];
+                else mx_group_deq(v, xa + (long)t * H + c);
+            }
+        }
+    }
+
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (e = 0; e < E; ++e) {
+        long n_e = 0, p, need = 0, r;
+        int es = exp_slot[e], h, c, n, ii, g;
+        double *WgK = NULL, *Wg2 = NULL, *WdK = NULL, *WdH = NULL;
+        double *gu = NULL, *hq = NULL, *y = NULL, *dyq = NULL, *dh = NULL, *dgu = NULL;
+        float *fv = NULL;
+        double *xs = NULL, *hs = NULL, *dys = NULL, *dgs = NULL;   /* per route of e, for the weight gradients */
+        long *rl = NULL;
+        for (r = 0; r < R; ++r)
+            if (ids[r] == e) {
+                ++n_e;
+                if (slot[r] >= 0) need = 1;
+            }
+        if (!need && es < 0) continue;
+        WgK = (double *)malloc(sizeof(double) * (size_t)H * I2);
+        Wg2 = (double *)malloc(sizeof(double) * (size_t)H * I2);
+        WdK = (double *)malloc(sizeof(double) * (size_t)I * H);
+        WdH = (double *)malloc(sizeof(double) * (size_t)I * H);
+        gu = (double *)malloc(sizeof(double) * (size_t)I2);
+        hq = (double *)malloc(sizeof(double) * (size_t)I);
+        y = (double *)malloc(sizeof(double) * (size_t)H);
+        dyq = (double *)malloc(sizeof(double) * (size_t)H);
+        dh = (double *)malloc(sizeof(double) * (size_t)I);
+        dgu = (double *)malloc(sizeof(double) * (size_t)I2);
+        fv = (float *)malloc(sizeof(float) * (size_t)(H > I2 ? H : I2));
+        rl = (long *)malloc(sizeof(long) * (size_t)(n_e > 0 ? n_e : 1));
+        if (es >= 0) {
+            xs = (double *)malloc(sizeof(double) * (size_t)(n_e > 0 ? n_e : 1) * H);
+            hs = (double *)malloc(sizeof(double) * (size_t)(n_e > 0 ? n_e : 1) * I);
+            dys = (double *)malloc(sizeof(double) * (size_t)(n_e > 0 ? n_e : 1) * H);
+            dgs = (double *)malloc(sizeof(double) * (size_t)(n_e > 0 ? n_e : 1) * I2);
+        }
+        if (!WgK || !Wg2 || !WdK || !WdH || !gu || !hq || !y || !dyq || !dh || !dgu || !fv || !rl ||
+            (es >= 0 && (!xs || !hs || !dys || !dgs))) {
+            bad |= 1;
+            goto next_e;
+        }
+        /* the expert's weights as each product sees them */
+        {
+            const uint16_t *wg = w_gu + (long)e * H * I2, *wd = w_d + (long)e * I * H;
+            float v[32];
+            double o[32];
+            int j;
+            for (h = 0; h < H; ++h)
+                for (c = 0; c < I2; ++c) WgK[(long)h * I2 + c] = Wg2[(long)h * I2 + c] = oracle_bf16_decode(wg[(long)h * I2 + c]);
+            for (ii = 0; ii < I; ++ii)
+                for (n = 0; n < H; ++n) WdK[(long)ii * H + n] = WdH[(long)ii * H + n] = oracle_bf16_decode(wd[(long)ii * H + n]);
+            if (!exact) {
+                for (c = 0; c < I2; ++c)          /* forward: W_gate_up along H */
+                    for (h = 0; h < H; h += 32) {
+                        for (j = 0; j < 32; ++j) v[j] = oracle_bf16_decode(wg[(long)(h + j) * I2 + c]);
+                        mx_group_deq(v, o);
+                        for (j = 0; j < 32; ++j) WgK[(long)(h + j) * I2 + c] = o[j];
+                    }
+                for (h = 0; h < H; ++h)           /* input gradient: W_gate_up along 2I */
+                    for (c = 0; c < I2; c += 32) {
+                        for (j = 0; j < 32; ++j) v[j] = oracle_bf16_decode(wg[(long)h * I2 + c + j]);
+                        mx_group_deq(v, Wg2 + (long)h * I2 + c);
+                    }
+                for (n = 0; n < H; ++n)           /* forward: W_down along I */
+                    for (ii = 0; ii < I; ii += 32) {
+                        for (j = 0; j < 32; ++j) v[j] = oracle_bf16_decode(wd[(long)(ii + j) * H + n]);
+                        mx_group_deq(v, o);
+                        for (j = 0; j < 32; ++j) WdK[(long)(ii + j) * H + n] = o[j];
+                    }
+                for (ii = 0; ii < I; ++ii)        /* input gradient: W_down along H */
+                    for (n = 0; n < H; n += 32) {
+                        for (j = 0; j < 32; ++j) v[j] = oracle_bf16_decode(wd[(long)ii * H + n + j]);
+                        mx_group_deq(v, WdH + (long)ii * H + n);
+                    }
+            }
+        }
+        /* every route of e in ascending route order */
+        p = 0;
+        for (r = 0; r < R; ++r) {
+            int t, j;
+            const double *a;
+            double dgr, wr;
+            if (ids[r] != e) continue;
+            rl[p] = r;
+            if (slot[r] < 0 && es < 0) { ++p; continue; }
+            t = (int)(r / k);
+            j = (int)(r % k);
+            (void)j;
+            a = xa + (long)t * H;
+            wr = (double)weights[r];
+            /* forward: [g | u] = a W_gate_up, h = silu(g) u, y = h W_down */
+            for (c = 0; c < I2; ++c) gu[c] = 0.0;
+            for (h = 0; h < H; ++h) {
+                double ah = a[h];
+                const double *wrow = WgK + (long)h * I2;
+                for (c = 0; c < I2; ++c) gu[c] += ah * wrow[c];
+            }
+            for (ii = 0; ii < I; ++ii) fv[ii] = (float)(silu_d(gu[ii]) * gu[I + ii]);
+            if (es >= 0)
+                for (ii = 0; ii < I; ++ii) hs[p * I + ii] = exact ? silu_d(gu[ii]) * gu[I + ii] : fv[ii];
+            if (exact) for (ii = 0; ii < I; ++ii) hq[ii] = silu_d(gu[ii]) * gu[I + ii];
+            else mx_row_deq(fv, I, hq);
+            for (n = 0; n < H; ++n) y[n] = 0.0;
+            for (ii = 0; ii < I; ++ii) {
+                double hv = hq[ii];
+                const double *wrow = WdK + (long)ii * H;
+                for (n = 0; n < H; ++n) y[n] += hv * wrow[n];
+            }
+            /* the gate's gradient */
+            dgr = 0.0;
+            for (n = 0; n < H; ++n) dgr += (double)oracle_bf16_decode(dout[(long)t * H + n]) * y[n];
+            /* dy = gate * dout; dh = dy W_down^T */
+            {
+                float *dyf = fv;
+                for (n = 0; n < H; ++n) dyf[n] = weights[r] * oracle_bf16_decode(dout[(long)t * H + n]);
+                if (es >= 0)
+                    for (n = 0; n < H; ++n) dys[p * H + n] = exact ? wr * oracle_bf16_decode(dout[(long)t * H + n]) : dyf[n];
+                if (exact) for (n = 0; n < H; ++n) dyq[n] = wr * oracle_bf16_decode(dout[(long)t * H + n]);
+                else mx_row_deq(dyf, H, dyq);
+            }
+            for (ii = 0; ii < I; ++ii) {
+                double s = 0.0;
+                const double *wrow = WdH + (long)ii * H;
+                for (n = 0; n < H; ++n) s += dyq[n] * wrow[n];
+                dh[ii] = s;
+            }
+            /* SwiGLU backward, then dGU = [dgate | dup] */
+            for (ii = 0; ii < I; ++ii) {
+                double gv = gu[ii], uv = gu[I + ii];
+                double sg = 1.0 / (1.0 + exp(-gv));
+                dgu[ii] = dh[ii] * uv * sg * (1.0 + gv * (1.0 - sg));
+                dgu[I + ii] = dh[ii] * gv * sg;
+            }
+            if (es >= 0) {
+                for (h = 0; h < H; ++h) xs[p * H + h] = oracle_bf16_decode(x[(long)t * H + h]);
+                for (c = 0; c < I2; ++c) dgs[p * I2 + c] = exact ? dgu[c] : (double)(float)dgu[c];
+            }
+            /* da = dGU W_gate_up^T, for the listed tokens */
+            if (slot[r] >= 0) {
+                double *dar = da + slot[r] * H;
+                if (!exact) {
+                    for (c = 0; c < I2; ++c) fv[c] = (float)dgu[c];
+                    mx_row_deq(fv, I2, dgu);
+                }
+                for (h = 0; h < H; ++h) {
+                    double s = 0.0;
+                    const double *wrow = Wg2 + (long)h * I2;
+                    for (c = 0; c < I2; ++c) s += dgu[c] * wrow[c];
+                    dar[h] = s;
+                }
+                dgate[slot[r]] = dgr;
+            }
+            ++p;
+        }
+        /* weight gradients of e: products over its routes, the operands
+         * quantised along the routes (the "dim1" cast) */
+        if (es >= 0) {
+            double *ow = dw_gu + (long)es * H * I2, *od = dw_d + (long)es * I * H;
+            long ng = (n_e + 31) / 32, np = ng * 32;
+            double *cq = (double *)malloc(sizeof(double) * (size_t)(np > 0 ? np : 1) * (H > I2 ? H : I2));
+            double *cq2 = (double *)malloc(sizeof(double) * (size_t)(np > 0 ? np : 1) * (H > I2 ? H : I2));
+            if (!cq || !cq2) {
+                bad |= 1;
+            } else {
+                /* column-quantise src [n_e][m] into dst [np][m] (zero rows past n_e) */
+#define ORC_DIM1(src, m, dst)                                                        \
+                for (c = 0; c < (m); ++c)                                            \
+                    for (g = 0; g < ng; ++g) {                                       \
+                        float v[32];                                                 \
+                        double o[32];                                                \
+                        int j;                                                       \
+                        for (j = 0; j < 32; ++j) {                                   \
+                            long pp = (long)g * 32 + j;                              \
+                            v[j] = pp < n_e ? (float)(src)[pp * (m) + c] : 0.0f;     \
+                        }                                                            \
+                        if (exact) for (j = 0; j < 32; ++j) {                        \
+                            long pp = (long)g * 32 + j;                              \
+                            o[j] = pp < n_e ? (src)[pp * (m) + c] : 0.0;             \
+                        }                                                            \
+                        else mx_group_deq(v, o);                                     \
+                        for (j = 0; j < 32; ++j) (dst)[((long)g * 32 + j) * (m) + c] = o[j]; \
+                    }
+                ORC_DIM1(xs, H, cq)
+                ORC_DIM1(dgs, I2, cq2)
+                for (h = 0; h < H; ++h)
+                    for (c = 0; c < I2; ++c) {
+                        double s = 0.0;
+                        for (p = 0; p < np; ++p) s += cq[p * H + h] * cq2[p * I2 + c];
+                        ow[(long)h * I2 + c] = s;
+                    }
+                ORC_DIM1(hs, I, cq)
+                ORC_DIM1(dys, H, cq2)
+                for (ii = 0; ii < I; ++ii)
+                    for (n = 0; n < H; ++n) {
+                        double s = 0.0;
+                        for (p = 0; p < np; ++p) s += cq[p * I + ii] * cq2[p * H + n];
+                        od[(long)ii * H + n] = s;
+                    }
+#undef ORC_DIM1
+            }
+            free(cq); free(cq2);
+        }
+    next_e:
+        free(WgK); free(Wg2); free(WdK); free(WdH); free(gu); free(hq); free(y); free(dyq);
+        free(dh); free(dgu); free(fv); free(rl); free(xs); free(hs); free(dys); free(dgs);
+    }
+    if (bad) goto done;
+    /* dx: the token's route input gradients summed over j ascending */
+    for (i = 0; i < n_tok; ++i) {
+        int j, h;
+        for (h = 0; h < H; ++h) {
+            double s = 0.0;
+            for (j = 0; j < k; ++j) s += da[((long)i * k + j) * H + h];
+            dx[(long)i * H + h] = s;
+        }
+    }
+done:
+    free(slot); free(exp_slot); free(xa); free(da);
+    return bad ? -1 : 0;
+}

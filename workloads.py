@@ -173,6 +173,12 @@ def random_activations(T, H, E, seed, logits="normal"):
     return dict(x=x, logits=np.ascontiguousarray(lg, dtype=np.float32))
 
 
+def random_upstream(T, H, seed):
+    """An upstream gradient dout for the layer output: bf16 bits [T, H], unit normal."""
+    rng = np.random.default_rng([seed, 7])
+    return to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+
+
 @functools.lru_cache(maxsize=2)
 def workload_weights(name: str):
     w = WORKLOADS[name]
