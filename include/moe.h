@@ -348,6 +348,77 @@ int moe_forward_profiled(const void *x, const moe_routes *routes, const moe_pack
                          void **stage_events, int n_events, int *n_stages,
                          const char **stage_names);
 
+/* ---------------------------------------------------- MX training backward --
+ * The layer's gradients under the MX training recipe of "[mxfp8 moe training]
+ * add per group blocked scale kernels" (Summary and its stacked pull requests:
+ * the "dim1" cast in the backward, per-expert weight scales, per-group padded
+ * scale rows).  Every backward product runs on MX operands (e4m3 codes, one
+ * E8M0 scale per 32 values) quantised along its own reduction dimension:
+ *   dh  = dy W_down^T, dy = gate * dout          (operands along H)
+ *   dx  = sum over the token's routes of dGU W_gate_up^T, dGU = [dgate | dup]
+ *         the SwiGLU backward                     (operands along 2I)
+ *   dW_down[e]    = h_e^T dy_e, dW_gate_up[e] = x_e^T dGU_e  (operands along
+ *         expert e's routes in sorted order, 32 per scale, each expert's
+ *         segment zero-padded to 64 at offsets built on the device)
+ *   dgate[r] = <dout[t], y_r>, y_r route r's Down output before its gate.
+ * The quantisers pass gradients through unchanged.  The forward quantities
+ * (g, u, h, y) are recomputed from x and the weights, as the MX forward
+ * computes them.  Grouped path only; H and I multiples of 256, up to 8192.
+ *
+ * Weight preparation, once per weight update: from bf16 master weights
+ * w_gate_up [E][H][2I] and w_down [E][I][H], four packed MX operand sets --
+ * W_gate_up along H and W_down along I (the recomputed forward), W_down^T
+ * along H and W_gate_up^T along 2I (the input gradients) -- in buf (device,
+ * moe_mx_train_weights_size bytes, caller-owned; 0 for an unsupported
+ * shape), described by *out (host; its tag is cleared on error).  Enqueued on
+ * stream; no synchronisation. */
+#define MOE_TRAIN_TAG 0x4d6f4542u
+typedef struct {
+    const void *gate_up_k;              /* W_gate_up along H: N = 2I, K = H */
+    const uint8_t *gate_up_k_scales;
+    const void *down_k;                 /* W_down along I: N = H, K = I */
+    const uint8_t *down_k_scales;
+    const void *down_t;                 /* W_down^T along H: N = I, K = H */
+    const uint8_t *down_t_scales;
+    const void *gate_up_t;              /* W_gate_up^T along 2I: N = H, K = 2I */
+    const uint8_t *gate_up_t_scales;
+    int32_t E, H, I;
+    uint32_t tag;                       /* MOE_TRAIN_TAG once prepared */
+} moe_mx_train_weights;
+
+size_t moe_mx_train_weights_size(int E, int H, int I);
+int moe_prepare_mx_train_weights(const void *w_gate_up, const void *w_down, int E, int H, int I, void *buf,
+                                 size_t buf_bytes, moe_mx_train_weights *out, void *stream);
+
+/* Bytes of workspace moe_backward needs (0 for an unsupported shape). */
+size_t moe_backward_workspace_size(int T, int H, int I, int E, int k);
+
+/* Gradients of the layer for the upstream gradient dout (bf16 [T][H]):
+ *   x       bf16 [T][H], the forward's input
+ *   routes  moe_route's output for the forward (expert_offsets, perm,
+ *           route_pos and topk_weights are read)
+ *   w       moe_prepare_mx_train_weights' descriptor (its E must be the
+ *           routes' E)
+ *   dx      bf16 [T][H]; dgate fp32 [T][k] (route r = t*k + j);
+ *   dw_gate_up fp32 [E][H][2I], dw_down fp32 [E][I][H] (zero for an expert
+ *           without routes)
+ * All pointers device, 16-byte aligned, caller-owned; ws as sized above.
+ * Returns MOE_ERR_INVALID_ARG / UNSUPPORTED / WORKSPACE before anything is
+ * enqueued, MOE_ERR_HIP if a launch fails.  Deterministic: every sum runs in
+ * a fixed order.  No synchronisation. */
+int moe_backward(const void *x, const moe_routes *routes, const moe_mx_train_weights *w, const void *dout,
+                 void *dx, float *dgate, float *dw_gate_up, float *dw_down, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/* moe_backward with stage events, as moe_forward_profiled: stage_events[0]
+ * on the first kernel's start, stage_events[i] on the end of stage i's last
+ * kernel; the stages are "init,quant_x,gate_up,swiglu,down,dy,dh,swiglu_bwd,
+ * dx_rows,combine,dim1,wgrad_gate_up,wgrad_down" (T = 0: the last two). */
+int moe_backward_profiled(const void *x, const moe_routes *routes, const moe_mx_train_weights *w,
+                          const void *dout, void *dx, float *dgate, float *dw_gate_up, float *dw_down, void *ws,
+                          size_t ws_bytes, void *stream, void **stage_events, int n_events, int *n_stages,
+                          const char **stage_names);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *moe_last_error(void);
 

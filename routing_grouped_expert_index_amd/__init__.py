@@ -8,6 +8,9 @@ no GPU is present, the calls raise.
     routes = route(logits, k)                         # top-k + grouping by expert
     w = pack_weights(w_gate_up, w_down, quant)        # once per weight set
     out = forward(x, routes, w, scales=(s_gu, s_d), path="auto")
+
+    tw = prepare_mx_train_weights(w_gate_up_bf16, w_down_bf16)   # per weight update
+    g = backward(x, routes, tw, dout)                 # dx, dgate, dw_gate_up, dw_down
 """
 from __future__ import annotations
 
@@ -30,8 +33,11 @@ EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_route_project_workspac
             "moe_forward_workspace_size", "moe_forward_workspace_views", "moe_forward_launch_info",
             "moe_forward", "moe_forward_ex", "moe_decode_forward", "moe_decode_forward_noalloc",
             "moe_forward_profiled", "moe_forward_timed",
+            "moe_mx_train_weights_size", "moe_prepare_mx_train_weights", "moe_backward_workspace_size",
+            "moe_backward", "moe_backward_profiled",
             "moe_last_error"]
 PACKED_TAG = 0x4D6F4557
+TRAIN_TAG = 0x4D6F4542
 
 
 class MoeError(RuntimeError):
@@ -60,6 +66,14 @@ class _CPacked(ctypes.Structure):
     _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("E", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("quant", ctypes.c_int32),
                 ("tag", ctypes.c_uint32)]
+
+
+class _CTrain(ctypes.Structure):
+    _fields_ = [("gate_up_k", ctypes.c_void_p), ("gate_up_k_scales", ctypes.c_void_p),
+                ("down_k", ctypes.c_void_p), ("down_k_scales", ctypes.c_void_p),
+                ("down_t", ctypes.c_void_p), ("down_t_scales", ctypes.c_void_p),
+                ("gate_up_t", ctypes.c_void_p), ("gate_up_t_scales", ctypes.c_void_p),
+                ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("tag", ctypes.c_uint32)]
 
 
 class _CViews(ctypes.Structure):
@@ -123,6 +137,15 @@ def lib():
                                                                ctypes.POINTER(ctypes.c_int),
                                                                ctypes.POINTER(ctypes.c_char_p)]
     L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_mx_train_weights_size.restype = sz
+    L.moe_mx_train_weights_size.argtypes = [i32, i32, i32]
+    L.moe_prepare_mx_train_weights.argtypes = [P, P, i32, i32, i32, P, sz, ctypes.POINTER(_CTrain), P]
+    L.moe_backward_workspace_size.restype = sz
+    L.moe_backward_workspace_size.argtypes = [i32] * 5
+    L.moe_backward.argtypes = [P, ctypes.POINTER(_CRoutes), ctypes.POINTER(_CTrain), P, P, P, P, P, P, sz, P]
+    L.moe_backward_profiled.argtypes = L.moe_backward.argtypes + [ctypes.POINTER(ctypes.c_void_p), i32,
+                                                                  ctypes.POINTER(ctypes.c_int),
+                                                                  ctypes.POINTER(ctypes.c_char_p)]
     L.moe_last_error.argtypes = []
     _lib = L
     return L
@@ -434,4 +457,82 @@ def forward(x: torch.Tensor, routes: Routes, weights: PackedWeights,
     n = ctypes.c_int(0)
     names = ctypes.c_char_p()
     _check(lib().moe_forward_profiled(*args, handles, len(events), ctypes.byref(n), ctypes.byref(names)))
+    return out, names.value.decode().split(",")[: n.value]
+
+
+class TrainWeights:
+    """The four packed MX operand sets moe_prepare_mx_train_weights builds from
+    bf16 master weights (one device buffer) and their C descriptor."""
+
+    def __init__(self, buf: torch.Tensor, desc: _CTrain):
+        self.buf, self.desc = buf, desc
+
+    E = property(lambda self: self.desc.E)
+    H = property(lambda self: self.desc.H)
+    I = property(lambda self: self.desc.I)
+
+
+def mx_train_weights_size(E: int, H: int, I: int) -> int:
+    return int(lib().moe_mx_train_weights_size(E, H, I))
+
+
+def prepare_mx_train_weights(w_gate_up: torch.Tensor, w_down: torch.Tensor, stream=None) -> TrainWeights:
+    """bf16 master weights [E,H,2I], [E,I,H] -> the MX operand sets of the
+    recomputed forward and of the input gradients (moe_prepare_mx_train_weights)."""
+    _need_cuda(w_gate_up, "w_gate_up")
+    _need_cuda(w_down, "w_down")
+    if w_gate_up.element_size() != 2 or w_down.element_size() != 2:
+        raise ValueError("master weights must be bf16")
+    E, H, I2 = w_gate_up.shape
+    I = I2 // 2
+    if tuple(w_down.shape) != (E, I, H):
+        raise ValueError("w_down must be [E, I, H]")
+    need = mx_train_weights_size(E, H, I)
+    buf = torch.empty(max(need, 256), dtype=torch.uint8, device=w_gate_up.device)
+    desc = _CTrain()
+    _check(lib().moe_prepare_mx_train_weights(_ptr(w_gate_up), _ptr(w_down), E, H, I, _ptr(buf), need,
+                                              ctypes.byref(desc), _stream(w_gate_up.device, stream)))
+    return TrainWeights(buf, desc)
+
+
+def backward_workspace_size(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(lib().moe_backward_workspace_size(T, H, I, E, k))
+
+
+def backward(x: torch.Tensor, routes: Routes, weights: TrainWeights, dout: torch.Tensor,
+             workspace: torch.Tensor | None = None, stream=None, events=None, out=None):
+    """The layer's gradients for the upstream gradient dout bf16 [T, H]
+    (moe_backward): dict(dx bf16 [T,H], dgate fp32 [T,k], dw_gate_up fp32
+    [E,H,2I], dw_down fp32 [E,I,H]).  With events (torch.cuda.Event list) it
+    calls moe_backward_profiled and also returns the stage names."""
+    _need_cuda(x, "x")
+    _need_cuda(dout, "dout")
+    if not isinstance(weights, TrainWeights):
+        raise TypeError("weights must be what prepare_mx_train_weights returned")
+    T, H = x.shape
+    E, k, I = routes.E, routes.k, weights.I
+    dev = x.device
+    if out is None:
+        out = {"dx": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+               "dgate": torch.empty((T, k), dtype=torch.float32, device=dev),
+               "dw_gate_up": torch.empty((E, H, 2 * I), dtype=torch.float32, device=dev),
+               "dw_down": torch.empty((E, I, H), dtype=torch.float32, device=dev)}
+    need = backward_workspace_size(T, H, I, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    cs = routes.c_struct()
+    args = (_ptr(x), ctypes.byref(cs), ctypes.byref(weights.desc), _ptr(dout), _ptr(out["dx"]),
+            _ptr(out["dgate"]), _ptr(out["dw_gate_up"]), _ptr(out["dw_down"]), _ptr(workspace),
+            workspace.numel(), _stream(dev, stream))
+    if events is None:
+        _check(lib().moe_backward(*args))
+        return out
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    for ev in events:
+        if ev is not None and not ev.cuda_event:
+            ev.record(st)
+    handles = (ctypes.c_void_p * len(events))(*[ev.cuda_event if ev is not None else None for ev in events])
+    n = ctypes.c_int(0)
+    names = ctypes.c_char_p()
+    _check(lib().moe_backward_profiled(*args, handles, len(events), ctypes.byref(n), ctypes.byref(names)))
     return out, names.value.decode().split(",")[: n.value]

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 SOURCES = ["route.hip", "pack.hip", "forward.hip", "gemm.hip", "route_direct.hip",
-           "noalloc.hip", "moe_api.cpp"]
+           "noalloc.hip", "backward.hip", "moe_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,0 +1,448 @@
+// Backward of the MoE FFN layer under the MX training recipe ("[mxfp8 moe
+// training] add per group blocked scale kernels": Summary and its stacked pull
+// requests -- the "dim1" cast in the backward, per-expert weight scales,
+// per-group padded scale rows).  Every backward product runs on MX operands
+// (e4m3 codes, one E8M0 scale per 32 values) quantised along that product's
+// own reduction dimension:
+//   input gradients   dh = dy W_down^T (along H), dx_r = dGU W_gate_up^T
+//                     (along 2I): the grouped MX GEMM of the forward, on
+//                     weights packed transposed;
+//   weight gradients  dW_down[e] = h_e^T dy_e, dW_gate_up[e] = x_e^T dGU_e:
+//                     both operands quantised along the expert's routes (the
+//                     "dim1" cast), each expert's route segment padded to 64
+//                     with zeros at offsets built on device, and multiplied
+//                     by wgrad_kernel.
+// The quantisers pass gradients through unchanged (straight-through).
+#include <hip/hip_ext.h>
+
+#include <algorithm>
+
+#include "common.cuh"
+#include "launch.h"
+
+namespace moe {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint8_t e4m3_byte(float v) { return (uint8_t)(f32x2_to_e4m3x2(v, 0.0f) & 0xffu); }
+
+// ------------------------------------------------------------- weights --
+
+// bf16 master weights -> e4m3 codes and E8M0 bytes in the [E][K][N]
+// orientation the packer takes (K the reduction dimension of the product that
+// will read them), one scale per 32 consecutive k of each column n:
+//   along_k = 1: src [E][K][N] (the groups run down the source's rows);
+//   along_k = 0: src [E][N][K] (the groups run along the source's rows: the
+//                transposed use of a weight).
+// One thread per group; threads vary n fastest.
+__global__ void __launch_bounds__(256)
+mx_weights_kernel(const uint16_t* __restrict__ src, int E, int K, int N, int along_k, uint8_t* __restrict__ codes,
+                  uint8_t* __restrict__ bytes) {
+    const long g = (long)blockIdx.x * 256 + threadIdx.x;
+    const int nkb = K / 32;
+    if (g >= (long)E * nkb * N) return;
+    const int n = (int)(g % N);
+    const int kb = (int)((g / N) % nkb);
+    const long e = g / N / nkb;
+    float v[32];
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const int kk = 32 * kb + j;
+        const uint16_t w = along_k ? src[(e * K + kk) * N + n] : src[(e * N + n) * K + kk];
+        v[j] = bf16_to_f32(w);
+        a = fmaxf(a, fabsf(v[j]));
+    }
+    const uint32_t b = mx_byte(a);
+    const float inv = mx_inv(b);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) codes[(e * K + 32 * kb + j) * N + n] = e4m3_byte(v[j] * inv);
+    bytes[(e * nkb + kb) * N + n] = (uint8_t)b;
+}
+
+hipError_t launch_mx_weights(const uint16_t* src, int E, int K, int N, bool along_k, uint8_t* codes, uint8_t* bytes,
+                             hipStream_t st) {
+    const long groups = (long)E * (K / 32) * N;
+    hipLaunchKernelGGL(mx_weights_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, src, E, K, N,
+                       along_k ? 1 : 0, codes, bytes);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------- row-wise MX of routes --
+
+// Four threads quantise one group of 32 values of a row (8 each): returns the
+// group's E8M0 byte; codes written as 8 bytes at q.
+__device__ __forceinline__ uint32_t mx_quad(const float v[8], uint8_t* q) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    const uint32_t b = mx_byte(a);
+    const float inv = mx_inv(b);
+    uint2 w;
+    w.x = f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    w.y = f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    *reinterpret_cast<uint2*>(q) = w;
+    return b;
+}
+
+__device__ __forceinline__ void load8_bf16(const uint16_t* p, float v[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ void load8_f32(const float* p, float v[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = a[i];
+        v[4 + i] = b[i];
+    }
+}
+
+__device__ __forceinline__ void store8_f32(float* p, const float v[8]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// Forward recomputation: g|u (fp32 [R][2I], sorted routes) -> h = silu(g) u
+// (fp32 [R][I], kept for the weight gradient) and its MX rows (codes [R][I],
+// bytes [R][I/32] in the MX GEMM's scale order) for the Down product.
+__global__ void __launch_bounds__(256)
+swiglu_fwd_kernel(const float* __restrict__ gu, long R, int I, float* __restrict__ h32, uint8_t* __restrict__ hq,
+                  uint8_t* __restrict__ sh) {
+    const int gpr = I / 32;
+    const long grp = (long)blockIdx.x * 64 + threadIdx.x / 4;
+    if (grp >= R * gpr) return;   // (whole quads: 64 groups per workgroup)
+    const int sub = threadIdx.x & 3;
+    const long row = grp / gpr;
+    const int c = (int)(grp % gpr) * 32 + sub * 8;
+    float g[8], u[8], h[8];
+    load8_f32(gu + row * 2 * I + c, g);
+    load8_f32(gu + row * 2 * I + I + c, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = silu(g[i]) * u[i];
+    store8_f32(h32 + row * I + c, h);
+    const uint32_t b = mx_quad(h, hq + row * I + c);
+    if (sub == 0) sh[row * gpr + mx_scale_pos((int)(grp % gpr))] = (uint8_t)b;
+}
+
+// One workgroup per sorted route i (route r = perm[i] of token t = r / k, gate
+// w = tw[r]): dy = w * dout[t] in fp32, its MX rows (codes [R][H], bytes
+// [R][H/32]) for dh = dy W_down^T, and the gate's gradient <dout[t], y_i>
+// (y: the recomputed Down output, fp32 [R][H] sorted) written to dgate[r].
+// The sum runs per thread over its columns in order, then over the wave and
+// the four waves in a fixed order.
+__global__ void __launch_bounds__(256)
+dy_kernel(const uint16_t* __restrict__ dout, const float* __restrict__ tw, const int32_t* __restrict__ perm, int k,
+          const float* __restrict__ y, int H, uint8_t* __restrict__ dyq, uint8_t* __restrict__ sdy,
+          float* __restrict__ dgate) {
+    __shared__ float part[4];
+    const long i = blockIdx.x;
+    const int r = perm[i];
+    const int t = r / k;
+    const float w = tw[r];
+    const int gpr = H / 32;
+    float dsum = 0.0f;
+    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+        float d[8], yy[8], v[8];
+        load8_bf16(dout + (long)t * H + c, d);
+        load8_f32(y + i * H + c, yy);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            v[j] = w * d[j];
+            dsum = fmaf(d[j], yy[j], dsum);
+        }
+        const uint32_t b = mx_quad(v, dyq + i * H + c);
+        if ((threadIdx.x & 3) == 0) sdy[i * gpr + mx_scale_pos(c / 32)] = (uint8_t)b;
+    }
+    dsum = wave_sum(dsum);
+    if (lane_id() == 0) part[threadIdx.x / kWave] = dsum;
+    __syncthreads();
+    if (threadIdx.x == 0) dgate[r] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+// SwiGLU backward per sorted route (g|u and dh fp32): dgate = dh u s (1 + g (1 - s)), dup = dh
+// g s (s = sigmoid(g)), kept as fp32 [R][2I] for the weight gradient, and its
+// MX rows (codes [R][2I], bytes [R][2I/32]) for dx_r = dGU W_gate_up^T.
+__global__ void __launch_bounds__(256)
+swiglu_bwd_kernel(const float* __restrict__ gu, const float* __restrict__ dh, long R, int I,
+                  float* __restrict__ dgu, uint8_t* __restrict__ dguq, uint8_t* __restrict__ sdgu) {
+    const int gpr = I / 32, gpr2 = 2 * gpr;
+    const long grp = (long)blockIdx.x * 64 + threadIdx.x / 4;
+    if (grp >= R * gpr) return;
+    const int sub = threadIdx.x & 3;
+    const long row = grp / gpr;
+    const int cg = (int)(grp % gpr);
+    const int c = cg * 32 + sub * 8;
+    float g[8], u[8], d[8], dg[8], du[8];
+    load8_f32(gu + row * 2 * I + c, g);
+    load8_f32(gu + row * 2 * I + I + c, u);
+    load8_f32(dh + row * I + c, d);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float s = 1.0f / (1.0f + __expf(-g[j]));
+        dg[j] = d[j] * u[j] * s * (1.0f + g[j] * (1.0f - s));
+        du[j] = d[j] * g[j] * s;
+    }
+    float* o = dgu + row * 2 * I;
+    store8_f32(o + c, dg);
+    store8_f32(o + I + c, du);
+    const uint32_t bg = mx_quad(dg, dguq + row * 2 * I + c);
+    const uint32_t bu = mx_quad(du, dguq + row * 2 * I + I + c);
+    if (sub == 0) {
+        sdgu[row * gpr2 + mx_scale_pos(cg)] = (uint8_t)bg;
+        sdgu[row * gpr2 + mx_scale_pos(gpr + cg)] = (uint8_t)bu;
+    }
+}
+
+// ------------------------------------------------- per-expert route segments --
+
+// poff[e] = sum over e' < e of the expert's route count rounded up to 64 (the
+// weight-gradient product's K step), poff[E] the padded total: the per-group
+// padded start offsets, built on the device from the routing's offsets.
+__global__ void __launch_bounds__(64)
+pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restrict__ poff) {
+    if (threadIdx.x != 0) return;
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+        poff[e] = acc;
+        acc += (offsets[e + 1] - offsets[e] + 63) & ~63;
+    }
+    poff[E] = acc;
+}
+
+// The "dim1" cast: an operand v[i][m] over sorted routes i (M columns),
+// quantised along the routes of each expert, 32 per E8M0 scale, and written
+// transposed: row m of the output holds the padded route positions p (expert
+// e's routes at poff[e] + (i - offsets[e]), zeros up to poff[e+1]) as e4m3
+// codes, each 64-position slice in chunk order 0, 2, 1, 3 (the scaled MFMA's
+// lane-half order: lane half hh reads bytes [32hh, 32hh + 32) of a slice), and
+// the scale bytes of route block b at mx_scale_pos(b) of the row's bytes.
+// One workgroup per 32 padded positions and 256 columns.
+enum Dim1Src { D1_X = 0, D1_DY = 1, D1_F32 = 2 };
+
+template <int SRC>
+__global__ void __launch_bounds__(256)
+dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, const float* __restrict__ tw,
+            const int32_t* __restrict__ perm, int k, const int32_t* __restrict__ offsets,
+            const int32_t* __restrict__ poff, int E, int M, long ldo, long lds_, uint8_t* __restrict__ out,
+            uint8_t* __restrict__ sout) {
+    const int gi = blockIdx.x;                     // block of 32 padded positions
+    const int m = blockIdx.y * 256 + threadIdx.x;
+    const int p0 = gi * 32;
+    if (p0 >= poff[E]) return;
+    // the expert whose padded segment holds p0
+    int lo = 0, hi = E;                            // poff[lo] <= p0 < poff[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (poff[mid] <= p0) lo = mid;
+        else hi = mid;
+    }
+    const int e = lo;
+    const int first = offsets[e] + (p0 - poff[e]);       // sorted row of position p0
+    const int cnt = min(32, offsets[e + 1] - first);     // real routes in this block (may be <= 0)
+    if (m >= M) return;
+    float v[32];
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        float x = 0.0f;
+        if (j < cnt) {
+            const long i = first + j;
+            if (SRC == D1_X) {
+                x = bf16_to_f32(static_cast<const uint16_t*>(src)[(long)(perm[i] / k) * M + m]);
+            } else if (SRC == D1_DY) {
+                const int r = perm[i];
+                x = tw[r] * bf16_to_f32(dout[(long)(r / k) * M + m]);
+            } else {
+                x = static_cast<const float*>(src)[i * M + m];
+            }
+        }
+        v[j] = x;
+        a = fmaxf(a, fabsf(x));
+    }
+    const uint32_t b = mx_byte(a);
+    const float inv = mx_inv(b);
+    u32x4 lo4, hi4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        lo4[t] = f32x4_to_e4m3x4(v[4 * t] * inv, v[4 * t + 1] * inv, v[4 * t + 2] * inv, v[4 * t + 3] * inv);
+        hi4[t] = f32x4_to_e4m3x4(v[16 + 4 * t] * inv, v[16 + 4 * t + 1] * inv, v[16 + 4 * t + 2] * inv,
+                                 v[16 + 4 * t + 3] * inv);
+    }
+    // block gi of its 64-position slice: even -> chunks 0, 1 at bytes 0, 32;
+    // odd -> chunks 2, 3 at bytes 16, 48
+    uint8_t* row = out + (long)m * ldo + (long)(gi >> 1) * 64 + 16 * (gi & 1);
+    *reinterpret_cast<u32x4*>(row) = lo4;
+    *reinterpret_cast<u32x4*>(row + 32) = hi4;
+    sout[(long)m * lds_ + mx_scale_pos(gi)] = (uint8_t)b;
+}
+
+// ------------------------------------------------------- weight gradients --
+
+// C[e] (fp32 [M][N]) = sum over expert e's padded route positions p of
+// A[m][p] B[n][p], with A, B the dim1-cast operands (row stride ldo bytes,
+// scale row stride lds_ bytes).  One workgroup per 128x128 output tile; wave
+// w takes rows 64 (w / 2) and columns 64 (w % 2) of it as 2x2 blocks of the
+// scaled 32x32x64 MFMA (K step: one 64-position slice); operand fragments
+// come straight from memory, one slice ahead.  An expert without routes gets
+// zeros.
+__global__ void __launch_bounds__(256)
+wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const uint8_t* __restrict__ B,
+             const uint8_t* __restrict__ sB, long ldo, long lds_, const int32_t* __restrict__ poff, int E, int M,
+             int N, float* __restrict__ C) {
+    const int tm = M / 128, tn = N / 128;
+    const long total = (long)E * tm * tn;
+    long tile = blockIdx.x;
+    // consecutive tiles (one expert's, sharing operand rows) on one XCD:
+    // workgroup b runs on XCD b % 8
+    if (total % 8 == 0) tile = (long)(blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
+    const int e = (int)(tile / ((long)tm * tn));
+    const int rem = (int)(tile % ((long)tm * tn));
+    const int mt = rem / tn, nt = rem % tn;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int j = lane & 31, hh = lane >> 5;
+    const int m0 = mt * 128 + (wave >> 1) * 64, n0 = nt * 128 + (wave & 1) * 64;
+    const int s0 = poff[e] / 64, s1 = poff[e + 1] / 64;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[f][g][i] = 0.0f;
+    const uint8_t* pa[2] = {A + (long)(m0 + j) * ldo + 32 * hh, A + (long)(m0 + 32 + j) * ldo + 32 * hh};
+    const uint8_t* pb[2] = {B + (long)(n0 + j) * ldo + 32 * hh, B + (long)(n0 + 32 + j) * ldo + 32 * hh};
+    const uint8_t* qa[2] = {sA + (long)(m0 + j) * lds_ + 4 * hh, sA + (long)(m0 + 32 + j) * lds_ + 4 * hh};
+    const uint8_t* qb[2] = {sB + (long)(n0 + j) * lds_ + 4 * hh, sB + (long)(n0 + 32 + j) * lds_ + 4 * hh};
+    struct Frag {
+        u32x4 a[2][2], b[2][2];
+        uint32_t sa[2], sb[2];
+    };
+    auto load = [&](int s, Frag& F) __attribute__((always_inline)) {
+        const long o = (long)s * 64, so = (long)(s >> 2) * 8;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            F.a[f][0] = *reinterpret_cast<const u32x4*>(pa[f] + o);
+            F.a[f][1] = *reinterpret_cast<const u32x4*>(pa[f] + o + 16);
+            F.b[f][0] = *reinterpret_cast<const u32x4*>(pb[f] + o);
+            F.b[f][1] = *reinterpret_cast<const u32x4*>(pb[f] + o + 16);
+            F.sa[f] = *reinterpret_cast<const uint32_t*>(qa[f] + so);
+            F.sb[f] = *reinterpret_cast<const uint32_t*>(qb[f] + so);
+        }
+    };
+    auto mma = [&](int s, const Frag& F) __attribute__((always_inline)) {
+        const int sh = 8 * (s & 3);   // byte s % 4 of the scale dword: slice s's block of this lane half
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const i32x8 av{(int)F.a[f][0][0], (int)F.a[f][0][1], (int)F.a[f][0][2], (int)F.a[f][0][3],
+                           (int)F.a[f][1][0], (int)F.a[f][1][1], (int)F.a[f][1][2], (int)F.a[f][1][3]};
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const i32x8 bv{(int)F.b[g][0][0], (int)F.b[g][0][1], (int)F.b[g][0][2], (int)F.b[g][0][3],
+                               (int)F.b[g][1][0], (int)F.b[g][1][1], (int)F.b[g][1][2], (int)F.b[g][1][3]};
+                acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    av, bv, acc[f][g], 0, 0, 0, (int)((F.sa[f] >> sh) & 0xffu), 0, (int)((F.sb[g] >> sh) & 0xffu));
+            }
+        }
+    };
+    if (s0 < s1) {
+        Frag cur, nxt;
+        load(s0, cur);
+        for (int s = s0; s < s1; ++s) {
+            if (s + 1 < s1) load(s + 1, nxt);
+            mma(s, cur);
+            cur = nxt;
+        }
+    }
+    // acc[f][g][i]: row m0 + 32f + 8(i/4) + 4hh + i%4, column n0 + 32g + j
+    float* ce = C + (long)e * M * N;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + 32 * f + 8 * (i >> 2) + 4 * hh + (i & 3);
+                ce[(long)row * N + n0 + 32 * g + j] = acc[f][g][i];
+            }
+}
+
+// a fill kernel (no memset node where a caller captures the sequence)
+__global__ void __launch_bounds__(256) fill_f32_kernel(float* __restrict__ p, long n, float v) {
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = v;
+}
+
+// ------------------------------------------------------------- launchers --
+
+hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<long>(1024, (n + 255) / 256);
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(grid), dim3(256), 0, st, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_fwd(const float* gu, long R, int I, float* h32, uint8_t* hq, uint8_t* sh,
+                             hipEvent_t ev_end, hipStream_t st) {
+    const long groups = R * (I / 32);
+    if (groups == 0) return hipSuccess;
+    hipExtLaunchKernelGGL(swiglu_fwd_kernel, dim3((unsigned)((groups + 63) / 64)), dim3(256), 0, st, nullptr, ev_end,
+                          0, gu, R, I, h32, hq, sh);
+    return hipGetLastError();
+}
+
+hipError_t launch_dy(const uint16_t* dout, const float* tw, const int32_t* perm, int k, const float* y, long R,
+                     int H, uint8_t* dyq, uint8_t* sdy, float* dgate, hipEvent_t ev_end, hipStream_t st) {
+    if (R == 0) return hipSuccess;
+    hipExtLaunchKernelGGL(dy_kernel, dim3((unsigned)R), dim3(256), 0, st, nullptr, ev_end, 0, dout, tw, perm, k, y,
+                          H, dyq, sdy, dgate);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const float* gu, const float* dh, long R, int I, float* dgu, uint8_t* dguq,
+                             uint8_t* sdgu, hipEvent_t ev_end, hipStream_t st) {
+    const long groups = R * (I / 32);
+    if (groups == 0) return hipSuccess;
+    hipExtLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((groups + 63) / 64)), dim3(256), 0, st, nullptr, ev_end,
+                          0, gu, dh, R, I, dgu, dguq, sdgu);
+    return hipGetLastError();
+}
+
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st) {
+    hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, st, offsets, E, poff);
+    return hipGetLastError();
+}
+
+hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, const float* tw, const int32_t* perm,
+                       int k, const int32_t* offsets, const int32_t* poff, int E, int M, long Rp, long ldo, long lds_,
+                       uint8_t* out, uint8_t* sout, hipEvent_t ev_end, hipStream_t st) {
+    const dim3 grid((unsigned)(Rp / 32), (unsigned)((M + 255) / 256));
+    if (Rp == 0) return hipSuccess;
+    if (src_kind == D1_X)
+        hipExtLaunchKernelGGL(dim1_kernel<D1_X>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm, k,
+                              offsets, poff, E, M, ldo, lds_, out, sout);
+    else if (src_kind == D1_DY)
+        hipExtLaunchKernelGGL(dim1_kernel<D1_DY>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm, k,
+                              offsets, poff, E, M, ldo, lds_, out, sout);
+    else
+        hipExtLaunchKernelGGL(dim1_kernel<D1_F32>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm,
+                              k, offsets, poff, E, M, ldo, lds_, out, sout);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, long ldo, long lds_,
+                        const int32_t* poff, int E, int M, int N, float* C, hipEvent_t ev_end, hipStream_t st) {
+    const long total = (long)E * (M / 128) * (N / 128);
+    hipExtLaunchKernelGGL(wgrad_kernel, dim3((unsigned)total), dim3(256), 0, st, nullptr, ev_end, 0, A, sA, B, sB, ldo,
+                          lds_, poff, E, M, N, C);
+    return hipGetLastError();
+}
+
+}  // namespace moe

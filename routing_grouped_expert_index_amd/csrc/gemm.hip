@@ -152,14 +152,14 @@ gemm32_kernel(const GemmArgs g) {
     // The resource starts at the tile's first output row (64-bit address
     // arithmetic in scalar registers) and covers at most 2 GiB, so C may be any
     // size and offset 2^31 is always past its end.
-    constexpr long EBC = EPI == EPI_SWIGLU_F32 ? 4 : (EPI == EPI_Y_BF16 || EPI == EPI_SWIGLU_BF16) ? 2 : 1;
+    constexpr long EBC = EPI == EPI_SWIGLU_F32 || EPI == EPI_Y_F32 ? 4 : (EPI == EPI_Y_BF16 || EPI == EPI_SWIGLU_BF16) ? 2 : 1;
     auto make_crsrc = [&](int row0_) __attribute__((always_inline)) {
         const long base = (long)row0_ * g.ldc * EBC, left = g.c_bytes - base;
         return __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(g.C) + base, 0,
                                                  (int)(left < 0x7fffffffL ? left : 0x7fffffffL), 0x00020000);
     };
     constexpr uint32_t kDropped = 0x80000000u;                // past the end of every C resource
-    constexpr int CPL = EPI == EPI_SWIGLU_BF16 ? 2 : 4;       // chunks per lane and row
+    constexpr int CPL = EPI == EPI_SWIGLU_BF16 ? 2 : EPI == EPI_Y_F32 ? 8 : 4;   // chunks per lane and row
     constexpr int CB = 2 * CPL;                               // chunks per row segment
     constexpr int RPP = kEpiStageBytes / (CB * 16);           // staged rows per phase
     constexpr int MPP = RPP / 32;                             // m blocks per phase
@@ -211,7 +211,7 @@ gemm32_kernel(const GemmArgs g) {
     // then scalar loads, not vector loads whose waits would drain the K loop
     auto col_blocks = [&](int wn0_, int& c0, int& c1) __attribute__((always_inline)) {
         const int P = wn0_ < g.N ? wn0_ : 0;
-        if constexpr (EPI == EPI_Y_BF16) {
+        if constexpr (EPI == EPI_Y_BF16 || EPI == EPI_Y_F32) {
             c0 = c1 = down_col_of_packed(P) / 128;
         } else {
             c0 = gate_up_col_of_packed(P, g.I) / 128;
@@ -548,6 +548,7 @@ gemm32_kernel(const GemmArgs g) {
         //   Y (bf16):       columns wn0 + 32hh + 16f + 8hv + [0,8)  -> chunk 4hh + 2f + hv
         //   SwiGLU bf16:    h columns wn0/2 + 16hh + 8h2 + [0,8)     -> chunk 2hh + h2
         //   SwiGLU fp32:    h columns wn0/2 + 16hh + 4h4 + [0,4)     -> chunk 4hh + h4
+        //   Y (fp32):       columns wn0 + 32hh + 16f + 8hv + 4q + [0,4) -> chunk 8hh + 4f + 2hv + q
         // Written straight out, one store instruction would touch 32 rows with two
         // 16-byte pieces each.  Instead the wave stages its segments in its own
         // LDS area and stores whole segments: each store instruction then covers
@@ -657,16 +658,16 @@ gemm32_kernel(const GemmArgs g) {
             // this lane's store offset for staged row lane/CB of phase 0, and how
             // many rows past it are valid (none for waves past N): a store of
             // row rr is kept while rr - lane/CB < rlim
-            constexpr int EB = EPI == EPI_SWIGLU_F32 ? 4 : 2;           // bytes per element
+            constexpr int EB = EPI == EPI_SWIGLU_F32 || EPI == EPI_Y_F32 ? 4 : 2;   // bytes per element
             constexpr int CE = 16 / EB;                                  // elements per chunk
-            const int c0 = EPI == EPI_Y_BF16 ? wn0 : wn0 / 2;
+            const int c0 = EPI == EPI_Y_BF16 || EPI == EPI_Y_F32 ? wn0 : wn0 / 2;
             const uint32_t lane_off =
                 ((uint32_t)(lane_e / CB) * (uint32_t)g.ldc + (uint32_t)(c0 + CE * (lane_e % CB))) * EB;
             const int rlim = wn0 < g.N ? rows - lane / CB : 0;
             const uint32_t row_bytes = (uint32_t)g.ldc * EB;
             // XOR swizzle of the chunk position: the 8 lanes an LDS cycle serves
             // land on 8 distinct 16-byte bank groups, for writes and reads
-            auto swz = [](int rr) { return CB == 8 ? (rr & 7) : ((rr >> 1) & 3); };
+            auto swz = [](int rr) { return CB == 16 ? (rr & 15) : CB == 8 ? (rr & 7) : ((rr >> 1) & 3); };
             uint8_t* ys = smem + LDS + wave * kEpiStageBytes;
             float fs = 1.0f;
             if constexpr (SC == SC_TENSOR) fs = ld_const(g.sa, 0) * ld_const(g.sw, e);
@@ -690,6 +691,18 @@ gemm32_kernel(const GemmArgs g) {
                                 for (int t = 0; t < 4; ++t)
                                     ch[2 * f + hv][t] = pack_bf16x2(acc[f][m][8 * hv + 2 * t] * fsc(f, m),
                                                                     acc[f][m][8 * hv + 2 * t + 1] * fsc(f, m));
+                    } else if constexpr (EPI == EPI_Y_F32) {
+                        // (each chunk goes to LDS as it is formed: 8 chunks held
+                        // at once would not fit beside the next tile's loads)
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {   // u = 4f + 2hv + q: columns ... + 8hv + 4q + [0,4)
+                            u32x4 v;
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                v[t] = __float_as_uint(acc[u >> 2][m][8 * ((u >> 1) & 1) + 4 * (u & 1) + t] *
+                                                       fsc(u >> 2, m));
+                            *reinterpret_cast<u32x4*>(ys + rr * (CB * 16) + (((CPL * hh + u) ^ swz(rr)) << 4)) = v;
+                        }
                     } else {
                         float hv[16];
 #pragma unroll
@@ -707,9 +720,11 @@ gemm32_kernel(const GemmArgs g) {
                                 for (int t = 0; t < 4; ++t) ch[h4][t] = __float_as_uint(hv[4 * h4 + t]);
                         }
                     }
+                    if constexpr (EPI != EPI_Y_F32) {
 #pragma unroll
-                    for (int u = 0; u < CPL; ++u)
-                        *reinterpret_cast<u32x4*>(ys + rr * (CB * 16) + (((CPL * hh + u) ^ swz(rr)) << 4)) = ch[u];
+                        for (int u = 0; u < CPL; ++u)
+                            *reinterpret_cast<u32x4*>(ys + rr * (CB * 16) + (((CPL * hh + u) ^ swz(rr)) << 4)) = ch[u];
+                    }
                 }
                 // LDS operations of one wave execute in order; this only keeps the
                 // compiler from moving the reads above the writes
@@ -895,6 +910,36 @@ hipError_t launch_grouped_down(const FwdPlan& p, hipStream_t st) {
     }
     a.sa_bytes = (long)p.T * p.k * (p.I / 128) * 4;
     return run_gemm32<true, false, SC_BLOCK, EPI_Y_BF16>(a, st, p.ev_stage_end);
+}
+
+hipError_t launch_grouped_mx_y(const MxProduct& q, hipStream_t st) {
+    GemmArgs a{};
+    a.A = q.A;
+    a.lda = q.K;
+    a.perm = q.perm;
+    a.k = q.k;
+    div_magic(q.k, a.kdiv_m, a.kdiv_s);
+    a.B = q.B;
+    a.N = q.N;
+    a.Kb = q.K;
+    a.tiles = q.tiles;
+    a.ntiles = q.ntiles;
+    a.offsets = q.offsets;
+    a.sa = reinterpret_cast<const float*>(q.sa);   // E8M0 bytes, K/128 dwords per row
+    a.sa_ld = q.K / 128;
+    a.swx = reinterpret_cast<const uint32_t*>(q.swx);
+    a.I = q.N;
+    a.C = q.C;
+    a.ldc = q.N;
+    a.c_bytes = q.R * q.N * (q.out_f32 ? 4 : 2);
+    a.max_tiles = q.max_tiles;
+    a.a_bytes = q.a_rows * q.K;
+    a.sa_bytes = q.a_rows * (q.K / 32);
+    if (q.out_f32)
+        return q.gather ? run_gemm32<true, true, SC_MX, EPI_Y_F32>(a, st, q.ev_end)
+                        : run_gemm32<true, false, SC_MX, EPI_Y_F32>(a, st, q.ev_end);
+    if (q.gather) return hipErrorInvalidValue;
+    return run_gemm32<true, false, SC_MX, EPI_Y_BF16>(a, st, q.ev_end);
 }
 
 }  // namespace moe

@@ -6,7 +6,7 @@
 
 namespace moe {
 
-enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_F32 = 1, EPI_SWIGLU_Q128 = 2, EPI_Y_BF16 = 3, EPI_SWIGLU_MX = 4 };
+enum Epi { EPI_SWIGLU_BF16 = 0, EPI_SWIGLU_F32 = 1, EPI_SWIGLU_Q128 = 2, EPI_Y_BF16 = 3, EPI_SWIGLU_MX = 4, EPI_Y_F32 = 5 };
 enum Scale { SC_NONE = 0, SC_TENSOR = 1, SC_BLOCK = 2, SC_MX = 3 };
 
 struct GemmArgs {

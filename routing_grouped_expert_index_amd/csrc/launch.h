@@ -102,6 +102,50 @@ struct FwdPlan {
 constexpr int kGemmBM = 128;
 
 int grouped_max_tiles(int R, int E);
+// MX products of the backward on the grouped GEMM kernel: C (fp32 or bf16
+// [R][N], sorted route rows; bf16 only without gather) = rows of A (e4m3, K bytes each, with E8M0 bytes per 32
+// in the MX scale order; the tokens perm[i] / k of an x-shaped A when gather)
+// times the packed B (N x K, moe_pack layout) of each row's expert.
+struct MxProduct {
+    const uint8_t* A;
+    const uint8_t* sa;
+    long a_rows;                // rows addressable in A and sa
+    int K, N;
+    const uint8_t* B;
+    const uint8_t* swx;         // packed weight scale dwords
+    bool gather;
+    const int32_t* perm;
+    int k;
+    const int32_t* tiles;
+    const int32_t* ntiles;
+    const int32_t* offsets;
+    int max_tiles;
+    void* C;
+    bool out_f32;
+    long R;
+    hipEvent_t ev_end;
+};
+hipError_t launch_grouped_mx_y(const MxProduct& q, hipStream_t st);
+
+// backward.hip
+hipError_t launch_mx_weights(const uint16_t* src, int E, int K, int N, bool along_k, uint8_t* codes, uint8_t* bytes,
+                             hipStream_t st);
+hipError_t launch_swiglu_fwd(const float* gu, long R, int I, float* h32, uint8_t* hq, uint8_t* sh,
+                             hipEvent_t ev_end, hipStream_t st);
+hipError_t launch_dy(const uint16_t* dout, const float* tw, const int32_t* perm, int k, const float* y, long R,
+                     int H, uint8_t* dyq, uint8_t* sdy, float* dgate, hipEvent_t ev_end, hipStream_t st);
+hipError_t launch_swiglu_bwd(const float* gu, const float* dh, long R, int I, float* dgu, uint8_t* dguq,
+                             uint8_t* sdgu, hipEvent_t ev_end, hipStream_t st);
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);
+// src_kind 0: x bf16 [T][M] through perm; 1: gate * dout (dout bf16 [T][M]);
+// 2: fp32 [R][M] in sorted order
+hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, const float* tw, const int32_t* perm,
+                       int k, const int32_t* offsets, const int32_t* poff, int E, int M, long Rp, long ldo, long lds_,
+                       uint8_t* out, uint8_t* sout, hipEvent_t ev_end, hipStream_t st);
+hipError_t launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, long ldo, long lds_,
+                        const int32_t* poff, int E, int M, int N, float* C, hipEvent_t ev_end, hipStream_t st);
+hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t st);
+
 hipError_t launch_forward_init(const FwdPlan& p, bool build_tiles, hipStream_t st);
 hipError_t launch_quant_x(const FwdPlan& p, hipStream_t st);
 hipError_t launch_quant_h(const FwdPlan& p, hipStream_t st);

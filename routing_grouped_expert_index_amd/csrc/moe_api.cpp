@@ -519,3 +519,321 @@ int moe_forward_profiled(const void* x, const moe_routes* routes, const moe_pack
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ MX backward --
+
+namespace {
+
+bool train_shape_ok(int H, int I, int E) {
+    return H > 0 && I > 0 && E >= 1 && E <= moe::kMaxExperts && H % 256 == 0 && I % 256 == 0 && H <= 8192 &&
+           I <= 8192 && (long)E * H * 2 * I < (1L << 40);
+}
+
+struct TrainLayout {
+    size_t gu_k, gu_k_s, d_k, d_k_s, d_t, d_t_s, gu_t, gu_t_s, tmp, tmp_s, total;
+};
+
+TrainLayout train_layout(int E, int H, int I) {
+    TrainLayout L{};
+    const size_t w = (size_t)E * H * I;   // elements of W_down; W_gate_up has 2w
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at_ = off;
+        off += align256(bytes);
+        return at_;
+    };
+    L.gu_k = take(2 * w);
+    L.gu_k_s = take(2 * w / 32);
+    L.d_k = take(w);
+    L.d_k_s = take(w / 32);
+    L.d_t = take(w);
+    L.d_t_s = take(w / 32);
+    L.gu_t = take(2 * w);
+    L.gu_t_s = take(2 * w / 32);
+    L.tmp = take(2 * w);
+    L.tmp_s = take(2 * w / 32);
+    L.total = off;
+    return L;
+}
+
+struct BwdLayout {
+    size_t tiles, ntiles, amax, xq, sx, gu, h32, hq, sh, y, dyq, sdy, dh, dgu, dguq, sdgu, ones, poff;
+    size_t xT, sxT, dguT, sdguT, hT, shT, dyT, sdyT, total;
+    long Rp;
+};
+
+// padded route positions of the weight-gradient operands: every expert's
+// segment rounded up to 64, in whole 256-position scale-dword groups
+long bwd_padded_routes(long R, int E) { return (R + 63L * E + 255) / 256 * 256; }
+
+BwdLayout bwd_layout(int T, int H, int I, int E, int k) {
+    BwdLayout L{};
+    const size_t R = (size_t)T * k;
+    L.Rp = bwd_padded_routes((long)R, E);
+    const size_t Rp = (size_t)L.Rp, Rb = Rp / 32;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at_ = off;
+        off += align256(bytes);
+        return bytes ? at_ : (size_t)-1;
+    };
+    L.tiles = take(sizeof(int32_t) * 2 * (size_t)moe::grouped_max_tiles((int)R, E));
+    L.ntiles = take(sizeof(int32_t));
+    L.amax = take(2 * sizeof(uint32_t));
+    L.xq = take((size_t)T * H);
+    L.sx = take((size_t)T * (H / 32));
+    L.gu = take(R * 2 * I * 4);
+    L.h32 = take(R * I * 4);
+    L.hq = take(R * I);
+    L.sh = take(R * (I / 32));
+    L.y = take(R * H * 4);          // the recomputed Down output (fp32), then the rows of dx (bf16)
+    L.dyq = take(R * H);
+    L.sdy = take(R * (H / 32));
+    L.dh = take(R * I * 4);
+    L.dgu = take(R * 2 * I * 4);
+    L.dguq = take(R * 2 * I);
+    L.sdgu = take(R * (2 * I / 32));
+    L.ones = take(R * 4);
+    L.poff = take(sizeof(int32_t) * (size_t)(E + 1));
+    L.xT = take((size_t)H * Rp);
+    L.sxT = take((size_t)H * Rb);
+    L.dguT = take((size_t)2 * I * Rp);
+    L.sdguT = take((size_t)2 * I * Rb);
+    L.hT = take((size_t)I * Rp);
+    L.shT = take((size_t)I * Rb);
+    L.dyT = take((size_t)H * Rp);
+    L.sdyT = take((size_t)H * Rb);
+    L.total = off;
+    return L;
+}
+
+int check_train_shape(int T, int H, int I, int E, int k) {
+    if (T < 0 || k < 1 || E < k || E > moe::kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "need T >= 0 and 1 <= k <= E <= %d (T=%d k=%d E=%d)", moe::kMaxExperts, T, k,
+                    E);
+    if (!train_shape_ok(H, I, E))
+        return fail(MOE_ERR_UNSUPPORTED, "MX backward: H and I multiples of 256 up to 8192 (H=%d, I=%d)", H, I);
+    const long R = (long)T * k;
+    if (R >= (1L << 31) || (long)T * H >= (1L << 31) || R * 2 * I >= (1L << 31) || R * H >= (1L << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "MX backward: T*k*H and T*k*2I must stay below 2^31");
+    if ((long)H * bwd_padded_routes(R, E) >= (1L << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "MX backward: transposed operands too large");
+    return MOE_OK;
+}
+
+int backward_impl(const void* x, const moe_routes* routes, const moe_mx_train_weights* w, const void* dout,
+                  void* dx, float* dgate, float* dw_gate_up, float* dw_down, void* ws, size_t ws_bytes, void* stream,
+                  void** events, int n_events, int* n_stages, const char** stage_names) {
+    if (!routes || !w) return fail(MOE_ERR_INVALID_ARG, "routes or w is NULL");
+    const int T = routes->T, E = routes->E, k = routes->k, H = w->H, I = w->I;
+    int rc = check_train_shape(T, H, I, E, k);
+    if (rc != MOE_OK) return rc;
+    if (w->tag != MOE_TRAIN_TAG) return fail(MOE_ERR_INVALID_ARG, "w was not filled by moe_prepare_mx_train_weights");
+    if (w->E != E) return fail(MOE_ERR_INVALID_ARG, "weights prepared for E=%d, routes have E=%d", w->E, E);
+    if (!dw_gate_up || !dw_down || !routes->expert_offsets)
+        return fail(MOE_ERR_INVALID_ARG, "null pointer among dw_gate_up / dw_down / routes->expert_offsets");
+    if (T > 0 && (!x || !dout || !dx || !dgate || !routes->topk_weights || !routes->perm || !routes->route_pos))
+        return fail(MOE_ERR_INVALID_ARG, "null pointer among x / dout / dx / dgate / routes");
+    const void* ptrs[] = {x, dout, dx, dgate, dw_gate_up, dw_down, routes->topk_weights, routes->expert_offsets,
+                          routes->perm, routes->route_pos, ws};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    const BwdLayout L = bwd_layout(T, H, I, E, k);
+    if (ws_bytes < L.total || !ws)
+        return fail(MOE_ERR_WORKSPACE, "backward workspace: need %zu bytes, got %zu", L.total, ws_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const long R = (long)T * k, Rp = L.Rp, Rb = Rp / 32;
+    int32_t* poff = at<int32_t>(ws, L.poff);
+
+    int stage = 0;
+    static thread_local char names[256];
+    names[0] = '\0';
+    auto ev = [&]() -> hipEvent_t {
+        return events && stage + 1 < n_events ? static_cast<hipEvent_t>(events[stage + 1]) : nullptr;
+    };
+    auto mark = [&](const char* name) {
+        if (names[0]) strncat(names, ",", sizeof names - strlen(names) - 1);
+        strncat(names, name, sizeof names - strlen(names) - 1);
+        ++stage;
+    };
+#define MOE_BSTEP(call, what)                                           \
+    do {                                                                \
+        if ((rc = hip_status((call), what)) != MOE_OK) return rc;       \
+        mark(what);                                                     \
+    } while (0)
+
+    moe::FwdPlan P{};
+    P.T = T; P.H = H; P.I = I; P.E = E; P.k = k; P.R = (int)R; P.quant = MOE_FP8_MX32;
+    P.x = static_cast<const uint16_t*>(x);
+    P.ids = routes->topk_ids;
+    P.tw = at<float>(ws, L.ones);
+    P.offsets = routes->expert_offsets;
+    P.perm = routes->perm;
+    P.route_pos = routes->route_pos;
+    P.out = static_cast<uint16_t*>(dx);
+    P.tiles = at<int32_t>(ws, L.tiles);
+    P.ntiles = at<int32_t>(ws, L.ntiles);
+    P.amax = at<uint32_t>(ws, L.amax);
+    P.xq = at<uint8_t>(ws, L.xq);
+    P.sx = at<float>(ws, L.sx);
+    P.y = at<uint16_t>(ws, L.y);   // (the combine reads the bf16 rows of dx there)
+    P.max_tiles = moe::grouped_max_tiles((int)R, E);
+    P.e0 = 0;
+    P.nloc = E;
+    P.acc = 0;
+    P.ev_first_start = static_cast<hipEvent_t>(events && n_events > 0 ? events[0] : nullptr);
+
+    float* gu = at<float>(ws, L.gu);
+    float* y32 = at<float>(ws, L.y);
+    float* h32 = at<float>(ws, L.h32);
+    uint8_t* hq = at<uint8_t>(ws, L.hq);
+    uint8_t* sh = at<uint8_t>(ws, L.sh);
+    uint8_t* dyq = at<uint8_t>(ws, L.dyq);
+    uint8_t* sdy = at<uint8_t>(ws, L.sdy);
+    float* dh = at<float>(ws, L.dh);
+    float* dgu = at<float>(ws, L.dgu);
+    uint8_t* dguq = at<uint8_t>(ws, L.dguq);
+    uint8_t* sdgu = at<uint8_t>(ws, L.sdgu);
+    const uint16_t* dout16 = static_cast<const uint16_t*>(dout);
+
+    if (R > 0) {
+        P.ev_stage_end = ev();
+        MOE_BSTEP(moe::launch_forward_init(P, true, st), "init");
+        P.ev_first_start = nullptr;
+        P.ev_stage_end = ev();
+        MOE_BSTEP(moe::launch_quant_x(P, st), "quant_x");
+        auto product = [&](const uint8_t* A, const uint8_t* sa, long a_rows, int K, int N, const void* B,
+                           const uint8_t* swx, bool gather, void* C, bool f32) {
+            moe::MxProduct q{};
+            q.A = A; q.sa = sa; q.a_rows = a_rows; q.K = K; q.N = N;
+            q.B = static_cast<const uint8_t*>(B); q.swx = swx; q.gather = gather;
+            q.perm = routes->perm; q.k = k; q.tiles = P.tiles; q.ntiles = P.ntiles; q.offsets = P.offsets;
+            q.max_tiles = P.max_tiles; q.C = C; q.out_f32 = f32; q.R = R; q.ev_end = ev();
+            return moe::launch_grouped_mx_y(q, st);
+        };
+        // forward recomputation: [g | u] = x W_gate_up, h, y = h W_down
+        MOE_BSTEP(product(P.xq, reinterpret_cast<const uint8_t*>(P.sx), T, H, 2 * I, w->gate_up_k,
+                          w->gate_up_k_scales, true, gu, true),
+                  "gate_up");
+        MOE_BSTEP(moe::launch_swiglu_fwd(gu, R, I, h32, hq, sh, ev(), st), "swiglu");
+        MOE_BSTEP(product(hq, sh, R, I, H, w->down_k, w->down_k_scales, false, y32, true), "down");
+        // dy = gate * dout, the gates' gradient, dh = dy W_down^T
+        MOE_BSTEP(moe::launch_dy(dout16, routes->topk_weights, routes->perm, k, y32, R, H, dyq, sdy, dgate, ev(), st),
+                  "dy");
+        MOE_BSTEP(product(dyq, sdy, R, H, I, w->down_t, w->down_t_scales, false, dh, true), "dh");
+        MOE_BSTEP(moe::launch_swiglu_bwd(gu, dh, R, I, dgu, dguq, sdgu, ev(), st), "swiglu_bwd");
+        // dx rows = dGU W_gate_up^T (into y's space), summed per token with unit weights
+        MOE_BSTEP(product(dguq, sdgu, R, 2 * I, H, w->gate_up_t, w->gate_up_t_scales, false, P.y, false), "dx_rows");
+        if ((rc = hip_status(moe::launch_fill_f32(at<float>(ws, L.ones), R, 1.0f, st), "fill")) != MOE_OK) return rc;
+        P.ev_stage_end = ev();
+        MOE_BSTEP(moe::launch_combine(P, st), "combine");
+    }
+    // weight gradients: each expert's routes padded to 64 (offsets built here),
+    // the four operands cast along the routes, then the per-expert products
+    if ((rc = hip_status(moe::launch_pad_offsets(routes->expert_offsets, E, poff, st), "pad_offsets")) != MOE_OK)
+        return rc;
+    uint8_t* xT = at<uint8_t>(ws, L.xT);
+    uint8_t* sxT = at<uint8_t>(ws, L.sxT);
+    uint8_t* dguT = at<uint8_t>(ws, L.dguT);
+    uint8_t* sdguT = at<uint8_t>(ws, L.sdguT);
+    uint8_t* hT = at<uint8_t>(ws, L.hT);
+    uint8_t* shT = at<uint8_t>(ws, L.shT);
+    uint8_t* dyT = at<uint8_t>(ws, L.dyT);
+    uint8_t* sdyT = at<uint8_t>(ws, L.sdyT);
+    if (R > 0) {
+        const int32_t* offs = routes->expert_offsets;
+        const float* tw = routes->topk_weights;
+        if ((rc = hip_status(moe::launch_dim1(0, x, nullptr, nullptr, routes->perm, k, offs, poff, E, H, Rp, Rp, Rb,
+                                              xT, sxT, nullptr, st), "dim1 x")) != MOE_OK)
+            return rc;
+        if ((rc = hip_status(moe::launch_dim1(2, dgu, nullptr, nullptr, routes->perm, k, offs, poff, E, 2 * I, Rp, Rp,
+                                              Rb, dguT, sdguT, nullptr, st), "dim1 dGU")) != MOE_OK)
+            return rc;
+        if ((rc = hip_status(moe::launch_dim1(2, h32, nullptr, nullptr, routes->perm, k, offs, poff, E, I, Rp, Rp, Rb,
+                                              hT, shT, nullptr, st), "dim1 h")) != MOE_OK)
+            return rc;
+        MOE_BSTEP(moe::launch_dim1(1, nullptr, dout16, tw, routes->perm, k, offs, poff, E, H, Rp, Rp, Rb, dyT, sdyT,
+                                   ev(), st),
+                  "dim1");
+    }
+    MOE_BSTEP(moe::launch_wgrad(xT, sxT, dguT, sdguT, Rp, Rb, poff, E, H, 2 * I, dw_gate_up, ev(), st),
+              "wgrad_gate_up");
+    MOE_BSTEP(moe::launch_wgrad(hT, shT, dyT, sdyT, Rp, Rb, poff, E, I, H, dw_down, ev(), st), "wgrad_down");
+#undef MOE_BSTEP
+    if (n_stages) *n_stages = stage;
+    if (stage_names) *stage_names = names;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_mx_train_weights_size(int E, int H, int I) {
+    if (!train_shape_ok(H, I, E)) return 0;
+    return train_layout(E, H, I).total;
+}
+
+int moe_prepare_mx_train_weights(const void* w_gate_up, const void* w_down, int E, int H, int I, void* buf,
+                                 size_t buf_bytes, moe_mx_train_weights* out, void* stream) {
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    out->tag = 0;
+    if (!train_shape_ok(H, I, E))
+        return fail(MOE_ERR_UNSUPPORTED, "MX backward: H and I multiples of 256 up to 8192, 1 <= E <= %d",
+                    moe::kMaxExperts);
+    if (!w_gate_up || !w_down || !buf) return fail(MOE_ERR_INVALID_ARG, "null pointer among weights / buf");
+    if (!aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(buf))
+        return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    const TrainLayout L = train_layout(E, H, I);
+    if (buf_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "need %zu bytes, got %zu", L.total, buf_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* b = static_cast<uint8_t*>(buf);
+    uint8_t *tmp = b + L.tmp, *tmp_s = b + L.tmp_s;
+    const uint16_t* wgu = static_cast<const uint16_t*>(w_gate_up);
+    const uint16_t* wd = static_cast<const uint16_t*>(w_down);
+    // (src, K, N, along_k) -> codes and bytes [E][K][N] -> packed (N rows of K)
+    auto one = [&](const uint16_t* src, int K, int N, bool along_k, size_t dst, size_t dst_s) -> int {
+        int r = hip_status(moe::launch_mx_weights(src, E, K, N, along_k, tmp, tmp_s, st), "mx weights");
+        if (r == MOE_OK) r = hip_status(moe::launch_pack_mx(tmp, b + dst, E, K, N, I, false, st), "pack");
+        if (r == MOE_OK) r = hip_status(moe::launch_pack_mx_scales(tmp_s, b + dst_s, E, K, N, I, false, st), "pack scales");
+        return r;
+    };
+    int rc;
+    if ((rc = one(wgu, H, 2 * I, true, L.gu_k, L.gu_k_s)) != MOE_OK) return rc;     // forward Gate/Up: along H
+    if ((rc = one(wd, I, H, true, L.d_k, L.d_k_s)) != MOE_OK) return rc;            // forward Down: along I
+    if ((rc = one(wd, H, I, false, L.d_t, L.d_t_s)) != MOE_OK) return rc;           // W_down^T: along H
+    if ((rc = one(wgu, 2 * I, H, false, L.gu_t, L.gu_t_s)) != MOE_OK) return rc;    // W_gate_up^T: along 2I
+    out->gate_up_k = b + L.gu_k;
+    out->gate_up_k_scales = b + L.gu_k_s;
+    out->down_k = b + L.d_k;
+    out->down_k_scales = b + L.d_k_s;
+    out->down_t = b + L.d_t;
+    out->down_t_scales = b + L.d_t_s;
+    out->gate_up_t = b + L.gu_t;
+    out->gate_up_t_scales = b + L.gu_t_s;
+    out->E = E;
+    out->H = H;
+    out->I = I;
+    out->tag = MOE_TRAIN_TAG;
+    return ok();
+}
+
+size_t moe_backward_workspace_size(int T, int H, int I, int E, int k) {
+    if (check_train_shape(T, H, I, E, k) != MOE_OK) return 0;
+    return bwd_layout(T, H, I, E, k).total;
+}
+
+int moe_backward(const void* x, const moe_routes* routes, const moe_mx_train_weights* w, const void* dout, void* dx,
+                 float* dgate, float* dw_gate_up, float* dw_down, void* ws, size_t ws_bytes, void* stream) {
+    return backward_impl(x, routes, w, dout, dx, dgate, dw_gate_up, dw_down, ws, ws_bytes, stream, nullptr, 0,
+                         nullptr, nullptr);
+}
+
+int moe_backward_profiled(const void* x, const moe_routes* routes, const moe_mx_train_weights* w, const void* dout,
+                          void* dx, float* dgate, float* dw_gate_up, float* dw_down, void* ws, size_t ws_bytes,
+                          void* stream, void** events, int n_events, int* n_stages, const char** stage_names) {
+    return backward_impl(x, routes, w, dout, dx, dgate, dw_gate_up, dw_down, ws, ws_bytes, stream, events, n_events,
+                         n_stages, stage_names);
+}
+
+}  // extern "C"
