@@ -14,6 +14,8 @@ line carries
     is left in the L2s or the MALL), with the HBM fraction of its dominant kernel;
   * fp8: the FP8 per-tensor decode (B=1..4, H=4096 I=192 E=192) and the FP8
     128x128-blockwise prefill (T=4096, H=4096, I=512) -- skipped with --quick;
+  * backward_fp8_mx32: the MX training backward at the MX prefill shape
+    (per-stage times against their bounds);
   * cpu_baseline: the CPU oracle on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
@@ -159,6 +161,84 @@ def counter_traffic(name):
         if hashlib.sha256(f.read()).hexdigest() != rec["gemm_sha256"]:
             return None
     return round((rec["fetch_kib"] * FETCH_SCALE + rec["write_kib"] * WRITE_SCALE) * 1024.0)
+
+
+def bench_backward(torch, moe, steps, warmup, stage_steps=10):
+    """The MX training backward (moe_backward) at the MX prefill layer's shape:
+    seeded bf16 master weights, x, logits and upstream gradient; the routing and
+    the weight preparation run once, outside the timed region.  Timed: `steps`
+    calls between two HIP events on the stream; then `stage_steps` calls with
+    events on every stage for the breakdown, each stage priced against its
+    bound (the products against the fp8 MFMA peak, the weight-gradient kernels
+    -- fp32 outputs, each written once -- against HBM)."""
+    from workloads import WORKLOADS, random_activations, random_upstream, random_weights
+    wl = WORKLOADS["prefill_fp8_mx"]
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    R = T * k
+    a = random_activations(T, H, E, seed=wl.act_seed)
+    w = random_weights(E, H, I, "bf16", seed=wl.weight_seed)
+    dout = random_upstream(T, H, seed=wl.act_seed)
+    dev = torch.device("cuda:0")
+    b16 = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    x, d = b16(a["x"]), b16(dout)
+    routes = moe.route(torch.from_numpy(a["logits"]).to(dev), k)
+    wgu, wd = b16(w["w_gate_up"]), b16(w["w_down"])
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
+    tw = moe.prepare_mx_train_weights(wgu, wd)
+    p1.record()
+    torch.cuda.synchronize()
+    prep_ms = p0.elapsed_time(p1)
+    del wgu, wd
+    out = {"dx": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+           "dgate": torch.empty((T, k), dtype=torch.float32, device=dev),
+           "dw_gate_up": torch.empty((E, H, 2 * I), dtype=torch.float32, device=dev),
+           "dw_down": torch.empty((E, I, H), dtype=torch.float32, device=dev)}
+    ws = torch.empty(moe.backward_workspace_size(T, H, I, E, k), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        moe.backward(x, routes, tw, d, workspace=ws, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        moe.backward(x, routes, tw, d, workspace=ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / steps
+    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(14)] for _ in range(stage_steps)]
+    names = None
+    for evs in ev_sets:
+        _, names = moe.backward(x, routes, tw, d, workspace=ws, out=out, events=evs)
+    torch.cuda.synchronize()
+    st = stage_times(torch, ev_sets, names)
+    counts = routes.expert_counts.cpu().numpy()
+    Rp = int(np.sum((counts + 63) // 64 * 64))           # padded route positions of the weight gradients
+    flops = {"gate_up": 2.0 * R * H * 2 * I, "down": 2.0 * R * I * H, "dh": 2.0 * R * H * I,
+             "dx_rows": 2.0 * R * 2 * I * H}
+    wbytes = {"wgrad_gate_up": 4.0 * E * H * 2 * I + (H + 2 * I) * Rp * (1 + 1 / 32),
+              "wgrad_down": 4.0 * E * I * H + (I + H) * Rp * (1 + 1 / 32)}
+    stages = {}
+    for n, ms in st.items():
+        rec = dict(us=round(ms * 1e3, 2))
+        if n in flops:
+            tf = flops[n] / (ms / 1e3) / 1e12
+            rec.update(bound="mfma", achieved=round(tf, 1), unit="TFLOP/s", frac=round(tf / PEAK_FP8_TFLOPS, 4))
+        elif n in wbytes:
+            gbs = wbytes[n] / (ms / 1e3) / 1e9
+            rec.update(bound="hbm", achieved=round(gbs, 1), unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                       bytes_per_launch=int(wbytes[n]))
+        stages[n] = rec
+    dom = max(stages, key=lambda n: stages[n]["us"])
+    del out, ws, tw
+    return dict(workload="MX training backward at prefill_fp8_mx: T=4096 H=4096 I=512 E=128 top-8; bf16 master "
+                         "weights, dW in fp32",
+                tokens_per_s=round(T * steps / dt, 1), ms_per_step=round(step_ms, 4),
+                ms_per_step_wall=round(dt / steps * 1e3, 4), prepare_weights_ms=round(prep_ms, 3),
+                stages=stages, dominant=dict(stage=dom, **stages[dom]),
+                flops_per_step=18.0 * R * H * I, padded_routes=Rp)
 
 
 def roofline_gemm(wl, gate_up_ms, peak):
@@ -560,6 +640,9 @@ def profile_only(torch, moe, args):
             bench_router(torch, moe, (1, 2, 3, 4), args.decode_iters)
         elif name.startswith("crossover_"):
             bench_crossover(torch, moe, name[len("crossover_"):], range(1, 17), 30)
+        elif name == "backward_fp8_mx":
+            bw = bench_backward(torch, moe, args.steps, args.warmup)
+            log(f"{name}: {bw['ms_per_step']:.3f} ms/step, stages us { {k: v['us'] for k, v in bw['stages'].items()} }")
         elif name.startswith("prefill"):
             pf = bench_prefill(torch, moe, name, args.steps, args.warmup)
             log(f"{name}: {pf['dt'] / args.steps * 1e3:.3f} ms/step, stages us "
@@ -582,7 +665,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline line only (no fp8 extras)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="profiling runs: comma list of prefill_bf16, prefill_fp8_block, prefill_fp8_mx, decode_bf16, "
+                    help="profiling runs: comma list of prefill_bf16, prefill_fp8_block, prefill_fp8_mx, backward_fp8_mx, "
+                         "decode_bf16, "
                          "decode_fp8_tensor, router, pages_shapes, copy (a plain 1 GiB device copy, the traffic-counter "
                          "reference); prints per-stage times instead of the JSON line")
     args = ap.parse_args()
@@ -692,6 +776,9 @@ def main():
             stages_us={k: round(v * 1e3, 2) for k, v in p6["stages_ms"].items()})
         del p6
         torch.cuda.empty_cache()
+        log("MX training backward T=4096 ...")
+        line["backward_fp8_mx32"] = bench_backward(torch, moe, max(5, args.steps // 5), max(3, args.warmup // 10))
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(a, w, wl)
@@ -729,6 +816,11 @@ def recap(line):
         log(f"recap {key}: {ms * 1e3:.1f} us/layer (budget {PREFILL_BUDGET_US[key]}), {tps:.4g} tokens/s; layer "
             f"{lay['mfma_frac']:.3f} of MFMA, {lay['hbm_frac']:.3f} of HBM; Gate/Up {roof['avg_launch_us']} us = "
             f"{roof['frac']:.3f} of MFMA peak")
+    bw = line.get("backward_fp8_mx32")
+    if bw:
+        dom = bw["dominant"]
+        log(f"recap backward MX T=4096: {bw['ms_per_step'] * 1e3:.1f} us/step, {bw['tokens_per_s']:.4g} tokens/s; "
+            f"dominant {dom['stage']} {dom['us']} us = {dom.get('frac', 0):.3f} of {dom.get('bound', '?')} peak")
     cb = line.get("cpu_baseline")
     if cb:
         log(f"recap cpu oracle: {cb['value']} {cb['unit']} on {cb['cores']} threads ({cb['sample']})")

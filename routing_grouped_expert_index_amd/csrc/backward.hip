@@ -23,6 +23,7 @@
 namespace moe {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define MOE_LDS_B(p) ((__attribute__((address_space(3))) void*)(p))
 
 __device__ __forceinline__ uint8_t e4m3_byte(float v) { return (uint8_t)(f32x2_to_e4m3x2(v, 0.0f) & 0xffu); }
 
@@ -289,15 +290,25 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
 
 // C[e] (fp32 [M][N]) = sum over expert e's padded route positions p of
 // A[m][p] B[n][p], with A, B the dim1-cast operands (row stride ldo bytes,
-// scale row stride lds_ bytes).  One workgroup per 128x128 output tile; wave
-// w takes rows 64 (w / 2) and columns 64 (w % 2) of it as 2x2 blocks of the
-// scaled 32x32x64 MFMA (K step: one 64-position slice); operand fragments
-// come straight from memory, one slice ahead.  An expert without routes gets
-// zeros.
+// scale row stride lds_ bytes).  One workgroup per 128x128 output tile.  The
+// tile's 128 rows of A and of B come into LDS by buffer loads with the LDS
+// bit, one 64-position slice (16 KB) at a time: the expert's K is short and
+// the tile is bound by latency and its output stores, so what counts is how
+// many workgroups share a CU (16 KB of LDS and 124 registers a lane: four per
+// SIMD; staging two or four slices per round measured 5% and 23% slower); row
+// r's 16-byte chunk c sits at physical chunk c ^ ((r / 4) % 4).  Wave w then takes rows 64 (w / 2) and columns
+// 64 (w % 2) of the tile as 2x2 blocks of the scaled 32x32x64 MFMA, B's rows
+// as the first operand so that a lane holds 4 consecutive columns of C per
+// result group (one 16-byte store each).  An expert without routes gets
+// zeros.  (C is row-major with N a multiple of 128.)
+constexpr int kWgSlices = 1;                      // slices staged per round
+constexpr int kWgLds = kWgSlices * 2 * 128 * 64;  // 16 KB
+
 __global__ void __launch_bounds__(256)
 wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const uint8_t* __restrict__ B,
              const uint8_t* __restrict__ sB, long ldo, long lds_, const int32_t* __restrict__ poff, int E, int M,
              int N, float* __restrict__ C) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tm = M / 128, tn = N / 128;
     const long total = (long)E * tm * tn;
     long tile = blockIdx.x;
@@ -309,7 +320,6 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
     const int mt = rem / tn, nt = rem % tn;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int j = lane & 31, hh = lane >> 5;
-    const int m0 = mt * 128 + (wave >> 1) * 64, n0 = nt * 128 + (wave & 1) * 64;
     const int s0 = poff[e] / 64, s1 = poff[e + 1] / 64;
     f32x16 acc[2][2];
 #pragma unroll
@@ -318,61 +328,80 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
         for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[f][g][i] = 0.0f;
-    const uint8_t* pa[2] = {A + (long)(m0 + j) * ldo + 32 * hh, A + (long)(m0 + 32 + j) * ldo + 32 * hh};
-    const uint8_t* pb[2] = {B + (long)(n0 + j) * ldo + 32 * hh, B + (long)(n0 + 32 + j) * ldo + 32 * hh};
-    const uint8_t* qa[2] = {sA + (long)(m0 + j) * lds_ + 4 * hh, sA + (long)(m0 + 32 + j) * lds_ + 4 * hh};
-    const uint8_t* qb[2] = {sB + (long)(n0 + j) * lds_ + 4 * hh, sB + (long)(n0 + 32 + j) * lds_ + 4 * hh};
-    struct Frag {
-        u32x4 a[2][2], b[2][2];
-        uint32_t sa[2], sb[2];
+    // the tile's rows of A and B as buffer resources (128 rows each)
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(A) + (long)mt * 128 * ldo, 0, (int)(128 * ldo), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(B) + (long)nt * 128 * ldo, 0, (int)(128 * ldo), 0x00020000);
+    // this lane's DMA row (two 16-row groups per wave and slice) and the
+    // logical chunk its physical chunk holds
+    const int dr0 = 32 * wave + (lane >> 2), dr1 = dr0 + 16;
+    const uint32_t dof0 = (uint32_t)(dr0 * ldo) + 16u * (uint32_t)((lane & 3) ^ ((dr0 >> 2) & 3));
+    const uint32_t dof1 = (uint32_t)(dr1 * ldo) + 16u * (uint32_t)((lane & 3) ^ ((dr1 >> 2) & 3));
+    // fragment rows of this lane: A rows ra0 + 32f, B rows rb0 + 32g
+    const int ra0 = (wave >> 1) * 64 + j, rb0 = (wave & 1) * 64 + j;
+    const uint8_t* qa[2] = {sA + (long)(mt * 128 + ra0) * lds_ + 4 * hh, sA + (long)(mt * 128 + ra0 + 32) * lds_ + 4 * hh};
+    const uint8_t* qb[2] = {sB + (long)(nt * 128 + rb0) * lds_ + 4 * hh, sB + (long)(nt * 128 + rb0 + 32) * lds_ + 4 * hh};
+    auto frag = [&](const uint8_t* base, int r) __attribute__((always_inline)) {
+        const int sw = (r >> 2) & 3;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + r * 64 + 16 * ((2 * hh) ^ sw));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + r * 64 + 16 * ((2 * hh + 1) ^ sw));
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
-    auto load = [&](int s, Frag& F) __attribute__((always_inline)) {
-        const long o = (long)s * 64, so = (long)(s >> 2) * 8;
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            F.a[f][0] = *reinterpret_cast<const u32x4*>(pa[f] + o);
-            F.a[f][1] = *reinterpret_cast<const u32x4*>(pa[f] + o + 16);
-            F.b[f][0] = *reinterpret_cast<const u32x4*>(pb[f] + o);
-            F.b[f][1] = *reinterpret_cast<const u32x4*>(pb[f] + o + 16);
-            F.sa[f] = *reinterpret_cast<const uint32_t*>(qa[f] + so);
-            F.sb[f] = *reinterpret_cast<const uint32_t*>(qb[f] + so);
+    for (int c0 = s0; c0 < s1; c0 += kWgSlices) {
+        const int nc = min(kWgSlices, s1 - c0);
+        if (c0 > s0) __syncthreads();   // every wave is done with the previous round's slices
+        for (int u = 0; u < nc; ++u) {
+            const uint32_t so = (uint32_t)((c0 + u) * 64);
+            uint8_t* la = smem + u * 16384 + wave * 2048;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la), 16, dof0 + so, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la + 1024), 16, dof1 + so, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192), 16, dof0 + so, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192 + 1024), 16, dof1 + so, 0, 0, 0);
         }
-    };
-    auto mma = [&](int s, const Frag& F) __attribute__((always_inline)) {
-        const int sh = 8 * (s & 3);   // byte s % 4 of the scale dword: slice s's block of this lane half
+        uint32_t sa[kWgSlices][2], sb[kWgSlices][2];
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            const i32x8 av{(int)F.a[f][0][0], (int)F.a[f][0][1], (int)F.a[f][0][2], (int)F.a[f][0][3],
-                           (int)F.a[f][1][0], (int)F.a[f][1][1], (int)F.a[f][1][2], (int)F.a[f][1][3]};
+        for (int u = 0; u < kWgSlices; ++u) {
+            const int s = min(c0 + u, s1 - 1);
+            const long so = (long)(s >> 2) * 8;
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                const i32x8 bv{(int)F.b[g][0][0], (int)F.b[g][0][1], (int)F.b[g][0][2], (int)F.b[g][0][3],
-                               (int)F.b[g][1][0], (int)F.b[g][1][1], (int)F.b[g][1][2], (int)F.b[g][1][3]};
-                acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    av, bv, acc[f][g], 0, 0, 0, (int)((F.sa[f] >> sh) & 0xffu), 0, (int)((F.sb[g] >> sh) & 0xffu));
+            for (int f = 0; f < 2; ++f) {
+                sa[u][f] = *reinterpret_cast<const uint32_t*>(qa[f] + so);
+                sb[u][f] = *reinterpret_cast<const uint32_t*>(qb[f] + so);
             }
         }
-    };
-    if (s0 < s1) {
-        Frag cur, nxt;
-        load(s0, cur);
-        for (int s = s0; s < s1; ++s) {
-            if (s + 1 < s1) load(s + 1, nxt);
-            mma(s, cur);
-            cur = nxt;
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's slices have landed
+        __syncthreads();                       // ... and every wave's
+#pragma unroll
+        for (int u = 0; u < kWgSlices; ++u) {
+            if (u < nc) {
+                const int sh = 8 * ((c0 + u) & 3);   // byte (slice % 4) of the scale dword: this lane half's block
+                const uint8_t* la = smem + u * 16384;
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const i32x8 av = frag(la, ra0 + 32 * f);
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        const i32x8 bv = frag(la + 8192, rb0 + 32 * g);
+                        acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            bv, av, acc[f][g], 0, 0, 0, (int)((sb[u][g] >> sh) & 0xffu), 0,
+                            (int)((sa[u][f] >> sh) & 0xffu));
+                    }
+                }
+            }
         }
     }
-    // acc[f][g][i]: row m0 + 32f + 8(i/4) + 4hh + i%4, column n0 + 32g + j
+    // acc[f][g][4q + t]: row mt 128 + ra0 + 32f, column nt 128 + rb0 - j + 8q + 4hh + t
     float* ce = C + (long)e * M * N;
+    const int n0 = nt * 128 + (wave & 1) * 64;
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = m0 + 32 * f + 8 * (i >> 2) + 4 * hh + (i & 3);
-                ce[(long)row * N + n0 + 32 * g + j] = acc[f][g][i];
-            }
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4*>(ce + (long)(mt * 128 + ra0 + 32 * f) * N + n0 + 32 * g + 8 * q + 4 * hh) =
+                    f32x4{acc[f][g][4 * q], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2], acc[f][g][4 * q + 3]};
 }
 
 // a fill kernel (no memset node where a caller captures the sequence)
@@ -440,8 +469,9 @@ hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, cons
 hipError_t launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, long ldo, long lds_,
                         const int32_t* poff, int E, int M, int N, float* C, hipEvent_t ev_end, hipStream_t st) {
     const long total = (long)E * (M / 128) * (N / 128);
-    hipExtLaunchKernelGGL(wgrad_kernel, dim3((unsigned)total), dim3(256), 0, st, nullptr, ev_end, 0, A, sA, B, sB, ldo,
-                          lds_, poff, E, M, N, C);
+    if (128 * ldo > 0x7fffffffL) return hipErrorInvalidValue;   // 32-bit offsets within a tile's rows
+    hipExtLaunchKernelGGL(wgrad_kernel, dim3((unsigned)total), dim3(256), kWgLds, st, nullptr, ev_end, 0, A, sA, B,
+                          sB, ldo, lds_, poff, E, M, N, C);
     return hipGetLastError();
 }
 

@@ -230,6 +230,57 @@ def test_workspace_views_layout():
         assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:])), (quant, path, spans)
 
 
+def test_backward_sizes_and_shape_rules():
+    """The MX backward's buffer sizes cover what it writes; unsupported shapes give 0."""
+    E, H, I = 128, 4096, 512
+    w = moe.mx_train_weights_size(E, H, I)
+    # four packed operand sets and a staging set: 2 x (E H 2I) + 2 x (E I H) codes plus staging, and scales
+    assert w >= (2 * 2 + 2 + 2) * E * H * I
+    T, k = 4096, 8
+    R = T * k
+    ws = moe.backward_workspace_size(T, H, I, E, k)
+    # g|u, h, y and dh in fp32, dGU in fp32 and codes, the four transposed operands
+    assert ws >= R * (2 * I * 4 + I * 4 + H * 4 + I * 4 + 2 * I * 5) + (2 * H + 3 * I) * (R + 63 * E)
+    assert moe.backward_workspace_size(0, H, I, E, k) > 0          # an empty batch still writes dW = 0
+    for bad in ((T, 4096 + 64, I, E, k), (T, H, 384, E, k), (T, H, I, 4, 8), (T, 16384, I, E, k)):
+        assert moe.backward_workspace_size(*bad) == 0, bad
+    assert moe.mx_train_weights_size(E, 4096 + 64, I) == 0
+    assert moe.mx_train_weights_size(E, H, 128) == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(),
+                    reason="passes fake device addresses; only run where no GPU can be reached")
+def test_backward_host_validation_before_any_launch():
+    L = moe.lib()
+    good = ctypes.c_void_p(4096)
+    bad = ctypes.c_void_p(4096 + 8)
+    tw = moe._CTrain()
+    # preparation: unsupported shape, null pointers, misalignment, short buffer
+    assert L.moe_prepare_mx_train_weights(good, good, 4, 320, 256, good, 1 << 40, ctypes.byref(tw), None) == -2
+    assert tw.tag == 0
+    assert L.moe_prepare_mx_train_weights(None, good, 4, 256, 256, good, 1 << 40, ctypes.byref(tw), None) == -1
+    assert L.moe_prepare_mx_train_weights(bad, good, 4, 256, 256, good, 1 << 40, ctypes.byref(tw), None) == -1
+    assert L.moe_prepare_mx_train_weights(good, good, 4, 256, 256, good, 16, ctypes.byref(tw), None) == -3
+    # backward: descriptor not prepared, E mismatch, misaligned, short workspace
+    r = moe._CRoutes()
+    r.T, r.E, r.k = 8, 4, 2
+    r.topk_ids = r.topk_weights = r.expert_offsets = r.perm = r.route_pos = 4096
+    w = moe._CTrain(4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4, 256, 256, 0)
+    args = [good, ctypes.byref(r), ctypes.byref(w), good, good, good, good, good, good, 1 << 40, None]
+    assert L.moe_backward(*args) == -1 and b"moe_prepare_mx_train_weights" in L.moe_last_error()
+    w.tag = moe.TRAIN_TAG
+    w.E = 8
+    assert L.moe_backward(*args) == -1
+    w.E = 4
+    args[3] = bad
+    assert L.moe_backward(*args) == -1
+    args[3] = good
+    args[9] = 16
+    assert L.moe_backward(*args) == -3
+    w.H = 320
+    assert L.moe_backward(*args) == -2
+
+
 def test_launch_info_shape():
     li = moe.forward_launch_info(8192, 2048, 768, 128, 8)
     assert li["path"] == "grouped" and li["gate_up_split"] == 0
