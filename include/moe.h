@@ -366,7 +366,8 @@ int moe_forward_profiled(const void *x, const moe_routes *routes, const moe_pack
  * computes them.  Grouped path only; H and I multiples of 256, up to 8192.
  *
  * Weight preparation, once per weight update: from bf16 master weights
- * w_gate_up [E][H][2I] and w_down [E][I][H], four packed MX operand sets --
+ * w_gate_up [E][H][2I] and w_down [E][I][H], in one pass each, four packed
+ * MX operand sets (the moe_pack_weights layout, plain column order) --
  * W_gate_up along H and W_down along I (the recomputed forward), W_down^T
  * along H and W_gate_up^T along 2I (the input gradients) -- in buf (device,
  * moe_mx_train_weights_size bytes, caller-owned; 0 for an unsupported

@@ -29,16 +29,20 @@ __device__ __forceinline__ uint8_t e4m3_byte(float v) { return (uint8_t)(f32x2_t
 
 // ------------------------------------------------------------- weights --
 
-// bf16 master weights -> e4m3 codes and E8M0 bytes in the [E][K][N]
-// orientation the packer takes (K the reduction dimension of the product that
-// will read them), one scale per 32 consecutive k of each column n:
+// bf16 master weights -> an MX operand set in the packed layout the grouped
+// MX GEMM reads (layout.cuh, MX chunk order, plain column order), one scale
+// per 32 consecutive k of each output column n, in one pass:
 //   along_k = 1: src [E][K][N] (the groups run down the source's rows);
 //   along_k = 0: src [E][N][K] (the groups run along the source's rows: the
 //                transposed use of a weight).
-// One thread per group; threads vary n fastest.
+// One thread per (expert, 32-group, column), columns fastest.  The group's 32
+// codes are two 16-byte pieces: K values 32kb + [0, 16) and + [16, 32) are
+// lane halves 0 and 1, half q = kb % 2, of slice kb / 2 of the column's packed
+// row; its E8M0 byte goes to the packed scale dword of that row and K group.
+template <bool ALONG_K>
 __global__ void __launch_bounds__(256)
-mx_weights_kernel(const uint16_t* __restrict__ src, int E, int K, int N, int along_k, uint8_t* __restrict__ codes,
-                  uint8_t* __restrict__ bytes) {
+mx_pack_weights_kernel(const uint16_t* __restrict__ src, int E, int K, int N, uint8_t* __restrict__ packed,
+                       uint8_t* __restrict__ packed_s) {
     const long g = (long)blockIdx.x * 256 + threadIdx.x;
     const int nkb = K / 32;
     if (g >= (long)E * nkb * N) return;
@@ -46,26 +50,52 @@ mx_weights_kernel(const uint16_t* __restrict__ src, int E, int K, int N, int alo
     const int kb = (int)((g / N) % nkb);
     const long e = g / N / nkb;
     float v[32];
+    if constexpr (ALONG_K) {   // down a column: each load is 64 lanes' adjacent columns
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) v[jj] = bf16_to_f32(src[(e * K + 32 * kb + jj) * N + n]);
+    } else {                   // along a row: the group's 64 bytes as four 16-byte loads
+        const u32x4* p4 = reinterpret_cast<const u32x4*>(src + (e * N + n) * K + 32 * kb);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const u32x4 w4 = p4[t];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[8 * t + 2 * i] = __uint_as_float(w4[i] << 16);
+                v[8 * t + 2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+            }
+        }
+    }
     float a = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        const int kk = 32 * kb + j;
-        const uint16_t w = along_k ? src[(e * K + kk) * N + n] : src[(e * N + n) * K + kk];
-        v[j] = bf16_to_f32(w);
-        a = fmaxf(a, fabsf(v[j]));
-    }
+    for (int jj = 0; jj < 32; ++jj) a = fmaxf(a, fabsf(v[jj]));
     const uint32_t b = mx_byte(a);
     const float inv = mx_inv(b);
+    u32x4 lo, hi;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) codes[(e * K + 32 * kb + j) * N + n] = e4m3_byte(v[j] * inv);
-    bytes[(e * nkb + kb) * N + n] = (uint8_t)b;
+    for (int t = 0; t < 4; ++t) {
+        lo[t] = f32x4_to_e4m3x4(v[4 * t] * inv, v[4 * t + 1] * inv, v[4 * t + 2] * inv, v[4 * t + 3] * inv);
+        hi[t] = f32x4_to_e4m3x4(v[16 + 4 * t] * inv, v[16 + 4 * t + 1] * inv, v[16 + 4 * t + 2] * inv,
+                                v[16 + 4 * t + 3] * inv);
+    }
+    // packed row of column n (the inverse of down_col_of_packed)
+    const int c = n & 63;
+    const int P = (n & ~63) + 32 * ((c >> 4) & 1) + 8 * ((c >> 2) & 3) + 4 * ((c >> 5) & 1) + (c & 3);
+    const int g32 = P >> 5, j = P & 31, nsl = K / 64;
+    uint8_t* blk = packed + e * (long)N * K + (((long)g32 * nsl + (kb >> 1)) * 2 + (kb & 1)) * 1024;
+    *reinterpret_cast<u32x4*>(blk + j * 16) = lo;
+    *reinterpret_cast<u32x4*>(blk + (32 + j) * 16) = hi;
+    const long dw = (((e * (N / 32) + g32) * (K / 256) + kb / 8) * 64 + 32 * (kb & 1) + j);
+    packed_s[dw * 4 + ((kb & 7) >> 1)] = (uint8_t)b;
 }
 
-hipError_t launch_mx_weights(const uint16_t* src, int E, int K, int N, bool along_k, uint8_t* codes, uint8_t* bytes,
-                             hipStream_t st) {
+hipError_t launch_mx_pack_weights(const uint16_t* src, int E, int K, int N, bool along_k, uint8_t* packed,
+                                  uint8_t* packed_s, hipStream_t st) {
     const long groups = (long)E * (K / 32) * N;
-    hipLaunchKernelGGL(mx_weights_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, src, E, K, N,
-                       along_k ? 1 : 0, codes, bytes);
+    const dim3 grid((unsigned)((groups + 255) / 256));
+    if (along_k)
+        hipLaunchKernelGGL(mx_pack_weights_kernel<true>, grid, dim3(256), 0, st, src, E, K, N, packed, packed_s);
+    else
+        hipLaunchKernelGGL(mx_pack_weights_kernel<false>, grid, dim3(256), 0, st, src, E, K, N, packed, packed_s);
     return hipGetLastError();
 }
 

@@ -530,7 +530,7 @@ bool train_shape_ok(int H, int I, int E) {
 }
 
 struct TrainLayout {
-    size_t gu_k, gu_k_s, d_k, d_k_s, d_t, d_t_s, gu_t, gu_t_s, tmp, tmp_s, total;
+    size_t gu_k, gu_k_s, d_k, d_k_s, d_t, d_t_s, gu_t, gu_t_s, total;
 };
 
 TrainLayout train_layout(int E, int H, int I) {
@@ -550,8 +550,6 @@ TrainLayout train_layout(int E, int H, int I) {
     L.d_t_s = take(w / 32);
     L.gu_t = take(2 * w);
     L.gu_t_s = take(2 * w / 32);
-    L.tmp = take(2 * w);
-    L.tmp_s = take(2 * w / 32);
     L.total = off;
     return L;
 }
@@ -788,15 +786,11 @@ int moe_prepare_mx_train_weights(const void* w_gate_up, const void* w_down, int 
     if (buf_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "need %zu bytes, got %zu", L.total, buf_bytes);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* b = static_cast<uint8_t*>(buf);
-    uint8_t *tmp = b + L.tmp, *tmp_s = b + L.tmp_s;
     const uint16_t* wgu = static_cast<const uint16_t*>(w_gate_up);
     const uint16_t* wd = static_cast<const uint16_t*>(w_down);
-    // (src, K, N, along_k) -> codes and bytes [E][K][N] -> packed (N rows of K)
+    // (src, K, N, along_k) -> the packed set (N rows of K) and its packed scales, one pass
     auto one = [&](const uint16_t* src, int K, int N, bool along_k, size_t dst, size_t dst_s) -> int {
-        int r = hip_status(moe::launch_mx_weights(src, E, K, N, along_k, tmp, tmp_s, st), "mx weights");
-        if (r == MOE_OK) r = hip_status(moe::launch_pack_mx(tmp, b + dst, E, K, N, I, false, st), "pack");
-        if (r == MOE_OK) r = hip_status(moe::launch_pack_mx_scales(tmp_s, b + dst_s, E, K, N, I, false, st), "pack scales");
-        return r;
+        return hip_status(moe::launch_mx_pack_weights(src, E, K, N, along_k, b + dst, b + dst_s, st), "mx pack");
     };
     int rc;
     if ((rc = one(wgu, H, 2 * I, true, L.gu_k, L.gu_k_s)) != MOE_OK) return rc;     // forward Gate/Up: along H

@@ -11,7 +11,7 @@ import torch
 
 from gpu_helpers import DEV, bf16_dev, check_out, check_routing, moe, oracle, random_activations, random_weights, \
     routes_np, say
-from workloads import WORKLOADS, random_upstream
+from workloads import WORKLOADS, bf16_bits_to_f32, quantise_weight_mx32, random_upstream
 
 pytestmark = pytest.mark.gpu
 
@@ -116,3 +116,37 @@ def test_backward_prefill_shape_sampled():
     ref = oracle.backward_mx(a["x"], ref_r["topk_ids"], ref_r["topk_weights"], w["w_gate_up"], w["w_down"], dout,
                              tokens=tokens, experts=experts)
     _compare(got, ref, tokens, experts, "prefill shape")
+
+
+def _slice(tw, ptr, nbytes):
+    off = ptr - tw.buf.data_ptr()
+    return tw.buf[off:off + nbytes]
+
+
+def test_prepared_sets_match_the_forward_packing():
+    """The one-pass preparation writes the same bytes as quantising with the input
+    generator's MX rule and packing with moe_pack_weights / moe_pack_mx_scales:
+    W_down along I as the forward packs it, and W_down^T along H packed as a
+    Down matrix of K = H, N = I."""
+    E, H, I = 4, 512, 256
+    w = random_weights(E, H, I, "bf16", seed=640)
+    tw = moe.prepare_mx_train_weights(bf16_dev(w["w_gate_up"]), bf16_dev(w["w_down"]))
+    wd = bf16_bits_to_f32(w["w_down"])                                   # [E, I, H]
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    # W_down along I, as the forward's Down weights
+    cd, sd = quantise_weight_mx32(wd)
+    cg, sg = quantise_weight_mx32(bf16_bits_to_f32(w["w_gate_up"]))
+    pw = moe.pack_weights(u8(cg), u8(cd), "fp8_mx32")
+    _, psd = moe.pack_mx_scales(u8(sg), u8(sd))
+    torch.cuda.synchronize()
+    assert torch.equal(_slice(tw, tw.desc.down_k, E * I * H), pw.down.view(torch.uint8).reshape(-1))
+    assert torch.equal(_slice(tw, tw.desc.down_k_scales, E * I * H // 32), psd.reshape(-1))
+    # W_down^T along H: a Down matrix with K = H, N = I (shape (E, H'=I, I'=H) for the packers)
+    ct, st = quantise_weight_mx32(np.ascontiguousarray(wd.transpose(0, 2, 1)))   # [E, H, I] along H
+    dummy_gu = np.zeros((E, I, 2 * H), np.uint8)
+    dummy_sg = np.zeros((E, I // 32, 2 * H), np.uint8)
+    pt = moe.pack_weights(u8(dummy_gu), u8(ct), "fp8_mx32")
+    _, pst = moe.pack_mx_scales(u8(dummy_sg), u8(st))
+    torch.cuda.synchronize()
+    assert torch.equal(_slice(tw, tw.desc.down_t, E * I * H), pt.down.view(torch.uint8).reshape(-1))
+    assert torch.equal(_slice(tw, tw.desc.down_t_scales, E * I * H // 32), pst.reshape(-1))
