@@ -33,6 +33,8 @@ Functions and what they follow (page titles and sections):
                 scale kernels", Summary and stacked pull requests: the dim1
                 cast in the backward, per-group padded scale rows); exact=True
                 is the same calculus with no quantiser.
+  route_backward -- the gates' gradient taken to the logits: the softmax
+                Jacobian over the k picks (the picks are piecewise constant).
   mx_scale_byte, quantise_group_mx, quant "fp8_mx32" -- MX FP8: e4m3 codes
                 with one power-of-two (E8M0) scale per 32 values along K
                 ("[mxfp8 moe training] add per group blocked scale kernels",
@@ -89,6 +91,8 @@ def _load():
     lib.oracle_quantise_activations.argtypes = [P, i32, i32, i32, P, P]
     lib.oracle_gate_up_h.restype = i32
     lib.oracle_gate_up_h.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, i32, P, ctypes.c_long, P]
+    lib.oracle_route_backward.restype = i32
+    lib.oracle_route_backward.argtypes = [P, P, P, i32, i32, i32, P]
     lib.oracle_backward_mx.restype = i32
     lib.oracle_backward_mx.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P, i32, P, i32, P, i32,
                                        P, P, P, P]
@@ -295,3 +299,15 @@ def backward_mx(x_bf16, topk_ids, topk_weights, w_gate_up, w_down, dout_bf16, ex
     if rc != 0:
         raise ValueError("oracle_backward_mx rejected the inputs")
     return {"dx": dx, "dgate": dg, "dw_gate_up": dwg, "dw_down": dwd}
+
+
+def route_backward(topk_ids, topk_weights, dgate, E):
+    """dlogits float64 [T, E] for the gates' upstream gradient dgate [T, k]."""
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    tw = _c(topk_weights, np.float32)
+    g = _c(dgate, np.float32)
+    out = np.zeros((T, E), np.float64)
+    if _load().oracle_route_backward(_ptr(ids), _ptr(tw), _ptr(g), T, E, k, _ptr(out)) != 0:
+        raise ValueError("oracle_route_backward rejected the inputs")
+    return out

@@ -905,3 +905,30 @@ done:
     free(slot); free(exp_slot); free(xa); free(da);
     return bad ? -1 : 0;
 }
+
+/*
+ * Gradient of the routing's gates with respect to the logits, for an upstream
+ * gradient dgate [T, k] of the gates (the layer backward returns it).  The
+ * gates are the softmax over all E renormalised over the k picks, which is the
+ * softmax over the picked logits alone; the picks themselves are a piecewise
+ * constant function of the logits, so only the picked entries get a gradient:
+ * dl[t][ids[t][j]] = w_j (g_j - sum_i w_i g_i), everything else 0, with w the
+ * routing's fp32 gates (read r5 of the design notes; the pages print no formula).
+ * dlogits [T, E] in double.  Returns 0, or -1 on a bad id.
+ */
+int oracle_route_backward(const int32_t *ids, const float *weights, const float *dgate, int T, int E, int k,
+                          double *dlogits) {
+    int t, j;
+    for (t = 0; t < T; ++t) {
+        double s = 0.0;
+        double *row = dlogits + (long)t * E;
+        for (j = 0; j < E; ++j) row[j] = 0.0;
+        for (j = 0; j < k; ++j) s += (double)weights[(long)t * k + j] * (double)dgate[(long)t * k + j];
+        for (j = 0; j < k; ++j) {
+            long r = (long)t * k + j;
+            if (ids[r] < 0 || ids[r] >= E) return -1;
+            row[ids[r]] += (double)weights[r] * ((double)dgate[r] - s);
+        }
+    }
+    return 0;
+}

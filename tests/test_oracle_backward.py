@@ -160,3 +160,26 @@ def test_backward_expert_without_routes_has_zero_weight_gradient():
     g = oracle.backward_mx(a["x"], r["topk_ids"], r["topk_weights"], w["w_gate_up"], w["w_down"], dout,
                            experts=np.array(idle, np.int32))
     assert not g["dw_gate_up"].any() and not g["dw_down"].any()
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(17, 8, 2, 51), (5, 16, 16, 52), (9, 4, 1, 53)])
+def test_route_backward_matches_autograd(T, E, k, seed):
+    """The gates' gradient taken to the logits equals torch's autograd through
+    the softmax over the picked logits (ids fixed: the picks do not move under
+    an infinitesimal change of the logits)."""
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    r = oracle.route(lg, k)
+    g = rng.standard_normal((T, k)).astype(np.float32)
+    got = oracle.route_backward(r["topk_ids"], r["topk_weights"], g, E)
+    l = torch.from_numpy(lg.astype(np.float64)).requires_grad_(True)
+    ids = torch.from_numpy(r["topk_ids"].astype(np.int64))
+    w = torch.softmax(torch.gather(l, 1, ids), dim=1)
+    (w * torch.from_numpy(g.astype(np.float64))).sum().backward()
+    ref = l.grad.numpy()
+    assert np.max(np.abs(got - ref)) <= 1e-6 * max(1.0, np.max(np.abs(ref)))
+    # unpicked logits get nothing, and each row sums to zero (the softmax's invariance to a shift)
+    mask = np.zeros((T, E), bool)
+    np.put_along_axis(mask, r["topk_ids"].astype(np.int64), True, axis=1)
+    assert not got[~mask].any()
+    assert np.max(np.abs(got.sum(axis=1))) <= 1e-6
