@@ -420,6 +420,17 @@ int moe_backward_profiled(const void *x, const moe_routes *routes, const moe_mx_
                           size_t ws_bytes, void *stream, void **stage_events, int n_events, int *n_stages,
                           const char **stage_names);
 
+/* The gates' gradient taken to the router logits: dlogits fp32 [T][E] for
+ * dgate fp32 [T][k] (moe_backward's gate gradient) and the routes moe_route
+ * returned (topk_ids, topk_weights, T, E, k are read).  The gates are the
+ * softmax over the k picked logits ("perf: add small-batch route MMA for
+ * MoE", Summary: routes are token/top-k; the renormalised softmax of the
+ * routing) and the picks are piecewise constant, so every entry is zero
+ * except dlogits[t][ids[t][j]] = w_j (g_j - sum_i w_i g_i).  Device pointers,
+ * 16-byte aligned, caller-owned; host validation before any launch; T = 0
+ * launches nothing.  No synchronisation. */
+int moe_route_backward(const moe_routes *routes, const float *dgate, float *dlogits, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *moe_last_error(void);
 

@@ -34,7 +34,7 @@ EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_route_project_workspac
             "moe_forward", "moe_forward_ex", "moe_decode_forward", "moe_decode_forward_noalloc",
             "moe_forward_profiled", "moe_forward_timed",
             "moe_mx_train_weights_size", "moe_prepare_mx_train_weights", "moe_backward_workspace_size",
-            "moe_backward", "moe_backward_profiled",
+            "moe_backward", "moe_backward_profiled", "moe_route_backward",
             "moe_last_error"]
 PACKED_TAG = 0x4D6F4557
 TRAIN_TAG = 0x4D6F4542
@@ -146,6 +146,7 @@ def lib():
     L.moe_backward_profiled.argtypes = L.moe_backward.argtypes + [ctypes.POINTER(ctypes.c_void_p), i32,
                                                                   ctypes.POINTER(ctypes.c_int),
                                                                   ctypes.POINTER(ctypes.c_char_p)]
+    L.moe_route_backward.argtypes = [ctypes.POINTER(_CRoutes), P, P, P]
     L.moe_last_error.argtypes = []
     _lib = L
     return L
@@ -536,3 +537,16 @@ def backward(x: torch.Tensor, routes: Routes, weights: TrainWeights, dout: torch
     names = ctypes.c_char_p()
     _check(lib().moe_backward_profiled(*args, handles, len(events), ctypes.byref(n), ctypes.byref(names)))
     return out, names.value.decode().split(",")[: n.value]
+
+
+def route_backward(routes: Routes, dgate: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """The gates' gradient dgate fp32 [T, k] taken to the router logits: fp32 [T, E]
+    (moe_route_backward)."""
+    _need_cuda(dgate, "dgate")
+    if dgate.dtype != torch.float32 or tuple(dgate.shape) != (routes.T, routes.k):
+        raise ValueError("dgate must be float32 [T, k]")
+    if out is None:
+        out = torch.empty((routes.T, routes.E), dtype=torch.float32, device=dgate.device)
+    cs = routes.c_struct()
+    _check(lib().moe_route_backward(ctypes.byref(cs), _ptr(dgate), _ptr(out), _stream(dgate.device, stream)))
+    return out

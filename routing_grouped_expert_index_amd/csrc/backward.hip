@@ -434,6 +434,33 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
                     f32x4{acc[f][g][4 * q], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2], acc[f][g][4 * q + 3]};
 }
 
+// The gates' gradient taken to the router logits: the gates are the softmax
+// over the k picked logits (the softmax over all E renormalised over the
+// picks), and the picks are piecewise constant, so row t of dlogits is zero
+// except dl[ids[t][j]] = w_j (g_j - sum_i w_i g_i) (the sum in ascending j).
+// One workgroup per token; the picks of a token are distinct experts.
+__global__ void __launch_bounds__(256)
+route_grad_kernel(const int32_t* __restrict__ ids, const float* __restrict__ tw, const float* __restrict__ dgate,
+                  int E, int k, float* __restrict__ dlogits) {
+    const long t = blockIdx.x;
+    float* row = dlogits + t * E;
+    for (int c = threadIdx.x; c < E; c += 256) row[c] = 0.0f;
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) s = fmaf(tw[t * k + j], dgate[t * k + j], s);
+    __syncthreads();   // (the zeros are written before the picks overwrite theirs)
+    for (int j = threadIdx.x; j < k; j += 256) {
+        const long r = t * k + j;
+        row[ids[r]] = tw[r] * (dgate[r] - s);
+    }
+}
+
+hipError_t launch_route_grad(const int32_t* ids, const float* tw, const float* dgate, int T, int E, int k,
+                             float* dlogits, hipStream_t st) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(route_grad_kernel, dim3((unsigned)T), dim3(256), 0, st, ids, tw, dgate, E, k, dlogits);
+    return hipGetLastError();
+}
+
 // a fill kernel (no memset node where a caller captures the sequence)
 __global__ void __launch_bounds__(256) fill_f32_kernel(float* __restrict__ p, long n, float v) {
     for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = v;

@@ -145,6 +145,8 @@ hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, cons
 hipError_t launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, long ldo, long lds_,
                         const int32_t* poff, int E, int M, int N, float* C, hipEvent_t ev_end, hipStream_t st);
 hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t st);
+hipError_t launch_route_grad(const int32_t* ids, const float* tw, const float* dgate, int T, int E, int k,
+                             float* dlogits, hipStream_t st);
 
 hipError_t launch_forward_init(const FwdPlan& p, bool build_tiles, hipStream_t st);
 hipError_t launch_quant_x(const FwdPlan& p, hipStream_t st);

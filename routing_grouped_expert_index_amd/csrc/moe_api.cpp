@@ -823,6 +823,25 @@ int moe_backward(const void* x, const moe_routes* routes, const moe_mx_train_wei
                          nullptr, nullptr);
 }
 
+int moe_route_backward(const moe_routes* routes, const float* dgate, float* dlogits, void* stream) {
+    if (!routes) return fail(MOE_ERR_INVALID_ARG, "routes is NULL");
+    const int T = routes->T, E = routes->E, k = routes->k;
+    if (T < 0 || k < 1 || E < k || E > moe::kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "need T >= 0 and 1 <= k <= E <= %d (T=%d k=%d E=%d)", moe::kMaxExperts, T, k,
+                    E);
+    if ((long)T * E >= (1L << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*E must fit in int32");
+    if (T == 0) return ok();
+    if (!dgate || !dlogits || !routes->topk_ids || !routes->topk_weights)
+        return fail(MOE_ERR_INVALID_ARG, "null pointer among dgate / dlogits / routes");
+    const void* ptrs[] = {dgate, dlogits, routes->topk_ids, routes->topk_weights};
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    const int rc = hip_status(moe::launch_route_grad(routes->topk_ids, routes->topk_weights, dgate, T, E, k, dlogits,
+                                                     static_cast<hipStream_t>(stream)),
+                              "moe_route_backward launch");
+    return rc == MOE_OK ? ok() : rc;
+}
+
 int moe_backward_profiled(const void* x, const moe_routes* routes, const moe_mx_train_weights* w, const void* dout,
                           void* dx, float* dgate, float* dw_gate_up, float* dw_down, void* ws, size_t ws_bytes,
                           void* stream, void** events, int n_events, int* n_stages, const char** stage_names) {

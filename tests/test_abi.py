@@ -279,6 +279,17 @@ def test_backward_host_validation_before_any_launch():
     assert L.moe_backward(*args) == -3
     w.H = 320
     assert L.moe_backward(*args) == -2
+    # the route backward: null routes, k > E, an empty batch, misalignment
+    assert L.moe_route_backward(None, good, good, None) == -1
+    r2 = moe._CRoutes()
+    r2.T, r2.E, r2.k = 4, 4, 8
+    assert L.moe_route_backward(ctypes.byref(r2), good, good, None) == -1
+    r2.T, r2.E, r2.k = 0, 8, 2
+    assert L.moe_route_backward(ctypes.byref(r2), None, None, None) == 0
+    r2.T = 4
+    r2.topk_ids = r2.topk_weights = 4096
+    assert L.moe_route_backward(ctypes.byref(r2), bad, good, None) == -1
+    assert L.moe_route_backward(ctypes.byref(r2), good, None, None) == -1
 
 
 def test_launch_info_shape():

@@ -150,3 +150,81 @@ def test_prepared_sets_match_the_forward_packing():
     torch.cuda.synchronize()
     assert torch.equal(_slice(tw, tw.desc.down_t, E * I * H), pt.down.view(torch.uint8).reshape(-1))
     assert torch.equal(_slice(tw, tw.desc.down_t_scales, E * I * H // 32), pst.reshape(-1))
+
+
+@pytest.mark.parametrize("T,E,k", [(37, 16, 4), (5, 512, 8), (64, 8, 8)])
+def test_route_backward_parity(T, E, k):
+    """moe_route_backward against the oracle's softmax Jacobian, on a seeded
+    upstream gradient of the gates and the oracle's own routing."""
+    rng = np.random.default_rng(650 + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    g = rng.standard_normal((T, k)).astype(np.float32)
+    r = moe.route(torch.from_numpy(lg).to(DEV), k)
+    dl = moe.route_backward(r, torch.from_numpy(g).to(DEV))
+    torch.cuda.synchronize()
+    ref_r = oracle.route(lg, k)
+    check_routing(routes_np(r), ref_r)
+    ref = oracle.route_backward(ref_r["topk_ids"], ref_r["topk_weights"], g, E)
+    got = dl.cpu().numpy()
+    assert np.max(np.abs(got - ref)) <= 2e-6 * max(1.0, np.max(np.abs(ref)))
+    mask = np.zeros((T, E), bool)
+    np.put_along_axis(mask, ref_r["topk_ids"].astype(np.int64), True, axis=1)
+    assert not got[~mask].any()
+
+
+def test_backward_to_the_logits():
+    """The layer's gate gradient taken to the logits, on the GPU end to end,
+    against the oracle's chain (its own gate gradient, then its Jacobian)."""
+    T, H, I, E, k = 96, 256, 256, 8, 2
+    a = random_activations(T, H, E, seed=660)
+    w = random_weights(E, H, I, "bf16", seed=661)
+    dout = random_upstream(T, H, 662)
+    r = moe.route(torch.from_numpy(a["logits"]).to(DEV), k)
+    tw = moe.prepare_mx_train_weights(bf16_dev(w["w_gate_up"]), bf16_dev(w["w_down"]))
+    g = moe.backward(bf16_dev(a["x"]), r, tw, bf16_dev(dout))
+    dl = moe.route_backward(r, g["dgate"])
+    torch.cuda.synchronize()
+    ref_r = oracle.route(a["logits"], k)
+    ref = oracle.backward_mx(a["x"], ref_r["topk_ids"], ref_r["topk_weights"], w["w_gate_up"], w["w_down"], dout)
+    ref_dl = oracle.route_backward(ref_r["topk_ids"], ref_r["topk_weights"], ref["dgate"].astype(np.float32), E)
+    check_out(dl.cpu().numpy(), ref_dl, "fp8", "dlogits")
+
+
+def test_backward_graph_replay_bitwise_equal():
+    """moe_backward captured in a HIP graph (it records no memset node) and replayed
+    three times, with eager work between the replays: every replay equals the eager
+    call bit for bit."""
+    T, H, I, E, k = 128, 256, 256, 8, 4
+    a = random_activations(T, H, E, seed=670)
+    w = random_weights(E, H, I, "bf16", seed=671)
+    dout = random_upstream(T, H, 672)
+    r = moe.route(torch.from_numpy(a["logits"]).to(DEV), k)
+    tw = moe.prepare_mx_train_weights(bf16_dev(w["w_gate_up"]), bf16_dev(w["w_down"]))
+    x, d = bf16_dev(a["x"]), bf16_dev(dout)
+    ws = torch.empty(moe.backward_workspace_size(T, H, I, E, k), dtype=torch.uint8, device=DEV)
+    out = {"dx": torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+           "dgate": torch.empty((T, k), dtype=torch.float32, device=DEV),
+           "dw_gate_up": torch.empty((E, H, 2 * I), dtype=torch.float32, device=DEV),
+           "dw_down": torch.empty((E, I, H), dtype=torch.float32, device=DEV)}
+    moe.backward(x, r, tw, d, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    eager = {n: v.clone() for n, v in out.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.backward(x, r, tw, d, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.backward(x, r, tw, d, workspace=ws, out=out)
+    for i in range(3):
+        for v in out.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in out:
+            assert torch.equal(out[n], eager[n]), (i, n)
+        moe.backward(x, r, tw, d, workspace=ws, out={n: torch.empty_like(v) for n, v in out.items()})
+        torch.cuda.synchronize()
