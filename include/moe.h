@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, k > E, negative sizes, ... */
-    MOE_ERR_UNSUPPORTED = -2,   /* shape or quantisation this build does not handle */
+    MOE_ERR_UNSUPPORTED = -2,   /* shape or quantisation the library does not handle */
     MOE_ERR_WORKSPACE = -3,     /* workspace smaller than the *_workspace_size query */
     MOE_ERR_HIP = -4            /* a kernel launch failed */
 } moe_status;

@@ -22,8 +22,7 @@
  * derived separately in oracle_route), in IEEE double, with the method's
  * quantisation decisions taken in fp32 as the method takes them.
  *
- * Readings taken where the pages are silent (each is also listed in the design
- * notes of the repository):
+ * Readings taken where the pages are silent:
  *  - top-k selects on the fp32 logits, descending, exact fp32 equality (so -0
  *    equals +0) broken to the lower expert id; slot j is the j-th pick;
  *  - gates are the softmax over all E experts renormalised over the k picks;
@@ -913,7 +912,7 @@ done:
  * softmax over the picked logits alone; the picks themselves are a piecewise
  * constant function of the logits, so only the picked entries get a gradient:
  * dl[t][ids[t][j]] = w_j (g_j - sum_i w_i g_i), everything else 0, with w the
- * routing's fp32 gates (read r5 of the design notes; the pages print no formula).
+ * routing's fp32 gates (the pages print no formula for this gradient).
  * dlogits [T, E] in double.  Returns 0, or -1 on a bad id.
  */
 int oracle_route_backward(const int32_t *ids, const float *weights, const float *dgate, int T, int E, int k,
