@@ -140,9 +140,17 @@ gemm32_kernel(const GemmArgs g) {
                                                  (int)(uint32_t)(left < 0xffffffffL ? left : 0xffffffffL),
                                                  0x00020000);
     };
-    auto make_ap = [&](int src, int row0_) __attribute__((always_inline)) {
+    // A padding row (past the tile's valid rows) takes offset 0xfff00000 plus its
+    // slice: past the end of the A resource whenever A is smaller than that
+    // (every shape the layer runs at), so the range check turns its loads into
+    // zeros and no A bytes are fetched for it; otherwise the offset still lies
+    // inside the resource's range and reads valid bytes.  Its MFMAs' results
+    // are dropped either way.  (Against re-reading a valid row: the bf16
+    // Gate/Up 0-1.5% faster over two sets of interleaved runs, FP8 unchanged.)
+    auto make_ap = [&](int src, int row0_, int rows_) __attribute__((always_inline)) {
         const long rel = GATHER ? src : src - row0_;
-        return (uint32_t)(rel * g.lda) + (uint32_t)(((lane & 3) ^ ((dma_r >> 2) & 3)) * 16);
+        return (dma_r >= rows_ ? 0xFFF00000u : (uint32_t)(rel * g.lda)) +
+               (uint32_t)(((lane & 3) ^ ((dma_r >> 2) & 3)) * 16);
     };
     // idle waves (past N) load a valid block, so every wave issues the same loads
     // Epilogue stores are buffer stores through a resource covering C: the
@@ -243,7 +251,7 @@ gemm32_kernel(const GemmArgs g) {
     decode(L, e, row0, rows, wn0);
     const int src0 = src_row(row0, rows);
     __amdgpu_buffer_rsrc_t arsrc = make_arsrc(row0);
-    uint32_t ap = make_ap(src0, row0);
+    uint32_t ap = make_ap(src0, row0, rows);
     const uint8_t* wp = make_wp(e, wn0);
     const uint32_t* wsp = MX ? make_wsp(e, wn0) : nullptr;
     table(src0);
@@ -532,7 +540,7 @@ gemm32_kernel(const GemmArgs g) {
         // (after the last tile the requests repeat this tile's valid data: an
         // unconditional prologue keeps the loop's wait counts exact)
         if (!GATHER && more) arsrc = make_arsrc(nrow0);   // (the DMAs of this tile are all issued)
-        const uint32_t nap = more ? make_ap(nsrc, nrow0) : ap;
+        const uint32_t nap = more ? make_ap(nsrc, nrow0, nrows) : ap;
         const uint8_t* nwp = more ? make_wp(ne, nwn0) : wp;
         const uint32_t* nwsp = MX && more ? make_wsp(ne, nwn0) : wsp;
         prologue(nap, nwp, nwsp);
