@@ -237,16 +237,38 @@ swiglu_bwd_kernel(const float* __restrict__ gu, const float* __restrict__ dh, lo
 
 // poff[e] = sum over e' < e of the expert's route count rounded up to 64 (the
 // weight-gradient product's K step), poff[E] the padded total: the per-group
-// padded start offsets, built on the device from the routing's offsets.
-__global__ void __launch_bounds__(64)
-pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restrict__ poff) {
-    if (threadIdx.x != 0) return;
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-        poff[e] = acc;
-        acc += (offsets[e + 1] - offsets[e] + 63) & ~63;
+// padded start offsets, built on the device from the routing's offsets; and
+// seg[s] = the expert whose padded segment holds 64-position slice s (for
+// every s below nseg; slices past poff[E] get E).
+__global__ void __launch_bounds__(256)
+pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restrict__ poff, int32_t* __restrict__ seg,
+                   int nseg) {
+    __shared__ int sp[kMaxExperts + 1];
+    if (threadIdx.x == 0) {
+        int acc = 0;
+        for (int e = 0; e < E; ++e) {
+            sp[e] = acc;
+            poff[e] = acc;
+            acc += (offsets[e + 1] - offsets[e] + 63) & ~63;
+        }
+        sp[E] = acc;
+        poff[E] = acc;
     }
-    poff[E] = acc;
+    __syncthreads();
+    for (int s = threadIdx.x; s < nseg; s += 256) {
+        const int p = 64 * s;
+        int lo = 0, hi = E;                    // sp[lo] <= p < sp[hi]
+        if (p >= sp[E]) {
+            lo = E;
+        } else {
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (sp[mid] <= p) lo = mid;
+                else hi = mid;
+            }
+        }
+        seg[s] = lo;
+    }
 }
 
 // The "dim1" cast: an operand v[i][m] over sorted routes i (M columns),
@@ -263,20 +285,13 @@ template <int SRC>
 __global__ void __launch_bounds__(256)
 dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, const float* __restrict__ tw,
             const int32_t* __restrict__ perm, int k, const int32_t* __restrict__ offsets,
-            const int32_t* __restrict__ poff, int E, int M, long ldo, long lds_, uint8_t* __restrict__ out,
-            uint8_t* __restrict__ sout) {
+            const int32_t* __restrict__ poff, const int32_t* __restrict__ seg, int E, int M, long ldo, long lds_,
+            uint8_t* __restrict__ out, uint8_t* __restrict__ sout) {
     const int gi = blockIdx.x;                     // block of 32 padded positions
     const int m = blockIdx.y * 256 + threadIdx.x;
     const int p0 = gi * 32;
-    if (p0 >= poff[E]) return;
-    // the expert whose padded segment holds p0
-    int lo = 0, hi = E;                            // poff[lo] <= p0 < poff[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (poff[mid] <= p0) lo = mid;
-        else hi = mid;
-    }
-    const int e = lo;
+    const int e = seg[gi >> 1];                    // the expert whose padded segment holds p0
+    if (e >= E) return;                            // past the padded total
     const int first = offsets[e] + (p0 - poff[e]);       // sorted row of position p0
     const int cnt = min(32, offsets[e + 1] - first);     // real routes in this block (may be <= 0)
     if (m >= M) return;
@@ -503,25 +518,25 @@ hipError_t launch_swiglu_bwd(const float* gu, const float* dh, long R, int I, fl
     return hipGetLastError();
 }
 
-hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st) {
-    hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, st, offsets, E, poff);
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, int32_t* seg, int nseg, hipStream_t st) {
+    hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, st, offsets, E, poff, seg, nseg);
     return hipGetLastError();
 }
 
 hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, const float* tw, const int32_t* perm,
-                       int k, const int32_t* offsets, const int32_t* poff, int E, int M, long Rp, long ldo, long lds_,
-                       uint8_t* out, uint8_t* sout, hipEvent_t ev_end, hipStream_t st) {
+                       int k, const int32_t* offsets, const int32_t* poff, const int32_t* seg, int E, int M, long Rp,
+                       long ldo, long lds_, uint8_t* out, uint8_t* sout, hipEvent_t ev_end, hipStream_t st) {
     const dim3 grid((unsigned)(Rp / 32), (unsigned)((M + 255) / 256));
     if (Rp == 0) return hipSuccess;
     if (src_kind == D1_X)
         hipExtLaunchKernelGGL(dim1_kernel<D1_X>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm, k,
-                              offsets, poff, E, M, ldo, lds_, out, sout);
+                              offsets, poff, seg, E, M, ldo, lds_, out, sout);
     else if (src_kind == D1_DY)
         hipExtLaunchKernelGGL(dim1_kernel<D1_DY>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm, k,
-                              offsets, poff, E, M, ldo, lds_, out, sout);
+                              offsets, poff, seg, E, M, ldo, lds_, out, sout);
     else
         hipExtLaunchKernelGGL(dim1_kernel<D1_F32>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm,
-                              k, offsets, poff, E, M, ldo, lds_, out, sout);
+                              k, offsets, poff, seg, E, M, ldo, lds_, out, sout);
     return hipGetLastError();
 }
 

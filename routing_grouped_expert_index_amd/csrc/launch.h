@@ -136,12 +136,12 @@ hipError_t launch_dy(const uint16_t* dout, const float* tw, const int32_t* perm,
                      int H, uint8_t* dyq, uint8_t* sdy, float* dgate, hipEvent_t ev_end, hipStream_t st);
 hipError_t launch_swiglu_bwd(const float* gu, const float* dh, long R, int I, float* dgu, uint8_t* dguq,
                              uint8_t* sdgu, hipEvent_t ev_end, hipStream_t st);
-hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, int32_t* seg, int nseg, hipStream_t st);
 // src_kind 0: x bf16 [T][M] through perm; 1: gate * dout (dout bf16 [T][M]);
 // 2: fp32 [R][M] in sorted order
 hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, const float* tw, const int32_t* perm,
-                       int k, const int32_t* offsets, const int32_t* poff, int E, int M, long Rp, long ldo, long lds_,
-                       uint8_t* out, uint8_t* sout, hipEvent_t ev_end, hipStream_t st);
+                       int k, const int32_t* offsets, const int32_t* poff, const int32_t* seg, int E, int M, long Rp,
+                       long ldo, long lds_, uint8_t* out, uint8_t* sout, hipEvent_t ev_end, hipStream_t st);
 hipError_t launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, long ldo, long lds_,
                         const int32_t* poff, int E, int M, int N, float* C, hipEvent_t ev_end, hipStream_t st);
 hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t st);

@@ -555,7 +555,7 @@ TrainLayout train_layout(int E, int H, int I) {
 }
 
 struct BwdLayout {
-    size_t tiles, ntiles, amax, xq, sx, gu, h32, hq, sh, y, dyq, sdy, dh, dgu, dguq, sdgu, ones, poff;
+    size_t tiles, ntiles, amax, xq, sx, gu, h32, hq, sh, y, dyq, sdy, dh, dgu, dguq, sdgu, ones, poff, seg;
     size_t xT, sxT, dguT, sdguT, hT, shT, dyT, sdyT, total;
     long Rp;
 };
@@ -593,6 +593,7 @@ BwdLayout bwd_layout(int T, int H, int I, int E, int k) {
     L.sdgu = take(R * (2 * I / 32));
     L.ones = take(R * 4);
     L.poff = take(sizeof(int32_t) * (size_t)(E + 1));
+    L.seg = take(sizeof(int32_t) * (size_t)(L.Rp / 64));
     L.xT = take((size_t)H * Rp);
     L.sxT = take((size_t)H * Rb);
     L.dguT = take((size_t)2 * I * Rp);
@@ -642,6 +643,7 @@ int backward_impl(const void* x, const moe_routes* routes, const moe_mx_train_we
     hipStream_t st = static_cast<hipStream_t>(stream);
     const long R = (long)T * k, Rp = L.Rp, Rb = Rp / 32;
     int32_t* poff = at<int32_t>(ws, L.poff);
+    int32_t* seg = at<int32_t>(ws, L.seg);
 
     int stage = 0;
     static thread_local char names[256];
@@ -728,7 +730,7 @@ int backward_impl(const void* x, const moe_routes* routes, const moe_mx_train_we
     }
     // weight gradients: each expert's routes padded to 64 (offsets built here),
     // the four operands cast along the routes, then the per-expert products
-    if ((rc = hip_status(moe::launch_pad_offsets(routes->expert_offsets, E, poff, st), "pad_offsets")) != MOE_OK)
+    if ((rc = hip_status(moe::launch_pad_offsets(routes->expert_offsets, E, poff, seg, (int)(Rp / 64), st), "pad_offsets")) != MOE_OK)
         return rc;
     uint8_t* xT = at<uint8_t>(ws, L.xT);
     uint8_t* sxT = at<uint8_t>(ws, L.sxT);
@@ -741,16 +743,16 @@ int backward_impl(const void* x, const moe_routes* routes, const moe_mx_train_we
     if (R > 0) {
         const int32_t* offs = routes->expert_offsets;
         const float* tw = routes->topk_weights;
-        if ((rc = hip_status(moe::launch_dim1(0, x, nullptr, nullptr, routes->perm, k, offs, poff, E, H, Rp, Rp, Rb,
+        if ((rc = hip_status(moe::launch_dim1(0, x, nullptr, nullptr, routes->perm, k, offs, poff, seg, E, H, Rp, Rp, Rb,
                                               xT, sxT, nullptr, st), "dim1 x")) != MOE_OK)
             return rc;
-        if ((rc = hip_status(moe::launch_dim1(2, dgu, nullptr, nullptr, routes->perm, k, offs, poff, E, 2 * I, Rp, Rp,
+        if ((rc = hip_status(moe::launch_dim1(2, dgu, nullptr, nullptr, routes->perm, k, offs, poff, seg, E, 2 * I, Rp, Rp,
                                               Rb, dguT, sdguT, nullptr, st), "dim1 dGU")) != MOE_OK)
             return rc;
-        if ((rc = hip_status(moe::launch_dim1(2, h32, nullptr, nullptr, routes->perm, k, offs, poff, E, I, Rp, Rp, Rb,
+        if ((rc = hip_status(moe::launch_dim1(2, h32, nullptr, nullptr, routes->perm, k, offs, poff, seg, E, I, Rp, Rp, Rb,
                                               hT, shT, nullptr, st), "dim1 h")) != MOE_OK)
             return rc;
-        MOE_BSTEP(moe::launch_dim1(1, nullptr, dout16, tw, routes->perm, k, offs, poff, E, H, Rp, Rp, Rb, dyT, sdyT,
+        MOE_BSTEP(moe::launch_dim1(1, nullptr, dout16, tw, routes->perm, k, offs, poff, seg, E, H, Rp, Rp, Rb, dyT, sdyT,
                                    ev(), st),
                   "dim1");
     }
