@@ -284,9 +284,12 @@ enum Dim1Src { D1_X = 0, D1_DY = 1, D1_F32 = 2 };
 template <int SRC>
 __global__ void __launch_bounds__(256)
 dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, const float* __restrict__ tw,
-            const int32_t* __restrict__ perm, int k, const int32_t* __restrict__ offsets,
+            const int32_t* __restrict__ perm, uint32_t kdiv_m, int kdiv_s, const int32_t* __restrict__ offsets,
             const int32_t* __restrict__ poff, const int32_t* __restrict__ seg, int E, int M, long ldo, long lds_,
             uint8_t* __restrict__ out, uint8_t* __restrict__ sout) {
+    // (a route's token r / k as a multiply-shift: a divide per route would be a
+    // long scalar sequence, 32 of them per thread)
+    auto tok = [&](int r) { return (long)(((uint64_t)(uint32_t)r * kdiv_m) >> kdiv_s); };
     const int gi = blockIdx.x;                     // block of 32 padded positions
     const int m = blockIdx.y * 256 + threadIdx.x;
     const int p0 = gi * 32;
@@ -303,10 +306,10 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
         if (j < cnt) {
             const long i = first + j;
             if (SRC == D1_X) {
-                x = bf16_to_f32(static_cast<const uint16_t*>(src)[(long)(perm[i] / k) * M + m]);
+                x = bf16_to_f32(static_cast<const uint16_t*>(src)[tok(perm[i]) * M + m]);
             } else if (SRC == D1_DY) {
                 const int r = perm[i];
-                x = tw[r] * bf16_to_f32(dout[(long)(r / k) * M + m]);
+                x = tw[r] * bf16_to_f32(dout[tok(r) * M + m]);
             } else {
                 x = static_cast<const float*>(src)[i * M + m];
             }
@@ -528,15 +531,21 @@ hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, cons
                        long ldo, long lds_, uint8_t* out, uint8_t* sout, hipEvent_t ev_end, hipStream_t st) {
     const dim3 grid((unsigned)(Rp / 32), (unsigned)((M + 255) / 256));
     if (Rp == 0) return hipSuccess;
+    // r / k == (r * m) >> s for every r < 2^31 and 1 <= k <= 2^10, with
+    // s = 31 + ceil(log2 k) and m = ceil(2^s / k) < 2^32
+    int l = 0;
+    while ((1 << l) < k) ++l;
+    const int kdiv_s = 31 + l;
+    const uint32_t kdiv_m = (uint32_t)(((1ULL << kdiv_s) + (uint64_t)k - 1) / (uint64_t)k);
     if (src_kind == D1_X)
-        hipExtLaunchKernelGGL(dim1_kernel<D1_X>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm, k,
+        hipExtLaunchKernelGGL(dim1_kernel<D1_X>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm, kdiv_m, kdiv_s,
                               offsets, poff, seg, E, M, ldo, lds_, out, sout);
     else if (src_kind == D1_DY)
-        hipExtLaunchKernelGGL(dim1_kernel<D1_DY>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm, k,
+        hipExtLaunchKernelGGL(dim1_kernel<D1_DY>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm, kdiv_m, kdiv_s,
                               offsets, poff, seg, E, M, ldo, lds_, out, sout);
     else
         hipExtLaunchKernelGGL(dim1_kernel<D1_F32>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm,
-                              k, offsets, poff, seg, E, M, ldo, lds_, out, sout);
+                              kdiv_m, kdiv_s, offsets, poff, seg, E, M, ldo, lds_, out, sout);
     return hipGetLastError();
 }
 
