@@ -371,8 +371,10 @@ int moe_forward_profiled(const void *x, const moe_routes *routes, const moe_pack
  * W_gate_up along H and W_down along I (the recomputed forward), W_down^T
  * along H and W_gate_up^T along 2I (the input gradients) -- in buf (device,
  * moe_mx_train_weights_size bytes, caller-owned; 0 for an unsupported
- * shape), described by *out (host; its tag is cleared on error).  Enqueued on
- * stream; no synchronisation. */
+ * shape), described by *out (host; its tag is cleared on error).  The same
+ * pass also lays out W_gate_up along H with gate and up interleaved, which
+ * with the W_down set is the MX forward's weights (out->forward,
+ * out->forward_scales).  Enqueued on stream; no synchronisation. */
 #define MOE_TRAIN_TAG 0x4d6f4542u
 typedef struct {
     const void *gate_up_k;              /* W_gate_up along H: N = 2I, K = H */
@@ -385,6 +387,12 @@ typedef struct {
     const uint8_t *gate_up_t_scales;
     int32_t E, H, I;
     uint32_t tag;                       /* MOE_TRAIN_TAG once prepared */
+    /* the MX forward of the same weights (W_gate_up along H with gate and up
+     * interleaved as moe_pack_weights lays them, W_down along I): pass them to
+     * moe_forward with quant MOE_FP8_MX32, so a training step runs its forward
+     * and its backward from one preparation */
+    moe_packed_weights forward;
+    moe_scales forward_scales;
 } moe_mx_train_weights;
 
 size_t moe_mx_train_weights_size(int E, int H, int I);

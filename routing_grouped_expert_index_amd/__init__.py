@@ -73,7 +73,8 @@ class _CTrain(ctypes.Structure):
                 ("down_k", ctypes.c_void_p), ("down_k_scales", ctypes.c_void_p),
                 ("down_t", ctypes.c_void_p), ("down_t_scales", ctypes.c_void_p),
                 ("gate_up_t", ctypes.c_void_p), ("gate_up_t_scales", ctypes.c_void_p),
-                ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("tag", ctypes.c_uint32)]
+                ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("tag", ctypes.c_uint32),
+                ("forward", _CPacked), ("forward_scales", _CScales)]
 
 
 class _CViews(ctypes.Structure):
@@ -462,11 +463,23 @@ def forward(x: torch.Tensor, routes: Routes, weights: PackedWeights,
 
 
 class TrainWeights:
-    """The four packed MX operand sets moe_prepare_mx_train_weights builds from
-    bf16 master weights (one device buffer) and their C descriptor."""
+    """The packed MX operand sets moe_prepare_mx_train_weights builds from bf16
+    master weights (one device buffer) and their C descriptor.  `forward` and
+    `forward_scales` are the MX forward's weights and scales, for forward()
+    with quant "fp8_mx32"."""
 
     def __init__(self, buf: torch.Tensor, desc: _CTrain):
         self.buf, self.desc = buf, desc
+        E, H, I = desc.E, desc.H, desc.I
+        base = buf.data_ptr()
+
+        def view(ptr, n):
+            return buf[ptr - base:ptr - base + n]
+
+        f = desc.forward
+        self.forward = PackedWeights(view(f.gate_up, 2 * E * H * I), view(f.down, E * H * I), f)
+        self.forward_scales = (view(desc.forward_scales.w_gate_up_scale, 2 * E * H * I // 32),
+                               view(desc.forward_scales.w_down_scale, E * H * I // 32))
 
     E = property(lambda self: self.desc.E)
     H = property(lambda self: self.desc.H)

@@ -19,6 +19,7 @@
 
 #include "common.cuh"
 #include "launch.h"
+#include "layout.cuh"
 
 namespace moe {
 
@@ -30,8 +31,9 @@ __device__ __forceinline__ uint8_t e4m3_byte(float v) { return (uint8_t)(f32x2_t
 // ------------------------------------------------------------- weights --
 
 // bf16 master weights -> an MX operand set in the packed layout the grouped
-// MX GEMM reads (layout.cuh, MX chunk order, plain column order), one scale
-// per 32 consecutive k of each output column n, in one pass:
+// MX GEMM reads (layout.cuh, MX chunk order; plain column order, or with
+// GATE_UP the forward's gate/up interleave of N = 2I columns), one scale per
+// 32 consecutive k of each output column n, in one pass:
 //   along_k = 1: src [E][K][N] (the groups run down the source's rows);
 //   along_k = 0: src [E][N][K] (the groups run along the source's rows: the
 //                transposed use of a weight).
@@ -39,7 +41,7 @@ __device__ __forceinline__ uint8_t e4m3_byte(float v) { return (uint8_t)(f32x2_t
 // codes are two 16-byte pieces: K values 32kb + [0, 16) and + [16, 32) are
 // lane halves 0 and 1, half q = kb % 2, of slice kb / 2 of the column's packed
 // row; its E8M0 byte goes to the packed scale dword of that row and K group.
-template <bool ALONG_K>
+template <bool ALONG_K, bool GATE_UP>
 __global__ void __launch_bounds__(256)
 mx_pack_weights_kernel(const uint16_t* __restrict__ src, int E, int K, int N, uint8_t* __restrict__ packed,
                        uint8_t* __restrict__ packed_s) {
@@ -77,9 +79,8 @@ mx_pack_weights_kernel(const uint16_t* __restrict__ src, int E, int K, int N, ui
         hi[t] = f32x4_to_e4m3x4(v[16 + 4 * t] * inv, v[16 + 4 * t + 1] * inv, v[16 + 4 * t + 2] * inv,
                                 v[16 + 4 * t + 3] * inv);
     }
-    // packed row of column n (the inverse of down_col_of_packed)
-    const int c = n & 63;
-    const int P = (n & ~63) + 32 * ((c >> 4) & 1) + 8 * ((c >> 2) & 3) + 4 * ((c >> 5) & 1) + (c & 3);
+    // packed row of column n
+    const int P = GATE_UP ? (n < N / 2 ? packed_gate_row(n) : packed_up_row(n - N / 2)) : packed_down_row(n);
     const int g32 = P >> 5, j = P & 31, nsl = K / 64;
     uint8_t* blk = packed + e * (long)N * K + (((long)g32 * nsl + (kb >> 1)) * 2 + (kb & 1)) * 1024;
     *reinterpret_cast<u32x4*>(blk + j * 16) = lo;
@@ -88,14 +89,20 @@ mx_pack_weights_kernel(const uint16_t* __restrict__ src, int E, int K, int N, ui
     packed_s[dw * 4 + ((kb & 7) >> 1)] = (uint8_t)b;
 }
 
-hipError_t launch_mx_pack_weights(const uint16_t* src, int E, int K, int N, bool along_k, uint8_t* packed,
-                                  uint8_t* packed_s, hipStream_t st) {
+hipError_t launch_mx_pack_weights(const uint16_t* src, int E, int K, int N, bool along_k, bool gate_up,
+                                  uint8_t* packed, uint8_t* packed_s, hipStream_t st) {
     const long groups = (long)E * (K / 32) * N;
     const dim3 grid((unsigned)((groups + 255) / 256));
-    if (along_k)
-        hipLaunchKernelGGL(mx_pack_weights_kernel<true>, grid, dim3(256), 0, st, src, E, K, N, packed, packed_s);
+    if (gate_up && !along_k) return hipErrorInvalidValue;
+    if (gate_up)
+        hipLaunchKernelGGL((mx_pack_weights_kernel<true, true>), grid, dim3(256), 0, st, src, E, K, N, packed,
+                           packed_s);
+    else if (along_k)
+        hipLaunchKernelGGL((mx_pack_weights_kernel<true, false>), grid, dim3(256), 0, st, src, E, K, N, packed,
+                           packed_s);
     else
-        hipLaunchKernelGGL(mx_pack_weights_kernel<false>, grid, dim3(256), 0, st, src, E, K, N, packed, packed_s);
+        hipLaunchKernelGGL((mx_pack_weights_kernel<false, false>), grid, dim3(256), 0, st, src, E, K, N, packed,
+                           packed_s);
     return hipGetLastError();
 }
 

@@ -530,7 +530,7 @@ bool train_shape_ok(int H, int I, int E) {
 }
 
 struct TrainLayout {
-    size_t gu_k, gu_k_s, d_k, d_k_s, d_t, d_t_s, gu_t, gu_t_s, total;
+    size_t gu_f, gu_f_s, gu_k, gu_k_s, d_k, d_k_s, d_t, d_t_s, gu_t, gu_t_s, total;
 };
 
 TrainLayout train_layout(int E, int H, int I) {
@@ -542,6 +542,8 @@ TrainLayout train_layout(int E, int H, int I) {
         off += align256(bytes);
         return at_;
     };
+    L.gu_f = take(2 * w);
+    L.gu_f_s = take(2 * w / 32);
     L.gu_k = take(2 * w);
     L.gu_k_s = take(2 * w / 32);
     L.d_k = take(w);
@@ -778,6 +780,7 @@ int moe_prepare_mx_train_weights(const void* w_gate_up, const void* w_down, int 
                                  size_t buf_bytes, moe_mx_train_weights* out, void* stream) {
     if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
     out->tag = 0;
+    out->forward.tag = 0;
     if (!train_shape_ok(H, I, E))
         return fail(MOE_ERR_UNSUPPORTED, "MX backward: H and I multiples of 256 up to 8192, 1 <= E <= %d",
                     moe::kMaxExperts);
@@ -791,10 +794,13 @@ int moe_prepare_mx_train_weights(const void* w_gate_up, const void* w_down, int 
     const uint16_t* wgu = static_cast<const uint16_t*>(w_gate_up);
     const uint16_t* wd = static_cast<const uint16_t*>(w_down);
     // (src, K, N, along_k) -> the packed set (N rows of K) and its packed scales, one pass
-    auto one = [&](const uint16_t* src, int K, int N, bool along_k, size_t dst, size_t dst_s) -> int {
-        return hip_status(moe::launch_mx_pack_weights(src, E, K, N, along_k, b + dst, b + dst_s, st), "mx pack");
+    auto one = [&](const uint16_t* src, int K, int N, bool along_k, size_t dst, size_t dst_s,
+                   bool gate_up = false) -> int {
+        return hip_status(moe::launch_mx_pack_weights(src, E, K, N, along_k, gate_up, b + dst, b + dst_s, st),
+                          "mx pack");
     };
     int rc;
+    if ((rc = one(wgu, H, 2 * I, true, L.gu_f, L.gu_f_s, true)) != MOE_OK) return rc;   // the forward's Gate/Up
     if ((rc = one(wgu, H, 2 * I, true, L.gu_k, L.gu_k_s)) != MOE_OK) return rc;     // forward Gate/Up: along H
     if ((rc = one(wd, I, H, true, L.d_k, L.d_k_s)) != MOE_OK) return rc;            // forward Down: along I
     if ((rc = one(wd, H, I, false, L.d_t, L.d_t_s)) != MOE_OK) return rc;           // W_down^T: along H
@@ -810,6 +816,16 @@ int moe_prepare_mx_train_weights(const void* w_gate_up, const void* w_down, int 
     out->E = E;
     out->H = H;
     out->I = I;
+    // the MX forward's weights: the interleaved Gate/Up set and the Down set
+    out->forward.gate_up = b + L.gu_f;
+    out->forward.down = b + L.d_k;
+    out->forward.E = E;
+    out->forward.H = H;
+    out->forward.I = I;
+    out->forward.quant = MOE_FP8_MX32;
+    out->forward.tag = MOE_PACKED_TAG;
+    out->forward_scales.w_gate_up_scale = reinterpret_cast<const float*>(b + L.gu_f_s);
+    out->forward_scales.w_down_scale = reinterpret_cast<const float*>(b + L.d_k_s);
     out->tag = MOE_TRAIN_TAG;
     return ok();
 }

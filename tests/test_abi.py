@@ -234,8 +234,8 @@ def test_backward_sizes_and_shape_rules():
     """The MX backward's buffer sizes cover what it writes; unsupported shapes give 0."""
     E, H, I = 128, 4096, 512
     w = moe.mx_train_weights_size(E, H, I)
-    # four packed operand sets: 2 x (E H 2I) + 2 x (E I H) codes, and their scales (one byte per 32)
-    assert w >= (2 + 1 + 1 + 2) * E * H * I * 33 // 32
+    # five packed operand sets: 3 x (E H 2I) + 2 x (E I H) codes, and their scales (one byte per 32)
+    assert w >= (2 + 2 + 1 + 1 + 2) * E * H * I * 33 // 32
     T, k = 4096, 8
     R = T * k
     ws = moe.backward_workspace_size(T, H, I, E, k)
@@ -265,7 +265,7 @@ def test_backward_host_validation_before_any_launch():
     r = moe._CRoutes()
     r.T, r.E, r.k = 8, 4, 2
     r.topk_ids = r.topk_weights = r.expert_offsets = r.perm = r.route_pos = 4096
-    w = moe._CTrain(4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4, 256, 256, 0)
+    w = moe._CTrain(4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4, 256, 256, 0, moe._CPacked(), moe._CScales())
     args = [good, ctypes.byref(r), ctypes.byref(w), good, good, good, good, good, good, 1 << 40, None]
     assert L.moe_backward(*args) == -1 and b"moe_prepare_mx_train_weights" in L.moe_last_error()
     w.tag = moe.TRAIN_TAG

@@ -228,3 +228,26 @@ def test_backward_graph_replay_bitwise_equal():
             assert torch.equal(out[n], eager[n]), (i, n)
         moe.backward(x, r, tw, d, workspace=ws, out={n: torch.empty_like(v) for n, v in out.items()})
         torch.cuda.synchronize()
+
+
+def test_prepared_forward_equals_the_classic_mx_forward():
+    """The forward set of the preparation runs moe_forward to the same bits as the
+    MX weights quantised with the input generator's rule and packed with
+    moe_pack_weights / moe_pack_mx_scales."""
+    T, H, I, E, k = 150, 512, 256, 8, 4
+    a = random_activations(T, H, E, seed=680)
+    w = random_weights(E, H, I, "bf16", seed=681)
+    u8 = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+    tw = moe.prepare_mx_train_weights(bf16_dev(w["w_gate_up"]), bf16_dev(w["w_down"]))
+    cg, sg = quantise_weight_mx32(bf16_bits_to_f32(w["w_gate_up"]))
+    cd, sd = quantise_weight_mx32(bf16_bits_to_f32(w["w_down"]))
+    pw = moe.pack_weights(u8(cg), u8(cd), "fp8_mx32")
+    ps = moe.pack_mx_scales(u8(sg), u8(sd))
+    r = moe.route(torch.from_numpy(a["logits"]).to(DEV), k)
+    x = bf16_dev(a["x"])
+    got = moe.forward(x, r, tw.forward, quant="fp8_mx32", scales=tw.forward_scales, path="grouped")
+    ref = moe.forward(x, r, pw, quant="fp8_mx32", scales=ps, path="grouped")
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert torch.equal(tw.forward.gate_up.reshape(-1), pw.gate_up.view(torch.uint8).reshape(-1))
+    assert torch.equal(tw.forward_scales[0], ps[0].reshape(-1))
