@@ -164,7 +164,8 @@ def counter_traffic(name):
 
 
 def bench_backward(torch, moe, steps, warmup, stage_steps=10):
-    """The MX training backward (moe_backward) at the MX prefill layer's shape:
+    """The MX training backward (moe_backward) at the MX prefill layer's shape,
+    and the training step around it (weight preparation + MX forward from it):
     seeded bf16 master weights, x, logits and upstream gradient; the routing and
     the weight preparation run once, outside the timed region.  Timed: `steps`
     calls between two HIP events on the stream; then `stage_steps` calls with
@@ -208,6 +209,21 @@ def bench_backward(torch, moe, steps, warmup, stage_steps=10):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     step_ms = e0.elapsed_time(e1) / steps
+    # the MX forward from the same preparation (the training step's forward)
+    fout = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    fws = torch.empty(moe.forward_workspace_size(T, H, I, E, k, "fp8_mx32", "grouped"), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        moe.forward(x, routes, tw.forward, quant="fp8_mx32", scales=tw.forward_scales, out=fout, path="grouped",
+                    workspace=fws)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(steps):
+        moe.forward(x, routes, tw.forward, quant="fp8_mx32", scales=tw.forward_scales, out=fout, path="grouped",
+                    workspace=fws)
+    f1.record()
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / steps
+    del fout, fws
     ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(14)] for _ in range(stage_steps)]
     names = None
     for evs in ev_sets:
@@ -237,6 +253,8 @@ def bench_backward(torch, moe, steps, warmup, stage_steps=10):
                          "weights, dW in fp32",
                 tokens_per_s=round(T * steps / dt, 1), ms_per_step=round(step_ms, 4),
                 ms_per_step_wall=round(dt / steps * 1e3, 4), prepare_weights_ms=round(prep_ms, 3),
+                forward_ms=round(fwd_ms, 4),
+                train_step_ms=round(prep_ms + fwd_ms + step_ms, 4),
                 stages=stages, dominant=dict(stage=dom, **stages[dom]),
                 flops_per_step=18.0 * R * H * I, padded_routes=Rp)
 
@@ -820,7 +838,8 @@ def recap(line):
     if bw:
         dom = bw["dominant"]
         log(f"recap backward MX T=4096: {bw['ms_per_step'] * 1e3:.1f} us/step, {bw['tokens_per_s']:.4g} tokens/s; "
-            f"dominant {dom['stage']} {dom['us']} us = {dom.get('frac', 0):.3f} of {dom.get('bound', '?')} peak")
+            f"dominant {dom['stage']} {dom['us']} us = {dom.get('frac', 0):.3f} of {dom.get('bound', '?')} peak; "
+            f"training step (prepare + forward + backward) {bw['train_step_ms']:.3f} ms")
     cb = line.get("cpu_baseline")
     if cb:
         log(f"recap cpu oracle: {cb['value']} {cb['unit']} on {cb['cores']} threads ({cb['sample']})")
