@@ -174,12 +174,13 @@ swiglu_fwd_kernel(const float* __restrict__ gu, long R, int I, float* __restrict
 // One workgroup per sorted route i (route r = perm[i] of token t = r / k, gate
 // w = tw[r]): dy = w * dout[t] in fp32, its MX rows (codes [R][H], bytes
 // [R][H/32]) for dh = dy W_down^T, and the gate's gradient <dout[t], y_i>
-// (y: the recomputed Down output, fp32 [R][H] sorted) written to dgate[r].
+// (y: the recomputed Down output, bf16 [R][H] sorted: it enters only this
+// dot product, where its rounding averages out) written to dgate[r].
 // The sum runs per thread over its columns in order, then over the wave and
 // the four waves in a fixed order.
 __global__ void __launch_bounds__(256)
 dy_kernel(const uint16_t* __restrict__ dout, const float* __restrict__ tw, const int32_t* __restrict__ perm, int k,
-          const float* __restrict__ y, int H, uint8_t* __restrict__ dyq, uint8_t* __restrict__ sdy,
+          const uint16_t* __restrict__ y, int H, uint8_t* __restrict__ dyq, uint8_t* __restrict__ sdy,
           float* __restrict__ dgate) {
     __shared__ float part[4];
     const long i = blockIdx.x;
@@ -191,7 +192,7 @@ dy_kernel(const uint16_t* __restrict__ dout, const float* __restrict__ tw, const
     for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
         float d[8], yy[8], v[8];
         load8_bf16(dout + (long)t * H + c, d);
-        load8_f32(y + i * H + c, yy);
+        load8_bf16(y + i * H + c, yy);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             v[j] = w * d[j];
@@ -511,7 +512,7 @@ hipError_t launch_swiglu_fwd(const float* gu, long R, int I, float* h32, uint8_t
     return hipGetLastError();
 }
 
-hipError_t launch_dy(const uint16_t* dout, const float* tw, const int32_t* perm, int k, const float* y, long R,
+hipError_t launch_dy(const uint16_t* dout, const float* tw, const int32_t* perm, int k, const uint16_t* y, long R,
                      int H, uint8_t* dyq, uint8_t* sdy, float* dgate, hipEvent_t ev_end, hipStream_t st) {
     if (R == 0) return hipSuccess;
     hipExtLaunchKernelGGL(dy_kernel, dim3((unsigned)R), dim3(256), 0, st, nullptr, ev_end, 0, dout, tw, perm, k, y,

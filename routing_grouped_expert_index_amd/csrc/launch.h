@@ -132,7 +132,7 @@ hipError_t launch_mx_pack_weights(const uint16_t* src, int E, int K, int N, bool
                                   uint8_t* packed, uint8_t* packed_s, hipStream_t st);
 hipError_t launch_swiglu_fwd(const float* gu, long R, int I, float* h32, uint8_t* hq, uint8_t* sh,
                              hipEvent_t ev_end, hipStream_t st);
-hipError_t launch_dy(const uint16_t* dout, const float* tw, const int32_t* perm, int k, const float* y, long R,
+hipError_t launch_dy(const uint16_t* dout, const float* tw, const int32_t* perm, int k, const uint16_t* y, long R,
                      int H, uint8_t* dyq, uint8_t* sdy, float* dgate, hipEvent_t ev_end, hipStream_t st);
 hipError_t launch_swiglu_bwd(const float* gu, const float* dh, long R, int I, float* dgu, uint8_t* dguq,
                              uint8_t* sdgu, hipEvent_t ev_end, hipStream_t st);

@@ -586,7 +586,7 @@ BwdLayout bwd_layout(int T, int H, int I, int E, int k) {
     L.h32 = take(R * I * 4);
     L.hq = take(R * I);
     L.sh = take(R * (I / 32));
-    L.y = take(R * H * 4);          // the recomputed Down output (fp32), then the rows of dx (bf16)
+    L.y = take(R * H * 2);          // the recomputed Down output, then the rows of dx (both bf16)
     L.dyq = take(R * H);
     L.sdy = take(R * (H / 32));
     L.dh = take(R * I * 4);
@@ -686,7 +686,6 @@ int backward_impl(const void* x, const moe_routes* routes, const moe_mx_train_we
     P.ev_first_start = static_cast<hipEvent_t>(events && n_events > 0 ? events[0] : nullptr);
 
     float* gu = at<float>(ws, L.gu);
-    float* y32 = at<float>(ws, L.y);
     float* h32 = at<float>(ws, L.h32);
     uint8_t* hq = at<uint8_t>(ws, L.hq);
     uint8_t* sh = at<uint8_t>(ws, L.sh);
@@ -718,9 +717,9 @@ int backward_impl(const void* x, const moe_routes* routes, const moe_mx_train_we
                           w->gate_up_k_scales, true, gu, true),
                   "gate_up");
         MOE_BSTEP(moe::launch_swiglu_fwd(gu, R, I, h32, hq, sh, ev(), st), "swiglu");
-        MOE_BSTEP(product(hq, sh, R, I, H, w->down_k, w->down_k_scales, false, y32, true), "down");
+        MOE_BSTEP(product(hq, sh, R, I, H, w->down_k, w->down_k_scales, false, P.y, false), "down");
         // dy = gate * dout, the gates' gradient, dh = dy W_down^T
-        MOE_BSTEP(moe::launch_dy(dout16, routes->topk_weights, routes->perm, k, y32, R, H, dyq, sdy, dgate, ev(), st),
+        MOE_BSTEP(moe::launch_dy(dout16, routes->topk_weights, routes->perm, k, P.y, R, H, dyq, sdy, dgate, ev(), st),
                   "dy");
         MOE_BSTEP(product(dyq, sdy, R, H, I, w->down_t, w->down_t_scales, false, dh, true), "dh");
         MOE_BSTEP(moe::launch_swiglu_bwd(gu, dh, R, I, dgu, dguq, sdgu, ev(), st), "swiglu_bwd");

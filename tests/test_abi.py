@@ -239,8 +239,8 @@ def test_backward_sizes_and_shape_rules():
     T, k = 4096, 8
     R = T * k
     ws = moe.backward_workspace_size(T, H, I, E, k)
-    # g|u, h, y and dh in fp32, dGU in fp32 and codes, the four transposed operands
-    assert ws >= R * (2 * I * 4 + I * 4 + H * 4 + I * 4 + 2 * I * 5) + (2 * H + 3 * I) * (R + 63 * E)
+    # g|u, h and dh in fp32, y in bf16, dGU in fp32 and codes, the four transposed operands
+    assert ws >= R * (2 * I * 4 + I * 4 + H * 2 + I * 4 + 2 * I * 5) + (2 * H + 3 * I) * (R + 63 * E)
     assert moe.backward_workspace_size(0, H, I, E, k) > 0          # an empty batch still writes dW = 0
     for bad in ((T, 4096 + 64, I, E, k), (T, H, 384, E, k), (T, H, I, 4, 8), (T, 16384, I, E, k)):
         assert moe.backward_workspace_size(*bad) == 0, bad
