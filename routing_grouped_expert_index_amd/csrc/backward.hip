@@ -308,11 +308,14 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
     if (m >= M) return;
     float v[32];
     float a = 0.0f;
+    if (cnt > 0) {
+        // every load unconditional (a route past the expert's last re-reads it
+        // and is masked afterwards): a load under a per-route condition would
+        // become a branch that waits for every load before it
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        float x = 0.0f;
-        if (j < cnt) {
-            const long i = first + j;
+        for (int j = 0; j < 32; ++j) {
+            const long i = first + min(j, cnt - 1);
+            float x;
             if (SRC == D1_X) {
                 x = bf16_to_f32(static_cast<const uint16_t*>(src)[tok(perm[i]) * M + m]);
             } else if (SRC == D1_DY) {
@@ -321,9 +324,12 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
             } else {
                 x = static_cast<const float*>(src)[i * M + m];
             }
+            v[j] = j < cnt ? x : 0.0f;
+            a = fmaxf(a, fabsf(v[j]));
         }
-        v[j] = x;
-        a = fmaxf(a, fabsf(x));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] = 0.0f;
     }
     const uint32_t b = mx_byte(a);
     const float inv = mx_inv(b);
