@@ -184,6 +184,7 @@ def bench_backward(torch, moe, steps, warmup, stage_steps=10):
     x, d = b16(a["x"]), b16(dout)
     routes = moe.route(torch.from_numpy(a["logits"]).to(dev), k)
     wgu, wd = b16(w["w_gate_up"]), b16(w["w_down"])
+    tw = moe.prepare_mx_train_weights(wgu, wd)   # (the first call loads the kernels)
     torch.cuda.synchronize()
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     p0.record()

@@ -44,7 +44,7 @@ __device__ __forceinline__ uint8_t e4m3_byte(float v) { return (uint8_t)(f32x2_t
 template <bool ALONG_K, bool GATE_UP>
 __global__ void __launch_bounds__(256)
 mx_pack_weights_kernel(const uint16_t* __restrict__ src, int E, int K, int N, uint8_t* __restrict__ packed,
-                       uint8_t* __restrict__ packed_s) {
+                       uint8_t* __restrict__ packed_s, uint8_t* __restrict__ plain, uint8_t* __restrict__ plain_s) {
     const long g = (long)blockIdx.x * 256 + threadIdx.x;
     const int nkb = K / 32;
     if (g >= (long)E * nkb * N) return;
@@ -79,30 +79,37 @@ mx_pack_weights_kernel(const uint16_t* __restrict__ src, int E, int K, int N, ui
         hi[t] = f32x4_to_e4m3x4(v[16 + 4 * t] * inv, v[16 + 4 * t + 1] * inv, v[16 + 4 * t + 2] * inv,
                                 v[16 + 4 * t + 3] * inv);
     }
-    // packed row of column n
-    const int P = GATE_UP ? (n < N / 2 ? packed_gate_row(n) : packed_up_row(n - N / 2)) : packed_down_row(n);
-    const int g32 = P >> 5, j = P & 31, nsl = K / 64;
-    uint8_t* blk = packed + e * (long)N * K + (((long)g32 * nsl + (kb >> 1)) * 2 + (kb & 1)) * 1024;
-    *reinterpret_cast<u32x4*>(blk + j * 16) = lo;
-    *reinterpret_cast<u32x4*>(blk + (32 + j) * 16) = hi;
-    const long dw = (((e * (N / 32) + g32) * (K / 256) + kb / 8) * 64 + 32 * (kb & 1) + j);
-    packed_s[dw * 4 + ((kb & 7) >> 1)] = (uint8_t)b;
+    // the group's pieces and byte at packed row P of a set
+    auto put = [&](uint8_t* dst, uint8_t* dst_s, int P) __attribute__((always_inline)) {
+        const int g32 = P >> 5, j = P & 31, nsl = K / 64;
+        uint8_t* blk = dst + e * (long)N * K + (((long)g32 * nsl + (kb >> 1)) * 2 + (kb & 1)) * 1024;
+        *reinterpret_cast<u32x4*>(blk + j * 16) = lo;
+        *reinterpret_cast<u32x4*>(blk + (32 + j) * 16) = hi;
+        const long dw = (((e * (N / 32) + g32) * (K / 256) + kb / 8) * 64 + 32 * (kb & 1) + j);
+        dst_s[dw * 4 + ((kb & 7) >> 1)] = (uint8_t)b;
+    };
+    put(packed, packed_s,
+        GATE_UP ? (n < N / 2 ? packed_gate_row(n) : packed_up_row(n - N / 2)) : packed_down_row(n));
+    // GATE_UP may also write the same codes in plain column order (the second
+    // set quantised along the same K)
+    if (GATE_UP && plain) put(plain, plain_s, packed_down_row(n));
 }
 
 hipError_t launch_mx_pack_weights(const uint16_t* src, int E, int K, int N, bool along_k, bool gate_up,
-                                  uint8_t* packed, uint8_t* packed_s, hipStream_t st) {
+                                  uint8_t* packed, uint8_t* packed_s, uint8_t* plain, uint8_t* plain_s,
+                                  hipStream_t st) {
     const long groups = (long)E * (K / 32) * N;
     const dim3 grid((unsigned)((groups + 255) / 256));
-    if (gate_up && !along_k) return hipErrorInvalidValue;
+    if ((gate_up && !along_k) || (plain && !gate_up)) return hipErrorInvalidValue;
     if (gate_up)
         hipLaunchKernelGGL((mx_pack_weights_kernel<true, true>), grid, dim3(256), 0, st, src, E, K, N, packed,
-                           packed_s);
+                           packed_s, plain, plain_s);
     else if (along_k)
         hipLaunchKernelGGL((mx_pack_weights_kernel<true, false>), grid, dim3(256), 0, st, src, E, K, N, packed,
-                           packed_s);
+                           packed_s, plain, plain_s);
     else
         hipLaunchKernelGGL((mx_pack_weights_kernel<false, false>), grid, dim3(256), 0, st, src, E, K, N, packed,
-                           packed_s);
+                           packed_s, plain, plain_s);
     return hipGetLastError();
 }
 

@@ -129,7 +129,8 @@ hipError_t launch_grouped_mx_y(const MxProduct& q, hipStream_t st);
 
 // backward.hip
 hipError_t launch_mx_pack_weights(const uint16_t* src, int E, int K, int N, bool along_k, bool gate_up,
-                                  uint8_t* packed, uint8_t* packed_s, hipStream_t st);
+                                  uint8_t* packed, uint8_t* packed_s, uint8_t* plain, uint8_t* plain_s,
+                                  hipStream_t st);
 hipError_t launch_swiglu_fwd(const float* gu, long R, int I, float* h32, uint8_t* hq, uint8_t* sh,
                              hipEvent_t ev_end, hipStream_t st);
 hipError_t launch_dy(const uint16_t* dout, const float* tw, const int32_t* perm, int k, const uint16_t* y, long R,

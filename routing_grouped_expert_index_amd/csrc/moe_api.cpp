@@ -793,14 +793,17 @@ int moe_prepare_mx_train_weights(const void* w_gate_up, const void* w_down, int 
     const uint16_t* wgu = static_cast<const uint16_t*>(w_gate_up);
     const uint16_t* wd = static_cast<const uint16_t*>(w_down);
     // (src, K, N, along_k) -> the packed set (N rows of K) and its packed scales, one pass
-    auto one = [&](const uint16_t* src, int K, int N, bool along_k, size_t dst, size_t dst_s,
-                   bool gate_up = false) -> int {
-        return hip_status(moe::launch_mx_pack_weights(src, E, K, N, along_k, gate_up, b + dst, b + dst_s, st),
+    auto one = [&](const uint16_t* src, int K, int N, bool along_k, size_t dst, size_t dst_s) -> int {
+        return hip_status(moe::launch_mx_pack_weights(src, E, K, N, along_k, false, b + dst, b + dst_s, nullptr,
+                                                      nullptr, st),
                           "mx pack");
     };
     int rc;
-    if ((rc = one(wgu, H, 2 * I, true, L.gu_f, L.gu_f_s, true)) != MOE_OK) return rc;   // the forward's Gate/Up
-    if ((rc = one(wgu, H, 2 * I, true, L.gu_k, L.gu_k_s)) != MOE_OK) return rc;     // forward Gate/Up: along H
+    // W_gate_up along H, once: the forward's interleaved set and the plain set of the recomputation
+    if ((rc = hip_status(moe::launch_mx_pack_weights(wgu, E, H, 2 * I, true, true, b + L.gu_f, b + L.gu_f_s,
+                                                     b + L.gu_k, b + L.gu_k_s, st),
+                         "mx pack")) != MOE_OK)
+        return rc;
     if ((rc = one(wd, I, H, true, L.d_k, L.d_k_s)) != MOE_OK) return rc;            // forward Down: along I
     if ((rc = one(wd, H, I, false, L.d_t, L.d_t_s)) != MOE_OK) return rc;           // W_down^T: along H
     if ((rc = one(wgu, 2 * I, H, false, L.gu_t, L.gu_t_s)) != MOE_OK) return rc;    // W_gate_up^T: along 2I
