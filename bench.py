@@ -195,8 +195,8 @@ def bench_backward(torch, moe, steps, warmup, stage_steps=10):
     del wgu, wd
     out = {"dx": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
            "dgate": torch.empty((T, k), dtype=torch.float32, device=dev),
-           "dw_gate_up": torch.empty((E, H, 2 * I), dtype=torch.float32, device=dev),
-           "dw_down": torch.empty((E, I, H), dtype=torch.float32, device=dev)}
+           "dw_gate_up": torch.empty((E, H, 2 * I), dtype=torch.bfloat16, device=dev),
+           "dw_down": torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)}
     ws = torch.empty(moe.backward_workspace_size(T, H, I, E, k), dtype=torch.uint8, device=dev)
     for _ in range(warmup):
         moe.backward(x, routes, tw, d, workspace=ws, out=out)
@@ -235,8 +235,8 @@ def bench_backward(torch, moe, steps, warmup, stage_steps=10):
     Rp = int(np.sum((counts + 63) // 64 * 64))           # padded route positions of the weight gradients
     flops = {"gate_up": 2.0 * R * H * 2 * I, "down": 2.0 * R * I * H, "dh": 2.0 * R * H * I,
              "dx_rows": 2.0 * R * 2 * I * H}
-    wbytes = {"wgrad_gate_up": 4.0 * E * H * 2 * I + (H + 2 * I) * Rp * (1 + 1 / 32),
-              "wgrad_down": 4.0 * E * I * H + (I + H) * Rp * (1 + 1 / 32)}
+    wbytes = {"wgrad_gate_up": 2.0 * E * H * 2 * I + (H + 2 * I) * Rp * (1 + 1 / 32),
+              "wgrad_down": 2.0 * E * I * H + (I + H) * Rp * (1 + 1 / 32)}
     stages = {}
     for n, ms in st.items():
         rec = dict(us=round(ms * 1e3, 2))
@@ -251,7 +251,7 @@ def bench_backward(torch, moe, steps, warmup, stage_steps=10):
     dom = max(stages, key=lambda n: stages[n]["us"])
     del out, ws, tw
     return dict(workload="MX training backward at prefill_fp8_mx: T=4096 H=4096 I=512 E=128 top-8; bf16 master "
-                         "weights, dW in fp32",
+                         "weights, dW in bf16",
                 tokens_per_s=round(T * steps / dt, 1), ms_per_step=round(step_ms, 4),
                 ms_per_step_wall=round(dt / steps * 1e3, 4), prepare_weights_ms=round(prep_ms, 3),
                 forward_ms=round(fwd_ms, 4),

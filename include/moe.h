@@ -409,14 +409,14 @@ size_t moe_backward_workspace_size(int T, int H, int I, int E, int k);
  *   w       moe_prepare_mx_train_weights' descriptor (its E must be the
  *           routes' E)
  *   dx      bf16 [T][H]; dgate fp32 [T][k] (route r = t*k + j);
- *   dw_gate_up fp32 [E][H][2I], dw_down fp32 [E][I][H] (zero for an expert
- *           without routes)
+ *   dw_gate_up bf16 [E][H][2I], dw_down bf16 [E][I][H], the master
+ *           weights' type (zero for an expert without routes)
  * All pointers device, 16-byte aligned, caller-owned; ws as sized above.
  * Returns MOE_ERR_INVALID_ARG / UNSUPPORTED / WORKSPACE before anything is
  * enqueued, MOE_ERR_HIP if a launch fails.  Deterministic: every sum runs in
  * a fixed order.  No synchronisation. */
 int moe_backward(const void *x, const moe_routes *routes, const moe_mx_train_weights *w, const void *dout,
-                 void *dx, float *dgate, float *dw_gate_up, float *dw_down, void *ws, size_t ws_bytes,
+                 void *dx, float *dgate, void *dw_gate_up, void *dw_down, void *ws, size_t ws_bytes,
                  void *stream);
 
 /* moe_backward with stage events, as moe_forward_profiled: stage_events[0]
@@ -424,7 +424,7 @@ int moe_backward(const void *x, const moe_routes *routes, const moe_mx_train_wei
  * kernel; the stages are "init,quant_x,gate_up,swiglu,down,dy,dh,swiglu_bwd,
  * dx_rows,combine,dim1,wgrad_gate_up,wgrad_down" (T = 0: the last two). */
 int moe_backward_profiled(const void *x, const moe_routes *routes, const moe_mx_train_weights *w,
-                          const void *dout, void *dx, float *dgate, float *dw_gate_up, float *dw_down, void *ws,
+                          const void *dout, void *dx, float *dgate, void *dw_gate_up, void *dw_down, void *ws,
                           size_t ws_bytes, void *stream, void **stage_events, int n_events, int *n_stages,
                           const char **stage_names);
 

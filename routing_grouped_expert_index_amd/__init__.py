@@ -516,8 +516,8 @@ def backward_workspace_size(T: int, H: int, I: int, E: int, k: int) -> int:
 def backward(x: torch.Tensor, routes: Routes, weights: TrainWeights, dout: torch.Tensor,
              workspace: torch.Tensor | None = None, stream=None, events=None, out=None):
     """The layer's gradients for the upstream gradient dout bf16 [T, H]
-    (moe_backward): dict(dx bf16 [T,H], dgate fp32 [T,k], dw_gate_up fp32
-    [E,H,2I], dw_down fp32 [E,I,H]).  With events (torch.cuda.Event list) it
+    (moe_backward): dict(dx bf16 [T,H], dgate fp32 [T,k], dw_gate_up bf16
+    [E,H,2I], dw_down bf16 [E,I,H]).  With events (torch.cuda.Event list) it
     calls moe_backward_profiled and also returns the stage names."""
     _need_cuda(x, "x")
     _need_cuda(dout, "dout")
@@ -529,8 +529,8 @@ def backward(x: torch.Tensor, routes: Routes, weights: TrainWeights, dout: torch
     if out is None:
         out = {"dx": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
                "dgate": torch.empty((T, k), dtype=torch.float32, device=dev),
-               "dw_gate_up": torch.empty((E, H, 2 * I), dtype=torch.float32, device=dev),
-               "dw_down": torch.empty((E, I, H), dtype=torch.float32, device=dev)}
+               "dw_gate_up": torch.empty((E, H, 2 * I), dtype=torch.bfloat16, device=dev),
+               "dw_down": torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)}
     need = backward_workspace_size(T, H, I, E, k)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)

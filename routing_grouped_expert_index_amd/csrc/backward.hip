@@ -357,7 +357,8 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
 
 // ------------------------------------------------------- weight gradients --
 
-// C[e] (fp32 [M][N]) = sum over expert e's padded route positions p of
+// C[e] (bf16 [M][N], the master weights' type) = sum over expert e's padded
+// route positions p of
 // A[m][p] B[n][p], with A, B the dim1-cast operands (row stride ldo bytes,
 // scale row stride lds_ bytes).  One workgroup per 128x128 output tile.  The
 // tile's 128 rows of A and of B come into LDS by buffer loads with the LDS
@@ -368,18 +369,22 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
 // r's 16-byte chunk c sits at physical chunk c ^ ((r / 4) % 4).  Wave w then takes rows 64 (w / 2) and columns
 // 64 (w % 2) of the tile as 2x2 blocks of the scaled 32x32x64 MFMA, B's rows
 // as the first operand so that a lane holds 4 consecutive columns of C per
-// result group; the groups go through LDS so that each non-temporal store
-// instruction writes whole 128-byte lines of C (C is written once and not
-// read back here; against 16-byte stores straight from the result registers:
-// dW_gate_up 750 -> 694 us, dW_down 419 -> 353 us).  An expert without routes
-// gets zeros.  (C is row-major with N a multiple of 128.)
+// result group; a wave's two 32x32 blocks of one row block go through LDS as
+// bf16 so that each non-temporal store instruction writes whole 128-byte
+// lines of C (C is written once and not read back here; against 16-byte fp32
+// stores straight from the result registers: dW_gate_up 750 -> 694 us,
+// dW_down 419 -> 353 us, and bf16 instead of fp32 output 700 -> 520 us and
+// 357 -> 274 us).  An expert without routes gets zeros.  (C is row-major with
+// N a multiple of 128.)
 constexpr int kWgSlices = 1;                      // slices staged per round
-constexpr int kWgLds = 4 * 32 * 36 * 4;            // 18 KB: the store staging (the operands take 16 KB)
+constexpr int kWgOperandLds = kWgSlices * 2 * 128 * 64;   // 16 KB: A and B rows of one slice
+constexpr int kWgStageLds = 4 * 32 * 72 * 2;                // 18 KB: each wave's 32 rows of 72 bf16
+constexpr int kWgLds = kWgOperandLds > kWgStageLds ? kWgOperandLds : kWgStageLds;
 
 __global__ void __launch_bounds__(256)
 wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const uint8_t* __restrict__ B,
              const uint8_t* __restrict__ sB, long ldo, long lds_, const int32_t* __restrict__ poff, int E, int M,
-             int N, float* __restrict__ C) {
+             int N, uint16_t* __restrict__ C) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tm = M / 128, tn = N / 128;
     const long total = (long)E * tm * tn;
@@ -463,33 +468,29 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
             }
         }
     }
-    // acc[f][g][4q + t]: row mt 128 + ra0 + 32f, column nt 128 + rb0 - j + 8q + 4hh + t.
-    // Each 32x32 block goes out through this wave's 4.5 KB of LDS (rows of 36
-    // floats): lanes write their 4 groups of 4 columns, then read back 8 rows
-    // of 128 bytes per instruction, so every store covers whole 128-byte lines.
     __syncthreads();   // every wave is done reading the operand slices
-    float* ws = reinterpret_cast<float*>(smem) + wave * (32 * 36);
-    float* ce = C + (long)e * M * N;
+    uint16_t* ws = reinterpret_cast<uint16_t*>(smem) + wave * (32 * 72);
+    uint16_t* ce = C + (long)e * M * N;
     const int n0 = nt * 128 + (wave & 1) * 64;
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < 2; ++f) {
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<f32x4*>(ws + j * 36 + 8 * q + 4 * hh) =
-                    f32x4{acc[f][g][4 * q], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2], acc[f][g][4 * q + 3]};
-            __asm__ volatile("" ::: "memory");   // (a wave's LDS operations run in order)
+                *reinterpret_cast<uint2*>(ws + j * 72 + 32 * g + 8 * q + 4 * hh) =
+                    uint2{pack_bf16x2(acc[f][g][4 * q], acc[f][g][4 * q + 1]),
+                          pack_bf16x2(acc[f][g][4 * q + 2], acc[f][g][4 * q + 3])};
+        __asm__ volatile("" ::: "memory");
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int rr = 8 * p + (lane >> 3), cc = 4 * (lane & 7);
-                const f32x4 v = *reinterpret_cast<const f32x4*>(ws + rr * 36 + cc);
-                __builtin_nontemporal_store(
-                    v, reinterpret_cast<f32x4*>(ce + (long)(mt * 128 + (wave >> 1) * 64 + 32 * f + rr) * N + n0 + 32 * g +
-                                                cc));
-            }
-            __asm__ volatile("" ::: "memory");
+        for (int p = 0; p < 4; ++p) {
+            const int rr = 8 * p + (lane >> 3), cc = 8 * (lane & 7);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ws + rr * 72 + cc);
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<u32x4*>(ce + (long)(mt * 128 + (wave >> 1) * 64 + 32 * f + rr) * N + n0 + cc));
         }
+        __asm__ volatile("" ::: "memory");
+    }
 }
 
 // The gates' gradient taken to the router logits: the gates are the softmax
@@ -588,7 +589,7 @@ hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, cons
 }
 
 hipError_t launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, long ldo, long lds_,
-                        const int32_t* poff, int E, int M, int N, float* C, hipEvent_t ev_end, hipStream_t st) {
+                        const int32_t* poff, int E, int M, int N, uint16_t* C, hipEvent_t ev_end, hipStream_t st) {
     const long total = (long)E * (M / 128) * (N / 128);
     if (128 * ldo > 0x7fffffffL) return hipErrorInvalidValue;   // 32-bit offsets within a tile's rows
     hipExtLaunchKernelGGL(wgrad_kernel, dim3((unsigned)total), dim3(256), kWgLds, st, nullptr, ev_end, 0, A, sA, B,

@@ -144,7 +144,7 @@ hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, cons
                        int k, const int32_t* offsets, const int32_t* poff, const int32_t* seg, int E, int M, long Rp,
                        long ldo, long lds_, uint8_t* out, uint8_t* sout, hipEvent_t ev_end, hipStream_t st);
 hipError_t launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, long ldo, long lds_,
-                        const int32_t* poff, int E, int M, int N, float* C, hipEvent_t ev_end, hipStream_t st);
+                        const int32_t* poff, int E, int M, int N, uint16_t* C, hipEvent_t ev_end, hipStream_t st);
 hipError_t launch_fill_f32(float* p, long n, float v, hipStream_t st);
 hipError_t launch_route_grad(const int32_t* ids, const float* tw, const float* dgate, int T, int E, int k,
                              float* dlogits, hipStream_t st);

@@ -623,7 +623,7 @@ int check_train_shape(int T, int H, int I, int E, int k) {
 }
 
 int backward_impl(const void* x, const moe_routes* routes, const moe_mx_train_weights* w, const void* dout,
-                  void* dx, float* dgate, float* dw_gate_up, float* dw_down, void* ws, size_t ws_bytes, void* stream,
+                  void* dx, float* dgate, void* dw_gate_up, void* dw_down, void* ws, size_t ws_bytes, void* stream,
                   void** events, int n_events, int* n_stages, const char** stage_names) {
     if (!routes || !w) return fail(MOE_ERR_INVALID_ARG, "routes or w is NULL");
     const int T = routes->T, E = routes->E, k = routes->k, H = w->H, I = w->I;
@@ -757,9 +757,11 @@ int backward_impl(const void* x, const moe_routes* routes, const moe_mx_train_we
                                    ev(), st),
                   "dim1");
     }
-    MOE_BSTEP(moe::launch_wgrad(xT, sxT, dguT, sdguT, Rp, Rb, poff, E, H, 2 * I, dw_gate_up, ev(), st),
+    MOE_BSTEP(moe::launch_wgrad(xT, sxT, dguT, sdguT, Rp, Rb, poff, E, H, 2 * I, static_cast<uint16_t*>(dw_gate_up),
+                                ev(), st),
               "wgrad_gate_up");
-    MOE_BSTEP(moe::launch_wgrad(hT, shT, dyT, sdyT, Rp, Rb, poff, E, I, H, dw_down, ev(), st), "wgrad_down");
+    MOE_BSTEP(moe::launch_wgrad(hT, shT, dyT, sdyT, Rp, Rb, poff, E, I, H, static_cast<uint16_t*>(dw_down), ev(), st),
+              "wgrad_down");
 #undef MOE_BSTEP
     if (n_stages) *n_stages = stage;
     if (stage_names) *stage_names = names;
@@ -838,7 +840,7 @@ size_t moe_backward_workspace_size(int T, int H, int I, int E, int k) {
 }
 
 int moe_backward(const void* x, const moe_routes* routes, const moe_mx_train_weights* w, const void* dout, void* dx,
-                 float* dgate, float* dw_gate_up, float* dw_down, void* ws, size_t ws_bytes, void* stream) {
+                 float* dgate, void* dw_gate_up, void* dw_down, void* ws, size_t ws_bytes, void* stream) {
     return backward_impl(x, routes, w, dout, dx, dgate, dw_gate_up, dw_down, ws, ws_bytes, stream, nullptr, 0,
                          nullptr, nullptr);
 }
@@ -863,7 +865,7 @@ int moe_route_backward(const moe_routes* routes, const float* dgate, float* dlog
 }
 
 int moe_backward_profiled(const void* x, const moe_routes* routes, const moe_mx_train_weights* w, const void* dout,
-                          void* dx, float* dgate, float* dw_gate_up, float* dw_down, void* ws, size_t ws_bytes,
+                          void* dx, float* dgate, void* dw_gate_up, void* dw_down, void* ws, size_t ws_bytes,
                           void* stream, void** events, int n_events, int* n_stages, const char** stage_names) {
     return backward_impl(x, routes, w, dout, dx, dgate, dw_gate_up, dw_down, ws, ws_bytes, stream, events, n_events,
                          n_stages, stage_names);

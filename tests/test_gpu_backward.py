@@ -71,8 +71,8 @@ def test_backward_empty_batch_gives_zero_weight_gradients():
     tw = moe.prepare_mx_train_weights(bf16_dev(w["w_gate_up"]), bf16_dev(w["w_down"]))
     out = {"dx": torch.empty((0, H), dtype=torch.bfloat16, device=DEV),
            "dgate": torch.empty((0, k), dtype=torch.float32, device=DEV),
-           "dw_gate_up": torch.full((E, H, 2 * I), 7.0, device=DEV),
-           "dw_down": torch.full((E, I, H), 7.0, device=DEV)}
+           "dw_gate_up": torch.full((E, H, 2 * I), 7.0, dtype=torch.bfloat16, device=DEV),
+           "dw_down": torch.full((E, I, H), 7.0, dtype=torch.bfloat16, device=DEV)}
     g = moe.backward(torch.empty((0, H), dtype=torch.bfloat16, device=DEV), r, tw,
                      torch.empty((0, H), dtype=torch.bfloat16, device=DEV), out=out)
     torch.cuda.synchronize()
@@ -204,8 +204,8 @@ def test_backward_graph_replay_bitwise_equal():
     ws = torch.empty(moe.backward_workspace_size(T, H, I, E, k), dtype=torch.uint8, device=DEV)
     out = {"dx": torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
            "dgate": torch.empty((T, k), dtype=torch.float32, device=DEV),
-           "dw_gate_up": torch.empty((E, H, 2 * I), dtype=torch.float32, device=DEV),
-           "dw_down": torch.empty((E, I, H), dtype=torch.float32, device=DEV)}
+           "dw_gate_up": torch.empty((E, H, 2 * I), dtype=torch.bfloat16, device=DEV),
+           "dw_down": torch.empty((E, I, H), dtype=torch.bfloat16, device=DEV)}
     moe.backward(x, r, tw, d, workspace=ws, out=out)
     torch.cuda.synchronize()
     eager = {n: v.clone() for n, v in out.items()}
