@@ -366,12 +366,17 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
 // route positions p of
 // A[m][p] B[n][p], with A, B the dim1-cast operands (row stride ldo bytes,
 // scale row stride lds_ bytes).  One workgroup per 128x128 output tile.  The
-// tile's 128 rows of A and of B come into LDS by buffer loads with the LDS
-// bit, one 64-position slice (16 KB) at a time: the expert's K is short and
-// the tile is bound by latency and its output stores, so what counts is how
-// many workgroups share a CU (16 KB of LDS and 124 registers a lane: four per
-// SIMD; staging two or four slices per round measured 5% and 23% slower); row
-// r's 16-byte chunk c sits at physical chunk c ^ ((r / 4) % 4).  Wave w then takes rows 64 (w / 2) and columns
+// tile's 128 rows of A and of B, and their E8M0 scale dwords, come into LDS by
+// buffer loads with the LDS bit, one 64-position slice (18 KB) at a time into
+// two alternating buffers: slice s + 1's loads are issued before the wait for
+// slice s, so each wait covers one slice's latency less (the expert's K is
+// short, 4-5 slices, and the tile is bound by latency and its output stores,
+// not by its products).  What counts beside that is how many workgroups share
+// a CU: 36 KB of LDS and 124 registers a lane keep four per SIMD (staging
+// two or four slices per round in one buffer measured 5% and 23% slower than
+// one; the two buffers against one: dW_gate_up 507 -> 459 us, dW_down 270 ->
+// 237 us, same bits).  Row r's 16-byte chunk c sits at physical chunk
+// c ^ ((r / 4) % 4).  Wave w then takes rows 64 (w / 2) and columns
 // 64 (w % 2) of the tile as 2x2 blocks of the scaled 32x32x64 MFMA, B's rows
 // as the first operand so that a lane holds 4 consecutive columns of C per
 // result group; a wave's two 32x32 blocks of one row block go through LDS as
@@ -381,9 +386,9 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
 // dW_down 419 -> 353 us, and bf16 instead of fp32 output 700 -> 520 us and
 // 357 -> 274 us).  An expert without routes gets zeros.  (C is row-major with
 // N a multiple of 128.)
-constexpr int kWgSlices = 1;                      // slices staged per round
-constexpr int kWgOperandLds = kWgSlices * 2 * 128 * 64;   // 16 KB: A and B rows of one slice
-constexpr int kWgStageLds = 4 * 32 * 72 * 2;                // 18 KB: each wave's 32 rows of 72 bf16
+constexpr int kWgBuf = 2 * 128 * 64 + 2 * 128 * 8;   // 18 KB: A and B rows of a slice, then their scale dwords
+constexpr int kWgOperandLds = 2 * kWgBuf;             // two buffers
+constexpr int kWgStageLds = 4 * 32 * 72 * 2;          // 18 KB: each wave's 32 rows of 72 bf16
 constexpr int kWgLds = kWgOperandLds > kWgStageLds ? kWgOperandLds : kWgStageLds;
 
 __global__ void __launch_bounds__(256)
@@ -422,54 +427,63 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
     const uint32_t dof1 = (uint32_t)(dr1 * ldo) + 16u * (uint32_t)((lane & 3) ^ ((dr1 >> 2) & 3));
     // fragment rows of this lane: A rows ra0 + 32f, B rows rb0 + 32g
     const int ra0 = (wave >> 1) * 64 + j, rb0 = (wave & 1) * 64 + j;
-    const uint8_t* qa[2] = {sA + (long)(mt * 128 + ra0) * lds_ + 4 * hh, sA + (long)(mt * 128 + ra0 + 32) * lds_ + 4 * hh};
-    const uint8_t* qb[2] = {sB + (long)(nt * 128 + rb0) * lds_ + 4 * hh, sB + (long)(nt * 128 + rb0 + 32) * lds_ + 4 * hh};
     auto frag = [&](const uint8_t* base, int r) __attribute__((always_inline)) {
         const int sw = (r >> 2) & 3;
         const u32x4 lo = *reinterpret_cast<const u32x4*>(base + r * 64 + 16 * ((2 * hh) ^ sw));
         const u32x4 hi = *reinterpret_cast<const u32x4*>(base + r * 64 + 16 * ((2 * hh + 1) ^ sw));
         return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
-    for (int c0 = s0; c0 < s1; c0 += kWgSlices) {
-        const int nc = min(kWgSlices, s1 - c0);
-        if (c0 > s0) __syncthreads();   // every wave is done with the previous round's slices
-        for (int u = 0; u < nc; ++u) {
-            const uint32_t so = (uint32_t)((c0 + u) * 64);
-            uint8_t* la = smem + u * 16384 + wave * 2048;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la), 16, dof0 + so, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la + 1024), 16, dof1 + so, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192), 16, dof0 + so, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192 + 1024), 16, dof1 + so, 0, 0, 0);
+    // two LDS buffers of one slice each (A rows, B rows, then their scale
+    // dwords): slice s + 1's DMA goes out before the wait for slice s.  The
+    // loop's barriers are bare s_barrier between compiler memory fences:
+    // __syncthreads' release fence would wait for every load into LDS still
+    // in flight, slice s + 1's included; the explicit vmcnt waits order the
+    // loads against the reads instead.
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sA) + (long)mt * 128 * lds_, 0, (int)(128 * lds_), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sB) + (long)nt * 128 * lds_, 0, (int)(128 * lds_), 0x00020000);
+    // scale DMA lane: row 32 wave + lane / 2, lane half lane % 2
+    const uint32_t sof = (uint32_t)((32 * wave + (lane >> 1)) * lds_) + 4u * (uint32_t)(lane & 1);
+    auto issue = [&](int s, int buf) __attribute__((always_inline)) {
+        const uint32_t so = (uint32_t)(s * 64);
+        uint8_t* lb = smem + buf * kWgBuf;
+        uint8_t* la = lb + wave * 2048;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la), 16, dof0 + so, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la + 1024), 16, dof1 + so, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192), 16, dof0 + so, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192 + 1024), 16, dof1 + so, 0, 0, 0);
+        const uint32_t sso = sof + (uint32_t)((s >> 2) * 8);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, MOE_LDS_B(lb + 16384 + wave * 256), 4, sso, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, MOE_LDS_B(lb + 17408 + wave * 256), 4, sso, 0, 0, 0);
+    };
+    if (s0 < s1) issue(s0, 0);
+    for (int s = s0; s < s1; ++s) {
+        const int buf = (s - s0) & 1;
+        __asm__ volatile("" ::: "memory");
+        if (s + 1 < s1) {
+            __builtin_amdgcn_s_barrier();          // every wave is done reading the other buffer
+            __asm__ volatile("" ::: "memory");
+            issue(s + 1, buf ^ 1);
+            __builtin_amdgcn_s_waitcnt(0x0F76);    // vmcnt(6): slice s has landed (s + 1's 6 requests may not)
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
         }
-        uint32_t sa[kWgSlices][2], sb[kWgSlices][2];
+        __builtin_amdgcn_s_barrier();              // ... for every wave
+        __asm__ volatile("" ::: "memory");
+        const int sh = 8 * (s & 3);   // byte (slice % 4) of the scale dword: this lane half's block
+        const uint8_t* la = smem + buf * kWgBuf;
+        const uint32_t* ls = reinterpret_cast<const uint32_t*>(la + 16384);
 #pragma unroll
-        for (int u = 0; u < kWgSlices; ++u) {
-            const int s = min(c0 + u, s1 - 1);
-            const long so = (long)(s >> 2) * 8;
+        for (int f = 0; f < 2; ++f) {
+            const i32x8 av = frag(la, ra0 + 32 * f);
+            const uint32_t sa = ls[(ra0 + 32 * f) * 2 + hh];
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                sa[u][f] = *reinterpret_cast<const uint32_t*>(qa[f] + so);
-                sb[u][f] = *reinterpret_cast<const uint32_t*>(qb[f] + so);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's slices have landed
-        __syncthreads();                       // ... and every wave's
-#pragma unroll
-        for (int u = 0; u < kWgSlices; ++u) {
-            if (u < nc) {
-                const int sh = 8 * ((c0 + u) & 3);   // byte (slice % 4) of the scale dword: this lane half's block
-                const uint8_t* la = smem + u * 16384;
-#pragma unroll
-                for (int f = 0; f < 2; ++f) {
-                    const i32x8 av = frag(la, ra0 + 32 * f);
-#pragma unroll
-                    for (int g = 0; g < 2; ++g) {
-                        const i32x8 bv = frag(la + 8192, rb0 + 32 * g);
-                        acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            bv, av, acc[f][g], 0, 0, 0, (int)((sb[u][g] >> sh) & 0xffu), 0,
-                            (int)((sa[u][f] >> sh) & 0xffu));
-                    }
-                }
+            for (int g = 0; g < 2; ++g) {
+                const i32x8 bv = frag(la + 8192, rb0 + 32 * g);
+                const uint32_t sb = ls[256 + (rb0 + 32 * g) * 2 + hh];
+                acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bv, av, acc[f][g], 0, 0, 0, (int)((sb >> sh) & 0xffu), 0, (int)((sa >> sh) & 0xffu));
             }
         }
     }
