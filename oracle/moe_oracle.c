@@ -251,13 +251,25 @@ typedef struct {
     const uint8_t *q_x;       /* fp8 activation codes [T, H] */
 } orc_layer;
 
+/* Every e4m3 code and E8M0 byte decoded once (the same decoders, looked up
+ * instead of called per weight: the layer reads each weight once per route). */
+static double e4m3_tab[256], e8m0_tab[256];
+
+static void decode_tables(void) {
+    int c;
+    for (c = 0; c < 256; ++c) {
+        e4m3_tab[c] = oracle_e4m3_decode((uint8_t)c);
+        e8m0_tab[c] = oracle_e8m0_decode((uint8_t)c);
+    }
+}
+
 static double w_gu_at(const orc_layer *L, int e, int h, int n) {
     long idx = ((long)e * L->H + h) * (2L * L->I) + n;
     if (L->quant == ORC_BF16) return oracle_bf16_decode(((const uint16_t *)L->w_gu)[idx]);
     {
-        double q = oracle_e4m3_decode(((const uint8_t *)L->w_gu)[idx]);
+        double q = e4m3_tab[((const uint8_t *)L->w_gu)[idx]];
         if (L->quant == ORC_FP8_MX32)   /* bytes [E][H/32][2I] */
-            return q * oracle_e8m0_decode(((const uint8_t *)L->s_gu)[((long)e * (L->H / 32) + h / 32) * (2L * L->I) + n]);
+            return q * e8m0_tab[((const uint8_t *)L->s_gu)[((long)e * (L->H / 32) + h / 32) * (2L * L->I) + n]];
         if (L->quant == ORC_FP8_PER_TENSOR) return q * L->s_gu[e];
         return q * L->s_gu[((long)e * (L->H / 128) + h / 128) * (2L * L->I / 128) + n / 128];
     }
@@ -267,9 +279,9 @@ static double w_d_at(const orc_layer *L, int e, int i, int n) {
     long idx = ((long)e * L->I + i) * L->H + n;
     if (L->quant == ORC_BF16) return oracle_bf16_decode(((const uint16_t *)L->w_d)[idx]);
     {
-        double q = oracle_e4m3_decode(((const uint8_t *)L->w_d)[idx]);
+        double q = e4m3_tab[((const uint8_t *)L->w_d)[idx]];
         if (L->quant == ORC_FP8_MX32)   /* bytes [E][I/32][H] */
-            return q * oracle_e8m0_decode(((const uint8_t *)L->s_d)[((long)e * (L->I / 32) + i / 32) * L->H + n]);
+            return q * e8m0_tab[((const uint8_t *)L->s_d)[((long)e * (L->I / 32) + i / 32) * L->H + n]];
         if (L->quant == ORC_FP8_PER_TENSOR) return q * L->s_d[e];
         return q * L->s_d[((long)e * (L->I / 128) + i / 128) * (L->H / 128) + n / 128];
     }
@@ -366,6 +378,7 @@ int oracle_forward_ep(const uint16_t *x, int T, int H, int I, int E, int k,
     L.T = T; L.H = H; L.I = I; L.E = E; L.k = k; L.quant = quant;
     L.x = x; L.w_gu = w_gu; L.w_d = w_d; L.s_gu = s_gu; L.s_d = s_d;
     if (n_tok == 0 || T == 0) return 0;
+    decode_tables();
 
     /* activation quantisation [P3 Summary: FP8 activations before each GEMM] */
     if (quant != ORC_BF16) {
