@@ -109,7 +109,6 @@ gemm32_kernel(const GemmArgs g) {
     // re-read a valid row.  The wave's 16 source rows are read with scalar
     // loads (a vector load here would need a vmcnt wait that drains the
     // prefetch) and each lane picks its own.
-    const int dma_r = 16 * wave + (lane >> 2);
     auto src_row = [&](int row0_, int rows_) __attribute__((always_inline)) {
         int sel = 0;
 #pragma unroll
@@ -147,10 +146,13 @@ gemm32_kernel(const GemmArgs g) {
     // inside the resource's range and reads valid bytes.  Its MFMAs' results
     // are dropped either way.  (Against re-reading a valid row: the bf16
     // Gate/Up 0-1.5% faster over two sets of interleaved runs, FP8 unchanged.)
+    // (the lane's DMA row 16 wave + lane/4 from the opaque lane index: see lane_o)
     auto make_ap = [&](int src, int row0_, int rows_) __attribute__((always_inline)) {
+        const int lo = lane_o();
+        const int dma_r = 16 * wave_u + (lo >> 2);
         const long rel = GATHER ? src : src - row0_;
         return (dma_r >= rows_ ? 0xFFF00000u : (uint32_t)(rel * g.lda)) +
-               (uint32_t)(((lane & 3) ^ ((dma_r >> 2) & 3)) * 16);
+               (uint32_t)(((lo & 3) ^ ((dma_r >> 2) & 3)) * 16);
     };
     // idle waves (past N) load a valid block, so every wave issues the same loads
     // Epilogue stores are buffer stores through a resource covering C: the
