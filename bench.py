@@ -143,11 +143,11 @@ def bench_prefill(torch, moe, name, steps, warmup, stage_steps=10):
 # (x1.0).  Valid only for the GEMM source the counters were taken on; any edit
 # to it turns the figure into null.
 FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524300.5, 1.0
-_GEMM_SHA = "1ca01fb168aa047f6434d72ad5760a57c75e1620836e989b0ad07bad9f641470"
+_GEMM_SHA = "64d025410162ebec64ba5fcf8c21f9be3ed30b9ba236628fb008f1b8ff7ffdfb"
 COUNTER_TRAFFIC = {
-    "prefill_bf16": dict(gemm_sha256=_GEMM_SHA, fetch_kib=808616.9, write_kib=98337.1),
-    "prefill_fp8_block": dict(gemm_sha256=_GEMM_SHA, fetch_kib=381933.4, write_kib=17429.9),
-    "prefill_fp8_mx": dict(gemm_sha256=_GEMM_SHA, fetch_kib=419778.1, write_kib=17507.2),
+    "prefill_bf16": dict(gemm_sha256=_GEMM_SHA, fetch_kib=802766.7, write_kib=98324.8),
+    "prefill_fp8_block": dict(gemm_sha256=_GEMM_SHA, fetch_kib=382458.6, write_kib=17438.7),
+    "prefill_fp8_mx": dict(gemm_sha256=_GEMM_SHA, fetch_kib=422189.2, write_kib=17505.8),
 }
 
 
