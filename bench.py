@@ -143,11 +143,11 @@ def bench_prefill(torch, moe, name, steps, warmup, stage_steps=10):
 # (x1.0).  Valid only for the GEMM source the counters were taken on; any edit
 # to it turns the figure into null.
 FETCH_SCALE, WRITE_SCALE = 1048576.0 / 524300.5, 1.0
-_GEMM_SHA = "64d025410162ebec64ba5fcf8c21f9be3ed30b9ba236628fb008f1b8ff7ffdfb"
+_GEMM_SHA = "f152d3404fb11001f3fd989a2db6f296e23cc0bd32c76b4281ca7cc08aba7230"
 COUNTER_TRAFFIC = {
-    "prefill_bf16": dict(gemm_sha256=_GEMM_SHA, fetch_kib=802766.7, write_kib=98324.8),
-    "prefill_fp8_block": dict(gemm_sha256=_GEMM_SHA, fetch_kib=382458.6, write_kib=17438.7),
-    "prefill_fp8_mx": dict(gemm_sha256=_GEMM_SHA, fetch_kib=422189.2, write_kib=17505.8),
+    "prefill_bf16": dict(gemm_sha256=_GEMM_SHA, fetch_kib=803991.4, write_kib=98324.4),
+    "prefill_fp8_block": dict(gemm_sha256=_GEMM_SHA, fetch_kib=382525.1, write_kib=17436.9),
+    "prefill_fp8_mx": dict(gemm_sha256=_GEMM_SHA, fetch_kib=421981.3, write_kib=17499.5),
 }
 
 
