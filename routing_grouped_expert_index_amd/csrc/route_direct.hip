@@ -158,6 +158,9 @@ __device__ __forceinline__ float block_max(float m, float* sred) {
 __device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int i) {
     return ((const __attribute__((address_space(4))) int32_t*)(p))[__builtin_amdgcn_readfirstlane(i)];
 }
+__device__ __forceinline__ float ld_uniform_f(const float* p, int i) {
+    return ((const __attribute__((address_space(4))) float*)(p))[__builtin_amdgcn_readfirstlane(i)];
+}
 
 // Activation rows are staged in LDS once per workgroup (every lane of a
 // 32-row weight block needs the same activation values): bf16 values, or e4m3
@@ -422,6 +425,7 @@ rd_gate_up_kernel(const RdArgs a) {
     const int NG = a.H / 256;
     // the expert's index in this call's slice and its weight rows; false for
     // another slice's expert (no h, a zero share of the h amax)
+    float sgu = 1.0f;
     auto resolve = [&](int eg) __attribute__((always_inline)) {
         e = eg - a.e0;
         if ((unsigned)e >= (unsigned)a.nloc) {
@@ -432,6 +436,9 @@ rd_gate_up_kernel(const RdArgs a) {
         }
         wg = a.wgu + (long)e * 2 * a.I * Kb + (long)(2 * G) * gstride + (32 * hh + jr) * 16 + ls * 2048;
         wu = wg + gstride;
+        // (the per-tensor weight scale is requested now: read only at the end, a
+        // load there would add a whole memory latency after the products)
+        if constexpr (Q == RD_TENSOR) sgu = ld_uniform_f(a.s_gu, e);
         if constexpr (Q == RD_MX) {
             swg = reinterpret_cast<const uint32_t*>(a.s_gu) + ((long)e * (2 * a.I / 32) + 2 * G) * NG * 64 + jr;
             swu = swg + NG * 64;
@@ -675,7 +682,7 @@ rd_gate_up_kernel(const RdArgs a) {
             }
         }
         if constexpr (Q == RD_TENSOR) {
-            const float fsc = xs * a.s_gu[e];
+            const float fsc = xs * sgu;
             gv *= fsc;
             uv *= fsc;
         }
@@ -771,6 +778,10 @@ rd_down_part_kernel(const RdArgs a) {
                                            ((long)e * nb + g32) * (a.I / 256) * 64 + (lane & 31)
                                      : nullptr;
 
+    // the route's gate (and per-tensor weight scale), used only at the end:
+    // requested before the weight stream so their latency is hidden under it
+    const float gate = ld_uniform_f(a.tw, r);
+    const float sdw = Q == RD_TENSOR ? ld_uniform_f(a.s_d, e) : 1.0f;
     u32x4 vw[U][2];
     uint32_t mw[Q == RD_MX ? U : 1][2];
     u32x4 va[U][2];   // bf16: activation slices of the batch (the row is not staged in LDS)
@@ -861,8 +872,8 @@ rd_down_part_kernel(const RdArgs a) {
     if (wave == 0 && hh == 0) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) v += red[w][lane];
-        float gw = a.tw[r];
-        if constexpr (Q == RD_TENSOR) gw *= hs * a.s_d[e];
+        float gw = gate;
+        if constexpr (Q == RD_TENSOR) gw *= hs * sdw;
         v *= gw;
     }
     rd_part_publish(a, tb, t, g32, it, items, v, last_s);
@@ -908,6 +919,7 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
     u32x4 hb[QPL];
     int r = 0, e = 0, s0 = 0;
     bool live = false;
+    float gate = 0.0f, sdw = 1.0f;
     auto issue = [&](int it) __attribute__((always_inline)) {
         const int jj = it / KP, kp = it - jj * KP;
         r = t * a.k + jj;
@@ -925,6 +937,9 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
         }
         e = ld_uniform(a.ids, r) - a.e0;   // index in this call's expert slice
         live = (unsigned)e < (unsigned)a.nloc;
+        // the slot's gate and weight scale with its weights (used after the dot)
+        gate = ld_uniform_f(a.tw, r);
+        if constexpr (Q == RD_TENSOR) sdw = ld_uniform_f(a.s_d, live ? e : 0);
         if (live) {
             const uint8_t* wb = a.wd + (long)e * a.H * Kb + (long)g32 * 32 * Kb + (long)s0 * 2048 + lane * 16;
 #pragma unroll
@@ -998,8 +1013,8 @@ __global__ void __launch_bounds__(64 * kRdBlockWaves) rd_down_block_kernel(const
             __builtin_amdgcn_sched_barrier(0);   // one slice's activations at a time
         }
         y += __shfl_xor(y, 32);
-        float gw = a.tw[r];
-        if constexpr (Q == RD_TENSOR) gw *= hs * a.s_d[e];
+        float gw = gate;
+        if constexpr (Q == RD_TENSOR) gw *= hs * sdw;
         if (hh == 0) red[it * 32 + j] = gw * y;
         __asm__ volatile("" ::: "memory");
     }
