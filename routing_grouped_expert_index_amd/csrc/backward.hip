@@ -292,7 +292,11 @@ pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restri
 // e's routes at poff[e] + (i - offsets[e]), zeros up to poff[e+1]) as e4m3
 // codes, each 64-position slice in chunk order 0, 2, 1, 3 (the scaled MFMA's
 // lane-half order: lane half hh reads bytes [32hh, 32hh + 32) of a slice), and
-// the scale bytes of route block b at mx_scale_pos(b) of the row's bytes.
+// the scale bytes in groups of 8 route blocks (256 positions): group q of row m
+// at bytes 8 (q M + m), route block b's byte at mx_scale_pos(b) % 8 of its
+// group, so that the 128 rows of a product tile hold one group's scales in 1 KB
+// in a row (the weight-gradient kernel reads them in 64-byte pieces, where with
+// each row's bytes together every 8-byte read was a request of its own).
 // One workgroup per 128 padded positions (two slices) and 64 columns: wave q
 // takes block 4x + q and lane l column l, so the four 32-byte pieces of a
 // row's 128-byte line come from one workgroup at about the same time (the
@@ -357,21 +361,27 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
     uint8_t* row = out + (long)m * ldo + (long)(gi >> 1) * 64 + 16 * (gi & 1);
     *reinterpret_cast<u32x4*>(row) = lo4;
     *reinterpret_cast<u32x4*>(row + 32) = hi4;
-    sout[(long)m * lds_ + mx_scale_pos(gi)] = (uint8_t)b;
+    sout[((long)(gi >> 3) * M + m) * 8 + (mx_scale_pos(gi) & 7)] = (uint8_t)b;
 }
 
 // ------------------------------------------------------- weight gradients --
 
 // C[e] (bf16 [M][N], the master weights' type) = sum over expert e's padded
 // route positions p of
-// A[m][p] B[n][p], with A, B the dim1-cast operands (row stride ldo bytes,
-// scale row stride lds_ bytes).  One workgroup per 128x128 output tile.  The
-// tile's 128 rows of A and of B, and their E8M0 scale dwords, come into LDS by
-// buffer loads with the LDS bit, one 64-position slice (18 KB) at a time into
-// two alternating buffers: slice s + 1's loads are issued before the wait for
-// slice s, so each wait covers one slice's latency less (the expert's K is
-// short, 4-5 slices, and the tile is bound by latency and its output stores,
-// not by its products).  What counts beside that is how many workgroups share
+// A[m][p] B[n][p], with A, B the dim1-cast operands (code rows of ldo bytes;
+// scales in groups of 8 route blocks, a group holding 8 bytes for each of the
+// M (N) rows, lds_ bytes a row in all).  One workgroup per 128x128 output
+// tile.  The tile's 128 rows of A and of B come into LDS by buffer loads with
+// the LDS bit, one 64-position slice (16 KB) at a time into two alternating
+// buffers, and their E8M0 scale dwords once per group of four slices (2 KB)
+// into two alternating scale areas: slice s + 1's loads are issued before the
+// wait for slice s, so each wait covers one slice's latency less (the
+// expert's K is short, 4-5 slices, and the tile is bound by latency, its
+// output stores and the number of requests the L2 serves, not by its
+// products: with each row's scale bytes 8 bytes apart from the next row's,
+// the 8-byte scale reads were half of the kernel's L2 requests, and storing
+// them group-major took dW_gate_up from 452 to 388 us and dW_down from 234
+// to 182 us at the MX prefill shape).  What counts beside that is how many workgroups share
 // a CU: 36 KB of LDS and 124 registers a lane keep four per SIMD (staging
 // two or four slices per round in one buffer measured 5% and 23% slower than
 // one; the two buffers against one: dW_gate_up 507 -> 459 us, dW_down 270 ->
@@ -439,12 +449,15 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
     // __syncthreads' release fence would wait for every load into LDS still
     // in flight, slice s + 1's included; the explicit vmcnt waits order the
     // loads against the reads instead.
-    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(sA) + (long)mt * 128 * lds_, 0, (int)(128 * lds_), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(sB) + (long)nt * 128 * lds_, 0, (int)(128 * lds_), 0x00020000);
-    // scale DMA lane: row 32 wave + lane / 2, lane half lane % 2
-    const uint32_t sof = (uint32_t)((32 * wave + (lane >> 1)) * lds_) + 4u * (uint32_t)(lane & 1);
+    // the scale arrays: groups of 8 route blocks, each group M (N) rows of 8
+    // bytes; this lane's 4 bytes of the wave's 32 rows (row 32 wave + lane / 2,
+    // lane half lane % 2) in group 0
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sA), 0,
+                                                                         (int)(M * lds_), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sB), 0,
+                                                                         (int)(N * lds_), 0x00020000);
+    const uint32_t sofa = (uint32_t)((mt * 128 + 32 * wave) * 8 + 4 * lane);
+    const uint32_t sofb = (uint32_t)((nt * 128 + 32 * wave) * 8 + 4 * lane);
     auto issue = [&](int s, int buf) __attribute__((always_inline)) {
         const uint32_t so = (uint32_t)(s * 64);
         uint8_t* lb = smem + buf * kWgBuf;
@@ -453,9 +466,16 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la + 1024), 16, dof1 + so, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192), 16, dof0 + so, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192 + 1024), 16, dof1 + so, 0, 0, 0);
-        const uint32_t sso = sof + (uint32_t)((s >> 2) * 8);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, MOE_LDS_B(lb + 16384 + wave * 256), 4, sso, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, MOE_LDS_B(lb + 17408 + wave * 256), 4, sso, 0, 0, 0);
+        if (s == s0 || (s & 3) == 0) {
+            // the scales of slice s's group of 4 slices, once per group, into
+            // the scale area of buffer (group % 2)
+            const uint32_t q = (uint32_t)(s >> 2);
+            uint8_t* lq = smem + (q & 1) * kWgBuf;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, MOE_LDS_B(lq + 16384 + wave * 256), 4,
+                                                     sofa + q * (uint32_t)M * 8u, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, MOE_LDS_B(lq + 17408 + wave * 256), 4,
+                                                     sofb + q * (uint32_t)N * 8u, 0, 0, 0);
+        }
     };
     if (s0 < s1) issue(s0, 0);
     for (int s = s0; s < s1; ++s) {
@@ -465,7 +485,10 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
             __builtin_amdgcn_s_barrier();          // every wave is done reading the other buffer
             __asm__ volatile("" ::: "memory");
             issue(s + 1, buf ^ 1);
-            __builtin_amdgcn_s_waitcnt(0x0F76);    // vmcnt(6): slice s has landed (s + 1's 6 requests may not)
+            if (((s + 1) & 3) == 0)
+                __builtin_amdgcn_s_waitcnt(0x0F76);    // vmcnt(6): slice s has landed (s + 1's 6 requests may not)
+            else
+                __builtin_amdgcn_s_waitcnt(0x0F74);    // vmcnt(4): the same, s + 1 without scales
         } else {
             __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
         }
@@ -473,7 +496,7 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
         __asm__ volatile("" ::: "memory");
         const int sh = 8 * (s & 3);   // byte (slice % 4) of the scale dword: this lane half's block
         const uint8_t* la = smem + buf * kWgBuf;
-        const uint32_t* ls = reinterpret_cast<const uint32_t*>(la + 16384);
+        const uint32_t* ls = reinterpret_cast<const uint32_t*>(smem + ((s >> 2) & 1) * kWgBuf + 16384);
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
             const i32x8 av = frag(la, ra0 + 32 * f);
@@ -610,7 +633,8 @@ hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, cons
 hipError_t launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, long ldo, long lds_,
                         const int32_t* poff, int E, int M, int N, uint16_t* C, hipEvent_t ev_end, hipStream_t st) {
     const long total = (long)E * (M / 128) * (N / 128);
-    if (128 * ldo > 0x7fffffffL) return hipErrorInvalidValue;   // 32-bit offsets within a tile's rows
+    // 32-bit offsets within a tile's rows and within the scale arrays
+    if (128 * ldo > 0x7fffffffL || (long)std::max(M, N) * lds_ > 0x7fffffffL) return hipErrorInvalidValue;
     hipExtLaunchKernelGGL(wgrad_kernel, dim3((unsigned)total), dim3(256), kWgLds, st, nullptr, ev_end, 0, A, sA, B,
                           sB, ldo, lds_, poff, E, M, N, C);
     return hipGetLastError();
