@@ -297,71 +297,135 @@ pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restri
 // group, so that the 128 rows of a product tile hold one group's scales in 1 KB
 // in a row (the weight-gradient kernel reads them in 64-byte pieces, where with
 // each row's bytes together every 8-byte read was a request of its own).
-// One workgroup per 128 padded positions (two slices) and 64 columns: wave q
-// takes block 4x + q and lane l column l, so the four 32-byte pieces of a
-// row's 128-byte line come from one workgroup at about the same time (the
-// cache merges them into whole-line writes; with a workgroup per block the
-// pieces came from four workgroups and the written bytes were 2.2x the
-// codes': 495 -> 395 us for the four casts at the MX prefill shape).
+// One workgroup per 128 padded positions (two slices) and 64 columns, a
+// transpose through LDS in three steps:
+//   1. the tile's 128 route rows of 64 source columns come in by 16-byte
+//      loads (eight lanes a 128-byte bf16 row segment, sixteen a 256-byte
+//      fp32 one), go to fp32 (and times the gate for dy) and into LDS, zero
+//      for padding positions;
+//   2. wave q quantises block q of 32 positions, lane l column l, reading its
+//      32 values down the LDS tile: the amax, the E8M0 byte (stored), and 32
+//      e4m3 codes written to an LDS tile of the output's 64 rows x 128 bytes;
+//   3. eight lanes write each output row's 128-byte line.
+// Against one lane per column reading its 32 routes straight from memory (two
+// bytes a lane for bf16) and writing its 32 codes as two 16-byte pieces into
+// a different row from every lane, this cuts the write requests to the L2
+// about fourfold.
 enum Dim1Src { D1_X = 0, D1_DY = 1, D1_F32 = 2 };
+constexpr int kD1CodeStride = 144;   // bytes an output row in LDS (128 + 16: writes by 8 lanes hit distinct banks)
 
 template <int SRC>
 __global__ void __launch_bounds__(256)
 dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, const float* __restrict__ tw,
             const int32_t* __restrict__ perm, uint32_t kdiv_m, int kdiv_s, const int32_t* __restrict__ offsets,
-            const int32_t* __restrict__ poff, const int32_t* __restrict__ seg, int E, int M, long ldo, long lds_,
+            const int32_t* __restrict__ poff, const int32_t* __restrict__ seg, int E, int M, long ldo,
             uint8_t* __restrict__ out, uint8_t* __restrict__ sout) {
-    // (a route's token r / k as a multiply-shift: a divide per route would be a
-    // long scalar sequence, 32 of them per thread)
+    __shared__ __attribute__((aligned(16))) float tile[128 * 64];   // [route position][column]
+    // (a route's token r / k as a multiply-shift)
     auto tok = [&](int r) { return (long)(((uint64_t)(uint32_t)r * kdiv_m) >> kdiv_s); };
-    const int gi = blockIdx.x * 4 + (threadIdx.x >> 6);   // block of 32 padded positions
-    const int m = blockIdx.y * 64 + (threadIdx.x & 63);
-    const int p0 = gi * 32;
-    const int e = seg[gi >> 1];                    // the expert whose padded segment holds p0
-    if (e >= E) return;                            // past the padded total
-    const int first = offsets[e] + (p0 - poff[e]);       // sorted row of position p0
-    const int cnt = min(32, offsets[e + 1] - first);     // real routes in this block (may be <= 0)
-    if (m >= M) return;
-    float v[32];
-    float a = 0.0f;
-    if (cnt > 0) {
-        // every load unconditional (a route past the expert's last re-reads it
-        // and is masked afterwards): a load under a per-route condition would
-        // become a branch that waits for every load before it
+    const int x = blockIdx.x, m0 = blockIdx.y * 64;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    // the two 64-position slices: expert, sorted row of the slice's first
+    // position, real routes in the slice (may be <= 0)
+    int first[2], cnt[2];
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const long i = first + min(j, cnt - 1);
-            float x;
-            if (SRC == D1_X) {
-                x = bf16_to_f32(static_cast<const uint16_t*>(src)[tok(perm[i]) * M + m]);
-            } else if (SRC == D1_DY) {
-                const int r = perm[i];
-                x = tw[r] * bf16_to_f32(dout[tok(r) * M + m]);
-            } else {
-                x = static_cast<const float*>(src)[i * M + m];
+    for (int h = 0; h < 2; ++h) {
+        const int e = seg[2 * x + h];
+        if (e < E) {
+            first[h] = offsets[e] + (64 * (2 * x + h) - poff[e]);
+            cnt[h] = min(64, offsets[e + 1] - first[h]);
+        } else {
+            first[h] = 0;
+            cnt[h] = 0;
+        }
+    }
+    // 1. source rows into LDS (fp32); a padding position loads a real row of
+    // the tile (every load unconditional: a load under a per-route condition
+    // would become a branch that waits for every load before it) and stores 0
+    const bool any = cnt[0] > 0 || cnt[1] > 0;
+    const int anyrow = cnt[0] > 0 ? first[0] : first[1];
+    auto row_of = [&](int r, bool& ok) __attribute__((always_inline)) {
+        const int h = r >> 6, j = r & 63;
+        ok = j < cnt[h];
+        return ok ? first[h] + j : anyrow;
+    };
+    if (any) {
+        if constexpr (SRC == D1_F32) {
+            const int c = t & 15;   // 4 columns
+            float4 v[8];
+            bool ok[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = row_of((t >> 4) + 16 * i, ok[i]);
+                v[i] = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + (long)row * M + m0 + 4 * c);
             }
-            v[j] = j < cnt ? x : 0.0f;
-            a = fmaxf(a, fabsf(v[j]));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 z = ok[i] ? v[i] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+                *reinterpret_cast<float4*>(tile + ((t >> 4) + 16 * i) * 64 + 4 * c) = z;
+            }
+        } else {
+            const int c = t & 7;   // 8 columns
+            u32x4 v[4];
+            float g[4];
+            bool ok[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = row_of((t >> 3) + 32 * i, ok[i]);
+                const int r = perm[row];
+                const uint16_t* base = SRC == D1_X ? static_cast<const uint16_t*>(src) : dout;
+                v[i] = *reinterpret_cast<const u32x4*>(base + tok(r) * M + m0 + 8 * c);
+                g[i] = SRC == D1_DY ? tw[r] : 1.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float w = ok[i] ? g[i] : 0.0f;
+                float* d = tile + ((t >> 3) + 32 * i) * 64 + 8 * c;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    d[2 * u] = w * __uint_as_float(v[i][u] << 16);
+                    d[2 * u + 1] = w * __uint_as_float(v[i][u] & 0xffff0000u);
+                }
+            }
         }
     } else {
+        for (int i = t; i < 128 * 64 / 4; i += 256) reinterpret_cast<float4*>(tile)[i] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    __syncthreads();
+    // 2. block q = wave of 32 positions, column lane
+    float v[32];
+    float a = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) v[j] = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+        v[j] = tile[(32 * wave + j) * 64 + lane];
+        a = fmaxf(a, fabsf(v[j]));
     }
     const uint32_t b = mx_byte(a);
     const float inv = mx_inv(b);
     u32x4 lo4, hi4;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        lo4[t] = f32x4_to_e4m3x4(v[4 * t] * inv, v[4 * t + 1] * inv, v[4 * t + 2] * inv, v[4 * t + 3] * inv);
-        hi4[t] = f32x4_to_e4m3x4(v[16 + 4 * t] * inv, v[16 + 4 * t + 1] * inv, v[16 + 4 * t + 2] * inv,
-                                 v[16 + 4 * t + 3] * inv);
+    for (int u = 0; u < 4; ++u) {
+        lo4[u] = f32x4_to_e4m3x4(v[4 * u] * inv, v[4 * u + 1] * inv, v[4 * u + 2] * inv, v[4 * u + 3] * inv);
+        hi4[u] = f32x4_to_e4m3x4(v[16 + 4 * u] * inv, v[16 + 4 * u + 1] * inv, v[16 + 4 * u + 2] * inv,
+                                 v[16 + 4 * u + 3] * inv);
     }
+    const int gi = 4 * x + wave;   // block of 32 padded positions
+    sout[((long)(gi >> 3) * M + m0 + lane) * 8 + (mx_scale_pos(gi) & 7)] = (uint8_t)b;
+    __syncthreads();   // every wave is done reading the source tile
     // block gi of its 64-position slice: even -> chunks 0, 1 at bytes 0, 32;
     // odd -> chunks 2, 3 at bytes 16, 48
-    uint8_t* row = out + (long)m * ldo + (long)(gi >> 1) * 64 + 16 * (gi & 1);
-    *reinterpret_cast<u32x4*>(row) = lo4;
-    *reinterpret_cast<u32x4*>(row + 32) = hi4;
-    sout[((long)(gi >> 3) * M + m) * 8 + (mx_scale_pos(gi) & 7)] = (uint8_t)b;
+    uint8_t* ct = reinterpret_cast<uint8_t*>(tile);
+    uint8_t* cr = ct + lane * kD1CodeStride + 64 * (wave >> 1) + 16 * (wave & 1);
+    *reinterpret_cast<u32x4*>(cr) = lo4;
+    *reinterpret_cast<u32x4*>(cr + 32) = hi4;
+    __syncthreads();
+    // 3. row m0 + rr, bytes [128x, 128x + 128): lanes 8 a row
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int rr = (t >> 3) + 32 * i, c = t & 7;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(ct + rr * kD1CodeStride + 16 * c);
+        *reinterpret_cast<u32x4*>(out + (long)(m0 + rr) * ldo + 128L * x + 16 * c) = w;
+    }
 }
 
 // ------------------------------------------------------- weight gradients --
@@ -610,7 +674,8 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, int3
 hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, const float* tw, const int32_t* perm,
                        int k, const int32_t* offsets, const int32_t* poff, const int32_t* seg, int E, int M, long Rp,
                        long ldo, long lds_, uint8_t* out, uint8_t* sout, hipEvent_t ev_end, hipStream_t st) {
-    const dim3 grid((unsigned)(Rp / 128), (unsigned)((M + 63) / 64));
+    if (M % 64 != 0 || Rp % 128 != 0 || lds_ * 32 != Rp) return hipErrorInvalidValue;   // whole tiles
+    const dim3 grid((unsigned)(Rp / 128), (unsigned)(M / 64));
     if (Rp == 0) return hipSuccess;
     // r / k == (r * m) >> s for every r < 2^31 and 1 <= k <= 2^10, with
     // s = 31 + ceil(log2 k) and m = ceil(2^s / k) < 2^32
@@ -620,13 +685,13 @@ hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, cons
     const uint32_t kdiv_m = (uint32_t)(((1ULL << kdiv_s) + (uint64_t)k - 1) / (uint64_t)k);
     if (src_kind == D1_X)
         hipExtLaunchKernelGGL(dim1_kernel<D1_X>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm, kdiv_m, kdiv_s,
-                              offsets, poff, seg, E, M, ldo, lds_, out, sout);
+                              offsets, poff, seg, E, M, ldo, out, sout);
     else if (src_kind == D1_DY)
         hipExtLaunchKernelGGL(dim1_kernel<D1_DY>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm, kdiv_m, kdiv_s,
-                              offsets, poff, seg, E, M, ldo, lds_, out, sout);
+                              offsets, poff, seg, E, M, ldo, out, sout);
     else
         hipExtLaunchKernelGGL(dim1_kernel<D1_F32>, grid, dim3(256), 0, st, nullptr, ev_end, 0, src, dout, tw, perm,
-                              kdiv_m, kdiv_s, offsets, poff, seg, E, M, ldo, lds_, out, sout);
+                              kdiv_m, kdiv_s, offsets, poff, seg, E, M, ldo, out, sout);
     return hipGetLastError();
 }
 
