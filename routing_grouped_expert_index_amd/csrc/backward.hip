@@ -379,12 +379,13 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float w = ok[i] ? g[i] : 0.0f;
+                // (a select, not a multiply by 0: the re-read row may hold an
+                // infinity)
                 float* d = tile + ((t >> 3) + 32 * i) * 64 + 8 * c;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    d[2 * u] = w * __uint_as_float(v[i][u] << 16);
-                    d[2 * u + 1] = w * __uint_as_float(v[i][u] & 0xffff0000u);
+                    d[2 * u] = ok[i] ? g[i] * __uint_as_float(v[i][u] << 16) : 0.0f;
+                    d[2 * u + 1] = ok[i] ? g[i] * __uint_as_float(v[i][u] & 0xffff0000u) : 0.0f;
                 }
             }
         }
