@@ -291,7 +291,10 @@ pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restri
 // transposed: row m of the output holds the padded route positions p (expert
 // e's routes at poff[e] + (i - offsets[e]), zeros up to poff[e+1]) as e4m3
 // codes, each 64-position slice in chunk order 0, 2, 1, 3 (the scaled MFMA's
-// lane-half order: lane half hh reads bytes [32hh, 32hh + 32) of a slice), and
+// lane-half order: lane half hh reads bytes [32hh, 32hh + 32) of a slice),
+// stored slice-major: slice s of row m at bytes 64 (s M + m), so that the 128
+// rows of a product tile hold one slice in 8 KB in a row (read in 128-byte
+// lines where row-major rows gave a 64-byte request a row and slice), and
 // the scale bytes in groups of 8 route blocks (256 positions): group q of row m
 // at bytes 8 (q M + m), route block b's byte at mx_scale_pos(b) % 8 of its
 // group, so that the 128 rows of a product tile hold one group's scales in 1 KB
@@ -420,12 +423,12 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
     *reinterpret_cast<u32x4*>(cr) = lo4;
     *reinterpret_cast<u32x4*>(cr + 32) = hi4;
     __syncthreads();
-    // 3. row m0 + rr, bytes [128x, 128x + 128): lanes 8 a row
+    // 3. slice 2x + h of rows m0 .. m0 + 63: 4 KB in a row, 16 bytes a lane
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int rr = (t >> 3) + 32 * i, c = t & 7;
-        const u32x4 w = *reinterpret_cast<const u32x4*>(ct + rr * kD1CodeStride + 16 * c);
-        *reinterpret_cast<u32x4*>(out + (long)(m0 + rr) * ldo + 128L * x + 16 * c) = w;
+    for (int h = 0; h < 2; ++h) {
+        const int rr = t >> 2, c = t & 3;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(ct + rr * kD1CodeStride + 64 * h + 16 * c);
+        *reinterpret_cast<u32x4*>(out + ((long)(2 * x + h) * M + m0 + rr) * 64 + 16 * c) = w;
     }
 }
 
@@ -433,7 +436,8 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
 
 // C[e] (bf16 [M][N], the master weights' type) = sum over expert e's padded
 // route positions p of
-// A[m][p] B[n][p], with A, B the dim1-cast operands (code rows of ldo bytes;
+// A[m][p] B[n][p], with A, B the dim1-cast operands (codes slice-major, 64
+// bytes of a row per 64-position slice, ldo bytes a row in all;
 // scales in groups of 8 route blocks, a group holding 8 bytes for each of the
 // M (N) rows, lds_ bytes a row in all).  One workgroup per 128x128 output
 // tile.  The tile's 128 rows of A and of B come into LDS by buffer loads with
@@ -491,15 +495,17 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[f][g][i] = 0.0f;
     // the tile's rows of A and B as buffer resources (128 rows each)
+    // (slice-major operands: slice s of row r at bytes 64 (s M + r); the
+    // resources start at the tile's first row of slice 0)
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(A) + (long)mt * 128 * ldo, 0, (int)(128 * ldo), 0x00020000);
+        const_cast<uint8_t*>(A) + (long)mt * 128 * 64, 0, (int)((long)M * ldo - (long)mt * 128 * 64), 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(B) + (long)nt * 128 * ldo, 0, (int)(128 * ldo), 0x00020000);
+        const_cast<uint8_t*>(B) + (long)nt * 128 * 64, 0, (int)((long)N * ldo - (long)nt * 128 * 64), 0x00020000);
     // this lane's DMA row (two 16-row groups per wave and slice) and the
     // logical chunk its physical chunk holds
     const int dr0 = 32 * wave + (lane >> 2), dr1 = dr0 + 16;
-    const uint32_t dof0 = (uint32_t)(dr0 * ldo) + 16u * (uint32_t)((lane & 3) ^ ((dr0 >> 2) & 3));
-    const uint32_t dof1 = (uint32_t)(dr1 * ldo) + 16u * (uint32_t)((lane & 3) ^ ((dr1 >> 2) & 3));
+    const uint32_t dof0 = (uint32_t)(dr0 * 64) + 16u * (uint32_t)((lane & 3) ^ ((dr0 >> 2) & 3));
+    const uint32_t dof1 = (uint32_t)(dr1 * 64) + 16u * (uint32_t)((lane & 3) ^ ((dr1 >> 2) & 3));
     // fragment rows of this lane: A rows ra0 + 32f, B rows rb0 + 32g
     const int ra0 = (wave >> 1) * 64 + j, rb0 = (wave & 1) * 64 + j;
     auto frag = [&](const uint8_t* base, int r) __attribute__((always_inline)) {
@@ -524,13 +530,13 @@ wgrad_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, cons
     const uint32_t sofa = (uint32_t)((mt * 128 + 32 * wave) * 8 + 4 * lane);
     const uint32_t sofb = (uint32_t)((nt * 128 + 32 * wave) * 8 + 4 * lane);
     auto issue = [&](int s, int buf) __attribute__((always_inline)) {
-        const uint32_t so = (uint32_t)(s * 64);
+        const uint32_t soa = (uint32_t)s * (uint32_t)M * 64u, sob = (uint32_t)s * (uint32_t)N * 64u;
         uint8_t* lb = smem + buf * kWgBuf;
         uint8_t* la = lb + wave * 2048;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la), 16, dof0 + so, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la + 1024), 16, dof1 + so, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192), 16, dof0 + so, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192 + 1024), 16, dof1 + so, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la), 16, dof0 + soa, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS_B(la + 1024), 16, dof1 + soa, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192), 16, dof0 + sob, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS_B(la + 8192 + 1024), 16, dof1 + sob, 0, 0, 0);
         if (s == s0 || (s & 3) == 0) {
             // the scales of slice s's group of 4 slices, once per group, into
             // the scale area of buffer (group % 2)
@@ -675,7 +681,7 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, int3
 hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, const float* tw, const int32_t* perm,
                        int k, const int32_t* offsets, const int32_t* poff, const int32_t* seg, int E, int M, long Rp,
                        long ldo, long lds_, uint8_t* out, uint8_t* sout, hipEvent_t ev_end, hipStream_t st) {
-    if (M % 64 != 0 || Rp % 128 != 0 || lds_ * 32 != Rp) return hipErrorInvalidValue;   // whole tiles
+    if (M % 64 != 0 || Rp % 128 != 0 || ldo != Rp || lds_ * 32 != Rp) return hipErrorInvalidValue;   // whole tiles
     const dim3 grid((unsigned)(Rp / 128), (unsigned)(M / 64));
     if (Rp == 0) return hipSuccess;
     // r / k == (r * m) >> s for every r < 2^31 and 1 <= k <= 2^10, with
@@ -699,8 +705,9 @@ hipError_t launch_dim1(int src_kind, const void* src, const uint16_t* dout, cons
 hipError_t launch_wgrad(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, long ldo, long lds_,
                         const int32_t* poff, int E, int M, int N, uint16_t* C, hipEvent_t ev_end, hipStream_t st) {
     const long total = (long)E * (M / 128) * (N / 128);
-    // 32-bit offsets within a tile's rows and within the scale arrays
-    if (128 * ldo > 0x7fffffffL || (long)std::max(M, N) * lds_ > 0x7fffffffL) return hipErrorInvalidValue;
+    // 32-bit offsets within the operand and scale arrays (codes: ldo bytes a
+    // row, slice-major; scales: ldo / 32 bytes a row)
+    if ((long)std::max(M, N) * ldo > 0x7fffffffL || lds_ * 32 != ldo || ldo % 64 != 0) return hipErrorInvalidValue;
     hipExtLaunchKernelGGL(wgrad_kernel, dim3((unsigned)total), dim3(256), kWgLds, st, nullptr, ev_end, 0, A, sA, B,
                           sB, ldo, lds_, poff, E, M, N, C);
     return hipGetLastError();
