@@ -451,7 +451,7 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
 // the 8-byte scale reads were half of the kernel's L2 requests, and storing
 // them group-major took dW_gate_up from 452 to 388 us and dW_down from 234
 // to 182 us at the MX prefill shape).  What counts beside that is how many workgroups share
-// a CU: 36 KB of LDS and 124 registers a lane keep four per SIMD (staging
+// a CU: 36 KB of LDS and 128 registers a lane keep four per SIMD (staging
 // two or four slices per round in one buffer measured 5% and 23% slower than
 // one; the two buffers against one: dW_gate_up 507 -> 459 us, dW_down 270 ->
 // 237 us, same bits).  Row r's 16-byte chunk c sits at physical chunk
