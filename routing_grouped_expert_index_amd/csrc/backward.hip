@@ -323,7 +323,12 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
             const int32_t* __restrict__ perm, uint32_t kdiv_m, int kdiv_s, const int32_t* __restrict__ offsets,
             const int32_t* __restrict__ poff, const int32_t* __restrict__ seg, int E, int M, long ldo,
             uint8_t* __restrict__ out, uint8_t* __restrict__ sout) {
-    __shared__ __attribute__((aligned(16))) float tile[128 * 64];   // [route position][column]
+    // [route position][column]: fp32 for fp32 sources, the bf16 values as
+    // loaded for x and dout (16 KB: eight workgroups a CU instead of five),
+    // with dy's gates beside them
+    constexpr bool F32 = SRC == D1_F32;
+    __shared__ __attribute__((aligned(16))) float tile[F32 ? 128 * 64 : 128 * 32];
+    __shared__ float gate[SRC == D1_DY ? 128 : 1];
     // (a route's token r / k as a multiply-shift)
     auto tok = [&](int r) { return (long)(((uint64_t)(uint32_t)r * kdiv_m) >> kdiv_s); };
     const int x = blockIdx.x, m0 = blockIdx.y * 64;
@@ -342,9 +347,10 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
             cnt[h] = 0;
         }
     }
-    // 1. source rows into LDS (fp32); a padding position loads a real row of
-    // the tile (every load unconditional: a load under a per-route condition
-    // would become a branch that waits for every load before it) and stores 0
+    // 1. source rows into LDS; a padding position loads a real row of the
+    // tile (every load unconditional: a load under a per-route condition
+    // would become a branch that waits for every load before it) and stores
+    // 0 (a select, not a multiply by 0: the re-read row may hold an infinity)
     const bool any = cnt[0] > 0 || cnt[1] > 0;
     const int anyrow = cnt[0] > 0 ? first[0] : first[1];
     auto row_of = [&](int r, bool& ok) __attribute__((always_inline)) {
@@ -353,7 +359,7 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
         return ok ? first[h] + j : anyrow;
     };
     if (any) {
-        if constexpr (SRC == D1_F32) {
+        if constexpr (F32) {
             const int c = t & 15;   // 4 columns
             float4 v[8];
             bool ok[8];
@@ -382,18 +388,17 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                // (a select, not a multiply by 0: the re-read row may hold an
-                // infinity)
-                float* d = tile + ((t >> 3) + 32 * i) * 64 + 8 * c;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    d[2 * u] = ok[i] ? g[i] * __uint_as_float(v[i][u] << 16) : 0.0f;
-                    d[2 * u + 1] = ok[i] ? g[i] * __uint_as_float(v[i][u] & 0xffff0000u) : 0.0f;
-                }
+                const int rr = (t >> 3) + 32 * i;
+                *reinterpret_cast<u32x4*>(tile + rr * 32 + 4 * c) = ok[i] ? v[i] : u32x4{0u, 0u, 0u, 0u};
+                if constexpr (SRC == D1_DY)
+                    if (c == 0) gate[rr] = ok[i] ? g[i] : 0.0f;
             }
         }
     } else {
-        for (int i = t; i < 128 * 64 / 4; i += 256) reinterpret_cast<float4*>(tile)[i] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = t; i < (F32 ? 128 * 64 : 128 * 32) / 4; i += 256)
+            reinterpret_cast<float4*>(tile)[i] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (SRC == D1_DY)
+            if (t < 128) gate[t] = 0.0f;
     }
     __syncthreads();
     // 2. block q = wave of 32 positions, column lane
@@ -401,7 +406,13 @@ dim1_kernel(const void* __restrict__ src, const uint16_t* __restrict__ dout, con
     float a = 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-        v[j] = tile[(32 * wave + j) * 64 + lane];
+        const int rr = 32 * wave + j;
+        if constexpr (F32) {
+            v[j] = tile[rr * 64 + lane];
+        } else {
+            v[j] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(tile)[rr * 64 + lane] << 16);
+            if constexpr (SRC == D1_DY) v[j] = gate[rr] * v[j];
+        }
         a = fmaxf(a, fabsf(v[j]));
     }
     const uint32_t b = mx_byte(a);
