@@ -304,10 +304,11 @@ pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restri
 // transpose through LDS in three steps:
 //   1. the tile's 128 route rows of 64 source columns come in by 16-byte
 //      loads (eight lanes a 128-byte bf16 row segment, sixteen a 256-byte
-//      fp32 one), go to fp32 (and times the gate for dy) and into LDS, zero
+//      fp32 one) and go into LDS as loaded (dy's gates beside them), zero
 //      for padding positions;
 //   2. wave q quantises block q of 32 positions, lane l column l, reading its
-//      32 values down the LDS tile: the amax, the E8M0 byte (stored), and 32
+//      32 values down the LDS tile (to fp32, times the gate for dy): the
+//      amax, the E8M0 byte (stored), and 32
 //      e4m3 codes written to an LDS tile of the output's 64 rows x 128 bytes;
 //   3. eight lanes write each output row's 128-byte line.
 // Against one lane per column reading its 32 routes straight from memory (two
